@@ -1,0 +1,149 @@
+"""Seeded synthetic workloads shared by the tests, the smoke check and the benchmark.
+
+This module only draws random inputs.  It holds none of the attention
+method's arithmetic, so both the HIP path and the CPU oracle can be fed from
+it without sharing any computation.
+
+Every tensor is drawn on the CPU with ``torch.Generator().manual_seed(seed)``
+in a fixed order -- Q, K, V, dO, selector scores, then the per-config extra
+(boosted columns or Gumbel noise) -- in float32 and then cast to the config
+dtype, so the oracle (which upcasts the cast values) and the GPU see identical
+bits.
+
+The five named workloads take the shapes of the paper's evaluation models
+(Qwen3-4B / 8B / 14B attention: 32 or 40 query heads over 8 KV heads,
+head_dim 128, blocks of 64 tokens) and its budgets (1024- and 2048-token
+budgets = 16 and 32 blocks, plus a sweep); the value distributions are the
+ones stated beside each entry.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    seq_len: int
+    head_dim: int
+    block: int
+    budgets: tuple
+    dtype: str              # "fp32" or "bf16"
+    seed: int
+    qkv_std: float = 1.0    # Q, K, V ~ N(0, qkv_std^2)
+    score_kind: str = "normal"   # "normal" | "normal_boost" | "gumbel"
+    score_std: float = 1.0
+    boost_frac: float = 0.0
+    boost_value: float = 0.0
+
+    @property
+    def n_blocks(self) -> int:
+        return self.seq_len // self.block
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "fp32" else torch.bfloat16
+
+
+WORKLOADS = {
+    # 1: tiny fp32 case, small enough for the brute-force oracle
+    "tiny_fp32": Workload("tiny_fp32", 1, 1, 1, 256, 64, 16, (4,), "fp32", 1),
+    # 2: Qwen3-4B attention shape, 8k context, 1024-token budget, scaled inputs
+    "qwen3_4b_8k": Workload("qwen3_4b_8k", 1, 32, 8, 8192, 128, 64, (16,), "bf16", 2,
+                            qkv_std=1.0 / math.sqrt(128.0), score_std=2.0),
+    # 3: Qwen3-8B attention shape, 32k context, K = 16, peaked ranking
+    #    (5% of context-block columns boosted by +4)
+    "qwen3_8b_32k": Workload("qwen3_8b_32k", 1, 32, 8, 32768, 128, 64, (16,), "bf16", 3,
+                             score_kind="normal_boost", score_std=2.0,
+                             boost_frac=0.05, boost_value=4.0),
+    # 4: Qwen3-14B attention shape (GQA 5), batch 2, 16k context, budget sweep
+    "qwen3_14b_16k": Workload("qwen3_14b_16k", 2, 40, 8, 16384, 128, 64, (8, 16, 32, 64),
+                              "bf16", 4),
+    # 5: long context, 128k, K = 32 (2048-token budget), Gumbel selector scores
+    "qwen3_8b_128k": Workload("qwen3_8b_128k", 1, 32, 8, 131072, 128, 64, (32,), "bf16", 5,
+                              score_kind="gumbel"),
+}
+
+# Order used by the tests and the benchmark; index 2 is the headline workload.
+WORKLOAD_ORDER = ["tiny_fp32", "qwen3_4b_8k", "qwen3_8b_32k", "qwen3_14b_16k", "qwen3_8b_128k"]
+
+
+def custom(batch, n_q_heads, n_kv_heads, seq_len, head_dim, block, budget, dtype="fp32",
+           seed=0, qkv_std=1.0, score_std=1.0, score_kind="normal") -> Workload:
+    """An ad-hoc workload (used for small parity and edge-case tests)."""
+    return Workload(f"custom_{seed}", batch, n_q_heads, n_kv_heads, seq_len, head_dim, block,
+                    (budget,), dtype, seed, qkv_std=qkv_std, score_kind=score_kind,
+                    score_std=score_std)
+
+
+def generate(w: Workload, with_grad_out: bool = True, seed: Optional[int] = None):
+    """Draw the inputs of workload ``w`` on the CPU.
+
+    Returns a dict with q [B,Hq,N,D], k and v [B,Hkv,N,D], do (like q, if
+    requested) in the workload dtype, and scores float32 [B,Hkv,C,C] (the whole
+    square table is drawn; entries on or above the diagonal are never read).
+    """
+    g = torch.Generator().manual_seed(w.seed if seed is None else seed)
+    dt = w.torch_dtype()
+    qshape = (w.batch, w.n_q_heads, w.seq_len, w.head_dim)
+    kshape = (w.batch, w.n_kv_heads, w.seq_len, w.head_dim)
+    c = w.n_blocks
+
+    def normal(shape, std):
+        x = torch.randn(shape, generator=g, dtype=torch.float32)
+        if std != 1.0:
+            x.mul_(std)
+        return x.to(dt)
+
+    out = {
+        "q": normal(qshape, w.qkv_std),
+        "k": normal(kshape, w.qkv_std),
+        "v": normal(kshape, w.qkv_std),
+    }
+    # dO is always drawn, so the scores that follow do not depend on the flag
+    do = normal(qshape, 1.0)
+    if with_grad_out:
+        out["do"] = do
+    else:
+        del do
+    sshape = (w.batch, w.n_kv_heads, c, c)
+    if w.score_kind == "gumbel":
+        u = torch.rand(sshape, generator=g, dtype=torch.float32)
+        tiny = torch.finfo(torch.float32).tiny
+        u.clamp_(min=tiny, max=1.0 - 2.0 ** -24)
+        scores = -torch.log(-torch.log(u))
+    else:
+        scores = torch.randn(sshape, generator=g, dtype=torch.float32) * w.score_std
+        if w.score_kind == "normal_boost":
+            nb = int(math.ceil(w.boost_frac * c))
+            for b in range(w.batch):
+                for h in range(w.n_kv_heads):
+                    cols = torch.randperm(c, generator=g)[:nb]
+                    scores[b, h][:, cols] += w.boost_value
+    out["scores"] = scores.contiguous()
+    return out
+
+
+def sample_units(w: Workload, count: int, seed: int = 1234):
+    """A seeded sample of (batch, kv head, block) units, always including the
+    first and last block of the first and last (batch, kv head)."""
+    g = torch.Generator().manual_seed(seed)
+    c = w.n_blocks
+    units = {(0, 0, 0), (0, 0, c - 1), (w.batch - 1, w.n_kv_heads - 1, c - 1)}
+    while len(units) < count:
+        b = int(torch.randint(w.batch, (1,), generator=g))
+        h = int(torch.randint(w.n_kv_heads, (1,), generator=g))
+        i = int(torch.randint(c, (1,), generator=g))
+        units.add((b, h, i))
+    return sorted(units)

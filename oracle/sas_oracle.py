@@ -1,0 +1,370 @@
+"""CPU oracle for SAS gated block-sparse attention (forward and backward).
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the package's smoke check and
+the CPU-baseline leg of the benchmark may import this module.  The product path
+(the HIP library and its Python binding) never calls it, and this module imports
+nothing from the product path.
+
+Source: "SAS: Simple Attention Sparsification via End-to-End Optimization of
+Context Ranking" (arXiv 2609.13141), cited below by section / equation /
+algorithm:
+
+  * Sec. 3 (Eq. 2-3): n context tokens are cut into C = n/b contiguous blocks;
+    a query attends to the union of its selected blocks.
+  * Sec. 4.1 (Eq. 4): the query's own block B0 is always kept with unit gate
+    g0 = 1 (zero additive bias); the historical blocks get gates g = phi(s).
+  * Sec. 4.2.2 (Eq. 6): with phi = softmax, log g_m = s_m - LSE(s) over the
+    historical blocks only.
+  * Sec. 4.3 (Eq. 9, Alg. 1): I = Top-K(g, K); S = B0 u U_{m in I} B_m;
+    o = softmax(q K_S^T + log g_S) V_S.
+  * Sec. 4.3 "Kernel Design" and App. E: Top-K is realised as a per-query
+    threshold on the gate (a block is active when it reaches the threshold);
+    the current block is causal and unbiased; sm_scale multiplies q.k only.
+  * App. E (backward): Delta = rowsum(O * dO), P recomputed from LSE,
+    dS = P * (dO V^T - Delta); the block log-gate gradient is the sum of dS over
+    the tokens of each selected block.
+  * App. D.3: softmax backward to the selector scores,
+    ds_m = g_m (dg_m - sum_l g_l dg_l), with dg_l = 0 for unselected blocks
+    under the sparse scope (Eq. 8).
+  * Sec. 4.2.2 (Eq. 5) / App. D.1: closed form of the inner-gate gradient,
+    dg_m = sum_{i in B_m} (p_i / g_m) dO^T (v_i - o).
+
+Readings where the pages leave a step open (each also listed in the design
+notes of the repository):
+  * gates, threshold and selection are per (batch, kv head, query block,
+    context block) and are shared by the G query heads of a KV group and by
+    the b queries of a query block; a shared gate's gradient is the sum over
+    its uses;
+  * K counts historical blocks only; the current block is extra; for query
+    block i <= K every historical block is selected; K = 0 selects none;
+  * the threshold is applied to the fp32 selector score s itself (log g is a
+    monotone shift of s), selection is s >= tau, so ties at tau are all kept;
+  * query head h reads kv head floor(h / G);
+  * sm_scale defaults to 1/sqrt(D) and never scales log g.
+
+Everything is float64 numpy; inputs are upcast from the exact values the GPU
+sees.  Two forms are provided: a brute-force dense evaluation per query head
+(``dense_*``, tiny sizes) and a per-query-block evaluation (``forward`` /
+``backward``), which evaluates the same definition one query block at a time
+because the attended set is fixed per query block.
+
+Parity pins: every function here is checked in ``tests/test_oracle.py``
+against closed forms, library routines and finite differences (no function is
+"parity unpinned").
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+# ---------------------------------------------------------------------------
+# Gate activation and Top-K selection (Eq. 4, Eq. 6, Alg. 1, App. E threshold)
+# ---------------------------------------------------------------------------
+
+def _logsumexp(x: np.ndarray) -> float:
+    mx = np.max(x)
+    return float(mx + np.log(np.sum(np.exp(x - mx))))
+
+
+def kth_largest_threshold(hist_f32: np.ndarray, k: int) -> np.float32:
+    """Threshold tau that realises Top-K over one row of historical scores.
+
+    App. E encodes the Top-K set as "selected iff the gate reaches tau".  With
+    tau equal to the K-th largest historical value the selected set is exactly
+    the K largest (plus any exact ties at tau).  If K >= number of historical
+    blocks every block is kept (tau = -inf); K = 0 keeps none (tau = +inf).
+    The comparison is made on the fp32 score values themselves.
+    """
+    n = hist_f32.shape[0]
+    if k >= n:
+        return np.float32(-np.inf)
+    if k == 0:
+        return np.float32(np.inf)
+    # np.partition: the element at index n-k is the k-th largest.
+    return np.float32(np.partition(hist_f32, n - k)[n - k])
+
+
+def gate_threshold(scores: np.ndarray, budget_k: int):
+    """Gates, thresholds and selected sets for every query block.
+
+    scores: fp32 [B, Hkv, C, C]; only entries m < i of row i are read (the
+    historical blocks of query block i, Sec. 4.1).
+
+    Returns (log_gate, tau, sel):
+      log_gate float64 [B, Hkv, C, C]: s_m - LSE_{m<i}(s) for m < i (Eq. 6),
+               0 on the diagonal (g0 = 1, Eq. 4), -inf above it;
+      tau      float32 [B, Hkv, C]: score-space threshold of each row;
+      sel      bool    [B, Hkv, C, C]: m < i and s_{i,m} >= tau_i.
+    """
+    scores = np.asarray(scores)
+    assert scores.dtype == np.float32 and scores.ndim == 4
+    bsz, hkv, c, c2 = scores.shape
+    assert c == c2
+    log_gate = np.full((bsz, hkv, c, c), NEG_INF, dtype=np.float64)
+    tau = np.empty((bsz, hkv, c), dtype=np.float32)
+    sel = np.zeros((bsz, hkv, c, c), dtype=bool)
+    for b in range(bsz):
+        for h in range(hkv):
+            for i in range(c):
+                hist = scores[b, h, i, :i]
+                if i > 0:
+                    s64 = hist.astype(np.float64)
+                    log_gate[b, h, i, :i] = s64 - _logsumexp(s64)
+                log_gate[b, h, i, i] = 0.0
+                t = kth_largest_threshold(hist, budget_k)
+                tau[b, h, i] = t
+                sel[b, h, i, :i] = hist >= t
+    return log_gate, tau, sel
+
+
+def selected_lists(sel: np.ndarray):
+    """Ascending selected-block index list and count per row of ``sel``."""
+    bsz, hkv, c, _ = sel.shape
+    cnt = sel.sum(axis=-1).astype(np.int64)
+    lists = [[[np.nonzero(sel[b, h, i])[0] for i in range(c)] for h in range(hkv)]
+             for b in range(bsz)]
+    return lists, cnt
+
+
+# ---------------------------------------------------------------------------
+# Attended set of one query block (Eq. 9 with the App. E current-block rule)
+# ---------------------------------------------------------------------------
+
+def _attended_keys(i: int, block: int, sel_row: np.ndarray, log_gate_row: np.ndarray):
+    """Key token indices, per-key additive bias and per-key block id for block i.
+
+    Keys are the current block (bias 0, causal inside it) followed by every
+    selected historical block m (bias log g_m).  The order of keys does not
+    change the softmax.
+    """
+    own = np.arange(i * block, (i + 1) * block)
+    blocks = [i] + [int(m) for m in np.nonzero(sel_row)[0]]
+    keys = np.concatenate([np.arange(m * block, (m + 1) * block) for m in blocks])
+    bias = np.concatenate([np.zeros(block)] +
+                          [np.full(block, log_gate_row[m]) for m in blocks[1:]])
+    kblk = np.repeat(np.array(blocks), block)
+    # causal mask inside the current block: key position must not exceed query
+    qpos = own[:, None]
+    mask = np.ones((block, keys.shape[0]), dtype=bool)
+    mask[:, :block] = keys[None, :block] <= qpos
+    return keys, bias, kblk, mask
+
+
+def _softmax_rows(z: np.ndarray):
+    mx = np.max(z, axis=1, keepdims=True)
+    e = np.exp(z - mx)
+    s = np.sum(e, axis=1, keepdims=True)
+    return e / s, (mx + np.log(s))[:, 0]
+
+
+def default_scale(head_dim: int, sm_scale: float | None) -> float:
+    if sm_scale is None or sm_scale <= 0:
+        return 1.0 / math.sqrt(head_dim)
+    return float(sm_scale)
+
+
+def forward(q, k, v, log_gate, sel, block: int, sm_scale: float | None = None,
+            query_blocks=None):
+    """Eq. 9 output and natural-log LSE, one query block at a time.
+
+    q: [B, Hq, N, D]; k, v: [B, Hkv, N, D]; log_gate/sel: [B, Hkv, C, C].
+    ``query_blocks``: optional iterable of (b, h_kv, i) to evaluate (others
+    are left NaN), so large shapes can be sampled.
+    Returns (o [B, Hq, N, D], lse [B, Hq, N]) in float64.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    bsz, hq, n, d = q.shape
+    hkv = k.shape[1]
+    g = hq // hkv
+    scale = default_scale(d, sm_scale)
+    c = n // block
+    o = np.full(q.shape, np.nan)
+    lse = np.full((bsz, hq, n), np.nan)
+    units = query_blocks if query_blocks is not None else \
+        [(b, h, i) for b in range(bsz) for h in range(hkv) for i in range(c)]
+    for (b, hk, i) in units:
+        keys, bias, _, mask = _attended_keys(i, block, sel[b, hk, i], log_gate[b, hk, i])
+        kk = k[b, hk, keys]
+        vv = v[b, hk, keys]
+        rows = slice(i * block, (i + 1) * block)
+        for hh in range(hk * g, (hk + 1) * g):
+            z = scale * (q[b, hh, rows] @ kk.T) + bias[None, :]
+            z = np.where(mask, z, NEG_INF)
+            p, l = _softmax_rows(z)
+            o[b, hh, rows] = p @ vv
+            lse[b, hh, rows] = l
+    return o, lse
+
+
+def backward(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = None,
+             query_blocks=None):
+    """Gradients of Eq. 9 w.r.t. q, k, v and the block log gates.
+
+    Follows the recomputation view of App. E: P from the attended logits,
+    dP = dO V^T, Delta = rowsum(P * dP) (= dO . o), dS = P * (dP - Delta);
+    dQ = sm_scale dS K, dK = sm_scale dS^T Q, dV = P^T dO, summed over the G
+    query heads that read the same kv head; dLogG[i, m] = sum of dS over the
+    query tokens of block i (all heads of the group) and the key tokens of
+    selected historical block m.  Zero for unselected m, the diagonal and the
+    upper triangle.
+
+    If ``query_blocks`` is given, only those query blocks contribute (their dQ
+    and dLogG rows are exact; dK/dV hold only their contributions).
+    Returns (dq, dk, dv, dlog_gate) in float64.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    do = np.asarray(do, np.float64)
+    bsz, hq, n, d = q.shape
+    hkv = k.shape[1]
+    g = hq // hkv
+    scale = default_scale(d, sm_scale)
+    c = n // block
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dlg = np.zeros((bsz, hkv, c, c))
+    units = query_blocks if query_blocks is not None else \
+        [(b, h, i) for b in range(bsz) for h in range(hkv) for i in range(c)]
+    for (b, hk, i) in units:
+        keys, bias, kblk, mask = _attended_keys(i, block, sel[b, hk, i], log_gate[b, hk, i])
+        kk = k[b, hk, keys]
+        vv = v[b, hk, keys]
+        rows = slice(i * block, (i + 1) * block)
+        ds_sum = np.zeros(keys.shape[0])
+        for hh in range(hk * g, (hk + 1) * g):
+            qq = q[b, hh, rows]
+            dd = do[b, hh, rows]
+            z = scale * (qq @ kk.T) + bias[None, :]
+            z = np.where(mask, z, NEG_INF)
+            p, _ = _softmax_rows(z)
+            dp = dd @ vv.T
+            delta = np.sum(p * dp, axis=1, keepdims=True)
+            ds = p * (dp - delta)
+            dq[b, hh, rows] = scale * (ds @ kk)
+            np.add.at(dk[b, hk], keys, scale * (ds.T @ qq))
+            np.add.at(dv[b, hk], keys, p.T @ dd)
+            ds_sum += ds.sum(axis=0)
+        for m in np.unique(kblk):
+            if m != i:
+                dlg[b, hk, i, m] = ds_sum[kblk == m].sum()
+    return dq, dk, dv, dlg
+
+
+def backward_kv_block(q, k, v, do, log_gate, sel, block: int, b: int, hk: int, j: int,
+                      sm_scale: float | None = None):
+    """dK and dV of one key block j of one (batch, kv head), exactly.
+
+    Sums the contributions of every query block that attends block j: the
+    diagonal block i = j and every i > j with j in I_i (Eq. 9 gradient).
+    Returns (dk_j [block, D], dv_j [block, D]).
+    """
+    c = q.shape[2] // block
+    users = [(b, hk, i) for i in range(j, c) if i == j or sel[b, hk, i, j]]
+    _, dk, dv, _ = backward(q, k, v, do, log_gate, sel, block, sm_scale, query_blocks=users)
+    rows = slice(j * block, (j + 1) * block)
+    return dk[b, hk, rows], dv[b, hk, rows]
+
+
+def dscores(dlog_gate, log_gate, sel):
+    """Selector-score gradient from the block log-gate gradient (App. D.3).
+
+    dg_m = dLogG_m / g_m on selected blocks and 0 on unselected ones (sparse
+    scope, Eq. 8); ds_m = g_m (dg_m - sum_l g_l dg_l) over the historical
+    blocks m < i.  Zero for m >= i.  No gradient flows through the Top-K
+    selection itself (it is piecewise constant in s, Sec. 3).
+    """
+    bsz, hkv, c, _ = dlog_gate.shape
+    out = np.zeros((bsz, hkv, c, c))
+    for b in range(bsz):
+        for h in range(hkv):
+            for i in range(1, c):
+                gate = np.exp(log_gate[b, h, i, :i])
+                s = sel[b, h, i, :i]
+                dg = np.zeros(i)
+                dg[s] = dlog_gate[b, h, i, :i][s] / gate[s]
+                out[b, h, i, :i] = gate * (dg - np.sum(gate * dg))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Brute-force dense form (tiny sizes): the full N x N logit matrix per head
+# ---------------------------------------------------------------------------
+
+def dense_bias(log_gate, sel, n: int, block: int, b: int, hk: int) -> np.ndarray:
+    """Additive N x N bias of Eq. 9 for one (batch, kv head).
+
+    bias[t, u] = 0 if u is in t's own block and u <= t (causal, unit gate);
+    log g_{blk t, blk u} if blk u is a selected historical block of blk t;
+    -inf otherwise.
+    """
+    bias = np.full((n, n), NEG_INF)
+    for t in range(n):
+        bt = t // block
+        for u in range(n):
+            bu = u // block
+            if bu == bt and u <= t:
+                bias[t, u] = 0.0
+            elif bu < bt and sel[b, hk, bt, bu]:
+                bias[t, u] = log_gate[b, hk, bt, bu]
+    return bias
+
+
+def dense_forward(q, k, v, log_gate, sel, block: int, sm_scale: float | None = None):
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    bsz, hq, n, d = q.shape
+    g = hq // k.shape[1]
+    scale = default_scale(d, sm_scale)
+    o = np.zeros_like(q)
+    lse = np.zeros((bsz, hq, n))
+    for b in range(bsz):
+        for hh in range(hq):
+            hk = hh // g
+            z = scale * (q[b, hh] @ k[b, hk].T) + dense_bias(log_gate, sel, n, block, b, hk)
+            p, l = _softmax_rows(z)
+            o[b, hh] = p @ v[b, hk]
+            lse[b, hh] = l
+    return o, lse
+
+
+def dense_backward(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = None):
+    """Softmax-Jacobian gradients on the full matrix (App. E backward, dense)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    do = np.asarray(do, np.float64)
+    bsz, hq, n, d = q.shape
+    hkv = k.shape[1]
+    g = hq // hkv
+    c = n // block
+    scale = default_scale(d, sm_scale)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dlg = np.zeros((bsz, hkv, c, c))
+    for b in range(bsz):
+        for hh in range(hq):
+            hk = hh // g
+            z = scale * (q[b, hh] @ k[b, hk].T) + dense_bias(log_gate, sel, n, block, b, hk)
+            p, _ = _softmax_rows(z)
+            dp = do[b, hh] @ v[b, hk].T
+            ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+            dq[b, hh] = scale * ds @ k[b, hk]
+            dk[b, hk] += scale * ds.T @ q[b, hh]
+            dv[b, hk] += p.T @ do[b, hh]
+            blk_sum = ds.reshape(c, block, c, block).sum(axis=(1, 3))
+            for i in range(c):
+                for m in range(i):
+                    if sel[b, hk, i, m]:
+                        dlg[b, hk, i, m] += blk_sum[i, m]
+    return dq, dk, dv, dlg
