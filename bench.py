@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Benchmark of the SAS gated block-sparse attention hot path on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input already resident
+in HBM: gate activation + Top-K threshold (sas_gate_threshold), forward
+(sas_gated_attn_fwd) and backward (sas_gated_attn_bwd_dq, which also writes
+dlog_gate and dscores, then sas_gated_attn_bwd_dkdv).
+
+Metric: fwd+bwd effective TFLOP/s = 14 * D * pairs / step time, where pairs
+counts only the attended (query, key) pairs: per query block the causal
+diagonal triangle plus the selected 64x64 blocks, times the G heads of a kv
+group.  Recomputation inside the backward is not counted.
+
+Prints one JSON line.  Default workload: Qwen3-8B attention shape, 32k
+context, K = 16 (batch 1, 32 query / 8 kv heads, head_dim 128, block 64).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd effective TFLOP/s at Qwen3-8B shape, 32k ctx, K=16 blocks"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3_8b_32k")
+    ap.add_argument("--budget", type=int, default=None)
+    ap.add_argument("--o-dtype", default="fp32", choices=["fp32", "bf16"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="wall-clock budget of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def count_pairs(sel_cnt, cap, block, group):
+    import torch
+    cnt = torch.clamp(sel_cnt.to(torch.int64), max=cap)
+    units = cnt.numel()
+    return group * (units * block * (block + 1) // 2 + block * block * int(cnt.sum().item()))
+
+
+def cpu_baseline(w, K, inp, budget_s, total_pairs):
+    """Time the float64 CPU oracle on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [x for x in threadpool_info() if x.get("user_api") == "blas"]
+        threads = int(blas[0]["num_threads"]) if blas else (os.cpu_count() or 1)
+        vendor = blas[0].get("internal_api", "?") if blas else "?"
+    except Exception:   # threadpoolctl missing
+        threads, vendor = os.cpu_count() or 1, "?"
+    scores = inp["scores"].numpy()
+    t0 = time.perf_counter()
+    lg, _, sel = oracle.gate_threshold(scores, K)
+    t_thr = time.perf_counter() - t0
+    q, k, v, do = (inp[n].float().numpy() for n in ("q", "k", "v", "do"))
+    c = w.n_blocks
+    rng = np.random.default_rng(0)
+    all_units = [(b, h, i) for b in range(w.batch) for h in range(w.n_kv_heads) for i in range(c)]
+    order = rng.permutation(len(all_units))
+    cnt = sel.sum(-1)
+
+    def pairs_of(units):
+        return sum(w.group * (w.block * (w.block + 1) // 2 + w.block * w.block * int(cnt[u]))
+                   for u in units)
+
+    def run(units):
+        t = time.perf_counter()
+        oracle.forward(q, k, v, lg, sel, w.block, query_blocks=units)
+        oracle.backward(q, k, v, do, lg, sel, w.block, query_blocks=units)
+        return time.perf_counter() - t
+
+    probe = [all_units[j] for j in order[:2]]
+    t_probe = run(probe)
+    per = t_probe / 2
+    n = int(max(2, min(len(all_units), (budget_s - t_thr - t_probe) / max(per, 1e-6))))
+    sample = [all_units[j] for j in order[2:2 + n]] or probe
+    t_fb = run(sample)
+    sp = pairs_of(sample)
+    est = t_thr + t_fb * total_pairs / sp
+    flops = 14 * w.head_dim * total_pairs
+    return {"value": flops / est / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"float64 numpy oracle: gate/threshold over all {len(all_units)} rows "
+                       f"({t_thr:.2f} s) + fwd+bwd of {len(sample)} of {len(all_units)} query "
+                       f"blocks ({t_fb:.2f} s), scaled by attended pairs to the whole workload "
+                       f"(est. {est:.1f} s per step); BLAS={vendor}")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards over (batch, kv head) with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from gated_block_sparse_attn_amd import api, workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    K = args.budget if args.budget is not None else w.budgets[0]
+    p = api.Problem(w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.block, K,
+                    w.dtype, 0.0, args.o_dtype if w.dtype == "bf16" else "fp32")
+    cap = p.default_cap()
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    inp = workloads.generate(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do, scores = (inp[n].to(dev) for n in ("q", "k", "v", "do", "scores"))
+    sh_q, sh_kv = q.shape, k.shape
+    c = w.n_blocks
+    lg = torch.empty(w.batch, w.n_kv_heads, c, c, dtype=torch.float32, device=dev)
+    tau = torch.empty(w.batch, w.n_kv_heads, c, dtype=torch.float32, device=dev)
+    sel_idx = torch.empty(w.batch, w.n_kv_heads, c, cap, dtype=torch.int32, device=dev)
+    sel_cnt = torch.empty(w.batch, w.n_kv_heads, c, dtype=torch.int32, device=dev)
+    o = torch.empty(sh_q, dtype=p.torch_o_dtype, device=dev)
+    lse = torch.empty(sh_q[:3], dtype=torch.float32, device=dev)
+    dq = torch.empty(sh_q, dtype=p.torch_dtype, device=dev)
+    dk = torch.empty(sh_kv, dtype=p.torch_dtype, device=dev)
+    dv = torch.empty(sh_kv, dtype=p.torch_dtype, device=dev)
+    dlg = torch.empty_like(lg)
+    dsc = torch.empty_like(lg)
+    ws = torch.empty(api.bwd_workspace_size(p, cap), dtype=torch.uint8, device=dev)
+    stages = ["threshold", "fwd", "bwd_dq", "bwd_dkdv"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        api.gate_threshold(p, scores, sel_cap=cap, outputs=(lg, tau, sel_idx, sel_cnt))
+        if ev is not None:
+            ev[1].record()
+        api.gated_attn_fwd(p, q, k, v, lg, sel_idx, sel_cnt, o=o, lse=lse)
+        if ev is not None:
+            ev[2].record()
+        api.gated_attn_bwd_dq(p, q, k, v, o, do, lse, lg, sel_idx, sel_cnt, dq, dlg, dsc, ws)
+        if ev is not None:
+            ev[3].record()
+        api.gated_attn_bwd_dkdv(p, q, k, v, do, lse, lg, sel_idx, sel_cnt, dk, dv, ws)
+        if ev is not None:
+            ev[4].record()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        step(events[s])
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+    stage_ms = {}
+    for si, name in enumerate(stages):
+        vals = sorted(events[s][si].elapsed_time(events[s][si + 1]) for s in range(args.steps))
+        stage_ms[name] = {"mean": sum(vals) / len(vals), "median": vals[len(vals) // 2],
+                          "min": vals[0]}
+
+    pairs = count_pairs(sel_cnt, cap, w.block, w.group)
+    D = w.head_dim
+    flops = 14 * D * pairs
+    value = flops / (ms_step * 1e-3) / 1e12
+    # algorithmic flops of the main kernel of each stage
+    kflops = {"fwd": 4 * D * pairs, "bwd_dq": 6 * D * pairs, "bwd_dkdv": 4 * D * pairs}
+    dom = max(kflops, key=lambda n: stage_ms[n]["mean"])
+    achieved = kflops[dom] / (stage_ms[dom]["mean"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "kernel": {"fwd": "fwd_mfma_kernel<4>", "bwd_dq": "bwd_dq_kernel<4>",
+                           "bwd_dkdv": "bwd_dkdv_kernel"}[dom],
+                "algorithmic_flops_per_launch": kflops[dom]}
+    result = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded torch generator; Qwen3-shaped, random values)",
+        "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "seq_len": w.seq_len, "head_dim": D,
+                   "block": w.block, "budget_k": K, "o_dtype": p.o_dtype,
+                   "attended_pairs": pairs, "flops_per_step": flops},
+        "roofline": roofline,
+        "stage_ms": stage_ms,
+        "wall_s_timed_region": t_wall,
+        "frac_of_bf16_peak": value / PEAK_BF16_TFLOPS,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        del q, k, v, do
+        result["cpu_baseline"] = cpu_baseline(w, K, inp, args.cpu_seconds, pairs)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

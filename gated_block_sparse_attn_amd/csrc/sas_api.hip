@@ -1,0 +1,242 @@
+// C ABI of libsas: argument validation, workspace sizing and kernel dispatch.
+// Every entry point validates on the host first and reports argument errors
+// before anything is enqueued; kernels are then enqueued on the caller's
+// stream.  No exception crosses the ABI; the only mutable state is the
+// thread-local error message.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/sas.h"
+#include "sas_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int32_t ok() {
+  g_last_error.clear();
+  return SAS_OK;
+}
+
+int32_t hip_fail(hipError_t e, const char* what) {
+  return fail(SAS_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Validate the problem and build the kernel-side shape.
+int32_t validate(const sas_problem* p, int32_t sel_cap, bool need_cap, sas::Shape* s) {
+  if (p == nullptr) return fail(SAS_E_INVALID, "problem pointer is NULL");
+  if (p->batch < 1 || p->n_q_heads < 1 || p->n_kv_heads < 1 || p->seq_len < 1 ||
+      p->head_dim < 1 || p->block_size < 1)
+    return fail(SAS_E_INVALID, "batch, heads, seq_len, head_dim and block_size must be >= 1");
+  if (p->n_q_heads % p->n_kv_heads != 0)
+    return fail(SAS_E_INVALID, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)",
+                p->n_q_heads, p->n_kv_heads);
+  if (p->budget_k < 0) return fail(SAS_E_INVALID, "budget_k must be >= 0 (got %d)", p->budget_k);
+  if (p->dtype != SAS_BF16 && p->dtype != SAS_FP32)
+    return fail(SAS_E_INVALID, "dtype %d is not a sas_dtype", p->dtype);
+  if (p->o_dtype != SAS_BF16 && p->o_dtype != SAS_FP32)
+    return fail(SAS_E_INVALID, "o_dtype %d is not a sas_dtype", p->o_dtype);
+  if (p->dtype == SAS_FP32 && p->o_dtype != SAS_FP32)
+    return fail(SAS_E_INVALID, "o_dtype must be SAS_FP32 when dtype is SAS_FP32");
+  if (isnan(p->sm_scale) || isinf(p->sm_scale))
+    return fail(SAS_E_INVALID, "sm_scale must be finite");
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(SAS_E_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", p->head_dim);
+  if (p->block_size != 16 && p->block_size != 32 && p->block_size != 64)
+    return fail(SAS_E_UNSUPPORTED, "block_size %d unsupported (16, 32 or 64)", p->block_size);
+  if (p->seq_len % p->block_size != 0)
+    return fail(SAS_E_UNSUPPORTED, "seq_len %d is not a multiple of block_size %d (ragged "
+                "blocks are not supported)", p->seq_len, p->block_size);
+  const int C = p->seq_len / p->block_size;
+  if (C > 8192) return fail(SAS_E_UNSUPPORTED, "%d blocks per sequence exceeds 8192", C);
+  if ((long long)p->batch * p->n_q_heads > 65535)
+    return fail(SAS_E_UNSUPPORTED, "batch * n_q_heads exceeds 65535");
+  if (need_cap) {
+    const int need = p->budget_k < C - 1 ? p->budget_k : C - 1;
+    if (sel_cap < 1 || sel_cap < need)
+      return fail(SAS_E_INVALID, "sel_cap %d is smaller than min(budget_k, C-1) = %d (and "
+                  "must be >= 1)", sel_cap, need);
+  }
+  s->B = p->batch;
+  s->Hq = p->n_q_heads;
+  s->Hkv = p->n_kv_heads;
+  s->G = p->n_q_heads / p->n_kv_heads;
+  s->N = p->seq_len;
+  s->D = p->head_dim;
+  s->blk = p->block_size;
+  s->C = C;
+  s->K = p->budget_k;
+  s->cap = sel_cap;
+  s->fp32 = p->dtype == SAS_FP32;
+  s->o_fp32 = p->o_dtype == SAS_FP32;
+  s->scale = p->sm_scale > 0.0f ? p->sm_scale : 1.0f / sqrtf((float)p->head_dim);
+  return SAS_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+namespace sas {
+
+bool mfma_path(const Shape& s) { return !s.fp32 && s.D == 128 && s.blk == 64; }
+
+BwdWorkspace bwd_workspace_layout(const Shape& s) {
+  BwdWorkspace w{};
+  const long long nrow = (long long)s.B * s.Hkv * s.C;  // rows == columns
+  // largest possible number of (row, selected block) entries
+  long long per_seq = 0;
+  for (int i = 0; i < s.C; ++i) per_seq += (i < s.cap ? i : s.cap);
+  const long long emax = per_seq * s.B * s.Hkv;
+  w.words = (s.C + 31) / 32;
+  size_t off = 0;
+  w.delta = off;    off = align256(off + sizeof(float) * (size_t)s.B * s.Hq * s.N);
+  if (mfma_path(s)) {
+    w.dlg_part = off;
+    off = align256(off + sizeof(float) * (size_t)bwd_head_parts(s.G) * nrow * (s.cap + 1));
+    w.colmask = off;  off = align256(off + sizeof(uint32_t) * (size_t)nrow * w.words);
+    w.collen = off;   off = align256(off + sizeof(int32_t) * (size_t)nrow);
+    w.coloff = off;   off = align256(off + sizeof(int32_t) * (size_t)(nrow + 1));
+    w.chunkoff = off; off = align256(off + sizeof(int32_t) * (size_t)(nrow + 1));
+    w.collist = off;  off = align256(off + sizeof(int32_t) * (size_t)(emax + nrow));
+    w.max_chunks = (emax + nrow + kColChunk - 1) / kColChunk + nrow;
+    w.partial = off;  off = align256(off + sizeof(float) * 2 * 64 * 128 * (size_t)w.max_chunks);
+  }
+  w.total = off;
+  return w;
+}
+
+}  // namespace sas
+
+extern "C" {
+
+int32_t sas_abi_version(void) { return SAS_ABI_VERSION; }
+
+const char* sas_last_error(void) { return g_last_error.c_str(); }
+
+int32_t sas_gate_threshold(const sas_problem* p, const float* scores, float* log_gate, float* tau,
+                           int32_t* sel_idx, int32_t* sel_cnt, int32_t sel_cap, int32_t* d_status,
+                           void* stream) {
+  sas::Shape s;
+  int32_t rc = validate(p, sel_cap, true, &s);
+  if (rc != SAS_OK) return rc;
+  if (!scores || !log_gate || !tau || !sel_idx || !sel_cnt)
+    return fail(SAS_E_INVALID, "sas_gate_threshold: a required pointer is NULL");
+  hipError_t e = sas::launch_threshold(s, scores, log_gate, tau, sel_idx, sel_cnt, d_status,
+                                       (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sas_gate_threshold launch");
+  return ok();
+}
+
+int32_t sas_gated_attn_fwd(const sas_problem* p, const void* q, const void* k, const void* v,
+                           const float* log_gate, const int32_t* sel_idx, const int32_t* sel_cnt,
+                           int32_t sel_cap, void* o, float* lse, void* stream) {
+  sas::Shape s;
+  int32_t rc = validate(p, sel_cap, true, &s);
+  if (rc != SAS_OK) return rc;
+  if (!q || !k || !v || !log_gate || !sel_idx || !sel_cnt || !o || !lse)
+    return fail(SAS_E_INVALID, "sas_gated_attn_fwd: a required pointer is NULL");
+  hipError_t e = sas::mfma_path(s)
+                     ? sas::launch_fwd_mfma(s, q, k, v, log_gate, sel_idx, sel_cnt, o, lse,
+                                            (hipStream_t)stream)
+                     : sas::launch_fwd_generic(s, q, k, v, log_gate, sel_idx, sel_cnt, o, lse,
+                                               (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sas_gated_attn_fwd launch");
+  return ok();
+}
+
+size_t sas_gated_attn_bwd_workspace_size(const sas_problem* p, int32_t sel_cap) {
+  sas::Shape s;
+  if (validate(p, sel_cap, true, &s) != SAS_OK) return 0;
+  g_last_error.clear();
+  return sas::bwd_workspace_layout(s).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+enum BwdStage { kStageDq = 1, kStageDkdv = 2 };
+
+int32_t run_bwd(const char* name, int stages, const sas_problem* p, const sas::BwdPtrs& ptr,
+                int32_t sel_cap, void* workspace, size_t workspace_bytes, void* stream) {
+  sas::Shape s;
+  int32_t rc = validate(p, sel_cap, true, &s);
+  if (rc != SAS_OK) return rc;
+  bool missing = !ptr.q || !ptr.k || !ptr.v || !ptr.d_o || !ptr.lse || !ptr.log_gate ||
+                 !ptr.sel_idx || !ptr.sel_cnt;
+  if (stages & kStageDq) missing = missing || !ptr.o || !ptr.dq || !ptr.dlog_gate;
+  if (stages & kStageDkdv) missing = missing || !ptr.dk || !ptr.dv;
+  if (missing) return fail(SAS_E_INVALID, "%s: a required pointer is NULL", name);
+  const sas::BwdWorkspace wl = sas::bwd_workspace_layout(s);
+  if (workspace == nullptr || workspace_bytes < wl.total)
+    return fail(SAS_E_WORKSPACE, "%s: workspace of %zu bytes given, %zu required", name,
+                workspace == nullptr ? (size_t)0 : workspace_bytes, wl.total);
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(SAS_E_WORKSPACE, "%s: workspace must be 256-byte aligned", name);
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const bool mf = sas::mfma_path(s);
+  hipError_t e = hipSuccess;
+  if (stages & kStageDq)
+    e = mf ? sas::launch_bwd_dq_mfma(s, ptr, ws, wl, st)
+           : sas::launch_bwd_dq_generic(s, ptr, ws, wl, st);
+  if (e == hipSuccess && (stages & kStageDkdv))
+    e = mf ? sas::launch_bwd_dkdv_mfma(s, ptr, ws, wl, st)
+           : sas::launch_bwd_dkdv_generic(s, ptr, ws, wl, st);
+  if (e != hipSuccess) return hip_fail(e, name);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sas_gated_attn_bwd(const sas_problem* p, const void* q, const void* k, const void* v,
+                           const void* o, const void* d_o, const float* lse, const float* log_gate,
+                           const int32_t* sel_idx, const int32_t* sel_cnt, int32_t sel_cap,
+                           void* dq, void* dk, void* dv, float* dlog_gate, float* dscores,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  const sas::BwdPtrs ptr{q, k, v, o, d_o, lse, log_gate, sel_idx, sel_cnt,
+                         dq, dk, dv, dlog_gate, dscores};
+  return run_bwd("sas_gated_attn_bwd", kStageDq | kStageDkdv, p, ptr, sel_cap, workspace,
+                 workspace_bytes, stream);
+}
+
+int32_t sas_gated_attn_bwd_dq(const sas_problem* p, const void* q, const void* k, const void* v,
+                              const void* o, const void* d_o, const float* lse,
+                              const float* log_gate, const int32_t* sel_idx,
+                              const int32_t* sel_cnt, int32_t sel_cap, void* dq, float* dlog_gate,
+                              float* dscores, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  const sas::BwdPtrs ptr{q, k, v, o, d_o, lse, log_gate, sel_idx, sel_cnt,
+                         dq, nullptr, nullptr, dlog_gate, dscores};
+  return run_bwd("sas_gated_attn_bwd_dq", kStageDq, p, ptr, sel_cap, workspace, workspace_bytes,
+                 stream);
+}
+
+int32_t sas_gated_attn_bwd_dkdv(const sas_problem* p, const void* q, const void* k,
+                                const void* v, const void* d_o, const float* lse,
+                                const float* log_gate, const int32_t* sel_idx,
+                                const int32_t* sel_cnt, int32_t sel_cap, void* dk, void* dv,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  const sas::BwdPtrs ptr{q, k, v, nullptr, d_o, lse, log_gate, sel_idx, sel_cnt,
+                         nullptr, dk, dv, nullptr, nullptr};
+  return run_bwd("sas_gated_attn_bwd_dkdv", kStageDkdv, p, ptr, sel_cap, workspace,
+                 workspace_bytes, stream);
+}
+
+}  // extern "C"

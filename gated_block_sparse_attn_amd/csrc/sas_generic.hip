@@ -1,0 +1,371 @@
+// Vector-ALU gated block-sparse attention, forward and backward, for every
+// supported (dtype, head_dim, block) combination.  The bf16 / D = 128 /
+// b = 64 shape normally runs on the matrix-core kernels instead; this path
+// covers fp32 tensors, D = 64 and blocks of 16 or 32 tokens, with the same
+// semantics:
+//
+//  forward  (SAS Sec. 4.3 Eq. 9, App. E Alg. 3): per query block the current
+//           block (causal, bias 0) and the selected historical blocks (bias
+//           log g), streamed tile by tile with an online softmax in base 2;
+//  backward (App. E Alg. 4): Delta = rowsum(O dO), P recomputed from LSE,
+//           dS = P (dP - Delta), dQ = scale dS K, dLogG = block sums of dS
+//           (query-major pass), dK = scale dS^T Q and dV = P^T dO
+//           (key-major pass).
+//
+// One thread owns one query row (forward, dQ pass) or one key row (dK/dV
+// pass); K/V tiles are staged in LDS as fp32.
+#include <math.h>
+
+#include <type_traits>
+
+#include "sas_internal.h"
+
+namespace sas {
+namespace {
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* p) { return (float)(*p); }
+template <typename T>
+__device__ __forceinline__ void st(T* p, float x) { *p = (T)x; }
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+struct GenArgs {
+  const void* q; const void* k; const void* v; const void* o; const void* d_o;
+  const float* lse; const float* lg; const int32_t* sel_idx; const int32_t* sel_cnt;
+  void* out; float* lse_out; void* dq; void* dk; void* dv; float* dlg; float* delta;
+  int Hq, Hkv, G, N, C, cap;
+  int o_fp32;   // o is stored as float32 (else as T)
+  float c2;     // sm_scale * log2(e)
+  float scale;  // sm_scale
+};
+
+// Stage rows [row0, row0 + BLK) of a [N, D] matrix into LDS as fp32.
+template <typename T, int D, int BLK>
+__device__ __forceinline__ void stage_tile(float* dst, const T* src) {
+  for (int e = threadIdx.x; e < BLK * D; e += blockDim.x) dst[e] = ld(src + e);
+}
+
+template <typename T, int D, int BLK>
+__global__ void __launch_bounds__(64) fwd_generic_kernel(GenArgs a) {
+  extern __shared__ float smem[];
+  float* ks = smem;
+  float* vs = smem + BLK * D;
+  const int i = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int bb = bh / a.Hq, h = bh % a.Hq, hk = h / a.G;
+  const int t = threadIdx.x;
+  const bool active = t < BLK;
+  const long long row = ((long long)bb * a.Hkv + hk) * a.C + i;
+  const int cnt = min(a.sel_cnt[row], a.cap);
+  const int32_t* sel = a.sel_idx + row * a.cap;
+  const T* qrow = (const T*)a.q + (((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + t) * D;
+  const T* kbase = (const T*)a.k + ((long long)bb * a.Hkv + hk) * a.N * D;
+  const T* vbase = (const T*)a.v + ((long long)bb * a.Hkv + hk) * a.N * D;
+
+  float q[D], acc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    q[d] = active ? ld(qrow + d) * a.c2 : 0.0f;
+    acc[d] = 0.0f;
+  }
+  float m = -INFINITY, l = 0.0f;
+  for (int tile = 0; tile <= cnt; ++tile) {
+    const int kb = tile == 0 ? i : sel[tile - 1];
+    const float beta = tile == 0 ? 0.0f : a.lg[row * a.C + kb] * kLog2e;
+    __syncthreads();
+    stage_tile<T, D, BLK>(ks, kbase + (long long)kb * BLK * D);
+    stage_tile<T, D, BLK>(vs, vbase + (long long)kb * BLK * D);
+    __syncthreads();
+    if (active) {
+      // per-key online softmax update (this path favours simplicity)
+#pragma unroll 1
+      for (int u = 0; u < BLK; ++u) {
+        if (tile == 0 && u > t) break;   // causal inside the current block
+        float x = beta;
+#pragma unroll
+        for (int d = 0; d < D; ++d) x += q[d] * ks[u * D + d];
+        const float mnew = fmaxf(m, x);
+        const float corr = exp2f(m - mnew);
+        const float p = exp2f(x - mnew);
+        l = l * corr + p;
+#pragma unroll
+        for (int d = 0; d < D; ++d) acc[d] = acc[d] * corr + p * vs[u * D + d];
+        m = mnew;
+      }
+    }
+  }
+  if (active) {
+    const long long qi = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + t;
+    const float inv = 1.0f / l;
+    if (a.o_fp32) {
+      float* orow = (float*)a.out + qi * D;
+#pragma unroll
+      for (int d = 0; d < D; ++d) orow[d] = acc[d] * inv;
+    } else {
+      T* orow = (T*)a.out + qi * D;
+#pragma unroll
+      for (int d = 0; d < D; ++d) st(orow + d, acc[d] * inv);
+    }
+    a.lse_out[qi] = (m + log2f(l)) * kLn2;
+  }
+}
+
+// Query-major backward: Delta, dQ and the block log-gate gradient.
+template <typename T, int D, int BLK>
+__global__ void __launch_bounds__(64) bwd_q_generic_kernel(GenArgs a) {
+  extern __shared__ float smem[];
+  float* ks = smem;
+  float* vs = smem + BLK * D;
+  const int i = blockIdx.x;
+  const int bhk = blockIdx.y;
+  const int bb = bhk / a.Hkv, hk = bhk % a.Hkv;
+  const int t = threadIdx.x;
+  const bool active = t < BLK;
+  const long long row = ((long long)bb * a.Hkv + hk) * a.C + i;
+  const int cnt = min(a.sel_cnt[row], a.cap);
+  const int32_t* sel = a.sel_idx + row * a.cap;
+  const T* kbase = (const T*)a.k + ((long long)bb * a.Hkv + hk) * a.N * D;
+  const T* vbase = (const T*)a.v + ((long long)bb * a.Hkv + hk) * a.N * D;
+  float* dlg_row = a.dlg + row * a.C;
+
+  // The whole dLogG row is owned by this workgroup: clear it, then let lane 0
+  // accumulate the selected entries (one wavefront: a fixed summation order).
+  for (int m = t; m < a.C; m += blockDim.x) dlg_row[m] = 0.0f;
+  __threadfence();
+  __syncthreads();
+
+  for (int hl = 0; hl < a.G; ++hl) {
+    const int h = hk * a.G + hl;
+    const long long qi = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + t;
+    float q[D], dov[D], dq[D];
+    float delta = 0.0f, lse2 = 0.0f;
+    if (active) {
+      const T* qrow = (const T*)a.q + qi * D;
+      const T* drow = (const T*)a.d_o + qi * D;
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        q[d] = ld(qrow + d);
+        dov[d] = ld(drow + d);
+        const float od = a.o_fp32 ? ((const float*)a.o)[qi * D + d] : ld((const T*)a.o + qi * D + d);
+        delta += od * dov[d];
+        dq[d] = 0.0f;
+      }
+      lse2 = a.lse[qi] * kLog2e;
+      a.delta[qi] = delta;
+    } else {
+#pragma unroll
+      for (int d = 0; d < D; ++d) { q[d] = 0.0f; dov[d] = 0.0f; dq[d] = 0.0f; }
+    }
+    for (int tile = 0; tile <= cnt; ++tile) {
+      const int kb = tile == 0 ? i : sel[tile - 1];
+      const float beta = tile == 0 ? 0.0f : a.lg[row * a.C + kb] * kLog2e;
+      __syncthreads();
+      stage_tile<T, D, BLK>(ks, kbase + (long long)kb * BLK * D);
+      stage_tile<T, D, BLK>(vs, vbase + (long long)kb * BLK * D);
+      __syncthreads();
+      float tsum = 0.0f;
+      if (active) {
+#pragma unroll 1
+        for (int u = 0; u < BLK; ++u) {
+          if (tile == 0 && u > t) break;
+          float x = 0.0f, dp = 0.0f;
+#pragma unroll
+          for (int d = 0; d < D; ++d) {
+            x += q[d] * ks[u * D + d];
+            dp += dov[d] * vs[u * D + d];
+          }
+          const float p = exp2f(x * a.c2 + beta - lse2);
+          const float ds = p * (dp - delta);
+          tsum += ds;
+#pragma unroll
+          for (int d = 0; d < D; ++d) dq[d] += ds * ks[u * D + d];
+        }
+      }
+      if (tile > 0) {
+        tsum = wave_sum(tsum);
+        if (t == 0) dlg_row[kb] += tsum;
+      }
+    }
+    if (active) {
+      T* dqrow = (T*)a.dq + qi * D;
+#pragma unroll
+      for (int d = 0; d < D; ++d) st(dqrow + d, dq[d] * a.scale);
+    }
+  }
+}
+
+// Key-major backward: dK and dV of one key block, over every query block that
+// attends it (the diagonal block and each later block that selected it).
+template <typename T, int D, int BLK>
+__global__ void __launch_bounds__(64) bwd_kv_generic_kernel(GenArgs a) {
+  extern __shared__ float smem[];
+  float* ks = smem;
+  float* vs = smem + BLK * D;
+  const int j = blockIdx.x;
+  const int bhk = blockIdx.y;
+  const int bb = bhk / a.Hkv, hk = bhk % a.Hkv;
+  const int u = threadIdx.x;
+  const bool active = u < BLK;
+  const T* kbase = (const T*)a.k + ((long long)bb * a.Hkv + hk) * a.N * D;
+  const T* vbase = (const T*)a.v + ((long long)bb * a.Hkv + hk) * a.N * D;
+  stage_tile<T, D, BLK>(ks, kbase + (long long)j * BLK * D);
+  stage_tile<T, D, BLK>(vs, vbase + (long long)j * BLK * D);
+  __syncthreads();
+  float dk[D], dv[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) { dk[d] = 0.0f; dv[d] = 0.0f; }
+  const long long rowbase = ((long long)bb * a.Hkv + hk) * a.C;
+  for (int i = j; i < a.C; ++i) {
+    float beta = 0.0f;
+    if (i != j) {
+      // is j in the ascending selected list of row i?  (binary search)
+      const int cnt = min(a.sel_cnt[rowbase + i], a.cap);
+      const int32_t* sel = a.sel_idx + (rowbase + i) * a.cap;
+      int lo = 0, hi = cnt;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (sel[mid] < j) lo = mid + 1; else hi = mid;
+      }
+      if (lo >= cnt || sel[lo] != j) continue;
+      beta = a.lg[(rowbase + i) * a.C + j] * kLog2e;
+    }
+    for (int hl = 0; hl < a.G; ++hl) {
+      const int h = hk * a.G + hl;
+      const long long q0 = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK;
+#pragma unroll 1
+      for (int tq = 0; tq < BLK; ++tq) {
+        if (!active || (i == j && u > tq)) continue;
+        const T* qrow = (const T*)a.q + (q0 + tq) * D;
+        const T* drow = (const T*)a.d_o + (q0 + tq) * D;
+        float x = 0.0f, dp = 0.0f;
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+          x += ld(qrow + d) * ks[u * D + d];
+          dp += ld(drow + d) * vs[u * D + d];
+        }
+        const float p = exp2f(x * a.c2 + beta - a.lse[q0 + tq] * kLog2e);
+        const float ds = p * (dp - a.delta[q0 + tq]);
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+          dv[d] += p * ld(drow + d);
+          dk[d] += ds * ld(qrow + d);
+        }
+      }
+    }
+  }
+  if (active) {
+    const long long r = ((long long)bb * a.Hkv + hk) * a.N + (long long)j * BLK + u;
+    T* dkrow = (T*)a.dk + r * D;
+    T* dvrow = (T*)a.dv + r * D;
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      st(dkrow + d, dk[d] * a.scale);
+      st(dvrow + d, dv[d]);
+    }
+  }
+}
+
+GenArgs make_args(const Shape& s) {
+  GenArgs a{};
+  a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.G; a.N = s.N; a.C = s.C; a.cap = s.cap;
+  a.o_fp32 = s.o_fp32;
+  a.c2 = s.scale * kLog2e;
+  a.scale = s.scale;
+  return a;
+}
+
+template <typename T, int D, int BLK>
+hipError_t fwd_launch(const GenArgs& a, const Shape& s, hipStream_t st) {
+  const size_t lds = 2 * BLK * D * sizeof(float);
+  hipLaunchKernelGGL((fwd_generic_kernel<T, D, BLK>), dim3(s.C, s.B * s.Hq), dim3(64), lds, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int BLK>
+hipError_t bwd_q_launch(const GenArgs& a, const Shape& s, hipStream_t st) {
+  const size_t lds = 2 * BLK * D * sizeof(float);
+  hipLaunchKernelGGL((bwd_q_generic_kernel<T, D, BLK>), dim3(s.C, s.B * s.Hkv), dim3(64), lds, st,
+                     a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int BLK>
+hipError_t bwd_kv_launch(const GenArgs& a, const Shape& s, hipStream_t st) {
+  const size_t lds = 2 * BLK * D * sizeof(float);
+  hipLaunchKernelGGL((bwd_kv_generic_kernel<T, D, BLK>), dim3(s.C, s.B * s.Hkv), dim3(64), lds,
+                     st, a);
+  return hipGetLastError();
+}
+
+// Dispatch over (dtype, D, blk).
+template <typename Fn>
+hipError_t dispatch(const Shape& s, Fn&& fn) {
+  if (s.fp32) {
+    if (s.D == 64) {
+      if (s.blk == 16) return fn((float*)nullptr, std::integral_constant<int, 64>{}, std::integral_constant<int, 16>{});
+      if (s.blk == 32) return fn((float*)nullptr, std::integral_constant<int, 64>{}, std::integral_constant<int, 32>{});
+      return fn((float*)nullptr, std::integral_constant<int, 64>{}, std::integral_constant<int, 64>{});
+    }
+    if (s.blk == 16) return fn((float*)nullptr, std::integral_constant<int, 128>{}, std::integral_constant<int, 16>{});
+    if (s.blk == 32) return fn((float*)nullptr, std::integral_constant<int, 128>{}, std::integral_constant<int, 32>{});
+    return fn((float*)nullptr, std::integral_constant<int, 128>{}, std::integral_constant<int, 64>{});
+  }
+  if (s.D == 64) {
+    if (s.blk == 16) return fn((__bf16*)nullptr, std::integral_constant<int, 64>{}, std::integral_constant<int, 16>{});
+    if (s.blk == 32) return fn((__bf16*)nullptr, std::integral_constant<int, 64>{}, std::integral_constant<int, 32>{});
+    return fn((__bf16*)nullptr, std::integral_constant<int, 64>{}, std::integral_constant<int, 64>{});
+  }
+  if (s.blk == 16) return fn((__bf16*)nullptr, std::integral_constant<int, 128>{}, std::integral_constant<int, 16>{});
+  if (s.blk == 32) return fn((__bf16*)nullptr, std::integral_constant<int, 128>{}, std::integral_constant<int, 32>{});
+  return fn((__bf16*)nullptr, std::integral_constant<int, 128>{}, std::integral_constant<int, 64>{});
+}
+
+}  // namespace
+
+hipError_t launch_fwd_generic(const Shape& s, const void* q, const void* k, const void* v,
+                              const float* log_gate, const int32_t* sel_idx,
+                              const int32_t* sel_cnt, void* o, float* lse, hipStream_t st) {
+  GenArgs a = make_args(s);
+  a.q = q; a.k = k; a.v = v; a.lg = log_gate; a.sel_idx = sel_idx; a.sel_cnt = sel_cnt;
+  a.out = o; a.lse_out = lse;
+  return dispatch(s, [&](auto tp, auto dc, auto bc) {
+    using T = std::remove_pointer_t<decltype(tp)>;
+    return fwd_launch<T, decltype(dc)::value, decltype(bc)::value>(a, s, st);
+  });
+}
+
+GenArgs bwd_args(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorkspace& wl) {
+  GenArgs a = make_args(s);
+  a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o; a.d_o = p.d_o; a.lse = p.lse; a.lg = p.log_gate;
+  a.sel_idx = p.sel_idx; a.sel_cnt = p.sel_cnt; a.dq = p.dq; a.dk = p.dk; a.dv = p.dv;
+  a.dlg = p.dlog_gate;
+  a.delta = (float*)(ws + wl.delta);
+  return a;
+}
+
+hipError_t launch_bwd_dq_generic(const Shape& s, const BwdPtrs& p, char* ws,
+                                 const BwdWorkspace& wl, hipStream_t st) {
+  const GenArgs a = bwd_args(s, p, ws, wl);
+  hipError_t e = dispatch(s, [&](auto tp, auto dc, auto bc) {
+    using T = std::remove_pointer_t<decltype(tp)>;
+    return bwd_q_launch<T, decltype(dc)::value, decltype(bc)::value>(a, s, st);
+  });
+  if (e != hipSuccess || p.dscores == nullptr) return e;
+  return launch_dscores(s, p.dlog_gate, p.log_gate, p.dscores, st);
+}
+
+hipError_t launch_bwd_dkdv_generic(const Shape& s, const BwdPtrs& p, char* ws,
+                                   const BwdWorkspace& wl, hipStream_t st) {
+  const GenArgs a = bwd_args(s, p, ws, wl);
+  return dispatch(s, [&](auto tp, auto dc, auto bc) {
+    using T = std::remove_pointer_t<decltype(tp)>;
+    return bwd_kv_launch<T, decltype(dc)::value, decltype(bc)::value>(a, s, st);
+  });
+}
+
+}  // namespace sas

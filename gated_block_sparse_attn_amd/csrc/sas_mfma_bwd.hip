@@ -1,0 +1,777 @@
+// Matrix-core (MFMA) backward of SAS gated block-sparse attention, bf16
+// inputs, fp32 accumulation, block b = 64, head_dim D = 128, on gfx950.
+//
+// Follows the recomputation backward of the SAS paper's App. E (Alg. 4):
+//   Delta = rowsum(O * dO);  P = exp(S - LSE);  dS = P * (dO V^T - Delta);
+//   dQ = scale dS K;  dK = scale dS^T Q;  dV = P^T dO;
+//   dLogG[i, m] = sum of dS over the query tokens of block i (all G heads of
+//                 the kv group) and the key tokens of selected block m;
+// and the selector-score gradient of App. D.3 / Eq. 8.
+//
+// Kernels (in launch order):
+//   bwd_dq_kernel       query-major pass: one workgroup per (batch, kv head,
+//                       query block, chunk of heads); each wavefront owns 64
+//                       query rows of one head and streams the diagonal block
+//                       and the selected blocks.  It computes Delta (from the
+//                       forward output), recomputes S^T = K Q^T and
+//                       dP^T = V dO^T, accumulates dQ^T += K^T dS^T in
+//                       registers and reduces dS of every tile to one block
+//                       log-gate gradient partial (deterministic: fixed lane
+//                       butterfly, fixed wave order).
+//   finalize_kernel     sums the per-head-chunk partials in a fixed order into
+//                       the dense dLogG table and, optionally, applies the
+//                       softmax backward to the selector scores.
+//   column kernels      transpose the selection: bit (j, i) of a column mask is
+//                       set when row i selected block j; each column j then
+//                       gets the ascending list {j} u {i > j : j in I_i} and is
+//                       cut into chunks of at most kColChunk query blocks.
+//   bwd_dkdv_kernel     key-major pass: one workgroup per column chunk; K_j
+//                       and V_j stay in LDS, each wavefront streams (query
+//                       block, head) items, recomputes S = Q K^T and
+//                       dP = dO V^T (keys in the lane dimension), and
+//                       accumulates dV^T += dO^T P and dK^T += Q^T dS, with
+//                       Q^T / dO^T staged transposed in wave-private LDS.  The
+//                       four wavefronts' partial sums are added in a fixed order.
+//   reduce_kernel       columns cut into several chunks: fp32 partials summed
+//                       in chunk order (deterministic).
+#include <math.h>
+
+#include "sas_internal.h"
+
+namespace sas {
+namespace {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int BLK = 64;
+constexpr int HD = 128;
+constexpr int KSTR = HD + 8;   // bf16 per row of a row-major [key][d] LDS tile
+constexpr int TSTR = BLK + 4;  // bf16 per row of a transposed [d][key] LDS tile
+constexpr int XSTR = 32 + 4;   // bf16 per row of a wave's transposed [d][32 queries] tile
+
+struct BwdArgs {
+  const bf16* q; const bf16* k; const bf16* v; const void* o; const bf16* d_o;
+  const float* lse; const float* lg; const int32_t* sel_idx; const int32_t* sel_cnt;
+  bf16* dq; bf16* dk; bf16* dv; float* dlg; float* dsc;
+  float* delta;
+  float* dlg_part;
+  uint32_t* colmask; int32_t* collen; int32_t* coloff; int32_t* chunkoff; int32_t* collist;
+  float* partial;
+  long long ncol;  // B * Hkv * C (rows of the score table == columns)
+  int Hq, Hkv, G, N, C, cap, W, o_fp32;
+  int head_base, nchunk, part_base, nparts;
+  float c2, scale;
+};
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float sum4(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// LDS written by some lanes of this wavefront is read by other lanes of the
+// same wavefront: wait for the LDS queue and keep the compiler from moving
+// memory operations across.
+__device__ __forceinline__ void wave_lds_sync() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+__device__ __forceinline__ bf16x8 join(bf16x4 lo, bf16x4 hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// ---------------------------------------------------------------------------
+// query-major pass: Delta, dQ, block log-gate gradient partials
+// ---------------------------------------------------------------------------
+template <int NW>
+__global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(BwdArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int KUN = 256 / NT;   // (4 keys x 8 d) K units per thread per tile
+  constexpr int VCH = 1024 / NT;  // 16-byte V chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) bf16 s_k[2][BLK * KSTR];
+  __shared__ __attribute__((aligned(16))) bf16 s_kt[2][HD * TSTR];
+  __shared__ __attribute__((aligned(16))) bf16 s_v[2][BLK * KSTR];
+  __shared__ float s_red[2][NW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int l16 = lane & 15;
+  const int g4 = lane >> 4;
+
+  const int unit = xcd_remap(blockIdx.x, gridDim.x);
+  const int chunk = unit % a.nchunk;
+  const int rest = unit / a.nchunk;
+  const int i = rest % a.C;
+  const int bhk = rest / a.C;
+  const int hk = bhk % a.Hkv;
+  const int bb = bhk / a.Hkv;
+  const int h = hk * a.G + a.head_base + chunk * NW + w;
+  const long long row = (long long)bhk * a.C + i;
+  const int cnt = min(a.sel_cnt[row], a.cap);
+  const int32_t* sel = a.sel_idx + row * a.cap;
+  const float* lgrow = a.lg + row * a.C;
+  const bf16* kbase = a.k + (long long)bhk * a.N * HD;
+  const bf16* vbase = a.v + (long long)bhk * a.N * HD;
+  const long long q0 = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK;
+  float* part = a.dlg_part + ((long long)(a.part_base + chunk) * a.ncol + row) * (a.cap + 1);
+
+  // Q^T and dO^T as B operands (lane: query qt*16 + l16, dims ks*32 + g4*8 .. +7)
+  bf16x8 qf[4][4], dof[4][4];
+  float lse2[4], dlt[4];
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) {
+    const long long r = q0 + qt * 16 + l16;
+    float part_d = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int d0 = ks * 32 + g4 * 8;
+      qf[qt][ks] = *(const bf16x8*)(a.q + r * HD + d0);
+      dof[qt][ks] = *(const bf16x8*)(a.d_o + r * HD + d0);
+      if (a.o_fp32) {
+        const f32x4 o0 = *(const f32x4*)((const float*)a.o + r * HD + d0);
+        const f32x4 o1 = *(const f32x4*)((const float*)a.o + r * HD + d0 + 4);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          part_d += o0[x] * (float)dof[qt][ks][x];
+          part_d += o1[x] * (float)dof[qt][ks][x + 4];
+        }
+      } else {
+        const bf16x8 ob = *(const bf16x8*)((const bf16*)a.o + r * HD + d0);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) part_d += (float)ob[x] * (float)dof[qt][ks][x];
+      }
+    }
+    dlt[qt] = sum4(part_d);   // Delta = rowsum(O * dO) over the 4 lanes of the query
+    lse2[qt] = a.lse[r] * kLog2e;
+    if (g4 == 0) a.delta[r] = dlt[qt];
+  }
+
+  u32x4 kreg[KUN][4];
+  u32x4 vreg[VCH];
+  auto gload = [&](int kb) {
+    const bf16* kt = kbase + (long long)kb * BLK * HD;
+    const bf16* vt = vbase + (long long)kb * BLK * HD;
+#pragma unroll
+    for (int r = 0; r < KUN; ++r) {
+      const int u = tid + r * NT;
+      const int kg = u >> 4, dg = u & 15;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) kreg[r][x] = *(const u32x4*)(kt + (kg * 4 + x) * HD + dg * 8);
+    }
+#pragma unroll
+    for (int r = 0; r < VCH; ++r) {
+      const int c = tid + r * NT;
+      vreg[r] = *(const u32x4*)(vt + (c >> 4) * HD + (c & 15) * 8);
+    }
+  };
+  auto lstore = [&](int stg) {
+#pragma unroll
+    for (int r = 0; r < KUN; ++r) {
+      const int u = tid + r * NT;
+      const int kg = u >> 4, dg = u & 15;
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        *(u32x4*)(&s_k[stg][(kg * 4 + x) * KSTR + dg * 8]) = kreg[r][x];
+#pragma unroll
+      for (int z = 0; z < 4; ++z) {
+        const uint32_t w0 = kreg[r][0][z], w1 = kreg[r][1][z];
+        const uint32_t w2 = kreg[r][2][z], w3 = kreg[r][3][z];
+        u32x2 lo, hi;
+        lo[0] = (w0 & 0xffffu) | (w1 << 16);
+        lo[1] = (w2 & 0xffffu) | (w3 << 16);
+        hi[0] = (w0 >> 16) | (w1 & 0xffff0000u);
+        hi[1] = (w2 >> 16) | (w3 & 0xffff0000u);
+        *(u32x2*)(&s_kt[stg][(dg * 8 + 2 * z) * TSTR + kg * 4]) = lo;
+        *(u32x2*)(&s_kt[stg][(dg * 8 + 2 * z + 1) * TSTR + kg * 4]) = hi;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < VCH; ++r) {
+      const int c = tid + r * NT;
+      *(u32x4*)(&s_v[stg][(c >> 4) * KSTR + (c & 15) * 8]) = vreg[r];
+    }
+  };
+
+  f32x4 dqacc[8][4];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) dqacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int ntiles = cnt + 1;
+  gload(i);
+  lstore(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int stg = t & 1;
+    const bool diag = (t == 0);
+    const int kb = diag ? i : sel[t - 1];
+    const float beta = diag ? 0.0f : lgrow[kb] * kLog2e;
+    if (t + 1 < ntiles) gload(sel[t]);
+    const bf16* Ks = s_k[stg];
+    const bf16* Kt = s_kt[stg];
+    const bf16* Vs = s_v[stg];
+
+    float tsum = 0.0f;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {   // two halves of 32 keys
+      f32x4 sacc[2][4], dpacc[2][4];
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) {
+          sacc[k2][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dpacc[k2][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int kt = kh * 2 + k2;
+          const bf16x8 ka = *(const bf16x8*)(Ks + (kt * 16 + l16) * KSTR + ks * 32 + g4 * 8);
+          const bf16x8 va = *(const bf16x8*)(Vs + (kt * 16 + l16) * KSTR + ks * 32 + g4 * 8);
+#pragma unroll
+          for (int qt = 0; qt < 4; ++qt) {
+            sacc[k2][qt] = mfma16(ka, qf[qt][ks], sacc[k2][qt]);
+            dpacc[k2][qt] = mfma16(va, dof[qt][ks], dpacc[k2][qt]);
+          }
+        }
+      }
+      bf16x8 dsb[4];
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) {
+        const int qi = qt * 16 + l16;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int key = (kh * 2 + k2) * 16 + g4 * 4 + j;
+            float p = exp2f(sacc[k2][qt][j] * a.c2 + beta - lse2[qt]);
+            if (diag && key > qi) p = 0.0f;
+            const float ds = p * (dpacc[k2][qt][j] - dlt[qt]);
+            tsum += ds;
+            dsb[qt][k2 * 4 + j] = (bf16)ds;
+          }
+      }
+      // dQ^T += K^T dS^T over these 32 keys
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const bf16* kp = Kt + (dt * 16 + l16) * TSTR + kh * 32 + g4 * 4;
+        const bf16x8 ka = join(*(const bf16x4*)kp, *(const bf16x4*)(kp + 16));
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) dqacc[dt][qt] = mfma16(ka, dsb[qt], dqacc[dt][qt]);
+      }
+    }
+    if (!diag) {
+      tsum = wave_sum(tsum);
+      if (lane == 0) s_red[t & 1][w] = tsum;
+    }
+    // previous tile's partial (its slot was filled before the last barrier)
+    if (tid == 0 && t >= 2) {
+      float s = 0.0f;
+#pragma unroll
+      for (int x = 0; x < NW; ++x) s += s_red[(t - 1) & 1][x];
+      part[t - 1] = s;
+    }
+    if (t + 1 < ntiles) lstore(stg ^ 1);
+    __syncthreads();
+  }
+  if (tid == 0 && ntiles >= 2) {
+    float s = 0.0f;
+#pragma unroll
+    for (int x = 0; x < NW; ++x) s += s_red[(ntiles - 1) & 1][x];
+    part[ntiles - 1] = s;
+  }
+
+  // dQ = scale * dQacc (lane: query qt*16 + l16, dims dt*16 + g4*4 .. +3)
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) {
+    bf16* dp = a.dq + (q0 + qt * 16 + l16) * HD + g4 * 4;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      bf16x4 r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[j] = (bf16)(dqacc[dt][qt][j] * a.scale);
+      *(bf16x4*)(dp + dt * 16) = r;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dLogG table (sum of head-chunk partials) and optional selector-score grad
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int find_sel(const int32_t* sel, int cnt, int m) {
+  int lo = 0, hi = cnt;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (sel[mid] < m) lo = mid + 1; else hi = mid;
+  }
+  return (lo < cnt && sel[lo] == m) ? lo : -1;
+}
+
+__global__ void __launch_bounds__(256) finalize_kernel(BwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.ncol) return;
+  const int i = (int)(row % a.C);
+  const int cnt = min(a.sel_cnt[row], a.cap);
+  const int32_t* sel = a.sel_idx + row * a.cap;
+  float* drow = a.dlg + row * a.C;
+  float tot = 0.0f;
+  for (int m = lane; m < a.C; m += 64) {
+    float val = 0.0f;
+    if (m < i) {
+      const int pos = find_sel(sel, cnt, m);
+      if (pos >= 0) {
+        for (int p = 0; p < a.nparts; ++p)
+          val += a.dlg_part[((long long)p * a.ncol + row) * (a.cap + 1) + pos + 1];
+      }
+    }
+    drow[m] = val;
+    tot += val;
+  }
+  if (a.dsc == nullptr) return;
+  tot = wave_sum(tot);
+  const float* grow = a.lg + row * a.C;
+  float* srow = a.dsc + row * a.C;
+  for (int m = lane; m < a.C; m += 64)
+    srow[m] = (m < i) ? (drow[m] - expf(grow[m]) * tot) : 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// selection transpose: column lists
+// ---------------------------------------------------------------------------
+__global__ void fill_zero_kernel(uint32_t* p, long long n) {
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (long long)gridDim.x * blockDim.x)
+    p[e] = 0u;
+}
+
+__global__ void mark_kernel(BwdArgs a) {
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long row = gid / a.cap;
+  const int t = (int)(gid % a.cap);
+  if (row >= a.ncol) return;
+  const int cnt = min(a.sel_cnt[row], a.cap);
+  if (t >= cnt) return;
+  const int m = a.sel_idx[row * a.cap + t];
+  const int i = (int)(row % a.C);
+  const long long col = row - i + m;  // same (batch, kv head), block m
+  atomicOr(&a.colmask[col * a.W + (i >> 5)], 1u << (i & 31));
+}
+
+__global__ void count_kernel(BwdArgs a) {
+  const long long col = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (col >= a.ncol) return;
+  int L = 1;  // the diagonal block
+  for (int w = 0; w < a.W; ++w) L += __popc(a.colmask[col * a.W + w]);
+  a.collen[col] = L;
+}
+
+// exclusive prefix sums of the column lengths and chunk counts (one workgroup)
+__global__ void __launch_bounds__(1024) scan_kernel(BwdArgs a) {
+  __shared__ int s_len[1024], s_chk[1024];
+  const int t = threadIdx.x;
+  const long long per = (a.ncol + 1023) / 1024;
+  const long long beg = min((long long)t * per, a.ncol);
+  const long long end = min(beg + per, a.ncol);
+  int sl = 0, sc = 0;
+  for (long long c = beg; c < end; ++c) {
+    const int L = a.collen[c];
+    sl += L;
+    sc += (L + kColChunk - 1) / kColChunk;
+  }
+  s_len[t] = sl;
+  s_chk[t] = sc;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {   // Hillis-Steele inclusive scan
+    const int xl = t >= off ? s_len[t - off] : 0;
+    const int xc = t >= off ? s_chk[t - off] : 0;
+    __syncthreads();
+    s_len[t] += xl;
+    s_chk[t] += xc;
+    __syncthreads();
+  }
+  int ol = s_len[t] - sl, oc = s_chk[t] - sc;
+  for (long long c = beg; c < end; ++c) {
+    const int L = a.collen[c];
+    a.coloff[c] = ol;
+    a.chunkoff[c] = oc;
+    ol += L;
+    oc += (L + kColChunk - 1) / kColChunk;
+  }
+  if (t == 1023) {
+    a.coloff[a.ncol] = s_len[1023];
+    a.chunkoff[a.ncol] = s_chk[1023];
+  }
+}
+
+__global__ void __launch_bounds__(256) fill_lists_kernel(BwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const long long col = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (col >= a.ncol) return;
+  const int j = (int)(col % a.C);
+  int32_t* out = a.collist + a.coloff[col];
+  if (lane == 0) out[0] = j;
+  int run = 1;
+  for (int w0 = 0; w0 < a.W; w0 += 64) {
+    const int wi = w0 + lane;
+    uint32_t bits = wi < a.W ? a.colmask[col * a.W + wi] : 0u;
+    const int c = __popc(bits);
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    int pos = run + incl - c;
+    while (bits) {
+      const int b = __builtin_ctz(bits);
+      out[pos++] = wi * 32 + b;
+      bits &= bits - 1u;
+    }
+    run += __shfl(incl, 63, 64);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// key-major pass: dK, dV
+// ---------------------------------------------------------------------------
+constexpr int KV_TILE_BYTES = BLK * KSTR * 2;              // 17408
+constexpr int XT_BYTES = HD * XSTR * 2;                      // 9216 per transposed tile
+constexpr int DKDV_LDS = 2 * KV_TILE_BYTES + 4 * 2 * XT_BYTES;  // 108544
+static_assert(DKDV_LDS >= 2 * 64 * 128 * 4, "reduction buffer must fit");
+
+__global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[DKDV_LDS];
+  bf16* Ks = (bf16*)smem;
+  bf16* Vs = (bf16*)(smem + KV_TILE_BYTES);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int l16 = lane & 15;
+  const int g4 = lane >> 4;
+  bf16* xo = (bf16*)(smem + 2 * KV_TILE_BYTES + (2 * w) * XT_BYTES);
+  bf16* xq = (bf16*)(smem + 2 * KV_TILE_BYTES + (2 * w + 1) * XT_BYTES);
+
+  const int g = xcd_remap(blockIdx.x, gridDim.x);
+  const int total = a.chunkoff[a.ncol];
+  if (g >= total) return;
+  long long lo = 0, hi = a.ncol;   // chunkoff[lo] <= g < chunkoff[hi]
+  while (hi - lo > 1) {
+    const long long mid = (lo + hi) >> 1;
+    if (a.chunkoff[mid] <= g) lo = mid; else hi = mid;
+  }
+  const long long col = lo;
+  const int c = g - a.chunkoff[col];
+  const int nch = a.chunkoff[col + 1] - a.chunkoff[col];
+  const int L = a.collen[col];
+  const int e0 = c * kColChunk;
+  const int e1 = min(L, e0 + kColChunk);
+  const int32_t* list = a.collist + a.coloff[col];
+  const int j = (int)(col % a.C);
+  const long long bhk = col / a.C;
+  const int hk = (int)(bhk % a.Hkv);
+  const int bb = (int)(bhk / a.Hkv);
+
+  {  // stage K_j, V_j (row-major)
+    const bf16* kt = a.k + (bhk * a.N + (long long)j * BLK) * HD;
+    const bf16* vt = a.v + (bhk * a.N + (long long)j * BLK) * HD;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int cc = tid + r * 256;
+      *(u32x4*)(&Ks[(cc >> 4) * KSTR + (cc & 15) * 8]) = *(const u32x4*)(kt + (cc >> 4) * HD + (cc & 15) * 8);
+      *(u32x4*)(&Vs[(cc >> 4) * KSTR + (cc & 15) * 8]) = *(const u32x4*)(vt + (cc >> 4) * HD + (cc & 15) * 8);
+    }
+  }
+  __syncthreads();
+
+  f32x4 dkacc[8][4], dvacc[8][4];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      dkacc[dt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dvacc[dt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  const int nitems = (e1 - e0) * a.G;
+  for (int it = w; it < nitems; it += 4) {
+    const int ent = e0 + it / a.G;
+    const int hl = it % a.G;
+    const int i = list[ent];
+    const int h = hk * a.G + hl;
+    const bool diag = (i == j);
+    const float beta = diag ? 0.0f : a.lg[(bhk * a.C + i) * a.C + j] * kLog2e;
+    const long long q0 = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK;
+#pragma unroll 1
+    for (int hq = 0; hq < 2; ++hq) {   // two halves of 32 query rows
+      bf16x8 qf[2][4], dof[2][4];
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const long long r = q0 + hq * 32 + q2 * 16 + l16;
+          qf[q2][ks] = *(const bf16x8*)(a.q + r * HD + ks * 32 + g4 * 8);
+          dof[q2][ks] = *(const bf16x8*)(a.d_o + r * HD + ks * 32 + g4 * 8);
+        }
+      f32x4 lsev[2], dlv[2];
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const long long r = q0 + hq * 32 + q2 * 16 + g4 * 4;
+        lsev[q2] = *(const f32x4*)(a.lse + r);
+        dlv[q2] = *(const f32x4*)(a.delta + r);
+      }
+      // S = Q K^T, dP = dO V^T   (lane: key kt*16 + l16; queries q2*16 + g4*4 + j)
+      f32x4 sacc[2][4], dpacc[2][4];
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          sacc[q2][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dpacc[q2][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const bf16x8 kb = *(const bf16x8*)(Ks + (kt * 16 + l16) * KSTR + ks * 32 + g4 * 8);
+          const bf16x8 vb = *(const bf16x8*)(Vs + (kt * 16 + l16) * KSTR + ks * 32 + g4 * 8);
+#pragma unroll
+          for (int q2 = 0; q2 < 2; ++q2) {
+            sacc[q2][kt] = mfma16(qf[q2][ks], kb, sacc[q2][kt]);
+            dpacc[q2][kt] = mfma16(dof[q2][ks], vb, dpacc[q2][kt]);
+          }
+        }
+      // stage dO^T and Q^T of these 32 rows in the wave's LDS tiles
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const int d = ks * 32 + g4 * 8 + x;
+            xo[d * XSTR + q2 * 16 + l16] = dof[q2][ks][x];
+            xq[d * XSTR + q2 * 16 + l16] = qf[q2][ks][x];
+          }
+      // P and dS as B operands (lane: key; queries x/4*16 + g4*4 + x%4)
+      bf16x8 pb[4], dsb[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const int key = kt * 16 + l16;
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int qi = hq * 32 + q2 * 16 + g4 * 4 + jj;
+            float p = exp2f(sacc[q2][kt][jj] * a.c2 + beta - lsev[q2][jj] * kLog2e);
+            if (diag && key > qi) p = 0.0f;
+            const float ds = p * (dpacc[q2][kt][jj] - dlv[q2][jj]);
+            pb[kt][q2 * 4 + jj] = (bf16)p;
+            dsb[kt][q2 * 4 + jj] = (bf16)ds;
+          }
+      }
+      wave_lds_sync();
+      // dV^T += dO^T P, dK^T += Q^T dS
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const bf16* op = xo + (dt * 16 + l16) * XSTR + g4 * 4;
+        const bf16* qp = xq + (dt * 16 + l16) * XSTR + g4 * 4;
+        const bf16x8 oa = join(*(const bf16x4*)op, *(const bf16x4*)(op + 16));
+        const bf16x8 qa = join(*(const bf16x4*)qp, *(const bf16x4*)(qp + 16));
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          dvacc[dt][kt] = mfma16(oa, pb[kt], dvacc[dt][kt]);
+          dkacc[dt][kt] = mfma16(qa, dsb[kt], dkacc[dt][kt]);
+        }
+      }
+      wave_lds_sync();
+    }
+  }
+
+  // add the four wavefronts' partial sums in a fixed order (LDS, fp32)
+  __syncthreads();
+  float* redk = (float*)smem;
+  float* redv = redk + 64 * 128;
+  for (int x = 0; x < 4; ++x) {
+    if (w == x) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const int off = (kt * 16 + l16) * 128 + dt * 16 + g4 * 4;
+          if (x == 0) {
+            *(f32x4*)(redk + off) = dkacc[dt][kt];
+            *(f32x4*)(redv + off) = dvacc[dt][kt];
+          } else {
+            *(f32x4*)(redk + off) += dkacc[dt][kt];
+            *(f32x4*)(redv + off) += dvacc[dt][kt];
+          }
+        }
+    }
+    __syncthreads();
+  }
+  const long long orow = bhk * a.N + (long long)j * BLK;
+  if (nch == 1) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = (tid + r * 256) * 8;   // 8 consecutive elements
+      bf16x8 ok, ov;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        ok[x] = (bf16)(redk[e + x] * a.scale);
+        ov[x] = (bf16)redv[e + x];
+      }
+      *(bf16x8*)(a.dk + orow * HD + e) = ok;
+      *(bf16x8*)(a.dv + orow * HD + e) = ov;
+    }
+  } else {
+    float* pk = a.partial + (long long)g * 2 * 8192;
+    float* pv = pk + 8192;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int e = (tid + r * 256) * 4;
+      *(f32x4*)(pk + e) = *(const f32x4*)(redk + e);
+      *(f32x4*)(pv + e) = *(const f32x4*)(redv + e);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) reduce_kernel(BwdArgs a) {
+  const long long col = blockIdx.x;
+  const int c0 = a.chunkoff[col];
+  const int nch = a.chunkoff[col + 1] - c0;
+  if (nch <= 1) return;
+  const int j = (int)(col % a.C);
+  const long long bhk = col / a.C;
+  const long long orow = bhk * a.N + (long long)j * BLK;
+  for (int r = 0; r < 4; ++r) {
+    const int e = (threadIdx.x + r * 256) * 8;
+    float sk[8], sv[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) { sk[x] = 0.0f; sv[x] = 0.0f; }
+    for (int cc = 0; cc < nch; ++cc) {
+      const float* pk = a.partial + (long long)(c0 + cc) * 2 * 8192 + e;
+      const float* pv = pk + 8192;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) { sk[x] += pk[x]; sv[x] += pv[x]; }
+    }
+    bf16x8 ok, ov;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      ok[x] = (bf16)(sk[x] * a.scale);
+      ov[x] = (bf16)sv[x];
+    }
+    *(bf16x8*)(a.dk + orow * HD + e) = ok;
+    *(bf16x8*)(a.dv + orow * HD + e) = ov;
+  }
+}
+
+template <int NW>
+hipError_t launch_dq(BwdArgs a, int head_base, int nchunk, int part_base, long long units,
+                     hipStream_t st) {
+  a.head_base = head_base;
+  a.nchunk = nchunk;
+  a.part_base = part_base;
+  hipLaunchKernelGGL((bwd_dq_kernel<NW>), dim3((unsigned)(units * nchunk)), dim3(NW * 64), 0, st,
+                     a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int bwd_head_parts(int G) { return G / 4 + (G % 4) / 2 + (G % 2); }
+
+namespace {
+BwdArgs make_bwd_args(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorkspace& wl) {
+  BwdArgs a{};
+  a.q = (const bf16*)p.q; a.k = (const bf16*)p.k; a.v = (const bf16*)p.v; a.o = p.o;
+  a.d_o = (const bf16*)p.d_o; a.lse = p.lse; a.lg = p.log_gate; a.sel_idx = p.sel_idx;
+  a.sel_cnt = p.sel_cnt; a.dq = (bf16*)p.dq; a.dk = (bf16*)p.dk; a.dv = (bf16*)p.dv;
+  a.dlg = p.dlog_gate; a.dsc = p.dscores;
+  a.delta = (float*)(ws + wl.delta);
+  a.dlg_part = (float*)(ws + wl.dlg_part);
+  a.colmask = (uint32_t*)(ws + wl.colmask);
+  a.collen = (int32_t*)(ws + wl.collen);
+  a.coloff = (int32_t*)(ws + wl.coloff);
+  a.chunkoff = (int32_t*)(ws + wl.chunkoff);
+  a.collist = (int32_t*)(ws + wl.collist);
+  a.partial = (float*)(ws + wl.partial);
+  a.ncol = (long long)s.B * s.Hkv * s.C;
+  a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.G; a.N = s.N; a.C = s.C; a.cap = s.cap; a.W = wl.words;
+  a.o_fp32 = s.o_fp32;
+  a.nparts = bwd_head_parts(s.G);
+  a.c2 = s.scale * kLog2e;
+  a.scale = s.scale;
+  return a;
+}
+}  // namespace
+
+hipError_t launch_bwd_dq_mfma(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorkspace& wl,
+                              hipStream_t st) {
+  BwdArgs a = make_bwd_args(s, p, ws, wl);
+  const long long units = a.ncol;
+  hipError_t e;
+  // query-major pass (heads in chunks of 4, 2, 1)
+  int h = 0, part = 0;
+  if (s.G / 4 > 0) {
+    e = launch_dq<4>(a, h, s.G / 4, part, units, st);
+    if (e != hipSuccess) return e;
+    part += s.G / 4;
+    h += 4 * (s.G / 4);
+  }
+  if ((s.G - h) / 2 > 0) {
+    e = launch_dq<2>(a, h, 1, part, units, st);
+    if (e != hipSuccess) return e;
+    part += 1;
+    h += 2;
+  }
+  if (s.G - h > 0) {
+    e = launch_dq<1>(a, h, 1, part, units, st);
+    if (e != hipSuccess) return e;
+  }
+  // dLogG table and selector-score gradient
+  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((a.ncol + 3) / 4)), dim3(256), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // selection transpose for the key-major stage
+  const long long nmask = a.ncol * a.W;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)min((nmask + 255) / 256, 65535LL)),
+                     dim3(256), 0, st, a.colmask, nmask);
+  const long long nmark = a.ncol * s.cap;
+  hipLaunchKernelGGL(mark_kernel, dim3((unsigned)((nmark + 255) / 256)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(count_kernel, dim3((unsigned)((a.ncol + 255) / 256)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, a);
+  hipLaunchKernelGGL(fill_lists_kernel, dim3((unsigned)((a.ncol + 3) / 4)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv_mfma(const Shape& s, const BwdPtrs& p, char* ws,
+                                const BwdWorkspace& wl, hipStream_t st) {
+  BwdArgs a = make_bwd_args(s, p, ws, wl);
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)wl.max_chunks), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)a.ncol), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace sas

@@ -1,0 +1,191 @@
+// Gate activation, Top-K threshold and selector-score gradient kernels.
+//
+// SAS paper (arXiv 2609.13141): Sec. 4.1 Eq. 4 (current block keeps a unit
+// gate), Sec. 4.2.2 Eq. 6 (log g_m = s_m - LSE(s) over the historical blocks),
+// Sec. 4.3 Alg. 1 and App. E (Top-K realised as a per-query threshold on the
+// gate, no sort), App. D.3 and Eq. 8 (softmax backward to the scores under
+// the sparse scope).
+//
+// One wavefront owns one row (b, h_kv, i) of the [C, C] score table: the
+// row's historical scores (m < i) are staged in LDS once and every pass
+// (max, sum, log-gate write, radix select, compaction) reads them from there.
+// Both kernels are HBM-bound: they read and write the score-table rows once.
+#include <math.h>
+
+#include "../../include/sas.h"
+#include "sas_internal.h"
+
+namespace sas {
+namespace {
+
+__device__ __forceinline__ float wave_max_f(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum_f(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ double wave_sum_d(double x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// Order-preserving map of fp32 bit patterns to unsigned integers:
+// a < b (as finite floats, -0 canonicalised to +0)  <=>  key(a) < key(b).
+__device__ __forceinline__ uint32_t f2key(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return b ^ ((b >> 31) ? 0xFFFFFFFFu : 0x80000000u);
+}
+__device__ __forceinline__ float key2f(uint32_t k) {
+  return __uint_as_float(k ^ ((k >> 31) ? 0x80000000u : 0xFFFFFFFFu));
+}
+
+__device__ __forceinline__ int popc64(unsigned long long m) { return __popcll(m); }
+
+// lanes below the current one whose bit is set in mask
+__device__ __forceinline__ int rank_below(unsigned long long mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__global__ void __launch_bounds__(256) threshold_kernel(const float* __restrict__ scores,
+                                                        float* __restrict__ log_gate,
+                                                        float* __restrict__ tau,
+                                                        int32_t* __restrict__ sel_idx,
+                                                        int32_t* __restrict__ sel_cnt,
+                                                        int32_t* __restrict__ d_status,
+                                                        long long rows, int C, int K, int cap) {
+  extern __shared__ float s_hist[];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const long long row = (long long)blockIdx.x * nw + w;
+  if (row >= rows) return;  // whole wavefront leaves; no workgroup barrier follows
+  const int i = (int)(row % C);
+  const float* srow = scores + row * (long long)C;
+  float* s = s_hist + (size_t)w * C;
+
+  // Stage the historical scores; +0.0f turns -0 into +0 so that the integer
+  // keys order exactly like the fp32 comparison used for the selected set.
+  float mx = -INFINITY;
+  for (int m = lane; m < i; m += 64) {
+    const float x = srow[m] + 0.0f;
+    s[m] = x;
+    mx = fmaxf(mx, x);
+  }
+  mx = wave_max_f(mx);
+
+  // LSE over the historical blocks (Eq. 6): fp32 exponentials of values <= 0,
+  // accumulated in fp64 so the normaliser does not drift with long rows.
+  double lse = 0.0;
+  if (i > 0) {
+    double acc = 0.0;
+    for (int m = lane; m < i; m += 64) acc += (double)expf(s[m] - mx);
+    acc = wave_sum_d(acc);
+    lse = (double)mx + log(acc);
+  }
+
+  // log_gate row: s - LSE for historical blocks, 0 for the current block
+  // (unit gate, Eq. 4), -inf above the diagonal.
+  float* lrow = log_gate + row * (long long)C;
+  for (int m = lane; m < C; m += 64) {
+    float val;
+    if (m < i) val = (float)((double)s[m] - lse);
+    else if (m == i) val = 0.0f;
+    else val = -INFINITY;
+    lrow[m] = val;
+  }
+
+  // Threshold: the K-th largest historical score, found bit by bit from the
+  // most significant end (radix select, no sort): keep the largest key T with
+  // #{key >= T} >= K.
+  float t;
+  if (K >= i) {
+    t = -INFINITY;
+  } else if (K == 0) {
+    t = INFINITY;
+  } else {
+    uint32_t prefix = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = prefix | (1u << bit);
+      int cnt = 0;
+      for (int m0 = 0; m0 < i; m0 += 64) {
+        const int m = m0 + lane;
+        const bool p = (m < i) && (f2key(s[m < i ? m : 0]) >= cand);
+        cnt += popc64(__ballot(p));
+      }
+      if (cnt >= K) prefix = cand;
+    }
+    t = key2f(prefix);
+  }
+
+  // Compact {m < i : s_m >= t} in ascending order.
+  int32_t* out = sel_idx + row * (long long)cap;
+  int base = 0;
+  for (int m0 = 0; m0 < i; m0 += 64) {
+    const int m = m0 + lane;
+    const bool p = (m < i) && (s[m < i ? m : 0] >= t);
+    const unsigned long long mask = __ballot(p);
+    if (p) {
+      const int pos = base + rank_below(mask);
+      if (pos < cap) out[pos] = m;
+    }
+    base += popc64(mask);
+  }
+  for (int pos = base + lane; pos < cap; pos += 64) out[pos] = -1;
+  if (lane == 0) {
+    sel_cnt[row] = base;
+    tau[row] = t;
+    if (base > cap && d_status != nullptr) *d_status = SAS_E_CAPACITY;
+  }
+}
+
+// dscores[i, m] = dLogG[i, m] - g[i, m] * sum_{l < i} dLogG[i, l] for m < i, else 0.
+// This is App. D.3's ds_m = g_m (dg_m - sum_l g_l dg_l) with dLogG = g * dg,
+// and dg = 0 on unselected blocks (sparse scope, Eq. 8).
+__global__ void __launch_bounds__(256) dscores_kernel(const float* __restrict__ dlg,
+                                                      const float* __restrict__ lg,
+                                                      float* __restrict__ ds, long long rows,
+                                                      int C) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int i = (int)(row % C);
+  const float* drow = dlg + row * (long long)C;
+  const float* grow = lg + row * (long long)C;
+  float tot = 0.0f;
+  for (int m = lane; m < i; m += 64) tot += drow[m];
+  tot = wave_sum_f(tot);
+  float* orow = ds + row * (long long)C;
+  for (int m = lane; m < C; m += 64)
+    orow[m] = (m < i) ? (drow[m] - expf(grow[m]) * tot) : 0.0f;
+}
+
+}  // namespace
+
+hipError_t launch_threshold(const Shape& s, const float* scores, float* log_gate, float* tau,
+                            int32_t* sel_idx, int32_t* sel_cnt, int32_t* d_status,
+                            hipStream_t st) {
+  const long long rows = (long long)s.B * s.Hkv * s.C;
+  const int nw = (s.C <= 4096) ? 4 : 1;
+  const size_t lds = (size_t)nw * s.C * sizeof(float);
+  const long long grid = (rows + nw - 1) / nw;
+  hipLaunchKernelGGL(threshold_kernel, dim3((unsigned)grid), dim3(64 * nw), lds, st, scores,
+                     log_gate, tau, sel_idx, sel_cnt, d_status, rows, s.C, s.K, s.cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_dscores(const Shape& s, const float* dlog_gate, const float* log_gate,
+                          float* dscores, hipStream_t st) {
+  const long long rows = (long long)s.B * s.Hkv * s.C;
+  const long long grid = (rows + 3) / 4;
+  hipLaunchKernelGGL(dscores_kernel, dim3((unsigned)grid), dim3(256), 0, st, dlog_gate, log_gate,
+                     dscores, rows, s.C);
+  return hipGetLastError();
+}
+
+}  // namespace sas

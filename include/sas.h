@@ -1,0 +1,232 @@
+/*
+ * sas.h -- C ABI of the MI355X (gfx950) gated block-sparse attention library.
+ *
+ * The library computes the training-time attention of SAS ("SAS: Simple
+ * Attention Sparsification via End-to-End Optimization of Context Ranking",
+ * arXiv 2609.13141): per query block, the always-kept current block (unit
+ * gate, causal) plus the Top-K historical blocks chosen from selector scores,
+ * each historical block carrying its softmax-normalised log gate inside the
+ * attention softmax (Sec. 4.3, Eq. 9), and the matching backward pass
+ * including the block log-gate gradient (App. E) and the selector-score
+ * gradient (App. D.3).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor arguments are DEVICE pointers owned by the caller.  The
+ *    library never allocates, frees or retains device memory; scratch space
+ *    is passed in explicitly (sas_gated_attn_bwd).
+ *  - Every call validates its arguments on the host and, when they are
+ *    valid, enqueues its kernels on `stream` (a hipStream_t; NULL = the
+ *    default stream) and returns without synchronising.  Argument errors are
+ *    reported BEFORE anything is enqueued; nothing is written then.
+ *  - Return value: SAS_OK (0) or a negative sas_status.  sas_last_error()
+ *    returns a thread-local message describing the last non-OK return.
+ *  - No exceptions cross the ABI.  There is no global mutable state other
+ *    than that thread-local message.
+ *  - Outputs are overwritten, never accumulated: every element of every
+ *    output buffer is written.
+ *
+ * Shapes and layouts (all contiguous, row-major, element strides implied):
+ *    B  = batch, Hq = query heads, Hkv = kv heads (Hq % Hkv == 0, G = Hq/Hkv),
+ *    N  = seq_len, D = head_dim, b = block_size (N % b == 0), C = N / b.
+ *    q, d_o, dq           [B, Hq,  N, D]   (dtype: bf16 or fp32)
+ *    o                    [B, Hq,  N, D]   (o_dtype: bf16 or fp32)
+ *    k, v, dk, dv         [B, Hkv, N, D]   (dtype: bf16 or fp32)
+ *    lse                  [B, Hq,  N]      fp32, natural-log LSE of each query row
+ *    scores, log_gate,
+ *    dlog_gate, dscores   [B, Hkv, C, C]   fp32, row = query block i,
+ *                                          column = context block m
+ *    tau, sel_cnt         [B, Hkv, C]      fp32 / int32
+ *    sel_idx              [B, Hkv, C, sel_cap] int32
+ *  Query head h reads kv head h / G.  Gates, threshold and selection are
+ *  shared by the G query heads of a kv group and by the b queries of a query
+ *  block (the per-query-group block selection of the paper's grouped-query
+ *  setting); the gradient of a shared gate is the sum over its uses.
+ *
+ * Supported problem sizes: D in {64, 128}; b in {16, 32, 64}; C <= 8192;
+ * K >= 0.  bf16 with D = 128 and b = 64 runs on the matrix-core (MFMA) path;
+ * every other supported combination runs on a plain vector-ALU HIP path with
+ * identical semantics.
+ */
+#ifndef SAS_H_
+#define SAS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAS_ABI_VERSION 1
+
+typedef enum sas_dtype {
+  SAS_BF16 = 0, /* q/k/v/o/d_o/dq/dk/dv are bfloat16 (fp32 accumulation) */
+  SAS_FP32 = 1  /* all tensors float32 */
+} sas_dtype;
+
+typedef enum sas_status {
+  SAS_OK = 0,
+  SAS_E_INVALID = -1,     /* malformed argument (null pointer, bad shape ...) */
+  SAS_E_UNSUPPORTED = -2, /* well-formed but outside the supported sizes      */
+  SAS_E_WORKSPACE = -3,   /* workspace missing or smaller than required       */
+  SAS_E_CAPACITY = -4,    /* device-side: a row selected more than sel_cap    */
+  SAS_E_HIP = -5          /* a HIP runtime call or kernel launch failed       */
+} sas_status;
+
+typedef struct sas_problem {
+  int32_t batch;      /* B   >= 1                                            */
+  int32_t n_q_heads;  /* Hq  >= 1                                            */
+  int32_t n_kv_heads; /* Hkv >= 1, divides Hq                                */
+  int32_t seq_len;    /* N   >= b, multiple of block_size                    */
+  int32_t head_dim;   /* D   in {64, 128}                                    */
+  int32_t block_size; /* b   in {16, 32, 64}                                 */
+  int32_t budget_k;   /* K   >= 0: historical blocks kept per query block    */
+  int32_t dtype;      /* a sas_dtype                                          */
+  int32_t o_dtype;    /* sas_dtype of the forward output o (and of the o read
+                         by the backward).  SAS_FP32 keeps o unrounded, so the
+                         backward's Delta = rowsum(o * dO) carries no bf16
+                         rounding; SAS_BF16 is the usual half-size output.
+                         Must be SAS_FP32 when dtype is SAS_FP32.            */
+  float sm_scale;     /* scale of q.k; <= 0 selects 1/sqrt(D).  It never
+                         multiplies the log gate (App. E, Alg. 3/4).          */
+} sas_problem;
+
+/* ABI version of the loaded library (SAS_ABI_VERSION). */
+int32_t sas_abi_version(void);
+
+/* Thread-local description of the last non-OK status returned on this thread
+ * ("" if none).  The pointer stays valid until the next library call on the
+ * same thread. */
+const char* sas_last_error(void);
+
+/*
+ * sas_gate_threshold -- gate activation and Top-K as a threshold.
+ *
+ * Defined by Sec. 4.1 Eq. 4 (current block has unit gate), Sec. 4.2.2 Eq. 6
+ * (softmax gate: log g_m = s_m - LSE(s) over the historical blocks),
+ * Sec. 4.3 Alg. 1 (I = Top-K) and App. E (Top-K encoded as a per-query
+ * threshold: a block is active when it reaches the threshold).
+ *
+ * For every row (b, h_kv, i):
+ *   log_gate[.., i, m] = s[i, m] - LSE_{m' < i} s[i, m']   for m < i,
+ *                        0                                 for m = i,
+ *                        -inf                              for m > i;
+ *   tau[.., i]  = the K-th largest of {s[i, m] : m < i} if 1 <= K < i,
+ *                 -inf if K >= i (every historical block kept),
+ *                 +inf if K == 0 and i >= 1 (none kept);
+ *   I_i = {m < i : s[i, m] >= tau_i}, compared in fp32 (ties at tau are
+ *   all kept, so |I_i| can exceed K only through exact ties);
+ *   sel_idx[.., i, 0 .. cnt-1] = I_i in ascending order, remaining slots -1;
+ *   sel_cnt[.., i] = |I_i| (the true count, even if it exceeds sel_cap).
+ * The threshold is found by a most-significant-bit-first radix select on
+ * order-preserving integer keys of the fp32 scores (no sort).
+ *
+ * Inputs : scores  fp32 [B,Hkv,C,C]; entries m >= i are never read; the
+ *          entries m < i must be finite.
+ * Outputs: log_gate fp32 [B,Hkv,C,C], tau fp32 [B,Hkv,C],
+ *          sel_idx int32 [B,Hkv,C,sel_cap], sel_cnt int32 [B,Hkv,C].
+ * sel_cap: >= min(K, C-1); sel_cap = C-1 can never overflow.
+ * d_status: optional device int32; when non-NULL it is set to
+ *          SAS_E_CAPACITY by any row whose |I_i| exceeds sel_cap (it is
+ *          never cleared by the library; the caller zeroes it).
+ */
+int32_t sas_gate_threshold(const sas_problem* p, const float* scores, float* log_gate, float* tau,
+                           int32_t* sel_idx, int32_t* sel_cnt, int32_t sel_cap, int32_t* d_status,
+                           void* stream);
+
+/*
+ * sas_gated_attn_fwd -- gated block-sparse attention forward.
+ *
+ * Defined by Sec. 4.3 Eq. 9 and the App. E forward (Alg. 3): for query token t
+ * of block i and query head h, the attended keys are the tokens u <= t of
+ * block i (bias 0) and every token of each selected block m in I_i
+ * (bias log_gate[i, m]):
+ *   z_u = sm_scale * q_t . k_u + bias_u,  o_t = sum_u softmax(z)_u v_u,
+ *   lse_t = log sum_u exp(z_u).
+ * Unselected blocks are skipped entirely, never materialised.
+ *
+ * Inputs : q, k, v (dtype), log_gate fp32 (only entries m in I_i are read),
+ *          sel_idx / sel_cnt as written by sas_gate_threshold (the first
+ *          min(sel_cnt, sel_cap) entries of each row are used; they must be
+ *          ascending block indices < i).
+ * Outputs: o (o_dtype) [B,Hq,N,D], lse fp32 [B,Hq,N].
+ */
+int32_t sas_gated_attn_fwd(const sas_problem* p, const void* q, const void* k, const void* v,
+                           const float* log_gate, const int32_t* sel_idx, const int32_t* sel_cnt,
+                           int32_t sel_cap, void* o, float* lse, void* stream);
+
+/* Bytes of device workspace sas_gated_attn_bwd needs for problem p and the
+ * given sel_cap (0 if p or sel_cap is invalid; then sas_last_error says why). */
+size_t sas_gated_attn_bwd_workspace_size(const sas_problem* p, int32_t sel_cap);
+
+/*
+ * sas_gated_attn_bwd -- gated block-sparse attention backward.
+ *
+ * Defined by the App. E backward (Alg. 4): Delta = rowsum(O * dO); P is
+ * recomputed from lse; dS = P * (dO V^T - Delta);
+ *   dq = sm_scale dS K,  dk = sm_scale dS^T Q,  dv = P^T dO
+ * (dk, dv summed over the G query heads of each kv head);
+ *   dlog_gate[i, m] = sum of dS over the query tokens of block i (all G heads)
+ *                     and the key tokens of block m, for m in I_i; 0 elsewhere
+ *                     (unselected, diagonal and upper-triangle entries);
+ * and, if dscores != NULL, the selector-score gradient of App. D.3 with the
+ * sparse-scope rule of Eq. 8:
+ *   dscores[i, m] = dlog_gate[i, m] - exp(log_gate[i, m]) * sum_{l<i} dlog_gate[i, l]
+ *   for m < i; 0 for m >= i.
+ *
+ * Inputs : q, k, v, d_o (dtype), o (o_dtype), lse from the forward, log_gate (all
+ *          entries m < i are read when dscores != NULL), sel_idx, sel_cnt.
+ * Outputs: dq, dk, dv (dtype), dlog_gate fp32 [B,Hkv,C,C], dscores fp32
+ *          [B,Hkv,C,C] or NULL.
+ * workspace: device memory of at least
+ *          sas_gated_attn_bwd_workspace_size(p, sel_cap) bytes, 256-byte
+ *          aligned, owned by the caller, not preserved across calls; calls
+ *          that share a workspace must not overlap in time.
+ * The dq, dlog_gate and dscores results are bitwise deterministic; so are dk
+ * and dv (split partial sums are reduced in a fixed order).
+ */
+int32_t sas_gated_attn_bwd(const sas_problem* p, const void* q, const void* k, const void* v,
+                           const void* o, const void* d_o, const float* lse, const float* log_gate,
+                           const int32_t* sel_idx, const int32_t* sel_cnt, int32_t sel_cap,
+                           void* dq, void* dk, void* dv, float* dlog_gate, float* dscores,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two stages of sas_gated_attn_bwd, for callers that schedule (or time)
+ * them separately.  Calling sas_gated_attn_bwd_dq and then
+ * sas_gated_attn_bwd_dkdv on the same stream with the same workspace is
+ * exactly sas_gated_attn_bwd.
+ *
+ * sas_gated_attn_bwd_dq -- the query-major stage (App. E backward, first pass
+ * of Alg. 4): Delta = rowsum(o * dO) (kept in the workspace), dq, dlog_gate
+ * and, if dscores != NULL, the selector-score gradient (App. D.3).  It also
+ * records, in the workspace, which query blocks attend each key block (the
+ * transpose of the selection) for the key-major stage.
+ */
+int32_t sas_gated_attn_bwd_dq(const sas_problem* p, const void* q, const void* k, const void* v,
+                              const void* o, const void* d_o, const float* lse,
+                              const float* log_gate, const int32_t* sel_idx,
+                              const int32_t* sel_cnt, int32_t sel_cap, void* dq, float* dlog_gate,
+                              float* dscores, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * sas_gated_attn_bwd_dkdv -- the key-major stage (second pass of Alg. 4):
+ * dk = sm_scale dS^T Q and dv = P^T dO for every key block, summed over the
+ * diagonal query block and every query block that selected it, and over the
+ * G heads of the kv group.  It reads Delta and the selection transpose that
+ * sas_gated_attn_bwd_dq left in `workspace`; it must follow that call, on the
+ * same stream, with the same workspace, problem, inputs and selection.
+ */
+int32_t sas_gated_attn_bwd_dkdv(const sas_problem* p, const void* q, const void* k,
+                                const void* v, const void* d_o, const float* lse,
+                                const float* log_gate, const int32_t* sel_idx,
+                                const int32_t* sel_cnt, int32_t sel_cap, void* dk, void* dv,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAS_H_ */

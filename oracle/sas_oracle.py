@@ -155,6 +155,11 @@ def _attended_keys(i: int, block: int, sel_row: np.ndarray, log_gate_row: np.nda
     return keys, bias, kblk, mask
 
 
+def _f64(x) -> np.ndarray:
+    """Exact upcast of a slice (inputs are bf16/fp32 values held in any float array)."""
+    return np.asarray(x, dtype=np.float64)
+
+
 def _softmax_rows(z: np.ndarray):
     mx = np.max(z, axis=1, keepdims=True)
     e = np.exp(z - mx)
@@ -174,28 +179,25 @@ def forward(q, k, v, log_gate, sel, block: int, sm_scale: float | None = None,
 
     q: [B, Hq, N, D]; k, v: [B, Hkv, N, D]; log_gate/sel: [B, Hkv, C, C].
     ``query_blocks``: optional iterable of (b, h_kv, i) to evaluate (others
-    are left NaN), so large shapes can be sampled.
+    are left 0), so large shapes can be sampled.
     Returns (o [B, Hq, N, D], lse [B, Hq, N]) in float64.
     """
-    q = np.asarray(q, np.float64)
-    k = np.asarray(k, np.float64)
-    v = np.asarray(v, np.float64)
     bsz, hq, n, d = q.shape
     hkv = k.shape[1]
     g = hq // hkv
     scale = default_scale(d, sm_scale)
     c = n // block
-    o = np.full(q.shape, np.nan)
-    lse = np.full((bsz, hq, n), np.nan)
+    o = np.zeros(q.shape)          # calloc: untouched pages cost nothing
+    lse = np.zeros((bsz, hq, n))
     units = query_blocks if query_blocks is not None else \
         [(b, h, i) for b in range(bsz) for h in range(hkv) for i in range(c)]
     for (b, hk, i) in units:
         keys, bias, _, mask = _attended_keys(i, block, sel[b, hk, i], log_gate[b, hk, i])
-        kk = k[b, hk, keys]
-        vv = v[b, hk, keys]
+        kk = _f64(k[b, hk, keys])
+        vv = _f64(v[b, hk, keys])
         rows = slice(i * block, (i + 1) * block)
         for hh in range(hk * g, (hk + 1) * g):
-            z = scale * (q[b, hh, rows] @ kk.T) + bias[None, :]
+            z = scale * (_f64(q[b, hh, rows]) @ kk.T) + bias[None, :]
             z = np.where(mask, z, NEG_INF)
             p, l = _softmax_rows(z)
             o[b, hh, rows] = p @ vv
@@ -219,30 +221,26 @@ def backward(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = No
     and dLogG rows are exact; dK/dV hold only their contributions).
     Returns (dq, dk, dv, dlog_gate) in float64.
     """
-    q = np.asarray(q, np.float64)
-    k = np.asarray(k, np.float64)
-    v = np.asarray(v, np.float64)
-    do = np.asarray(do, np.float64)
     bsz, hq, n, d = q.shape
     hkv = k.shape[1]
     g = hq // hkv
     scale = default_scale(d, sm_scale)
     c = n // block
-    dq = np.zeros_like(q)
-    dk = np.zeros_like(k)
-    dv = np.zeros_like(v)
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
     dlg = np.zeros((bsz, hkv, c, c))
     units = query_blocks if query_blocks is not None else \
         [(b, h, i) for b in range(bsz) for h in range(hkv) for i in range(c)]
     for (b, hk, i) in units:
         keys, bias, kblk, mask = _attended_keys(i, block, sel[b, hk, i], log_gate[b, hk, i])
-        kk = k[b, hk, keys]
-        vv = v[b, hk, keys]
+        kk = _f64(k[b, hk, keys])
+        vv = _f64(v[b, hk, keys])
         rows = slice(i * block, (i + 1) * block)
         ds_sum = np.zeros(keys.shape[0])
         for hh in range(hk * g, (hk + 1) * g):
-            qq = q[b, hh, rows]
-            dd = do[b, hh, rows]
+            qq = _f64(q[b, hh, rows])
+            dd = _f64(do[b, hh, rows])
             z = scale * (qq @ kk.T) + bias[None, :]
             z = np.where(mask, z, NEG_INF)
             p, _ = _softmax_rows(z)

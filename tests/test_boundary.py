@@ -1,0 +1,124 @@
+"""Host-side tests of the C ABI: the library loads, exports every symbol the
+header declares, and rejects malformed or unsupported arguments before any
+launch (these calls never reach the GPU, so they run on a CPU-only host)."""
+
+import ctypes
+
+import pytest
+import torch
+
+from gated_block_sparse_attn_amd import _native as nat
+from gated_block_sparse_attn_amd import api
+
+FAKE = 0x1000  # never dereferenced: validation fails before any launch
+
+
+def lib():
+    return nat.lib()
+
+
+def prob(**kw):
+    base = dict(batch=1, n_q_heads=8, n_kv_heads=2, seq_len=1024, head_dim=128, block_size=64,
+                budget_k=4, dtype=nat.SAS_BF16, o_dtype=nat.SAS_FP32, sm_scale=0.0)
+    base.update(kw)
+    return nat.SasProblem(**base)
+
+
+def fwd(p, cap=4, **ptrs):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, lg=FAKE, si=FAKE, sc=FAKE, o=FAKE, lse=FAKE)
+    a.update(ptrs)
+    return lib().sas_gated_attn_fwd(ctypes.byref(p) if p is not None else None, a["q"], a["k"],
+                                    a["v"], a["lg"], a["si"], a["sc"], cap, a["o"], a["lse"],
+                                    None)
+
+
+def thr(p, cap=4, **ptrs):
+    a = dict(s=FAKE, lg=FAKE, tau=FAKE, si=FAKE, sc=FAKE)
+    a.update(ptrs)
+    return lib().sas_gate_threshold(ctypes.byref(p), a["s"], a["lg"], a["tau"], a["si"], a["sc"],
+                                    cap, None, None)
+
+
+def bwd(p, cap=4, ws=FAKE * 256, ws_bytes=1 << 40, **ptrs):
+    a = {n: FAKE for n in ("q", "k", "v", "o", "do", "lse", "lg", "si", "sc", "dq", "dk", "dv",
+                           "dlg")}
+    a.update(ptrs)
+    return lib().sas_gated_attn_bwd(ctypes.byref(p), a["q"], a["k"], a["v"], a["o"], a["do"],
+                                    a["lse"], a["lg"], a["si"], a["sc"], cap, a["dq"], a["dk"],
+                                    a["dv"], a["dlg"], None, ws, ws_bytes, None)
+
+
+def test_library_exports_every_header_symbol():
+    names = nat.header_symbols()
+    assert {"sas_gate_threshold", "sas_gated_attn_fwd", "sas_gated_attn_bwd",
+            "sas_gated_attn_bwd_workspace_size", "sas_last_error", "sas_abi_version"} <= set(names)
+    handle = ctypes.CDLL(nat.LIB_PATH)
+    for n in names:
+        assert hasattr(handle, n), n
+
+
+def test_abi_version():
+    assert lib().sas_abi_version() == 1
+    assert api.abi_version() == 1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), nat.SAS_E_INVALID),
+    (dict(n_q_heads=6, n_kv_heads=4), nat.SAS_E_INVALID),
+    (dict(budget_k=-1), nat.SAS_E_INVALID),
+    (dict(dtype=7), nat.SAS_E_INVALID),
+    (dict(o_dtype=3), nat.SAS_E_INVALID),
+    (dict(dtype=nat.SAS_FP32, o_dtype=nat.SAS_BF16), nat.SAS_E_INVALID),
+    (dict(sm_scale=float("nan")), nat.SAS_E_INVALID),
+    (dict(head_dim=96), nat.SAS_E_UNSUPPORTED),
+    (dict(block_size=128, seq_len=1024), nat.SAS_E_UNSUPPORTED),
+    (dict(seq_len=1000), nat.SAS_E_UNSUPPORTED),          # ragged last block
+    (dict(seq_len=64 * 8193), nat.SAS_E_UNSUPPORTED),     # too many blocks
+])
+def test_invalid_problems_rejected_by_every_entry_point(kw, code):
+    p = prob(**kw)
+    assert thr(p) == code
+    assert lib().sas_last_error()
+    assert fwd(p) == code
+    assert bwd(p) == code
+    assert lib().sas_gated_attn_bwd_workspace_size(ctypes.byref(p), 4) == 0
+
+
+def test_null_problem_and_null_pointers():
+    assert fwd(None) == nat.SAS_E_INVALID
+    p = prob()
+    assert fwd(p, q=None) == nat.SAS_E_INVALID
+    assert fwd(p, lse=None) == nat.SAS_E_INVALID
+    assert thr(p, s=None) == nat.SAS_E_INVALID
+    assert bwd(p, dlg=None) == nat.SAS_E_INVALID
+    assert b"NULL" in lib().sas_last_error()
+
+
+def test_selection_capacity_must_hold_the_budget():
+    p = prob(budget_k=8)               # C = 16 -> need cap >= min(8, 15) = 8
+    assert thr(p, cap=7) == nat.SAS_E_INVALID
+    assert fwd(p, cap=0) == nat.SAS_E_INVALID
+    assert bwd(p, cap=3) == nat.SAS_E_INVALID
+    p = prob(budget_k=100)             # K >= C: every historical block, cap >= C - 1 = 15
+    assert thr(p, cap=14) == nat.SAS_E_INVALID
+
+
+def test_workspace_size_and_shortfall():
+    p = prob()
+    n = lib().sas_gated_attn_bwd_workspace_size(ctypes.byref(p), 4)
+    assert n > 0 and n % 256 == 0
+    # grows with the selection capacity
+    assert lib().sas_gated_attn_bwd_workspace_size(ctypes.byref(p), 15) > n
+    assert bwd(p, ws_bytes=n - 1) == nat.SAS_E_WORKSPACE
+    assert bwd(p, ws=None) == nat.SAS_E_WORKSPACE
+    assert bwd(p, ws=FAKE * 256 + 8, ws_bytes=n) == nat.SAS_E_WORKSPACE   # misaligned
+    # fp32 / generic shapes need only the Delta buffer
+    p32 = prob(dtype=nat.SAS_FP32, o_dtype=nat.SAS_FP32)
+    assert 0 < lib().sas_gated_attn_bwd_workspace_size(ctypes.byref(p32), 4) < n
+
+
+def test_python_binding_rejects_host_tensors_before_calling():
+    p = api.Problem(1, 2, 1, 128, 64, 16, 2, "fp32")
+    s = torch.zeros(1, 1, 8, 8)
+    with pytest.raises(ValueError, match="device tensor"):
+        api.gate_threshold(p, s)

@@ -1,0 +1,150 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Selected sets, counts, thresholds and zero patterns are compared exactly;
+floating-point outputs within rtol = atol = 2e-2 (bf16) or 1e-5 (fp32), and
+also within that fraction of each tensor's largest magnitude.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from gated_block_sparse_attn_amd import api, workloads
+
+from parity import check_selection, full_parity, log, problem_of, run_gpu, sampled_parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------
+# small shapes: whole-tensor parity (several tiles, every path)
+# --------------------------------------------------------------------------
+
+SMALL = [
+    # name, B, Hq, Hkv, N, D, blk, K, dtype, qkv_std
+    ("tiny_fp32_cfg", 1, 1, 1, 256, 64, 16, 4, "fp32", 1.0),
+    ("mfma_g4", 1, 8, 2, 1024, 128, 64, 4, "bf16", 1.0),
+    ("mfma_g4_scaled", 2, 4, 1, 768, 128, 64, 3, "bf16", 128 ** -0.5),
+    ("mfma_g5", 1, 10, 2, 640, 128, 64, 3, "bf16", 1.0),
+    ("mfma_g1", 1, 2, 2, 512, 128, 64, 2, "bf16", 1.0),
+    ("mfma_g2", 1, 4, 2, 512, 128, 64, 5, "bf16", 1.0),
+    ("mfma_k0", 1, 4, 1, 512, 128, 64, 0, "bf16", 1.0),
+    ("mfma_kall", 1, 4, 1, 512, 128, 64, 20, "bf16", 1.0),
+    ("mfma_one_block", 1, 4, 1, 64, 128, 64, 4, "bf16", 1.0),
+    ("generic_bf16_d64_b16", 1, 4, 2, 256, 64, 16, 3, "bf16", 1.0),
+    ("generic_bf16_d128_b32", 1, 2, 1, 256, 128, 32, 2, "bf16", 1.0),
+    ("generic_fp32_d128_b64", 1, 2, 1, 384, 128, 64, 2, "fp32", 1.0),
+    ("generic_fp32_d64_b32", 2, 3, 1, 256, 64, 32, 3, "fp32", 1.0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_shapes_full_parity(case):
+    name, B, Hq, Hkv, N, D, blk, K, dt, std = case
+    log(f"case {name}")
+    w = workloads.custom(B, Hq, Hkv, N, D, blk, K, dtype=dt, seed=zlib.crc32(name.encode()) % 1000,
+                         qkv_std=std, score_std=2.0)
+    cap = max(1, min(K, N // blk - 1))
+    full_parity(w, K, cap=cap)
+
+
+def test_tiny_fp32_workload():
+    w = workloads.WORKLOADS["tiny_fp32"]
+    log("workload tiny_fp32")
+    full_parity(w, w.budgets[0])
+
+
+# --------------------------------------------------------------------------
+# threshold edge cases
+# --------------------------------------------------------------------------
+
+def test_threshold_ties_and_capacity_flag():
+    C, blk = 8, 16
+    p = api.Problem(1, 1, 1, C * blk, 64, blk, 2, "fp32")
+    s = torch.randn(1, 1, C, C, generator=torch.Generator().manual_seed(0))
+    s[0, 0, 5, :5] = torch.tensor([1.0, 2.0, 2.0, 2.0, 0.5])   # three-way tie at tau
+    s[0, 0, 6, :6] = torch.tensor([-0.0, 0.0, -1.0, 3.0, 0.0, -2.0])  # signed zeros tie
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lg, tau, idx, cnt = api.gate_threshold(p, s.cuda(), sel_cap=2, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == -4                      # SAS_E_CAPACITY
+    assert int(cnt[0, 0, 5]) == 3 and float(tau[0, 0, 5]) == 2.0
+    assert idx[0, 0, 5].tolist() == [1, 2]               # capped, ascending
+    assert int(cnt[0, 0, 6]) == 4                         # 3.0 and the three zeros
+    # with room for every tie: exact sets, flag untouched
+    status.zero_()
+    gpu = {}
+    gpu["log_gate"], gpu["tau"], gpu["sel_idx"], gpu["sel_cnt"] = (
+        t.cpu() for t in api.gate_threshold(p, s.cuda(), sel_cap=C - 1, status=status))
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    check_selection(gpu, s.numpy(), 2)
+
+
+def test_threshold_matches_oracle_on_long_rows():
+    # 2048 blocks per row (the 128k-token shape) with Gumbel scores
+    w = workloads.custom(1, 4, 2, 2048 * 16, 64, 16, 32, dtype="fp32", seed=11,
+                         score_kind="gumbel")
+    p = problem_of(w, 32)
+    g = torch.Generator().manual_seed(5)
+    u = torch.rand(1, 2, 2048, 2048, generator=g).clamp_(1e-30, 1 - 2 ** -24)
+    s = -torch.log(-torch.log(u))
+    gpu = {}
+    gpu["log_gate"], gpu["tau"], gpu["sel_idx"], gpu["sel_cnt"] = (
+        t.cpu() for t in api.gate_threshold(p, s.cuda(), sel_cap=32))
+    check_selection(gpu, s.numpy(), 32)
+
+
+# --------------------------------------------------------------------------
+# determinism (bitwise run-to-run)
+# --------------------------------------------------------------------------
+
+def test_bitwise_deterministic():
+    w = workloads.custom(1, 8, 2, 2048, 128, 64, 6, dtype="bf16", seed=21, score_std=2.0)
+    p = problem_of(w, 6)
+    inp = workloads.generate(w)
+    a = run_gpu(p, inp)
+    b = run_gpu(p, inp)
+    bits = {torch.bfloat16: torch.int16, torch.float32: torch.int32, torch.int32: torch.int32}
+    for n in a:
+        assert torch.equal(a[n].view(bits[a[n].dtype]), b[n].view(bits[b[n].dtype])), n
+
+
+# --------------------------------------------------------------------------
+# the named workloads at full size (sampled oracle)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["qwen3_4b_8k", "qwen3_8b_32k"])
+def test_named_workload_sampled(name):
+    w = workloads.WORKLOADS[name]
+    log(f"workload {name}")
+    sampled_parity(w, w.budgets[0])
+
+
+def test_qwen3_14b_budget_sweep_sampled():
+    w = workloads.WORKLOADS["qwen3_14b_16k"]
+    inp = workloads.generate(w)
+    prev = None
+    for K in w.budgets:
+        log(f"workload {w.name} K={K}")
+        gpu = sampled_parity(w, K, n_units=6, n_kv_blocks=3, inp=inp)
+        cnt = gpu["sel_cnt"].numpy()
+        if prev is not None:
+            assert np.all(cnt >= prev)          # sets grow with the budget
+        prev = cnt
+
+
+def test_long_context_sampled():
+    w = workloads.WORKLOADS["qwen3_8b_128k"]
+    log(f"workload {w.name}")
+    sampled_parity(w, w.budgets[0], n_units=6, n_kv_blocks=3)
