@@ -114,6 +114,9 @@ BwdWorkspace bwd_workspace_layout(const Shape& s) {
     w.collist = off;  off = align256(off + sizeof(int32_t) * (size_t)(emax + nrow));
     w.max_chunks = (emax + nrow + kColChunk - 1) / kColChunk + nrow;
     w.partial = off;  off = align256(off + sizeof(float) * 2 * 64 * 128 * (size_t)w.max_chunks);
+    w.chunk_rank = off;  off = align256(off + sizeof(int32_t) * (size_t)w.max_chunks);
+    w.chunk_hist = off;  off = align256(off + sizeof(int32_t) * (size_t)(nrow + 1));
+    w.chunk_order = off; off = align256(off + sizeof(int32_t) * (size_t)w.max_chunks);
   }
   w.total = off;
   return w;

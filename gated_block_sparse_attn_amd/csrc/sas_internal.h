@@ -36,6 +36,9 @@ struct BwdWorkspace {
   size_t chunkoff;   // int32  [B*Hkv*C + 1]         prefix of ceil(collen / CH)
   size_t collist;    // int32  [B*Hkv*C*(cap+1)]     column lists, diagonal first
   size_t partial;    // float  [max_chunks * 2 * 64 * 128]  split dK/dV partial sums
+  size_t chunk_rank; // int32  [max_chunks]           rank of a chunk inside its order bucket
+  size_t chunk_hist; // int32  [B*Hkv*C + 1]         chunks per (batch, kv head, first row)
+  size_t chunk_order;// int32  [max_chunks]           chunk ids sorted by that key
   size_t total;
   long long max_chunks;
   int words;         // W = ceil(C / 32)

@@ -36,6 +36,8 @@
 //                       in chunk order (deterministic).
 #include <math.h>
 
+#include <type_traits>
+
 #include "sas_internal.h"
 
 namespace sas {
@@ -51,7 +53,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int BLK = 64;
 constexpr int HD = 128;
 constexpr int KSTR = HD + 8;   // bf16 per row of a row-major [key][d] LDS tile
-constexpr int TSTR = BLK + 4;  // bf16 per row of a transposed [d][key] LDS tile
 constexpr int XSTR = 32 + 4;   // bf16 per row of a wave's transposed [d][32 queries] tile
 
 struct BwdArgs {
@@ -62,6 +63,7 @@ struct BwdArgs {
   float* dlg_part;
   uint32_t* colmask; int32_t* collen; int32_t* coloff; int32_t* chunkoff; int32_t* collist;
   float* partial;
+  int32_t* chunk_rank; int32_t* chunk_hist; int32_t* chunk_order;
   long long ncol;  // B * Hkv * C (rows of the score table == columns)
   int Hq, Hkv, G, N, C, cap, W, o_fp32;
   int head_base, nchunk, part_base, nparts;
@@ -96,17 +98,58 @@ __device__ __forceinline__ bf16x8 join(bf16x4 lo, bf16x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// gfx950 transposed LDS read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane u receives element u % 4 of the 8-byte chunks addressed by lanes
+// u / 4 + 4x (x = 0..3).  With lane u addressing row base + u / 4, columns
+// c0 + 4 (u % 4) .. +3 of a row-major tile, lane u therefore gets rows
+// base .. base + 3 of column c0 + u: a column fragment of the tile.
+__device__ __forceinline__ bf16x4 ds_read_tr(const bf16* p) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
 // ---------------------------------------------------------------------------
 // query-major pass: Delta, dQ, block log-gate gradient partials
 // ---------------------------------------------------------------------------
+constexpr int TILE = BLK * HD;   // bf16 elements of one 64 x 128 tile
+
+// LDS tiles are row-major with 256-byte rows and no padding; the 16-byte chunk
+// c of row r sits in slot c ^ (r & 15), so the 16 rows read by a lane group
+// for one chunk land in 16 different slots (all banks).
+__device__ __forceinline__ int swz(int r, int c) { return r * HD + ((c ^ (r & 15)) << 3); }
+
+// Asynchronous global -> LDS copy of one 64 x 128 tile by NW wavefronts
+// (global_load_lds_dwordx4); completion is awaited with s_waitcnt vmcnt(0).
 template <int NW>
-__global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(BwdArgs a) {
-  constexpr int NT = NW * 64;
-  constexpr int KUN = 256 / NT;   // (4 keys x 8 d) K units per thread per tile
-  constexpr int VCH = 1024 / NT;  // 16-byte V chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) bf16 s_k[2][BLK * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16 s_kt[2][HD * TSTR];
-  __shared__ __attribute__((aligned(16))) bf16 s_v[2][BLK * KSTR];
+__device__ __forceinline__ void tile_to_lds(bf16* lds, const bf16* g, int w, int lane) {
+  typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+  for (int r = 0; r < 16 / NW; ++r) {
+    const int seg = w + NW * r;               // 1 KB segment = rows 4 seg .. 4 seg + 3
+    const int row = seg * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ (row & 15);
+    __builtin_amdgcn_global_load_lds(g + row * HD + c * 8, (lds_void*)(lds + seg * 512), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_vm() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// A column fragment (8 rows r0 + {g4*4 .. +3, 16 + g4*4 .. +3} of column
+// c0 + l16) of a swizzled row-major tile, via two transposed reads.
+__device__ __forceinline__ bf16x8 col_frag(const bf16* t, int r0, int c0, int l16, int g4) {
+  const int r = r0 + g4 * 4 + (l16 >> 2);
+  const int c = (c0 >> 3) + ((l16 >> 1) & 1);
+  const int e = (c0 & 7) + (l16 & 1) * 4;
+  return join(ds_read_tr(t + swz(r, c) + e), ds_read_tr(t + swz(r + 16, c) + e));
+}
+
+// One workgroup = NH query heads of one (batch, kv head, query block); two
+// wavefronts per head, each owning 32 of the 64 query rows.
+template <int NH>
+__global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
+  constexpr int NW = 2 * NH;
+  __shared__ __attribute__((aligned(16))) bf16 s_k[2][TILE];
+  __shared__ __attribute__((aligned(16))) bf16 s_v[2][TILE];
   __shared__ float s_red[2][NW];
 
   const int tid = threadIdx.x;
@@ -114,6 +157,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(BwdArgs a) {
   const int w = tid >> 6;
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
+  const int half = w & 1;
 
   const int unit = xcd_remap(blockIdx.x, gridDim.x);
   const int chunk = unit % a.nchunk;
@@ -122,21 +166,28 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(BwdArgs a) {
   const int bhk = rest / a.C;
   const int hk = bhk % a.Hkv;
   const int bb = bhk / a.Hkv;
-  const int h = hk * a.G + a.head_base + chunk * NW + w;
+  const int h = hk * a.G + a.head_base + chunk * NH + (w >> 1);
   const long long row = (long long)bhk * a.C + i;
   const int cnt = min(a.sel_cnt[row], a.cap);
   const int32_t* sel = a.sel_idx + row * a.cap;
   const float* lgrow = a.lg + row * a.C;
   const bf16* kbase = a.k + (long long)bhk * a.N * HD;
   const bf16* vbase = a.v + (long long)bhk * a.N * HD;
-  const long long q0 = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK;
+  const long long q0 = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + half * 32;
   float* part = a.dlg_part + ((long long)(a.part_base + chunk) * a.ncol + row) * (a.cap + 1);
 
-  // Q^T and dO^T as B operands (lane: query qt*16 + l16, dims ks*32 + g4*8 .. +7)
-  bf16x8 qf[4][4], dof[4][4];
-  float lse2[4], dlt[4];
+  auto load_tile = [&](int kb, int stg) {
+    tile_to_lds<NW>(s_k[stg], kbase + (long long)kb * TILE, w, lane);
+    tile_to_lds<NW>(s_v[stg], vbase + (long long)kb * TILE, w, lane);
+  };
+  const int ntiles = cnt + 1;
+  load_tile(i, 0);
+
+  // Q^T and dO^T as B operands (lane: row qt*16 + l16, dims ks*32 + g4*8 .. +7)
+  bf16x8 qf[2][4], dof[2][4];
+  float lse2[2], dlt[2];
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
+  for (int qt = 0; qt < 2; ++qt) {
     const long long r = q0 + qt * 16 + l16;
     float part_d = 0.0f;
 #pragma unroll
@@ -158,86 +209,31 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(BwdArgs a) {
         for (int x = 0; x < 8; ++x) part_d += (float)ob[x] * (float)dof[qt][ks][x];
       }
     }
-    dlt[qt] = sum4(part_d);   // Delta = rowsum(O * dO) over the 4 lanes of the query
+    dlt[qt] = sum4(part_d);   // Delta = rowsum(O * dO) over the 4 lanes of the row
     lse2[qt] = a.lse[r] * kLog2e;
     if (g4 == 0) a.delta[r] = dlt[qt];
   }
 
-  u32x4 kreg[KUN][4];
-  u32x4 vreg[VCH];
-  auto gload = [&](int kb) {
-    const bf16* kt = kbase + (long long)kb * BLK * HD;
-    const bf16* vt = vbase + (long long)kb * BLK * HD;
-#pragma unroll
-    for (int r = 0; r < KUN; ++r) {
-      const int u = tid + r * NT;
-      const int kg = u >> 4, dg = u & 15;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) kreg[r][x] = *(const u32x4*)(kt + (kg * 4 + x) * HD + dg * 8);
-    }
-#pragma unroll
-    for (int r = 0; r < VCH; ++r) {
-      const int c = tid + r * NT;
-      vreg[r] = *(const u32x4*)(vt + (c >> 4) * HD + (c & 15) * 8);
-    }
-  };
-  auto lstore = [&](int stg) {
-#pragma unroll
-    for (int r = 0; r < KUN; ++r) {
-      const int u = tid + r * NT;
-      const int kg = u >> 4, dg = u & 15;
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-        *(u32x4*)(&s_k[stg][(kg * 4 + x) * KSTR + dg * 8]) = kreg[r][x];
-#pragma unroll
-      for (int z = 0; z < 4; ++z) {
-        const uint32_t w0 = kreg[r][0][z], w1 = kreg[r][1][z];
-        const uint32_t w2 = kreg[r][2][z], w3 = kreg[r][3][z];
-        u32x2 lo, hi;
-        lo[0] = (w0 & 0xffffu) | (w1 << 16);
-        lo[1] = (w2 & 0xffffu) | (w3 << 16);
-        hi[0] = (w0 >> 16) | (w1 & 0xffff0000u);
-        hi[1] = (w2 >> 16) | (w3 & 0xffff0000u);
-        *(u32x2*)(&s_kt[stg][(dg * 8 + 2 * z) * TSTR + kg * 4]) = lo;
-        *(u32x2*)(&s_kt[stg][(dg * 8 + 2 * z + 1) * TSTR + kg * 4]) = hi;
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < VCH; ++r) {
-      const int c = tid + r * NT;
-      *(u32x4*)(&s_v[stg][(c >> 4) * KSTR + (c & 15) * 8]) = vreg[r];
-    }
-  };
-
-  f32x4 dqacc[8][4];
+  f32x4 dqacc[8][2];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) dqacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int qt = 0; qt < 2; ++qt) dqacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int ntiles = cnt + 1;
-  gload(i);
-  lstore(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int stg = t & 1;
-    const bool diag = (t == 0);
-    const int kb = diag ? i : sel[t - 1];
-    const float beta = diag ? 0.0f : lgrow[kb] * kLog2e;
-    if (t + 1 < ntiles) gload(sel[t]);
+  // One 64-key tile: recompute S^T and dP^T, form dS, accumulate dQ^T and the
+  // tile's dS sum.
+  auto tile = [&](auto diag_tag, int stg, float beta) -> float {
+    constexpr bool DIAG = decltype(diag_tag)::value;
     const bf16* Ks = s_k[stg];
-    const bf16* Kt = s_kt[stg];
     const bf16* Vs = s_v[stg];
-
     float tsum = 0.0f;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {   // two halves of 32 keys
-      f32x4 sacc[2][4], dpacc[2][4];
+      f32x4 sacc[2][2], dpacc[2][2];
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-        for (int qt = 0; qt < 4; ++qt) {
+        for (int qt = 0; qt < 2; ++qt) {
           sacc[k2][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
           dpacc[k2][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
@@ -245,65 +241,75 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_kernel(BwdArgs a) {
       for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-          const int kt = kh * 2 + k2;
-          const bf16x8 ka = *(const bf16x8*)(Ks + (kt * 16 + l16) * KSTR + ks * 32 + g4 * 8);
-          const bf16x8 va = *(const bf16x8*)(Vs + (kt * 16 + l16) * KSTR + ks * 32 + g4 * 8);
+          const int kr = (kh * 2 + k2) * 16 + l16;
+          const bf16x8 ka = *(const bf16x8*)(Ks + swz(kr, ks * 4 + g4));
+          const bf16x8 va = *(const bf16x8*)(Vs + swz(kr, ks * 4 + g4));
 #pragma unroll
-          for (int qt = 0; qt < 4; ++qt) {
+          for (int qt = 0; qt < 2; ++qt) {
             sacc[k2][qt] = mfma16(ka, qf[qt][ks], sacc[k2][qt]);
             dpacc[k2][qt] = mfma16(va, dof[qt][ks], dpacc[k2][qt]);
           }
         }
       }
-      bf16x8 dsb[4];
+      bf16x8 dsb[2];
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt) {
-        const int qi = qt * 16 + l16;
+      for (int qt = 0; qt < 2; ++qt) {
+        const float off = beta - lse2[qt];
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int key = (kh * 2 + k2) * 16 + g4 * 4 + j;
-            float p = exp2f(sacc[k2][qt][j] * a.c2 + beta - lse2[qt]);
-            if (diag && key > qi) p = 0.0f;
+            float p = __builtin_amdgcn_exp2f(fmaf(sacc[k2][qt][j], a.c2, off));
+            if (DIAG && ((kh * 2 + k2) * 16 + g4 * 4 + j > half * 32 + qt * 16 + l16)) p = 0.0f;
             const float ds = p * (dpacc[k2][qt][j] - dlt[qt]);
-            tsum += ds;
+            if (!DIAG) tsum += ds;
             dsb[qt][k2 * 4 + j] = (bf16)ds;
           }
       }
-      // dQ^T += K^T dS^T over these 32 keys
+      // dQ^T += K^T dS^T over these 32 keys (K^T fragments: transposed reads)
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const bf16* kp = Kt + (dt * 16 + l16) * TSTR + kh * 32 + g4 * 4;
-        const bf16x8 ka = join(*(const bf16x4*)kp, *(const bf16x4*)(kp + 16));
+        const bf16x8 ka = col_frag(Ks, kh * 32, dt * 16, l16, g4);
 #pragma unroll
-        for (int qt = 0; qt < 4; ++qt) dqacc[dt][qt] = mfma16(ka, dsb[qt], dqacc[dt][qt]);
+        for (int qt = 0; qt < 2; ++qt) dqacc[dt][qt] = mfma16(ka, dsb[qt], dqacc[dt][qt]);
       }
     }
-    if (!diag) {
-      tsum = wave_sum(tsum);
-      if (lane == 0) s_red[t & 1][w] = tsum;
-    }
+    return tsum;
+  };
+
+  wait_vm();
+  __syncthreads();
+  if (ntiles > 1) load_tile(sel[0], 1);
+  tile(std::true_type{}, 0, 0.0f);   // diagonal: no gate gradient
+  wait_vm();
+  __syncthreads();
+  for (int t = 1; t < ntiles; ++t) {
+    const int stg = t & 1;
+    const float beta = lgrow[sel[t - 1]] * kLog2e;
+    if (t + 1 < ntiles) load_tile(sel[t], stg ^ 1);
+    float tsum = tile(std::false_type{}, stg, beta);
+    tsum = wave_sum(tsum);
+    if (lane == 0) s_red[t & 1][w] = tsum;
     // previous tile's partial (its slot was filled before the last barrier)
     if (tid == 0 && t >= 2) {
-      float s = 0.0f;
+      float sum = 0.0f;
 #pragma unroll
-      for (int x = 0; x < NW; ++x) s += s_red[(t - 1) & 1][x];
-      part[t - 1] = s;
+      for (int x = 0; x < NW; ++x) sum += s_red[(t - 1) & 1][x];
+      part[t - 1] = sum;
     }
-    if (t + 1 < ntiles) lstore(stg ^ 1);
+    wait_vm();
     __syncthreads();
   }
   if (tid == 0 && ntiles >= 2) {
-    float s = 0.0f;
+    float sum = 0.0f;
 #pragma unroll
-    for (int x = 0; x < NW; ++x) s += s_red[(ntiles - 1) & 1][x];
-    part[ntiles - 1] = s;
+    for (int x = 0; x < NW; ++x) sum += s_red[(ntiles - 1) & 1][x];
+    part[ntiles - 1] = sum;
   }
 
-  // dQ = scale * dQacc (lane: query qt*16 + l16, dims dt*16 + g4*4 .. +3)
+  // dQ = scale * dQacc (lane: row qt*16 + l16, dims dt*16 + g4*4 .. +3)
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
+  for (int qt = 0; qt < 2; ++qt) {
     bf16* dp = a.dq + (q0 + qt * 16 + l16) * HD + g4 * 4;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
@@ -452,13 +458,81 @@ __global__ void __launch_bounds__(256) fill_lists_kernel(BwdArgs a) {
   }
 }
 
+// Column chunk g -> (column, chunk index within the column).
+__device__ __forceinline__ long long chunk_column(const BwdArgs& a, int g) {
+  long long lo = 0, hi = a.ncol;   // chunkoff[lo] <= g < chunkoff[hi]
+  while (hi - lo > 1) {
+    const long long mid = (lo + hi) >> 1;
+    if (a.chunkoff[mid] <= g) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Order of the key-major work: chunks sorted by (batch, kv head, first query
+// block they read).  Workgroups that run at the same time then stream nearby
+// query blocks, so their Q / dO rows are shared through the L2 / MALL.  The
+// order only schedules work; every result is reduced in a fixed order.
+__global__ void chunk_count_kernel(BwdArgs a) {
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= a.chunkoff[a.ncol]) return;
+  const long long col = chunk_column(a, g);
+  const int c = g - a.chunkoff[col];
+  const int first = a.collist[a.coloff[col] + c * kColChunk];
+  const long long key = col - col % a.C + first;   // (batch, kv head) row base + first row
+  a.chunk_rank[g] = atomicAdd(&a.chunk_hist[key], 1);
+}
+
+// exclusive prefix sum of n ints in place (one workgroup); x[n] = total
+__global__ void __launch_bounds__(1024) scan_ints_kernel(int32_t* x, long long n) {
+  __shared__ int s[1024];
+  const int t = threadIdx.x;
+  const long long per = (n + 1023) / 1024;
+  const long long beg = min((long long)t * per, n);
+  const long long end = min(beg + per, n);
+  int sum = 0;
+  for (long long e = beg; e < end; ++e) sum += x[e];
+  s[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int y = t >= off ? s[t - off] : 0;
+    __syncthreads();
+    s[t] += y;
+    __syncthreads();
+  }
+  int run = s[t] - sum;
+  for (long long e = beg; e < end; ++e) {
+    const int v = x[e];
+    x[e] = run;
+    run += v;
+  }
+  if (t == 1023) x[n] = s[1023];
+}
+
+__global__ void chunk_scatter_kernel(BwdArgs a) {
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= a.chunkoff[a.ncol]) return;
+  const long long col = chunk_column(a, g);
+  const int c = g - a.chunkoff[col];
+  const int first = a.collist[a.coloff[col] + c * kColChunk];
+  const long long key = col - col % a.C + first;
+  a.chunk_order[a.chunk_hist[key] + a.chunk_rank[g]] = g;
+}
+
 // ---------------------------------------------------------------------------
 // key-major pass: dK, dV
 // ---------------------------------------------------------------------------
-constexpr int KV_TILE_BYTES = BLK * KSTR * 2;              // 17408
-constexpr int XT_BYTES = HD * XSTR * 2;                      // 9216 per transposed tile
-constexpr int DKDV_LDS = 2 * KV_TILE_BYTES + 4 * 2 * XT_BYTES;  // 108544
+constexpr int KV_TILE_BYTES = BLK * KSTR * 2;                 // 17408
+constexpr int XH_BYTES = 32 * KSTR * 2;                         // 8704: 32 rows, row-major
+constexpr int DKDV_LDS = 2 * KV_TILE_BYTES + 4 * 2 * XH_BYTES;  // 104448
 static_assert(DKDV_LDS >= 2 * 64 * 128 * 4, "reduction buffer must fit");
+
+// One half item: 32 query rows of one (query block, head): Q and dO rows as
+// A operands (lane: row q2*16 + l16, dims ks*32 + g4*8 .. +7), and the LSE /
+// Delta of the rows this lane's accumulator entries belong to (q2*16 + g4*4 + j).
+struct HalfItem {
+  bf16x8 q[2][4];
+  bf16x8 o[2][4];
+};
 
 __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[DKDV_LDS];
@@ -470,18 +544,14 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a) {
   const int w = tid >> 6;
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
-  bf16* xo = (bf16*)(smem + 2 * KV_TILE_BYTES + (2 * w) * XT_BYTES);
-  bf16* xq = (bf16*)(smem + 2 * KV_TILE_BYTES + (2 * w + 1) * XT_BYTES);
+  bf16* xq = (bf16*)(smem + 2 * KV_TILE_BYTES + (2 * w) * XH_BYTES);
+  bf16* xo = (bf16*)(smem + 2 * KV_TILE_BYTES + (2 * w + 1) * XH_BYTES);
 
-  const int g = xcd_remap(blockIdx.x, gridDim.x);
+  const int slot = xcd_remap(blockIdx.x, gridDim.x);
   const int total = a.chunkoff[a.ncol];
-  if (g >= total) return;
-  long long lo = 0, hi = a.ncol;   // chunkoff[lo] <= g < chunkoff[hi]
-  while (hi - lo > 1) {
-    const long long mid = (lo + hi) >> 1;
-    if (a.chunkoff[mid] <= g) lo = mid; else hi = mid;
-  }
-  const long long col = lo;
+  if (slot >= total) return;
+  const int g = a.chunk_order[slot];
+  const long long col = chunk_column(a, g);
   const int c = g - a.chunkoff[col];
   const int nch = a.chunkoff[col + 1] - a.chunkoff[col];
   const int L = a.collen[col];
@@ -503,7 +573,31 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a) {
       *(u32x4*)(&Vs[(cc >> 4) * KSTR + (cc & 15) * 8]) = *(const u32x4*)(vt + (cc >> 4) * HD + (cc & 15) * 8);
     }
   }
-  __syncthreads();
+
+  // this wavefront's work: items it = w, w + 4, ... (item = entry x head), each
+  // processed as two halves of 32 query rows
+  const int nitems = (e1 - e0) * a.G;
+  const int myitems = w < nitems ? (nitems - w + 3) / 4 : 0;
+  const int nsteps = 2 * myitems;
+
+  auto step_row0 = [&](int s) -> long long {   // first query row of half-step s
+    const int it = w + 4 * (s >> 1);
+    const int i = list[e0 + it / a.G];
+    const int h = hk * a.G + it % a.G;
+    return ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + (s & 1) * 32;
+  };
+  auto load_half = [&](int s, HalfItem& hi_) {
+    const long long r0 = step_row0(s);
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const long long r = r0 + q2 * 16 + l16;
+        hi_.q[q2][ks] = *(const bf16x8*)(a.q + r * HD + ks * 32 + g4 * 8);
+        hi_.o[q2][ks] = *(const bf16x8*)(a.d_o + r * HD + ks * 32 + g4 * 8);
+      }
+    }
+  };
 
   f32x4 dkacc[8][4], dvacc[8][4];
 #pragma unroll
@@ -514,111 +608,117 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a) {
       dvacc[dt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-  const int nitems = (e1 - e0) * a.G;
-  for (int it = w; it < nitems; it += 4) {
-    const int ent = e0 + it / a.G;
-    const int hl = it % a.G;
-    const int i = list[ent];
-    const int h = hk * a.G + hl;
+  // LSE and Delta of this lane's rows of half-step s (q2*16 + g4*4 + jj)
+  auto load_stats = [&](int s, f32x4 (&lv)[2], f32x4 (&dv)[2]) {
+    const long long r0 = step_row0(s);
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      lv[q2] = *(const f32x4*)(a.lse + r0 + q2 * 16 + g4 * 4);
+      dv[q2] = *(const f32x4*)(a.delta + r0 + q2 * 16 + g4 * 4);
+    }
+  };
+
+  // Half-step s with its Q / dO rows in `cur`.  The next half-step's rows are
+  // loaded into `nxt` once S, dP, P and dS are formed: their registers are
+  // free by then, and the loads overlap the dV / dK matrix work.  (Refilling
+  // `cur` right after the S / dP instructions instead makes the wavefront wait
+  // for those queued instructions to read their operands first.)
+  auto half_step = [&](int s, const HalfItem& cur, HalfItem& nxt) {
+    const int it = w + 4 * (s >> 1);
+    const int hq = s & 1;
+    const int i = list[e0 + it / a.G];
     const bool diag = (i == j);
     const float beta = diag ? 0.0f : a.lg[(bhk * a.C + i) * a.C + j] * kLog2e;
-    const long long q0 = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK;
-#pragma unroll 1
-    for (int hq = 0; hq < 2; ++hq) {   // two halves of 32 query rows
-      bf16x8 qf[2][4], dof[2][4];
+    f32x4 lv[2], dv[2];   // consumed only after the matrix work below
+    load_stats(s, lv, dv);
+    // S = Q K^T, dP = dO V^T   (lane: key kt*16 + l16; rows q2*16 + g4*4 + jj)
+    f32x4 sacc[2][4], dpacc[2][4];
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const long long r = q0 + hq * 32 + q2 * 16 + l16;
-          qf[q2][ks] = *(const bf16x8*)(a.q + r * HD + ks * 32 + g4 * 8);
-          dof[q2][ks] = *(const bf16x8*)(a.d_o + r * HD + ks * 32 + g4 * 8);
-        }
-      f32x4 lsev[2], dlv[2];
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        const long long r = q0 + hq * 32 + q2 * 16 + g4 * 4;
-        lsev[q2] = *(const f32x4*)(a.lse + r);
-        dlv[q2] = *(const f32x4*)(a.delta + r);
-      }
-      // S = Q K^T, dP = dO V^T   (lane: key kt*16 + l16; queries q2*16 + g4*4 + j)
-      f32x4 sacc[2][4], dpacc[2][4];
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          sacc[q2][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dpacc[q2][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const bf16x8 kb = *(const bf16x8*)(Ks + (kt * 16 + l16) * KSTR + ks * 32 + g4 * 8);
-          const bf16x8 vb = *(const bf16x8*)(Vs + (kt * 16 + l16) * KSTR + ks * 32 + g4 * 8);
-#pragma unroll
-          for (int q2 = 0; q2 < 2; ++q2) {
-            sacc[q2][kt] = mfma16(qf[q2][ks], kb, sacc[q2][kt]);
-            dpacc[q2][kt] = mfma16(dof[q2][ks], vb, dpacc[q2][kt]);
-          }
-        }
-      // stage dO^T and Q^T of these 32 rows in the wave's LDS tiles
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const int d = ks * 32 + g4 * 8 + x;
-            xo[d * XSTR + q2 * 16 + l16] = dof[q2][ks][x];
-            xq[d * XSTR + q2 * 16 + l16] = qf[q2][ks][x];
-          }
-      // P and dS as B operands (lane: key; queries x/4*16 + g4*4 + x%4)
-      bf16x8 pb[4], dsb[4];
+    for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const int key = kt * 16 + l16;
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int qi = hq * 32 + q2 * 16 + g4 * 4 + jj;
-            float p = exp2f(sacc[q2][kt][jj] * a.c2 + beta - lsev[q2][jj] * kLog2e);
-            if (diag && key > qi) p = 0.0f;
-            const float ds = p * (dpacc[q2][kt][jj] - dlv[q2][jj]);
-            pb[kt][q2 * 4 + jj] = (bf16)p;
-            dsb[kt][q2 * 4 + jj] = (bf16)ds;
-          }
+        sacc[q2][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dpacc[q2][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      wave_lds_sync();
-      // dV^T += dO^T P, dK^T += Q^T dS
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const bf16* op = xo + (dt * 16 + l16) * XSTR + g4 * 4;
-        const bf16* qp = xq + (dt * 16 + l16) * XSTR + g4 * 4;
-        const bf16x8 oa = join(*(const bf16x4*)op, *(const bf16x4*)(op + 16));
-        const bf16x8 qa = join(*(const bf16x4*)qp, *(const bf16x4*)(qp + 16));
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          dvacc[dt][kt] = mfma16(oa, pb[kt], dvacc[dt][kt]);
-          dkacc[dt][kt] = mfma16(qa, dsb[kt], dkacc[dt][kt]);
+      for (int kt = 0; kt < 4; ++kt) {
+        const bf16x8 kb = *(const bf16x8*)(Ks + (kt * 16 + l16) * KSTR + ks * 32 + g4 * 8);
+        const bf16x8 vb = *(const bf16x8*)(Vs + (kt * 16 + l16) * KSTR + ks * 32 + g4 * 8);
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          sacc[q2][kt] = mfma16(cur.q[q2][ks], kb, sacc[q2][kt]);
+          dpacc[q2][kt] = mfma16(cur.o[q2][ks], vb, dpacc[q2][kt]);
         }
       }
-      wave_lds_sync();
+    // stage Q and dO rows (row-major) for the transposed reads below
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        *(bf16x8*)(xq + (q2 * 16 + l16) * KSTR + ks * 32 + g4 * 8) = cur.q[q2][ks];
+        *(bf16x8*)(xo + (q2 * 16 + l16) * KSTR + ks * 32 + g4 * 8) = cur.o[q2][ks];
+      }
+    // P and dS as B operands (lane: key; rows x/4*16 + g4*4 + x%4)
+    bf16x8 pb[4], dsb[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          float p = __builtin_amdgcn_exp2f(
+              fmaf(sacc[q2][kt][jj], a.c2, fmaf(-lv[q2][jj], kLog2e, beta)));
+          if (diag && (kt * 16 + l16) > (hq * 32 + q2 * 16 + g4 * 4 + jj)) p = 0.0f;
+          const float ds = p * (dpacc[q2][kt][jj] - dv[q2][jj]);
+          pb[kt][q2 * 4 + jj] = (bf16)p;
+          dsb[kt][q2 * 4 + jj] = (bf16)ds;
+        }
     }
+    if (s + 1 < nsteps) load_half(s + 1, nxt);
+    wave_lds_sync();
+    // dV^T += dO^T P, dK^T += Q^T dS; A operands read transposed from the
+    // row-major tiles (ds_read_b64_tr_b16: lane gets 4 consecutive rows of
+    // its column)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int roff = (g4 * 4 + (l16 >> 2)) * KSTR + dt * 16 + (l16 & 3) * 4;
+      const bf16x8 oa = join(ds_read_tr(xo + roff), ds_read_tr(xo + roff + 16 * KSTR));
+      const bf16x8 qa = join(ds_read_tr(xq + roff), ds_read_tr(xq + roff + 16 * KSTR));
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        dvacc[dt][kt] = mfma16(oa, pb[kt], dvacc[dt][kt]);
+        dkacc[dt][kt] = mfma16(qa, dsb[kt], dkacc[dt][kt]);
+      }
+    }
+    wave_lds_sync();
+  };
+
+  HalfItem cur;
+  if (nsteps > 0) load_half(0, cur);
+  __syncthreads();   // K_j, V_j staged
+#pragma unroll 1
+  for (int s = 0; s < nsteps; ++s) {
+    HalfItem nxt;
+    half_step(s, cur, nxt);
+    cur = nxt;
   }
 
-  // add the four wavefronts' partial sums in a fixed order (LDS, fp32)
+  // add the four wavefronts' partial sums in a fixed order (LDS, fp32); the
+  // 16-byte chunk c of key row r is stored at chunk c ^ (r & 31) so that the
+  // 16 rows written by one instruction spread over the banks
   __syncthreads();
   float* redk = (float*)smem;
   float* redv = redk + 64 * 128;
+  auto roff = [](int r, int d) { return r * 128 + ((((d >> 2) ^ (r & 31))) << 2) + (d & 3); };
   for (int x = 0; x < 4; ++x) {
     if (w == x) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-          const int off = (kt * 16 + l16) * 128 + dt * 16 + g4 * 4;
+          const int off = roff(kt * 16 + l16, dt * 16 + g4 * 4);
           if (x == 0) {
             *(f32x4*)(redk + off) = dkacc[dt][kt];
             *(f32x4*)(redv + off) = dvacc[dt][kt];
@@ -634,12 +734,19 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a) {
   if (nch == 1) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int e = (tid + r * 256) * 8;   // 8 consecutive elements
+      const int e = (tid + r * 256) * 8;   // 8 consecutive elements of key row e / 128
+      const int kr = e >> 7, d = e & 127;
+      const f32x4 k0 = *(const f32x4*)(redk + roff(kr, d));
+      const f32x4 k1 = *(const f32x4*)(redk + roff(kr, d + 4));
+      const f32x4 v0 = *(const f32x4*)(redv + roff(kr, d));
+      const f32x4 v1 = *(const f32x4*)(redv + roff(kr, d + 4));
       bf16x8 ok, ov;
 #pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        ok[x] = (bf16)(redk[e + x] * a.scale);
-        ov[x] = (bf16)redv[e + x];
+      for (int x = 0; x < 4; ++x) {
+        ok[x] = (bf16)(k0[x] * a.scale);
+        ok[x + 4] = (bf16)(k1[x] * a.scale);
+        ov[x] = (bf16)v0[x];
+        ov[x + 4] = (bf16)v1[x];
       }
       *(bf16x8*)(a.dk + orow * HD + e) = ok;
       *(bf16x8*)(a.dv + orow * HD + e) = ov;
@@ -650,8 +757,9 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int e = (tid + r * 256) * 4;
-      *(f32x4*)(pk + e) = *(const f32x4*)(redk + e);
-      *(f32x4*)(pv + e) = *(const f32x4*)(redv + e);
+      const int kr = e >> 7, d = e & 127;
+      *(f32x4*)(pk + e) = *(const f32x4*)(redk + roff(kr, d));
+      *(f32x4*)(pv + e) = *(const f32x4*)(redv + roff(kr, d));
     }
   }
 }
@@ -686,13 +794,13 @@ __global__ void __launch_bounds__(256) reduce_kernel(BwdArgs a) {
   }
 }
 
-template <int NW>
+template <int NH>
 hipError_t launch_dq(BwdArgs a, int head_base, int nchunk, int part_base, long long units,
                      hipStream_t st) {
   a.head_base = head_base;
   a.nchunk = nchunk;
   a.part_base = part_base;
-  hipLaunchKernelGGL((bwd_dq_kernel<NW>), dim3((unsigned)(units * nchunk)), dim3(NW * 64), 0, st,
+  hipLaunchKernelGGL((bwd_dq_kernel<NH>), dim3((unsigned)(units * nchunk)), dim3(NH * 128), 0, st,
                      a);
   return hipGetLastError();
 }
@@ -716,6 +824,9 @@ BwdArgs make_bwd_args(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorks
   a.chunkoff = (int32_t*)(ws + wl.chunkoff);
   a.collist = (int32_t*)(ws + wl.collist);
   a.partial = (float*)(ws + wl.partial);
+  a.chunk_rank = (int32_t*)(ws + wl.chunk_rank);
+  a.chunk_hist = (int32_t*)(ws + wl.chunk_hist);
+  a.chunk_order = (int32_t*)(ws + wl.chunk_order);
   a.ncol = (long long)s.B * s.Hkv * s.C;
   a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.G; a.N = s.N; a.C = s.C; a.cap = s.cap; a.W = wl.words;
   a.o_fp32 = s.o_fp32;
@@ -761,6 +872,13 @@ hipError_t launch_bwd_dq_mfma(const Shape& s, const BwdPtrs& p, char* ws, const 
   hipLaunchKernelGGL(count_kernel, dim3((unsigned)((a.ncol + 255) / 256)), dim3(256), 0, st, a);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, a);
   hipLaunchKernelGGL(fill_lists_kernel, dim3((unsigned)((a.ncol + 3) / 4)), dim3(256), 0, st, a);
+  // schedule order of the key-major chunks
+  const unsigned cgrid = (unsigned)((wl.max_chunks + 255) / 256);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)min((a.ncol + 256) / 256, 65535LL)),
+                     dim3(256), 0, st, (uint32_t*)a.chunk_hist, a.ncol + 1);
+  hipLaunchKernelGGL(chunk_count_kernel, dim3(cgrid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(scan_ints_kernel, dim3(1), dim3(1024), 0, st, a.chunk_hist, a.ncol);
+  hipLaunchKernelGGL(chunk_scatter_kernel, dim3(cgrid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -9,9 +9,10 @@
 // the attention matrix; O = acc / l and LSE = m + log l.
 //
 // gfx950 mapping
-//  * One workgroup per (batch, kv head, query block, chunk of NW query heads);
-//    each wavefront owns the 64 query rows of one head, so the G heads of a
-//    kv group share every K/V tile staged in LDS (GQA reuse through LDS).
+//  * One workgroup per (batch, kv head, query block, chunk of query heads);
+//    two wavefronts per head, each owning 32 of its 64 query rows, so the G
+//    heads of a kv group share every K/V tile staged in LDS (GQA reuse
+//    through LDS) and two wavefronts share each SIMD.
 //  * The scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_16x16x32_bf16: in the accumulator layout a lane then holds
 //    one query column and 4 consecutive keys of each 16-key tile, so
@@ -20,16 +21,21 @@
 //      - the probabilities are already in the B-operand layout of
 //        O^T += V^T P^T (keys permuted consistently on both operands), so P
 //        never goes through LDS.
-//  * K tiles are kept row-major in LDS (A operand of K Q^T: 16-byte reads);
-//    V tiles are written transposed ([d][key]) when staged, so the A operand
-//    of V^T P^T is two 8-byte reads.  Row strides are padded so the 16 rows
-//    read by one lane group fall in distinct banks.
-//  * K/V tiles are double buffered: the next tile's global loads are issued
-//    before the current tile's matrix work and written to the other LDS
-//    stage after it (one barrier per tile).
+//  * K and V tiles are copied global -> LDS asynchronously (global_load_lds,
+//    no registers), row-major with an XOR-swizzled 16-byte chunk order.  The
+//    A operand of K Q^T is one 16-byte read; the A operand of V^T P^T (a
+//    column fragment of V) comes from two transposed reads
+//    (ds_read_b64_tr_b16), so V is never transposed in memory.
+//  * Two LDS stages: the next tile's copy is issued before the current
+//    tile's matrix work (one barrier per tile).
+//  * The online softmax rescales O lazily (only when a row max grows by more
+//    than 2^8) and the diagonal tile is peeled, so the steady-state tile has
+//    no masking and, almost always, no accumulator rescale.
 //  * Workgroup ids are remapped so that each XCD (own L2) works through a
 //    contiguous range of (batch, kv head, query block) units.
 #include <math.h>
+
+#include <type_traits>
 
 #include "sas_internal.h"
 
@@ -45,8 +51,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BLK = 64;
 constexpr int HD = 128;
-constexpr int KSTR = HD + 8;   // bf16 per row of a row-major [key][d] LDS tile (272 B)
-constexpr int TSTR = BLK + 4;  // bf16 per row of a transposed [d][key] LDS tile (136 B)
+constexpr int TILE = BLK * HD;  // bf16 elements of one 64 x 128 K or V tile (16 KB)
 
 struct FwdArgs {
   const bf16* q; const bf16* k; const bf16* v;
@@ -78,19 +83,63 @@ __device__ __forceinline__ float sum4(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// gfx950 transposed LDS read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane u receives element u % 4 of the 8-byte chunks addressed by lanes
+// u / 4 + 4x (x = 0..3).  With lane u addressing row base + u / 4, columns
+// c0 + 4 (u % 4) .. +3 of a row-major tile, lane u gets rows base .. base + 3
+// of column c0 + u.
+__device__ __forceinline__ bf16x4 ds_read_tr(const bf16* p) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+// LDS tiles are row-major with 256-byte rows and no padding; the 16-byte chunk
+// c of row r sits in slot c ^ (r & 15).  The 16 rows read by one lane group
+// (same chunk) then fall in 16 different slots, i.e. all 64 banks.
+__device__ __forceinline__ int swz(int r, int c) { return r * HD + ((c ^ (r & 15)) << 3); }
+
+// Asynchronous global -> LDS copy of one 64 x 128 tile by NW wavefronts
+// (global_load_lds_dwordx4: each instruction writes 64 x 16 contiguous bytes
+// of LDS; the lanes pick their global chunk so the result is swizzled).
+// Completion is waited for with s_waitcnt vmcnt(0) before the next barrier.
 template <int NW>
-__global__ void __launch_bounds__(NW * 64, 1) fwd_mfma_kernel(FwdArgs a) {
-  constexpr int NT = NW * 64;
-  constexpr int KCH = 1024 / NT;  // 16-byte K chunks per thread per tile
-  constexpr int VUN = 256 / NT;   // (4 keys x 8 d) V units per thread per tile
-  __shared__ __attribute__((aligned(16))) bf16 s_k[2][BLK * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16 s_vt[2][HD * TSTR];
+__device__ __forceinline__ void tile_to_lds(bf16* lds, const bf16* g, int w, int lane) {
+  typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+  for (int r = 0; r < 16 / NW; ++r) {
+    const int seg = w + NW * r;               // 1 KB segment = rows 4 seg .. 4 seg + 3
+    const int row = seg * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ (row & 15);
+    __builtin_amdgcn_global_load_lds(g + row * HD + c * 8, (lds_void*)(lds + seg * 512), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_vm() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Rescale threshold of the lazy online softmax (log2 units): the running max
+// is only moved (and O, l rescaled) when a tile raises some row's max by more
+// than this; otherwise exp2 arguments stay <= kLazy, so P <= 2^kLazy.
+constexpr float kLazy = 8.0f;
+
+// One workgroup = NH query heads of one (batch, kv head, query block); two
+// wavefronts per head, each owning 32 of the 64 query rows (two 16-row tiles).
+// At <= 256 registers per wavefront two wavefronts share a SIMD, so one
+// wavefront's softmax runs while the other's matrix instructions issue.
+// SPLIT: P enters O^T += V^T P^T as hi + lo bf16 terms (two MFMAs), which
+// makes O accurate to ~2^-16 relative instead of ~2^-9 (used when o is kept
+// in fp32, so the backward's Delta = rowsum(O dO) is exact to fp32 level).
+template <int NH, bool SPLIT>
+__global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
+  constexpr int NW = 2 * NH;
+  __shared__ __attribute__((aligned(16))) bf16 s_k[2][TILE];
+  __shared__ __attribute__((aligned(16))) bf16 s_v[2][TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
+  const int half = w & 1;           // rows half*32 .. half*32 + 31 of the block
 
   const int unit = xcd_remap(blockIdx.x, gridDim.x);
   const int chunk = unit % a.nchunk;
@@ -99,166 +148,152 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_mfma_kernel(FwdArgs a) {
   const int bhk = rest / a.C;
   const int hk = bhk % a.Hkv;
   const int bb = bhk / a.Hkv;
-  const int h = hk * a.G + a.head_base + chunk * NW + w;
+  const int h = hk * a.G + a.head_base + chunk * NH + (w >> 1);
   const long long row = (long long)bhk * a.C + i;
   const int cnt = min(a.sel_cnt[row], a.cap);
   const int32_t* sel = a.sel_idx + row * a.cap;
   const float* lgrow = a.lg + row * a.C;
   const bf16* kbase = a.k + (long long)bhk * a.N * HD;
   const bf16* vbase = a.v + (long long)bhk * a.N * HD;
-  const long long q0 = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK;
+  const long long q0 = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + half * 32;
 
-  // Q^T as the B operand of S^T = K Q^T: lane holds query qt*16 + l16 and
-  // head dims ks*32 + g4*8 .. +7.  Pre-scaled by nothing (scale is applied to S).
-  bf16x8 qf[4][4];
-  {
-    const bf16* qp = a.q + q0 * HD;
+  // Q^T as the B operand of S^T = K Q^T: lane holds row qt*16 + l16 (of this
+  // wavefront's 32) and head dims ks*32 + g4*8 .. +7.
+  bf16x8 qf[2][4];
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt)
+  for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        qf[qt][ks] = *(const bf16x8*)(qp + (qt * 16 + l16) * HD + ks * 32 + g4 * 8);
-  }
+    for (int ks = 0; ks < 4; ++ks)
+      qf[qt][ks] = *(const bf16x8*)(a.q + (q0 + qt * 16 + l16) * HD + ks * 32 + g4 * 8);
 
-  u32x4 kreg[KCH];
-  u32x4 vreg[VUN][4];
-  auto gload = [&](int kb) {
-    const bf16* kt = kbase + (long long)kb * BLK * HD;
-    const bf16* vt = vbase + (long long)kb * BLK * HD;
-#pragma unroll
-    for (int r = 0; r < KCH; ++r) {
-      const int c = tid + r * NT;
-      kreg[r] = *(const u32x4*)(kt + (c >> 4) * HD + (c & 15) * 8);
-    }
-#pragma unroll
-    for (int r = 0; r < VUN; ++r) {
-      const int u = tid + r * NT;
-      const int kg = u >> 4, dg = u & 15;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) vreg[r][x] = *(const u32x4*)(vt + (kg * 4 + x) * HD + dg * 8);
-    }
-  };
-  auto lstore = [&](int stg) {
-#pragma unroll
-    for (int r = 0; r < KCH; ++r) {
-      const int c = tid + r * NT;
-      *(u32x4*)(&s_k[stg][(c >> 4) * KSTR + (c & 15) * 8]) = kreg[r];
-    }
-#pragma unroll
-    for (int r = 0; r < VUN; ++r) {
-      const int u = tid + r * NT;
-      const int kg = u >> 4, dg = u & 15;
-#pragma unroll
-      for (int z = 0; z < 4; ++z) {
-        const uint32_t w0 = vreg[r][0][z], w1 = vreg[r][1][z];
-        const uint32_t w2 = vreg[r][2][z], w3 = vreg[r][3][z];
-        u32x2 lo, hi;
-        lo[0] = (w0 & 0xffffu) | (w1 << 16);
-        lo[1] = (w2 & 0xffffu) | (w3 << 16);
-        hi[0] = (w0 >> 16) | (w1 & 0xffff0000u);
-        hi[1] = (w2 >> 16) | (w3 & 0xffff0000u);
-        *(u32x2*)(&s_vt[stg][(dg * 8 + 2 * z) * TSTR + kg * 4]) = lo;
-        *(u32x2*)(&s_vt[stg][(dg * 8 + 2 * z + 1) * TSTR + kg * 4]) = hi;
-      }
-    }
+  auto load_tile = [&](int kb, int stg) {
+    tile_to_lds<NW>(s_k[stg], kbase + (long long)kb * TILE, w, lane);
+    tile_to_lds<NW>(s_v[stg], vbase + (long long)kb * TILE, w, lane);
   };
 
-  f32x4 oacc[8][4];
+  f32x4 oacc[8][2];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) oacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrow[4], lrow[4];
-#pragma unroll
-  for (int qt = 0; qt < 4; ++qt) { mrow[qt] = -INFINITY; lrow[qt] = 0.0f; }
+    for (int qt = 0; qt < 2; ++qt) oacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrow[2], lrow[2];   // running max (log2 units) and per-lane partial sums
 
-  const int ntiles = cnt + 1;
-  gload(i);
-  lstore(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int stg = t & 1;
-    const bool diag = (t == 0);
-    const int kb = diag ? i : sel[t - 1];
-    const float beta = diag ? 0.0f : lgrow[kb] * kLog2e;
-    if (t + 1 < ntiles) gload(sel[t]);
-
+  // One 64-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
+  auto tile = [&](auto diag_tag, int stg, float beta) {
+    constexpr bool DIAG = decltype(diag_tag)::value;
     const bf16* Ks = s_k[stg];
-    const bf16* Vt = s_vt[stg];
-
-    // ---- S^T = K Q^T ----
-    f32x4 sacc[4][4];
+    const bf16* Vs = s_v[stg];
+    f32x4 sacc[4][2];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt) sacc[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int qt = 0; qt < 2; ++qt) sacc[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const bf16x8 ka = *(const bf16x8*)(Ks + (kt * 16 + l16) * KSTR + ks * 32 + g4 * 8);
+        const bf16x8 ka = *(const bf16x8*)(Ks + swz(kt * 16 + l16, ks * 4 + g4));
 #pragma unroll
-        for (int qt = 0; qt < 4; ++qt) sacc[kt][qt] = mfma16(ka, qf[qt][ks], sacc[kt][qt]);
+        for (int qt = 0; qt < 2; ++qt) sacc[kt][qt] = mfma16(ka, qf[qt][ks], sacc[kt][qt]);
       }
     }
-
-    // ---- online softmax (base 2) ----
-    bf16x8 pb[2][4];
+    if (DIAG) {   // causal mask inside the current block: key > query -> -inf
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
-      const int qi = qt * 16 + l16;  // query index inside the block
-      float x[16];
-      float mx = -INFINITY;
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (kt * 16 + g4 * 4 + j > half * 32 + qt * 16 + l16) sacc[kt][qt][j] = -INFINITY;
+    }
+    // tile row max (raw scores; c2 > 0 keeps the order)
+    float tmax[2];
+    bool grow = false;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float mx = fmaxf(fmaxf(sacc[0][qt][0], sacc[0][qt][1]), fmaxf(sacc[0][qt][2], sacc[0][qt][3]));
+#pragma unroll
+      for (int kt = 1; kt < 4; ++kt)
+        mx = fmaxf(mx, fmaxf(fmaxf(sacc[kt][qt][0], sacc[kt][qt][1]),
+                             fmaxf(sacc[kt][qt][2], sacc[kt][qt][3])));
+      tmax[qt] = max4(mx) * a.c2 + beta;
+      if (!DIAG) grow |= tmax[qt] > mrow[qt] + kLazy;
+    }
+    if (DIAG) {
+      // first tile: O and l are still zero, the max just starts here
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) { mrow[qt] = tmax[qt]; lrow[qt] = 0.0f; }
+    } else if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform, rare
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const float mnew = fmaxf(mrow[qt], tmax[qt]);
+        const float alpha = __builtin_amdgcn_exp2f(mrow[qt] - mnew);
+        mrow[qt] = mnew;
+        lrow[qt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) oacc[dt][qt] *= alpha;
+      }
+    }
+    // P = exp2(c2 s + beta - m), packed as the B operand of O^T += V^T P^T
+    bf16x8 pb[2][2], pl[2][2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const float off = beta - mrow[qt];
+      float ps = 0.0f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float val = sacc[kt][qt][j] * a.c2 + beta;
-          if (diag && (kt * 16 + g4 * 4 + j) > qi) val = -INFINITY;
-          x[kt * 4 + j] = val;
-          mx = fmaxf(mx, val);
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][qt][j], a.c2, off));
+          ps += p;
+          const bf16 ph = (bf16)p;
+          pb[kt >> 1][qt][(kt & 1) * 4 + j] = ph;
+          if (SPLIT) pl[kt >> 1][qt][(kt & 1) * 4 + j] = (bf16)(p - (float)ph);
         }
-      mx = max4(mx);
-      const float mnew = fmaxf(mrow[qt], mx);
-      const float alpha = exp2f(mrow[qt] - mnew);
-      mrow[qt] = mnew;
-      float ps = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        x[e] = exp2f(x[e] - mnew);
-        ps += x[e];
-      }
-      lrow[qt] = lrow[qt] * alpha + ps;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) oacc[dt][qt] *= alpha;
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[k2][qt][e] = (bf16)x[k2 * 8 + e];
+      lrow[qt] += ps;
     }
-
-    // ---- O^T += V^T P^T ----
+    // O^T += V^T P^T; V^T fragments read transposed from the row-major tile
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        const bf16* vp = Vt + (dt * 16 + l16) * TSTR + k2 * 32 + g4 * 4;
-        const bf16x4 lo = *(const bf16x4*)(vp);
-        const bf16x4 hi = *(const bf16x4*)(vp + 16);
-        const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const int vr = k2 * 32 + g4 * 4 + (l16 >> 2);
+        const int vc = dt * 2 + ((l16 >> 1) & 1);
+        const int ve = (l16 & 1) * 4;
+        const bf16x8 va = __builtin_shufflevector(ds_read_tr(Vs + swz(vr, vc) + ve),
+                                                  ds_read_tr(Vs + swz(vr + 16, vc) + ve),
+                                                  0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-        for (int qt = 0; qt < 4; ++qt) oacc[dt][qt] = mfma16(va, pb[k2][qt], oacc[dt][qt]);
+        for (int qt = 0; qt < 2; ++qt) {
+          oacc[dt][qt] = mfma16(va, pb[k2][qt], oacc[dt][qt]);
+          if (SPLIT) oacc[dt][qt] = mfma16(va, pl[k2][qt], oacc[dt][qt]);
+        }
       }
     }
+  };
 
-    if (t + 1 < ntiles) lstore(stg ^ 1);
+  const int ntiles = cnt + 1;
+  load_tile(i, 0);
+  wait_vm();
+  __syncthreads();
+  // diagonal tile (unit gate, causal); the next tile streams into the other stage
+  if (ntiles > 1) load_tile(sel[0], 1);
+  tile(std::true_type{}, 0, 0.0f);
+  wait_vm();
+  __syncthreads();
+  // selected tiles (additive log gate)
+  for (int t = 1; t < ntiles; ++t) {
+    const int stg = t & 1;
+    const float beta = lgrow[sel[t - 1]] * kLog2e;
+    if (t + 1 < ntiles) load_tile(sel[t], stg ^ 1);
+    tile(std::false_type{}, stg, beta);
+    wait_vm();
     __syncthreads();
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
+  for (int qt = 0; qt < 2; ++qt) {
     const float ltot = sum4(lrow[qt]);
     const float inv = 1.0f / ltot;
     const long long qrow = q0 + qt * 16 + l16;
@@ -280,13 +315,16 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_mfma_kernel(FwdArgs a) {
   }
 }
 
-template <int NW>
+template <int NH>
 hipError_t launch_chunks(FwdArgs a, int head_base, int nchunk, long long units,
                          hipStream_t st) {
   a.head_base = head_base;
   a.nchunk = nchunk;
   const long long grid = units * nchunk;
-  hipLaunchKernelGGL((fwd_mfma_kernel<NW>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a);
+  if (a.o_fp32)
+    hipLaunchKernelGGL((fwd_mfma_kernel<NH, true>), dim3((unsigned)grid), dim3(NH * 128), 0, st, a);
+  else
+    hipLaunchKernelGGL((fwd_mfma_kernel<NH, false>), dim3((unsigned)grid), dim3(NH * 128), 0, st, a);
   return hipGetLastError();
 }
 
