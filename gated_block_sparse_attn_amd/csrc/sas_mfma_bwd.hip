@@ -521,20 +521,26 @@ __global__ void chunk_scatter_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // key-major pass: dK, dV
 // ---------------------------------------------------------------------------
-constexpr int KV_TILE_BYTES = BLK * KSTR * 2;                 // 17408
-constexpr int XH_BYTES = 32 * KSTR * 2;                         // 8704: 32 rows, row-major
-constexpr int DKDV_LDS = 2 * KV_TILE_BYTES + 4 * 2 * XH_BYTES;  // 104448
+// One workgroup per column chunk (key block j, up to kColChunk query blocks).
+// Eight wavefronts = four pairs; pair `slot` streams the (query block, head)
+// items slot, slot + 4, ... in two halves of 32 query rows, and the two
+// wavefronts of a pair split the work by tensor:
+//   wave A (role 0): S = Q K^T -> P, and dV^T += dO^T P   (dV accumulator)
+//   wave B (role 1): dP = dO V^T -> dS = P (dP - Delta), dK^T += Q^T dS
+// Each wavefront holds one 64 x 128 fp32 accumulator (128 registers), so two
+// wavefronts fit per SIMD and every matrix product is computed once.  Per
+// half item, A stages its Q rows and P in LDS, B stages its dO rows; the
+// transposed operands Q^T / dO^T come from ds_read_b64_tr_b16 reads of the
+// staged rows.  The four pairs advance in lockstep (two workgroup barriers
+// per half item).
+constexpr int KV_TILE_BYTES = BLK * KSTR * 2;                  // 17408 (padded rows)
+constexpr int XH_BYTES = 32 * KSTR * 2;                          // 8704: 32 staged rows
+constexpr int XP_BYTES = 32 * 64 * 4;                            // 8192: P, [value][lane]
+constexpr int SLOT_BYTES = 2 * XH_BYTES + XP_BYTES;              // 25600
+constexpr int DKDV_LDS = 2 * KV_TILE_BYTES + 4 * SLOT_BYTES;     // 137216
 static_assert(DKDV_LDS >= 2 * 64 * 128 * 4, "reduction buffer must fit");
 
-// One half item: 32 query rows of one (query block, head): Q and dO rows as
-// A operands (lane: row q2*16 + l16, dims ks*32 + g4*8 .. +7), and the LSE /
-// Delta of the rows this lane's accumulator entries belong to (q2*16 + g4*4 + j).
-struct HalfItem {
-  bf16x8 q[2][4];
-  bf16x8 o[2][4];
-};
-
-__global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[DKDV_LDS];
   bf16* Ks = (bf16*)smem;
   bf16* Vs = (bf16*)(smem + KV_TILE_BYTES);
@@ -542,15 +548,19 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int role = w >> 2;   // 0: S / P / dV, 1: dP / dS / dK
+  const int slot = w & 3;
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
-  bf16* xq = (bf16*)(smem + 2 * KV_TILE_BYTES + (2 * w) * XH_BYTES);
-  bf16* xo = (bf16*)(smem + 2 * KV_TILE_BYTES + (2 * w + 1) * XH_BYTES);
+  char* sbase = smem + 2 * KV_TILE_BYTES + slot * SLOT_BYTES;
+  bf16* xq = (bf16*)sbase;                    // Q rows of the slot's half item
+  bf16* xo = (bf16*)(sbase + XH_BYTES);       // dO rows
+  float* xp = (float*)(sbase + 2 * XH_BYTES);  // P (fp32), [value index][lane]
 
-  const int slot = xcd_remap(blockIdx.x, gridDim.x);
+  const int sid = xcd_remap(blockIdx.x, gridDim.x);
   const int total = a.chunkoff[a.ncol];
-  if (slot >= total) return;
-  const int g = a.chunk_order[slot];
+  if (sid >= total) return;
+  const int g = a.chunk_order[sid];
   const long long col = chunk_column(a, g);
   const int c = g - a.chunkoff[col];
   const int nch = a.chunkoff[col + 1] - a.chunkoff[col];
@@ -563,169 +573,151 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a) {
   const int hk = (int)(bhk % a.Hkv);
   const int bb = (int)(bhk / a.Hkv);
 
-  {  // stage K_j, V_j (row-major)
+  {  // stage K_j, V_j (row-major, padded rows)
     const bf16* kt = a.k + (bhk * a.N + (long long)j * BLK) * HD;
     const bf16* vt = a.v + (bhk * a.N + (long long)j * BLK) * HD;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int cc = tid + r * 256;
+    for (int r = 0; r < 2; ++r) {
+      const int cc = tid + r * 512;
       *(u32x4*)(&Ks[(cc >> 4) * KSTR + (cc & 15) * 8]) = *(const u32x4*)(kt + (cc >> 4) * HD + (cc & 15) * 8);
       *(u32x4*)(&Vs[(cc >> 4) * KSTR + (cc & 15) * 8]) = *(const u32x4*)(vt + (cc >> 4) * HD + (cc & 15) * 8);
     }
   }
 
-  // this wavefront's work: items it = w, w + 4, ... (item = entry x head), each
-  // processed as two halves of 32 query rows
   const int nitems = (e1 - e0) * a.G;
-  const int myitems = w < nitems ? (nitems - w + 3) / 4 : 0;
-  const int nsteps = 2 * myitems;
+  const int myitems = slot < nitems ? (nitems - slot + 3) / 4 : 0;
+  const int nsteps = 2 * myitems;            // this pair's half items
+  const int lockstep = 2 * ((nitems + 3) / 4);   // half items of the busiest pair
 
-  auto step_row0 = [&](int s) -> long long {   // first query row of half-step s
-    const int it = w + 4 * (s >> 1);
+  // first query row of half item s of this pair
+  auto step_row0 = [&](int s) -> long long {
+    const int it = slot + 4 * (s >> 1);
     const int i = list[e0 + it / a.G];
     const int h = hk * a.G + it % a.G;
     return ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + (s & 1) * 32;
   };
-  auto load_half = [&](int s, HalfItem& hi_) {
+  // A loads Q rows, B loads dO rows (lane: row q2*16 + l16, dims ks*32 + g4*8 .. +7)
+  const bf16* src = role == 0 ? a.q : a.d_o;
+  auto load_rows = [&](int s, bf16x8 (&rw)[2][4]) {
     const long long r0 = step_row0(s);
 #pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) {
+    for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const long long r = r0 + q2 * 16 + l16;
-        hi_.q[q2][ks] = *(const bf16x8*)(a.q + r * HD + ks * 32 + g4 * 8);
-        hi_.o[q2][ks] = *(const bf16x8*)(a.d_o + r * HD + ks * 32 + g4 * 8);
-      }
-    }
+      for (int ks = 0; ks < 4; ++ks)
+        rw[q2][ks] = *(const bf16x8*)(src + (r0 + q2 * 16 + l16) * HD + ks * 32 + g4 * 8);
   };
+  // A: LSE (log2 units folded later), B: Delta, of this lane's accumulator rows
+  const float* stat = role == 0 ? a.lse : a.delta;
 
-  f32x4 dkacc[8][4], dvacc[8][4];
+  f32x4 acc[8][4];   // A: dV^T, B: dK^T  (lane: key kt*16 + l16, dims dt*16 + g4*4 .. +3)
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      dkacc[dt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dvacc[dt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int kt = 0; kt < 4; ++kt) acc[dt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // LSE and Delta of this lane's rows of half-step s (q2*16 + g4*4 + jj)
-  auto load_stats = [&](int s, f32x4 (&lv)[2], f32x4 (&dv)[2]) {
-    const long long r0 = step_row0(s);
-#pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) {
-      lv[q2] = *(const f32x4*)(a.lse + r0 + q2 * 16 + g4 * 4);
-      dv[q2] = *(const f32x4*)(a.delta + r0 + q2 * 16 + g4 * 4);
-    }
-  };
+  bf16x8 rows[2][4];
+  if (nsteps > 0) load_rows(0, rows);
+  __syncthreads();   // K_j, V_j staged
 
-  // Half-step s with its Q / dO rows in `cur`.  The next half-step's rows are
-  // loaded into `nxt` once S, dP, P and dS are formed: their registers are
-  // free by then, and the loads overlap the dV / dK matrix work.  (Refilling
-  // `cur` right after the S / dP instructions instead makes the wavefront wait
-  // for those queued instructions to read their operands first.)
-  auto half_step = [&](int s, const HalfItem& cur, HalfItem& nxt) {
-    const int it = w + 4 * (s >> 1);
-    const int hq = s & 1;
-    const int i = list[e0 + it / a.G];
-    const bool diag = (i == j);
-    const float beta = diag ? 0.0f : a.lg[(bhk * a.C + i) * a.C + j] * kLog2e;
-    f32x4 lv[2], dv[2];   // consumed only after the matrix work below
-    load_stats(s, lv, dv);
-    // S = Q K^T, dP = dO V^T   (lane: key kt*16 + l16; rows q2*16 + g4*4 + jj)
-    f32x4 sacc[2][4], dpacc[2][4];
+#pragma unroll 1
+  for (int s = 0; s < lockstep; ++s) {
+    const bool active = s < nsteps;
+    bf16x8 bop[4];   // B operand of this wave's accumulation (A: P, B: dS)
+    f32x4 sacc[2][4];
+    f32x4 st[2];
+    bool diag = false;
+    int hq = s & 1;
+    if (active) {
+      const int it = slot + 4 * (s >> 1);
+      const int i = list[e0 + it / a.G];
+      diag = (i == j);
+      const long long r0 = step_row0(s);
 #pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        sacc[q2][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dpacc[q2][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const bf16x8 kb = *(const bf16x8*)(Ks + (kt * 16 + l16) * KSTR + ks * 32 + g4 * 8);
-        const bf16x8 vb = *(const bf16x8*)(Vs + (kt * 16 + l16) * KSTR + ks * 32 + g4 * 8);
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-          sacc[q2][kt] = mfma16(cur.q[q2][ks], kb, sacc[q2][kt]);
-          dpacc[q2][kt] = mfma16(cur.o[q2][ks], vb, dpacc[q2][kt]);
-        }
-      }
-    // stage Q and dO rows (row-major) for the transposed reads below
-#pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        *(bf16x8*)(xq + (q2 * 16 + l16) * KSTR + ks * 32 + g4 * 8) = cur.q[q2][ks];
-        *(bf16x8*)(xo + (q2 * 16 + l16) * KSTR + ks * 32 + g4 * 8) = cur.o[q2][ks];
-      }
-    // P and dS as B operands (lane: key; rows x/4*16 + g4*4 + x%4)
-    bf16x8 pb[4], dsb[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+      for (int q2 = 0; q2 < 2; ++q2) st[q2] = *(const f32x4*)(stat + r0 + q2 * 16 + g4 * 4);
+      // stage the rows for the partner's transposed reads
+      bf16* xs = role == 0 ? xq : xo;
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          float p = __builtin_amdgcn_exp2f(
-              fmaf(sacc[q2][kt][jj], a.c2, fmaf(-lv[q2][jj], kLog2e, beta)));
-          if (diag && (kt * 16 + l16) > (hq * 32 + q2 * 16 + g4 * 4 + jj)) p = 0.0f;
-          const float ds = p * (dpacc[q2][kt][jj] - dv[q2][jj]);
-          pb[kt][q2 * 4 + jj] = (bf16)p;
-          dsb[kt][q2 * 4 + jj] = (bf16)ds;
+        for (int ks = 0; ks < 4; ++ks)
+          *(bf16x8*)(xs + (q2 * 16 + l16) * KSTR + ks * 32 + g4 * 8) = rows[q2][ks];
+      // A: S = Q K^T   B: dP = dO V^T   (lane: key kt*16 + l16; rows q2*16 + g4*4 + jj)
+      const bf16* T = role == 0 ? Ks : Vs;
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) sacc[q2][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const bf16x8 tb = *(const bf16x8*)(T + (kt * 16 + l16) * KSTR + ks * 32 + g4 * 8);
+#pragma unroll
+          for (int q2 = 0; q2 < 2; ++q2) sacc[q2][kt] = mfma16(rows[q2][ks], tb, sacc[q2][kt]);
         }
+      if (role == 0) {
+        // P = exp2(c2 s + beta - lse2): kept as bf16 B operand (dV) and as
+        // fp32 in LDS for the partner's dS
+        const float beta = diag ? 0.0f : a.lg[(bhk * a.C + i) * a.C + j] * kLog2e;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              float p = __builtin_amdgcn_exp2f(
+                  fmaf(sacc[q2][kt][jj], a.c2, fmaf(-st[q2][jj], kLog2e, beta)));
+              if (diag && (kt * 16 + l16) > (hq * 32 + q2 * 16 + g4 * 4 + jj)) p = 0.0f;
+              bop[kt][q2 * 4 + jj] = (bf16)p;
+              xp[((kt * 2 + q2) * 4 + jj) * 64 + lane] = p;
+            }
+      }
+      if (s + 1 < nsteps) load_rows(s + 1, rows);
     }
-    if (s + 1 < nsteps) load_half(s + 1, nxt);
-    wave_lds_sync();
-    // dV^T += dO^T P, dK^T += Q^T dS; A operands read transposed from the
-    // row-major tiles (ds_read_b64_tr_b16: lane gets 4 consecutive rows of
-    // its column)
+    __syncthreads();   // staged rows and P visible to the partner
+    if (active) {
+      if (role == 1) {
+        // dS = P (dP - Delta), as the B operand of dK^T += Q^T dS
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int roff = (g4 * 4 + (l16 >> 2)) * KSTR + dt * 16 + (l16 & 3) * 4;
-      const bf16x8 oa = join(ds_read_tr(xo + roff), ds_read_tr(xo + roff + 16 * KSTR));
-      const bf16x8 qa = join(ds_read_tr(xq + roff), ds_read_tr(xq + roff + 16 * KSTR));
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        dvacc[dt][kt] = mfma16(oa, pb[kt], dvacc[dt][kt]);
-        dkacc[dt][kt] = mfma16(qa, dsb[kt], dkacc[dt][kt]);
+          for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const float p = xp[((kt * 2 + q2) * 4 + jj) * 64 + lane];
+              bop[kt][q2 * 4 + jj] = (bf16)(p * (sacc[q2][kt][jj] - st[q2][jj]));
+            }
+      }
+      // A: dV^T += dO^T P   B: dK^T += Q^T dS  (A operands: transposed reads of
+      // the partner's staged rows: lane gets 4 consecutive rows of its column)
+      const bf16* xt = role == 0 ? xo : xq;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int ro = (g4 * 4 + (l16 >> 2)) * KSTR + dt * 16 + (l16 & 3) * 4;
+        const bf16x8 ta = join(ds_read_tr(xt + ro), ds_read_tr(xt + ro + 16 * KSTR));
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) acc[dt][kt] = mfma16(ta, bop[kt], acc[dt][kt]);
       }
     }
-    wave_lds_sync();
-  };
-
-  HalfItem cur;
-  if (nsteps > 0) load_half(0, cur);
-  __syncthreads();   // K_j, V_j staged
-#pragma unroll 1
-  for (int s = 0; s < nsteps; ++s) {
-    HalfItem nxt;
-    half_step(s, cur, nxt);
-    cur = nxt;
+    __syncthreads();   // the slot's buffers are free for the next half item
   }
 
-  // add the four wavefronts' partial sums in a fixed order (LDS, fp32); the
-  // 16-byte chunk c of key row r is stored at chunk c ^ (r & 31) so that the
-  // 16 rows written by one instruction spread over the banks
-  __syncthreads();
-  float* redk = (float*)smem;
-  float* redv = redk + 64 * 128;
+  // add the four pairs' partial sums in a fixed order (LDS, fp32); the 16-byte
+  // chunk c of key row r is stored at chunk c ^ (r & 31) so that the 16 rows
+  // written by one instruction spread over the banks
+  float* redv = (float*)smem;      // role 0 accumulates dV
+  float* redk = redv + 64 * 128;   // role 1 accumulates dK
+  float* red = role == 0 ? redv : redk;
   auto roff = [](int r, int d) { return r * 128 + ((((d >> 2) ^ (r & 31))) << 2) + (d & 3); };
   for (int x = 0; x < 4; ++x) {
-    if (w == x) {
+    if (slot == x) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
           const int off = roff(kt * 16 + l16, dt * 16 + g4 * 4);
-          if (x == 0) {
-            *(f32x4*)(redk + off) = dkacc[dt][kt];
-            *(f32x4*)(redv + off) = dvacc[dt][kt];
-          } else {
-            *(f32x4*)(redk + off) += dkacc[dt][kt];
-            *(f32x4*)(redv + off) += dvacc[dt][kt];
-          }
+          if (x == 0) *(f32x4*)(red + off) = acc[dt][kt];
+          else *(f32x4*)(red + off) += acc[dt][kt];
         }
     }
     __syncthreads();
@@ -733,8 +725,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a) {
   const long long orow = bhk * a.N + (long long)j * BLK;
   if (nch == 1) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int e = (tid + r * 256) * 8;   // 8 consecutive elements of key row e / 128
+    for (int r = 0; r < 2; ++r) {
+      const int e = (tid + r * 512) * 8;   // 8 consecutive elements of key row e / 128
       const int kr = e >> 7, d = e & 127;
       const f32x4 k0 = *(const f32x4*)(redk + roff(kr, d));
       const f32x4 k1 = *(const f32x4*)(redk + roff(kr, d + 4));
@@ -755,8 +747,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a) {
     float* pk = a.partial + (long long)g * 2 * 8192;
     float* pv = pk + 8192;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int e = (tid + r * 256) * 4;
+    for (int r = 0; r < 4; ++r) {
+      const int e = (tid + r * 512) * 4;
       const int kr = e >> 7, d = e & 127;
       *(f32x4*)(pk + e) = *(const f32x4*)(redk + roff(kr, d));
       *(f32x4*)(pv + e) = *(const f32x4*)(redv + roff(kr, d));
@@ -885,7 +877,7 @@ hipError_t launch_bwd_dq_mfma(const Shape& s, const BwdPtrs& p, char* ws, const 
 hipError_t launch_bwd_dkdv_mfma(const Shape& s, const BwdPtrs& p, char* ws,
                                 const BwdWorkspace& wl, hipStream_t st) {
   BwdArgs a = make_bwd_args(s, p, ws, wl);
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)wl.max_chunks), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)wl.max_chunks), dim3(512), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)a.ncol), dim3(256), 0, st, a);
