@@ -91,4 +91,83 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + idx;
 }
 
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  typedef __attribute__((address_space(3))) const char* lptr;
+  return (unsigned)(uintptr_t)(lptr)p;
+}
+
+// Batches of transposed LDS reads (ds_read_b64_tr_b16) issued back to back
+// and awaited inside the same asm block.  Written as asm because the
+// compiler, unable to tell these reads apart from the addresses that pending
+// global -> LDS copies write, would otherwise wait for every copy in flight
+// (including the next tile's prefetch) before the first of them.
+typedef uint32_t tr_u32x2 __attribute__((ext_vector_type(2)));
+
+// r[4k + x] = read at a_k + x * 4096 bytes (k = 0, 1; x = 0..3)
+__device__ __forceinline__ void tr_read_2x4(unsigned a0, unsigned a1, tr_u32x2 (&r)[8]) {
+  __asm__ volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %2, %8 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %3, %8 offset:12288\n\t"
+      "ds_read_b64_tr_b16 %4, %9\n\t"
+      "ds_read_b64_tr_b16 %5, %9 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %6, %9 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %7, %9 offset:12288\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a0), "v"(a1)
+      : "memory");
+}
+
+// r[2k + x] = read at a_k + x * 4096 bytes (k = 0..3; x = 0, 1)
+__device__ __forceinline__ void tr_read_4x2(unsigned a0, unsigned a1, unsigned a2, unsigned a3,
+                                            tr_u32x2 (&r)[8]) {
+  __asm__ volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %2, %9\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %4, %10\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %6, %11\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:4096\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+}
+
+// Asynchronous global -> LDS copies (global_load_lds_dword[x4]): every lane
+// copies 4 / 16 bytes from its own global address to lds_base + 4 / 16 * lane
+// (lds_base wave-uniform, in M0).  Issued from asm so that the compiler does
+// not track them: it would otherwise make every later LDS access wait for all
+// copies in flight, prefetches included.  Completion is the caller's: an
+// explicit s_waitcnt vmcnt before the barrier that publishes the data (any
+// vmcnt wait the compiler places for its own loads only waits longer).
+__device__ __forceinline__ void dma16(const void* g, unsigned lds_base) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_base);
+  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                   :: "v"(g), "s"(m0) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, unsigned lds_base) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_base);
+  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                   :: "v"(g), "s"(m0) : "memory", "m0");
+}
+
+// Forces the loads that produced x to complete here (an asm use of x).
+template <typename T>
+__device__ __forceinline__ void settle(const T& x) { __asm__ volatile("" ::"v"(x)); }
+
+__device__ __forceinline__ int lane_value(int v, int lane) {
+  return __builtin_amdgcn_readlane(v, lane);
+}
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
 }  // namespace sas

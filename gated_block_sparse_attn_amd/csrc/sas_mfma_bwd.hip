@@ -52,8 +52,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BLK = 64;
 constexpr int HD = 128;
-constexpr int KSTR = HD + 8;   // bf16 per row of a row-major [key][d] LDS tile
-constexpr int XSTR = 32 + 4;   // bf16 per row of a wave's transposed [d][32 queries] tile
 
 struct BwdArgs {
   const bf16* q; const bf16* k; const bf16* v; const void* o; const bf16* d_o;
@@ -122,13 +120,12 @@ __device__ __forceinline__ int swz(int r, int c) { return r * HD + ((c ^ (r & 15
 // (global_load_lds_dwordx4); completion is awaited with s_waitcnt vmcnt(0).
 template <int NW>
 __device__ __forceinline__ void tile_to_lds(bf16* lds, const bf16* g, int w, int lane) {
-  typedef __attribute__((address_space(3))) void lds_void;
 #pragma unroll
   for (int r = 0; r < 16 / NW; ++r) {
     const int seg = w + NW * r;               // 1 KB segment = rows 4 seg .. 4 seg + 3
     const int row = seg * 4 + (lane >> 4);
     const int c = (lane & 15) ^ (row & 15);
-    __builtin_amdgcn_global_load_lds(g + row * HD + c * 8, (lds_void*)(lds + seg * 512), 16, 0, 0);
+    dma16(g + row * HD + c * 8, lds_addr(lds + seg * 512));
   }
 }
 
@@ -266,27 +263,59 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
             dsb[qt][k2 * 4 + j] = (bf16)ds;
           }
       }
-      // dQ^T += K^T dS^T over these 32 keys (K^T fragments: transposed reads)
+      // dQ^T += K^T dS^T over these 32 keys; K^T fragments are column
+      // fragments (rows kh*32 + {g4*4 .. +3, 16 + g4*4 .. +3}) read transposed,
+      // four head-dim tiles per batch of reads
+      const int kr = kh * 32 + g4 * 4 + (l16 >> 2);
+      const unsigned kbase_l = lds_addr(Ks) + (unsigned)(kr * HD + (l16 & 1) * 4) * 2;
+      auto kaddr = [&](int dt) { return kbase_l + (((dt * 2 + ((l16 >> 1) & 1)) ^ (kr & 15)) << 4); };
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const bf16x8 ka = col_frag(Ks, kh * 32, dt * 16, l16, g4);
+      for (int dq4 = 0; dq4 < 2; ++dq4) {
+        tr_u32x2 r[8];
+        tr_read_4x2(kaddr(dq4 * 4), kaddr(dq4 * 4 + 1), kaddr(dq4 * 4 + 2), kaddr(dq4 * 4 + 3), r);
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) dqacc[dt][qt] = mfma16(ka, dsb[qt], dqacc[dt][qt]);
+        for (int d4 = 0; d4 < 4; ++d4) {
+          const int dt = dq4 * 4 + d4;
+          const tr_u32x2 lo = r[d4 * 2], hi = r[d4 * 2 + 1];
+          const bf16x8 ka = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) dqacc[dt][qt] = mfma16(ka, dsb[qt], dqacc[dt][qt]);
+        }
       }
     }
     return tsum;
   };
 
+  // the row's selection, 64 entries at a time, in registers (lane e: block
+  // sel[e0 + e] and its log gate in log2 units), read with readlane
+  int selv = 0;
+  float betav = 0.0f;
+  auto load_sel = [&](int e0) {
+    const int e = e0 + lane;
+    selv = e < cnt ? sel[e] : 0;
+    betav = e < cnt ? lgrow[selv] * kLog2e : 0.0f;
+    settle(betav);
+  };
+  load_sel(0);
+
   wait_vm();
   __syncthreads();
-  if (ntiles > 1) load_tile(sel[0], 1);
+  float nbeta = 0.0f;   // log gate of the tile in the other stage
+  if (ntiles > 1) {
+    load_tile(lane_value(selv, 0), 1);
+    nbeta = lane_value(betav, 0);
+  }
   tile(std::true_type{}, 0, 0.0f);   // diagonal: no gate gradient
   wait_vm();
   __syncthreads();
   for (int t = 1; t < ntiles; ++t) {
     const int stg = t & 1;
-    const float beta = lgrow[sel[t - 1]] * kLog2e;
-    if (t + 1 < ntiles) load_tile(sel[t], stg ^ 1);
+    const float beta = nbeta;
+    if (t + 1 < ntiles) {   // entry t of the selection feeds tile t + 1
+      if ((t & 63) == 0) load_sel(t);
+      load_tile(lane_value(selv, t & 63), stg ^ 1);
+      nbeta = lane_value(betav, t & 63);
+    }
     float tsum = tile(std::false_type{}, stg, beta);
     tsum = wave_sum(tsum);
     if (lane == 0) s_red[t & 1][w] = tsum;
@@ -521,238 +550,346 @@ __global__ void chunk_scatter_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // key-major pass: dK, dV
 // ---------------------------------------------------------------------------
-// One workgroup per column chunk (key block j, up to kColChunk query blocks).
-// Eight wavefronts = four pairs; pair `slot` streams the (query block, head)
-// items slot, slot + 4, ... in two halves of 32 query rows, and the two
-// wavefronts of a pair split the work by tensor:
-//   wave A (role 0): S = Q K^T -> P, and dV^T += dO^T P   (dV accumulator)
+// One workgroup = one wavefront pair = one column chunk (key block j, up to
+// kColChunk query blocks).  The pair streams the chunk's (query block, head)
+// items in steps of 32 query rows and splits the work by tensor:
+//   wave A (role 0): S = Q K^T -> P, and dV^T += dO^T P   (K_j in registers)
 //   wave B (role 1): dP = dO V^T -> dS = P (dP - Delta), dK^T += Q^T dS
-// Each wavefront holds one 64 x 128 fp32 accumulator (128 registers), so two
-// wavefronts fit per SIMD and every matrix product is computed once.  Per
-// half item, A stages its Q rows and P in LDS, B stages its dO rows; the
-// transposed operands Q^T / dO^T come from ds_read_b64_tr_b16 reads of the
-// staged rows.  The four pairs advance in lockstep (two workgroup barriers
-// per half item).
-constexpr int KV_TILE_BYTES = BLK * KSTR * 2;                  // 17408 (padded rows)
-constexpr int XH_BYTES = 32 * KSTR * 2;                          // 8704: 32 staged rows
-constexpr int XP_BYTES = 32 * 64 * 4;                            // 8192: P, [value][lane]
-constexpr int SLOT_BYTES = 2 * XH_BYTES + XP_BYTES;              // 25600
-constexpr int DKDV_LDS = 2 * KV_TILE_BYTES + 4 * SLOT_BYTES;     // 137216
-static_assert(DKDV_LDS >= 2 * 64 * 128 * 4, "reduction buffer must fit");
+//                    (V_j in registers)
+// Every product is a 32x32x16 MFMA, which a single wavefront issues at the
+// full matrix rate; one wavefront runs per SIMD (about 300 registers).
+//
+// The rows and row statistics of each step reach LDS by asynchronous
+// global -> LDS copies (A copies Q and LSE, B copies dO and Delta) into a ring
+// of four buffers, two steps ahead.  Window s (between the pair's barriers
+// s - 1 and s) holds: A: S_s, P_s, dV_s;  B: dP_s, dS_{s-1}, dK_{s-1}.  A
+// publishes P_s (fp16) at barrier s; step t's buffer is copied during window
+// t - 2, awaited before barrier t - 1 and last read in window t + 1.
+//
+// 32x32x16 operand layouts (lane l, g = l / 32):
+//   A: row l % 32, k = 8 g .. 8 g + 7;   B: column l % 32, same k;
+//   C: column l % 32, rows 8 (jj / 4) + 4 g + jj % 4 for jj = 0..15.
+// The C fragment of S (rows x keys) feeds the B operand of the row
+// contraction directly: its elements 8 sl .. 8 sl + 7 are rows
+// 16 sl + {4 g .. 4 g + 3, 8 + 4 g .. 8 + 4 g + 3}, and the transposed reads of
+// the staged rows use the same row order.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-__global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[DKDV_LDS];
-  bf16* Ks = (bf16*)smem;
-  bf16* Vs = (bf16*)(smem + KV_TILE_BYTES);
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+constexpr int KV_NBUF = 4;
+constexpr int XS_BYTES = 32 * HD * 2;                          // 32 staged rows
+constexpr int RING_BYTES = 2 * XS_BYTES + 2 * 256;             // Q, dO, LSE, Delta
+constexpr int PX_BYTES = 64 * 32 * 2;                          // P of one step (fp16)
+constexpr int KV_LDS = KV_NBUF * RING_BYTES + 2 * PX_BYTES + 2 * kColChunk * 4;
+
+// Element offset of 16-byte chunk c of row r in a staged 32 x 128 tile.  The
+// chunk is stored at c ^ f(r), f(r) = 2 (r & 3) + ((r >> 2) & 1): the eight
+// rows read by one 8-lane phase of a 16-byte access hit eight different
+// slots, and the four rows x 32 bytes of one 16-lane transposed read as well.
+__device__ __forceinline__ int xsw(int r, int c) {
+  return r * HD + ((c ^ (((r & 3) << 1) | ((r >> 2) & 1))) << 3);
+}
+
+// Pair barrier: this wavefront's LDS accesses and all but its newest nine
+// global -> LDS copies are complete, then s_barrier.  (__syncthreads would
+// also wait for the newest copies, which are meant to stay in flight.)
+__device__ __forceinline__ void ring_barrier() {
+  __asm__ volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The eight transposed A-operand fragments (dt = 0..3, sl = 0..1) of one
+// staged 32 x 128 tile: 16 ds_read_b64_tr_b16 in flight, awaited inside the
+// same asm block.  p0 / p1: this lane's addresses of the dt = 0 / dt = 1
+// fragments (sl = 0, first four rows); dt + 2 adds 128 bytes, sl 4096 and the
+// second four rows 2048.
+__device__ __forceinline__ void tr_tile(const bf16* p0, const bf16* p1, bf16x8 (&t)[4][2]) {
+  typedef __attribute__((address_space(3))) const char* lptr;
+  const unsigned a0 = (unsigned)(uintptr_t)(lptr)p0;
+  const unsigned a1 = (unsigned)(uintptr_t)(lptr)p1;
+  u32x2 r[16];
+  __asm__ volatile(
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %2, %16 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %3, %16 offset:6144\n\t"
+      "ds_read_b64_tr_b16 %4, %17\n\t"
+      "ds_read_b64_tr_b16 %5, %17 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %6, %17 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %7, %17 offset:6144\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:128\n\t"
+      "ds_read_b64_tr_b16 %9, %16 offset:2176\n\t"
+      "ds_read_b64_tr_b16 %10, %16 offset:4224\n\t"
+      "ds_read_b64_tr_b16 %11, %16 offset:6272\n\t"
+      "ds_read_b64_tr_b16 %12, %17 offset:128\n\t"
+      "ds_read_b64_tr_b16 %13, %17 offset:2176\n\t"
+      "ds_read_b64_tr_b16 %14, %17 offset:4224\n\t"
+      "ds_read_b64_tr_b16 %15, %17 offset:6272\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
+        "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+      : "v"(a0), "v"(a1)
+      : "memory");
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const int k = (dt >> 1) * 8 + (dt & 1) * 4 + sl * 2;
+      const u32x4 w = u32x4{r[k][0], r[k][1], r[k + 1][0], r[k + 1][1]};
+      t[dt][sl] = __builtin_bit_cast(bf16x8, w);
+    }
+}
+
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1)))
+bwd_dkdv_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[KV_LDS];
+  int32_t* itab = (int32_t*)(smem + KV_NBUF * RING_BYTES + 2 * PX_BYTES);   // query block per entry
+  float* btab = (float*)(itab + kColChunk);                                 // its log gate (log2 units)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int role = w >> 2;   // 0: S / P / dV, 1: dP / dS / dK
-  const int slot = w & 3;
-  const int l16 = lane & 15;
-  const int g4 = lane >> 4;
-  char* sbase = smem + 2 * KV_TILE_BYTES + slot * SLOT_BYTES;
-  bf16* xq = (bf16*)sbase;                    // Q rows of the slot's half item
-  bf16* xo = (bf16*)(sbase + XH_BYTES);       // dO rows
-  float* xp = (float*)(sbase + 2 * XH_BYTES);  // P (fp32), [value index][lane]
+  const int role = tid >> 6;   // 0: S / P / dV, 1: dP / dS / dK
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
 
-  const int sid = xcd_remap(blockIdx.x, gridDim.x);
+  // the grid is sized for the most chunks a selection can produce; the first
+  // `total` workgroups take the chunks, spread evenly over the XCDs
   const int total = a.chunkoff[a.ncol];
-  if (sid >= total) return;
-  const int g = a.chunk_order[sid];
-  const long long col = chunk_column(a, g);
-  const int c = g - a.chunkoff[col];
+  if ((int)blockIdx.x >= total) return;
+  const int gch = a.chunk_order[xcd_remap(blockIdx.x, total)];
+  const long long col = chunk_column(a, gch);
+  const int c = gch - a.chunkoff[col];
   const int nch = a.chunkoff[col + 1] - a.chunkoff[col];
   const int L = a.collen[col];
   const int e0 = c * kColChunk;
-  const int e1 = min(L, e0 + kColChunk);
-  const int32_t* list = a.collist + a.coloff[col];
+  const int ne = min(L, e0 + kColChunk) - e0;
   const int j = (int)(col % a.C);
   const long long bhk = col / a.C;
   const int hk = (int)(bhk % a.Hkv);
   const int bb = (int)(bhk / a.Hkv);
+  const int G = a.G;
 
-  {  // stage K_j, V_j (row-major, padded rows)
-    const bf16* kt = a.k + (bhk * a.N + (long long)j * BLK) * HD;
-    const bf16* vt = a.v + (bhk * a.N + (long long)j * BLK) * HD;
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int cc = tid + r * 512;
-      *(u32x4*)(&Ks[(cc >> 4) * KSTR + (cc & 15) * 8]) = *(const u32x4*)(kt + (cc >> 4) * HD + (cc & 15) * 8);
-      *(u32x4*)(&Vs[(cc >> 4) * KSTR + (cc & 15) * 8]) = *(const u32x4*)(vt + (cc >> 4) * HD + (cc & 15) * 8);
-    }
+  if (tid < ne) {
+    const int i = a.collist[a.coloff[col] + e0 + tid];
+    itab[tid] = i;
+    btab[tid] = i == j ? 0.0f : a.lg[(bhk * a.C + i) * a.C + j] * kLog2e;
   }
 
-  const int nitems = (e1 - e0) * a.G;
-  const int myitems = slot < nitems ? (nitems - slot + 3) / 4 : 0;
-  const int nsteps = 2 * myitems;            // this pair's half items
-  const int lockstep = 2 * ((nitems + 3) / 4);   // half items of the busiest pair
+  // resident B operand of S (A: K_j) or dP (B: V_j): key kt*32 + l32,
+  // dims ds*16 + g*8 .. +7
+  bf16x8 kf[2][8];
+  {
+    const bf16* t = (role == 0 ? a.k : a.v) + (bhk * a.N + (long long)j * BLK) * HD;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ds = 0; ds < 8; ++ds)
+        kf[kt][ds] = *(const bf16x8*)(t + (kt * 32 + l32) * HD + ds * 16 + g * 8);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ds = 0; ds < 8; ++ds) settle(kf[kt][ds]);   // complete before the loop
+  }
+  __syncthreads();   // item table
 
-  // first query row of half item s of this pair
-  auto step_row0 = [&](int s) -> long long {
-    const int it = slot + 4 * (s >> 1);
-    const int i = list[e0 + it / a.G];
-    const int h = hk * a.G + it % a.G;
-    return ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + (s & 1) * 32;
-  };
-  // A loads Q rows, B loads dO rows (lane: row q2*16 + l16, dims ks*32 + g4*8 .. +7)
+  const int nsteps = 2 * ne * G;
   const bf16* src = role == 0 ? a.q : a.d_o;
-  auto load_rows = [&](int s, bf16x8 (&rw)[2][4]) {
-    const long long r0 = step_row0(s);
-#pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        rw[q2][ks] = *(const bf16x8*)(src + (r0 + q2 * 16 + l16) * HD + ks * 32 + g4 * 8);
-  };
-  // A: LSE (log2 units folded later), B: Delta, of this lane's accumulator rows
   const float* stat = role == 0 ? a.lse : a.delta;
-
-  f32x4 acc[8][4];   // A: dV^T, B: dK^T  (lane: key kt*16 + l16, dims dt*16 + g4*4 .. +3)
+  // copy step t's rows (32 x 128) and statistics into ring buffer t % 4;
+  // steps past the end recopy the last step (same buffer rule, never read)
+  auto copy_step = [&](int t) {
+    const int tc = min(t, nsteps - 1);
+    const int it = tc >> 1;
+    const int e = it / G;
+    const long long r0 = ((long long)bb * a.Hq + hk * G + (it - e * G)) * a.N +
+                         (long long)itab[e] * BLK + (tc & 1) * 32;
+    char* rb = smem + (t & 3) * RING_BYTES;
+    char* xs = rb + role * XS_BYTES;
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) acc[dt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < 8; ++q) {   // 1 KB = rows 4q .. 4q + 3; lane -> (row, slot)
+      const int row = q * 4 + (lane >> 4);
+      const int ch = (lane & 15) ^ (((row & 3) << 1) | ((row >> 2) & 1));
+      dma16(src + (r0 + row) * HD + ch * 8, lds_addr(xs + q * 1024));
+    }
+    dma4(stat + r0 + l32, lds_addr(rb + 2 * XS_BYTES + role * 256));
+  };
 
-  bf16x8 rows[2][4];
-  if (nsteps > 0) load_rows(0, rows);
-  __syncthreads();   // K_j, V_j staged
+  f32x16 acc[4][2];   // A: dV^T, B: dK^T; lane: key kt*32 + l32, dims dt*32 + 8 (jj/4) + 4 g + jj%4
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) acc[dt][kt][x] = 0.0f;
+
+  const int u = lane & 15;
+  const int dhalf = (lane >> 4) & 1;
+  // A operands of the row contraction: transposed reads of staged tile xs
+  // (lane: column dt*32 + l32, rows sl*16 + {4g..4g+3, 8+4g..8+4g+3})
+  const int tr_r = g * 4 + (u >> 2);
+  const int tr_e = (u & 1) * 4;
+  const int tr0 = xsw(tr_r, dhalf * 2 + ((u >> 1) & 1)) + tr_e;       // dt = 0
+  const int tr1 = xsw(tr_r, 4 + dhalf * 2 + ((u >> 1) & 1)) + tr_e;   // dt = 1
+  auto row_contract = [&](const bf16* xs, const bf16x8 (&bop)[2][2]) {
+    bf16x8 ta[4][2];
+    tr_tile(xs + tr0, xs + tr1, ta);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) acc[dt][kt] = mfma32(ta[dt][sl], bop[kt][sl], acc[dt][kt]);
+  };
+  // this lane's 16 C-row statistics (rows 8t + 4g + u)
+  auto read_stat = [&](const char* rb, float (&st)[16]) {
+    const float* sp = (const float*)(rb + 2 * XS_BYTES + role * 256);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const f32x4 v = *(const f32x4*)(sp + t * 8 + g * 4);
+#pragma unroll
+      for (int y = 0; y < 4; ++y) st[t * 4 + y] = v[y];
+    }
+  };
+  // rows x keys product with the resident operand: A: S, B: dP
+  auto rows_product = [&](const char* rb, f32x16 (&sc)[2]) {
+    const bf16* xs = (const bf16*)(rb + role * XS_BYTES);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) sc[kt][x] = 0.0f;
+    bf16x8 qa[8];
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) qa[ds] = *(const bf16x8*)(xs + xsw(l32, ds * 2 + g));
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) sc[kt] = mfma32(qa[ds], kf[kt][ds], sc[kt]);
+  };
+
+  copy_step(0);
+  copy_step(1);
+  ring_barrier();   // step 0 staged
+
+  f32x16 dp0[2], dp1[2];   // B: dP of the previous and current step
+  auto window = [&](int s, f32x16 (&dprev)[2], f32x16 (&dcur)[2]) {
+    copy_step(s + 2);
+    const char* rb = smem + (s & 3) * RING_BYTES;
+    if (role == 0) {
+      // S_s, P_s (published for B, fp16), dV_s += dO_s^T P_s
+      f32x16 sc[2];
+      rows_product(rb, sc);
+      float st[16];
+      read_stat(rb, st);
+      const int ent = (s >> 1) / G;
+      const float beta = btab[ent];
+      const bool diag = itab[ent] == j;
+      const int hrow = (s & 1) * 32;
+      _Float16* px = (_Float16*)(smem + KV_NBUF * RING_BYTES + (s & 1) * PX_BYTES);
+      bf16x8 bop[2][2];
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) st[jj] = fmaf(-st[jj], kLog2e, beta);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x16 p;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) p[jj] = __builtin_amdgcn_exp2f(fmaf(sc[kt][jj], a.c2, st[jj]));
+        if (diag) {
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj)
+            if (kt * 32 + l32 > hrow + (jj >> 2) * 8 + g * 4 + (jj & 3)) p[jj] = 0.0f;
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          f16x8 ph;
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            ph[x] = (_Float16)p[h2 * 8 + x];
+            bop[kt][h2][x] = (bf16)p[h2 * 8 + x];
+          }
+          *(f16x8*)(px + ((kt * 2 + h2) * 64 + lane) * 8) = ph;
+        }
+      }
+      row_contract((const bf16*)(rb + XS_BYTES), bop);
+    } else {
+      // dP_s; then dS_{s-1} = P_{s-1} (dP_{s-1} - Delta) and dK_{s-1} += Q^T dS
+      rows_product(rb, dcur);
+      if (s > 0) {
+        const char* rp = smem + ((s - 1) & 3) * RING_BYTES;
+        float st[16];
+        read_stat(rp, st);
+        const _Float16* px = (const _Float16*)(smem + KV_NBUF * RING_BYTES + ((s - 1) & 1) * PX_BYTES);
+        bf16x8 bop[2][2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const f16x8 ph = *(const f16x8*)(px + ((kt * 2 + h2) * 64 + lane) * 8);
+#pragma unroll
+            for (int x = 0; x < 8; ++x)
+              bop[kt][h2][x] = (bf16)((float)ph[x] * (dprev[kt][h2 * 8 + x] - st[h2 * 8 + x]));
+          }
+        row_contract((const bf16*)rp, bop);
+      }
+    }
+    ring_barrier();   // P_s published; step s + 1 staged
+  };
 
 #pragma unroll 1
-  for (int s = 0; s < lockstep; ++s) {
-    const bool active = s < nsteps;
-    bf16x8 bop[4];   // B operand of this wave's accumulation (A: P, B: dS)
-    f32x4 sacc[2][4];
-    f32x4 st[2];
-    bool diag = false;
-    int hq = s & 1;
-    if (active) {
-      const int it = slot + 4 * (s >> 1);
-      const int i = list[e0 + it / a.G];
-      diag = (i == j);
-      const long long r0 = step_row0(s);
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) st[q2] = *(const f32x4*)(stat + r0 + q2 * 16 + g4 * 4);
-      // stage the rows for the partner's transposed reads
-      bf16* xs = role == 0 ? xq : xo;
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          *(bf16x8*)(xs + (q2 * 16 + l16) * KSTR + ks * 32 + g4 * 8) = rows[q2][ks];
-      // A: S = Q K^T   B: dP = dO V^T   (lane: key kt*16 + l16; rows q2*16 + g4*4 + jj)
-      const bf16* T = role == 0 ? Ks : Vs;
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) sacc[q2][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const bf16x8 tb = *(const bf16x8*)(T + (kt * 16 + l16) * KSTR + ks * 32 + g4 * 8);
-#pragma unroll
-          for (int q2 = 0; q2 < 2; ++q2) sacc[q2][kt] = mfma16(rows[q2][ks], tb, sacc[q2][kt]);
-        }
-      if (role == 0) {
-        // P = exp2(c2 s + beta - lse2): kept as bf16 B operand (dV) and as
-        // fp32 in LDS for the partner's dS
-        const float beta = diag ? 0.0f : a.lg[(bhk * a.C + i) * a.C + j] * kLog2e;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              float p = __builtin_amdgcn_exp2f(
-                  fmaf(sacc[q2][kt][jj], a.c2, fmaf(-st[q2][jj], kLog2e, beta)));
-              if (diag && (kt * 16 + l16) > (hq * 32 + q2 * 16 + g4 * 4 + jj)) p = 0.0f;
-              bop[kt][q2 * 4 + jj] = (bf16)p;
-              xp[((kt * 2 + q2) * 4 + jj) * 64 + lane] = p;
-            }
-      }
-      if (s + 1 < nsteps) load_rows(s + 1, rows);
-    }
-    __syncthreads();   // staged rows and P visible to the partner
-    if (active) {
-      if (role == 1) {
-        // dS = P (dP - Delta), as the B operand of dK^T += Q^T dS
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const float p = xp[((kt * 2 + q2) * 4 + jj) * 64 + lane];
-              bop[kt][q2 * 4 + jj] = (bf16)(p * (sacc[q2][kt][jj] - st[q2][jj]));
-            }
-      }
-      // A: dV^T += dO^T P   B: dK^T += Q^T dS  (A operands: transposed reads of
-      // the partner's staged rows: lane gets 4 consecutive rows of its column)
-      const bf16* xt = role == 0 ? xo : xq;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const int ro = (g4 * 4 + (l16 >> 2)) * KSTR + dt * 16 + (l16 & 3) * 4;
-        const bf16x8 ta = join(ds_read_tr(xt + ro), ds_read_tr(xt + ro + 16 * KSTR));
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) acc[dt][kt] = mfma16(ta, bop[kt], acc[dt][kt]);
-      }
-    }
-    __syncthreads();   // the slot's buffers are free for the next half item
+  for (int s = 0; s < nsteps; s += 2) {   // nsteps is even
+    window(s, dp1, dp0);
+    window(s + 1, dp0, dp1);
   }
+  if (role == 1) {   // dS and dK of the last step
+    const int s = nsteps;
+    const char* rp = smem + ((s - 1) & 3) * RING_BYTES;
+    float st[16];
+    read_stat(rp, st);
+    const _Float16* px = (const _Float16*)(smem + KV_NBUF * RING_BYTES + ((s - 1) & 1) * PX_BYTES);
+    bf16x8 bop[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const f16x8 ph = *(const f16x8*)(px + ((kt * 2 + h2) * 64 + lane) * 8);
+#pragma unroll
+        for (int x = 0; x < 8; ++x)
+          bop[kt][h2][x] = (bf16)((float)ph[x] * (dp1[kt][h2 * 8 + x] - st[h2 * 8 + x]));
+      }
+    row_contract((const bf16*)rp, bop);
+  }
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the trailing copies
 
-  // add the four pairs' partial sums in a fixed order (LDS, fp32); the 16-byte
-  // chunk c of key row r is stored at chunk c ^ (r & 31) so that the 16 rows
-  // written by one instruction spread over the banks
-  float* redv = (float*)smem;      // role 0 accumulates dV
-  float* redk = redv + 64 * 128;   // role 1 accumulates dK
-  float* red = role == 0 ? redv : redk;
-  auto roff = [](int r, int d) { return r * 128 + ((((d >> 2) ^ (r & 31))) << 2) + (d & 3); };
-  for (int x = 0; x < 4; ++x) {
-    if (slot == x) {
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const int off = roff(kt * 16 + l16, dt * 16 + g4 * 4);
-          if (x == 0) *(f32x4*)(red + off) = acc[dt][kt];
-          else *(f32x4*)(red + off) += acc[dt][kt];
-        }
-    }
-    __syncthreads();
-  }
+  // epilogue: A writes dV, B writes dK (times the softmax scale)
   const long long orow = bhk * a.N + (long long)j * BLK;
+  const float mul = role == 0 ? 1.0f : a.scale;
   if (nch == 1) {
+    bf16* dst = role == 0 ? a.dv : a.dk;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int e = (tid + r * 512) * 8;   // 8 consecutive elements of key row e / 128
-      const int kr = e >> 7, d = e & 127;
-      const f32x4 k0 = *(const f32x4*)(redk + roff(kr, d));
-      const f32x4 k1 = *(const f32x4*)(redk + roff(kr, d + 4));
-      const f32x4 v0 = *(const f32x4*)(redv + roff(kr, d));
-      const f32x4 v1 = *(const f32x4*)(redv + roff(kr, d + 4));
-      bf16x8 ok, ov;
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        ok[x] = (bf16)(k0[x] * a.scale);
-        ok[x + 4] = (bf16)(k1[x] * a.scale);
-        ov[x] = (bf16)v0[x];
-        ov[x + 4] = (bf16)v1[x];
-      }
-      *(bf16x8*)(a.dk + orow * HD + e) = ok;
-      *(bf16x8*)(a.dv + orow * HD + e) = ov;
-    }
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          bf16x4 o;
+#pragma unroll
+          for (int y = 0; y < 4; ++y) o[y] = (bf16)(acc[dt][kt][q4 * 4 + y] * mul);
+          *(bf16x4*)(dst + (orow + kt * 32 + l32) * HD + dt * 32 + q4 * 8 + g * 4) = o;
+        }
   } else {
-    float* pk = a.partial + (long long)g * 2 * 8192;
-    float* pv = pk + 8192;
+    float* dst = a.partial + (long long)gch * 2 * 8192 + (role == 0 ? 8192 : 0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int e = (tid + r * 512) * 4;
-      const int kr = e >> 7, d = e & 127;
-      *(f32x4*)(pk + e) = *(const f32x4*)(redk + roff(kr, d));
-      *(f32x4*)(pv + e) = *(const f32x4*)(redv + roff(kr, d));
-    }
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *(f32x4*)(dst + (kt * 32 + l32) * HD + dt * 32 + q4 * 8 + g * 4) =
+              f32x4{acc[dt][kt][q4 * 4] * mul, acc[dt][kt][q4 * 4 + 1] * mul,
+                    acc[dt][kt][q4 * 4 + 2] * mul, acc[dt][kt][q4 * 4 + 3] * mul};
   }
 }
 
@@ -778,7 +915,7 @@ __global__ void __launch_bounds__(256) reduce_kernel(BwdArgs a) {
     bf16x8 ok, ov;
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
-      ok[x] = (bf16)(sk[x] * a.scale);
+      ok[x] = (bf16)sk[x];
       ov[x] = (bf16)sv[x];
     }
     *(bf16x8*)(a.dk + orow * HD + e) = ok;
@@ -877,7 +1014,7 @@ hipError_t launch_bwd_dq_mfma(const Shape& s, const BwdPtrs& p, char* ws, const 
 hipError_t launch_bwd_dkdv_mfma(const Shape& s, const BwdPtrs& p, char* ws,
                                 const BwdWorkspace& wl, hipStream_t st) {
   BwdArgs a = make_bwd_args(s, p, ws, wl);
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)wl.max_chunks), dim3(512), 0, st, a);
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)wl.max_chunks), dim3(128), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)a.ncol), dim3(256), 0, st, a);

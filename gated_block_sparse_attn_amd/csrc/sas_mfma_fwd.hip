@@ -110,7 +110,7 @@ __device__ __forceinline__ void tile_to_lds(bf16* lds, const bf16* g, int w, int
     const int seg = w + NW * r;               // 1 KB segment = rows 4 seg .. 4 seg + 3
     const int row = seg * 4 + (lane >> 4);
     const int c = (lane & 15) ^ (row & 15);
-    __builtin_amdgcn_global_load_lds(g + row * HD + c * 8, (lds_void*)(lds + seg * 512), 16, 0, 0);
+    dma16(g + row * HD + c * 8, lds_addr(lds + seg * 512));
   }
 }
 
@@ -252,40 +252,69 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
         }
       lrow[qt] += ps;
     }
-    // O^T += V^T P^T; V^T fragments read transposed from the row-major tile
+    // O^T += V^T P^T; V^T fragments read transposed from the row-major tile:
+    // for head-dim tile dt, rows vr + {0, 16, 32, 48} of column dt*16 + l16
+    // (the swizzle slot depends only on the row mod 16, so the four reads are
+    // 4 KB apart)
+    const int vr = g4 * 4 + (l16 >> 2);
+    const unsigned vbase = lds_addr(Vs) + (unsigned)(vr * HD + (l16 & 1) * 4) * 2;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
+    for (int dp = 0; dp < 4; ++dp) {   // two head-dim tiles per batch of reads
+      tr_u32x2 r[8];
+      tr_read_2x4(vbase + (((dp * 4 + ((l16 >> 1) & 1)) ^ (vr & 15)) << 4),
+                  vbase + (((dp * 4 + 2 + ((l16 >> 1) & 1)) ^ (vr & 15)) << 4), r);
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const int vr = k2 * 32 + g4 * 4 + (l16 >> 2);
-        const int vc = dt * 2 + ((l16 >> 1) & 1);
-        const int ve = (l16 & 1) * 4;
-        const bf16x8 va = __builtin_shufflevector(ds_read_tr(Vs + swz(vr, vc) + ve),
-                                                  ds_read_tr(Vs + swz(vr + 16, vc) + ve),
-                                                  0, 1, 2, 3, 4, 5, 6, 7);
+      for (int d2 = 0; d2 < 2; ++d2) {
+        const int dt = dp * 2 + d2;
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          oacc[dt][qt] = mfma16(va, pb[k2][qt], oacc[dt][qt]);
-          if (SPLIT) oacc[dt][qt] = mfma16(va, pl[k2][qt], oacc[dt][qt]);
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const tr_u32x2 lo = r[d2 * 4 + k2 * 2], hi = r[d2 * 4 + k2 * 2 + 1];
+          const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) {
+            oacc[dt][qt] = mfma16(va, pb[k2][qt], oacc[dt][qt]);
+            if (SPLIT) oacc[dt][qt] = mfma16(va, pl[k2][qt], oacc[dt][qt]);
+          }
         }
       }
     }
   };
 
+  // The row's selection, 64 entries at a time, in registers: lane e holds
+  // block sel[e0 + e] and its log gate (log2 units); the tile loop reads them
+  // with readlane, so it issues no global loads besides the tile copies.
+  int selv = 0;
+  float betav = 0.0f;
+  auto load_sel = [&](int e0) {
+    const int e = e0 + lane;
+    selv = e < cnt ? sel[e] : 0;
+    betav = e < cnt ? lgrow[selv] * kLog2e : 0.0f;
+    settle(betav);
+  };
+
   const int ntiles = cnt + 1;
+  load_sel(0);
   load_tile(i, 0);
   wait_vm();
   __syncthreads();
   // diagonal tile (unit gate, causal); the next tile streams into the other stage
-  if (ntiles > 1) load_tile(sel[0], 1);
+  float nbeta = 0.0f;   // log gate of the tile in the other stage
+  if (ntiles > 1) {
+    load_tile(lane_value(selv, 0), 1);
+    nbeta = lane_value(betav, 0);
+  }
   tile(std::true_type{}, 0, 0.0f);
   wait_vm();
   __syncthreads();
   // selected tiles (additive log gate)
   for (int t = 1; t < ntiles; ++t) {
     const int stg = t & 1;
-    const float beta = lgrow[sel[t - 1]] * kLog2e;
-    if (t + 1 < ntiles) load_tile(sel[t], stg ^ 1);
+    const float beta = nbeta;
+    if (t + 1 < ntiles) {   // entry t of the selection feeds tile t + 1
+      if ((t & 63) == 0) load_sel(t);
+      load_tile(lane_value(selv, t & 63), stg ^ 1);
+      nbeta = lane_value(betav, t & 63);
+    }
     tile(std::false_type{}, stg, beta);
     wait_vm();
     __syncthreads();
