@@ -91,6 +91,15 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + idx;
 }
 
+// Swizzle of the 16-byte chunks of a row-major LDS tile with 256-byte rows:
+// chunk c of row r is stored in slot c ^ slot16(r).  gfx950's LDS has 64
+// banks; a 16-byte read is served 16 lanes (256 bytes) at a time and an
+// 8-byte or transposed read 16 lanes (128 bytes) at a time.  slot16 permutes
+// the low four bits of r, so (a) sixteen consecutive rows read at one chunk
+// hit sixteen different slots, and (b) the four rows of an aligned group,
+// read as 32-byte chunk pairs by a transposed read, hit four different pairs.
+__device__ __forceinline__ int slot16(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
+
 // LDS byte address of a pointer into __shared__ memory.
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   typedef __attribute__((address_space(3))) const char* lptr;
@@ -157,6 +166,25 @@ __device__ __forceinline__ void dma4(const void* g, unsigned lds_base) {
   const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_base);
   __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                    :: "v"(g), "s"(m0) : "memory", "m0");
+}
+
+// Same copies with a wave-uniform 64-bit base (SGPRs) and a per-lane 32-bit
+// byte offset: the address arithmetic stays in scalar registers.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void dma16s(const void* base, unsigned voff, unsigned lds_base) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_base);
+  __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                   :: "v"(voff), "s"(uniform_ptr(base)), "s"(m0) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4s(const void* base, unsigned voff, unsigned lds_base) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_base);
+  __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                   :: "v"(voff), "s"(uniform_ptr(base)), "s"(m0) : "memory", "m0");
 }
 
 // Forces the loads that produced x to complete here (an asm use of x).

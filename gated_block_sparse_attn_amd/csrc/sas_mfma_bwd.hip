@@ -114,7 +114,7 @@ constexpr int TILE = BLK * HD;   // bf16 elements of one 64 x 128 tile
 // LDS tiles are row-major with 256-byte rows and no padding; the 16-byte chunk
 // c of row r sits in slot c ^ (r & 15), so the 16 rows read by a lane group
 // for one chunk land in 16 different slots (all banks).
-__device__ __forceinline__ int swz(int r, int c) { return r * HD + ((c ^ (r & 15)) << 3); }
+__device__ __forceinline__ int swz(int r, int c) { return r * HD + ((c ^ slot16(r)) << 3); }
 
 // Asynchronous global -> LDS copy of one 64 x 128 tile by NW wavefronts
 // (global_load_lds_dwordx4); completion is awaited with s_waitcnt vmcnt(0).
@@ -124,21 +124,12 @@ __device__ __forceinline__ void tile_to_lds(bf16* lds, const bf16* g, int w, int
   for (int r = 0; r < 16 / NW; ++r) {
     const int seg = w + NW * r;               // 1 KB segment = rows 4 seg .. 4 seg + 3
     const int row = seg * 4 + (lane >> 4);
-    const int c = (lane & 15) ^ (row & 15);
+    const int c = (lane & 15) ^ slot16(row);
     dma16(g + row * HD + c * 8, lds_addr(lds + seg * 512));
   }
 }
 
 __device__ __forceinline__ void wait_vm() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// A column fragment (8 rows r0 + {g4*4 .. +3, 16 + g4*4 .. +3} of column
-// c0 + l16) of a swizzled row-major tile, via two transposed reads.
-__device__ __forceinline__ bf16x8 col_frag(const bf16* t, int r0, int c0, int l16, int g4) {
-  const int r = r0 + g4 * 4 + (l16 >> 2);
-  const int c = (c0 >> 3) + ((l16 >> 1) & 1);
-  const int e = (c0 & 7) + (l16 & 1) * 4;
-  return join(ds_read_tr(t + swz(r, c) + e), ds_read_tr(t + swz(r + 16, c) + e));
-}
 
 // One workgroup = NH query heads of one (batch, kv head, query block); two
 // wavefronts per head, each owning 32 of the 64 query rows.
@@ -268,7 +259,7 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
       // four head-dim tiles per batch of reads
       const int kr = kh * 32 + g4 * 4 + (l16 >> 2);
       const unsigned kbase_l = lds_addr(Ks) + (unsigned)(kr * HD + (l16 & 1) * 4) * 2;
-      auto kaddr = [&](int dt) { return kbase_l + (((dt * 2 + ((l16 >> 1) & 1)) ^ (kr & 15)) << 4); };
+      auto kaddr = [&](int dt) { return kbase_l + (((dt * 2 + ((l16 >> 1) & 1)) ^ slot16(kr)) << 4); };
 #pragma unroll
       for (int dq4 = 0; dq4 < 2; ++dq4) {
         tr_u32x2 r[8];
@@ -552,19 +543,24 @@ __global__ void chunk_scatter_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // One workgroup = one wavefront pair = one column chunk (key block j, up to
 // kColChunk query blocks).  The pair streams the chunk's (query block, head)
-// items in steps of 32 query rows and splits the work by tensor:
+// items in steps of 32 query rows (n steps) and splits the work by tensor:
 //   wave A (role 0): S = Q K^T -> P, and dV^T += dO^T P   (K_j in registers)
 //   wave B (role 1): dP = dO V^T -> dS = P (dP - Delta), dK^T += Q^T dS
 //                    (V_j in registers)
 // Every product is a 32x32x16 MFMA, which a single wavefront issues at the
-// full matrix rate; one wavefront runs per SIMD (about 300 registers).
+// full matrix rate; one wavefront runs per SIMD (about 400 registers).
 //
-// The rows and row statistics of each step reach LDS by asynchronous
-// global -> LDS copies (A copies Q and LSE, B copies dO and Delta) into a ring
-// of four buffers, two steps ahead.  Window s (between the pair's barriers
-// s - 1 and s) holds: A: S_s, P_s, dV_s;  B: dP_s, dS_{s-1}, dK_{s-1}.  A
-// publishes P_s (fp16) at barrier s; step t's buffer is copied during window
-// t - 2, awaited before barrier t - 1 and last read in window t + 1.
+// Software pipeline (window s lies between the pair's barriers s - 1 and s):
+//   A: S_{s+1} (matrix core) overlapped with P_s = exp(S_s ...) (vector ALU),
+//      then dV_s += dO_s^T P_s;  P_s is published (fp16) at barrier s.
+//   B: dP_s (matrix core) overlapped with dS_{s-1} (vector ALU), then
+//      dK_{s-1} += Q_{s-1}^T dS_{s-1}.
+// The rows of each step reach LDS by asynchronous global -> LDS copies into
+// two rings: A copies Q rows and Delta into a 5-slot ring (step t is read in
+// windows t - 1 .. t + 1), B copies dO rows and LSE into a 3-slot ring (read
+// in window t).  Both copies are issued two windows before they are first
+// read; every wavefront waits for its own copies before the barrier that
+// publishes them.
 //
 // 32x32x16 operand layouts (lane l, g = l / 32):
 //   A: row l % 32, k = 8 g .. 8 g + 7;   B: column l % 32, same k;
@@ -580,19 +576,20 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-constexpr int KV_NBUF = 4;
-constexpr int XS_BYTES = 32 * HD * 2;                          // 32 staged rows
-constexpr int RING_BYTES = 2 * XS_BYTES + 2 * 256;             // Q, dO, LSE, Delta
-constexpr int PX_BYTES = 64 * 32 * 2;                          // P of one step (fp16)
-constexpr int KV_LDS = KV_NBUF * RING_BYTES + 2 * PX_BYTES + 2 * kColChunk * 4;
+constexpr int XS_BYTES = 32 * HD * 2;               // 32 staged rows
+constexpr int SLOT_BYTES = XS_BYTES + 256;           // rows + one statistic (64 floats)
+constexpr int Q_SLOTS = 5, O_SLOTS = 3;
+constexpr int QRING = 0;
+constexpr int ORING = QRING + Q_SLOTS * SLOT_BYTES;
+constexpr int PX_BYTES = 64 * 32 * 2;                // P of one step (fp16)
+constexpr int PBUF = ORING + O_SLOTS * SLOT_BYTES;
+constexpr int ITAB = PBUF + 2 * PX_BYTES;
+constexpr int KV_LDS = ITAB + 2 * kColChunk * 4;
+static_assert(2 * KV_LDS <= 160 * 1024, "two workgroups per CU");
 
-// Element offset of 16-byte chunk c of row r in a staged 32 x 128 tile.  The
-// chunk is stored at c ^ f(r), f(r) = 2 (r & 3) + ((r >> 2) & 1): the eight
-// rows read by one 8-lane phase of a 16-byte access hit eight different
-// slots, and the four rows x 32 bytes of one 16-lane transposed read as well.
-__device__ __forceinline__ int xsw(int r, int c) {
-  return r * HD + ((c ^ (((r & 3) << 1) | ((r >> 2) & 1))) << 3);
-}
+// Element offset of 16-byte chunk c of row r in a staged 32 x 128 tile
+// (slot16 swizzle).
+__device__ __forceinline__ int xsw(int r, int c) { return r * HD + ((c ^ slot16(r)) << 3); }
 
 // Pair barrier: this wavefront's LDS accesses and all but its newest nine
 // global -> LDS copies are complete, then s_barrier.  (__syncthreads would
@@ -603,42 +600,40 @@ __device__ __forceinline__ void ring_barrier() {
 
 // The eight transposed A-operand fragments (dt = 0..3, sl = 0..1) of one
 // staged 32 x 128 tile: 16 ds_read_b64_tr_b16 in flight, awaited inside the
-// same asm block.  p0 / p1: this lane's addresses of the dt = 0 / dt = 1
-// fragments (sl = 0, first four rows); dt + 2 adds 128 bytes, sl 4096 and the
-// second four rows 2048.
-__device__ __forceinline__ void tr_tile(const bf16* p0, const bf16* p1, bf16x8 (&t)[4][2]) {
-  typedef __attribute__((address_space(3))) const char* lptr;
-  const unsigned a0 = (unsigned)(uintptr_t)(lptr)p0;
-  const unsigned a1 = (unsigned)(uintptr_t)(lptr)p1;
-  u32x2 r[16];
+// same asm block.  p[dt][h]: this lane's address for head-dim tile dt, sl = 0,
+// first (h = 0) or second (h = 1) group of four rows; sl = 1 adds 4096 bytes
+// (sixteen rows: the swizzle slot is unchanged).
+__device__ __forceinline__ void tr_tile(const unsigned (&p)[4][2], bf16x8 (&t)[4][2]) {
+  tr_u32x2 r[16];
   __asm__ volatile(
       "ds_read_b64_tr_b16 %0, %16\n\t"
-      "ds_read_b64_tr_b16 %1, %16 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %1, %17\n\t"
       "ds_read_b64_tr_b16 %2, %16 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %3, %16 offset:6144\n\t"
-      "ds_read_b64_tr_b16 %4, %17\n\t"
-      "ds_read_b64_tr_b16 %5, %17 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %6, %17 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %7, %17 offset:6144\n\t"
-      "ds_read_b64_tr_b16 %8, %16 offset:128\n\t"
-      "ds_read_b64_tr_b16 %9, %16 offset:2176\n\t"
-      "ds_read_b64_tr_b16 %10, %16 offset:4224\n\t"
-      "ds_read_b64_tr_b16 %11, %16 offset:6272\n\t"
-      "ds_read_b64_tr_b16 %12, %17 offset:128\n\t"
-      "ds_read_b64_tr_b16 %13, %17 offset:2176\n\t"
-      "ds_read_b64_tr_b16 %14, %17 offset:4224\n\t"
-      "ds_read_b64_tr_b16 %15, %17 offset:6272\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %4, %18\n\t"
+      "ds_read_b64_tr_b16 %5, %19\n\t"
+      "ds_read_b64_tr_b16 %6, %18 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %8, %20\n\t"
+      "ds_read_b64_tr_b16 %9, %21\n\t"
+      "ds_read_b64_tr_b16 %10, %20 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %11, %21 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %12, %22\n\t"
+      "ds_read_b64_tr_b16 %13, %23\n\t"
+      "ds_read_b64_tr_b16 %14, %22 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %15, %23 offset:4096\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
         "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
         "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
-      : "v"(a0), "v"(a1)
+      : "v"(p[0][0]), "v"(p[0][1]), "v"(p[1][0]), "v"(p[1][1]), "v"(p[2][0]), "v"(p[2][1]),
+        "v"(p[3][0]), "v"(p[3][1])
       : "memory");
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) {
-      const int k = (dt >> 1) * 8 + (dt & 1) * 4 + sl * 2;
+      const int k = dt * 4 + sl * 2;   // rows +0, then +8
       const u32x4 w = u32x4{r[k][0], r[k][1], r[k + 1][0], r[k + 1][1]};
       t[dt][sl] = __builtin_bit_cast(bf16x8, w);
     }
@@ -647,12 +642,12 @@ __device__ __forceinline__ void tr_tile(const bf16* p0, const bf16* p1, bf16x8 (
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[KV_LDS];
-  int32_t* itab = (int32_t*)(smem + KV_NBUF * RING_BYTES + 2 * PX_BYTES);   // query block per entry
-  float* btab = (float*)(itab + kColChunk);                                 // its log gate (log2 units)
+  int32_t* itab = (int32_t*)(smem + ITAB);   // query block of each chunk entry
+  float* btab = (float*)(itab + kColChunk);  // its log gate (log2 units; 0 on the diagonal)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int role = tid >> 6;   // 0: S / P / dV, 1: dP / dS / dK
+  const int role = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0: S / P / dV, 1: dP / dS / dK (wave-uniform)
   const int g = lane >> 5;
   const int l32 = lane & 31;
 
@@ -673,10 +668,16 @@ bwd_dkdv_kernel(BwdArgs a) {
   const int bb = (int)(bhk / a.Hkv);
   const int G = a.G;
 
-  if (tid < ne) {
-    const int i = a.collist[a.coloff[col] + e0 + tid];
-    itab[tid] = i;
-    btab[tid] = i == j ? 0.0f : a.lg[(bhk * a.C + i) * a.C + j] * kLog2e;
+  // per chunk entry e (lane e): its query block and log gate (LDS), and the
+  // element offset of row 0 of (batch, first head of the kv group, block)
+  long long rowbase = 0;
+  if (lane < ne) {
+    const int i = a.collist[a.coloff[col] + e0 + lane];
+    if (role == 0) {
+      itab[lane] = i;
+      btab[lane] = i == j ? 0.0f : a.lg[(bhk * a.C + i) * a.C + j] * kLog2e;
+    }
+    rowbase = ((long long)bb * a.Hq + hk * G) * a.N + (long long)i * BLK;
   }
 
   // resident B operand of S (A: K_j) or dP (B: V_j): key kt*32 + l32,
@@ -696,27 +697,40 @@ bwd_dkdv_kernel(BwdArgs a) {
   }
   __syncthreads();   // item table
 
-  const int nsteps = 2 * ne * G;
+  const int n = 2 * ne * G;   // steps (even): entry e, head h, half x -> step 2 (e G + h) + x
+  // Copy stream: step t's rows (32 x 128) and statistic go to slot t mod
+  // nslots of this wavefront's ring (A: Q and Delta, B: dO and LSE).  Steps
+  // past the end recopy the last step into their (free, never read) slot.
+  const int nslots = role == 0 ? Q_SLOTS : O_SLOTS;
+  char* const ring = smem + (role == 0 ? QRING : ORING);
   const bf16* src = role == 0 ? a.q : a.d_o;
-  const float* stat = role == 0 ? a.lse : a.delta;
-  // copy step t's rows (32 x 128) and statistics into ring buffer t % 4;
-  // steps past the end recopy the last step (same buffer rule, never read)
-  auto copy_step = [&](int t) {
-    const int tc = min(t, nsteps - 1);
-    const int it = tc >> 1;
-    const int e = it / G;
-    const long long r0 = ((long long)bb * a.Hq + hk * G + (it - e * G)) * a.N +
-                         (long long)itab[e] * BLK + (tc & 1) * 32;
-    char* rb = smem + (t & 3) * RING_BYTES;
-    char* xs = rb + role * XS_BYTES;
+  const float* stat = role == 0 ? a.delta : a.lse;
+  unsigned voff[8];   // byte offset of this lane's 16 bytes in copy q (rows 4q .. 4q + 3)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {   // 1 KB = rows 4q .. 4q + 3; lane -> (row, slot)
-      const int row = q * 4 + (lane >> 4);
-      const int ch = (lane & 15) ^ (((row & 3) << 1) | ((row >> 2) & 1));
-      dma16(src + (r0 + row) * HD + ch * 8, lds_addr(xs + q * 1024));
+  for (int q = 0; q < 8; ++q) {
+    const int row = q * 4 + (lane >> 4);
+    voff[q] = (unsigned)(row * HD + (((lane & 15) ^ slot16(row)) << 3)) * 2;
+  }
+  const unsigned soff = (unsigned)l32 * 4;
+  int ct = 0, ce = 0, chh = 0, cx = 0, cslot = 0;   // next step to copy: (entry, head, half, slot)
+  auto copy_next = [&]() {
+    const long long rbase = (long long)(unsigned)__builtin_amdgcn_readlane((int)rowbase, ce) |
+                            ((long long)__builtin_amdgcn_readlane((int)(rowbase >> 32), ce) << 32);
+    const long long r0 = rbase + (long long)chh * a.N + cx * 32;
+    const char* sl = ring + cslot * SLOT_BYTES;
+    const bf16* rb = src + r0 * HD;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dma16s(rb, voff[q], lds_addr(sl + q * 1024));
+    dma4s(stat + r0, soff, lds_addr(sl + XS_BYTES));
+    cslot = cslot + 1 == nslots ? 0 : cslot + 1;
+    if (++ct < n) {   // advance (entry, head, half); past the end it stays on the last step
+      cx ^= 1;
+      if (cx == 0 && ++chh == G) { chh = 0; ++ce; }
     }
-    dma4(stat + r0 + l32, lds_addr(rb + 2 * XS_BYTES + role * 256));
   };
+  auto qring = [&](int k) -> char* { return smem + QRING + k * SLOT_BYTES; };
+  auto oring = [&](int k) -> char* { return smem + ORING + k * SLOT_BYTES; };
+  auto inc = [](int k, int m) { return k + 1 == m ? 0 : k + 1; };
 
   f32x16 acc[4][2];   // A: dV^T, B: dK^T; lane: key kt*32 + l32, dims dt*32 + 8 (jj/4) + 4 g + jj%4
 #pragma unroll
@@ -726,17 +740,26 @@ bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int x = 0; x < 16; ++x) acc[dt][kt][x] = 0.0f;
 
+  // transposed-read addresses (element offsets inside a staged tile): head-dim
+  // tile dt, rows tr_r + 8 h (sl = 0)
   const int u = lane & 15;
   const int dhalf = (lane >> 4) & 1;
-  // A operands of the row contraction: transposed reads of staged tile xs
-  // (lane: column dt*32 + l32, rows sl*16 + {4g..4g+3, 8+4g..8+4g+3})
   const int tr_r = g * 4 + (u >> 2);
-  const int tr_e = (u & 1) * 4;
-  const int tr0 = xsw(tr_r, dhalf * 2 + ((u >> 1) & 1)) + tr_e;       // dt = 0
-  const int tr1 = xsw(tr_r, 4 + dhalf * 2 + ((u >> 1) & 1)) + tr_e;   // dt = 1
-  auto row_contract = [&](const bf16* xs, const bf16x8 (&bop)[2][2]) {
-    bf16x8 ta[4][2];
-    tr_tile(xs + tr0, xs + tr1, ta);
+  int tro[4][2];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) tro[dt][h] = xsw(tr_r + 8 * h, dt * 4 + dhalf * 2 + ((u >> 1) & 1)) + (u & 1) * 4;
+  auto read_tr = [&](const char* rows, bf16x8 (&ta)[4][2]) {
+    const unsigned xa = lds_addr(rows);
+    unsigned pa[4][2];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) pa[dt][h] = xa + 2 * tro[dt][h];
+    tr_tile(pa, ta);
+  };
+  auto contract = [&](const bf16x8 (&ta)[4][2], const bf16x8 (&bop)[2][2]) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -744,9 +767,9 @@ bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) acc[dt][kt] = mfma32(ta[dt][sl], bop[kt][sl], acc[dt][kt]);
   };
-  // this lane's 16 C-row statistics (rows 8t + 4g + u)
-  auto read_stat = [&](const char* rb, float (&st)[16]) {
-    const float* sp = (const float*)(rb + 2 * XS_BYTES + role * 256);
+  // this lane's 16 C-row statistics (rows 8t + 4g + u) of a slot
+  auto read_stat = [&](const char* sl, float (&st)[16]) {
+    const float* sp = (const float*)(sl + XS_BYTES);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const f32x4 v = *(const f32x4*)(sp + t * 8 + g * 4);
@@ -754,112 +777,190 @@ bwd_dkdv_kernel(BwdArgs a) {
       for (int y = 0; y < 4; ++y) st[t * 4 + y] = v[y];
     }
   };
-  // rows x keys product with the resident operand: A: S, B: dP
-  auto rows_product = [&](const char* rb, f32x16 (&sc)[2]) {
-    const bf16* xs = (const bf16*)(rb + role * XS_BYTES);
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) sc[kt][x] = 0.0f;
+  auto pbuf = [&](int t) -> _Float16* { return (_Float16*)(smem + PBUF + (t & 1) * PX_BYTES); };
+  // S (A) or dP (B) of the rows in slot sl into `out`, one MFMA at a time;
+  // after MFMA m (m = 0..15) the vector-ALU work `per_mfma(m)` of the
+  // previous step is issued, so the two overlap in the instruction stream
+  // (sched_barrier keeps the scheduler from regrouping them).
+  auto rows_product_with = [&](const char* sl, f32x16 (&out)[2], auto&& per_mfma) {
+    const bf16* xs = (const bf16*)sl;
     bf16x8 qa[8];
 #pragma unroll
     for (int ds = 0; ds < 8; ++ds) qa[ds] = *(const bf16x8*)(xs + xsw(l32, ds * 2 + g));
 #pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) out[kt][x] = 0.0f;
+#pragma unroll
     for (int ds = 0; ds < 8; ++ds)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) sc[kt] = mfma32(qa[ds], kf[kt][ds], sc[kt]);
-  };
-
-  copy_step(0);
-  copy_step(1);
-  ring_barrier();   // step 0 staged
-
-  f32x16 dp0[2], dp1[2];   // B: dP of the previous and current step
-  auto window = [&](int s, f32x16 (&dprev)[2], f32x16 (&dcur)[2]) {
-    copy_step(s + 2);
-    const char* rb = smem + (s & 3) * RING_BYTES;
-    if (role == 0) {
-      // S_s, P_s (published for B, fp16), dV_s += dO_s^T P_s
-      f32x16 sc[2];
-      rows_product(rb, sc);
-      float st[16];
-      read_stat(rb, st);
-      const int ent = (s >> 1) / G;
-      const float beta = btab[ent];
-      const bool diag = itab[ent] == j;
-      const int hrow = (s & 1) * 32;
-      _Float16* px = (_Float16*)(smem + KV_NBUF * RING_BYTES + (s & 1) * PX_BYTES);
-      bf16x8 bop[2][2];
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) st[jj] = fmaf(-st[jj], kLog2e, beta);
-#pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        f32x16 p;
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) p[jj] = __builtin_amdgcn_exp2f(fmaf(sc[kt][jj], a.c2, st[jj]));
-        if (diag) {
-#pragma unroll
-          for (int jj = 0; jj < 16; ++jj)
-            if (kt * 32 + l32 > hrow + (jj >> 2) * 8 + g * 4 + (jj & 3)) p[jj] = 0.0f;
-        }
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          f16x8 ph;
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            ph[x] = (_Float16)p[h2 * 8 + x];
-            bop[kt][h2][x] = (bf16)p[h2 * 8 + x];
-          }
-          *(f16x8*)(px + ((kt * 2 + h2) * 64 + lane) * 8) = ph;
-        }
+        out[kt] = mfma32(qa[ds], kf[kt][ds], out[kt]);
+        per_mfma(ds * 2 + kt);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      row_contract((const bf16*)(rb + XS_BYTES), bop);
-    } else {
-      // dP_s; then dS_{s-1} = P_{s-1} (dP_{s-1} - Delta) and dK_{s-1} += Q^T dS
-      rows_product(rb, dcur);
-      if (s > 0) {
-        const char* rp = smem + ((s - 1) & 3) * RING_BYTES;
-        float st[16];
-        read_stat(rp, st);
-        const _Float16* px = (const _Float16*)(smem + KV_NBUF * RING_BYTES + ((s - 1) & 1) * PX_BYTES);
-        bf16x8 bop[2][2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const f16x8 ph = *(const f16x8*)(px + ((kt * 2 + h2) * 64 + lane) * 8);
-#pragma unroll
-            for (int x = 0; x < 8; ++x)
-              bop[kt][h2][x] = (bf16)((float)ph[x] * (dprev[kt][h2 * 8 + x] - st[h2 * 8 + x]));
-          }
-        row_contract((const bf16*)rp, bop);
-      }
-    }
-    ring_barrier();   // P_s published; step s + 1 staged
   };
 
-#pragma unroll 1
-  for (int s = 0; s < nsteps; s += 2) {   // nsteps is even
-    window(s, dp1, dp0);
-    window(s + 1, dp0, dp1);
-  }
-  if (role == 1) {   // dS and dK of the last step
-    const int s = nsteps;
-    const char* rp = smem + ((s - 1) & 3) * RING_BYTES;
-    float st[16];
-    read_stat(rp, st);
-    const _Float16* px = (const _Float16*)(smem + KV_NBUF * RING_BYTES + ((s - 1) & 1) * PX_BYTES);
+  // A, window s: S_{s+1} (rows in qn) interleaved with
+  // P_s = exp2(c2 S_s + beta - lse) (LSE and dO_s in os), then dV_s += dO_s^T P_s.
+  // P_s also goes to LDS (fp16) for B.  HALF: the step's half of its query block.
+  auto window_a = [&](auto diag_tag, auto half_tag, const char* qn, const char* os, _Float16* px,
+                      float beta, const f32x16 (&sprev)[2], f32x16 (&snext)[2]) {
+    constexpr bool DIAG = decltype(diag_tag)::value;
+    constexpr int hrow = decltype(half_tag)::value * 32;
+    float nl[16];
+    read_stat(os, nl);   // LSE_s
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) nl[jj] = fmaf(-nl[jj], kLog2e, beta);
+    float pv[2][16];
+    // MFMA m of S_{s+1} is followed by elements 2m, 2m + 1 of P_s
+    rows_product_with(qn, snext, [&](int m) {
+      const int kt = m >> 3;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int jj = (m & 7) * 2 + x;
+        float e = __builtin_amdgcn_exp2f(fmaf(sprev[kt][jj], a.c2, nl[jj]));
+        if (DIAG && kt * 32 + l32 > hrow + (jj >> 2) * 8 + g * 4 + (jj & 3)) e = 0.0f;
+        pv[kt][jj] = e;
+      }
+    });
     bf16x8 bop[2][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        const f16x8 ph = *(const f16x8*)(px + ((kt * 2 + h2) * 64 + lane) * 8);
+        f16x8 ph;
 #pragma unroll
-        for (int x = 0; x < 8; ++x)
-          bop[kt][h2][x] = (bf16)((float)ph[x] * (dp1[kt][h2 * 8 + x] - st[h2 * 8 + x]));
+        for (int x = 0; x < 8; ++x) {
+          ph[x] = (_Float16)pv[kt][h2 * 8 + x];
+          bop[kt][h2][x] = (bf16)pv[kt][h2 * 8 + x];
+        }
+        *(f16x8*)(px + ((kt * 2 + h2) * 64 + lane) * 8) = ph;
       }
-    row_contract((const bf16*)rp, bop);
+    bf16x8 ta[4][2];
+    read_tr(os, ta);     // dO_s^T
+    contract(ta, bop);   // dV_s
+  };
+  // B: dS = P (dP - Delta) of a step (Delta and Q rows in qs, P in px) as the
+  // bf16 B operand, element pair m after MFMA m of the next dP, then
+  // dK += Q^T dS.
+  auto window_b = [&](const char* on, const char* qs, const _Float16* px,
+                      const f32x16 (&dprev)[2], f32x16 (&dcur)[2]) {
+    float dl[16];
+    read_stat(qs, dl);   // Delta of the previous step
+    f16x8 ph[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) ph[kt][h2] = *(const f16x8*)(px + ((kt * 2 + h2) * 64 + lane) * 8);
+    float dsv[2][16];
+    rows_product_with(on, dcur, [&](int m) {
+      const int kt = m >> 3;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int jj = (m & 7) * 2 + x;
+        dsv[kt][jj] = (float)ph[kt][jj >> 3][jj & 7] * (dprev[kt][jj] - dl[jj]);
+      }
+    });
+    bf16x8 bop[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int x = 0; x < 8; ++x) bop[kt][h2][x] = (bf16)dsv[kt][h2 * 8 + x];
+    bf16x8 ta[4][2];
+    read_tr(qs, ta);     // Q^T of the previous step
+    contract(ta, bop);   // dK
+  };
+
+  // Each wavefront runs its own loop of n windows, one pair barrier per
+  // window (P_s published; A's Q of step s + 2 and B's dO of step s + 1 landed).
+  f32x16 r0[2], r1[2];   // A: S of the current / next step; B: dP of the previous / current step
+  if (role == 0) {
+    copy_next();
+    copy_next();
+    copy_next();
+    ring_barrier();   // Q of steps 0, 1 landed
+    rows_product_with(qring(0), r0, [](int) {});   // S_0
+    // window s reads Q of step s + 1 (ring slot qk) and dO / LSE of step s
+    // (slot ok); the diagonal block, when in this chunk, is its first entry
+    // (2G steps, gate 0)
+    int qk = 1, ok = 0;
+    const int nd = itab[0] == j ? 2 * G : 0;
+#pragma unroll 1
+    for (int s = 0; s < nd; s += 2) {
+      copy_next();
+      window_a(std::true_type{}, std::integral_constant<int, 0>{}, qring(qk), oring(ok), pbuf(0), 0.0f, r0, r1);
+      ring_barrier();
+      qk = inc(qk, Q_SLOTS); ok = inc(ok, O_SLOTS);
+      copy_next();
+      window_a(std::true_type{}, std::integral_constant<int, 1>{}, qring(qk), oring(ok), pbuf(1), 0.0f, r1, r0);
+      ring_barrier();
+      qk = inc(qk, Q_SLOTS); ok = inc(ok, O_SLOTS);
+    }
+    int ent = nd ? 1 : 0, hh = 0;   // entry and head of the window pair
+    float beta = btab[ent < ne ? ent : 0];
+#pragma unroll 1
+    for (int s = nd; s < n; s += 2) {   // n, nd even
+      copy_next();
+      window_a(std::false_type{}, std::integral_constant<int, 0>{}, qring(qk), oring(ok), pbuf(0), beta, r0, r1);
+      ring_barrier();
+      qk = inc(qk, Q_SLOTS); ok = inc(ok, O_SLOTS);
+      copy_next();
+      window_a(std::false_type{}, std::integral_constant<int, 1>{}, qring(qk), oring(ok), pbuf(1), beta, r1, r0);
+      ring_barrier();
+      qk = inc(qk, Q_SLOTS); ok = inc(ok, O_SLOTS);
+      if (++hh == G) {
+        hh = 0;
+        ++ent;
+        beta = btab[ent < ne ? ent : 0];
+      }
+    }
+  } else {
+    copy_next();
+    copy_next();
+    ring_barrier();   // dO of step 0 landed
+    copy_next();
+    rows_product_with(oring(0), r0, [](int) {});   // dP_0
+    ring_barrier();
+    // window s (>= 1) reads dO of step s (slot ok), and Delta / Q of step s - 1 (slot qk)
+    int ok = 1, qk = 0;
+    int s = 1;
+#pragma unroll 1
+    for (; s + 1 < n; s += 2) {
+      copy_next();
+      window_b(oring(ok), qring(qk), pbuf(0), r0, r1);   // step s - 1 is even
+      ring_barrier();
+      ok = inc(ok, O_SLOTS); qk = inc(qk, Q_SLOTS);
+      copy_next();
+      window_b(oring(ok), qring(qk), pbuf(1), r1, r0);
+      ring_barrier();
+      ok = inc(ok, O_SLOTS); qk = inc(qk, Q_SLOTS);
+    }
+    copy_next();   // window n - 1: dP_{n-1} -> r1, dS / dK of step n - 2
+    window_b(oring(ok), qring(qk), pbuf(0), r0, r1);
+    ring_barrier();
+    qk = inc(qk, Q_SLOTS);
+    // dS and dK of the last step (odd)
+    bf16x8 bop[2][2];
+    {
+      float dl[16];
+      read_stat(qring(qk), dl);
+      const _Float16* px = pbuf(1);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const f16x8 ph = *(const f16x8*)(px + ((kt * 2 + h2) * 64 + lane) * 8);
+#pragma unroll
+          for (int x = 0; x < 8; ++x)
+            bop[kt][h2][x] = (bf16)((float)ph[x] * (r1[kt][h2 * 8 + x] - dl[h2 * 8 + x]));
+        }
+    }
+    bf16x8 ta[4][2];
+    read_tr(qring(qk), ta);
+    contract(ta, bop);
   }
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the trailing copies
 

@@ -96,7 +96,7 @@ __device__ __forceinline__ bf16x4 ds_read_tr(const bf16* p) {
 // LDS tiles are row-major with 256-byte rows and no padding; the 16-byte chunk
 // c of row r sits in slot c ^ (r & 15).  The 16 rows read by one lane group
 // (same chunk) then fall in 16 different slots, i.e. all 64 banks.
-__device__ __forceinline__ int swz(int r, int c) { return r * HD + ((c ^ (r & 15)) << 3); }
+__device__ __forceinline__ int swz(int r, int c) { return r * HD + ((c ^ slot16(r)) << 3); }
 
 // Asynchronous global -> LDS copy of one 64 x 128 tile by NW wavefronts
 // (global_load_lds_dwordx4: each instruction writes 64 x 16 contiguous bytes
@@ -109,7 +109,7 @@ __device__ __forceinline__ void tile_to_lds(bf16* lds, const bf16* g, int w, int
   for (int r = 0; r < 16 / NW; ++r) {
     const int seg = w + NW * r;               // 1 KB segment = rows 4 seg .. 4 seg + 3
     const int row = seg * 4 + (lane >> 4);
-    const int c = (lane & 15) ^ (row & 15);
+    const int c = (lane & 15) ^ slot16(row);
     dma16(g + row * HD + c * 8, lds_addr(lds + seg * 512));
   }
 }
@@ -261,8 +261,8 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
     for (int dp = 0; dp < 4; ++dp) {   // two head-dim tiles per batch of reads
       tr_u32x2 r[8];
-      tr_read_2x4(vbase + (((dp * 4 + ((l16 >> 1) & 1)) ^ (vr & 15)) << 4),
-                  vbase + (((dp * 4 + 2 + ((l16 >> 1) & 1)) ^ (vr & 15)) << 4), r);
+      tr_read_2x4(vbase + (((dp * 4 + ((l16 >> 1) & 1)) ^ slot16(vr)) << 4),
+                  vbase + (((dp * 4 + 2 + ((l16 >> 1) & 1)) ^ slot16(vr)) << 4), r);
 #pragma unroll
       for (int d2 = 0; d2 < 2; ++d2) {
         const int dt = dp * 2 + d2;
