@@ -587,6 +587,12 @@ constexpr int ITAB = PBUF + 2 * PX_BYTES;
 constexpr int KV_LDS = ITAB + 2 * kColChunk * 4;
 static_assert(2 * KV_LDS <= 160 * 1024, "two workgroups per CU");
 
+// Keeps the computation of x at this point of the instruction stream: the
+// vector-ALU work that is meant to overlap a matrix instruction would
+// otherwise be sunk to its first use.
+template <typename T>
+__device__ __forceinline__ void pin(T& x) { __asm__ volatile("" : "+v"(x)); }
+
 // Element offset of 16-byte chunk c of row r in a staged 32 x 128 tile
 // (slot16 swizzle).
 __device__ __forceinline__ int xsw(int r, int c) { return r * HD + ((c ^ slot16(r)) << 3); }
@@ -596,47 +602,6 @@ __device__ __forceinline__ int xsw(int r, int c) { return r * HD + ((c ^ slot16(
 // also wait for the newest copies, which are meant to stay in flight.)
 __device__ __forceinline__ void ring_barrier() {
   __asm__ volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// The eight transposed A-operand fragments (dt = 0..3, sl = 0..1) of one
-// staged 32 x 128 tile: 16 ds_read_b64_tr_b16 in flight, awaited inside the
-// same asm block.  p[dt][h]: this lane's address for head-dim tile dt, sl = 0,
-// first (h = 0) or second (h = 1) group of four rows; sl = 1 adds 4096 bytes
-// (sixteen rows: the swizzle slot is unchanged).
-__device__ __forceinline__ void tr_tile(const unsigned (&p)[4][2], bf16x8 (&t)[4][2]) {
-  tr_u32x2 r[16];
-  __asm__ volatile(
-      "ds_read_b64_tr_b16 %0, %16\n\t"
-      "ds_read_b64_tr_b16 %1, %17\n\t"
-      "ds_read_b64_tr_b16 %2, %16 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %3, %17 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %4, %18\n\t"
-      "ds_read_b64_tr_b16 %5, %19\n\t"
-      "ds_read_b64_tr_b16 %6, %18 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %7, %19 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %8, %20\n\t"
-      "ds_read_b64_tr_b16 %9, %21\n\t"
-      "ds_read_b64_tr_b16 %10, %20 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %11, %21 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %12, %22\n\t"
-      "ds_read_b64_tr_b16 %13, %23\n\t"
-      "ds_read_b64_tr_b16 %14, %22 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %15, %23 offset:4096\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
-        "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
-        "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
-      : "v"(p[0][0]), "v"(p[0][1]), "v"(p[1][0]), "v"(p[1][1]), "v"(p[2][0]), "v"(p[2][1]),
-        "v"(p[3][0]), "v"(p[3][1])
-      : "memory");
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
-      const int k = dt * 4 + sl * 2;   // rows +0, then +8
-      const u32x4 w = u32x4{r[k][0], r[k][1], r[k + 1][0], r[k + 1][1]};
-      t[dt][sl] = __builtin_bit_cast(bf16x8, w);
-    }
 }
 
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -713,20 +678,31 @@ bwd_dkdv_kernel(BwdArgs a) {
   }
   const unsigned soff = (unsigned)l32 * 4;
   int ct = 0, ce = 0, chh = 0, cx = 0, cslot = 0;   // next step to copy: (entry, head, half, slot)
-  auto copy_next = [&]() {
+  const unsigned ring_lds = lds_addr(ring);
+  // one step's copies: prepare() fixes the sources and the slot, then
+  // issue(q) sends rows 4q .. 4q + 3 (q < 8) or the statistic (q = 8), so the
+  // nine copies can be spread between matrix instructions
+  struct Copy { const bf16* rows; const float* st; unsigned lds; };
+  auto prepare = [&]() -> Copy {
     const long long rbase = (long long)(unsigned)__builtin_amdgcn_readlane((int)rowbase, ce) |
                             ((long long)__builtin_amdgcn_readlane((int)(rowbase >> 32), ce) << 32);
-    const long long r0 = rbase + (long long)chh * a.N + cx * 32;
-    const char* sl = ring + cslot * SLOT_BYTES;
-    const bf16* rb = src + r0 * HD;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) dma16s(rb, voff[q], lds_addr(sl + q * 1024));
-    dma4s(stat + r0, soff, lds_addr(sl + XS_BYTES));
+    const long long r0 = rbase + (long long)(unsigned)(chh * a.N + cx * 32);
+    Copy cp{src + r0 * HD, stat + r0, ring_lds + (unsigned)(cslot * SLOT_BYTES)};
     cslot = cslot + 1 == nslots ? 0 : cslot + 1;
     if (++ct < n) {   // advance (entry, head, half); past the end it stays on the last step
       cx ^= 1;
       if (cx == 0 && ++chh == G) { chh = 0; ++ce; }
     }
+    return cp;
+  };
+  auto issue = [&](const Copy& cp, int q) {
+    if (q < 8) dma16s(cp.rows, voff[q], cp.lds + q * 1024);
+    else dma4s(cp.st, soff, cp.lds + XS_BYTES);
+  };
+  auto copy_next = [&]() {
+    const Copy cp = prepare();
+#pragma unroll
+    for (int q = 0; q < 9; ++q) issue(cp, q);
   };
   auto qring = [&](int k) -> char* { return smem + QRING + k * SLOT_BYTES; };
   auto oring = [&](int k) -> char* { return smem + ORING + k * SLOT_BYTES; };
@@ -751,21 +727,26 @@ bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) tro[dt][h] = xsw(tr_r + 8 * h, dt * 4 + dhalf * 2 + ((u >> 1) & 1)) + (u & 1) * 4;
   auto read_tr = [&](const char* rows, bf16x8 (&ta)[4][2]) {
-    const unsigned xa = lds_addr(rows);
-    unsigned pa[4][2];
+    const bf16* xs = (const bf16*)rows;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) pa[dt][h] = xa + 2 * tro[dt][h];
-    tr_tile(pa, ta);
+      for (int sl = 0; sl < 2; ++sl)
+        ta[dt][sl] = join(ds_read_tr(xs + tro[dt][0] + sl * 16 * HD), ds_read_tr(xs + tro[dt][1] + sl * 16 * HD));
   };
-  auto contract = [&](const bf16x8 (&ta)[4][2], const bf16x8 (&bop)[2][2]) {
+  // row contraction into the dV^T / dK^T accumulators; after MFMA m the
+  // work `per_mfma(m)` is issued (sched_barrier keeps the interleave)
+  auto contract = [&](const bf16x8 (&ta)[4][2], const bf16x8 (&bop)[2][2], auto&& per_mfma) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) acc[dt][kt] = mfma32(ta[dt][sl], bop[kt][sl], acc[dt][kt]);
+        for (int kt = 0; kt < 2; ++kt) {
+          acc[dt][kt] = mfma32(ta[dt][sl], bop[kt][sl], acc[dt][kt]);
+          per_mfma((dt * 2 + sl) * 2 + kt);
+          __builtin_amdgcn_sched_barrier(0);
+        }
   };
   // this lane's 16 C-row statistics (rows 8t + 4g + u) of a slot
   auto read_stat = [&](const char* sl, float (&st)[16]) {
@@ -782,11 +763,12 @@ bwd_dkdv_kernel(BwdArgs a) {
   // after MFMA m (m = 0..15) the vector-ALU work `per_mfma(m)` of the
   // previous step is issued, so the two overlap in the instruction stream
   // (sched_barrier keeps the scheduler from regrouping them).
-  auto rows_product_with = [&](const char* sl, f32x16 (&out)[2], auto&& per_mfma) {
+  auto read_rows = [&](const char* sl, bf16x8 (&qa)[8]) {
     const bf16* xs = (const bf16*)sl;
-    bf16x8 qa[8];
 #pragma unroll
     for (int ds = 0; ds < 8; ++ds) qa[ds] = *(const bf16x8*)(xs + xsw(l32, ds * 2 + g));
+  };
+  auto rows_product_with = [&](const bf16x8 (&qa)[8], f32x16 (&out)[2], auto&& per_mfma) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -808,44 +790,51 @@ bwd_dkdv_kernel(BwdArgs a) {
                       float beta, const f32x16 (&sprev)[2], f32x16 (&snext)[2]) {
     constexpr bool DIAG = decltype(diag_tag)::value;
     constexpr int hrow = decltype(half_tag)::value * 32;
+    bf16x8 qa[8];
+    read_rows(qn, qa);   // Q of step s + 1
     float nl[16];
     read_stat(os, nl);   // LSE_s
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) nl[jj] = fmaf(-nl[jj], kLog2e, beta);
-    float pv[2][16];
-    // MFMA m of S_{s+1} is followed by elements 2m, 2m + 1 of P_s
-    rows_product_with(qn, snext, [&](int m) {
+    bf16x8 bop[2][2];
+    f16x8 ph[2][2];
+    // MFMA m of S_{s+1} is followed by elements 2m, 2m + 1 of P_s (packed to
+    // bf16 for dV and to fp16 for B)
+    rows_product_with(qa, snext, [&](int m) {
       const int kt = m >> 3;
+      float e2[2];
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int jj = (m & 7) * 2 + x;
         float e = __builtin_amdgcn_exp2f(fmaf(sprev[kt][jj], a.c2, nl[jj]));
         if (DIAG && kt * 32 + l32 > hrow + (jj >> 2) * 8 + g * 4 + (jj & 3)) e = 0.0f;
-        pv[kt][jj] = e;
+        e2[x] = e;
       }
+      const int h2 = (m >> 2) & 1, x0 = (m & 3) * 2;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        bop[kt][h2][x0 + x] = (bf16)e2[x];
+        ph[kt][h2][x0 + x] = (_Float16)e2[x];
+      }
+      pin(bop[kt][h2]);
+      pin(ph[kt][h2]);
     });
-    bf16x8 bop[2][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        f16x8 ph;
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          ph[x] = (_Float16)pv[kt][h2 * 8 + x];
-          bop[kt][h2][x] = (bf16)pv[kt][h2 * 8 + x];
-        }
-        *(f16x8*)(px + ((kt * 2 + h2) * 64 + lane) * 8) = ph;
-      }
+      for (int h2 = 0; h2 < 2; ++h2) *(f16x8*)(px + ((kt * 2 + h2) * 64 + lane) * 8) = ph[kt][h2];
     bf16x8 ta[4][2];
-    read_tr(os, ta);     // dO_s^T
-    contract(ta, bop);   // dV_s
+    read_tr(os, ta);   // dO_s^T
+    const Copy cp = prepare();
+    contract(ta, bop, [&](int m) { if (m < 9) issue(cp, m); });   // dV_s, this window's copies
   };
   // B: dS = P (dP - Delta) of a step (Delta and Q rows in qs, P in px) as the
   // bf16 B operand, element pair m after MFMA m of the next dP, then
   // dK += Q^T dS.
   auto window_b = [&](const char* on, const char* qs, const _Float16* px,
                       const f32x16 (&dprev)[2], f32x16 (&dcur)[2]) {
+    bf16x8 qa[8];
+    read_rows(on, qa);   // dO of step s
     float dl[16];
     read_stat(qs, dl);   // Delta of the previous step
     f16x8 ph[2][2];
@@ -853,25 +842,20 @@ bwd_dkdv_kernel(BwdArgs a) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) ph[kt][h2] = *(const f16x8*)(px + ((kt * 2 + h2) * 64 + lane) * 8);
-    float dsv[2][16];
-    rows_product_with(on, dcur, [&](int m) {
+    bf16x8 bop[2][2];
+    rows_product_with(qa, dcur, [&](int m) {
       const int kt = m >> 3;
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int jj = (m & 7) * 2 + x;
-        dsv[kt][jj] = (float)ph[kt][jj >> 3][jj & 7] * (dprev[kt][jj] - dl[jj]);
+        bop[kt][jj >> 3][jj & 7] = (bf16)((float)ph[kt][jj >> 3][jj & 7] * (dprev[kt][jj] - dl[jj]));
       }
+      pin(bop[kt][(m >> 2) & 1]);
     });
-    bf16x8 bop[2][2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int x = 0; x < 8; ++x) bop[kt][h2][x] = (bf16)dsv[kt][h2 * 8 + x];
     bf16x8 ta[4][2];
-    read_tr(qs, ta);     // Q^T of the previous step
-    contract(ta, bop);   // dK
+    read_tr(qs, ta);   // Q^T of the previous step
+    const Copy cp = prepare();
+    contract(ta, bop, [&](int m) { if (m < 9) issue(cp, m); });   // dK, this window's copies
   };
 
   // Each wavefront runs its own loop of n windows, one pair barrier per
@@ -882,7 +866,11 @@ bwd_dkdv_kernel(BwdArgs a) {
     copy_next();
     copy_next();
     ring_barrier();   // Q of steps 0, 1 landed
-    rows_product_with(qring(0), r0, [](int) {});   // S_0
+    {
+      bf16x8 qa[8];
+      read_rows(qring(0), qa);
+      rows_product_with(qa, r0, [](int) {});   // S_0
+    }
     // window s reads Q of step s + 1 (ring slot qk) and dO / LSE of step s
     // (slot ok); the diagonal block, when in this chunk, is its first entry
     // (2G steps, gate 0)
@@ -890,11 +878,9 @@ bwd_dkdv_kernel(BwdArgs a) {
     const int nd = itab[0] == j ? 2 * G : 0;
 #pragma unroll 1
     for (int s = 0; s < nd; s += 2) {
-      copy_next();
       window_a(std::true_type{}, std::integral_constant<int, 0>{}, qring(qk), oring(ok), pbuf(0), 0.0f, r0, r1);
       ring_barrier();
       qk = inc(qk, Q_SLOTS); ok = inc(ok, O_SLOTS);
-      copy_next();
       window_a(std::true_type{}, std::integral_constant<int, 1>{}, qring(qk), oring(ok), pbuf(1), 0.0f, r1, r0);
       ring_barrier();
       qk = inc(qk, Q_SLOTS); ok = inc(ok, O_SLOTS);
@@ -903,11 +889,9 @@ bwd_dkdv_kernel(BwdArgs a) {
     float beta = btab[ent < ne ? ent : 0];
 #pragma unroll 1
     for (int s = nd; s < n; s += 2) {   // n, nd even
-      copy_next();
       window_a(std::false_type{}, std::integral_constant<int, 0>{}, qring(qk), oring(ok), pbuf(0), beta, r0, r1);
       ring_barrier();
       qk = inc(qk, Q_SLOTS); ok = inc(ok, O_SLOTS);
-      copy_next();
       window_a(std::false_type{}, std::integral_constant<int, 1>{}, qring(qk), oring(ok), pbuf(1), beta, r1, r0);
       ring_barrier();
       qk = inc(qk, Q_SLOTS); ok = inc(ok, O_SLOTS);
@@ -921,24 +905,26 @@ bwd_dkdv_kernel(BwdArgs a) {
     copy_next();
     copy_next();
     ring_barrier();   // dO of step 0 landed
-    copy_next();
-    rows_product_with(oring(0), r0, [](int) {});   // dP_0
+    {
+      bf16x8 qa[8];
+      read_rows(oring(0), qa);
+      copy_next();
+      rows_product_with(qa, r0, [](int) {});   // dP_0
+    }
     ring_barrier();
     // window s (>= 1) reads dO of step s (slot ok), and Delta / Q of step s - 1 (slot qk)
     int ok = 1, qk = 0;
     int s = 1;
 #pragma unroll 1
     for (; s + 1 < n; s += 2) {
-      copy_next();
       window_b(oring(ok), qring(qk), pbuf(0), r0, r1);   // step s - 1 is even
       ring_barrier();
       ok = inc(ok, O_SLOTS); qk = inc(qk, Q_SLOTS);
-      copy_next();
       window_b(oring(ok), qring(qk), pbuf(1), r1, r0);
       ring_barrier();
       ok = inc(ok, O_SLOTS); qk = inc(qk, Q_SLOTS);
     }
-    copy_next();   // window n - 1: dP_{n-1} -> r1, dS / dK of step n - 2
+    // window n - 1: dP_{n-1} -> r1, dS / dK of step n - 2
     window_b(oring(ok), qring(qk), pbuf(0), r0, r1);
     ring_barrier();
     qk = inc(qk, Q_SLOTS);
@@ -960,7 +946,7 @@ bwd_dkdv_kernel(BwdArgs a) {
     }
     bf16x8 ta[4][2];
     read_tr(qring(qk), ta);
-    contract(ta, bop);
+    contract(ta, bop, [](int) {});
   }
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the trailing copies
 
