@@ -48,6 +48,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BLK = 64;
 constexpr int HD = 128;
@@ -64,8 +66,15 @@ struct FwdArgs {
   float c2;       // sm_scale * log2(e)
 };
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// v_mfma_f32_32x32x16_bf16.  Lane l (g = l / 32): A row l % 32, k = 8 g .. +7;
+// B column l % 32, same k; C column l % 32, rows 8 (jj / 4) + 4 g + jj % 4.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // max / sum over the lanes l, l^16, l^32, l^48 (the four lanes that share a
@@ -75,6 +84,15 @@ __device__ __forceinline__ float max4(float x) {
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+// max / sum over the lanes l, l ^ 32 (the two lanes of a 32x32 C column)
+__device__ __forceinline__ float max2(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+__device__ __forceinline__ float sum2(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
 }
 __device__ __forceinline__ float sum4(float x) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -116,6 +134,12 @@ __device__ __forceinline__ void tile_to_lds(bf16* lds, const bf16* g, int w, int
 
 __device__ __forceinline__ void wait_vm() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Keeps the computation of x at this point of the instruction stream (the
+// vector-ALU work meant to overlap a matrix instruction would otherwise be
+// sunk to its first use).
+template <typename T>
+__device__ __forceinline__ void pin(T& x) { __asm__ volatile("" : "+v"(x)); }
+
 // Rescale threshold of the lazy online softmax (log2 units): the running max
 // is only moved (and O, l rescaled) when a tile raises some row's max by more
 // than this; otherwise exp2 arguments stay <= kLazy, so P <= 2^kLazy.
@@ -123,11 +147,26 @@ constexpr float kLazy = 8.0f;
 
 // One workgroup = NH query heads of one (batch, kv head, query block); two
 // wavefronts per head, each owning 32 of the 64 query rows (two 16-row tiles).
-// At <= 256 registers per wavefront two wavefronts share a SIMD, so one
-// wavefront's softmax runs while the other's matrix instructions issue.
+// At <= 256 registers per wavefront two wavefronts share a SIMD.
 // SPLIT: P enters O^T += V^T P^T as hi + lo bf16 terms (two MFMAs), which
 // makes O accurate to ~2^-16 relative instead of ~2^-9 (used when o is kept
 // in fp32, so the backward's Delta = rowsum(O dO) is exact to fp32 level).
+//
+// Software pipeline over half tiles: unit u = 2t + kh is keys kh*32 .. +31 of
+// tile t (t = 0: the diagonal block, t = 1 .. cnt: the selected blocks).
+// Window u holds S_{u+1} = K Q^T (matrix core) interleaved with the softmax
+// of S_u (vector ALU), then O^T += V_u^T P_u, and ends with a barrier.
+// K and V tiles live in two LDS slots each; window (t, 0) copies V_{t+1} and
+// window (t, 1) copies K_{t+2} (their slots' previous tiles were last read in
+// window (t - 1, 1) and (t, 0)), and each window waits only for the copies of
+// the window before it.
+template <int NW>
+__device__ __forceinline__ void wait_vm_prev() {   // all but this window's 16 / NW copies
+  if (NW == 8) __asm__ volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  else if (NW == 4) __asm__ volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");
+}
+
 template <int NH, bool SPLIT>
 __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
   constexpr int NW = 2 * NH;
@@ -136,9 +175,9 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int l16 = lane & 15;
-  const int g4 = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;          // half of the 32x32 operand k range
+  const int l32 = lane & 31;        // query column of this lane
   const int half = w & 1;           // rows half*32 .. half*32 + 31 of the block
 
   const int unit = xcd_remap(blockIdx.x, gridDim.x);
@@ -157,190 +196,226 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
   const bf16* vbase = a.v + (long long)bhk * a.N * HD;
   const long long q0 = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + half * 32;
 
-  // Q^T as the B operand of S^T = K Q^T: lane holds row qt*16 + l16 (of this
-  // wavefront's 32) and head dims ks*32 + g4*8 .. +7.
-  bf16x8 qf[2][4];
+  // Q^T as the B operand of S^T = K Q^T (32x32x16): lane holds query row
+  // l32 and head dims ks*16 + g*8 .. +7.
+  bf16x8 qf[8];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qf[qt][ks] = *(const bf16x8*)(a.q + (q0 + qt * 16 + l16) * HD + ks * 32 + g4 * 8);
-
-  auto load_tile = [&](int kb, int stg) {
-    tile_to_lds<NW>(s_k[stg], kbase + (long long)kb * TILE, w, lane);
-    tile_to_lds<NW>(s_v[stg], vbase + (long long)kb * TILE, w, lane);
-  };
-
-  f32x4 oacc[8][2];
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) oacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrow[2], lrow[2];   // running max (log2 units) and per-lane partial sums
-
-  // One 64-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-  auto tile = [&](auto diag_tag, int stg, float beta) {
-    constexpr bool DIAG = decltype(diag_tag)::value;
-    const bf16* Ks = s_k[stg];
-    const bf16* Vs = s_v[stg];
-    f32x4 sacc[4][2];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) sacc[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const bf16x8 ka = *(const bf16x8*)(Ks + swz(kt * 16 + l16, ks * 4 + g4));
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) sacc[kt][qt] = mfma16(ka, qf[qt][ks], sacc[kt][qt]);
-      }
-    }
-    if (DIAG) {   // causal mask inside the current block: key > query -> -inf
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (kt * 16 + g4 * 4 + j > half * 32 + qt * 16 + l16) sacc[kt][qt][j] = -INFINITY;
-    }
-    // tile row max (raw scores; c2 > 0 keeps the order)
-    float tmax[2];
-    bool grow = false;
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      float mx = fmaxf(fmaxf(sacc[0][qt][0], sacc[0][qt][1]), fmaxf(sacc[0][qt][2], sacc[0][qt][3]));
-#pragma unroll
-      for (int kt = 1; kt < 4; ++kt)
-        mx = fmaxf(mx, fmaxf(fmaxf(sacc[kt][qt][0], sacc[kt][qt][1]),
-                             fmaxf(sacc[kt][qt][2], sacc[kt][qt][3])));
-      tmax[qt] = max4(mx) * a.c2 + beta;
-      if (!DIAG) grow |= tmax[qt] > mrow[qt] + kLazy;
-    }
-    if (DIAG) {
-      // first tile: O and l are still zero, the max just starts here
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) { mrow[qt] = tmax[qt]; lrow[qt] = 0.0f; }
-    } else if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform, rare
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const float mnew = fmaxf(mrow[qt], tmax[qt]);
-        const float alpha = __builtin_amdgcn_exp2f(mrow[qt] - mnew);
-        mrow[qt] = mnew;
-        lrow[qt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) oacc[dt][qt] *= alpha;
-      }
-    }
-    // P = exp2(c2 s + beta - m), packed as the B operand of O^T += V^T P^T
-    bf16x8 pb[2][2], pl[2][2];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const float off = beta - mrow[qt];
-      float ps = 0.0f;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][qt][j], a.c2, off));
-          ps += p;
-          const bf16 ph = (bf16)p;
-          pb[kt >> 1][qt][(kt & 1) * 4 + j] = ph;
-          if (SPLIT) pl[kt >> 1][qt][(kt & 1) * 4 + j] = (bf16)(p - (float)ph);
-        }
-      lrow[qt] += ps;
-    }
-    // O^T += V^T P^T; V^T fragments read transposed from the row-major tile:
-    // for head-dim tile dt, rows vr + {0, 16, 32, 48} of column dt*16 + l16
-    // (the swizzle slot depends only on the row mod 16, so the four reads are
-    // 4 KB apart)
-    const int vr = g4 * 4 + (l16 >> 2);
-    const unsigned vbase = lds_addr(Vs) + (unsigned)(vr * HD + (l16 & 1) * 4) * 2;
-#pragma unroll
-    for (int dp = 0; dp < 4; ++dp) {   // two head-dim tiles per batch of reads
-      tr_u32x2 r[8];
-      tr_read_2x4(vbase + (((dp * 4 + ((l16 >> 1) & 1)) ^ slot16(vr)) << 4),
-                  vbase + (((dp * 4 + 2 + ((l16 >> 1) & 1)) ^ slot16(vr)) << 4), r);
-#pragma unroll
-      for (int d2 = 0; d2 < 2; ++d2) {
-        const int dt = dp * 2 + d2;
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const tr_u32x2 lo = r[d2 * 4 + k2 * 2], hi = r[d2 * 4 + k2 * 2 + 1];
-          const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt) {
-            oacc[dt][qt] = mfma16(va, pb[k2][qt], oacc[dt][qt]);
-            if (SPLIT) oacc[dt][qt] = mfma16(va, pl[k2][qt], oacc[dt][qt]);
-          }
-        }
-      }
-    }
-  };
+  for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)(a.q + (q0 + l32) * HD + ks * 16 + g * 8);
 
   // The row's selection, 64 entries at a time, in registers: lane e holds
-  // block sel[e0 + e] and its log gate (log2 units); the tile loop reads them
-  // with readlane, so it issues no global loads besides the tile copies.
+  // block sel[e0 + e] and its log gate (log2 units); read with readlane.
   int selv = 0;
   float betav = 0.0f;
+  int selwin = 0;   // e0 / 64 of the entries in selv
   auto load_sel = [&](int e0) {
     const int e = e0 + lane;
     selv = e < cnt ? sel[e] : 0;
     betav = e < cnt ? lgrow[selv] * kLog2e : 0.0f;
     settle(betav);
   };
-
-  const int ntiles = cnt + 1;
+  // block and log gate of tile t (t = 0: the diagonal block, gate 0; tiles
+  // past the end: the diagonal block again); asked for in increasing order
+  const int nt = cnt + 1;
+  auto tile_block = [&](int t, float& beta) -> int {
+    if (t == 0 || t >= nt) { beta = 0.0f; return i; }
+    const int e = t - 1;
+    if ((e >> 6) != selwin) { selwin = e >> 6; load_sel(selwin * 64); }
+    beta = lane_value(betav, e & 63);
+    return lane_value(selv, e & 63);
+  };
   load_sel(0);
-  load_tile(i, 0);
-  wait_vm();
-  __syncthreads();
-  // diagonal tile (unit gate, causal); the next tile streams into the other stage
-  float nbeta = 0.0f;   // log gate of the tile in the other stage
-  if (ntiles > 1) {
-    load_tile(lane_value(selv, 0), 1);
-    nbeta = lane_value(betav, 0);
-  }
-  tile(std::true_type{}, 0, 0.0f);
-  wait_vm();
-  __syncthreads();
-  // selected tiles (additive log gate)
-  for (int t = 1; t < ntiles; ++t) {
-    const int stg = t & 1;
-    const float beta = nbeta;
-    if (t + 1 < ntiles) {   // entry t of the selection feeds tile t + 1
-      if ((t & 63) == 0) load_sel(t);
-      load_tile(lane_value(selv, t & 63), stg ^ 1);
-      nbeta = lane_value(betav, t & 63);
-    }
-    tile(std::false_type{}, stg, beta);
-    wait_vm();
-    __syncthreads();
-  }
 
-  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
+  // O^T (lane: head dims dt*32 + 8 (jj/4) + 4 g + jj%4, query l32)
+  f32x16 oacc[4];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const float ltot = sum4(lrow[qt]);
-    const float inv = 1.0f / ltot;
-    const long long qrow = q0 + qt * 16 + l16;
-    if (g4 == 0) a.lse[qrow] = (mrow[qt] + log2f(ltot)) * kLn2;
-    if (a.o_fp32) {
-      float* op = (float*)a.o + qrow * HD + g4 * 4;
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) *(f32x4*)(op + dt * 16) = oacc[dt][qt] * inv;
+    for (int x = 0; x < 16; ++x) oacc[dt][x] = 0.0f;
+  float mrow, lrow = 0.0f;   // running max (log2 units), per-lane partial sum
+
+  // S^T of keys kh*32 .. +31 of the K tile in Ks (lane: query l32, keys
+  // 8 (jj/4) + 4 g + jj%4); after MFMA m (m = 0..7) the work per_mfma(m) is
+  // issued (sched_barrier keeps the interleave)
+  auto scores_with = [&](const bf16* Ks, int kh, f32x16& sc, auto&& per_mfma) {
+    bf16x8 ka[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) ka[ks] = *(const bf16x8*)(Ks + swz(kh * 32 + l32, ks * 2 + g));
+#pragma unroll
+    for (int x = 0; x < 16; ++x) sc[x] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      sc = mfma32(ka[ks], qf[ks], sc);
+      per_mfma(ks);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // causal mask of the diagonal tile: key > query -> -inf
+  auto mask_diag = [&](int kh, f32x16& sc) {
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj)
+      if (kh * 32 + (jj >> 2) * 8 + g * 4 + (jj & 3) > half * 32 + l32) sc[jj] = -INFINITY;
+  };
+  // running max over a unit's keys (FIRST: the max starts here; otherwise O
+  // and l are rescaled only when the row's max grows by more than kLazy)
+  auto update_max = [&](auto first_tag, const f32x16& sc, float beta) {
+    constexpr bool FIRST = decltype(first_tag)::value;
+    float mx = sc[0];
+#pragma unroll
+    for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, sc[jj]);
+    const float tmax = max2(mx) * a.c2 + beta;
+    if (FIRST) {
+      mrow = tmax;
+    } else if (__builtin_amdgcn_ballot_w64(tmax > mrow + kLazy) != 0) {   // wave-uniform, rare
+      const float mnew = fmaxf(mrow, tmax);
+      const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
+      mrow = mnew;
+      lrow *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
+    }
+  };
+  // P element pair n (n = 0..7) of a unit: P = exp2(c2 s + beta - m), summed
+  // into l and packed (hi, and lo when SPLIT) into the B operand of
+  // O^T += V^T P^T: element jj -> k-slice jj / 8, word (jj % 8) / 2
+  auto p_pair = [&](int n, const f32x16& sc, float off, uint32_t (&pb)[2][4], uint32_t (&pl)[2][4]) {
+    const int jj = 2 * n;
+    const f32x2 pp = {__builtin_amdgcn_exp2f(fmaf(sc[jj], a.c2, off)),
+                      __builtin_amdgcn_exp2f(fmaf(sc[jj + 1], a.c2, off))};
+    lrow += pp[0] + pp[1];
+    const bf16x2 hi = __builtin_convertvector(pp, bf16x2);
+    uint32_t wh = __builtin_bit_cast(uint32_t, hi);
+    pin(wh);
+    pb[jj >> 3][(jj & 7) >> 1] = wh;
+    if (SPLIT) {
+      const bf16x2 lo = __builtin_convertvector(pp - __builtin_convertvector(hi, f32x2), bf16x2);
+      uint32_t wl = __builtin_bit_cast(uint32_t, lo);
+      pin(wl);
+      pl[jj >> 3][(jj & 7) >> 1] = wl;
+    }
+  };
+  // O^T += V^T P^T over keys kh*32 .. +31.  V^T fragments (A operand, lane:
+  // head dim dt*32 + l32, keys 16 sl + {4g .. 4g+3, 8+4g .. 8+4g+3}) come from
+  // transposed reads of the row-major V tile.
+  const int u = lane & 15;
+  const int dhalf = (lane >> 4) & 1;
+  int tro[4][2];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      tro[dt][hh] = swz(g * 4 + (u >> 2) + 8 * hh, dt * 4 + dhalf * 2 + ((u >> 1) & 1)) + (u & 1) * 4;
+  auto pv = [&](const bf16* Vs, int kh, const uint32_t (&pbw)[2][4], const uint32_t (&plw)[2][4]) {
+    bf16x8 pb[2], pl[2];
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      pb[sl] = __builtin_bit_cast(bf16x8, u32x4{pbw[sl][0], pbw[sl][1], pbw[sl][2], pbw[sl][3]});
+      pl[sl] = __builtin_bit_cast(bf16x8, u32x4{plw[sl][0], plw[sl][1], plw[sl][2], plw[sl][3]});
+    }
+    bf16x8 va[4][2];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        const bf16* vp = Vs + (kh * 32 + sl * 16) * HD;
+        va[dt][sl] = __builtin_shufflevector(ds_read_tr(vp + tro[dt][0]), ds_read_tr(vp + tro[dt][1]),
+                                             0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        oacc[dt] = mfma32(va[dt][sl], pb[sl], oacc[dt]);
+        if (SPLIT) oacc[dt] = mfma32(va[dt][sl], pl[sl], oacc[dt]);
+      }
+  };
+
+  auto copy_k = [&](int kb, int slot) { tile_to_lds<NW>(s_k[slot], kbase + (long long)kb * TILE, w, lane); };
+  auto copy_v = [&](int kb, int slot) { tile_to_lds<NW>(s_v[slot], vbase + (long long)kb * TILE, w, lane); };
+
+  // prologue: K_0, V_0, K_1 in; S of unit 0 (masked) starts the running max
+  float beta1 = 0.0f;
+  copy_k(i, 0);
+  copy_v(i, 0);
+  copy_k(tile_block(1, beta1), 1);
+  wait_vm();
+  __syncthreads();
+  f32x16 s0, s1;   // S of the unit being finished / the next unit
+  scores_with(s_k[0], 0, s0, [](int) {});
+  mask_diag(0, s0);
+  update_max(std::true_type{}, s0, 0.0f);
+
+  // window (t, kh): copy (V_{t+1} for kh = 0, K_{t+2} for kh = 1); S of the
+  // next unit with the softmax of this one; O += V^T P; barrier; max of the
+  // next unit
+  float beta_cur = 0.0f;   // gate of tile t
+  float beta_v = beta1;    // gate of the tile whose V was copied last (t + 1)
+  auto window = [&](auto kh_tag, auto diag_tag, int t, f32x16& scur, f32x16& snext) {
+    constexpr int KH = decltype(kh_tag)::value;
+    constexpr bool DIAG = decltype(diag_tag)::value;
+    const bool more = KH == 0 || t + 1 < nt;   // is there a next unit
+    if (KH == 0) {
+      copy_v(tile_block(t + 1, beta_v), (t + 1) & 1);
     } else {
-      bf16* op = (bf16*)a.o + qrow * HD + g4 * 4;
+      float bk;
+      copy_k(tile_block(t + 2, bk), t & 1);
+    }
+    const float off = beta_cur - mrow;
+    uint32_t pb[2][4], pl[2][4];
+    // next unit: (t, 1) reads K_t, (t + 1, 0) reads K_{t+1}
+    const bf16* kn = KH == 0 ? s_k[t & 1] : s_k[(t + 1) & 1];
+    if (more) {
+      scores_with(kn, KH ^ 1, snext, [&](int m) { p_pair(m, scur, off, pb, pl); });
+    } else {
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        bf16x4 r;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) r[j] = (bf16)(oacc[dt][qt][j] * inv);
-        *(bf16x4*)(op + dt * 16) = r;
+      for (int n = 0; n < 8; ++n) p_pair(n, scur, off, pb, pl);
+    }
+    pv(s_v[t & 1], KH, pb, pl);
+    wait_vm_prev<NW>();
+    __syncthreads();
+    if (more) {
+      if (KH == 0) {
+        if (DIAG) mask_diag(1, snext);
+        update_max(std::false_type{}, snext, beta_cur);
+      } else {
+        beta_cur = beta_v;   // tile t + 1
+        update_max(std::false_type{}, snext, beta_cur);
       }
     }
+  };
+  window(std::integral_constant<int, 0>{}, std::true_type{}, 0, s0, s1);
+  window(std::integral_constant<int, 1>{}, std::true_type{}, 0, s1, s0);
+#pragma unroll 1
+  for (int t = 1; t < nt; ++t) {
+    window(std::integral_constant<int, 0>{}, std::false_type{}, t, s0, s1);
+    window(std::integral_constant<int, 1>{}, std::false_type{}, t, s1, s0);
+  }
+  wait_vm();   // trailing copies
+
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
+  const float ltot = sum2(lrow);
+  const float inv = 1.0f / ltot;
+  const long long qrow = q0 + l32;
+  if (g == 0) a.lse[qrow] = (mrow + log2f(ltot)) * kLn2;
+  if (a.o_fp32) {
+    float* op = (float*)a.o + qrow * HD + g * 4;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *(f32x4*)(op + dt * 32 + q4 * 8) =
+            f32x4{oacc[dt][q4 * 4] * inv, oacc[dt][q4 * 4 + 1] * inv, oacc[dt][q4 * 4 + 2] * inv,
+                  oacc[dt][q4 * 4 + 3] * inv};
+  } else {
+    bf16* op = (bf16*)a.o + qrow * HD + g * 4;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 r;
+#pragma unroll
+        for (int y = 0; y < 4; ++y) r[y] = (bf16)(oacc[dt][q4 * 4 + y] * inv);
+        *(bf16x4*)(op + dt * 32 + q4 * 8) = r;
+      }
   }
 }
 
