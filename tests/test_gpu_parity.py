@@ -148,3 +148,37 @@ def test_long_context_sampled():
     w = workloads.WORKLOADS["qwen3_8b_128k"]
     log(f"workload {w.name}")
     sampled_parity(w, w.budgets[0], n_units=6, n_kv_blocks=3)
+
+
+# --------------------------------------------------------------------------
+# staged backward (the calls the benchmark times) == combined backward
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(1, 8, 2, 2048, 128, 64, 4, "bf16"),    # matrix-core path
+                                   (1, 2, 1, 512, 64, 32, 3, "bf16")],     # vector-ALU path
+                         ids=["mfma", "generic"])
+def test_staged_backward_matches_combined(shape):
+    """sas_gated_attn_bwd_dq followed by sas_gated_attn_bwd_dkdv reproduces
+    sas_gated_attn_bwd bit for bit (both run the same kernels in the same
+    order; the staged form is what the benchmark times)."""
+    B, Hq, Hkv, N, D, blk, K, dt = shape
+    log(f"staged backward {shape}")
+    w = workloads.custom(B, Hq, Hkv, N, D, blk, K, dtype=dt, seed=11, score_std=2.0)
+    p = problem_of(w, K)
+    inp = workloads.generate(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do, sc = (inp[n].to(dev) for n in ("q", "k", "v", "do", "scores"))
+    lg, tau, si, cnt = api.gate_threshold(p, sc)
+    o, lse = api.gated_attn_fwd(p, q, k, v, lg, si, cnt)
+    ref = api.gated_attn_bwd(p, q, k, v, o, do, lse, lg, si, cnt)
+    ws = torch.empty(api.bwd_workspace_size(p, si.shape[-1]), dtype=torch.uint8, device=dev)
+    dq = torch.full_like(q, float("nan"))
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(v, float("nan"))
+    dlg = torch.full_like(lg, float("nan"))
+    dsc = torch.full_like(lg, float("nan"))
+    api.gated_attn_bwd_dq(p, q, k, v, o, do, lse, lg, si, cnt, dq, dlg, dsc, ws)
+    api.gated_attn_bwd_dkdv(p, q, k, v, do, lse, lg, si, cnt, dk, dv, ws)
+    torch.cuda.synchronize()
+    for name, got, want in zip(("dq", "dk", "dv", "dlog_gate", "dscores"), (dq, dk, dv, dlg, dsc), ref):
+        assert torch.equal(got.cpu(), want.cpu()), f"{name} differs between staged and combined backward"
