@@ -3,8 +3,8 @@
 
 One step = the whole hot path on one batch of synthetic input already resident
 in HBM: gate activation + Top-K threshold (sas_gate_threshold), forward
-(sas_gated_attn_fwd) and backward (sas_gated_attn_bwd_dq, which also writes
-dlog_gate and dscores, then sas_gated_attn_bwd_dkdv).
+(sas_gated_attn_fwd) and backward (sas_gated_attn_bwd_dq, then
+sas_gated_attn_bwd_dkdv, which also writes dlog_gate and dscores).
 
 Metric: fwd+bwd effective TFLOP/s = 14 * D * pairs / step time, where pairs
 counts only the attended (query, key) pairs: per query block the causal
@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3_8b_32k")
     ap.add_argument("--budget", type=int, default=None)
-    ap.add_argument("--o-dtype", default="fp32", choices=["fp32", "bf16"])
+    ap.add_argument("--o-dtype", default="bf16", choices=["fp32", "bf16"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -198,10 +198,10 @@ def main():
         api.gated_attn_fwd(p, q, k, v, lg, sel_idx, sel_cnt, o=o, lse=lse)
         if ev is not None:
             ev[2].record()
-        api.gated_attn_bwd_dq(p, q, k, v, o, do, lse, lg, sel_idx, sel_cnt, dq, dlg, dsc, ws)
+        api.gated_attn_bwd_dq(p, q, k, v, o, do, lse, lg, sel_idx, sel_cnt, dq, ws)
         if ev is not None:
             ev[3].record()
-        api.gated_attn_bwd_dkdv(p, q, k, v, do, lse, lg, sel_idx, sel_cnt, dk, dv, ws)
+        api.gated_attn_bwd_dkdv(p, q, k, v, do, lse, lg, sel_idx, sel_cnt, dk, dv, dlg, dsc, ws)
         if ev is not None:
             ev[4].record()
 

@@ -50,9 +50,9 @@ SIGNATURES = {
     "sas_gated_attn_bwd": ([_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                             _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp], _i32),
     "sas_gated_attn_bwd_dq": ([_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
-                               _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp], _i32),
+                               _vp, _vp, ctypes.c_size_t, _vp], _i32),
     "sas_gated_attn_bwd_dkdv": ([_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
-                                 _vp, _vp, _vp, ctypes.c_size_t, _vp], _i32),
+                                 _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp], _i32),
 }
 
 _lib = None

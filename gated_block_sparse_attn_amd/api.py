@@ -34,8 +34,12 @@ class Problem:
     budget_k: int
     dtype: str = "bf16"        # "bf16" or "fp32": q, k, v, dO and the gradients
     sm_scale: float = 0.0      # <= 0: 1/sqrt(head_dim)
-    o_dtype: str = "fp32"      # dtype of the forward output o ("fp32" keeps the
-                               # backward's Delta = rowsum(o dO) unrounded)
+    o_dtype: str = "bf16"      # dtype of the forward output o (fp32 problems:
+                               # always "fp32")
+
+    def __post_init__(self):
+        if self.dtype == "fp32" and self.o_dtype != "fp32":
+            object.__setattr__(self, "o_dtype", "fp32")
 
     @property
     def n_blocks(self) -> int:
@@ -61,7 +65,7 @@ class Problem:
 
     @staticmethod
     def from_tensors(q: torch.Tensor, k: torch.Tensor, block_size: int, budget_k: int,
-                     sm_scale: float = 0.0, o_dtype: str = "fp32") -> "Problem":
+                     sm_scale: float = 0.0, o_dtype: str = "bf16") -> "Problem":
         b, hq, n, d = q.shape
         dt = "bf16" if q.dtype == torch.bfloat16 else "fp32"
         return Problem(b, hq, k.shape[1], n, d, block_size, budget_k, dt, sm_scale,
@@ -227,32 +231,31 @@ def _check_bwd_inputs(p, q, k, v, do, lse, log_gate, sel_idx, sel_cnt, o=None):
 
 
 def gated_attn_bwd_dq(p: Problem, q, k, v, o, do, lse, log_gate, sel_idx, sel_cnt, dq,
-                      dlog_gate, dscores, workspace, stream=None):
+                      workspace, stream=None):
     """sas_gated_attn_bwd_dq (first backward stage) into preallocated outputs."""
     cap, sh = _check_bwd_inputs(p, q, k, v, do, lse, log_gate, sel_idx, sel_cnt, o)
     _expect(dq, "dq", sh["q"], p.torch_dtype)
-    _expect(dlog_gate, "dlog_gate", sh["table"], torch.float32)
-    if dscores is not None:
-        _expect(dscores, "dscores", sh["table"], torch.float32)
     pc = p.c()
     check(lib().sas_gated_attn_bwd_dq(ctypes_ref(pc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                       _ptr(do), _ptr(lse), _ptr(log_gate), _ptr(sel_idx),
-                                      _ptr(sel_cnt), cap, _ptr(dq), _ptr(dlog_gate),
-                                      _ptr(dscores), _ptr(workspace), workspace.numel(),
-                                      _stream(stream)))
+                                      _ptr(sel_cnt), cap, _ptr(dq), _ptr(workspace),
+                                      workspace.numel(), _stream(stream)))
 
 
 def gated_attn_bwd_dkdv(p: Problem, q, k, v, do, lse, log_gate, sel_idx, sel_cnt, dk, dv,
-                        workspace, stream=None):
+                        dlog_gate, dscores, workspace, stream=None):
     """sas_gated_attn_bwd_dkdv (second backward stage) into preallocated outputs."""
     cap, sh = _check_bwd_inputs(p, q, k, v, do, lse, log_gate, sel_idx, sel_cnt)
     _expect(dk, "dk", sh["kv"], p.torch_dtype)
     _expect(dv, "dv", sh["kv"], p.torch_dtype)
+    _expect(dlog_gate, "dlog_gate", sh["table"], torch.float32)
+    if dscores is not None:
+        _expect(dscores, "dscores", sh["table"], torch.float32)
     pc = p.c()
     check(lib().sas_gated_attn_bwd_dkdv(ctypes_ref(pc), _ptr(q), _ptr(k), _ptr(v), _ptr(do),
                                         _ptr(lse), _ptr(log_gate), _ptr(sel_idx), _ptr(sel_cnt),
-                                        cap, _ptr(dk), _ptr(dv), _ptr(workspace),
-                                        workspace.numel(), _stream(stream)))
+                                        cap, _ptr(dk), _ptr(dv), _ptr(dlog_gate), _ptr(dscores),
+                                        _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def ctypes_ref(pc: SasProblem):

@@ -105,8 +105,6 @@ BwdWorkspace bwd_workspace_layout(const Shape& s) {
   size_t off = 0;
   w.delta = off;    off = align256(off + sizeof(float) * (size_t)s.B * s.Hq * s.N);
   if (mfma_path(s)) {
-    w.dlg_part = off;
-    off = align256(off + sizeof(float) * (size_t)bwd_head_parts(s.G) * nrow * (s.cap + 1));
     w.colmask = off;  off = align256(off + sizeof(uint32_t) * (size_t)nrow * w.words);
     w.collen = off;   off = align256(off + sizeof(int32_t) * (size_t)nrow);
     w.coloff = off;   off = align256(off + sizeof(int32_t) * (size_t)(nrow + 1));
@@ -181,8 +179,8 @@ int32_t run_bwd(const char* name, int stages, const sas_problem* p, const sas::B
   if (rc != SAS_OK) return rc;
   bool missing = !ptr.q || !ptr.k || !ptr.v || !ptr.d_o || !ptr.lse || !ptr.log_gate ||
                  !ptr.sel_idx || !ptr.sel_cnt;
-  if (stages & kStageDq) missing = missing || !ptr.o || !ptr.dq || !ptr.dlog_gate;
-  if (stages & kStageDkdv) missing = missing || !ptr.dk || !ptr.dv;
+  if (stages & kStageDq) missing = missing || !ptr.o || !ptr.dq;
+  if (stages & kStageDkdv) missing = missing || !ptr.dk || !ptr.dv || !ptr.dlog_gate;
   if (missing) return fail(SAS_E_INVALID, "%s: a required pointer is NULL", name);
   const sas::BwdWorkspace wl = sas::bwd_workspace_layout(s);
   if (workspace == nullptr || workspace_bytes < wl.total)
@@ -222,11 +220,10 @@ int32_t sas_gated_attn_bwd(const sas_problem* p, const void* q, const void* k, c
 int32_t sas_gated_attn_bwd_dq(const sas_problem* p, const void* q, const void* k, const void* v,
                               const void* o, const void* d_o, const float* lse,
                               const float* log_gate, const int32_t* sel_idx,
-                              const int32_t* sel_cnt, int32_t sel_cap, void* dq, float* dlog_gate,
-                              float* dscores, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+                              const int32_t* sel_cnt, int32_t sel_cap, void* dq, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   const sas::BwdPtrs ptr{q, k, v, o, d_o, lse, log_gate, sel_idx, sel_cnt,
-                         dq, nullptr, nullptr, dlog_gate, dscores};
+                         dq, nullptr, nullptr, nullptr, nullptr};
   return run_bwd("sas_gated_attn_bwd_dq", kStageDq, p, ptr, sel_cap, workspace, workspace_bytes,
                  stream);
 }
@@ -235,9 +232,10 @@ int32_t sas_gated_attn_bwd_dkdv(const sas_problem* p, const void* q, const void*
                                 const void* v, const void* d_o, const float* lse,
                                 const float* log_gate, const int32_t* sel_idx,
                                 const int32_t* sel_cnt, int32_t sel_cap, void* dk, void* dv,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+                                float* dlog_gate, float* dscores, void* workspace,
+                                size_t workspace_bytes, void* stream) {
   const sas::BwdPtrs ptr{q, k, v, nullptr, d_o, lse, log_gate, sel_idx, sel_cnt,
-                         nullptr, dk, dv, nullptr, nullptr};
+                         nullptr, dk, dv, dlog_gate, dscores};
   return run_bwd("sas_gated_attn_bwd_dkdv", kStageDkdv, p, ptr, sel_cap, workspace,
                  workspace_bytes, stream);
 }

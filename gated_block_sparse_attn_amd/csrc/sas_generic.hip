@@ -7,10 +7,11 @@
 //  forward  (SAS Sec. 4.3 Eq. 9, App. E Alg. 3): per query block the current
 //           block (causal, bias 0) and the selected historical blocks (bias
 //           log g), streamed tile by tile with an online softmax in base 2;
-//  backward (App. E Alg. 4): Delta = rowsum(O dO), P recomputed from LSE,
-//           dS = P (dP - Delta), dQ = scale dS K, dLogG = block sums of dS
-//           (query-major pass), dK = scale dS^T Q and dV = P^T dO
-//           (key-major pass).
+//  backward (App. E Alg. 4): P recomputed from LSE, dS = P (dP - Delta);
+//           query-major pass: dQ = scale dS K with Delta = rowsum(O dO), and
+//           the row sum of P dP (Delta without the rounding of O); key-major
+//           pass, with that Delta: dK = scale dS^T Q, dV = P^T dO and
+//           dLogG = block sums of dS.
 //
 // One thread owns one query row (forward, dQ pass) or one key row (dK/dV
 // pass); K/V tiles are staged in LDS as fp32.
@@ -115,7 +116,7 @@ __global__ void __launch_bounds__(64) fwd_generic_kernel(GenArgs a) {
   }
 }
 
-// Query-major backward: Delta, dQ and the block log-gate gradient.
+// Query-major backward: dQ, and Delta = sum of P dP over each query row.
 template <typename T, int D, int BLK>
 __global__ void __launch_bounds__(64) bwd_q_generic_kernel(GenArgs a) {
   extern __shared__ float smem[];
@@ -131,19 +132,12 @@ __global__ void __launch_bounds__(64) bwd_q_generic_kernel(GenArgs a) {
   const int32_t* sel = a.sel_idx + row * a.cap;
   const T* kbase = (const T*)a.k + ((long long)bb * a.Hkv + hk) * a.N * D;
   const T* vbase = (const T*)a.v + ((long long)bb * a.Hkv + hk) * a.N * D;
-  float* dlg_row = a.dlg + row * a.C;
-
-  // The whole dLogG row is owned by this workgroup: clear it, then let lane 0
-  // accumulate the selected entries (one wavefront: a fixed summation order).
-  for (int m = t; m < a.C; m += blockDim.x) dlg_row[m] = 0.0f;
-  __threadfence();
-  __syncthreads();
 
   for (int hl = 0; hl < a.G; ++hl) {
     const int h = hk * a.G + hl;
     const long long qi = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + t;
     float q[D], dov[D], dq[D];
-    float delta = 0.0f, lse2 = 0.0f;
+    float delta = 0.0f, lse2 = 0.0f, dx = 0.0f;
     if (active) {
       const T* qrow = (const T*)a.q + qi * D;
       const T* drow = (const T*)a.d_o + qi * D;
@@ -156,7 +150,6 @@ __global__ void __launch_bounds__(64) bwd_q_generic_kernel(GenArgs a) {
         dq[d] = 0.0f;
       }
       lse2 = a.lse[qi] * kLog2e;
-      a.delta[qi] = delta;
     } else {
 #pragma unroll
       for (int d = 0; d < D; ++d) { q[d] = 0.0f; dov[d] = 0.0f; dq[d] = 0.0f; }
@@ -168,7 +161,6 @@ __global__ void __launch_bounds__(64) bwd_q_generic_kernel(GenArgs a) {
       stage_tile<T, D, BLK>(ks, kbase + (long long)kb * BLK * D);
       stage_tile<T, D, BLK>(vs, vbase + (long long)kb * BLK * D);
       __syncthreads();
-      float tsum = 0.0f;
       if (active) {
 #pragma unroll 1
         for (int u = 0; u < BLK; ++u) {
@@ -181,17 +173,14 @@ __global__ void __launch_bounds__(64) bwd_q_generic_kernel(GenArgs a) {
           }
           const float p = exp2f(x * a.c2 + beta - lse2);
           const float ds = p * (dp - delta);
-          tsum += ds;
+          dx += p * dp;
 #pragma unroll
           for (int d = 0; d < D; ++d) dq[d] += ds * ks[u * D + d];
         }
       }
-      if (tile > 0) {
-        tsum = wave_sum(tsum);
-        if (t == 0) dlg_row[kb] += tsum;
-      }
     }
     if (active) {
+      a.delta[qi] = dx;
       T* dqrow = (T*)a.dq + qi * D;
 #pragma unroll
       for (int d = 0; d < D; ++d) st(dqrow + d, dq[d] * a.scale);
@@ -199,8 +188,10 @@ __global__ void __launch_bounds__(64) bwd_q_generic_kernel(GenArgs a) {
   }
 }
 
-// Key-major backward: dK and dV of one key block, over every query block that
-// attends it (the diagonal block and each later block that selected it).
+// Key-major backward: dK and dV of one key block j, over every query block
+// that attends it (the diagonal block and each later block that selected it),
+// and column j of the dLogG table (every entry written: the dS sum of a
+// selecting block i > j, else 0; one wavefront, fixed summation order).
 template <typename T, int D, int BLK>
 __global__ void __launch_bounds__(64) bwd_kv_generic_kernel(GenArgs a) {
   extern __shared__ float smem[];
@@ -220,6 +211,7 @@ __global__ void __launch_bounds__(64) bwd_kv_generic_kernel(GenArgs a) {
 #pragma unroll
   for (int d = 0; d < D; ++d) { dk[d] = 0.0f; dv[d] = 0.0f; }
   const long long rowbase = ((long long)bb * a.Hkv + hk) * a.C;
+  for (int i = u; i <= j && i < a.C; i += blockDim.x) a.dlg[(rowbase + i) * a.C + j] = 0.0f;
   for (int i = j; i < a.C; ++i) {
     float beta = 0.0f;
     if (i != j) {
@@ -231,9 +223,13 @@ __global__ void __launch_bounds__(64) bwd_kv_generic_kernel(GenArgs a) {
         const int mid = (lo + hi) >> 1;
         if (sel[mid] < j) lo = mid + 1; else hi = mid;
       }
-      if (lo >= cnt || sel[lo] != j) continue;
+      if (lo >= cnt || sel[lo] != j) {
+        if (u == 0) a.dlg[(rowbase + i) * a.C + j] = 0.0f;
+        continue;
+      }
       beta = a.lg[(rowbase + i) * a.C + j] * kLog2e;
     }
+    float gsum = 0.0f;
     for (int hl = 0; hl < a.G; ++hl) {
       const int h = hk * a.G + hl;
       const long long q0 = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK;
@@ -250,12 +246,17 @@ __global__ void __launch_bounds__(64) bwd_kv_generic_kernel(GenArgs a) {
         }
         const float p = exp2f(x * a.c2 + beta - a.lse[q0 + tq] * kLog2e);
         const float ds = p * (dp - a.delta[q0 + tq]);
+        gsum += ds;
 #pragma unroll
         for (int d = 0; d < D; ++d) {
           dv[d] += p * ld(drow + d);
           dk[d] += ds * ld(qrow + d);
         }
       }
+    }
+    if (i != j) {
+      gsum = wave_sum(gsum);
+      if (u == 0) a.dlg[(rowbase + i) * a.C + j] = gsum;
     }
   }
   if (active) {
@@ -355,17 +356,18 @@ hipError_t launch_bwd_dq_generic(const Shape& s, const BwdPtrs& p, char* ws,
     using T = std::remove_pointer_t<decltype(tp)>;
     return bwd_q_launch<T, decltype(dc)::value, decltype(bc)::value>(a, s, st);
   });
-  if (e != hipSuccess || p.dscores == nullptr) return e;
-  return launch_dscores(s, p.dlog_gate, p.log_gate, p.dscores, st);
+  return e;
 }
 
 hipError_t launch_bwd_dkdv_generic(const Shape& s, const BwdPtrs& p, char* ws,
                                    const BwdWorkspace& wl, hipStream_t st) {
   const GenArgs a = bwd_args(s, p, ws, wl);
-  return dispatch(s, [&](auto tp, auto dc, auto bc) {
+  hipError_t e = dispatch(s, [&](auto tp, auto dc, auto bc) {
     using T = std::remove_pointer_t<decltype(tp)>;
     return bwd_kv_launch<T, decltype(dc)::value, decltype(bc)::value>(a, s, st);
   });
+  if (e != hipSuccess || p.dscores == nullptr) return e;
+  return launch_dscores(s, p.dlog_gate, p.log_gate, p.dscores, st);
 }
 
 }  // namespace sas

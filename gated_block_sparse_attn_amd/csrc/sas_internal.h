@@ -28,8 +28,7 @@ struct Shape {
 
 // Workspace carve-up of the backward pass (byte offsets, 256-aligned).
 struct BwdWorkspace {
-  size_t delta;      // float  [B*Hq*N]              rowsum(O * dO)
-  size_t dlg_part;   // float  [parts*B*Hkv*C*(cap+1)] per-head-chunk dLogG partials
+  size_t delta;      // float  [B*Hq*N]              Delta: sum of P * dP over a query row
   size_t colmask;    // uint32 [B*Hkv*C*W]           bit (j, i): row i selected block j
   size_t collen;     // int32  [B*Hkv*C]             1 + #rows selecting column j
   size_t coloff;     // int32  [B*Hkv*C + 1]         prefix of collen
@@ -48,7 +47,6 @@ struct BwdWorkspace {
 constexpr int kColChunk = 16;
 
 bool mfma_path(const Shape& s);
-int bwd_head_parts(int G);   // head chunks (of 4, 2, 1) the matrix-core passes use
 BwdWorkspace bwd_workspace_layout(const Shape& s);
 
 // ---- launchers (return the hipError_t of the last launch) ----
@@ -61,8 +59,9 @@ hipError_t launch_dscores(const Shape& s, const float* dlog_gate, const float* l
 hipError_t launch_fwd_generic(const Shape& s, const void* q, const void* k, const void* v,
                               const float* log_gate, const int32_t* sel_idx,
                               const int32_t* sel_cnt, void* o, float* lse, hipStream_t st);
-// Backward stages.  Stage "dq": Delta, dq, dlog_gate (+ dscores if non-null)
-// and, on the matrix-core path, the selection transpose.  Stage "dkdv": dk, dv.
+// Backward stages.  Stage "dq": dq, Delta (sum of P dP per query row, in the
+// workspace) and, on the matrix-core path, the selection transpose.  Stage
+// "dkdv": dk, dv, dlog_gate (+ dscores if non-null).
 struct BwdPtrs {
   const void* q; const void* k; const void* v; const void* o; const void* d_o;
   const float* lse; const float* log_gate; const int32_t* sel_idx; const int32_t* sel_cnt;

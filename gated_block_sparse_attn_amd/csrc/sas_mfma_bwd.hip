@@ -58,13 +58,12 @@ struct BwdArgs {
   const float* lse; const float* lg; const int32_t* sel_idx; const int32_t* sel_cnt;
   bf16* dq; bf16* dk; bf16* dv; float* dlg; float* dsc;
   float* delta;
-  float* dlg_part;
   uint32_t* colmask; int32_t* collen; int32_t* coloff; int32_t* chunkoff; int32_t* collist;
   float* partial;
   int32_t* chunk_rank; int32_t* chunk_hist; int32_t* chunk_order;
   long long ncol;  // B * Hkv * C (rows of the score table == columns)
   int Hq, Hkv, G, N, C, cap, W, o_fp32;
-  int head_base, nchunk, part_base, nparts;
+  int head_base, nchunk;
   float c2, scale;
 };
 
@@ -138,7 +137,6 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
   constexpr int NW = 2 * NH;
   __shared__ __attribute__((aligned(16))) bf16 s_k[2][TILE];
   __shared__ __attribute__((aligned(16))) bf16 s_v[2][TILE];
-  __shared__ float s_red[2][NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -162,7 +160,6 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
   const bf16* kbase = a.k + (long long)bhk * a.N * HD;
   const bf16* vbase = a.v + (long long)bhk * a.N * HD;
   const long long q0 = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + half * 32;
-  float* part = a.dlg_part + ((long long)(a.part_base + chunk) * a.ncol + row) * (a.cap + 1);
 
   auto load_tile = [&](int kb, int stg) {
     tile_to_lds<NW>(s_k[stg], kbase + (long long)kb * TILE, w, lane);
@@ -171,9 +168,12 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
   const int ntiles = cnt + 1;
   load_tile(i, 0);
 
-  // Q^T and dO^T as B operands (lane: row qt*16 + l16, dims ks*32 + g4*8 .. +7)
+  // Q^T and dO^T as B operands (lane: row qt*16 + l16, dims ks*32 + g4*8 .. +7);
+  // dlt = rowsum(O * dO) (the Delta of dS in this pass), dx = the row's
+  // sum of P * dP over every attended key (the same quantity without the
+  // rounding of O; the key-major pass uses it)
   bf16x8 qf[2][4], dof[2][4];
-  float lse2[2], dlt[2];
+  float lse2[2], dlt[2], dx[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     const long long r = q0 + qt * 16 + l16;
@@ -197,9 +197,8 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
         for (int x = 0; x < 8; ++x) part_d += (float)ob[x] * (float)dof[qt][ks][x];
       }
     }
-    dlt[qt] = sum4(part_d);   // Delta = rowsum(O * dO) over the 4 lanes of the row
+    dlt[qt] = sum4(part_d);   // over the 4 lanes of the row
     lse2[qt] = a.lse[r] * kLog2e;
-    if (g4 == 0) a.delta[r] = dlt[qt];
   }
 
   f32x4 dqacc[8][2];
@@ -208,13 +207,12 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) dqacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // One 64-key tile: recompute S^T and dP^T, form dS, accumulate dQ^T and the
-  // tile's dS sum.
-  auto tile = [&](auto diag_tag, int stg, float beta) -> float {
+  // One 64-key tile: recompute S^T and dP^T, form dS, accumulate dQ^T and
+  // the rows' P * dP sums.
+  auto tile = [&](auto diag_tag, int stg, float beta) {
     constexpr bool DIAG = decltype(diag_tag)::value;
     const bf16* Ks = s_k[stg];
     const bf16* Vs = s_v[stg];
-    float tsum = 0.0f;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {   // two halves of 32 keys
       f32x4 sacc[2][2], dpacc[2][2];
@@ -249,9 +247,8 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
           for (int j = 0; j < 4; ++j) {
             float p = __builtin_amdgcn_exp2f(fmaf(sacc[k2][qt][j], a.c2, off));
             if (DIAG && ((kh * 2 + k2) * 16 + g4 * 4 + j > half * 32 + qt * 16 + l16)) p = 0.0f;
-            const float ds = p * (dpacc[k2][qt][j] - dlt[qt]);
-            if (!DIAG) tsum += ds;
-            dsb[qt][k2 * 4 + j] = (bf16)ds;
+            dx[qt] = fmaf(p, dpacc[k2][qt][j], dx[qt]);
+            dsb[qt][k2 * 4 + j] = (bf16)(p * (dpacc[k2][qt][j] - dlt[qt]));
           }
       }
       // dQ^T += K^T dS^T over these 32 keys; K^T fragments are column
@@ -274,7 +271,6 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
         }
       }
     }
-    return tsum;
   };
 
   // the row's selection, 64 entries at a time, in registers (lane e: block
@@ -296,7 +292,7 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
     load_tile(lane_value(selv, 0), 1);
     nbeta = lane_value(betav, 0);
   }
-  tile(std::true_type{}, 0, 0.0f);   // diagonal: no gate gradient
+  tile(std::true_type{}, 0, 0.0f);   // diagonal block (causal, gate 0)
   wait_vm();
   __syncthreads();
   for (int t = 1; t < ntiles; ++t) {
@@ -307,24 +303,14 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
       load_tile(lane_value(selv, t & 63), stg ^ 1);
       nbeta = lane_value(betav, t & 63);
     }
-    float tsum = tile(std::false_type{}, stg, beta);
-    tsum = wave_sum(tsum);
-    if (lane == 0) s_red[t & 1][w] = tsum;
-    // previous tile's partial (its slot was filled before the last barrier)
-    if (tid == 0 && t >= 2) {
-      float sum = 0.0f;
-#pragma unroll
-      for (int x = 0; x < NW; ++x) sum += s_red[(t - 1) & 1][x];
-      part[t - 1] = sum;
-    }
+    tile(std::false_type{}, stg, beta);
     wait_vm();
     __syncthreads();
   }
-  if (tid == 0 && ntiles >= 2) {
-    float sum = 0.0f;
 #pragma unroll
-    for (int x = 0; x < NW; ++x) sum += s_red[(ntiles - 1) & 1][x];
-    part[ntiles - 1] = sum;
+  for (int qt = 0; qt < 2; ++qt) {
+    const float d = sum4(dx[qt]);
+    if (g4 == 0) a.delta[q0 + qt * 16 + l16] = d;
   }
 
   // dQ = scale * dQacc (lane: row qt*16 + l16, dims dt*16 + g4*4 .. +3)
@@ -339,47 +325,6 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
       *(bf16x4*)(dp + dt * 16) = r;
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// dLogG table (sum of head-chunk partials) and optional selector-score grad
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int find_sel(const int32_t* sel, int cnt, int m) {
-  int lo = 0, hi = cnt;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (sel[mid] < m) lo = mid + 1; else hi = mid;
-  }
-  return (lo < cnt && sel[lo] == m) ? lo : -1;
-}
-
-__global__ void __launch_bounds__(256) finalize_kernel(BwdArgs a) {
-  const int lane = threadIdx.x & 63;
-  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.ncol) return;
-  const int i = (int)(row % a.C);
-  const int cnt = min(a.sel_cnt[row], a.cap);
-  const int32_t* sel = a.sel_idx + row * a.cap;
-  float* drow = a.dlg + row * a.C;
-  float tot = 0.0f;
-  for (int m = lane; m < a.C; m += 64) {
-    float val = 0.0f;
-    if (m < i) {
-      const int pos = find_sel(sel, cnt, m);
-      if (pos >= 0) {
-        for (int p = 0; p < a.nparts; ++p)
-          val += a.dlg_part[((long long)p * a.ncol + row) * (a.cap + 1) + pos + 1];
-      }
-    }
-    drow[m] = val;
-    tot += val;
-  }
-  if (a.dsc == nullptr) return;
-  tot = wave_sum(tot);
-  const float* grow = a.lg + row * a.C;
-  float* srow = a.dsc + row * a.C;
-  for (int m = lane; m < a.C; m += 64)
-    srow[m] = (m < i) ? (drow[m] - expf(grow[m]) * tot) : 0.0f;
 }
 
 // ---------------------------------------------------------------------------
@@ -830,9 +775,11 @@ bwd_dkdv_kernel(BwdArgs a) {
   };
   // B: dS = P (dP - Delta) of a step (Delta and Q rows in qs, P in px) as the
   // bf16 B operand, element pair m after MFMA m of the next dP, then
-  // dK += Q^T dS.
+  // dK += Q^T dS.  gsum collects the step's dS for the block log-gate gradient.
+  // (fma with a zero addend and an fp16 operand maps to one mixed-precision
+  // fma, with no separate fp16 -> fp32 conversion.)
   auto window_b = [&](const char* on, const char* qs, const _Float16* px,
-                      const f32x16 (&dprev)[2], f32x16 (&dcur)[2]) {
+                      const f32x16 (&dprev)[2], f32x16 (&dcur)[2], float& gsum) {
     bf16x8 qa[8];
     read_rows(on, qa);   // dO of step s
     float dl[16];
@@ -848,7 +795,9 @@ bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int jj = (m & 7) * 2 + x;
-        bop[kt][jj >> 3][jj & 7] = (bf16)((float)ph[kt][jj >> 3][jj & 7] * (dprev[kt][jj] - dl[jj]));
+        const float ds = fmaf((float)ph[kt][jj >> 3][jj & 7], dprev[kt][jj] - dl[jj], 0.0f);
+        gsum += ds;
+        bop[kt][jj >> 3][jj & 7] = (bf16)ds;
       }
       pin(bop[kt][(m >> 2) & 1]);
     });
@@ -902,6 +851,19 @@ bwd_dkdv_kernel(BwdArgs a) {
       }
     }
   } else {
+    // dLogG[i, j] of entry e (query block i = itab[e] != j) = sum of dS over
+    // its 2G steps (G heads x 64 rows) and the 64 keys; fixed summation order
+    float gsum = 0.0f;
+    int gstep = 0, gent = 0;
+    auto step_done = [&]() {
+      if (++gstep < 2 * G) return;
+      const float tot = wave_sum(gsum);
+      gsum = 0.0f;
+      gstep = 0;
+      const int ib = itab[gent];
+      if (lane == 0 && ib != j) a.dlg[(bhk * a.C + ib) * a.C + j] = tot;
+      ++gent;
+    };
     copy_next();
     copy_next();
     ring_barrier();   // dO of step 0 landed
@@ -917,16 +879,19 @@ bwd_dkdv_kernel(BwdArgs a) {
     int s = 1;
 #pragma unroll 1
     for (; s + 1 < n; s += 2) {
-      window_b(oring(ok), qring(qk), pbuf(0), r0, r1);   // step s - 1 is even
+      window_b(oring(ok), qring(qk), pbuf(0), r0, r1, gsum);   // step s - 1 is even
       ring_barrier();
+      step_done();
       ok = inc(ok, O_SLOTS); qk = inc(qk, Q_SLOTS);
-      window_b(oring(ok), qring(qk), pbuf(1), r1, r0);
+      window_b(oring(ok), qring(qk), pbuf(1), r1, r0, gsum);
       ring_barrier();
+      step_done();
       ok = inc(ok, O_SLOTS); qk = inc(qk, Q_SLOTS);
     }
     // window n - 1: dP_{n-1} -> r1, dS / dK of step n - 2
-    window_b(oring(ok), qring(qk), pbuf(0), r0, r1);
+    window_b(oring(ok), qring(qk), pbuf(0), r0, r1, gsum);
     ring_barrier();
+    step_done();
     qk = inc(qk, Q_SLOTS);
     // dS and dK of the last step (odd)
     bf16x8 bop[2][2];
@@ -940,10 +905,14 @@ bwd_dkdv_kernel(BwdArgs a) {
         for (int h2 = 0; h2 < 2; ++h2) {
           const f16x8 ph = *(const f16x8*)(px + ((kt * 2 + h2) * 64 + lane) * 8);
 #pragma unroll
-          for (int x = 0; x < 8; ++x)
-            bop[kt][h2][x] = (bf16)((float)ph[x] * (r1[kt][h2 * 8 + x] - dl[h2 * 8 + x]));
+          for (int x = 0; x < 8; ++x) {
+            const float ds = fmaf((float)ph[x], r1[kt][h2 * 8 + x] - dl[h2 * 8 + x], 0.0f);
+            gsum += ds;
+            bop[kt][h2][x] = (bf16)ds;
+          }
         }
     }
+    step_done();
     bf16x8 ta[4][2];
     read_tr(qring(qk), ta);
     contract(ta, bop, [](int) {});
@@ -1011,19 +980,15 @@ __global__ void __launch_bounds__(256) reduce_kernel(BwdArgs a) {
 }
 
 template <int NH>
-hipError_t launch_dq(BwdArgs a, int head_base, int nchunk, int part_base, long long units,
-                     hipStream_t st) {
+hipError_t launch_dq(BwdArgs a, int head_base, int nchunk, long long units, hipStream_t st) {
   a.head_base = head_base;
   a.nchunk = nchunk;
-  a.part_base = part_base;
   hipLaunchKernelGGL((bwd_dq_kernel<NH>), dim3((unsigned)(units * nchunk)), dim3(NH * 128), 0, st,
                      a);
   return hipGetLastError();
 }
 
 }  // namespace
-
-int bwd_head_parts(int G) { return G / 4 + (G % 4) / 2 + (G % 2); }
 
 namespace {
 BwdArgs make_bwd_args(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorkspace& wl) {
@@ -1033,7 +998,6 @@ BwdArgs make_bwd_args(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorks
   a.sel_cnt = p.sel_cnt; a.dq = (bf16*)p.dq; a.dk = (bf16*)p.dk; a.dv = (bf16*)p.dv;
   a.dlg = p.dlog_gate; a.dsc = p.dscores;
   a.delta = (float*)(ws + wl.delta);
-  a.dlg_part = (float*)(ws + wl.dlg_part);
   a.colmask = (uint32_t*)(ws + wl.colmask);
   a.collen = (int32_t*)(ws + wl.collen);
   a.coloff = (int32_t*)(ws + wl.coloff);
@@ -1046,7 +1010,6 @@ BwdArgs make_bwd_args(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorks
   a.ncol = (long long)s.B * s.Hkv * s.C;
   a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.G; a.N = s.N; a.C = s.C; a.cap = s.cap; a.W = wl.words;
   a.o_fp32 = s.o_fp32;
-  a.nparts = bwd_head_parts(s.G);
   a.c2 = s.scale * kLog2e;
   a.scale = s.scale;
   return a;
@@ -1059,26 +1022,21 @@ hipError_t launch_bwd_dq_mfma(const Shape& s, const BwdPtrs& p, char* ws, const 
   const long long units = a.ncol;
   hipError_t e;
   // query-major pass (heads in chunks of 4, 2, 1)
-  int h = 0, part = 0;
+  int h = 0;
   if (s.G / 4 > 0) {
-    e = launch_dq<4>(a, h, s.G / 4, part, units, st);
+    e = launch_dq<4>(a, h, s.G / 4, units, st);
     if (e != hipSuccess) return e;
-    part += s.G / 4;
     h += 4 * (s.G / 4);
   }
   if ((s.G - h) / 2 > 0) {
-    e = launch_dq<2>(a, h, 1, part, units, st);
+    e = launch_dq<2>(a, h, 1, units, st);
     if (e != hipSuccess) return e;
-    part += 1;
     h += 2;
   }
   if (s.G - h > 0) {
-    e = launch_dq<1>(a, h, 1, part, units, st);
+    e = launch_dq<1>(a, h, 1, units, st);
     if (e != hipSuccess) return e;
   }
-  // dLogG table and selector-score gradient
-  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((a.ncol + 3) / 4)), dim3(256), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   // selection transpose for the key-major stage
   const long long nmask = a.ncol * a.W;
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)min((nmask + 255) / 256, 65535LL)),
@@ -1101,11 +1059,17 @@ hipError_t launch_bwd_dq_mfma(const Shape& s, const BwdPtrs& p, char* ws, const 
 hipError_t launch_bwd_dkdv_mfma(const Shape& s, const BwdPtrs& p, char* ws,
                                 const BwdWorkspace& wl, hipStream_t st) {
   BwdArgs a = make_bwd_args(s, p, ws, wl);
+  // dLogG: zero everywhere, then the key-major pass writes the selected entries
+  const long long ntab = a.ncol * s.C;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)min((ntab + 255) / 256, 65535LL)),
+                     dim3(256), 0, st, (uint32_t*)a.dlg, ntab);
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)wl.max_chunks), dim3(128), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)a.ncol), dim3(256), 0, st, a);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (p.dscores == nullptr) return hipSuccess;
+  return launch_dscores(s, p.dlog_gate, p.log_gate, p.dscores, st);
 }
 
 }  // namespace sas

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SAS_ABI_VERSION 1
+#define SAS_ABI_VERSION 2
 
 typedef enum sas_dtype {
   SAS_BF16 = 0, /* q/k/v/o/d_o/dq/dk/dv are bfloat16 (fp32 accumulation) */
@@ -84,10 +84,10 @@ typedef struct sas_problem {
   int32_t budget_k;   /* K   >= 0: historical blocks kept per query block    */
   int32_t dtype;      /* a sas_dtype                                          */
   int32_t o_dtype;    /* sas_dtype of the forward output o (and of the o read
-                         by the backward).  SAS_FP32 keeps o unrounded, so the
-                         backward's Delta = rowsum(o * dO) carries no bf16
-                         rounding; SAS_BF16 is the usual half-size output.
-                         Must be SAS_FP32 when dtype is SAS_FP32.            */
+                         by the backward).  SAS_BF16 is the usual half-size
+                         output; SAS_FP32 keeps o unrounded (the bf16 forward
+                         then also splits P into two bf16 terms for the PV
+                         product).  Must be SAS_FP32 when dtype is SAS_FP32.  */
   float sm_scale;     /* scale of q.k; <= 0 selects 1/sqrt(D).  It never
                          multiplies the log gate (App. E, Alg. 3/4).          */
 } sas_problem;
@@ -163,10 +163,15 @@ size_t sas_gated_attn_bwd_workspace_size(const sas_problem* p, int32_t sel_cap);
 /*
  * sas_gated_attn_bwd -- gated block-sparse attention backward.
  *
- * Defined by the App. E backward (Alg. 4): Delta = rowsum(O * dO); P is
- * recomputed from lse; dS = P * (dO V^T - Delta);
+ * Defined by the App. E backward (Alg. 4): P is recomputed from lse;
+ * dS = P * (dO V^T - Delta);
  *   dq = sm_scale dS K,  dk = sm_scale dS^T Q,  dv = P^T dO
- * (dk, dv summed over the G query heads of each kv head);
+ * (dk, dv summed over the G query heads of each kv head).  Delta is the row
+ * correction of App. E, rowsum(O * dO), which equals sum_u P_u dP_u for the
+ * probabilities P of the row.  The first (query-major) pass forms dS for dq
+ * with Delta = rowsum(o * dO) and accumulates sum_u P_u dP_u of its
+ * recomputed P; the second (key-major) pass uses that sum for dS, so dk and
+ * dlog_gate carry no rounding of o;
  *   dlog_gate[i, m] = sum of dS over the query tokens of block i (all G heads)
  *                     and the key tokens of block m, for m in I_i; 0 elsewhere
  *                     (unselected, diagonal and upper-triangle entries);
@@ -199,23 +204,24 @@ int32_t sas_gated_attn_bwd(const sas_problem* p, const void* q, const void* k, c
  * exactly sas_gated_attn_bwd.
  *
  * sas_gated_attn_bwd_dq -- the query-major stage (App. E backward, first pass
- * of Alg. 4): Delta = rowsum(o * dO) (kept in the workspace), dq, dlog_gate
- * and, if dscores != NULL, the selector-score gradient (App. D.3).  It also
- * records, in the workspace, which query blocks attend each key block (the
- * transpose of the selection) for the key-major stage.
+ * of Alg. 4): dq (with Delta = rowsum(o * dO)), and the row sums
+ * sum_u P_u dP_u kept in the workspace.  It also records, in the workspace,
+ * which query blocks attend each key block (the transpose of the selection)
+ * for the key-major stage.
  */
 int32_t sas_gated_attn_bwd_dq(const sas_problem* p, const void* q, const void* k, const void* v,
                               const void* o, const void* d_o, const float* lse,
                               const float* log_gate, const int32_t* sel_idx,
-                              const int32_t* sel_cnt, int32_t sel_cap, void* dq, float* dlog_gate,
-                              float* dscores, void* workspace, size_t workspace_bytes,
-                              void* stream);
+                              const int32_t* sel_cnt, int32_t sel_cap, void* dq, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /*
  * sas_gated_attn_bwd_dkdv -- the key-major stage (second pass of Alg. 4):
  * dk = sm_scale dS^T Q and dv = P^T dO for every key block, summed over the
  * diagonal query block and every query block that selected it, and over the
- * G heads of the kv group.  It reads Delta and the selection transpose that
+ * G heads of the kv group; dlog_gate (every entry written, as described for
+ * sas_gated_attn_bwd) and, if dscores != NULL, the selector-score gradient
+ * (App. D.3).  It reads Delta and the selection transpose that
  * sas_gated_attn_bwd_dq left in `workspace`; it must follow that call, on the
  * same stream, with the same workspace, problem, inputs and selection.
  */
@@ -223,7 +229,8 @@ int32_t sas_gated_attn_bwd_dkdv(const sas_problem* p, const void* q, const void*
                                 const void* v, const void* d_o, const float* lse,
                                 const float* log_gate, const int32_t* sel_idx,
                                 const int32_t* sel_cnt, int32_t sel_cap, void* dk, void* dv,
-                                void* workspace, size_t workspace_bytes, void* stream);
+                                float* dlog_gate, float* dscores, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -20,9 +20,9 @@ def log(msg):
     sys.stdout.flush()
 
 
-def problem_of(w: workloads.Workload, K: int) -> api.Problem:
+def problem_of(w: workloads.Workload, K: int, o_dtype: str = "bf16") -> api.Problem:
     return api.Problem(w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.block,
-                       K, w.dtype)
+                       K, w.dtype, 0.0, o_dtype if w.dtype == "bf16" else "fp32")
 
 
 def run_gpu(p: api.Problem, inp: dict, cap=None, poison=True, status=None):
@@ -104,9 +104,9 @@ def compare(name, got, ref, dtype, mask=None):
     assert rel_to_max <= rtol, f"{name}: max error {rel_to_max:.3e} of the tensor's max magnitude"
 
 
-def full_parity(w, K, inp=None, cap=None):
+def full_parity(w, K, inp=None, cap=None, o_dtype="bf16"):
     """Whole-tensor parity of every output (sizes the oracle finishes quickly)."""
-    p = problem_of(w, K)
+    p = problem_of(w, K, o_dtype)
     inp = inp or workloads.generate(w)
     gpu = run_gpu(p, inp, cap=cap)
     scores = inp["scores"].numpy()

@@ -58,8 +58,8 @@ def test_library_exports_every_header_symbol():
 
 
 def test_abi_version():
-    assert lib().sas_abi_version() == 1
-    assert api.abi_version() == 1
+    assert lib().sas_abi_version() == 2
+    assert api.abi_version() == 2
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -92,6 +92,36 @@ def test_null_problem_and_null_pointers():
     assert thr(p, s=None) == nat.SAS_E_INVALID
     assert bwd(p, dlg=None) == nat.SAS_E_INVALID
     assert b"NULL" in lib().sas_last_error()
+
+
+def bwd_dq(p, cap=4, ws=FAKE * 256, ws_bytes=1 << 40, **ptrs):
+    a = {n: FAKE for n in ("q", "k", "v", "o", "do", "lse", "lg", "si", "sc", "dq")}
+    a.update(ptrs)
+    return lib().sas_gated_attn_bwd_dq(ctypes.byref(p), a["q"], a["k"], a["v"], a["o"], a["do"],
+                                       a["lse"], a["lg"], a["si"], a["sc"], cap, a["dq"], ws,
+                                       ws_bytes, None)
+
+
+def bwd_dkdv(p, cap=4, ws=FAKE * 256, ws_bytes=1 << 40, **ptrs):
+    a = {n: FAKE for n in ("q", "k", "v", "do", "lse", "lg", "si", "sc", "dk", "dv", "dlg")}
+    a.update(ptrs)
+    return lib().sas_gated_attn_bwd_dkdv(ctypes.byref(p), a["q"], a["k"], a["v"], a["do"],
+                                         a["lse"], a["lg"], a["si"], a["sc"], cap, a["dk"],
+                                         a["dv"], a["dlg"], None, ws, ws_bytes, None)
+
+
+def test_staged_backward_validates_its_own_outputs():
+    """The query-major stage needs o and dq; the key-major stage needs dk, dv
+    and dlog_gate (it writes the block log-gate gradient)."""
+    p = prob()
+    assert bwd_dq(p, o=None) == nat.SAS_E_INVALID
+    assert bwd_dq(p, dq=None) == nat.SAS_E_INVALID
+    assert bwd_dkdv(p, dlg=None) == nat.SAS_E_INVALID
+    assert bwd_dkdv(p, dk=None) == nat.SAS_E_INVALID
+    assert bwd_dq(p, ws=None) == nat.SAS_E_WORKSPACE
+    assert bwd_dkdv(p, ws_bytes=16) == nat.SAS_E_WORKSPACE
+    assert bwd_dq(prob(head_dim=96)) == nat.SAS_E_UNSUPPORTED
+    assert bwd_dkdv(prob(head_dim=96)) == nat.SAS_E_UNSUPPORTED
 
 
 def test_selection_capacity_must_hold_the_budget():

@@ -31,18 +31,21 @@ def _gpu():
 # --------------------------------------------------------------------------
 
 SMALL = [
-    # name, B, Hq, Hkv, N, D, blk, K, dtype, qkv_std
+    # name, B, Hq, Hkv, N, D, blk, K, dtype, qkv_std[, o_dtype (default bf16)]
     ("tiny_fp32_cfg", 1, 1, 1, 256, 64, 16, 4, "fp32", 1.0),
     ("mfma_g4", 1, 8, 2, 1024, 128, 64, 4, "bf16", 1.0),
     ("mfma_g4_scaled", 2, 4, 1, 768, 128, 64, 3, "bf16", 128 ** -0.5),
     ("mfma_g5", 1, 10, 2, 640, 128, 64, 3, "bf16", 1.0),
     ("mfma_g1", 1, 2, 2, 512, 128, 64, 2, "bf16", 1.0),
     ("mfma_g2", 1, 4, 2, 512, 128, 64, 5, "bf16", 1.0),
+    ("mfma_g2_ofp32", 1, 4, 2, 512, 128, 64, 5, "bf16", 1.0, "fp32"),
+    ("mfma_g4_ofp32", 1, 8, 2, 1024, 128, 64, 4, "bf16", 1.0, "fp32"),
     ("mfma_k0", 1, 4, 1, 512, 128, 64, 0, "bf16", 1.0),
     ("mfma_kall", 1, 4, 1, 512, 128, 64, 20, "bf16", 1.0),
     ("mfma_one_block", 1, 4, 1, 64, 128, 64, 4, "bf16", 1.0),
     ("generic_bf16_d64_b16", 1, 4, 2, 256, 64, 16, 3, "bf16", 1.0),
     ("generic_bf16_d128_b32", 1, 2, 1, 256, 128, 32, 2, "bf16", 1.0),
+    ("generic_bf16_d128_b32_ofp32", 1, 2, 1, 256, 128, 32, 2, "bf16", 1.0, "fp32"),
     ("generic_fp32_d128_b64", 1, 2, 1, 384, 128, 64, 2, "fp32", 1.0),
     ("generic_fp32_d64_b32", 2, 3, 1, 256, 64, 32, 3, "fp32", 1.0),
 ]
@@ -50,12 +53,13 @@ SMALL = [
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_small_shapes_full_parity(case):
-    name, B, Hq, Hkv, N, D, blk, K, dt, std = case
+    name, B, Hq, Hkv, N, D, blk, K, dt, std = case[:10]
+    o_dtype = case[10] if len(case) > 10 else "bf16"
     log(f"case {name}")
     w = workloads.custom(B, Hq, Hkv, N, D, blk, K, dtype=dt, seed=zlib.crc32(name.encode()) % 1000,
                          qkv_std=std, score_std=2.0)
     cap = max(1, min(K, N // blk - 1))
-    full_parity(w, K, cap=cap)
+    full_parity(w, K, cap=cap, o_dtype=o_dtype)
 
 
 def test_tiny_fp32_workload():
@@ -177,8 +181,8 @@ def test_staged_backward_matches_combined(shape):
     dv = torch.full_like(v, float("nan"))
     dlg = torch.full_like(lg, float("nan"))
     dsc = torch.full_like(lg, float("nan"))
-    api.gated_attn_bwd_dq(p, q, k, v, o, do, lse, lg, si, cnt, dq, dlg, dsc, ws)
-    api.gated_attn_bwd_dkdv(p, q, k, v, do, lse, lg, si, cnt, dk, dv, ws)
+    api.gated_attn_bwd_dq(p, q, k, v, o, do, lse, lg, si, cnt, dq, ws)
+    api.gated_attn_bwd_dkdv(p, q, k, v, do, lse, lg, si, cnt, dk, dv, dlg, dsc, ws)
     torch.cuda.synchronize()
     for name, got, want in zip(("dq", "dk", "dv", "dlog_gate", "dscores"), (dq, dk, dv, dlg, dsc), ref):
         assert torch.equal(got.cpu(), want.cpu()), f"{name} differs between staged and combined backward"
