@@ -2,38 +2,37 @@
 // inputs, fp32 accumulation, block b = 64, head_dim D = 128, on gfx950.
 //
 // Follows the recomputation backward of the SAS paper's App. E (Alg. 4):
-//   Delta = rowsum(O * dO);  P = exp(S - LSE);  dS = P * (dO V^T - Delta);
+//   P = exp(S - LSE);  dS = P * (dO V^T - Delta);
 //   dQ = scale dS K;  dK = scale dS^T Q;  dV = P^T dO;
 //   dLogG[i, m] = sum of dS over the query tokens of block i (all G heads of
 //                 the kv group) and the key tokens of selected block m;
-// and the selector-score gradient of App. D.3 / Eq. 8.
+// and the selector-score gradient of App. D.3 / Eq. 8.  Delta, the row
+// correction of App. E, is rowsum(O * dO) = sum_u P_u dP_u.
 //
 // Kernels (in launch order):
 //   bwd_dq_kernel       query-major pass: one workgroup per (batch, kv head,
-//                       query block, chunk of heads); each wavefront owns 64
+//                       query block, chunk of heads); each wavefront owns 32
 //                       query rows of one head and streams the diagonal block
-//                       and the selected blocks.  It computes Delta (from the
-//                       forward output), recomputes S^T = K Q^T and
-//                       dP^T = V dO^T, accumulates dQ^T += K^T dS^T in
-//                       registers and reduces dS of every tile to one block
-//                       log-gate gradient partial (deterministic: fixed lane
-//                       butterfly, fixed wave order).
-//   finalize_kernel     sums the per-head-chunk partials in a fixed order into
-//                       the dense dLogG table and, optionally, applies the
-//                       softmax backward to the selector scores.
+//                       and the selected blocks.  It recomputes S^T = K Q^T
+//                       and dP^T = V dO^T, forms dS with Delta = rowsum(O dO)
+//                       and accumulates dQ^T += K^T dS^T in registers; on the
+//                       side it sums P * dP of every row (Delta without the
+//                       rounding of O), which the key-major pass uses.
 //   column kernels      transpose the selection: bit (j, i) of a column mask is
 //                       set when row i selected block j; each column j then
 //                       gets the ascending list {j} u {i > j : j in I_i} and is
-//                       cut into chunks of at most kColChunk query blocks.
-//   bwd_dkdv_kernel     key-major pass: one workgroup per column chunk; K_j
-//                       and V_j stay in LDS, each wavefront streams (query
-//                       block, head) items, recomputes S = Q K^T and
-//                       dP = dO V^T (keys in the lane dimension), and
-//                       accumulates dV^T += dO^T P and dK^T += Q^T dS, with
-//                       Q^T / dO^T staged transposed in wave-private LDS.  The
-//                       four wavefronts' partial sums are added in a fixed order.
+//                       cut into chunks of at most kColChunk query blocks,
+//                       ordered for L2 reuse.
+//   bwd_dkdv_kernel     key-major pass: one wavefront pair per column chunk
+//                       (key block j); K_j / V_j are resident MFMA operands,
+//                       the (query block, head) rows stream through LDS rings;
+//                       it recomputes S and dP, accumulates dV^T += dO^T P and
+//                       dK^T += Q^T dS, and writes dLogG[i, j] of each
+//                       selecting query block i (sum of its dS).
 //   reduce_kernel       columns cut into several chunks: fp32 partials summed
 //                       in chunk order (deterministic).
+//   dscores_kernel      (sas_threshold.hip) selector-score gradient from the
+//                       dense dLogG table.
 #include <math.h>
 
 #include <type_traits>
@@ -67,15 +66,9 @@ struct BwdArgs {
   float c2, scale;
 };
 
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float sum4(float x) {
+__device__ __forceinline__ float sum2(float x) {   // lanes l, l ^ 32
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
@@ -106,7 +99,7 @@ __device__ __forceinline__ bf16x4 ds_read_tr(const bf16* p) {
 }
 
 // ---------------------------------------------------------------------------
-// query-major pass: Delta, dQ, block log-gate gradient partials
+// query-major pass: dQ and the row sums of P * dP
 // ---------------------------------------------------------------------------
 constexpr int TILE = BLK * HD;   // bf16 elements of one 64 x 128 tile
 
@@ -130,8 +123,28 @@ __device__ __forceinline__ void tile_to_lds(bf16* lds, const bf16* g, int w, int
 
 __device__ __forceinline__ void wait_vm() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// v_mfma_f32_32x32x16_bf16.  Lane l (g = l / 32): A row l % 32, k = 8 g .. +7;
+// B column l % 32, same k; C column l % 32, rows 8 (jj / 4) + 4 g + jj % 4.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 // One workgroup = NH query heads of one (batch, kv head, query block); two
-// wavefronts per head, each owning 32 of the 64 query rows.
+// wavefronts per head, each owning 32 of the 64 query rows; two wavefronts per
+// SIMD (<= 256 registers), so the vector work of one overlaps the matrix
+// instructions of the other.  Every product is a 32x32x16 MFMA:
+//   S^T = K Q^T and dP^T = V dO^T, 32 keys at a time (lane: query l32 and 16
+//   keys), so P and dS of a lane belong to one query row (its LSE and Delta
+//   are per-lane scalars);
+//   dQ^T += K^T dS^T, with dS^T packed to bf16 straight from the accumulator
+//   layout as the B operand and K^T from transposed reads of the K tile (the
+//   keys of both operands permuted the same way).
+// K / V tiles are double-buffered in LDS: tile t + 1 is copied while tile t
+// is processed, one barrier per tile.
 template <int NH>
 __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
   constexpr int NW = 2 * NH;
@@ -140,9 +153,9 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int l16 = lane & 15;
-  const int g4 = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
   const int half = w & 1;
 
   const int unit = xcd_remap(blockIdx.x, gridDim.x);
@@ -159,7 +172,7 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
   const float* lgrow = a.lg + row * a.C;
   const bf16* kbase = a.k + (long long)bhk * a.N * HD;
   const bf16* vbase = a.v + (long long)bhk * a.N * HD;
-  const long long q0 = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + half * 32;
+  const long long qr = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + half * 32 + l32;
 
   auto load_tile = [&](int kb, int stg) {
     tile_to_lds<NW>(s_k[stg], kbase + (long long)kb * TILE, w, lane);
@@ -168,108 +181,144 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
   const int ntiles = cnt + 1;
   load_tile(i, 0);
 
-  // Q^T and dO^T as B operands (lane: row qt*16 + l16, dims ks*32 + g4*8 .. +7);
-  // dlt = rowsum(O * dO) (the Delta of dS in this pass), dx = the row's
-  // sum of P * dP over every attended key (the same quantity without the
-  // rounding of O; the key-major pass uses it)
-  bf16x8 qf[2][4], dof[2][4];
-  float lse2[2], dlt[2], dx[2] = {0.0f, 0.0f};
+  // Q^T and dO^T as B operands (lane: query row l32, dims ks*16 + g*8 .. +7);
+  // dlt = rowsum(O * dO) over the row's two lanes (the Delta of dS in this
+  // pass), dx = the row's sum of P * dP over every attended key (the same
+  // quantity without the rounding of O; the key-major pass uses it)
+  bf16x8 qf[8], dof[8];
+  float part_d = 0.0f;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const long long r = q0 + qt * 16 + l16;
-    float part_d = 0.0f;
+  for (int ks = 0; ks < 8; ++ks) {
+    const int d0 = ks * 16 + g * 8;
+    qf[ks] = *(const bf16x8*)(a.q + qr * HD + d0);
+    dof[ks] = *(const bf16x8*)(a.d_o + qr * HD + d0);
+  }
+  if (a.o_fp32) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int d0 = ks * 32 + g4 * 8;
-      qf[qt][ks] = *(const bf16x8*)(a.q + r * HD + d0);
-      dof[qt][ks] = *(const bf16x8*)(a.d_o + r * HD + d0);
-      if (a.o_fp32) {
-        const f32x4 o0 = *(const f32x4*)((const float*)a.o + r * HD + d0);
-        const f32x4 o1 = *(const f32x4*)((const float*)a.o + r * HD + d0 + 4);
+    for (int ks = 0; ks < 8; ++ks) {
+      const float* op = (const float*)a.o + qr * HD + ks * 16 + g * 8;
+      const f32x4 o0 = *(const f32x4*)op;
+      const f32x4 o1 = *(const f32x4*)(op + 4);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          part_d += o0[x] * (float)dof[qt][ks][x];
-          part_d += o1[x] * (float)dof[qt][ks][x + 4];
-        }
-      } else {
-        const bf16x8 ob = *(const bf16x8*)((const bf16*)a.o + r * HD + d0);
-#pragma unroll
-        for (int x = 0; x < 8; ++x) part_d += (float)ob[x] * (float)dof[qt][ks][x];
+      for (int x = 0; x < 4; ++x) {
+        part_d += o0[x] * (float)dof[ks][x];
+        part_d += o1[x] * (float)dof[ks][x + 4];
       }
     }
-    dlt[qt] = sum4(part_d);   // over the 4 lanes of the row
-    lse2[qt] = a.lse[r] * kLog2e;
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 ob = *(const bf16x8*)((const bf16*)a.o + qr * HD + ks * 16 + g * 8);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) part_d += (float)ob[x] * (float)dof[ks][x];
+    }
   }
+  const float dlt = sum2(part_d);
+  const float lse2 = a.lse[qr] * kLog2e;
+  float dx = 0.0f;
 
-  f32x4 dqacc[8][2];
+  f32x16 dqacc[4];   // dQ^T (lane: dims dt*32 + 8 (jj/4) + 4 g + jj%4, query l32)
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) dqacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int x = 0; x < 16; ++x) dqacc[dt][x] = 0.0f;
 
-  // One 64-key tile: recompute S^T and dP^T, form dS, accumulate dQ^T and
-  // the rows' P * dP sums.
+  // transposed-read offsets of the K^T fragments (A operand of dQ^T, lane:
+  // head dim dt*32 + l32, keys 16 sl + {4g .. 4g+3, 8+4g .. 8+4g+3})
+  const int u = lane & 15;
+  const int dhalf = (lane >> 4) & 1;
+  int tro[4][2];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      tro[dt][hh] = swz(g * 4 + (u >> 2) + 8 * hh, dt * 4 + dhalf * 2 + ((u >> 1) & 1)) + (u & 1) * 4;
+
+  // One 64-key tile, as two halves of 32 keys: recompute S^T and dP^T, form
+  // P and dS (packed to bf16 as the B operand of dQ^T: element jj -> k-slice
+  // jj / 8, word (jj % 8) / 2), accumulate dQ^T and the row's P * dP.
+  // The instruction order is pinned (sched_barrier): K / V fragments are read
+  // two MFMAs ahead, and the first K^T fragments of the dQ^T product are read
+  // before the vector work of P and dS, which hides their latency.  The
+  // matrix sections run at raised wave priority: after each barrier the two
+  // wavefronts of a SIMD fall into alternation, one issuing MFMAs while the
+  // other does its vector work.
+  auto ktr = [&](const bf16* Ks, int kh, int dt, int sl) {
+    const bf16* kp = Ks + (kh * 32 + sl * 16) * HD;
+    return join(ds_read_tr(kp + tro[dt][0]), ds_read_tr(kp + tro[dt][1]));
+  };
   auto tile = [&](auto diag_tag, int stg, float beta) {
     constexpr bool DIAG = decltype(diag_tag)::value;
     const bf16* Ks = s_k[stg];
     const bf16* Vs = s_v[stg];
+    const float off = beta - lse2;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {   // two halves of 32 keys
-      f32x4 sacc[2][2], dpacc[2][2];
+    for (int kh = 0; kh < 2; ++kh) {
+      const int rr = kh * 32 + l32;
+      f32x16 sc, dp;
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
+      for (int x = 0; x < 16; ++x) { sc[x] = 0.0f; dp[x] = 0.0f; }
+      bf16x8 ka[2], va[2];
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          sacc[k2][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dpacc[k2][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const int kr = (kh * 2 + k2) * 16 + l16;
-          const bf16x8 ka = *(const bf16x8*)(Ks + swz(kr, ks * 4 + g4));
-          const bf16x8 va = *(const bf16x8*)(Vs + swz(kr, ks * 4 + g4));
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt) {
-            sacc[k2][qt] = mfma16(ka, qf[qt][ks], sacc[k2][qt]);
-            dpacc[k2][qt] = mfma16(va, dof[qt][ks], dpacc[k2][qt]);
-          }
-        }
+      for (int ks = 0; ks < 2; ++ks) {
+        ka[ks] = *(const bf16x8*)(Ks + swz(rr, ks * 2 + g));
+        va[ks] = *(const bf16x8*)(Vs + swz(rr, ks * 2 + g));
       }
-      bf16x8 dsb[2];
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const float off = beta - lse2[qt];
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float p = __builtin_amdgcn_exp2f(fmaf(sacc[k2][qt][j], a.c2, off));
-            if (DIAG && ((kh * 2 + k2) * 16 + g4 * 4 + j > half * 32 + qt * 16 + l16)) p = 0.0f;
-            dx[qt] = fmaf(p, dpacc[k2][qt][j], dx[qt]);
-            dsb[qt][k2 * 4 + j] = (bf16)(p * (dpacc[k2][qt][j] - dlt[qt]));
-          }
-      }
-      // dQ^T += K^T dS^T over these 32 keys; K^T fragments are column
-      // fragments (rows kh*32 + {g4*4 .. +3, 16 + g4*4 .. +3}) read transposed,
-      // four head-dim tiles per batch of reads
-      const int kr = kh * 32 + g4 * 4 + (l16 >> 2);
-      const unsigned kbase_l = lds_addr(Ks) + (unsigned)(kr * HD + (l16 & 1) * 4) * 2;
-      auto kaddr = [&](int dt) { return kbase_l + (((dt * 2 + ((l16 >> 1) & 1)) ^ slot16(kr)) << 4); };
-#pragma unroll
-      for (int dq4 = 0; dq4 < 2; ++dq4) {
-        tr_u32x2 r[8];
-        tr_read_4x2(kaddr(dq4 * 4), kaddr(dq4 * 4 + 1), kaddr(dq4 * 4 + 2), kaddr(dq4 * 4 + 3), r);
-#pragma unroll
-        for (int d4 = 0; d4 < 4; ++d4) {
-          const int dt = dq4 * 4 + d4;
-          const tr_u32x2 lo = r[d4 * 2], hi = r[d4 * 2 + 1];
-          const bf16x8 ka = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt) dqacc[dt][qt] = mfma16(ka, dsb[qt], dqacc[dt][qt]);
+      for (int ks = 0; ks < 8; ++ks) {
+        sc = mfma32(ka[ks & 1], qf[ks], sc);
+        dp = mfma32(va[ks & 1], dof[ks], dp);
+        if (ks + 2 < 8) {
+          ka[ks & 1] = *(const bf16x8*)(Ks + swz(rr, (ks + 2) * 2 + g));
+          va[ks & 1] = *(const bf16x8*)(Vs + swz(rr, (ks + 2) * 2 + g));
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
+      bf16x8 kt[2][2];   // K^T fragments of head-dim tiles dt, dt + 1
+#pragma unroll
+      for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) kt[d2][sl] = ktr(Ks, kh, d2, sl);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+      uint32_t dsw[2][4];
+#pragma unroll
+      for (int jj = 0; jj < 16; jj += 2) {
+        f32x2 pp;
+        pp[0] = __builtin_amdgcn_exp2f(fmaf(sc[jj], a.c2, off));
+        pp[1] = __builtin_amdgcn_exp2f(fmaf(sc[jj + 1], a.c2, off));
+        if (DIAG) {   // causal mask: key > query -> P = 0
+          const int key = kh * 32 + (jj >> 2) * 8 + g * 4 + (jj & 3);
+          const int qrow = half * 32 + l32;
+          if (key > qrow) pp[0] = 0.0f;
+          if (key + 1 > qrow) pp[1] = 0.0f;
+        }
+        dx = fmaf(pp[0], dp[jj], dx);
+        dx = fmaf(pp[1], dp[jj + 1], dx);
+        const f32x2 ds = {pp[0] * (dp[jj] - dlt), pp[1] * (dp[jj + 1] - dlt)};
+        dsw[jj >> 3][(jj & 7) >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(ds, bf16x2));
+      }
+      bf16x8 db[2];
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl)
+        db[sl] = __builtin_bit_cast(bf16x8, u32x4{dsw[sl][0], dsw[sl][1], dsw[sl][2], dsw[sl][3]});
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
+      // dQ^T: tiles dt = 0..3; the fragments of tile dt + 2 are read while
+      // the MFMAs of tile dt run
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) dqacc[dt] = mfma32(kt[dt & 1][sl], db[sl], dqacc[dt]);
+        if (dt + 2 < 4) {
+#pragma unroll
+          for (int sl = 0; sl < 2; ++sl) kt[dt & 1][sl] = ktr(Ks, kh, dt + 2, sl);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_setprio(0);
     }
   };
 
@@ -307,24 +356,20 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
     wait_vm();
     __syncthreads();
   }
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const float d = sum4(dx[qt]);
-    if (g4 == 0) a.delta[q0 + qt * 16 + l16] = d;
-  }
+  const float dsum = sum2(dx);
+  if (g == 0) a.delta[qr] = dsum;
 
-  // dQ = scale * dQacc (lane: row qt*16 + l16, dims dt*16 + g4*4 .. +3)
+  // dQ = scale * dQacc (lane: query l32, dims dt*32 + q4*8 + 4 g .. +3)
+  bf16* dqp = a.dq + qr * HD + g * 4;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    bf16* dp = a.dq + (q0 + qt * 16 + l16) * HD + g4 * 4;
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
+    for (int q4 = 0; q4 < 4; ++q4) {
       bf16x4 r;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) r[j] = (bf16)(dqacc[dt][qt][j] * a.scale);
-      *(bf16x4*)(dp + dt * 16) = r;
+      for (int y = 0; y < 4; ++y) r[y] = (bf16)(dqacc[dt][q4 * 4 + y] * a.scale);
+      *(bf16x4*)(dqp + dt * 32 + q4 * 8) = r;
     }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -514,12 +559,7 @@ __global__ void chunk_scatter_kernel(BwdArgs a) {
 // contraction directly: its elements 8 sl .. 8 sl + 7 are rows
 // 16 sl + {4 g .. 4 g + 3, 8 + 4 g .. 8 + 4 g + 3}, and the transposed reads of
 // the staged rows use the same row order.
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 constexpr int XS_BYTES = 32 * HD * 2;               // 32 staged rows
 constexpr int SLOT_BYTES = XS_BYTES + 256;           // rows + one statistic (64 floats)
