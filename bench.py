@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode", nargs="?", const="qwen3_4b_decode_b8_64k", default=None,
+                    metavar="WORKLOAD",
+                    help="time the sparse-decode step (select + attention) of a decode workload "
+                         "instead of the training step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counter scale) and exit")
@@ -151,10 +155,110 @@ def cpu_baseline(w, K, inp, budget_s, total_pairs):
                        f"(est. {est:.1f} s per step); BLAS={vendor}")}
 
 
+def decode_bench(args):
+    """One step = sas_decode_select + sas_decode_attn for a batch of sequences,
+    inputs resident in HBM.  value = sequences (new tokens) per second."""
+    import numpy as np
+    import torch
+    from gated_block_sparse_attn_amd import api, workloads
+
+    w = workloads.DECODE_WORKLOADS[args.decode]
+    p = api.DecodeProblem(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block, w.max_blocks,
+                          w.pages, w.budget, w.dtype)
+    cap = p.default_cap()
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    inp = workloads.generate_decode(w)
+    dev = torch.device("cuda:0")
+    t = {k: v.to(dev) for k, v in inp.items()}
+    tau = torch.empty(w.batch, w.n_kv_heads, dtype=torch.float32, device=dev)
+    si = torch.empty(w.batch, w.n_kv_heads, cap, dtype=torch.int32, device=dev)
+    sc = torch.empty(w.batch, w.n_kv_heads, dtype=torch.int32, device=dev)
+    o = torch.empty(w.batch, w.n_q_heads, w.head_dim, dtype=p.torch_dtype, device=dev)
+    lse = torch.empty(w.batch, w.n_q_heads, dtype=torch.float32, device=dev)
+    ws = torch.empty(api.decode_workspace_size(p, cap), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        api.decode_select(p, t["scores"], t["seq_lens"], sel_cap=cap, outputs=(tau, si, sc))
+        if ev is not None:
+            ev[1].record()
+        api.decode_attn(p, t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                        si, sc, o=o, lse=lse, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        step(events[k])
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    stage_ms = {}
+    for si_, name in enumerate(("select", "attn")):
+        vals = sorted(events[k][si_].elapsed_time(events[k][si_ + 1]) for k in range(args.steps))
+        stage_ms[name] = {"mean": sum(vals) / len(vals), "median": vals[len(vals) // 2],
+                          "min": vals[0]}
+    # algorithmic HBM bytes of the attention stage: the attended K / V rows of
+    # every (sequence, kv head) once, q, o and lse
+    el = 2 if w.dtype == "bf16" else 4
+    cnt = np.minimum(sc.cpu().numpy(), cap)
+    lens = np.array(w.seq_lens)
+    cur = lens - ((lens - 1) // w.block) * w.block
+    rows = w.block * cnt.sum() + w.n_kv_heads * cur.sum()
+    attn_bytes = (2 * rows * w.head_dim * el + 2 * w.batch * w.n_q_heads * w.head_dim * el
+                  + 4 * w.batch * w.n_q_heads)
+    achieved = attn_bytes / (stage_ms["attn"]["mean"] * 1e-3) / 1e9
+    result = {
+        "metric": "sparse decode tokens/s (select + attention, one new token per sequence)",
+        "value": w.batch / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded torch generator; Qwen3-shaped paged cache, random values)",
+        "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "block": w.block,
+                   "budget_k": w.budget, "max_seq_len": int(max(w.seq_lens)),
+                   "max_blocks": w.max_blocks},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "decode_attn_kernel + decode_combine_kernel",
+                     "stage_ms_mean": stage_ms["attn"]["mean"],
+                     "algorithmic_bytes_per_launch": int(attn_bytes)},
+        "stage_ms": stage_ms,
+    }
+    if not args.no_cpu_baseline:
+        import oracle.sas_decode_oracle as dec
+        f = lambda x: x.float().numpy()   # noqa: E731
+        t0 = time.perf_counter()
+        _, sel = dec.decode_select(inp["scores"].numpy(), inp["seq_lens"].numpy(), w.block,
+                                   w.budget)
+        dec.decode_attn(f(inp["q"]), f(inp["k_pool"]), f(inp["v_pool"]),
+                        inp["block_table"].numpy(), inp["seq_lens"].numpy(), sel, w.block)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": w.batch / dt, "unit": "tokens/s", "cores": 1,
+                                  "kind": "oracle",
+                                  "sample": f"float64 numpy decode oracle, the whole step "
+                                            f"({w.batch} sequences) once: {dt:.3f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.decode:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            sys.exit(2)
+        decode_bench(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

@@ -37,7 +37,16 @@ class SasProblem(ctypes.Structure):
                 ("o_dtype", ctypes.c_int32), ("sm_scale", ctypes.c_float)]
 
 
+class SasDecodeProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+                ("pool_blocks", ctypes.c_int32), ("budget_k", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("sm_scale", ctypes.c_float)]
+
+
 _P = ctypes.POINTER(SasProblem)
+_PD = ctypes.POINTER(SasDecodeProblem)
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
 
@@ -53,6 +62,10 @@ SIGNATURES = {
                                _vp, _vp, ctypes.c_size_t, _vp], _i32),
     "sas_gated_attn_bwd_dkdv": ([_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                  _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp], _i32),
+    "sas_decode_select": ([_PD, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp], _i32),
+    "sas_decode_workspace_size": ([_PD, _i32], ctypes.c_size_t),
+    "sas_decode_attn": ([_PD, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
+                         ctypes.c_size_t, _vp, _vp], _i32),
 }
 
 _lib = None

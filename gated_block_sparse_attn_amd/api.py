@@ -19,7 +19,8 @@ from ._native import SasError, SasProblem, check, lib
 
 __all__ = ["Problem", "SasError", "gate_threshold", "gated_attn_fwd", "gated_attn_bwd",
            "gated_attn_bwd_dq", "gated_attn_bwd_dkdv", "bwd_workspace_size", "abi_version",
-           "SASAttention", "sas_attention"]
+           "SASAttention", "sas_attention", "DecodeProblem", "decode_select",
+           "decode_workspace_size", "decode_attn"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -297,3 +298,102 @@ def sas_attention(q, k, v, scores, block_size: int, budget_k: int, sm_scale: flo
 
 def default_scale(head_dim: int, sm_scale: float = 0.0) -> float:
     return sm_scale if sm_scale > 0 else 1.0 / math.sqrt(head_dim)
+
+
+# ---------------------------------------------------------------------------
+# sparse decode
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class DecodeProblem:
+    """Sizes of one batched sparse-decode step (mirrors sas_decode_problem)."""
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    block_size: int
+    max_blocks: int
+    pool_blocks: int
+    budget_k: int
+    dtype: str = "bf16"
+    sm_scale: float = 0.0
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def c(self) -> _native.SasDecodeProblem:
+        return _native.SasDecodeProblem(self.batch, self.n_q_heads, self.n_kv_heads,
+                                        self.head_dim, self.block_size, self.max_blocks,
+                                        self.pool_blocks, self.budget_k,
+                                        _native.SAS_BF16 if self.dtype == "bf16"
+                                        else _native.SAS_FP32, float(self.sm_scale))
+
+    def default_cap(self) -> int:
+        return max(1, min(self.budget_k, self.max_blocks - 1))
+
+
+def decode_select(p: DecodeProblem, scores, seq_lens, sel_cap: Optional[int] = None,
+                  status: Optional[torch.Tensor] = None, outputs=None, stream=None):
+    """sas_decode_select: returns (tau, sel_idx, sel_cnt)."""
+    cap = p.default_cap() if sel_cap is None else sel_cap
+    _expect(scores, "scores", (p.batch, p.n_kv_heads, p.max_blocks), torch.float32)
+    _expect(seq_lens, "seq_lens", (p.batch,), torch.int32)
+    dev = scores.device
+    if outputs is None:
+        tau = torch.empty(p.batch, p.n_kv_heads, dtype=torch.float32, device=dev)
+        sel_idx = torch.empty(p.batch, p.n_kv_heads, cap, dtype=torch.int32, device=dev)
+        sel_cnt = torch.empty(p.batch, p.n_kv_heads, dtype=torch.int32, device=dev)
+    else:
+        tau, sel_idx, sel_cnt = outputs
+        if tau is not None:
+            _expect(tau, "tau", (p.batch, p.n_kv_heads), torch.float32)
+        _expect(sel_idx, "sel_idx", (p.batch, p.n_kv_heads, cap), torch.int32)
+        _expect(sel_cnt, "sel_cnt", (p.batch, p.n_kv_heads), torch.int32)
+    if status is not None:
+        _expect(status, "status", (1,), torch.int32)
+    pc = p.c()
+    check(lib().sas_decode_select(ctypes_ref(pc), _ptr(scores), _ptr(seq_lens), _ptr(tau),
+                                  _ptr(sel_idx), _ptr(sel_cnt), cap, _ptr(status),
+                                  _stream(stream)))
+    return tau, sel_idx, sel_cnt
+
+
+def decode_workspace_size(p: DecodeProblem, sel_cap: int) -> int:
+    pc = p.c()
+    n = lib().sas_decode_workspace_size(ctypes_ref(pc), sel_cap)
+    if n == 0:
+        check(_native.SAS_E_INVALID)
+    return int(n)
+
+
+def decode_attn(p: DecodeProblem, q, k_pool, v_pool, block_table, seq_lens, sel_idx, sel_cnt,
+                o=None, lse=None, workspace=None, status: Optional[torch.Tensor] = None,
+                stream=None):
+    """sas_decode_attn: returns (o, lse)."""
+    cap = sel_idx.shape[-1]
+    dt = p.torch_dtype
+    pool = (p.pool_blocks, p.n_kv_heads, p.block_size, p.head_dim)
+    _expect(q, "q", (p.batch, p.n_q_heads, p.head_dim), dt)
+    _expect(k_pool, "k_pool", pool, dt)
+    _expect(v_pool, "v_pool", pool, dt)
+    _expect(block_table, "block_table", (p.batch, p.max_blocks), torch.int32)
+    _expect(seq_lens, "seq_lens", (p.batch,), torch.int32)
+    _expect(sel_idx, "sel_idx", (p.batch, p.n_kv_heads, cap), torch.int32)
+    _expect(sel_cnt, "sel_cnt", (p.batch, p.n_kv_heads), torch.int32)
+    if o is None:
+        o = torch.empty(p.batch, p.n_q_heads, p.head_dim, dtype=dt, device=q.device)
+    if lse is None:
+        lse = torch.empty(p.batch, p.n_q_heads, dtype=torch.float32, device=q.device)
+    _expect(o, "o", (p.batch, p.n_q_heads, p.head_dim), dt)
+    _expect(lse, "lse", (p.batch, p.n_q_heads), torch.float32)
+    if workspace is None:
+        workspace = torch.empty(decode_workspace_size(p, cap), dtype=torch.uint8, device=q.device)
+    if status is not None:
+        _expect(status, "status", (1,), torch.int32)
+    pc = p.c()
+    check(lib().sas_decode_attn(ctypes_ref(pc), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                _ptr(block_table), _ptr(seq_lens), _ptr(sel_idx), _ptr(sel_cnt),
+                                cap, _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                _ptr(status), _stream(stream)))
+    return o, lse

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsas.so")
 SOURCES = ["sas_api.hip", "sas_threshold.hip", "sas_generic.hip", "sas_mfma_fwd.hip",
-           "sas_mfma_bwd.hip"]
+           "sas_mfma_bwd.hip", "sas_decode.hip"]
 ARCH = os.environ.get("SAS_OFFLOAD_ARCH", "gfx950")
 
 

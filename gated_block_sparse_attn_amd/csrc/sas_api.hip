@@ -241,3 +241,109 @@ int32_t sas_gated_attn_bwd_dkdv(const sas_problem* p, const void* q, const void*
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// sparse decode
+// ---------------------------------------------------------------------------
+namespace {
+
+int32_t validate_decode(const sas_decode_problem* p, int32_t sel_cap, sas::DecodeShape* s) {
+  if (p == nullptr) return fail(SAS_E_INVALID, "decode problem pointer is NULL");
+  if (p->batch < 1 || p->n_q_heads < 1 || p->n_kv_heads < 1 || p->head_dim < 1 ||
+      p->block_size < 1 || p->max_blocks < 1 || p->pool_blocks < 1)
+    return fail(SAS_E_INVALID, "batch, heads, head_dim, block_size, max_blocks and pool_blocks "
+                "must be >= 1");
+  if (p->n_q_heads % p->n_kv_heads != 0)
+    return fail(SAS_E_INVALID, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)",
+                p->n_q_heads, p->n_kv_heads);
+  if (p->budget_k < 0) return fail(SAS_E_INVALID, "budget_k must be >= 0 (got %d)", p->budget_k);
+  if (p->dtype != SAS_BF16 && p->dtype != SAS_FP32)
+    return fail(SAS_E_INVALID, "dtype %d is not a sas_dtype", p->dtype);
+  if (isnan(p->sm_scale) || isinf(p->sm_scale))
+    return fail(SAS_E_INVALID, "sm_scale must be finite");
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(SAS_E_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", p->head_dim);
+  if (p->block_size != 16 && p->block_size != 32 && p->block_size != 64)
+    return fail(SAS_E_UNSUPPORTED, "block_size %d unsupported (16, 32 or 64)", p->block_size);
+  if (p->max_blocks > 16384)
+    return fail(SAS_E_UNSUPPORTED, "max_blocks %d exceeds 16384", p->max_blocks);
+  if ((long long)p->max_blocks * p->block_size > 0x7fffffffLL)
+    return fail(SAS_E_UNSUPPORTED, "max_blocks * block_size overflows int32");
+  const int G = p->n_q_heads / p->n_kv_heads;
+  if (G > 64) return fail(SAS_E_UNSUPPORTED, "more than 64 query heads per kv head");
+  if ((long long)p->batch * p->n_q_heads > 0x7fffffffLL / 128)
+    return fail(SAS_E_UNSUPPORTED, "batch * n_q_heads too large");
+  const int need = p->budget_k < p->max_blocks - 1 ? p->budget_k : p->max_blocks - 1;
+  if (sel_cap < 1 || sel_cap < need || sel_cap > 65534)
+    return fail(SAS_E_INVALID, "sel_cap %d must lie in [max(1, min(budget_k, max_blocks-1)) = %d, "
+                "65534]", sel_cap, need < 1 ? 1 : need);
+  s->B = p->batch;
+  s->Hq = p->n_q_heads;
+  s->Hkv = p->n_kv_heads;
+  s->G = G;
+  s->D = p->head_dim;
+  s->blk = p->block_size;
+  s->cmax = p->max_blocks;
+  s->pool = p->pool_blocks;
+  s->K = p->budget_k;
+  s->cap = sel_cap;
+  s->fp32 = p->dtype == SAS_FP32;
+  s->scale = p->sm_scale > 0.0f ? p->sm_scale : 1.0f / sqrtf((float)p->head_dim);
+  return SAS_OK;
+}
+
+size_t decode_ws_bytes(const sas::DecodeShape& s) {
+  return align256(sizeof(float) * (size_t)s.B * s.Hkv * (s.cap + 1) * s.G * (s.D + 2));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sas_decode_select(const sas_decode_problem* p, const float* scores,
+                          const int32_t* seq_lens, float* tau, int32_t* sel_idx, int32_t* sel_cnt,
+                          int32_t sel_cap, int32_t* d_status, void* stream) {
+  sas::DecodeShape s;
+  int32_t rc = validate_decode(p, sel_cap, &s);
+  if (rc != SAS_OK) return rc;
+  if (!scores || !seq_lens || !sel_idx || !sel_cnt)
+    return fail(SAS_E_INVALID, "sas_decode_select: a required pointer is NULL");
+  hipError_t e = sas::launch_decode_select(s, scores, seq_lens, tau, sel_idx, sel_cnt, d_status,
+                                           (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sas_decode_select launch");
+  return ok();
+}
+
+size_t sas_decode_workspace_size(const sas_decode_problem* p, int32_t sel_cap) {
+  sas::DecodeShape s;
+  if (validate_decode(p, sel_cap, &s) != SAS_OK) return 0;
+  g_last_error.clear();
+  return decode_ws_bytes(s);
+}
+
+int32_t sas_decode_attn(const sas_decode_problem* p, const void* q, const void* k_pool,
+                        const void* v_pool, const int32_t* block_table, const int32_t* seq_lens,
+                        const int32_t* sel_idx, const int32_t* sel_cnt, int32_t sel_cap, void* o,
+                        float* lse, void* workspace, size_t workspace_bytes, int32_t* d_status,
+                        void* stream) {
+  sas::DecodeShape s;
+  int32_t rc = validate_decode(p, sel_cap, &s);
+  if (rc != SAS_OK) return rc;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !sel_idx || !sel_cnt || !o || !lse)
+    return fail(SAS_E_INVALID, "sas_decode_attn: a required pointer is NULL");
+  const size_t need = decode_ws_bytes(s);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(SAS_E_WORKSPACE, "sas_decode_attn: workspace of %zu bytes given, %zu required",
+                workspace == nullptr ? (size_t)0 : workspace_bytes, need);
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(SAS_E_WORKSPACE, "sas_decode_attn: workspace must be 256-byte aligned");
+  if (sas::decode_attn_lds_bytes(s) > 160 * 1024)
+    return fail(SAS_E_UNSUPPORTED, "sas_decode_attn: too many query heads per kv head");
+  hipError_t e = sas::launch_decode_attn(s, q, k_pool, v_pool, block_table, seq_lens, sel_idx,
+                                         sel_cnt, o, lse, (float*)workspace, d_status,
+                                         (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sas_decode_attn launch");
+  return ok();
+}
+
+}  // extern "C"

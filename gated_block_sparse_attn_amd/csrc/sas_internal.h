@@ -6,6 +6,8 @@
 //   sas_mfma_fwd.hip   bf16 matrix-core forward (b = 64, D = 128)
 //   sas_mfma_bwd.hip   bf16 matrix-core backward (b = 64, D = 128) and the
 //                      selection transpose it needs
+//   sas_decode.hip     sparse decode: per-group Top-K select, attention over
+//                      the gathered blocks of a paged cache
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -75,6 +77,23 @@ hipError_t launch_bwd_dq_mfma(const Shape& s, const BwdPtrs& p, char* ws, const 
                               hipStream_t st);
 hipError_t launch_bwd_dkdv_mfma(const Shape& s, const BwdPtrs& p, char* ws,
                                 const BwdWorkspace& wl, hipStream_t st);
+
+// ---- sparse decode (sas_decode.hip) ----
+struct DecodeShape {
+  int B, Hq, Hkv, G, D, blk, cmax, pool, K, cap;
+  int fp32;
+  float scale;
+};
+size_t decode_attn_lds_bytes(const DecodeShape& s);
+hipError_t launch_decode_select(const DecodeShape& s, const float* scores, const int32_t* seq_lens,
+                                float* tau, int32_t* sel_idx, int32_t* sel_cnt, int32_t* d_status,
+                                hipStream_t st);
+// part: workspace of B * Hkv * (cap + 1) * G * (D + 2) floats (tile partials)
+hipError_t launch_decode_attn(const DecodeShape& s, const void* q, const void* k_pool,
+                              const void* v_pool, const int32_t* block_table,
+                              const int32_t* seq_lens, const int32_t* sel_idx,
+                              const int32_t* sel_cnt, void* o, float* lse, float* part,
+                              int32_t* d_status, hipStream_t st);
 
 hipError_t launch_fwd_mfma(const Shape& s, const void* q, const void* k, const void* v,
                            const float* log_gate, const int32_t* sel_idx, const int32_t* sel_cnt,

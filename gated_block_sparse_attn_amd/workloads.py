@@ -147,3 +147,105 @@ def sample_units(w: Workload, count: int, seed: int = 1234):
         i = int(torch.randint(c, (1,), generator=g))
         units.add((b, h, i))
     return sorted(units)
+
+
+# ---------------------------------------------------------------------------
+# sparse decode workloads: one new token per sequence over a paged KV cache
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    block: int
+    seq_lens: tuple         # tokens in the cache per sequence (the last one is the query's)
+    budget: int
+    dtype: str
+    seed: int
+    pool_pages: int = 0     # 0: one page per logical block; else a shared pool of this size
+    score_kind: str = "normal"   # "normal" | "normal_boost" | "gumbel"
+    boost_frac: float = 0.05
+    boost_value: float = 4.0
+
+    @property
+    def max_blocks(self) -> int:
+        return (max(self.seq_lens) + self.block - 1) // self.block
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def pages(self) -> int:
+        return self.pool_pages or self.batch * self.max_blocks
+
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "fp32" else torch.bfloat16
+
+
+_LENS_64K = tuple(65536 - x for x in (0, 1, 17, 63, 64, 100, 501, 1000))
+
+DECODE_WORKLOADS = {
+    # Qwen3-4B attention shape (32 / 8 heads, D = 128), block 64, 2048-token
+    # budget (K = 32); batch 8 of ~64k-token sequences (ragged lengths), the
+    # decode setting of the paper's batched measurement; peaked scores
+    "qwen3_4b_decode_b8_64k": DecodeWorkload("qwen3_4b_decode_b8_64k", 8, 32, 8, 128, 64,
+                                             _LENS_64K, 32, "bf16", 21, pool_pages=4096,
+                                             score_kind="normal_boost"),
+    # the same model at batch 1 and 512k tokens (8192 blocks per row): the
+    # long-context point where Top-K selection dominates the step
+    "qwen3_4b_decode_b1_512k": DecodeWorkload("qwen3_4b_decode_b1_512k", 1, 32, 8, 128, 64,
+                                              (524288,), 32, "bf16", 22, pool_pages=2048,
+                                              score_kind="gumbel"),
+}
+
+
+def decode_custom(batch, n_q_heads, n_kv_heads, head_dim, block, seq_lens, budget,
+                  dtype="bf16", seed=0, pool_pages=0, score_kind="normal") -> DecodeWorkload:
+    return DecodeWorkload(f"decode_custom_{seed}", batch, n_q_heads, n_kv_heads, head_dim, block,
+                          tuple(seq_lens), budget, dtype, seed, pool_pages=pool_pages,
+                          score_kind=score_kind)
+
+
+def generate_decode(w: DecodeWorkload):
+    """Draw a decode problem on the CPU, in the fixed order q, k_pool, v_pool,
+    page table, scores (then the boost columns).
+
+    q [B,Hq,D] and the pools [P,Hkv,b,D] ~ N(0, 1) in the workload dtype; the
+    page of logical block m of sequence s is a seeded random page (a
+    permutation when every logical block has its own page, else drawn with
+    replacement from the shared pool); scores fp32 [B,Hkv,max_blocks].
+    """
+    g = torch.Generator().manual_seed(w.seed)
+    dt = w.torch_dtype()
+    cmax = w.max_blocks
+    P = w.pages
+
+    def normal(shape):
+        return torch.randn(shape, generator=g, dtype=torch.float32).to(dt)
+
+    q = normal((w.batch, w.n_q_heads, w.head_dim))
+    kp = normal((P, w.n_kv_heads, w.block, w.head_dim))
+    vp = normal((P, w.n_kv_heads, w.block, w.head_dim))
+    if w.pool_pages:
+        bt = torch.randint(P, (w.batch, cmax), generator=g, dtype=torch.int64)
+    else:
+        bt = torch.randperm(P, generator=g).reshape(w.batch, cmax)
+    sshape = (w.batch, w.n_kv_heads, cmax)
+    if w.score_kind == "gumbel":
+        u = torch.rand(sshape, generator=g, dtype=torch.float32)
+        u.clamp_(min=torch.finfo(torch.float32).tiny, max=1.0 - 2.0 ** -24)
+        scores = -torch.log(-torch.log(u))
+    else:
+        scores = torch.randn(sshape, generator=g, dtype=torch.float32)
+        if w.score_kind == "normal_boost":
+            nb = int(math.ceil(w.boost_frac * cmax))
+            for b in range(w.batch):
+                for h in range(w.n_kv_heads):
+                    cols = torch.randperm(cmax, generator=g)[:nb]
+                    scores[b, h, cols] += w.boost_value
+    return {"q": q, "k_pool": kp, "v_pool": vp, "block_table": bt.to(torch.int32),
+            "seq_lens": torch.tensor(w.seq_lens, dtype=torch.int32), "scores": scores.contiguous()}

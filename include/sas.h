@@ -232,6 +232,95 @@ int32_t sas_gated_attn_bwd_dkdv(const sas_problem* p, const void* q, const void*
                                 float* dlog_gate, float* dscores, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Sparse decode (one new query token per sequence)
+ *
+ * The inference step of the paper (Sec. 4.3, Alg. 2; Sec. 5.1 "Inference
+ * implementation"): per query group (kv head) the Top-K historical blocks
+ * are chosen from selector scores, and the new token attends its current
+ * block plus the selected blocks, gathered from a paged KV cache, with a plain
+ * softmax (no gates at inference):  o = softmax(sm_scale q K_S^T) V_S.
+ *
+ * Sequence s holds n_s = seq_lens[s] tokens, the newest one being the query
+ * (its K / V already in the cache).  Its current block is c_s = (n_s - 1) / b
+ * (tokens c_s * b .. n_s - 1 are attended); its historical blocks are
+ * 0 .. c_s - 1.  K counts historical blocks; K >= c_s keeps them all; K = 0
+ * keeps none.
+ *
+ * Layouts (contiguous):
+ *    q, o                 [B, Hq, D]          (dtype)
+ *    k_pool, v_pool       [P, Hkv, b, D]      (dtype): page p holds one block
+ *                                              of b tokens for every kv head
+ *    block_table          [B, max_blocks]     int32: page of logical block m
+ *    seq_lens             [B]                 int32, 1 <= n_s <= max_blocks * b
+ *    scores               [B, Hkv, max_blocks] fp32 selector scores; entries
+ *                                              m >= c_s are never read
+ *    tau                  [B, Hkv]            fp32
+ *    sel_idx              [B, Hkv, sel_cap]   int32, ascending, padded with -1
+ *    sel_cnt              [B, Hkv]            int32
+ *    lse                  [B, Hq]             fp32, natural log
+ * Query head h reads kv head h / G.  seq_lens, block_table and the selection
+ * live in device memory and are checked by the kernels: an out-of-range
+ * length is clamped into [1, max_blocks * b], an out-of-range page or a
+ * selected index outside [0, c_s) contributes nothing, and each of these sets
+ * *d_status = SAS_E_INVALID when d_status is non-NULL (never cleared by the
+ * library).  Every other convention of this header applies (caller-owned
+ * device memory, host validation before any launch, thread-local messages).
+ * Supported: D in {64, 128}, b in {16, 32, 64}, max_blocks <= 16384,
+ * G = Hq / Hkv <= 64, dtype bf16 or fp32.
+ * ------------------------------------------------------------------------ */
+typedef struct sas_decode_problem {
+  int32_t batch;       /* B sequences, one query token each                    */
+  int32_t n_q_heads;   /* Hq                                                   */
+  int32_t n_kv_heads;  /* Hkv, divides Hq                                      */
+  int32_t head_dim;    /* D in {64, 128}                                       */
+  int32_t block_size;  /* b in {16, 32, 64}: tokens per block = per page       */
+  int32_t max_blocks;  /* row length of scores / block_table                   */
+  int32_t pool_blocks; /* P: pages in k_pool / v_pool                          */
+  int32_t budget_k;    /* K >= 0 historical blocks per query group             */
+  int32_t dtype;       /* sas_dtype of q, k_pool, v_pool, o                    */
+  float sm_scale;      /* <= 0 selects 1/sqrt(D)                               */
+} sas_decode_problem;
+
+/*
+ * sas_decode_select -- per-group Top-K of the selector scores (Alg. 2 step
+ * "I = Top-K(s, K)"; Sec. 5.1: Top-K blocks per query group).  As in the
+ * training path the set is a threshold: tau = the K-th largest fp32 score of
+ * the historical blocks and I = {m < c_s : s_m >= tau} (ties at tau all kept,
+ * so |I| can exceed K only through exact ties), found by a most-significant-
+ * digit-first radix select over order-preserving integer keys (no sort), one
+ * workgroup per (sequence, kv head).
+ * Outputs: tau (nullable; -inf when K >= c_s, +inf when K = 0 < c_s),
+ * sel_idx (ascending, remaining slots -1), sel_cnt (the true count); a count
+ * above sel_cap sets *d_status = SAS_E_CAPACITY.
+ * sel_cap: >= max(1, min(K, max_blocks - 1)) and <= 65534.
+ */
+int32_t sas_decode_select(const sas_decode_problem* p, const float* scores,
+                          const int32_t* seq_lens, float* tau, int32_t* sel_idx, int32_t* sel_cnt,
+                          int32_t sel_cap, int32_t* d_status, void* stream);
+
+/* Bytes of device workspace sas_decode_attn needs (0 if p or sel_cap is
+ * invalid; sas_last_error says why). */
+size_t sas_decode_workspace_size(const sas_decode_problem* p, int32_t sel_cap);
+
+/*
+ * sas_decode_attn -- attention of each new token over its current block and
+ * its selected blocks (Alg. 2: S = B0 u U_{m in I} B_m,
+ * o = softmax(q K_S^T) V_S; Sec. 5.1: only the selected KV blocks are
+ * gathered from the paged cache; the G query heads of a group share them).
+ * Reads the first min(sel_cnt, sel_cap) entries of each sel_idx row (as
+ * written by sas_decode_select, or any ascending list of blocks < c_s).
+ * Outputs: o (dtype) [B, Hq, D], lse fp32 [B, Hq].
+ * workspace: >= sas_decode_workspace_size(p, sel_cap) bytes, 256-byte
+ * aligned, caller-owned, not preserved; calls sharing it must not overlap.
+ * Results are bitwise deterministic (tile partials merged in a fixed order).
+ */
+int32_t sas_decode_attn(const sas_decode_problem* p, const void* q, const void* k_pool,
+                        const void* v_pool, const int32_t* block_table, const int32_t* seq_lens,
+                        const int32_t* sel_idx, const int32_t* sel_cnt, int32_t sel_cap, void* o,
+                        float* lse, void* workspace, size_t workspace_bytes, int32_t* d_status,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -152,3 +152,65 @@ def test_python_binding_rejects_host_tensors_before_calling():
     s = torch.zeros(1, 1, 8, 8)
     with pytest.raises(ValueError, match="device tensor"):
         api.gate_threshold(p, s)
+
+
+# ---------------------------------------------------------------- sparse decode
+
+def dprob(**kw):
+    base = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, block_size=64, max_blocks=16,
+                pool_blocks=40, budget_k=4, dtype=nat.SAS_BF16, sm_scale=0.0)
+    base.update(kw)
+    return nat.SasDecodeProblem(**base)
+
+
+def dsel(p, cap=4, **ptrs):
+    a = dict(s=FAKE, n=FAKE, tau=FAKE, si=FAKE, sc=FAKE)
+    a.update(ptrs)
+    return lib().sas_decode_select(ctypes.byref(p) if p is not None else None, a["s"], a["n"],
+                                   a["tau"], a["si"], a["sc"], cap, None, None)
+
+
+def dattn(p, cap=4, ws=FAKE * 256, ws_bytes=1 << 40, **ptrs):
+    a = {n: FAKE for n in ("q", "kp", "vp", "bt", "n", "si", "sc", "o", "lse")}
+    a.update(ptrs)
+    return lib().sas_decode_attn(ctypes.byref(p), a["q"], a["kp"], a["vp"], a["bt"], a["n"],
+                                 a["si"], a["sc"], cap, a["o"], a["lse"], ws, ws_bytes, None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), nat.SAS_E_INVALID),
+    (dict(n_q_heads=6, n_kv_heads=4), nat.SAS_E_INVALID),
+    (dict(budget_k=-1), nat.SAS_E_INVALID),
+    (dict(pool_blocks=0), nat.SAS_E_INVALID),
+    (dict(max_blocks=0), nat.SAS_E_INVALID),
+    (dict(dtype=5), nat.SAS_E_INVALID),
+    (dict(sm_scale=float("inf")), nat.SAS_E_INVALID),
+    (dict(head_dim=80), nat.SAS_E_UNSUPPORTED),
+    (dict(block_size=8), nat.SAS_E_UNSUPPORTED),
+    (dict(max_blocks=16385), nat.SAS_E_UNSUPPORTED),
+    (dict(n_q_heads=130, n_kv_heads=2), nat.SAS_E_UNSUPPORTED),   # G = 65
+])
+def test_decode_invalid_problems_rejected(kw, code):
+    p = dprob(**kw)
+    assert dsel(p) == code
+    assert lib().sas_last_error()
+    assert dattn(p) == code
+    assert lib().sas_decode_workspace_size(ctypes.byref(p), 4) == 0
+
+
+def test_decode_null_pointers_capacity_and_workspace():
+    assert dsel(None) == nat.SAS_E_INVALID
+    p = dprob()
+    assert dsel(p, s=None) == nat.SAS_E_INVALID
+    assert dsel(p, n=None) == nat.SAS_E_INVALID
+    assert dattn(p, bt=None) == nat.SAS_E_INVALID
+    assert dattn(p, lse=None) == nat.SAS_E_INVALID
+    assert b"NULL" in lib().sas_last_error()
+    assert dsel(p, cap=3) == nat.SAS_E_INVALID            # cap < min(K, max_blocks - 1)
+    assert dsel(p, cap=65535) == nat.SAS_E_INVALID
+    n = lib().sas_decode_workspace_size(ctypes.byref(p), 4)
+    assert n > 0 and n % 256 == 0
+    assert lib().sas_decode_workspace_size(ctypes.byref(p), 8) > n
+    assert dattn(p, ws_bytes=n - 1) == nat.SAS_E_WORKSPACE
+    assert dattn(p, ws=None) == nat.SAS_E_WORKSPACE
+    assert dattn(p, ws=FAKE * 256 + 4, ws_bytes=n) == nat.SAS_E_WORKSPACE
