@@ -28,6 +28,12 @@ algorithm:
     under the sparse scope (Eq. 8).
   * Sec. 4.2.2 (Eq. 5) / App. D.1: closed form of the inner-gate gradient,
     dg_m = sum_{i in B_m} (p_i / g_m) dO^T (v_i - o).
+  * Sec. 4.1 "Components of learnable ranking" and Tab. 1 (the ablated
+    variants, kept as switches): gate position outer, o = softmax(q K^T)
+    (g . V), with dg_m = sum_{i in B_m} p_i dO^T v_i (Eq. 5 outer); gate
+    activation sigmoid (log g = log sigmoid(s)) or raw logits (log g = s),
+    beside the default softmax (Eq. 6); the current block keeps g0 = 1 in
+    every variant.
 
 Readings where the pages leave a step open (each also listed in the design
 notes of the repository):
@@ -89,15 +95,29 @@ def kth_largest_threshold(hist_f32: np.ndarray, k: int) -> np.float32:
     return np.float32(np.partition(hist_f32, n - k)[n - k])
 
 
-def gate_threshold(scores: np.ndarray, budget_k: int):
+def log_activation(hist64: np.ndarray, act: str) -> np.ndarray:
+    """log g of one row's historical scores under gate activation ``act``:
+    softmax (Eq. 6: s - LSE(s)), sigmoid (log sigmoid(s), Tab. 1 row 5) or
+    raw logits (s itself, Tab. 1 row 6)."""
+    if act == "softmax":
+        return hist64 - _logsumexp(hist64)
+    if act == "sigmoid":
+        # log sigmoid(s) = -log(1 + exp(-s)), evaluated without overflow
+        return -np.logaddexp(0.0, -hist64)
+    if act == "raw":
+        return hist64.copy()
+    raise ValueError(act)
+
+
+def gate_threshold(scores: np.ndarray, budget_k: int, act: str = "softmax"):
     """Gates, thresholds and selected sets for every query block.
 
     scores: fp32 [B, Hkv, C, C]; only entries m < i of row i are read (the
-    historical blocks of query block i, Sec. 4.1).
+    historical blocks of query block i, Sec. 4.1).  ``act``: gate activation.
 
     Returns (log_gate, tau, sel):
-      log_gate float64 [B, Hkv, C, C]: s_m - LSE_{m<i}(s) for m < i (Eq. 6),
-               0 on the diagonal (g0 = 1, Eq. 4), -inf above it;
+      log_gate float64 [B, Hkv, C, C]: log phi(s)_m for m < i (Eq. 6 for the
+               softmax), 0 on the diagonal (g0 = 1, Eq. 4), -inf above it;
       tau      float32 [B, Hkv, C]: score-space threshold of each row;
       sel      bool    [B, Hkv, C, C]: m < i and s_{i,m} >= tau_i.
     """
@@ -113,8 +133,7 @@ def gate_threshold(scores: np.ndarray, budget_k: int):
             for i in range(c):
                 hist = scores[b, h, i, :i]
                 if i > 0:
-                    s64 = hist.astype(np.float64)
-                    log_gate[b, h, i, :i] = s64 - _logsumexp(s64)
+                    log_gate[b, h, i, :i] = log_activation(hist.astype(np.float64), act)
                 log_gate[b, h, i, i] = 0.0
                 t = kth_largest_threshold(hist, budget_k)
                 tau[b, h, i] = t
@@ -174,12 +193,16 @@ def default_scale(head_dim: int, sm_scale: float | None) -> float:
 
 
 def forward(q, k, v, log_gate, sel, block: int, sm_scale: float | None = None,
-            query_blocks=None):
+            query_blocks=None, gate_pos: str = "inner"):
     """Eq. 9 output and natural-log LSE, one query block at a time.
 
     q: [B, Hq, N, D]; k, v: [B, Hkv, N, D]; log_gate/sel: [B, Hkv, C, C].
     ``query_blocks``: optional iterable of (b, h_kv, i) to evaluate (others
     are left 0), so large shapes can be sampled.
+    ``gate_pos``: "inner" adds log g to the logits (Eq. 9); "outer" leaves the
+    logits ungated and multiplies the value rows of each block by its gate,
+    o = softmax(q K^T) (g . V) (Sec. 4.1, Tab. 1 row 3); lse is then the
+    ungated one.
     Returns (o [B, Hq, N, D], lse [B, Hq, N]) in float64.
     """
     bsz, hq, n, d = q.shape
@@ -195,6 +218,9 @@ def forward(q, k, v, log_gate, sel, block: int, sm_scale: float | None = None,
         keys, bias, _, mask = _attended_keys(i, block, sel[b, hk, i], log_gate[b, hk, i])
         kk = _f64(k[b, hk, keys])
         vv = _f64(v[b, hk, keys])
+        if gate_pos == "outer":
+            vv = vv * np.exp(bias)[:, None]
+            bias = np.zeros_like(bias)
         rows = slice(i * block, (i + 1) * block)
         for hh in range(hk * g, (hk + 1) * g):
             z = scale * (_f64(q[b, hh, rows]) @ kk.T) + bias[None, :]
@@ -206,7 +232,7 @@ def forward(q, k, v, log_gate, sel, block: int, sm_scale: float | None = None,
 
 
 def backward(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = None,
-             query_blocks=None):
+             query_blocks=None, gate_pos: str = "inner"):
     """Gradients of Eq. 9 w.r.t. q, k, v and the block log gates.
 
     Follows the recomputation view of App. E: P from the attended logits,
@@ -216,6 +242,10 @@ def backward(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = No
     query tokens of block i (all heads of the group) and the key tokens of
     selected historical block m.  Zero for unselected m, the diagonal and the
     upper triangle.
+
+    ``gate_pos`` = "outer": the value rows are scaled by their block's gate,
+    so dP = dO (g . V)^T, dV = g . (P^T dO), and dLogG[i, m] = g_m dg_m =
+    sum over the block of P * dP (Eq. 5 outer: dg_m = sum_i p_i dO^T v_i).
 
     If ``query_blocks`` is given, only those query blocks contribute (their dQ
     and dLogG rows are exact; dK/dV hold only their contributions).
@@ -236,6 +266,11 @@ def backward(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = No
         keys, bias, kblk, mask = _attended_keys(i, block, sel[b, hk, i], log_gate[b, hk, i])
         kk = _f64(k[b, hk, keys])
         vv = _f64(v[b, hk, keys])
+        gkey = np.ones(keys.shape[0])
+        if gate_pos == "outer":
+            gkey = np.exp(bias)
+            vv = vv * gkey[:, None]
+            bias = np.zeros_like(bias)
         rows = slice(i * block, (i + 1) * block)
         ds_sum = np.zeros(keys.shape[0])
         for hh in range(hk * g, (hk + 1) * g):
@@ -249,8 +284,8 @@ def backward(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = No
             ds = p * (dp - delta)
             dq[b, hh, rows] = scale * (ds @ kk)
             np.add.at(dk[b, hk], keys, scale * (ds.T @ qq))
-            np.add.at(dv[b, hk], keys, p.T @ dd)
-            ds_sum += ds.sum(axis=0)
+            np.add.at(dv[b, hk], keys, gkey[:, None] * (p.T @ dd))
+            ds_sum += (p * dp).sum(axis=0) if gate_pos == "outer" else ds.sum(axis=0)
         for m in np.unique(kblk):
             if m != i:
                 dlg[b, hk, i, m] = ds_sum[kblk == m].sum()
@@ -258,7 +293,7 @@ def backward(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = No
 
 
 def backward_kv_block(q, k, v, do, log_gate, sel, block: int, b: int, hk: int, j: int,
-                      sm_scale: float | None = None):
+                      sm_scale: float | None = None, gate_pos: str = "inner"):
     """dK and dV of one key block j of one (batch, kv head), exactly.
 
     Sums the contributions of every query block that attends block j: the
@@ -267,18 +302,21 @@ def backward_kv_block(q, k, v, do, log_gate, sel, block: int, b: int, hk: int, j
     """
     c = q.shape[2] // block
     users = [(b, hk, i) for i in range(j, c) if i == j or sel[b, hk, i, j]]
-    _, dk, dv, _ = backward(q, k, v, do, log_gate, sel, block, sm_scale, query_blocks=users)
+    _, dk, dv, _ = backward(q, k, v, do, log_gate, sel, block, sm_scale, query_blocks=users,
+                            gate_pos=gate_pos)
     rows = slice(j * block, (j + 1) * block)
     return dk[b, hk, rows], dv[b, hk, rows]
 
 
-def dscores(dlog_gate, log_gate, sel):
+def dscores(dlog_gate, log_gate, sel, act: str = "softmax"):
     """Selector-score gradient from the block log-gate gradient (App. D.3).
 
     dg_m = dLogG_m / g_m on selected blocks and 0 on unselected ones (sparse
-    scope, Eq. 8); ds_m = g_m (dg_m - sum_l g_l dg_l) over the historical
-    blocks m < i.  Zero for m >= i.  No gradient flows through the Top-K
-    selection itself (it is piecewise constant in s, Sec. 3).
+    scope, Eq. 8); for the softmax gate ds_m = g_m (dg_m - sum_l g_l dg_l)
+    over the historical blocks m < i.  For the sigmoid gate each block's
+    gate depends on its own score only: ds_m = g_m (1 - g_m) dg_m; for raw
+    logits log g = s, so ds_m = dLogG_m.  Zero for m >= i.  No gradient flows
+    through the Top-K selection itself (it is piecewise constant in s, Sec. 3).
     """
     bsz, hkv, c, _ = dlog_gate.shape
     out = np.zeros((bsz, hkv, c, c))
@@ -289,7 +327,14 @@ def dscores(dlog_gate, log_gate, sel):
                 s = sel[b, h, i, :i]
                 dg = np.zeros(i)
                 dg[s] = dlog_gate[b, h, i, :i][s] / gate[s]
-                out[b, h, i, :i] = gate * (dg - np.sum(gate * dg))
+                if act == "softmax":
+                    out[b, h, i, :i] = gate * (dg - np.sum(gate * dg))
+                elif act == "sigmoid":
+                    out[b, h, i, :i] = gate * (1.0 - gate) * dg
+                elif act == "raw":
+                    out[b, h, i, :i] = gate * dg
+                else:
+                    raise ValueError(act)
     return out
 
 
