@@ -17,6 +17,14 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "sas.h")
 SAS_BF16 = 0
 SAS_FP32 = 1
 
+SAS_GATE_SOFTMAX = 0
+SAS_GATE_SIGMOID = 1
+SAS_GATE_RAW = 2
+SAS_GATE_INNER = 0
+SAS_GATE_OUTER = 1
+GATE_ACTS = {"softmax": SAS_GATE_SOFTMAX, "sigmoid": SAS_GATE_SIGMOID, "raw": SAS_GATE_RAW}
+GATE_POS = {"inner": SAS_GATE_INNER, "outer": SAS_GATE_OUTER}
+
 SAS_OK = 0
 SAS_E_INVALID = -1
 SAS_E_UNSUPPORTED = -2
@@ -34,7 +42,8 @@ class SasProblem(ctypes.Structure):
                 ("n_kv_heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("budget_k", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("o_dtype", ctypes.c_int32), ("sm_scale", ctypes.c_float)]
+                ("o_dtype", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+                ("gate_act", ctypes.c_int32), ("gate_pos", ctypes.c_int32)]
 
 
 class SasDecodeProblem(ctypes.Structure):

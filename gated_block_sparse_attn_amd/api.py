@@ -37,6 +37,8 @@ class Problem:
     sm_scale: float = 0.0      # <= 0: 1/sqrt(head_dim)
     o_dtype: str = "bf16"      # dtype of the forward output o (fp32 problems:
                                # always "fp32")
+    gate_act: str = "softmax"  # "softmax" | "sigmoid" | "raw"
+    gate_pos: str = "inner"    # "inner" (log g in the logits) | "outer" (g scales V)
 
     def __post_init__(self):
         if self.dtype == "fp32" and self.o_dtype != "fp32":
@@ -59,7 +61,8 @@ class Problem:
                           self.head_dim, self.block_size, self.budget_k,
                           _native.SAS_BF16 if self.dtype == "bf16" else _native.SAS_FP32,
                           _native.SAS_BF16 if self.o_dtype == "bf16" else _native.SAS_FP32,
-                          float(self.sm_scale))
+                          float(self.sm_scale), _native.GATE_ACTS[self.gate_act],
+                          _native.GATE_POS[self.gate_pos])
 
     def default_cap(self) -> int:
         return max(1, min(self.budget_k, self.n_blocks - 1))

@@ -53,6 +53,11 @@ int32_t validate(const sas_problem* p, int32_t sel_cap, bool need_cap, sas::Shap
     return fail(SAS_E_INVALID, "o_dtype must be SAS_FP32 when dtype is SAS_FP32");
   if (isnan(p->sm_scale) || isinf(p->sm_scale))
     return fail(SAS_E_INVALID, "sm_scale must be finite");
+  if (p->gate_act != SAS_GATE_SOFTMAX && p->gate_act != SAS_GATE_SIGMOID &&
+      p->gate_act != SAS_GATE_RAW)
+    return fail(SAS_E_INVALID, "gate_act %d is not a sas_gate_act", p->gate_act);
+  if (p->gate_pos != SAS_GATE_INNER && p->gate_pos != SAS_GATE_OUTER)
+    return fail(SAS_E_INVALID, "gate_pos %d is not a sas_gate_pos", p->gate_pos);
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(SAS_E_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", p->head_dim);
   if (p->block_size != 16 && p->block_size != 32 && p->block_size != 64)
@@ -83,6 +88,8 @@ int32_t validate(const sas_problem* p, int32_t sel_cap, bool need_cap, sas::Shap
   s->fp32 = p->dtype == SAS_FP32;
   s->o_fp32 = p->o_dtype == SAS_FP32;
   s->scale = p->sm_scale > 0.0f ? p->sm_scale : 1.0f / sqrtf((float)p->head_dim);
+  s->act = p->gate_act;
+  s->outer = p->gate_pos == SAS_GATE_OUTER;
   return SAS_OK;
 }
 
@@ -92,7 +99,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 namespace sas {
 
-bool mfma_path(const Shape& s) { return !s.fp32 && s.D == 128 && s.blk == 64; }
+bool mfma_path(const Shape& s) { return !s.fp32 && s.D == 128 && s.blk == 64 && !s.outer; }
 
 BwdWorkspace bwd_workspace_layout(const Shape& s) {
   BwdWorkspace w{};

@@ -7,6 +7,8 @@
 //  forward  (SAS Sec. 4.3 Eq. 9, App. E Alg. 3): per query block the current
 //           block (causal, bias 0) and the selected historical blocks (bias
 //           log g), streamed tile by tile with an online softmax in base 2;
+//           with the outer gate position (Sec. 4.1, Tab. 1 row 3) the logits
+//           carry no bias and the block's value rows are scaled by g;
 //  backward (App. E Alg. 4): P recomputed from LSE, dS = P (dP - Delta);
 //           query-major pass: dQ = scale dS K with Delta = rowsum(O dO), and
 //           the row sum of P dP (Delta without the rounding of O); key-major
@@ -41,6 +43,7 @@ struct GenArgs {
   void* out; float* lse_out; void* dq; void* dk; void* dv; float* dlg; float* delta;
   int Hq, Hkv, G, N, C, cap;
   int o_fp32;   // o is stored as float32 (else as T)
+  int outer;    // gates scale the value rows after the softmax (else log g bias)
   float c2;     // sm_scale * log2(e)
   float scale;  // sm_scale
 };
@@ -77,7 +80,9 @@ __global__ void __launch_bounds__(64) fwd_generic_kernel(GenArgs a) {
   float m = -INFINITY, l = 0.0f;
   for (int tile = 0; tile <= cnt; ++tile) {
     const int kb = tile == 0 ? i : sel[tile - 1];
-    const float beta = tile == 0 ? 0.0f : a.lg[row * a.C + kb] * kLog2e;
+    const float lgv = tile == 0 ? 0.0f : a.lg[row * a.C + kb] * kLog2e;
+    const float beta = a.outer ? 0.0f : lgv;           // bias of the logits
+    const float gv = a.outer ? exp2f(lgv) : 1.0f;      // factor of the value rows
     __syncthreads();
     stage_tile<T, D, BLK>(ks, kbase + (long long)kb * BLK * D);
     stage_tile<T, D, BLK>(vs, vbase + (long long)kb * BLK * D);
@@ -94,8 +99,9 @@ __global__ void __launch_bounds__(64) fwd_generic_kernel(GenArgs a) {
         const float corr = exp2f(m - mnew);
         const float p = exp2f(x - mnew);
         l = l * corr + p;
+        const float pv = p * gv;
 #pragma unroll
-        for (int d = 0; d < D; ++d) acc[d] = acc[d] * corr + p * vs[u * D + d];
+        for (int d = 0; d < D; ++d) acc[d] = acc[d] * corr + pv * vs[u * D + d];
         m = mnew;
       }
     }
@@ -156,7 +162,9 @@ __global__ void __launch_bounds__(64) bwd_q_generic_kernel(GenArgs a) {
     }
     for (int tile = 0; tile <= cnt; ++tile) {
       const int kb = tile == 0 ? i : sel[tile - 1];
-      const float beta = tile == 0 ? 0.0f : a.lg[row * a.C + kb] * kLog2e;
+      const float lgv = tile == 0 ? 0.0f : a.lg[row * a.C + kb] * kLog2e;
+      const float beta = a.outer ? 0.0f : lgv;
+      const float gv = a.outer ? exp2f(lgv) : 1.0f;   // outer: dP = g dO . v
       __syncthreads();
       stage_tile<T, D, BLK>(ks, kbase + (long long)kb * BLK * D);
       stage_tile<T, D, BLK>(vs, vbase + (long long)kb * BLK * D);
@@ -171,6 +179,7 @@ __global__ void __launch_bounds__(64) bwd_q_generic_kernel(GenArgs a) {
             x += q[d] * ks[u * D + d];
             dp += dov[d] * vs[u * D + d];
           }
+          dp *= gv;
           const float p = exp2f(x * a.c2 + beta - lse2);
           const float ds = p * (dp - delta);
           dx += p * dp;
@@ -229,6 +238,9 @@ __global__ void __launch_bounds__(64) bwd_kv_generic_kernel(GenArgs a) {
       }
       beta = a.lg[(rowbase + i) * a.C + j] * kLog2e;
     }
+    // outer: no bias; dP = g dO . v, dV = g P^T dO, dLogG = sum of P dP
+    const float gv = a.outer ? exp2f(beta) : 1.0f;
+    if (a.outer) beta = 0.0f;
     float gsum = 0.0f;
     for (int hl = 0; hl < a.G; ++hl) {
       const int h = hk * a.G + hl;
@@ -244,12 +256,14 @@ __global__ void __launch_bounds__(64) bwd_kv_generic_kernel(GenArgs a) {
           x += ld(qrow + d) * ks[u * D + d];
           dp += ld(drow + d) * vs[u * D + d];
         }
+        dp *= gv;
         const float p = exp2f(x * a.c2 + beta - a.lse[q0 + tq] * kLog2e);
         const float ds = p * (dp - a.delta[q0 + tq]);
-        gsum += ds;
+        gsum += a.outer ? p * dp : ds;
+        const float pg = p * gv;
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-          dv[d] += p * ld(drow + d);
+          dv[d] += pg * ld(drow + d);
           dk[d] += ds * ld(qrow + d);
         }
       }
@@ -275,6 +289,7 @@ GenArgs make_args(const Shape& s) {
   GenArgs a{};
   a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.G; a.N = s.N; a.C = s.C; a.cap = s.cap;
   a.o_fp32 = s.o_fp32;
+  a.outer = s.outer;
   a.c2 = s.scale * kLog2e;
   a.scale = s.scale;
   return a;

@@ -26,6 +26,8 @@ struct Shape {
   int fp32;          // 1: tensors are float32, 0: bfloat16
   int o_fp32;        // 1: the forward output o is float32
   float scale;       // sm_scale (already defaulted)
+  int act;           // sas_gate_act
+  int outer;         // 1: gates scale the value rows after the softmax
 };
 
 // Workspace carve-up of the backward pass (byte offsets, 256-aligned).

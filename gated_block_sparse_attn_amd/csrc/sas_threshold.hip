@@ -1,7 +1,8 @@
 // Gate activation, Top-K threshold and selector-score gradient kernels.
 //
 // SAS paper (arXiv 2609.13141): Sec. 4.1 Eq. 4 (current block keeps a unit
-// gate), Sec. 4.2.2 Eq. 6 (log g_m = s_m - LSE(s) over the historical blocks),
+// gate), Sec. 4.2.2 Eq. 6 (log g_m = s_m - LSE(s) over the historical blocks;
+// the sigmoid and raw-logit activations of Sec. 4.1 / Tab. 1 as switches),
 // Sec. 4.3 Alg. 1 and App. E (Top-K realised as a per-query threshold on the
 // gate, no sort), App. D.3 and Eq. 8 (softmax backward to the scores under
 // the sparse scope).
@@ -58,7 +59,8 @@ __global__ void __launch_bounds__(256) threshold_kernel(const float* __restrict_
                                                         int32_t* __restrict__ sel_idx,
                                                         int32_t* __restrict__ sel_cnt,
                                                         int32_t* __restrict__ d_status,
-                                                        long long rows, int C, int K, int cap) {
+                                                        long long rows, int C, int K, int cap,
+                                                        int act) {
   extern __shared__ float s_hist[];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -82,20 +84,26 @@ __global__ void __launch_bounds__(256) threshold_kernel(const float* __restrict_
   // LSE over the historical blocks (Eq. 6): fp32 exponentials of values <= 0,
   // accumulated in fp64 so the normaliser does not drift with long rows.
   double lse = 0.0;
-  if (i > 0) {
+  if (i > 0 && act == SAS_GATE_SOFTMAX) {
     double acc = 0.0;
     for (int m = lane; m < i; m += 64) acc += (double)expf(s[m] - mx);
     acc = wave_sum_d(acc);
     lse = (double)mx + log(acc);
   }
 
-  // log_gate row: s - LSE for historical blocks, 0 for the current block
-  // (unit gate, Eq. 4), -inf above the diagonal.
+  // log_gate row: log phi(s) for historical blocks (softmax: s - LSE;
+  // sigmoid: log sigmoid(s) = -log(1 + exp(-s)), evaluated without overflow;
+  // raw: s), 0 for the current block (unit gate, Eq. 4), -inf above the
+  // diagonal.
   float* lrow = log_gate + row * (long long)C;
   for (int m = lane; m < C; m += 64) {
     float val;
-    if (m < i) val = (float)((double)s[m] - lse);
-    else if (m == i) val = 0.0f;
+    if (m < i) {
+      const float x = s[m];
+      if (act == SAS_GATE_SOFTMAX) val = (float)((double)x - lse);
+      else if (act == SAS_GATE_SIGMOID) val = x >= 0.0f ? -log1pf(expf(-x)) : x - log1pf(expf(x));
+      else val = x;
+    } else if (m == i) val = 0.0f;
     else val = -INFINITY;
     lrow[m] = val;
   }
@@ -146,23 +154,32 @@ __global__ void __launch_bounds__(256) threshold_kernel(const float* __restrict_
 
 // dscores[i, m] = dLogG[i, m] - g[i, m] * sum_{l < i} dLogG[i, l] for m < i, else 0.
 // This is App. D.3's ds_m = g_m (dg_m - sum_l g_l dg_l) with dLogG = g * dg,
-// and dg = 0 on unselected blocks (sparse scope, Eq. 8).
+// and dg = 0 on unselected blocks (sparse scope, Eq. 8).  Sigmoid gates
+// depend on their own score only: ds_m = g_m (1 - g_m) dg_m = (1 - g_m) dLogG_m;
+// raw logits: ds_m = dLogG_m.
 __global__ void __launch_bounds__(256) dscores_kernel(const float* __restrict__ dlg,
                                                       const float* __restrict__ lg,
                                                       float* __restrict__ ds, long long rows,
-                                                      int C) {
+                                                      int C, int act) {
   const int lane = threadIdx.x & 63;
   const long long row = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int i = (int)(row % C);
   const float* drow = dlg + row * (long long)C;
   const float* grow = lg + row * (long long)C;
-  float tot = 0.0f;
-  for (int m = lane; m < i; m += 64) tot += drow[m];
-  tot = wave_sum_f(tot);
   float* orow = ds + row * (long long)C;
-  for (int m = lane; m < C; m += 64)
-    orow[m] = (m < i) ? (drow[m] - expf(grow[m]) * tot) : 0.0f;
+  if (act == SAS_GATE_SOFTMAX) {
+    float tot = 0.0f;
+    for (int m = lane; m < i; m += 64) tot += drow[m];
+    tot = wave_sum_f(tot);
+    for (int m = lane; m < C; m += 64)
+      orow[m] = (m < i) ? (drow[m] - expf(grow[m]) * tot) : 0.0f;
+  } else if (act == SAS_GATE_SIGMOID) {
+    for (int m = lane; m < C; m += 64)
+      orow[m] = (m < i) ? drow[m] * (1.0f - expf(grow[m])) : 0.0f;
+  } else {
+    for (int m = lane; m < C; m += 64) orow[m] = (m < i) ? drow[m] : 0.0f;
+  }
 }
 
 }  // namespace
@@ -175,7 +192,7 @@ hipError_t launch_threshold(const Shape& s, const float* scores, float* log_gate
   const size_t lds = (size_t)nw * s.C * sizeof(float);
   const long long grid = (rows + nw - 1) / nw;
   hipLaunchKernelGGL(threshold_kernel, dim3((unsigned)grid), dim3(64 * nw), lds, st, scores,
-                     log_gate, tau, sel_idx, sel_cnt, d_status, rows, s.C, s.K, s.cap);
+                     log_gate, tau, sel_idx, sel_cnt, d_status, rows, s.C, s.K, s.cap, s.act);
   return hipGetLastError();
 }
 
@@ -184,7 +201,7 @@ hipError_t launch_dscores(const Shape& s, const float* dlog_gate, const float* l
   const long long rows = (long long)s.B * s.Hkv * s.C;
   const long long grid = (rows + 3) / 4;
   hipLaunchKernelGGL(dscores_kernel, dim3((unsigned)grid), dim3(256), 0, st, dlog_gate, log_gate,
-                     dscores, rows, s.C);
+                     dscores, rows, s.C, s.act);
   return hipGetLastError();
 }
 

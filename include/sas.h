@@ -58,12 +58,28 @@
 extern "C" {
 #endif
 
-#define SAS_ABI_VERSION 2
+#define SAS_ABI_VERSION 3
 
 typedef enum sas_dtype {
   SAS_BF16 = 0, /* q/k/v/o/d_o/dq/dk/dv are bfloat16 (fp32 accumulation) */
   SAS_FP32 = 1  /* all tensors float32 */
 } sas_dtype;
+
+/* Gate activation (Sec. 4.1 "Components of learnable ranking", Tab. 1):
+ * log g of a historical block from its selector score s.  The current block
+ * keeps g0 = 1 in every variant (Eq. 4). */
+typedef enum sas_gate_act {
+  SAS_GATE_SOFTMAX = 0, /* log g_m = s_m - LSE_{historical}(s)  (Eq. 6, default) */
+  SAS_GATE_SIGMOID = 1, /* log g_m = log sigmoid(s_m)          (Tab. 1 row 5)    */
+  SAS_GATE_RAW = 2      /* log g_m = s_m, raw logit injection   (Tab. 1 row 6)    */
+} sas_gate_act;
+
+/* Gate position (Sec. 4.1, Tab. 1 rows 2 and 3). */
+typedef enum sas_gate_pos {
+  SAS_GATE_INNER = 0, /* o = softmax(q K^T + log g) V            (Eq. 9, default) */
+  SAS_GATE_OUTER = 1  /* o = softmax(q K^T) (g . V): each block's value rows are
+                         scaled by its gate after the softmax                   */
+} sas_gate_pos;
 
 typedef enum sas_status {
   SAS_OK = 0,
@@ -90,6 +106,10 @@ typedef struct sas_problem {
                          product).  Must be SAS_FP32 when dtype is SAS_FP32.  */
   float sm_scale;     /* scale of q.k; <= 0 selects 1/sqrt(D).  It never
                          multiplies the log gate (App. E, Alg. 3/4).          */
+  int32_t gate_act;   /* a sas_gate_act (SAS_GATE_SOFTMAX for the method)      */
+  int32_t gate_pos;   /* a sas_gate_pos (SAS_GATE_INNER for the method).  The
+                         outer position runs on the vector-ALU path for every
+                         shape.                                                */
 } sas_problem;
 
 /* ABI version of the loaded library (SAS_ABI_VERSION). */
@@ -108,7 +128,8 @@ const char* sas_last_error(void);
  * Sec. 4.3 Alg. 1 (I = Top-K) and App. E (Top-K encoded as a per-query
  * threshold: a block is active when it reaches the threshold).
  *
- * For every row (b, h_kv, i):
+ * For every row (b, h_kv, i) (softmax activation; with SAS_GATE_SIGMOID the
+ * m < i entries are log sigmoid(s[i, m]), with SAS_GATE_RAW s[i, m] itself):
  *   log_gate[.., i, m] = s[i, m] - LSE_{m' < i} s[i, m']   for m < i,
  *                        0                                 for m = i,
  *                        -inf                              for m > i;
@@ -144,7 +165,10 @@ int32_t sas_gate_threshold(const sas_problem* p, const float* scores, float* log
  * (bias log_gate[i, m]):
  *   z_u = sm_scale * q_t . k_u + bias_u,  o_t = sum_u softmax(z)_u v_u,
  *   lse_t = log sum_u exp(z_u).
- * Unselected blocks are skipped entirely, never materialised.
+ * Unselected blocks are skipped entirely, never materialised.  With
+ * gate_pos = SAS_GATE_OUTER the logits carry no bias and the value rows of a
+ * selected block m are multiplied by g = exp(log_gate[i, m]) instead:
+ *   o_t = sum_u softmax(sm_scale q_t . k_u)_u g_{blk(u)} v_u  (lse ungated).
  *
  * Inputs : q, k, v (dtype), log_gate fp32 (only entries m in I_i are read),
  *          sel_idx / sel_cnt as written by sas_gate_threshold (the first
@@ -178,7 +202,11 @@ size_t sas_gated_attn_bwd_workspace_size(const sas_problem* p, int32_t sel_cap);
  * and, if dscores != NULL, the selector-score gradient of App. D.3 with the
  * sparse-scope rule of Eq. 8:
  *   dscores[i, m] = dlog_gate[i, m] - exp(log_gate[i, m]) * sum_{l<i} dlog_gate[i, l]
- *   for m < i; 0 for m >= i.
+ *   for m < i; 0 for m >= i (softmax activation; SAS_GATE_SIGMOID:
+ *   dlog_gate[i, m] * (1 - exp(log_gate[i, m])); SAS_GATE_RAW: dlog_gate[i, m]).
+ * With gate_pos = SAS_GATE_OUTER the value rows carry their gates: dP = dO
+ * (g . V)^T, dv = g . (P^T dO), and dlog_gate[i, m] = g_m dg_m = the sum of
+ * P * dP over the block (Eq. 5, outer form).
  *
  * Inputs : q, k, v, d_o (dtype), o (o_dtype), lse from the forward, log_gate (all
  *          entries m < i are read when dscores != NULL), sel_idx, sel_cnt.

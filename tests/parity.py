@@ -20,9 +20,11 @@ def log(msg):
     sys.stdout.flush()
 
 
-def problem_of(w: workloads.Workload, K: int, o_dtype: str = "bf16") -> api.Problem:
+def problem_of(w: workloads.Workload, K: int, o_dtype: str = "bf16", gate_act: str = "softmax",
+               gate_pos: str = "inner") -> api.Problem:
     return api.Problem(w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.block,
-                       K, w.dtype, 0.0, o_dtype if w.dtype == "bf16" else "fp32")
+                       K, w.dtype, 0.0, o_dtype if w.dtype == "bf16" else "fp32", gate_act,
+                       gate_pos)
 
 
 def run_gpu(p: api.Problem, inp: dict, cap=None, poison=True, status=None):
@@ -57,9 +59,9 @@ def f32(t: torch.Tensor) -> np.ndarray:
     return t.float().numpy()
 
 
-def check_selection(gpu, scores_np, K):
+def check_selection(gpu, scores_np, K, act="softmax"):
     """Selected sets, counts and thresholds must match the oracle exactly."""
-    lg, tau, sel = oracle.gate_threshold(scores_np, K)
+    lg, tau, sel = oracle.gate_threshold(scores_np, K, act=act)
     cnt = sel.sum(-1)
     assert np.array_equal(gpu["sel_cnt"].numpy(), cnt), "selection counts differ"
     assert np.array_equal(gpu["tau"].numpy(), tau), "thresholds differ"
@@ -104,17 +106,17 @@ def compare(name, got, ref, dtype, mask=None):
     assert rel_to_max <= rtol, f"{name}: max error {rel_to_max:.3e} of the tensor's max magnitude"
 
 
-def full_parity(w, K, inp=None, cap=None, o_dtype="bf16"):
+def full_parity(w, K, inp=None, cap=None, o_dtype="bf16", gate_act="softmax", gate_pos="inner"):
     """Whole-tensor parity of every output (sizes the oracle finishes quickly)."""
-    p = problem_of(w, K, o_dtype)
+    p = problem_of(w, K, o_dtype, gate_act, gate_pos)
     inp = inp or workloads.generate(w)
     gpu = run_gpu(p, inp, cap=cap)
     scores = inp["scores"].numpy()
-    lg, tau, sel = check_selection(gpu, scores, K)
+    lg, tau, sel = check_selection(gpu, scores, K, act=gate_act)
     q, k, v, do = (f32(inp[n]) for n in ("q", "k", "v", "do"))
-    o, lse = oracle.forward(q, k, v, lg, sel, w.block)
-    dq, dk, dv, dlg = oracle.backward(q, k, v, do, lg, sel, w.block)
-    dsc = oracle.dscores(dlg, lg, sel)
+    o, lse = oracle.forward(q, k, v, lg, sel, w.block, gate_pos=gate_pos)
+    dq, dk, dv, dlg = oracle.backward(q, k, v, do, lg, sel, w.block, gate_pos=gate_pos)
+    dsc = oracle.dscores(dlg, lg, sel, act=gate_act)
     dt = w.dtype
     compare("o", f32(gpu["o"]), o, dt)
     compare("lse", gpu["lse"].numpy(), lse, dt)

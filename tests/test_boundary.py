@@ -19,7 +19,8 @@ def lib():
 
 def prob(**kw):
     base = dict(batch=1, n_q_heads=8, n_kv_heads=2, seq_len=1024, head_dim=128, block_size=64,
-                budget_k=4, dtype=nat.SAS_BF16, o_dtype=nat.SAS_FP32, sm_scale=0.0)
+                budget_k=4, dtype=nat.SAS_BF16, o_dtype=nat.SAS_FP32, sm_scale=0.0, gate_act=0,
+                gate_pos=0)
     base.update(kw)
     return nat.SasProblem(**base)
 
@@ -58,8 +59,8 @@ def test_library_exports_every_header_symbol():
 
 
 def test_abi_version():
-    assert lib().sas_abi_version() == 2
-    assert api.abi_version() == 2
+    assert lib().sas_abi_version() == 3
+    assert api.abi_version() == 3
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -70,6 +71,8 @@ def test_abi_version():
     (dict(o_dtype=3), nat.SAS_E_INVALID),
     (dict(dtype=nat.SAS_FP32, o_dtype=nat.SAS_BF16), nat.SAS_E_INVALID),
     (dict(sm_scale=float("nan")), nat.SAS_E_INVALID),
+    (dict(gate_act=3), nat.SAS_E_INVALID),
+    (dict(gate_pos=2), nat.SAS_E_INVALID),
     (dict(head_dim=96), nat.SAS_E_UNSUPPORTED),
     (dict(block_size=128, seq_len=1024), nat.SAS_E_UNSUPPORTED),
     (dict(seq_len=1000), nat.SAS_E_UNSUPPORTED),          # ragged last block

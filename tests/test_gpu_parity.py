@@ -62,6 +62,28 @@ def test_small_shapes_full_parity(case):
     full_parity(w, K, cap=cap, o_dtype=o_dtype)
 
 
+VARIANTS = [
+    # name, B, Hq, Hkv, N, D, blk, K, dtype, gate_act, gate_pos
+    ("mfma_sigmoid", 1, 8, 2, 1024, 128, 64, 4, "bf16", "sigmoid", "inner"),
+    ("mfma_raw", 1, 8, 2, 768, 128, 64, 3, "bf16", "raw", "inner"),
+    ("outer_bf16_d128_b64", 1, 8, 2, 512, 128, 64, 3, "bf16", "softmax", "outer"),
+    ("outer_sigmoid_fp32_d64_b16", 1, 4, 2, 256, 64, 16, 3, "fp32", "sigmoid", "outer"),
+    ("generic_raw_fp32_d64_b32", 1, 2, 1, 256, 64, 32, 2, "fp32", "raw", "inner"),
+    ("outer_full_scope", 1, 4, 1, 384, 128, 64, 100, "bf16", "softmax", "outer"),
+]
+
+
+@pytest.mark.parametrize("case", VARIANTS, ids=[c[0] for c in VARIANTS])
+def test_gate_variants_full_parity(case):
+    """The ablated gate variants of the pages' Tab. 1 (activation, position)."""
+    name, B, Hq, Hkv, N, D, blk, K, dt, act, pos = case
+    log(f"variant {name}")
+    w = workloads.custom(B, Hq, Hkv, N, D, blk, K, dtype=dt, seed=zlib.crc32(name.encode()) % 1000,
+                         score_std=2.0)
+    cap = max(1, min(K, N // blk - 1))
+    full_parity(w, K, cap=cap, gate_act=act, gate_pos=pos)
+
+
 def test_tiny_fp32_workload():
     w = workloads.WORKLOADS["tiny_fp32"]
     log("workload tiny_fp32")
