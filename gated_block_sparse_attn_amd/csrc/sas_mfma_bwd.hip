@@ -23,9 +23,10 @@
 //                       gets the ascending list {j} u {i > j : j in I_i} and is
 //                       cut into chunks of at most kColChunk query blocks,
 //                       ordered for L2 reuse.
-//   bwd_dkdv_kernel     key-major pass: one wavefront pair per column chunk
-//                       (key block j); K_j / V_j are resident MFMA operands,
-//                       the (query block, head) rows stream through LDS rings;
+//   bwd_dkdv_kernel     key-major pass: four wavefronts (two pairs, one per
+//                       half of key block j) per column chunk; K_j / V_j are
+//                       resident MFMA operands, the (query block, head) rows
+//                       stream through LDS rings;
 //                       it recomputes S and dP, accumulates dV^T += dO^T P and
 //                       dK^T += Q^T dS, and writes dLogG[i, j] of each
 //                       selecting query block i (sum of its dS).
@@ -529,29 +530,8 @@ __global__ void chunk_scatter_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// key-major pass: dK, dV
+// key-major pass: dK, dV and the block log-gate gradient
 // ---------------------------------------------------------------------------
-// One workgroup = one wavefront pair = one column chunk (key block j, up to
-// kColChunk query blocks).  The pair streams the chunk's (query block, head)
-// items in steps of 32 query rows (n steps) and splits the work by tensor:
-//   wave A (role 0): S = Q K^T -> P, and dV^T += dO^T P   (K_j in registers)
-//   wave B (role 1): dP = dO V^T -> dS = P (dP - Delta), dK^T += Q^T dS
-//                    (V_j in registers)
-// Every product is a 32x32x16 MFMA, which a single wavefront issues at the
-// full matrix rate; one wavefront runs per SIMD (about 400 registers).
-//
-// Software pipeline (window s lies between the pair's barriers s - 1 and s):
-//   A: S_{s+1} (matrix core) overlapped with P_s = exp(S_s ...) (vector ALU),
-//      then dV_s += dO_s^T P_s;  P_s is published (fp16) at barrier s.
-//   B: dP_s (matrix core) overlapped with dS_{s-1} (vector ALU), then
-//      dK_{s-1} += Q_{s-1}^T dS_{s-1}.
-// The rows of each step reach LDS by asynchronous global -> LDS copies into
-// two rings: A copies Q rows and Delta into a 5-slot ring (step t is read in
-// windows t - 1 .. t + 1), B copies dO rows and LSE into a 3-slot ring (read
-// in window t).  Both copies are issued two windows before they are first
-// read; every wavefront waits for its own copies before the barrier that
-// publishes them.
-//
 // 32x32x16 operand layouts (lane l, g = l / 32):
 //   A: row l % 32, k = 8 g .. 8 g + 7;   B: column l % 32, same k;
 //   C: column l % 32, rows 8 (jj / 4) + 4 g + jj % 4 for jj = 0..15.
@@ -566,11 +546,6 @@ constexpr int SLOT_BYTES = XS_BYTES + 256;           // rows + one statistic (64
 constexpr int Q_SLOTS = 5, O_SLOTS = 3;
 constexpr int QRING = 0;
 constexpr int ORING = QRING + Q_SLOTS * SLOT_BYTES;
-constexpr int PX_BYTES = 64 * 32 * 2;                // P of one step (fp16)
-constexpr int PBUF = ORING + O_SLOTS * SLOT_BYTES;
-constexpr int ITAB = PBUF + 2 * PX_BYTES;
-constexpr int KV_LDS = ITAB + 2 * kColChunk * 4;
-static_assert(2 * KV_LDS <= 160 * 1024, "two workgroups per CU");
 
 // Keeps the computation of x at this point of the instruction stream: the
 // vector-ALU work that is meant to overlap a matrix instruction would
@@ -582,27 +557,62 @@ __device__ __forceinline__ void pin(T& x) { __asm__ volatile("" : "+v"(x)); }
 // (slot16 swizzle).
 __device__ __forceinline__ int xsw(int r, int c) { return r * HD + ((c ^ slot16(r)) << 3); }
 
-// Pair barrier: this wavefront's LDS accesses and all but its newest nine
+
+// One workgroup = four wavefronts = one column chunk (key block j, up to
+// kColChunk query blocks), streamed in steps of 32 query rows of one head
+// (n steps: entry e, head h, half x -> step 2 (e G + h) + x).  Pair kh (waves
+// 2 kh, 2 kh + 1) owns keys kh*32 .. kh*32 + 31 of the block and splits the
+// work by tensor:
+//   wave A (role 0): S = Q K^T -> P, and dV^T += dO^T P   (its K rows resident)
+//   wave B (role 1): dP = dO V^T -> dS = P (dP - Delta), dK^T += Q^T dS
+//                    (its V rows resident)
+// Each wavefront holds 32 keys (about 225 registers), so two run per SIMD and
+// one's vector work overlaps the other's matrix instructions; every product
+// is a 32x32x16 MFMA.
+//
+// Software pipeline (window s lies between barriers s - 1 and s):
+//   A: S_{s+1} (matrix core) overlapped with P_s = exp(S_s ...) (vector ALU),
+//      then dV_s += dO_s^T P_s;  P_s is published (fp16) at barrier s.
+//   B: dP_s (matrix core) overlapped with dS_{s-1} (vector ALU), then
+//      dK_{s-1} += Q_{s-1}^T dS_{s-1}.
+// A step's rows reach LDS by asynchronous global -> LDS copies into two rings
+// shared by the pairs: the A waves copy the Q rows (half each) and Delta into
+// a 5-slot ring (step t is read in windows t - 1 .. t + 1), the B waves the dO
+// rows and LSE into a 3-slot ring (read in window t), two windows before
+// first use, spread between the contraction's MFMAs; every wavefront waits for
+// its own copies before the barrier that publishes them.  The Q / dO operand
+// fragments are read two MFMAs ahead.  B's per-entry dS sums of the two key
+// halves meet in LDS and are added in a fixed order after the loops
+// (deterministic).
+constexpr int PX4_BYTES = 32 * 32 * 2;                       // P of one step, one key half (fp16)
+constexpr int PBUF4 = ORING + O_SLOTS * SLOT_BYTES;
+constexpr int ITAB4 = PBUF4 + 2 * 2 * PX4_BYTES;             // [key half][step parity]
+constexpr int GTAB4 = ITAB4 + 2 * kColChunk * 4;             // itab + btab
+constexpr int KV4_LDS = GTAB4 + 2 * kColChunk * 4;           // dLogG partials [key half][entry]
+static_assert(2 * KV4_LDS <= 160 * 1024, "two workgroups per CU");
+
+// Ring barrier: this wavefront's LDS accesses and all but its newest five
 // global -> LDS copies are complete, then s_barrier.  (__syncthreads would
 // also wait for the newest copies, which are meant to stay in flight.)
-__device__ __forceinline__ void ring_barrier() {
-  __asm__ volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+__device__ __forceinline__ void ring_barrier5() {
+  __asm__ volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[KV_LDS];
-  int32_t* itab = (int32_t*)(smem + ITAB);   // query block of each chunk entry
-  float* btab = (float*)(itab + kColChunk);  // its log gate (log2 units; 0 on the diagonal)
+  __shared__ __attribute__((aligned(16))) char smem[KV4_LDS];
+  int32_t* itab = (int32_t*)(smem + ITAB4);   // query block of each chunk entry
+  float* btab = (float*)(itab + kColChunk);   // its log gate (log2 units; 0 on the diagonal)
+  float* gtab = (float*)(smem + GTAB4);       // [key half][entry] dS sums
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int role = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0: S / P / dV, 1: dP / dS / dK (wave-uniform)
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int role = wv & 1;   // 0: S / P / dV, 1: dP / dS / dK (wave-uniform)
+  const int kh = wv >> 1;    // key half
   const int g = lane >> 5;
   const int l32 = lane & 31;
 
-  // the grid is sized for the most chunks a selection can produce; the first
-  // `total` workgroups take the chunks, spread evenly over the XCDs
   const int total = a.chunkoff[a.ncol];
   if ((int)blockIdx.x >= total) return;
   const int gch = a.chunk_order[xcd_remap(blockIdx.x, total)];
@@ -618,55 +628,42 @@ bwd_dkdv_kernel(BwdArgs a) {
   const int bb = (int)(bhk / a.Hkv);
   const int G = a.G;
 
-  // per chunk entry e (lane e): its query block and log gate (LDS), and the
-  // element offset of row 0 of (batch, first head of the kv group, block)
   long long rowbase = 0;
   if (lane < ne) {
     const int i = a.collist[a.coloff[col] + e0 + lane];
-    if (role == 0) {
+    if (wv == 0) {
       itab[lane] = i;
       btab[lane] = i == j ? 0.0f : a.lg[(bhk * a.C + i) * a.C + j] * kLog2e;
     }
     rowbase = ((long long)bb * a.Hq + hk * G) * a.N + (long long)i * BLK;
   }
 
-  // resident B operand of S (A: K_j) or dP (B: V_j): key kt*32 + l32,
+  // resident B operand of S (A: K_j) or dP (B: V_j): key kh*32 + l32,
   // dims ds*16 + g*8 .. +7
-  bf16x8 kf[2][8];
+  bf16x8 kf[8];
   {
-    const bf16* t = (role == 0 ? a.k : a.v) + (bhk * a.N + (long long)j * BLK) * HD;
+    const bf16* t = (role == 0 ? a.k : a.v) + (bhk * a.N + (long long)j * BLK + kh * 32 + l32) * HD;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int ds = 0; ds < 8; ++ds) kf[ds] = *(const bf16x8*)(t + ds * 16 + g * 8);
 #pragma unroll
-      for (int ds = 0; ds < 8; ++ds)
-        kf[kt][ds] = *(const bf16x8*)(t + (kt * 32 + l32) * HD + ds * 16 + g * 8);
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int ds = 0; ds < 8; ++ds) settle(kf[kt][ds]);   // complete before the loop
+    for (int ds = 0; ds < 8; ++ds) settle(kf[ds]);
   }
   __syncthreads();   // item table
 
-  const int n = 2 * ne * G;   // steps (even): entry e, head h, half x -> step 2 (e G + h) + x
-  // Copy stream: step t's rows (32 x 128) and statistic go to slot t mod
-  // nslots of this wavefront's ring (A: Q and Delta, B: dO and LSE).  Steps
-  // past the end recopy the last step into their (free, never read) slot.
+  const int n = 2 * ne * G;   // steps: entry e, head h, half x -> step 2 (e G + h) + x
   const int nslots = role == 0 ? Q_SLOTS : O_SLOTS;
   char* const ring = smem + (role == 0 ? QRING : ORING);
   const bf16* src = role == 0 ? a.q : a.d_o;
   const float* stat = role == 0 ? a.delta : a.lse;
-  unsigned voff[8];   // byte offset of this lane's 16 bytes in copy q (rows 4q .. 4q + 3)
+  unsigned voff[4];   // this lane's 16 bytes of copy q: rows (kh*4 + q)*4 .. +3
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int row = q * 4 + (lane >> 4);
+  for (int q = 0; q < 4; ++q) {
+    const int row = (kh * 4 + q) * 4 + (lane >> 4);
     voff[q] = (unsigned)(row * HD + (((lane & 15) ^ slot16(row)) << 3)) * 2;
   }
   const unsigned soff = (unsigned)l32 * 4;
-  int ct = 0, ce = 0, chh = 0, cx = 0, cslot = 0;   // next step to copy: (entry, head, half, slot)
+  int ct = 0, ce = 0, chh = 0, cx = 0, cslot = 0;
   const unsigned ring_lds = lds_addr(ring);
-  // one step's copies: prepare() fixes the sources and the slot, then
-  // issue(q) sends rows 4q .. 4q + 3 (q < 8) or the statistic (q = 8), so the
-  // nine copies can be spread between matrix instructions
   struct Copy { const bf16* rows; const float* st; unsigned lds; };
   auto prepare = [&]() -> Copy {
     const long long rbase = (long long)(unsigned)__builtin_amdgcn_readlane((int)rowbase, ce) |
@@ -674,35 +671,32 @@ bwd_dkdv_kernel(BwdArgs a) {
     const long long r0 = rbase + (long long)(unsigned)(chh * a.N + cx * 32);
     Copy cp{src + r0 * HD, stat + r0, ring_lds + (unsigned)(cslot * SLOT_BYTES)};
     cslot = cslot + 1 == nslots ? 0 : cslot + 1;
-    if (++ct < n) {   // advance (entry, head, half); past the end it stays on the last step
+    if (++ct < n) {
       cx ^= 1;
       if (cx == 0 && ++chh == G) { chh = 0; ++ce; }
     }
     return cp;
   };
+  // five copies per step and wave: four 1 KB row groups, and the statistic
   auto issue = [&](const Copy& cp, int q) {
-    if (q < 8) dma16s(cp.rows, voff[q], cp.lds + q * 1024);
+    if (q < 4) dma16s(cp.rows, voff[q], cp.lds + (kh * 4 + q) * 1024);
     else dma4s(cp.st, soff, cp.lds + XS_BYTES);
   };
   auto copy_next = [&]() {
     const Copy cp = prepare();
 #pragma unroll
-    for (int q = 0; q < 9; ++q) issue(cp, q);
+    for (int q = 0; q < 5; ++q) issue(cp, q);
   };
   auto qring = [&](int k) -> char* { return smem + QRING + k * SLOT_BYTES; };
   auto oring = [&](int k) -> char* { return smem + ORING + k * SLOT_BYTES; };
   auto inc = [](int k, int m) { return k + 1 == m ? 0 : k + 1; };
 
-  f32x16 acc[4][2];   // A: dV^T, B: dK^T; lane: key kt*32 + l32, dims dt*32 + 8 (jj/4) + 4 g + jj%4
+  f32x16 acc[4];   // A: dV^T, B: dK^T; lane: key kh*32 + l32, dims dt*32 + 8 (jj/4) + 4 g + jj%4
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) acc[dt][kt][x] = 0.0f;
+    for (int x = 0; x < 16; ++x) acc[dt][x] = 0.0f;
 
-  // transposed-read addresses (element offsets inside a staged tile): head-dim
-  // tile dt, rows tr_r + 8 h (sl = 0)
   const int u = lane & 15;
   const int dhalf = (lane >> 4) & 1;
   const int tr_r = g * 4 + (u >> 2);
@@ -711,29 +705,25 @@ bwd_dkdv_kernel(BwdArgs a) {
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int h = 0; h < 2; ++h) tro[dt][h] = xsw(tr_r + 8 * h, dt * 4 + dhalf * 2 + ((u >> 1) & 1)) + (u & 1) * 4;
-  auto read_tr = [&](const char* rows, bf16x8 (&ta)[4][2]) {
+  auto tr_frag = [&](const char* rows, int dt, int sl) -> bf16x8 {
     const bf16* xs = (const bf16*)rows;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int sl = 0; sl < 2; ++sl)
-        ta[dt][sl] = join(ds_read_tr(xs + tro[dt][0] + sl * 16 * HD), ds_read_tr(xs + tro[dt][1] + sl * 16 * HD));
+    return join(ds_read_tr(xs + tro[dt][0] + sl * 16 * HD), ds_read_tr(xs + tro[dt][1] + sl * 16 * HD));
   };
-  // row contraction into the dV^T / dK^T accumulators; after MFMA m the
-  // work `per_mfma(m)` is issued (sched_barrier keeps the interleave)
-  auto contract = [&](const bf16x8 (&ta)[4][2], const bf16x8 (&bop)[2][2], auto&& per_mfma) {
+  // row contraction into the accumulators (8 MFMAs); the transposed
+  // fragments are read two MFMAs ahead; after MFMA m the work per_mfma(m)
+  auto contract = [&](const char* rows, const bf16x8 (&bop)[2], auto&& per_mfma) {
+    bf16x8 ta[2];
+    ta[0] = tr_frag(rows, 0, 0);
+    ta[1] = tr_frag(rows, 0, 1);
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int sl = 0; sl < 2; ++sl)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          acc[dt][kt] = mfma32(ta[dt][sl], bop[kt][sl], acc[dt][kt]);
-          per_mfma((dt * 2 + sl) * 2 + kt);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+    for (int m = 0; m < 8; ++m) {
+      const int dt = m >> 1, sl = m & 1;
+      acc[dt] = mfma32(ta[m & 1], bop[sl], acc[dt]);
+      if (m + 2 < 8) ta[m & 1] = tr_frag(rows, (m + 2) >> 1, (m + 2) & 1);
+      per_mfma(m);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
-  // this lane's 16 C-row statistics (rows 8t + 4g + u) of a slot
   auto read_stat = [&](const char* sl, float (&st)[16]) {
     const float* sp = (const float*)(sl + XS_BYTES);
 #pragma unroll
@@ -743,146 +733,115 @@ bwd_dkdv_kernel(BwdArgs a) {
       for (int y = 0; y < 4; ++y) st[t * 4 + y] = v[y];
     }
   };
-  auto pbuf = [&](int t) -> _Float16* { return (_Float16*)(smem + PBUF + (t & 1) * PX_BYTES); };
-  // S (A) or dP (B) of the rows in slot sl into `out`, one MFMA at a time;
-  // after MFMA m (m = 0..15) the vector-ALU work `per_mfma(m)` of the
-  // previous step is issued, so the two overlap in the instruction stream
-  // (sched_barrier keeps the scheduler from regrouping them).
-  auto read_rows = [&](const char* sl, bf16x8 (&qa)[8]) {
+  auto pbuf = [&](int t) -> _Float16* { return (_Float16*)(smem + PBUF4 + (kh * 2 + (t & 1)) * PX4_BYTES); };
+  // S (A) or dP (B) of the rows in slot sl: 8 MFMAs, row fragments read two
+  // ahead; after MFMA m the vector work per_mfma(m) of the previous step
+  auto rows_product_with = [&](const char* sl, f32x16& out, auto&& per_mfma) {
     const bf16* xs = (const bf16*)sl;
+    bf16x8 qa[2];
+    qa[0] = *(const bf16x8*)(xs + xsw(l32, 0 * 2 + g));
+    qa[1] = *(const bf16x8*)(xs + xsw(l32, 1 * 2 + g));
 #pragma unroll
-    for (int ds = 0; ds < 8; ++ds) qa[ds] = *(const bf16x8*)(xs + xsw(l32, ds * 2 + g));
-  };
-  auto rows_product_with = [&](const bf16x8 (&qa)[8], f32x16 (&out)[2], auto&& per_mfma) {
+    for (int x = 0; x < 16; ++x) out[x] = 0.0f;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) out[kt][x] = 0.0f;
-#pragma unroll
-    for (int ds = 0; ds < 8; ++ds)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        out[kt] = mfma32(qa[ds], kf[kt][ds], out[kt]);
-        per_mfma(ds * 2 + kt);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int ds = 0; ds < 8; ++ds) {
+      out = mfma32(qa[ds & 1], kf[ds], out);
+      if (ds + 2 < 8) qa[ds & 1] = *(const bf16x8*)(xs + xsw(l32, (ds + 2) * 2 + g));
+      per_mfma(ds);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
-  // A, window s: S_{s+1} (rows in qn) interleaved with
-  // P_s = exp2(c2 S_s + beta - lse) (LSE and dO_s in os), then dV_s += dO_s^T P_s.
-  // P_s also goes to LDS (fp16) for B.  HALF: the step's half of its query block.
+  // A, window s: S_{s+1} (rows in qn) interleaved with P_s = exp2(c2 S_s +
+  // beta - lse) (LSE in os), then dV_s += dO_s^T P_s; P_s also goes to LDS
+  // (fp16) for B.  HALF: the step's half of its query block.
+  const int key = kh * 32 + l32;
   auto window_a = [&](auto diag_tag, auto half_tag, const char* qn, const char* os, _Float16* px,
-                      float beta, const f32x16 (&sprev)[2], f32x16 (&snext)[2]) {
+                      float beta, const f32x16& sprev, f32x16& snext) {
     constexpr bool DIAG = decltype(diag_tag)::value;
     constexpr int hrow = decltype(half_tag)::value * 32;
-    bf16x8 qa[8];
-    read_rows(qn, qa);   // Q of step s + 1
     float nl[16];
-    read_stat(os, nl);   // LSE_s
+    read_stat(os, nl);
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) nl[jj] = fmaf(-nl[jj], kLog2e, beta);
-    bf16x8 bop[2][2];
-    f16x8 ph[2][2];
-    // MFMA m of S_{s+1} is followed by elements 2m, 2m + 1 of P_s (packed to
-    // bf16 for dV and to fp16 for B)
-    rows_product_with(qa, snext, [&](int m) {
-      const int kt = m >> 3;
+    bf16x8 bop[2];
+    f16x8 ph[2];
+    rows_product_with(qn, snext, [&](int m) {
       float e2[2];
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
-        const int jj = (m & 7) * 2 + x;
-        float e = __builtin_amdgcn_exp2f(fmaf(sprev[kt][jj], a.c2, nl[jj]));
-        if (DIAG && kt * 32 + l32 > hrow + (jj >> 2) * 8 + g * 4 + (jj & 3)) e = 0.0f;
+        const int jj = m * 2 + x;
+        float e = __builtin_amdgcn_exp2f(fmaf(sprev[jj], a.c2, nl[jj]));
+        if (DIAG && key > hrow + (jj >> 2) * 8 + g * 4 + (jj & 3)) e = 0.0f;
         e2[x] = e;
       }
-      const int h2 = (m >> 2) & 1, x0 = (m & 3) * 2;
+      const int h2 = m >> 2, x0 = (m & 3) * 2;
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
-        bop[kt][h2][x0 + x] = (bf16)e2[x];
-        ph[kt][h2][x0 + x] = (_Float16)e2[x];
+        bop[h2][x0 + x] = (bf16)e2[x];
+        ph[h2][x0 + x] = (_Float16)e2[x];
       }
-      pin(bop[kt][h2]);
-      pin(ph[kt][h2]);
+      pin(bop[h2]);
+      pin(ph[h2]);
     });
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) *(f16x8*)(px + ((kt * 2 + h2) * 64 + lane) * 8) = ph[kt][h2];
-    bf16x8 ta[4][2];
-    read_tr(os, ta);   // dO_s^T
+    for (int h2 = 0; h2 < 2; ++h2) *(f16x8*)(px + (h2 * 64 + lane) * 8) = ph[h2];
     const Copy cp = prepare();
-    contract(ta, bop, [&](int m) { if (m < 9) issue(cp, m); });   // dV_s, this window's copies
+    contract(os, bop, [&](int m) { if (m < 5) issue(cp, m); });   // dV_s, this window's copies
   };
-  // B: dS = P (dP - Delta) of a step (Delta and Q rows in qs, P in px) as the
-  // bf16 B operand, element pair m after MFMA m of the next dP, then
-  // dK += Q^T dS.  gsum collects the step's dS for the block log-gate gradient.
-  // (fma with a zero addend and an fp16 operand maps to one mixed-precision
-  // fma, with no separate fp16 -> fp32 conversion.)
-  auto window_b = [&](const char* on, const char* qs, const _Float16* px,
-                      const f32x16 (&dprev)[2], f32x16 (&dcur)[2], float& gsum) {
-    bf16x8 qa[8];
-    read_rows(on, qa);   // dO of step s
+  // B: dS = P (dP - Delta) of the previous step (Delta and Q rows in qs, P
+  // in px) as the bf16 B operand, element pair m after MFMA m of the next
+  // dP, then dK += Q^T dS.  gsum collects the step's dS (fma with a zero
+  // addend and the fp16 operand: one mixed-precision fma).
+  auto window_b = [&](const char* on, const char* qs, const _Float16* px, const f32x16& dprev,
+                      f32x16& dcur, float& gsum) {
     float dl[16];
-    read_stat(qs, dl);   // Delta of the previous step
-    f16x8 ph[2][2];
+    read_stat(qs, dl);
+    f16x8 ph[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) ph[kt][h2] = *(const f16x8*)(px + ((kt * 2 + h2) * 64 + lane) * 8);
-    bf16x8 bop[2][2];
-    rows_product_with(qa, dcur, [&](int m) {
-      const int kt = m >> 3;
+    for (int h2 = 0; h2 < 2; ++h2) ph[h2] = *(const f16x8*)(px + (h2 * 64 + lane) * 8);
+    bf16x8 bop[2];
+    rows_product_with(on, dcur, [&](int m) {
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
-        const int jj = (m & 7) * 2 + x;
-        const float ds = fmaf((float)ph[kt][jj >> 3][jj & 7], dprev[kt][jj] - dl[jj], 0.0f);
+        const int jj = m * 2 + x;
+        const float ds = fmaf((float)ph[jj >> 3][jj & 7], dprev[jj] - dl[jj], 0.0f);
         gsum += ds;
-        bop[kt][jj >> 3][jj & 7] = (bf16)ds;
+        bop[jj >> 3][jj & 7] = (bf16)ds;
       }
-      pin(bop[kt][(m >> 2) & 1]);
+      pin(bop[m >> 2]);
     });
-    bf16x8 ta[4][2];
-    read_tr(qs, ta);   // Q^T of the previous step
     const Copy cp = prepare();
-    contract(ta, bop, [&](int m) { if (m < 9) issue(cp, m); });   // dK, this window's copies
+    contract(qs, bop, [&](int m) { if (m < 5) issue(cp, m); });   // dK, this window's copies
   };
 
-  // Each wavefront runs its own loop of n windows, one pair barrier per
-  // window (P_s published; A's Q of step s + 2 and B's dO of step s + 1 landed).
-  f32x16 r0[2], r1[2];   // A: S of the current / next step; B: dP of the previous / current step
+  f32x16 r0, r1;
   if (role == 0) {
     copy_next();
     copy_next();
     copy_next();
-    ring_barrier();   // Q of steps 0, 1 landed
-    {
-      bf16x8 qa[8];
-      read_rows(qring(0), qa);
-      rows_product_with(qa, r0, [](int) {});   // S_0
-    }
-    // window s reads Q of step s + 1 (ring slot qk) and dO / LSE of step s
-    // (slot ok); the diagonal block, when in this chunk, is its first entry
-    // (2G steps, gate 0)
+    ring_barrier5();   // Q of steps 0, 1 landed
+    rows_product_with(qring(0), r0, [](int) {});   // S_0
     int qk = 1, ok = 0;
     const int nd = itab[0] == j ? 2 * G : 0;
 #pragma unroll 1
     for (int s = 0; s < nd; s += 2) {
       window_a(std::true_type{}, std::integral_constant<int, 0>{}, qring(qk), oring(ok), pbuf(0), 0.0f, r0, r1);
-      ring_barrier();
+      ring_barrier5();
       qk = inc(qk, Q_SLOTS); ok = inc(ok, O_SLOTS);
       window_a(std::true_type{}, std::integral_constant<int, 1>{}, qring(qk), oring(ok), pbuf(1), 0.0f, r1, r0);
-      ring_barrier();
+      ring_barrier5();
       qk = inc(qk, Q_SLOTS); ok = inc(ok, O_SLOTS);
     }
-    int ent = nd ? 1 : 0, hh = 0;   // entry and head of the window pair
+    int ent = nd ? 1 : 0, hh = 0;
     float beta = btab[ent < ne ? ent : 0];
 #pragma unroll 1
-    for (int s = nd; s < n; s += 2) {   // n, nd even
+    for (int s = nd; s < n; s += 2) {
       window_a(std::false_type{}, std::integral_constant<int, 0>{}, qring(qk), oring(ok), pbuf(0), beta, r0, r1);
-      ring_barrier();
+      ring_barrier5();
       qk = inc(qk, Q_SLOTS); ok = inc(ok, O_SLOTS);
       window_a(std::false_type{}, std::integral_constant<int, 1>{}, qring(qk), oring(ok), pbuf(1), beta, r1, r0);
-      ring_barrier();
+      ring_barrier5();
       qk = inc(qk, Q_SLOTS); ok = inc(ok, O_SLOTS);
       if (++hh == G) {
         hh = 0;
@@ -891,8 +850,6 @@ bwd_dkdv_kernel(BwdArgs a) {
       }
     }
   } else {
-    // dLogG[i, j] of entry e (query block i = itab[e] != j) = sum of dS over
-    // its 2G steps (G heads x 64 rows) and the 64 keys; fixed summation order
     float gsum = 0.0f;
     int gstep = 0, gent = 0;
     auto step_done = [&]() {
@@ -900,92 +857,86 @@ bwd_dkdv_kernel(BwdArgs a) {
       const float tot = wave_sum(gsum);
       gsum = 0.0f;
       gstep = 0;
-      const int ib = itab[gent];
-      if (lane == 0 && ib != j) a.dlg[(bhk * a.C + ib) * a.C + j] = tot;
+      if (lane == 0) gtab[kh * kColChunk + gent] = tot;
       ++gent;
     };
     copy_next();
     copy_next();
-    ring_barrier();   // dO of step 0 landed
+    ring_barrier5();   // dO of step 0 landed
     {
-      bf16x8 qa[8];
-      read_rows(oring(0), qa);
+      const char* o0 = oring(0);
       copy_next();
-      rows_product_with(qa, r0, [](int) {});   // dP_0
+      rows_product_with(o0, r0, [](int) {});   // dP_0
     }
-    ring_barrier();
-    // window s (>= 1) reads dO of step s (slot ok), and Delta / Q of step s - 1 (slot qk)
+    ring_barrier5();
     int ok = 1, qk = 0;
     int s = 1;
 #pragma unroll 1
     for (; s + 1 < n; s += 2) {
       window_b(oring(ok), qring(qk), pbuf(0), r0, r1, gsum);   // step s - 1 is even
-      ring_barrier();
+      ring_barrier5();
       step_done();
       ok = inc(ok, O_SLOTS); qk = inc(qk, Q_SLOTS);
       window_b(oring(ok), qring(qk), pbuf(1), r1, r0, gsum);
-      ring_barrier();
+      ring_barrier5();
       step_done();
       ok = inc(ok, O_SLOTS); qk = inc(qk, Q_SLOTS);
     }
-    // window n - 1: dP_{n-1} -> r1, dS / dK of step n - 2
-    window_b(oring(ok), qring(qk), pbuf(0), r0, r1, gsum);
-    ring_barrier();
+    window_b(oring(ok), qring(qk), pbuf(0), r0, r1, gsum);   // dP_{n-1}; dS / dK of step n - 2
+    ring_barrier5();
     step_done();
     qk = inc(qk, Q_SLOTS);
-    // dS and dK of the last step (odd)
-    bf16x8 bop[2][2];
+    bf16x8 bop[2];
     {
       float dl[16];
       read_stat(qring(qk), dl);
       const _Float16* px = pbuf(1);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const f16x8 ph = *(const f16x8*)(px + (h2 * 64 + lane) * 8);
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const f16x8 ph = *(const f16x8*)(px + ((kt * 2 + h2) * 64 + lane) * 8);
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const float ds = fmaf((float)ph[x], r1[kt][h2 * 8 + x] - dl[h2 * 8 + x], 0.0f);
-            gsum += ds;
-            bop[kt][h2][x] = (bf16)ds;
-          }
+        for (int x = 0; x < 8; ++x) {
+          const float ds = fmaf((float)ph[x], r1[h2 * 8 + x] - dl[h2 * 8 + x], 0.0f);
+          gsum += ds;
+          bop[h2][x] = (bf16)ds;
         }
+      }
     }
     step_done();
-    bf16x8 ta[4][2];
-    read_tr(qring(qk), ta);
-    contract(ta, bop, [](int) {});
+    contract(qring(qk), bop, [](int) {});
   }
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the trailing copies
+  __syncthreads();   // dLogG partials of both key halves are in gtab
 
-  // epilogue: A writes dV, B writes dK (times the softmax scale)
-  const long long orow = bhk * a.N + (long long)j * BLK;
+  // dLogG[i, j] of every entry with i != j (key halves added in order)
+  if (wv == 1 && lane < ne) {
+    const int ib = itab[lane];
+    if (ib != j) a.dlg[(bhk * a.C + ib) * a.C + j] = gtab[lane] + gtab[kColChunk + lane];
+  }
+
+  // epilogue: A writes dV, B writes dK (times the softmax scale), keys kh*32 + l32
+  const long long orow = bhk * a.N + (long long)j * BLK + kh * 32;
   const float mul = role == 0 ? 1.0f : a.scale;
   if (nch == 1) {
     bf16* dst = role == 0 ? a.dv : a.dk;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 o;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          bf16x4 o;
-#pragma unroll
-          for (int y = 0; y < 4; ++y) o[y] = (bf16)(acc[dt][kt][q4 * 4 + y] * mul);
-          *(bf16x4*)(dst + (orow + kt * 32 + l32) * HD + dt * 32 + q4 * 8 + g * 4) = o;
-        }
+        for (int y = 0; y < 4; ++y) o[y] = (bf16)(acc[dt][q4 * 4 + y] * mul);
+        *(bf16x4*)(dst + (orow + l32) * HD + dt * 32 + q4 * 8 + g * 4) = o;
+      }
   } else {
-    float* dst = a.partial + (long long)gch * 2 * 8192 + (role == 0 ? 8192 : 0);
+    float* dst = a.partial + (long long)gch * 2 * 8192 + (role == 0 ? 8192 : 0) + kh * 32 * HD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *(f32x4*)(dst + (kt * 32 + l32) * HD + dt * 32 + q4 * 8 + g * 4) =
-              f32x4{acc[dt][kt][q4 * 4] * mul, acc[dt][kt][q4 * 4 + 1] * mul,
-                    acc[dt][kt][q4 * 4 + 2] * mul, acc[dt][kt][q4 * 4 + 3] * mul};
+      for (int q4 = 0; q4 < 4; ++q4)
+        *(f32x4*)(dst + l32 * HD + dt * 32 + q4 * 8 + g * 4) =
+            f32x4{acc[dt][q4 * 4] * mul, acc[dt][q4 * 4 + 1] * mul,
+                  acc[dt][q4 * 4 + 2] * mul, acc[dt][q4 * 4 + 3] * mul};
   }
 }
 
@@ -1103,7 +1054,7 @@ hipError_t launch_bwd_dkdv_mfma(const Shape& s, const BwdPtrs& p, char* ws,
   const long long ntab = a.ncol * s.C;
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)min((ntab + 255) / 256, 65535LL)),
                      dim3(256), 0, st, (uint32_t*)a.dlg, ntab);
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)wl.max_chunks), dim3(128), 0, st, a);
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)wl.max_chunks), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)a.ncol), dim3(256), 0, st, a);
