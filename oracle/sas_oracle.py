@@ -34,6 +34,12 @@ algorithm:
     activation sigmoid (log g = log sigmoid(s)) or raw logits (log g = s),
     beside the default softmax (Eq. 6); the current block keeps g0 = 1 in
     every variant.
+  * Sec. 4.1 "Ranking preservation", Eq. 7, Tab. 1 row 8: hard Top-K gates
+    with the straight-through estimator, g_hat = stopgrad(g_hard - g) + g:
+    the forward attends the selected blocks with unit gates; the gate
+    gradient of a dropped block is the attention mass its tokens would get
+    under the selected set's normaliser (Eq. 7), so every historical block
+    receives dg (see ``ste_gate_grad``).
 
 Readings where the pages leave a step open (each also listed in the design
 notes of the repository):
@@ -306,6 +312,60 @@ def backward_kv_block(q, k, v, do, log_gate, sel, block: int, b: int, hk: int, j
                             gate_pos=gate_pos)
     rows = slice(j * block, (j + 1) * block)
     return dk[b, hk, rows], dv[b, hk, rows]
+
+
+def ste_gate_grad(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = None):
+    """Gate gradients of the hard Top-K gates with the straight-through estimator
+    (Sec. 4.1 "Ranking preservation", Eq. 7, Tab. 1 row 8).
+
+    Forward: g_hat = 1 on selected blocks and 0 on dropped ones, so the output
+    is the selected-set attention with zero bias.  With p_i = g_hat_b(i) e^z_i /
+    sum_j g_hat_b(j) e^z_j, dL/dg_hat_m = sum_{i in B_m} (dp_i/dg_hat_m ...) =
+    sum_{t, u in B_m} e^{z_tu - lse_t} (dO_t . v_u - Delta_t), where lse_t is
+    the selected set's log normaliser (Eq. 7: the weight a dropped block's
+    token would get under it); for a selected block this is the block's dS sum.
+    The STE passes dL/dg = dL/dg_hat.
+    Returns dg float64 [B, Hkv, C, C] for every historical block m < i (0 for
+    m >= i).
+    """
+    bsz, hq, n, d = q.shape
+    hkv = k.shape[1]
+    grp = hq // hkv
+    scale = default_scale(d, sm_scale)
+    c = n // block
+    zero = np.where(np.isfinite(log_gate), 0.0, log_gate)
+    o, lse = forward(q, k, v, zero, sel, block, sm_scale)
+    dg = np.zeros((bsz, hkv, c, c))
+    for b in range(bsz):
+        for hk in range(hkv):
+            for i in range(1, c):
+                rows = slice(i * block, (i + 1) * block)
+                for m in range(i):
+                    cols = slice(m * block, (m + 1) * block)
+                    kk = _f64(k[b, hk, cols])
+                    vv = _f64(v[b, hk, cols])
+                    tot = 0.0
+                    for hh in range(hk * grp, (hk + 1) * grp):
+                        dd = _f64(do[b, hh, rows])
+                        z = scale * (_f64(q[b, hh, rows]) @ kk.T)
+                        pw = np.exp(z - lse[b, hh, rows][:, None])
+                        delta = np.sum(dd * o[b, hh, rows], axis=1, keepdims=True)
+                        tot += float(np.sum(pw * (dd @ vv.T - delta)))
+                    dg[b, hk, i, m] = tot
+    return dg
+
+
+def dscores_from_dg(dg, log_gate):
+    """Softmax backward (App. D.3) from gate gradients given for every
+    historical block (full scope): ds_m = g_m (dg_m - sum_l g_l dg_l)."""
+    bsz, hkv, c, _ = dg.shape
+    out = np.zeros((bsz, hkv, c, c))
+    for b in range(bsz):
+        for h in range(hkv):
+            for i in range(1, c):
+                gate = np.exp(log_gate[b, h, i, :i])
+                out[b, h, i, :i] = gate * (dg[b, h, i, :i] - np.sum(gate * dg[b, h, i, :i]))
+    return out
 
 
 def dscores(dlog_gate, log_gate, sel, act: str = "softmax"):

@@ -167,3 +167,65 @@ def test_planted_mistake_outer_dlogg_from_ds_is_caught(monkeypatch):
     *_, ds_t = torch_model(p, "outer")
     tri = np.tril(np.ones((8, 8), bool), -1)
     assert np.max(np.abs(ds_bad[..., tri] - ds_t[..., tri])) > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# hard Top-K gates with the straight-through estimator (Eq. 7, Tab. 1 row 8)
+# ---------------------------------------------------------------------------
+
+def torch_ste_model(p):
+    """Multiplicative-gate form p_i = g_hat e^z_i / sum_j g_hat e^z_j with
+    g_hat = (g_hard - g).detach() + g and g = softmax(s) over the historical
+    blocks (the current block keeps 1); scores are the leaf."""
+    B, Hq, N, D = p["q"].shape
+    Hkv = p["k"].shape[1]
+    G = Hq // Hkv
+    blk = p["block"]
+    C = N // blk
+    scale = 1.0 / math.sqrt(D)
+    q = torch.tensor(p["q"], requires_grad=True)
+    k = torch.tensor(p["k"], requires_grad=True)
+    v = torch.tensor(p["v"], requires_grad=True)
+    s = torch.tensor(p["scores"].astype(np.float64), requires_grad=True)
+    tri = torch.tril(torch.ones(C, C, dtype=torch.bool), diagonal=-1)
+    s_m = torch.where(tri, s, torch.tensor(-1e30, dtype=torch.float64))
+    g = torch.where(tri, torch.softmax(s_m, dim=-1), torch.zeros_like(s))
+    hard = torch.from_numpy(p["sel"]).to(torch.float64)
+    ghat = (hard - g).detach() + g
+    ghat = ghat + torch.eye(C, dtype=torch.float64)          # current block: 1
+    tok = torch.arange(N)
+    tb = tok // blk
+    causal = tok[None, :] <= tok[:, None]
+    outs = []
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // G
+            w = ghat[b, hk][tb][:, tb]
+            z = scale * q[b, h] @ k[b, hk].T
+            z = torch.where(causal, z, torch.tensor(-math.inf, dtype=torch.float64))
+            e = torch.exp(z - z.max(dim=-1, keepdim=True).values) * w
+            outs.append((e / e.sum(-1, keepdim=True)) @ v[b, hk])
+    o = torch.stack(outs).reshape(B, Hq, N, D)
+    (o * torch.from_numpy(p["do"])).sum().backward()
+    return o.detach().numpy(), q.grad.numpy(), k.grad.numpy(), v.grad.numpy(), s.grad.numpy()
+
+
+def test_ste_hard_gates_match_torch_autograd():
+    p = rand_problem(31, B=1, Hq=4, Hkv=2, N=40, D=8, block=4, K=3)
+    zero = np.where(np.isfinite(p["lg"]), 0.0, p["lg"])
+    o, _ = oracle.forward(p["q"], p["k"], p["v"], zero, p["sel"], 4)
+    dq, dk, dv, dlg_sel = oracle.backward(p["q"], p["k"], p["v"], p["do"], zero, p["sel"], 4)
+    dg = sas_oracle.ste_gate_grad(p["q"], p["k"], p["v"], p["do"], p["lg"], p["sel"], 4)
+    ds = sas_oracle.dscores_from_dg(dg, p["lg"])
+    o_t, dq_t, dk_t, dv_t, ds_t = torch_ste_model(p)
+    np.testing.assert_allclose(o, o_t, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(dq, dq_t, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(dk, dk_t, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(dv, dv_t, rtol=1e-10, atol=1e-10)
+    C = 10
+    tri = np.tril(np.ones((C, C), bool), -1)
+    np.testing.assert_allclose(ds[..., tri], ds_t[..., tri], rtol=1e-9, atol=1e-10)
+    # on selected blocks the STE gradient is the block's dS sum (unit gates)
+    np.testing.assert_allclose(dg[p["sel"]], dlg_sel[p["sel"]], rtol=1e-11, atol=1e-12)
+    # dropped blocks get a gradient of their own (Eq. 7), unlike the sparse scope
+    assert np.count_nonzero(np.abs(dg[tri[None, None] & ~p["sel"]]) > 1e-9) > 10
