@@ -24,6 +24,9 @@ SAS_GATE_INNER = 0
 SAS_GATE_OUTER = 1
 GATE_ACTS = {"softmax": SAS_GATE_SOFTMAX, "sigmoid": SAS_GATE_SIGMOID, "raw": SAS_GATE_RAW}
 GATE_POS = {"inner": SAS_GATE_INNER, "outer": SAS_GATE_OUTER}
+SAS_GATE_SOFT = 0
+SAS_GATE_HARD_STE = 1
+GATE_RANK = {"soft": SAS_GATE_SOFT, "hard_ste": SAS_GATE_HARD_STE}
 
 SAS_OK = 0
 SAS_E_INVALID = -1
@@ -43,7 +46,8 @@ class SasProblem(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("budget_k", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("o_dtype", ctypes.c_int32), ("sm_scale", ctypes.c_float),
-                ("gate_act", ctypes.c_int32), ("gate_pos", ctypes.c_int32)]
+                ("gate_act", ctypes.c_int32), ("gate_pos", ctypes.c_int32),
+                ("gate_rank", ctypes.c_int32)]
 
 
 class SasDecodeProblem(ctypes.Structure):

@@ -39,6 +39,7 @@ class Problem:
                                # always "fp32")
     gate_act: str = "softmax"  # "softmax" | "sigmoid" | "raw"
     gate_pos: str = "inner"    # "inner" (log g in the logits) | "outer" (g scales V)
+    gate_rank: str = "soft"    # "soft" | "hard_ste" (hard Top-K gates, straight-through)
 
     def __post_init__(self):
         if self.dtype == "fp32" and self.o_dtype != "fp32":
@@ -62,7 +63,7 @@ class Problem:
                           _native.SAS_BF16 if self.dtype == "bf16" else _native.SAS_FP32,
                           _native.SAS_BF16 if self.o_dtype == "bf16" else _native.SAS_FP32,
                           float(self.sm_scale), _native.GATE_ACTS[self.gate_act],
-                          _native.GATE_POS[self.gate_pos])
+                          _native.GATE_POS[self.gate_pos], _native.GATE_RANK[self.gate_rank])
 
     def default_cap(self) -> int:
         return max(1, min(self.budget_k, self.n_blocks - 1))

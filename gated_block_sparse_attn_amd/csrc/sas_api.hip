@@ -58,6 +58,12 @@ int32_t validate(const sas_problem* p, int32_t sel_cap, bool need_cap, sas::Shap
     return fail(SAS_E_INVALID, "gate_act %d is not a sas_gate_act", p->gate_act);
   if (p->gate_pos != SAS_GATE_INNER && p->gate_pos != SAS_GATE_OUTER)
     return fail(SAS_E_INVALID, "gate_pos %d is not a sas_gate_pos", p->gate_pos);
+  if (p->gate_rank != SAS_GATE_SOFT && p->gate_rank != SAS_GATE_HARD_STE)
+    return fail(SAS_E_INVALID, "gate_rank %d is not a sas_gate_rank", p->gate_rank);
+  if (p->gate_rank == SAS_GATE_HARD_STE &&
+      (p->gate_act != SAS_GATE_SOFTMAX || p->gate_pos != SAS_GATE_INNER))
+    return fail(SAS_E_UNSUPPORTED, "hard Top-K gates need the softmax activation and the "
+                "inner gate position");
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(SAS_E_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", p->head_dim);
   if (p->block_size != 16 && p->block_size != 32 && p->block_size != 64)
@@ -90,6 +96,7 @@ int32_t validate(const sas_problem* p, int32_t sel_cap, bool need_cap, sas::Shap
   s->scale = p->sm_scale > 0.0f ? p->sm_scale : 1.0f / sqrtf((float)p->head_dim);
   s->act = p->gate_act;
   s->outer = p->gate_pos == SAS_GATE_OUTER;
+  s->hard = p->gate_rank == SAS_GATE_HARD_STE;
   return SAS_OK;
 }
 
@@ -99,7 +106,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 namespace sas {
 
-bool mfma_path(const Shape& s) { return !s.fp32 && s.D == 128 && s.blk == 64 && !s.outer; }
+bool mfma_path(const Shape& s) {
+  return !s.fp32 && s.D == 128 && s.blk == 64 && !s.outer && !s.hard;
+}
 
 BwdWorkspace bwd_workspace_layout(const Shape& s) {
   BwdWorkspace w{};

@@ -8,7 +8,10 @@
 //           block (causal, bias 0) and the selected historical blocks (bias
 //           log g), streamed tile by tile with an online softmax in base 2;
 //           with the outer gate position (Sec. 4.1, Tab. 1 row 3) the logits
-//           carry no bias and the block's value rows are scaled by g;
+//           carry no bias and the block's value rows are scaled by g; with
+//           hard Top-K gates (Eq. 7, Tab. 1 row 8) the selected blocks carry
+//           unit gates and the dropped blocks' gate gradients come from
+//           ste_dropped_kernel;
 //  backward (App. E Alg. 4): P recomputed from LSE, dS = P (dP - Delta);
 //           query-major pass: dQ = scale dS K with Delta = rowsum(O dO), and
 //           the row sum of P dP (Delta without the rounding of O); key-major
@@ -44,6 +47,7 @@ struct GenArgs {
   int Hq, Hkv, G, N, C, cap;
   int o_fp32;   // o is stored as float32 (else as T)
   int outer;    // gates scale the value rows after the softmax (else log g bias)
+  int hard;     // hard Top-K gates (straight-through estimator): unit gates
   float c2;     // sm_scale * log2(e)
   float scale;  // sm_scale
 };
@@ -80,7 +84,7 @@ __global__ void __launch_bounds__(64) fwd_generic_kernel(GenArgs a) {
   float m = -INFINITY, l = 0.0f;
   for (int tile = 0; tile <= cnt; ++tile) {
     const int kb = tile == 0 ? i : sel[tile - 1];
-    const float lgv = tile == 0 ? 0.0f : a.lg[row * a.C + kb] * kLog2e;
+    const float lgv = (tile == 0 || a.hard) ? 0.0f : a.lg[row * a.C + kb] * kLog2e;
     const float beta = a.outer ? 0.0f : lgv;           // bias of the logits
     const float gv = a.outer ? exp2f(lgv) : 1.0f;      // factor of the value rows
     __syncthreads();
@@ -162,7 +166,7 @@ __global__ void __launch_bounds__(64) bwd_q_generic_kernel(GenArgs a) {
     }
     for (int tile = 0; tile <= cnt; ++tile) {
       const int kb = tile == 0 ? i : sel[tile - 1];
-      const float lgv = tile == 0 ? 0.0f : a.lg[row * a.C + kb] * kLog2e;
+      const float lgv = (tile == 0 || a.hard) ? 0.0f : a.lg[row * a.C + kb] * kLog2e;
       const float beta = a.outer ? 0.0f : lgv;
       const float gv = a.outer ? exp2f(lgv) : 1.0f;   // outer: dP = g dO . v
       __syncthreads();
@@ -236,7 +240,7 @@ __global__ void __launch_bounds__(64) bwd_kv_generic_kernel(GenArgs a) {
         if (u == 0) a.dlg[(rowbase + i) * a.C + j] = 0.0f;
         continue;
       }
-      beta = a.lg[(rowbase + i) * a.C + j] * kLog2e;
+      beta = a.hard ? 0.0f : a.lg[(rowbase + i) * a.C + j] * kLog2e;
     }
     // outer: no bias; dP = g dO . v, dV = g P^T dO, dLogG = sum of P dP
     const float gv = a.outer ? exp2f(beta) : 1.0f;
@@ -285,11 +289,65 @@ __global__ void __launch_bounds__(64) bwd_kv_generic_kernel(GenArgs a) {
   }
 }
 
+// Hard Top-K gates with the straight-through estimator (Sec. 4.1 "Ranking
+// preservation", Eq. 7): the gate gradient of every dropped historical block
+// m of query block i is the attention mass its tokens would receive under the
+// selected set's normaliser, exp(z - lse), times (dP - Delta), summed over
+// the block's tokens, the query block's rows and the G heads.  One wavefront
+// per row (b, h_kv, i); dropped blocks are found by walking the ascending
+// selected list; fixed summation order.
+template <typename T, int D, int BLK>
+__global__ void __launch_bounds__(64) ste_dropped_kernel(GenArgs a) {
+  extern __shared__ float smem[];
+  float* ks = smem;
+  float* vs = smem + BLK * D;
+  const int i = blockIdx.x;
+  const int bhk = blockIdx.y;
+  const int bb = bhk / a.Hkv, hk = bhk % a.Hkv;
+  const int t = threadIdx.x;
+  const bool active = t < BLK;
+  const long long row = ((long long)bb * a.Hkv + hk) * a.C + i;
+  const int cnt = min(a.sel_cnt[row], a.cap);
+  const int32_t* sel = a.sel_idx + row * a.cap;
+  const T* kbase = (const T*)a.k + ((long long)bb * a.Hkv + hk) * a.N * D;
+  const T* vbase = (const T*)a.v + ((long long)bb * a.Hkv + hk) * a.N * D;
+  int e = 0;
+  for (int m = 0; m < i; ++m) {
+    while (e < cnt && sel[e] < m) ++e;
+    if (e < cnt && sel[e] == m) continue;   // selected: its dS sum comes from the kv pass
+    __syncthreads();
+    stage_tile<T, D, BLK>(ks, kbase + (long long)m * BLK * D);
+    stage_tile<T, D, BLK>(vs, vbase + (long long)m * BLK * D);
+    __syncthreads();
+    float acc = 0.0f;
+    for (int hl = 0; hl < a.G; ++hl) {
+      const long long qi = ((long long)bb * a.Hq + hk * a.G + hl) * a.N + (long long)i * BLK + t;
+      if (!active) continue;
+      const T* qrow = (const T*)a.q + qi * D;
+      const T* drow = (const T*)a.d_o + qi * D;
+      const float lse2 = a.lse[qi] * kLog2e;
+      const float delta = a.delta[qi];
+#pragma unroll 1
+      for (int u = 0; u < BLK; ++u) {
+        float x = 0.0f, dp = 0.0f;
+        for (int d = 0; d < D; ++d) {
+          x += ld(qrow + d) * ks[u * D + d];
+          dp += ld(drow + d) * vs[u * D + d];
+        }
+        acc += exp2f(x * a.c2 - lse2) * (dp - delta);
+      }
+    }
+    acc = wave_sum(acc);
+    if (t == 0) a.dlg[row * a.C + m] = acc;
+  }
+}
+
 GenArgs make_args(const Shape& s) {
   GenArgs a{};
   a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.G; a.N = s.N; a.C = s.C; a.cap = s.cap;
   a.o_fp32 = s.o_fp32;
   a.outer = s.outer;
+  a.hard = s.hard;
   a.c2 = s.scale * kLog2e;
   a.scale = s.scale;
   return a;
@@ -381,6 +439,16 @@ hipError_t launch_bwd_dkdv_generic(const Shape& s, const BwdPtrs& p, char* ws,
     using T = std::remove_pointer_t<decltype(tp)>;
     return bwd_kv_launch<T, decltype(dc)::value, decltype(bc)::value>(a, s, st);
   });
+  if (e == hipSuccess && s.hard) {   // gate gradients of the dropped blocks
+    e = dispatch(s, [&](auto tp, auto dc, auto bc) {
+      using T = std::remove_pointer_t<decltype(tp)>;
+      constexpr int D = decltype(dc)::value, BLK = decltype(bc)::value;
+      const size_t lds = 2 * BLK * D * sizeof(float);
+      hipLaunchKernelGGL((ste_dropped_kernel<T, D, BLK>), dim3(s.C, s.B * s.Hkv), dim3(64), lds,
+                         st, a);
+      return hipGetLastError();
+    });
+  }
   if (e != hipSuccess || p.dscores == nullptr) return e;
   return launch_dscores(s, p.dlog_gate, p.log_gate, p.dscores, st);
 }

@@ -28,6 +28,7 @@ struct Shape {
   float scale;       // sm_scale (already defaulted)
   int act;           // sas_gate_act
   int outer;         // 1: gates scale the value rows after the softmax
+  int hard;          // 1: hard Top-K gates with the straight-through estimator
 };
 
 // Workspace carve-up of the backward pass (byte offsets, 256-aligned).

@@ -156,11 +156,13 @@ __global__ void __launch_bounds__(256) threshold_kernel(const float* __restrict_
 // This is App. D.3's ds_m = g_m (dg_m - sum_l g_l dg_l) with dLogG = g * dg,
 // and dg = 0 on unselected blocks (sparse scope, Eq. 8).  Sigmoid gates
 // depend on their own score only: ds_m = g_m (1 - g_m) dg_m = (1 - g_m) dLogG_m;
-// raw logits: ds_m = dLogG_m.
+// raw logits: ds_m = dLogG_m.  Hard gates (straight-through estimator): the
+// table holds dg itself for every historical block (full scope), so
+// ds_m = g_m (dg_m - sum_l g_l dg_l).
 __global__ void __launch_bounds__(256) dscores_kernel(const float* __restrict__ dlg,
                                                       const float* __restrict__ lg,
                                                       float* __restrict__ ds, long long rows,
-                                                      int C, int act) {
+                                                      int C, int act, int hard) {
   const int lane = threadIdx.x & 63;
   const long long row = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -168,7 +170,13 @@ __global__ void __launch_bounds__(256) dscores_kernel(const float* __restrict__ 
   const float* drow = dlg + row * (long long)C;
   const float* grow = lg + row * (long long)C;
   float* orow = ds + row * (long long)C;
-  if (act == SAS_GATE_SOFTMAX) {
+  if (hard) {   // dlog_gate holds dg of every historical block: g (dg - sum g dg)
+    float tot = 0.0f;
+    for (int m = lane; m < i; m += 64) tot += expf(grow[m]) * drow[m];
+    tot = wave_sum_f(tot);
+    for (int m = lane; m < C; m += 64)
+      orow[m] = (m < i) ? expf(grow[m]) * (drow[m] - tot) : 0.0f;
+  } else if (act == SAS_GATE_SOFTMAX) {
     float tot = 0.0f;
     for (int m = lane; m < i; m += 64) tot += drow[m];
     tot = wave_sum_f(tot);
@@ -201,7 +209,7 @@ hipError_t launch_dscores(const Shape& s, const float* dlog_gate, const float* l
   const long long rows = (long long)s.B * s.Hkv * s.C;
   const long long grid = (rows + 3) / 4;
   hipLaunchKernelGGL(dscores_kernel, dim3((unsigned)grid), dim3(256), 0, st, dlog_gate, log_gate,
-                     dscores, rows, s.C, s.act);
+                     dscores, rows, s.C, s.act, s.hard);
   return hipGetLastError();
 }
 

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SAS_ABI_VERSION 3
+#define SAS_ABI_VERSION 4
 
 typedef enum sas_dtype {
   SAS_BF16 = 0, /* q/k/v/o/d_o/dq/dk/dv are bfloat16 (fp32 accumulation) */
@@ -80,6 +80,20 @@ typedef enum sas_gate_pos {
   SAS_GATE_OUTER = 1  /* o = softmax(q K^T) (g . V): each block's value rows are
                          scaled by its gate after the softmax                   */
 } sas_gate_pos;
+
+/* Ranking preservation (Sec. 4.1, Eq. 7, Tab. 1 rows 7 and 8). */
+typedef enum sas_gate_rank {
+  SAS_GATE_SOFT = 0,    /* continuous gates log g (the method)                   */
+  SAS_GATE_HARD_STE = 1 /* hard Top-K gates, straight-through estimator: the
+                           forward gives the selected blocks unit gates (zero
+                           bias); the backward gives every historical block a
+                           gate gradient dg (selected: its dS sum; dropped: the
+                           attention mass its tokens would get under the
+                           selected set's normaliser, Eq. 7), written to
+                           dlog_gate, and dscores = g (dg - sum_l g_l dg_l).
+                           Softmax activation and inner position only; runs on
+                           the vector-ALU path (full-scope work).            */
+} sas_gate_rank;
 
 typedef enum sas_status {
   SAS_OK = 0,
@@ -110,6 +124,7 @@ typedef struct sas_problem {
   int32_t gate_pos;   /* a sas_gate_pos (SAS_GATE_INNER for the method).  The
                          outer position runs on the vector-ALU path for every
                          shape.                                                */
+  int32_t gate_rank;  /* a sas_gate_rank (SAS_GATE_SOFT for the method)        */
 } sas_problem;
 
 /* ABI version of the loaded library (SAS_ABI_VERSION). */

@@ -21,10 +21,10 @@ def log(msg):
 
 
 def problem_of(w: workloads.Workload, K: int, o_dtype: str = "bf16", gate_act: str = "softmax",
-               gate_pos: str = "inner") -> api.Problem:
+               gate_pos: str = "inner", gate_rank: str = "soft") -> api.Problem:
     return api.Problem(w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.block,
                        K, w.dtype, 0.0, o_dtype if w.dtype == "bf16" else "fp32", gate_act,
-                       gate_pos)
+                       gate_pos, gate_rank)
 
 
 def run_gpu(p: api.Problem, inp: dict, cap=None, poison=True, status=None):
@@ -106,17 +106,26 @@ def compare(name, got, ref, dtype, mask=None):
     assert rel_to_max <= rtol, f"{name}: max error {rel_to_max:.3e} of the tensor's max magnitude"
 
 
-def full_parity(w, K, inp=None, cap=None, o_dtype="bf16", gate_act="softmax", gate_pos="inner"):
+def full_parity(w, K, inp=None, cap=None, o_dtype="bf16", gate_act="softmax", gate_pos="inner",
+                gate_rank="soft"):
     """Whole-tensor parity of every output (sizes the oracle finishes quickly)."""
-    p = problem_of(w, K, o_dtype, gate_act, gate_pos)
+    p = problem_of(w, K, o_dtype, gate_act, gate_pos, gate_rank)
     inp = inp or workloads.generate(w)
     gpu = run_gpu(p, inp, cap=cap)
     scores = inp["scores"].numpy()
     lg, tau, sel = check_selection(gpu, scores, K, act=gate_act)
     q, k, v, do = (f32(inp[n]) for n in ("q", "k", "v", "do"))
-    o, lse = oracle.forward(q, k, v, lg, sel, w.block, gate_pos=gate_pos)
-    dq, dk, dv, dlg = oracle.backward(q, k, v, do, lg, sel, w.block, gate_pos=gate_pos)
-    dsc = oracle.dscores(dlg, lg, sel, act=gate_act)
+    if gate_rank == "hard_ste":
+        # unit gates on the selected blocks; every historical block gets dg
+        zero = np.where(np.isfinite(lg), 0.0, lg)
+        o, lse = oracle.forward(q, k, v, zero, sel, w.block)
+        dq, dk, dv, _ = oracle.backward(q, k, v, do, zero, sel, w.block)
+        dlg = oracle.sas_oracle.ste_gate_grad(q, k, v, do, lg, sel, w.block)
+        dsc = oracle.sas_oracle.dscores_from_dg(dlg, lg)
+    else:
+        o, lse = oracle.forward(q, k, v, lg, sel, w.block, gate_pos=gate_pos)
+        dq, dk, dv, dlg = oracle.backward(q, k, v, do, lg, sel, w.block, gate_pos=gate_pos)
+        dsc = oracle.dscores(dlg, lg, sel, act=gate_act)
     dt = w.dtype
     compare("o", f32(gpu["o"]), o, dt)
     compare("lse", gpu["lse"].numpy(), lse, dt)
@@ -125,8 +134,12 @@ def full_parity(w, K, inp=None, cap=None, o_dtype="bf16", gate_act="softmax", ga
     compare("dv", f32(gpu["dv"]), dv, dt)
     compare("dlog_gate", gpu["dlog_gate"].numpy(), dlg, dt)
     compare("dscores", gpu["dscores"].numpy(), dsc, dt)
-    # exact zero pattern of the block log-gate gradient
-    assert np.all(gpu["dlog_gate"].numpy()[~sel] == 0.0)
+    # exact zero pattern of the block log-gate gradient (hard gates: only the
+    # diagonal and the upper triangle)
+    c = sel.shape[-1]
+    hist = np.broadcast_to(np.tril(np.ones((c, c), bool), -1), sel.shape)
+    zero_at = ~hist if gate_rank == "hard_ste" else ~sel
+    assert np.all(gpu["dlog_gate"].numpy()[zero_at] == 0.0)
     return gpu
 
 

@@ -63,25 +63,29 @@ def test_small_shapes_full_parity(case):
 
 
 VARIANTS = [
-    # name, B, Hq, Hkv, N, D, blk, K, dtype, gate_act, gate_pos
+    # name, B, Hq, Hkv, N, D, blk, K, dtype, gate_act, gate_pos[, gate_rank]
     ("mfma_sigmoid", 1, 8, 2, 1024, 128, 64, 4, "bf16", "sigmoid", "inner"),
     ("mfma_raw", 1, 8, 2, 768, 128, 64, 3, "bf16", "raw", "inner"),
     ("outer_bf16_d128_b64", 1, 8, 2, 512, 128, 64, 3, "bf16", "softmax", "outer"),
     ("outer_sigmoid_fp32_d64_b16", 1, 4, 2, 256, 64, 16, 3, "fp32", "sigmoid", "outer"),
     ("generic_raw_fp32_d64_b32", 1, 2, 1, 256, 64, 32, 2, "fp32", "raw", "inner"),
     ("outer_full_scope", 1, 4, 1, 384, 128, 64, 100, "bf16", "softmax", "outer"),
+    ("hard_ste_bf16_d128_b64", 1, 8, 2, 512, 128, 64, 3, "bf16", "softmax", "inner", "hard_ste"),
+    ("hard_ste_fp32_d64_b16", 1, 2, 1, 256, 64, 16, 4, "fp32", "softmax", "inner", "hard_ste"),
 ]
 
 
 @pytest.mark.parametrize("case", VARIANTS, ids=[c[0] for c in VARIANTS])
 def test_gate_variants_full_parity(case):
-    """The ablated gate variants of the pages' Tab. 1 (activation, position)."""
-    name, B, Hq, Hkv, N, D, blk, K, dt, act, pos = case
+    """The ablated gate variants of the pages' Tab. 1 (activation, position,
+    hard Top-K gates with the straight-through estimator)."""
+    name, B, Hq, Hkv, N, D, blk, K, dt, act, pos = case[:11]
+    rank = case[11] if len(case) > 11 else "soft"
     log(f"variant {name}")
     w = workloads.custom(B, Hq, Hkv, N, D, blk, K, dtype=dt, seed=zlib.crc32(name.encode()) % 1000,
                          score_std=2.0)
     cap = max(1, min(K, N // blk - 1))
-    full_parity(w, K, cap=cap, gate_act=act, gate_pos=pos)
+    full_parity(w, K, cap=cap, gate_act=act, gate_pos=pos, gate_rank=rank)
 
 
 def test_tiny_fp32_workload():
