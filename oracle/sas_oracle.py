@@ -202,8 +202,11 @@ def forward(q, k, v, log_gate, sel, block: int, sm_scale: float | None = None,
             query_blocks=None, gate_pos: str = "inner"):
     """Eq. 9 output and natural-log LSE, one query block at a time.
 
-    q: [B, Hq, N, D]; k, v: [B, Hkv, N, D]; log_gate/sel: [B, Hkv, C, C].
-    ``query_blocks``: optional iterable of (b, h_kv, i) to evaluate (others
+    q: [B, Hq, N, D]; k, v: [B, Hkv, N, D]; log_gate/sel: [B, Hs, C, C] with
+    Hs score heads: Hs = Hkv (one gate / selection per query group, the
+    default) or Hs = Hq (per query head); score head s covers query heads
+    s Gs .. s Gs + Gs - 1 (Gs = Hq / Hs), which read kv head s Gs / G.
+    ``query_blocks``: optional iterable of (b, s, i) to evaluate (others
     are left 0), so large shapes can be sampled.
     ``gate_pos``: "inner" adds log g to the logits (Eq. 9); "outer" leaves the
     logits ungated and multiplies the value rows of each block by its gate,
@@ -212,23 +215,25 @@ def forward(q, k, v, log_gate, sel, block: int, sm_scale: float | None = None,
     Returns (o [B, Hq, N, D], lse [B, Hq, N]) in float64.
     """
     bsz, hq, n, d = q.shape
-    hkv = k.shape[1]
-    g = hq // hkv
+    g = hq // k.shape[1]
+    hs = log_gate.shape[1]
+    gs = hq // hs
     scale = default_scale(d, sm_scale)
     c = n // block
     o = np.zeros(q.shape)          # calloc: untouched pages cost nothing
     lse = np.zeros((bsz, hq, n))
     units = query_blocks if query_blocks is not None else \
-        [(b, h, i) for b in range(bsz) for h in range(hkv) for i in range(c)]
-    for (b, hk, i) in units:
-        keys, bias, _, mask = _attended_keys(i, block, sel[b, hk, i], log_gate[b, hk, i])
-        kk = _f64(k[b, hk, keys])
-        vv = _f64(v[b, hk, keys])
+        [(b, h, i) for b in range(bsz) for h in range(hs) for i in range(c)]
+    for (b, sh, i) in units:
+        keys, bias, _, mask = _attended_keys(i, block, sel[b, sh, i], log_gate[b, sh, i])
+        kvh = (sh * gs) // g
+        kk = _f64(k[b, kvh, keys])
+        vv = _f64(v[b, kvh, keys])
         if gate_pos == "outer":
             vv = vv * np.exp(bias)[:, None]
             bias = np.zeros_like(bias)
         rows = slice(i * block, (i + 1) * block)
-        for hh in range(hk * g, (hk + 1) * g):
+        for hh in range(sh * gs, (sh + 1) * gs):
             z = scale * (_f64(q[b, hh, rows]) @ kk.T) + bias[None, :]
             z = np.where(mask, z, NEG_INF)
             p, l = _softmax_rows(z)
@@ -245,9 +250,9 @@ def backward(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = No
     dP = dO V^T, Delta = rowsum(P * dP) (= dO . o), dS = P * (dP - Delta);
     dQ = sm_scale dS K, dK = sm_scale dS^T Q, dV = P^T dO, summed over the G
     query heads that read the same kv head; dLogG[i, m] = sum of dS over the
-    query tokens of block i (all heads of the group) and the key tokens of
-    selected historical block m.  Zero for unselected m, the diagonal and the
-    upper triangle.
+    query tokens of block i (all query heads of the score head) and the key
+    tokens of selected historical block m.  Zero for unselected m, the
+    diagonal and the upper triangle.  Score heads as in ``forward``.
 
     ``gate_pos`` = "outer": the value rows are scaled by their block's gate,
     so dP = dO (g . V)^T, dV = g . (P^T dO), and dLogG[i, m] = g_m dg_m =
@@ -258,18 +263,20 @@ def backward(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = No
     Returns (dq, dk, dv, dlog_gate) in float64.
     """
     bsz, hq, n, d = q.shape
-    hkv = k.shape[1]
-    g = hq // hkv
+    g = hq // k.shape[1]
+    hs = log_gate.shape[1]
+    gs = hq // hs
     scale = default_scale(d, sm_scale)
     c = n // block
     dq = np.zeros(q.shape)
     dk = np.zeros(k.shape)
     dv = np.zeros(v.shape)
-    dlg = np.zeros((bsz, hkv, c, c))
+    dlg = np.zeros((bsz, hs, c, c))
     units = query_blocks if query_blocks is not None else \
-        [(b, h, i) for b in range(bsz) for h in range(hkv) for i in range(c)]
-    for (b, hk, i) in units:
-        keys, bias, kblk, mask = _attended_keys(i, block, sel[b, hk, i], log_gate[b, hk, i])
+        [(b, h, i) for b in range(bsz) for h in range(hs) for i in range(c)]
+    for (b, sh, i) in units:
+        keys, bias, kblk, mask = _attended_keys(i, block, sel[b, sh, i], log_gate[b, sh, i])
+        hk = (sh * gs) // g
         kk = _f64(k[b, hk, keys])
         vv = _f64(v[b, hk, keys])
         gkey = np.ones(keys.shape[0])
@@ -279,7 +286,7 @@ def backward(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = No
             bias = np.zeros_like(bias)
         rows = slice(i * block, (i + 1) * block)
         ds_sum = np.zeros(keys.shape[0])
-        for hh in range(hk * g, (hk + 1) * g):
+        for hh in range(sh * gs, (sh + 1) * gs):
             qq = _f64(q[b, hh, rows])
             dd = _f64(do[b, hh, rows])
             z = scale * (qq @ kk.T) + bias[None, :]
@@ -294,7 +301,7 @@ def backward(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = No
             ds_sum += (p * dp).sum(axis=0) if gate_pos == "outer" else ds.sum(axis=0)
         for m in np.unique(kblk):
             if m != i:
-                dlg[b, hk, i, m] = ds_sum[kblk == m].sum()
+                dlg[b, sh, i, m] = ds_sum[kblk == m].sum()
     return dq, dk, dv, dlg
 
 
@@ -307,7 +314,10 @@ def backward_kv_block(q, k, v, do, log_gate, sel, block: int, b: int, hk: int, j
     Returns (dk_j [block, D], dv_j [block, D]).
     """
     c = q.shape[2] // block
-    users = [(b, hk, i) for i in range(j, c) if i == j or sel[b, hk, i, j]]
+    g = q.shape[1] // k.shape[1]
+    gs = q.shape[1] // sel.shape[1]
+    heads = range(hk * g // gs, (hk + 1) * g // gs)   # score heads of kv head hk
+    users = [(b, sh, i) for sh in heads for i in range(j, c) if i == j or sel[b, sh, i, j]]
     _, dk, dv, _ = backward(q, k, v, do, log_gate, sel, block, sm_scale, query_blocks=users,
                             gate_pos=gate_pos)
     rows = slice(j * block, (j + 1) * block)
