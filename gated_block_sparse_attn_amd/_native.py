@@ -47,7 +47,7 @@ class SasProblem(ctypes.Structure):
                 ("budget_k", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("o_dtype", ctypes.c_int32), ("sm_scale", ctypes.c_float),
                 ("gate_act", ctypes.c_int32), ("gate_pos", ctypes.c_int32),
-                ("gate_rank", ctypes.c_int32)]
+                ("gate_rank", ctypes.c_int32), ("n_score_heads", ctypes.c_int32)]
 
 
 class SasDecodeProblem(ctypes.Structure):

@@ -40,6 +40,7 @@ class Problem:
     gate_act: str = "softmax"  # "softmax" | "sigmoid" | "raw"
     gate_pos: str = "inner"    # "inner" (log g in the logits) | "outer" (g scales V)
     gate_rank: str = "soft"    # "soft" | "hard_ste" (hard Top-K gates, straight-through)
+    score_heads: str = "group" # "group": gates per kv group; "head": per query head
 
     def __post_init__(self):
         if self.dtype == "fp32" and self.o_dtype != "fp32":
@@ -63,10 +64,15 @@ class Problem:
                           _native.SAS_BF16 if self.dtype == "bf16" else _native.SAS_FP32,
                           _native.SAS_BF16 if self.o_dtype == "bf16" else _native.SAS_FP32,
                           float(self.sm_scale), _native.GATE_ACTS[self.gate_act],
-                          _native.GATE_POS[self.gate_pos], _native.GATE_RANK[self.gate_rank])
+                          _native.GATE_POS[self.gate_pos], _native.GATE_RANK[self.gate_rank],
+                          self.n_score_heads)
 
     def default_cap(self) -> int:
         return max(1, min(self.budget_k, self.n_blocks - 1))
+
+    @property
+    def n_score_heads(self) -> int:
+        return self.n_q_heads if self.score_heads == "head" else self.n_kv_heads
 
     @staticmethod
     def from_tensors(q: torch.Tensor, k: torch.Tensor, block_size: int, budget_k: int,
@@ -105,12 +111,13 @@ def _expect(t: torch.Tensor, name: str, shape, dtype):
 
 def _shapes(p: Problem, cap: int):
     c = p.n_blocks
+    hs = p.n_score_heads
     return dict(q=(p.batch, p.n_q_heads, p.seq_len, p.head_dim),
                 kv=(p.batch, p.n_kv_heads, p.seq_len, p.head_dim),
                 lse=(p.batch, p.n_q_heads, p.seq_len),
-                table=(p.batch, p.n_kv_heads, c, c),
-                row=(p.batch, p.n_kv_heads, c),
-                sel=(p.batch, p.n_kv_heads, c, cap))
+                table=(p.batch, hs, c, c),
+                row=(p.batch, hs, c),
+                sel=(p.batch, hs, c, cap))
 
 
 def gate_threshold(p: Problem, scores: torch.Tensor, sel_cap: Optional[int] = None,

@@ -58,6 +58,10 @@ int32_t validate(const sas_problem* p, int32_t sel_cap, bool need_cap, sas::Shap
     return fail(SAS_E_INVALID, "gate_act %d is not a sas_gate_act", p->gate_act);
   if (p->gate_pos != SAS_GATE_INNER && p->gate_pos != SAS_GATE_OUTER)
     return fail(SAS_E_INVALID, "gate_pos %d is not a sas_gate_pos", p->gate_pos);
+  if (p->n_score_heads != 0 && p->n_score_heads != p->n_kv_heads &&
+      p->n_score_heads != p->n_q_heads)
+    return fail(SAS_E_INVALID, "n_score_heads %d must be 0, n_kv_heads or n_q_heads",
+                p->n_score_heads);
   if (p->gate_rank != SAS_GATE_SOFT && p->gate_rank != SAS_GATE_HARD_STE)
     return fail(SAS_E_INVALID, "gate_rank %d is not a sas_gate_rank", p->gate_rank);
   if (p->gate_rank == SAS_GATE_HARD_STE &&
@@ -97,6 +101,7 @@ int32_t validate(const sas_problem* p, int32_t sel_cap, bool need_cap, sas::Shap
   s->act = p->gate_act;
   s->outer = p->gate_pos == SAS_GATE_OUTER;
   s->hard = p->gate_rank == SAS_GATE_HARD_STE;
+  s->Hs = p->n_score_heads == 0 ? p->n_kv_heads : p->n_score_heads;
   return SAS_OK;
 }
 
@@ -107,7 +112,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 namespace sas {
 
 bool mfma_path(const Shape& s) {
-  return !s.fp32 && s.D == 128 && s.blk == 64 && !s.outer && !s.hard;
+  return !s.fp32 && s.D == 128 && s.blk == 64 && !s.outer && !s.hard && s.Hs == s.Hkv;
 }
 
 BwdWorkspace bwd_workspace_layout(const Shape& s) {

@@ -45,6 +45,7 @@ struct GenArgs {
   const float* lse; const float* lg; const int32_t* sel_idx; const int32_t* sel_cnt;
   void* out; float* lse_out; void* dq; void* dk; void* dv; float* dlg; float* delta;
   int Hq, Hkv, G, N, C, cap;
+  int Hs, Gs;   // score heads (rows of the gate tables) and query heads per score head
   int o_fp32;   // o is stored as float32 (else as T)
   int outer;    // gates scale the value rows after the softmax (else log g bias)
   int hard;     // hard Top-K gates (straight-through estimator): unit gates
@@ -68,7 +69,7 @@ __global__ void __launch_bounds__(64) fwd_generic_kernel(GenArgs a) {
   const int bb = bh / a.Hq, h = bh % a.Hq, hk = h / a.G;
   const int t = threadIdx.x;
   const bool active = t < BLK;
-  const long long row = ((long long)bb * a.Hkv + hk) * a.C + i;
+  const long long row = ((long long)bb * a.Hs + h / a.Gs) * a.C + i;   // this head's gate row
   const int cnt = min(a.sel_cnt[row], a.cap);
   const int32_t* sel = a.sel_idx + row * a.cap;
   const T* qrow = (const T*)a.q + (((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + t) * D;
@@ -137,14 +138,14 @@ __global__ void __launch_bounds__(64) bwd_q_generic_kernel(GenArgs a) {
   const int bb = bhk / a.Hkv, hk = bhk % a.Hkv;
   const int t = threadIdx.x;
   const bool active = t < BLK;
-  const long long row = ((long long)bb * a.Hkv + hk) * a.C + i;
-  const int cnt = min(a.sel_cnt[row], a.cap);
-  const int32_t* sel = a.sel_idx + row * a.cap;
   const T* kbase = (const T*)a.k + ((long long)bb * a.Hkv + hk) * a.N * D;
   const T* vbase = (const T*)a.v + ((long long)bb * a.Hkv + hk) * a.N * D;
 
   for (int hl = 0; hl < a.G; ++hl) {
     const int h = hk * a.G + hl;
+    const long long row = ((long long)bb * a.Hs + h / a.Gs) * a.C + i;   // this head's gate row
+    const int cnt = min(a.sel_cnt[row], a.cap);
+    const int32_t* sel = a.sel_idx + row * a.cap;
     const long long qi = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + t;
     float q[D], dov[D], dq[D];
     float delta = 0.0f, lse2 = 0.0f, dx = 0.0f;
@@ -202,9 +203,11 @@ __global__ void __launch_bounds__(64) bwd_q_generic_kernel(GenArgs a) {
 }
 
 // Key-major backward: dK and dV of one key block j, over every query block
-// that attends it (the diagonal block and each later block that selected it),
-// and column j of the dLogG table (every entry written: the dS sum of a
-// selecting block i > j, else 0; one wavefront, fixed summation order).
+// that attends it (the diagonal block and each later block that selected it)
+// and every query head of the kv group, and column j of the dLogG table of
+// each score head of the group (every entry written: the dS sum of a
+// selecting block i > j over the score head's query heads, else 0; one
+// wavefront, fixed summation order).
 template <typename T, int D, int BLK>
 __global__ void __launch_bounds__(64) bwd_kv_generic_kernel(GenArgs a) {
   extern __shared__ float smem[];
@@ -223,9 +226,14 @@ __global__ void __launch_bounds__(64) bwd_kv_generic_kernel(GenArgs a) {
   float dk[D], dv[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) { dk[d] = 0.0f; dv[d] = 0.0f; }
-  const long long rowbase = ((long long)bb * a.Hkv + hk) * a.C;
-  for (int i = u; i <= j && i < a.C; i += blockDim.x) a.dlg[(rowbase + i) * a.C + j] = 0.0f;
-  for (int i = j; i < a.C; ++i) {
+  const int ns = a.G / a.Gs;   // score heads of this kv group
+  for (int si = 0; si < ns; ++si) {
+    const long long rb = ((long long)bb * a.Hs + hk * ns + si) * a.C;
+    for (int i = u; i <= j && i < a.C; i += blockDim.x) a.dlg[(rb + i) * a.C + j] = 0.0f;
+  }
+  for (int i = j; i < a.C; ++i)
+  for (int si = 0; si < ns; ++si) {
+    const long long rowbase = ((long long)bb * a.Hs + hk * ns + si) * a.C;
     float beta = 0.0f;
     if (i != j) {
       // is j in the ascending selected list of row i?  (binary search)
@@ -246,8 +254,8 @@ __global__ void __launch_bounds__(64) bwd_kv_generic_kernel(GenArgs a) {
     const float gv = a.outer ? exp2f(beta) : 1.0f;
     if (a.outer) beta = 0.0f;
     float gsum = 0.0f;
-    for (int hl = 0; hl < a.G; ++hl) {
-      const int h = hk * a.G + hl;
+    for (int hl = 0; hl < a.Gs; ++hl) {
+      const int h = (hk * ns + si) * a.Gs + hl;
       const long long q0 = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK;
 #pragma unroll 1
       for (int tq = 0; tq < BLK; ++tq) {
@@ -293,20 +301,21 @@ __global__ void __launch_bounds__(64) bwd_kv_generic_kernel(GenArgs a) {
 // preservation", Eq. 7): the gate gradient of every dropped historical block
 // m of query block i is the attention mass its tokens would receive under the
 // selected set's normaliser, exp(z - lse), times (dP - Delta), summed over
-// the block's tokens, the query block's rows and the G heads.  One wavefront
-// per row (b, h_kv, i); dropped blocks are found by walking the ascending
-// selected list; fixed summation order.
+// the block's tokens, the query block's rows and the query heads of the
+// score head.  One wavefront per gate row (b, score head, i); dropped blocks
+// are found by walking the ascending selected list; fixed summation order.
 template <typename T, int D, int BLK>
 __global__ void __launch_bounds__(64) ste_dropped_kernel(GenArgs a) {
   extern __shared__ float smem[];
   float* ks = smem;
   float* vs = smem + BLK * D;
   const int i = blockIdx.x;
-  const int bhk = blockIdx.y;
-  const int bb = bhk / a.Hkv, hk = bhk % a.Hkv;
+  const int bs = blockIdx.y;
+  const int bb = bs / a.Hs, sh = bs % a.Hs;
+  const int hk = sh * a.Gs / a.G;
   const int t = threadIdx.x;
   const bool active = t < BLK;
-  const long long row = ((long long)bb * a.Hkv + hk) * a.C + i;
+  const long long row = ((long long)bb * a.Hs + sh) * a.C + i;
   const int cnt = min(a.sel_cnt[row], a.cap);
   const int32_t* sel = a.sel_idx + row * a.cap;
   const T* kbase = (const T*)a.k + ((long long)bb * a.Hkv + hk) * a.N * D;
@@ -320,8 +329,8 @@ __global__ void __launch_bounds__(64) ste_dropped_kernel(GenArgs a) {
     stage_tile<T, D, BLK>(vs, vbase + (long long)m * BLK * D);
     __syncthreads();
     float acc = 0.0f;
-    for (int hl = 0; hl < a.G; ++hl) {
-      const long long qi = ((long long)bb * a.Hq + hk * a.G + hl) * a.N + (long long)i * BLK + t;
+    for (int hl = 0; hl < a.Gs; ++hl) {
+      const long long qi = ((long long)bb * a.Hq + sh * a.Gs + hl) * a.N + (long long)i * BLK + t;
       if (!active) continue;
       const T* qrow = (const T*)a.q + qi * D;
       const T* drow = (const T*)a.d_o + qi * D;
@@ -345,6 +354,7 @@ __global__ void __launch_bounds__(64) ste_dropped_kernel(GenArgs a) {
 GenArgs make_args(const Shape& s) {
   GenArgs a{};
   a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.G; a.N = s.N; a.C = s.C; a.cap = s.cap;
+  a.Hs = s.Hs; a.Gs = s.Hq / s.Hs;
   a.o_fp32 = s.o_fp32;
   a.outer = s.outer;
   a.hard = s.hard;
@@ -444,7 +454,7 @@ hipError_t launch_bwd_dkdv_generic(const Shape& s, const BwdPtrs& p, char* ws,
       using T = std::remove_pointer_t<decltype(tp)>;
       constexpr int D = decltype(dc)::value, BLK = decltype(bc)::value;
       const size_t lds = 2 * BLK * D * sizeof(float);
-      hipLaunchKernelGGL((ste_dropped_kernel<T, D, BLK>), dim3(s.C, s.B * s.Hkv), dim3(64), lds,
+      hipLaunchKernelGGL((ste_dropped_kernel<T, D, BLK>), dim3(s.C, s.B * s.Hs), dim3(64), lds,
                          st, a);
       return hipGetLastError();
     });

@@ -195,7 +195,7 @@ __global__ void __launch_bounds__(256) dscores_kernel(const float* __restrict__ 
 hipError_t launch_threshold(const Shape& s, const float* scores, float* log_gate, float* tau,
                             int32_t* sel_idx, int32_t* sel_cnt, int32_t* d_status,
                             hipStream_t st) {
-  const long long rows = (long long)s.B * s.Hkv * s.C;
+  const long long rows = (long long)s.B * s.Hs * s.C;
   const int nw = (s.C <= 4096) ? 4 : 1;
   const size_t lds = (size_t)nw * s.C * sizeof(float);
   const long long grid = (rows + nw - 1) / nw;
@@ -206,7 +206,7 @@ hipError_t launch_threshold(const Shape& s, const float* scores, float* log_gate
 
 hipError_t launch_dscores(const Shape& s, const float* dlog_gate, const float* log_gate,
                           float* dscores, hipStream_t st) {
-  const long long rows = (long long)s.B * s.Hkv * s.C;
+  const long long rows = (long long)s.B * s.Hs * s.C;
   const long long grid = (rows + 3) / 4;
   hipLaunchKernelGGL(dscores_kernel, dim3((unsigned)grid), dim3(256), 0, st, dlog_gate, log_gate,
                      dscores, rows, s.C, s.act, s.hard);

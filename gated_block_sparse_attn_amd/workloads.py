@@ -43,10 +43,15 @@ class Workload:
     score_std: float = 1.0
     boost_frac: float = 0.0
     boost_value: float = 0.0
+    score_heads: str = "group"   # "group": score rows per kv head; "head": per query head
 
     @property
     def n_blocks(self) -> int:
         return self.seq_len // self.block
+
+    @property
+    def n_score_heads(self) -> int:
+        return self.n_q_heads if self.score_heads == "head" else self.n_kv_heads
 
     @property
     def group(self) -> int:
@@ -80,19 +85,21 @@ WORKLOAD_ORDER = ["tiny_fp32", "qwen3_4b_8k", "qwen3_8b_32k", "qwen3_14b_16k", "
 
 
 def custom(batch, n_q_heads, n_kv_heads, seq_len, head_dim, block, budget, dtype="fp32",
-           seed=0, qkv_std=1.0, score_std=1.0, score_kind="normal") -> Workload:
+           seed=0, qkv_std=1.0, score_std=1.0, score_kind="normal",
+           score_heads="group") -> Workload:
     """An ad-hoc workload (used for small parity and edge-case tests)."""
     return Workload(f"custom_{seed}", batch, n_q_heads, n_kv_heads, seq_len, head_dim, block,
                     (budget,), dtype, seed, qkv_std=qkv_std, score_kind=score_kind,
-                    score_std=score_std)
+                    score_std=score_std, score_heads=score_heads)
 
 
 def generate(w: Workload, with_grad_out: bool = True, seed: Optional[int] = None):
     """Draw the inputs of workload ``w`` on the CPU.
 
     Returns a dict with q [B,Hq,N,D], k and v [B,Hkv,N,D], do (like q, if
-    requested) in the workload dtype, and scores float32 [B,Hkv,C,C] (the whole
-    square table is drawn; entries on or above the diagonal are never read).
+    requested) in the workload dtype, and scores float32 [B,Hs,C,C] (Hs = Hkv,
+    or Hq for per-head scores; the whole square table is drawn; entries on or
+    above the diagonal are never read).
     """
     g = torch.Generator().manual_seed(w.seed if seed is None else seed)
     dt = w.torch_dtype()
@@ -117,7 +124,7 @@ def generate(w: Workload, with_grad_out: bool = True, seed: Optional[int] = None
         out["do"] = do
     else:
         del do
-    sshape = (w.batch, w.n_kv_heads, c, c)
+    sshape = (w.batch, w.n_score_heads, c, c)
     if w.score_kind == "gumbel":
         u = torch.rand(sshape, generator=g, dtype=torch.float32)
         tiny = torch.finfo(torch.float32).tiny
@@ -128,7 +135,7 @@ def generate(w: Workload, with_grad_out: bool = True, seed: Optional[int] = None
         if w.score_kind == "normal_boost":
             nb = int(math.ceil(w.boost_frac * c))
             for b in range(w.batch):
-                for h in range(w.n_kv_heads):
+                for h in range(w.n_score_heads):
                     cols = torch.randperm(c, generator=g)[:nb]
                     scores[b, h][:, cols] += w.boost_value
     out["scores"] = scores.contiguous()

@@ -34,14 +34,15 @@
  *    k, v, dk, dv         [B, Hkv, N, D]   (dtype: bf16 or fp32)
  *    lse                  [B, Hq,  N]      fp32, natural-log LSE of each query row
  *    scores, log_gate,
- *    dlog_gate, dscores   [B, Hkv, C, C]   fp32, row = query block i,
+ *    dlog_gate, dscores   [B, Hs, C, C]    fp32, row = query block i,
  *                                          column = context block m
- *    tau, sel_cnt         [B, Hkv, C]      fp32 / int32
- *    sel_idx              [B, Hkv, C, sel_cap] int32
- *  Query head h reads kv head h / G.  Gates, threshold and selection are
- *  shared by the G query heads of a kv group and by the b queries of a query
- *  block (the per-query-group block selection of the paper's grouped-query
- *  setting); the gradient of a shared gate is the sum over its uses.
+ *    tau, sel_cnt         [B, Hs, C]       fp32 / int32
+ *    sel_idx              [B, Hs, C, sel_cap] int32
+ *  Query head h reads kv head h / G.  Hs = n_score_heads (Hkv by default):
+ *  gates, threshold and selection are shared by the Hq / Hs query heads of a
+ *  score head (by default the G heads of a kv group: the per-query-group block
+ *  selection of the paper's grouped-query setting) and by the b queries of a
+ *  query block; the gradient of a shared gate is the sum over its uses.
  *
  * Supported problem sizes: D in {64, 128}; b in {16, 32, 64}; C <= 8192;
  * K >= 0.  bf16 with D = 128 and b = 64 runs on the matrix-core (MFMA) path;
@@ -58,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SAS_ABI_VERSION 4
+#define SAS_ABI_VERSION 5
 
 typedef enum sas_dtype {
   SAS_BF16 = 0, /* q/k/v/o/d_o/dq/dk/dv are bfloat16 (fp32 accumulation) */
@@ -125,6 +126,13 @@ typedef struct sas_problem {
                          outer position runs on the vector-ALU path for every
                          shape.                                                */
   int32_t gate_rank;  /* a sas_gate_rank (SAS_GATE_SOFT for the method)        */
+  int32_t n_score_heads; /* Hs: rows of the gate tables per batch element.
+                         0 or Hkv: one gate / selection per query group (the
+                         per-group selection of the paper's GQA setting);
+                         Hq: one per query head (the training kernel's
+                         per-head log gates, App. E); score head s covers
+                         query heads s*(Hq/Hs) .. +Hq/Hs-1.  Hs = Hq with
+                         G > 1 runs on the vector-ALU path.                  */
 } sas_problem;
 
 /* ABI version of the loaded library (SAS_ABI_VERSION). */

@@ -335,19 +335,21 @@ def ste_gate_grad(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None
     the selected set's log normaliser (Eq. 7: the weight a dropped block's
     token would get under it); for a selected block this is the block's dS sum.
     The STE passes dL/dg = dL/dg_hat.
-    Returns dg float64 [B, Hkv, C, C] for every historical block m < i (0 for
-    m >= i).
+    Returns dg float64 [B, Hs, C, C] (score heads as in ``forward``) for every
+    historical block m < i (0 for m >= i).
     """
     bsz, hq, n, d = q.shape
-    hkv = k.shape[1]
-    grp = hq // hkv
+    g = hq // k.shape[1]
+    hs = log_gate.shape[1]
+    gs = hq // hs
     scale = default_scale(d, sm_scale)
     c = n // block
     zero = np.where(np.isfinite(log_gate), 0.0, log_gate)
     o, lse = forward(q, k, v, zero, sel, block, sm_scale)
-    dg = np.zeros((bsz, hkv, c, c))
+    dg = np.zeros((bsz, hs, c, c))
     for b in range(bsz):
-        for hk in range(hkv):
+        for sh in range(hs):
+            hk = (sh * gs) // g
             for i in range(1, c):
                 rows = slice(i * block, (i + 1) * block)
                 for m in range(i):
@@ -355,13 +357,13 @@ def ste_gate_grad(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None
                     kk = _f64(k[b, hk, cols])
                     vv = _f64(v[b, hk, cols])
                     tot = 0.0
-                    for hh in range(hk * grp, (hk + 1) * grp):
+                    for hh in range(sh * gs, (sh + 1) * gs):
                         dd = _f64(do[b, hh, rows])
                         z = scale * (_f64(q[b, hh, rows]) @ kk.T)
                         pw = np.exp(z - lse[b, hh, rows][:, None])
                         delta = np.sum(dd * o[b, hh, rows], axis=1, keepdims=True)
                         tot += float(np.sum(pw * (dd @ vv.T - delta)))
-                    dg[b, hk, i, m] = tot
+                    dg[b, sh, i, m] = tot
     return dg
 
 

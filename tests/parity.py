@@ -24,7 +24,7 @@ def problem_of(w: workloads.Workload, K: int, o_dtype: str = "bf16", gate_act: s
                gate_pos: str = "inner", gate_rank: str = "soft") -> api.Problem:
     return api.Problem(w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.block,
                        K, w.dtype, 0.0, o_dtype if w.dtype == "bf16" else "fp32", gate_act,
-                       gate_pos, gate_rank)
+                       gate_pos, gate_rank, w.score_heads)
 
 
 def run_gpu(p: api.Problem, inp: dict, cap=None, poison=True, status=None):

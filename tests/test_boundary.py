@@ -20,7 +20,7 @@ def lib():
 def prob(**kw):
     base = dict(batch=1, n_q_heads=8, n_kv_heads=2, seq_len=1024, head_dim=128, block_size=64,
                 budget_k=4, dtype=nat.SAS_BF16, o_dtype=nat.SAS_FP32, sm_scale=0.0, gate_act=0,
-                gate_pos=0, gate_rank=0)
+                gate_pos=0, gate_rank=0, n_score_heads=0)
     base.update(kw)
     return nat.SasProblem(**base)
 
@@ -59,8 +59,8 @@ def test_library_exports_every_header_symbol():
 
 
 def test_abi_version():
-    assert lib().sas_abi_version() == 4
-    assert api.abi_version() == 4
+    assert lib().sas_abi_version() == 5
+    assert api.abi_version() == 5
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -74,6 +74,7 @@ def test_abi_version():
     (dict(gate_act=3), nat.SAS_E_INVALID),
     (dict(gate_pos=2), nat.SAS_E_INVALID),
     (dict(gate_rank=2), nat.SAS_E_INVALID),
+    (dict(n_score_heads=3), nat.SAS_E_INVALID),                # neither Hkv nor Hq
     (dict(gate_rank=1, gate_act=1), nat.SAS_E_UNSUPPORTED),   # hard gates: softmax only
     (dict(gate_rank=1, gate_pos=1), nat.SAS_E_UNSUPPORTED),   # hard gates: inner only
     (dict(head_dim=96), nat.SAS_E_UNSUPPORTED),

@@ -63,7 +63,7 @@ def test_small_shapes_full_parity(case):
 
 
 VARIANTS = [
-    # name, B, Hq, Hkv, N, D, blk, K, dtype, gate_act, gate_pos[, gate_rank]
+    # name, B, Hq, Hkv, N, D, blk, K, dtype, gate_act, gate_pos[, gate_rank[, score_heads]]
     ("mfma_sigmoid", 1, 8, 2, 1024, 128, 64, 4, "bf16", "sigmoid", "inner"),
     ("mfma_raw", 1, 8, 2, 768, 128, 64, 3, "bf16", "raw", "inner"),
     ("outer_bf16_d128_b64", 1, 8, 2, 512, 128, 64, 3, "bf16", "softmax", "outer"),
@@ -72,6 +72,13 @@ VARIANTS = [
     ("outer_full_scope", 1, 4, 1, 384, 128, 64, 100, "bf16", "softmax", "outer"),
     ("hard_ste_bf16_d128_b64", 1, 8, 2, 512, 128, 64, 3, "bf16", "softmax", "inner", "hard_ste"),
     ("hard_ste_fp32_d64_b16", 1, 2, 1, 256, 64, 16, 4, "fp32", "softmax", "inner", "hard_ste"),
+    # per-query-head gates (score heads = query heads)
+    ("heads_bf16_d128_b64_g4", 1, 8, 2, 512, 128, 64, 3, "bf16", "softmax", "inner", "soft", "head"),
+    ("heads_fp32_d64_b16_g2", 2, 4, 2, 256, 64, 16, 4, "fp32", "sigmoid", "inner", "soft", "head"),
+    ("heads_hard_ste_fp32_d64_b32", 1, 4, 2, 256, 64, 32, 3, "fp32", "softmax", "inner", "hard_ste",
+     "head"),
+    ("heads_outer_bf16_d128_b64_g5", 1, 10, 2, 384, 128, 64, 2, "bf16", "softmax", "outer", "soft",
+     "head"),
 ]
 
 
@@ -81,9 +88,10 @@ def test_gate_variants_full_parity(case):
     hard Top-K gates with the straight-through estimator)."""
     name, B, Hq, Hkv, N, D, blk, K, dt, act, pos = case[:11]
     rank = case[11] if len(case) > 11 else "soft"
+    heads = case[12] if len(case) > 12 else "group"
     log(f"variant {name}")
     w = workloads.custom(B, Hq, Hkv, N, D, blk, K, dtype=dt, seed=zlib.crc32(name.encode()) % 1000,
-                         score_std=2.0)
+                         score_std=2.0, score_heads=heads)
     cap = max(1, min(K, N // blk - 1))
     full_parity(w, K, cap=cap, gate_act=act, gate_pos=pos, gate_rank=rank)
 

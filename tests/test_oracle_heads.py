@@ -99,3 +99,15 @@ def test_group_of_one_is_the_same_either_way():
     o, _ = oracle.forward(p["q"], p["k"], p["v"], p["lg"], p["sel"], 4)
     o_t, *_ = torch_per_head(p)
     np.testing.assert_allclose(o, o_t, rtol=1e-11, atol=1e-11)
+
+
+def test_per_head_hard_gates_reduce_to_group_gates():
+    """ste_gate_grad with per-head scores that repeat the group's scores sums
+    to the group-gate result."""
+    from oracle import sas_oracle
+    pg = problem(4, per_head=False)
+    scores_h = np.repeat(pg["scores"], 2, axis=1)
+    lg_h, _, sel_h = oracle.gate_threshold(scores_h, 3)
+    dg_g = sas_oracle.ste_gate_grad(pg["q"], pg["k"], pg["v"], pg["do"], pg["lg"], pg["sel"], 4)
+    dg_h = sas_oracle.ste_gate_grad(pg["q"], pg["k"], pg["v"], pg["do"], lg_h, sel_h, 4)
+    np.testing.assert_allclose(dg_h.reshape(1, 2, 2, 10, 10).sum(2), dg_g, rtol=1e-12, atol=1e-12)
