@@ -52,7 +52,13 @@ notes of the repository):
   * the threshold is applied to the fp32 selector score s itself (log g is a
     monotone shift of s), selection is s >= tau, so ties at tau are all kept;
   * query head h reads kv head floor(h / G);
-  * sm_scale defaults to 1/sqrt(D) and never scales log g.
+  * sm_scale defaults to 1/sqrt(D) and never scales log g;
+  * variable-length batches (the packed varlen sequences of the pages'
+    training kernel, held here in a padded [B, H, N, D] layout): sequence b
+    has n_b valid tokens and C_b = ceil(n_b / b) blocks, the last one possibly
+    ragged; query rows t >= n_b are padding (no output, no gradient), gate
+    rows i >= C_b select nothing; the valid rows of a ragged last block attend
+    their block causally, so padding keys are never attended.
 
 Everything is float64 numpy; inputs are upcast from the exact values the GPU
 sees.  Two forms are provided: a brute-force dense evaluation per query head
@@ -115,7 +121,13 @@ def log_activation(hist64: np.ndarray, act: str) -> np.ndarray:
     raise ValueError(act)
 
 
-def gate_threshold(scores: np.ndarray, budget_k: int, act: str = "softmax"):
+def n_blocks_of(n: int, block: int) -> int:
+    """Blocks of a sequence of n tokens (the last one may be ragged)."""
+    return (int(n) + block - 1) // block
+
+
+def gate_threshold(scores: np.ndarray, budget_k: int, act: str = "softmax", seq_lens=None,
+                   block: int | None = None):
     """Gates, thresholds and selected sets for every query block.
 
     scores: fp32 [B, Hkv, C, C]; only entries m < i of row i are read (the
@@ -126,6 +138,8 @@ def gate_threshold(scores: np.ndarray, budget_k: int, act: str = "softmax"):
                softmax), 0 on the diagonal (g0 = 1, Eq. 4), -inf above it;
       tau      float32 [B, Hkv, C]: score-space threshold of each row;
       sel      bool    [B, Hkv, C, C]: m < i and s_{i,m} >= tau_i.
+    With ``seq_lens`` (and ``block``) a row i >= C_b of sequence b holds no
+    query and selects nothing (tau = +inf); its gates are still written.
     """
     scores = np.asarray(scores)
     assert scores.dtype == np.float32 and scores.ndim == 4
@@ -141,6 +155,9 @@ def gate_threshold(scores: np.ndarray, budget_k: int, act: str = "softmax"):
                 if i > 0:
                     log_gate[b, h, i, :i] = log_activation(hist.astype(np.float64), act)
                 log_gate[b, h, i, i] = 0.0
+                if seq_lens is not None and i >= n_blocks_of(seq_lens[b], block):
+                    tau[b, h, i] = np.float32(np.inf)
+                    continue
                 t = kth_largest_threshold(hist, budget_k)
                 tau[b, h, i] = t
                 sel[b, h, i, :i] = hist >= t
@@ -198,8 +215,15 @@ def default_scale(head_dim: int, sm_scale: float | None) -> float:
     return float(sm_scale)
 
 
+def _valid_rows(b: int, i: int, block: int, seq_lens) -> int:
+    """Valid query rows of block i of sequence b (0 .. block)."""
+    if seq_lens is None:
+        return block
+    return int(min(block, max(0, int(seq_lens[b]) - i * block)))
+
+
 def forward(q, k, v, log_gate, sel, block: int, sm_scale: float | None = None,
-            query_blocks=None, gate_pos: str = "inner"):
+            query_blocks=None, gate_pos: str = "inner", seq_lens=None):
     """Eq. 9 output and natural-log LSE, one query block at a time.
 
     q: [B, Hq, N, D]; k, v: [B, Hkv, N, D]; log_gate/sel: [B, Hs, C, C] with
@@ -212,6 +236,7 @@ def forward(q, k, v, log_gate, sel, block: int, sm_scale: float | None = None,
     logits ungated and multiplies the value rows of each block by its gate,
     o = softmax(q K^T) (g . V) (Sec. 4.1, Tab. 1 row 3); lse is then the
     ungated one.
+    ``seq_lens``: valid tokens per sequence (padding rows get o = 0, lse = 0).
     Returns (o [B, Hq, N, D], lse [B, Hq, N]) in float64.
     """
     bsz, hq, n, d = q.shape
@@ -225,14 +250,22 @@ def forward(q, k, v, log_gate, sel, block: int, sm_scale: float | None = None,
     units = query_blocks if query_blocks is not None else \
         [(b, h, i) for b in range(bsz) for h in range(hs) for i in range(c)]
     for (b, sh, i) in units:
+        nv = _valid_rows(b, i, block, seq_lens)
+        if nv == 0:
+            continue
         keys, bias, _, mask = _attended_keys(i, block, sel[b, sh, i], log_gate[b, sh, i])
+        mask = mask[:nv]
         kvh = (sh * gs) // g
         kk = _f64(k[b, kvh, keys])
         vv = _f64(v[b, kvh, keys])
+        if seq_lens is not None:   # padding keys are never attended; keep them out of the sums
+            pad = keys >= int(seq_lens[b])
+            kk[pad] = 0.0
+            vv[pad] = 0.0
         if gate_pos == "outer":
             vv = vv * np.exp(bias)[:, None]
             bias = np.zeros_like(bias)
-        rows = slice(i * block, (i + 1) * block)
+        rows = slice(i * block, i * block + nv)
         for hh in range(sh * gs, (sh + 1) * gs):
             z = scale * (_f64(q[b, hh, rows]) @ kk.T) + bias[None, :]
             z = np.where(mask, z, NEG_INF)
@@ -243,7 +276,7 @@ def forward(q, k, v, log_gate, sel, block: int, sm_scale: float | None = None,
 
 
 def backward(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = None,
-             query_blocks=None, gate_pos: str = "inner"):
+             query_blocks=None, gate_pos: str = "inner", seq_lens=None):
     """Gradients of Eq. 9 w.r.t. q, k, v and the block log gates.
 
     Follows the recomputation view of App. E: P from the attended logits,
@@ -260,6 +293,7 @@ def backward(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = No
 
     If ``query_blocks`` is given, only those query blocks contribute (their dQ
     and dLogG rows are exact; dK/dV hold only their contributions).
+    ``seq_lens``: padding query rows contribute nothing and get dQ = 0.
     Returns (dq, dk, dv, dlog_gate) in float64.
     """
     bsz, hq, n, d = q.shape
@@ -275,16 +309,24 @@ def backward(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = No
     units = query_blocks if query_blocks is not None else \
         [(b, h, i) for b in range(bsz) for h in range(hs) for i in range(c)]
     for (b, sh, i) in units:
+        nv = _valid_rows(b, i, block, seq_lens)
+        if nv == 0:
+            continue
         keys, bias, kblk, mask = _attended_keys(i, block, sel[b, sh, i], log_gate[b, sh, i])
+        mask = mask[:nv]
         hk = (sh * gs) // g
         kk = _f64(k[b, hk, keys])
         vv = _f64(v[b, hk, keys])
+        if seq_lens is not None:
+            pad = keys >= int(seq_lens[b])
+            kk[pad] = 0.0
+            vv[pad] = 0.0
         gkey = np.ones(keys.shape[0])
         if gate_pos == "outer":
             gkey = np.exp(bias)
             vv = vv * gkey[:, None]
             bias = np.zeros_like(bias)
-        rows = slice(i * block, (i + 1) * block)
+        rows = slice(i * block, i * block + nv)
         ds_sum = np.zeros(keys.shape[0])
         for hh in range(sh * gs, (sh + 1) * gs):
             qq = _f64(q[b, hh, rows])
@@ -324,7 +366,8 @@ def backward_kv_block(q, k, v, do, log_gate, sel, block: int, b: int, hk: int, j
     return dk[b, hk, rows], dv[b, hk, rows]
 
 
-def ste_gate_grad(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = None):
+def ste_gate_grad(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = None,
+                  seq_lens=None):
     """Gate gradients of the hard Top-K gates with the straight-through estimator
     (Sec. 4.1 "Ranking preservation", Eq. 7, Tab. 1 row 8).
 
@@ -345,13 +388,16 @@ def ste_gate_grad(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None
     scale = default_scale(d, sm_scale)
     c = n // block
     zero = np.where(np.isfinite(log_gate), 0.0, log_gate)
-    o, lse = forward(q, k, v, zero, sel, block, sm_scale)
+    o, lse = forward(q, k, v, zero, sel, block, sm_scale, seq_lens=seq_lens)
     dg = np.zeros((bsz, hs, c, c))
     for b in range(bsz):
         for sh in range(hs):
             hk = (sh * gs) // g
             for i in range(1, c):
-                rows = slice(i * block, (i + 1) * block)
+                nv = _valid_rows(b, i, block, seq_lens)
+                if nv == 0:
+                    continue
+                rows = slice(i * block, i * block + nv)
                 for m in range(i):
                     cols = slice(m * block, (m + 1) * block)
                     kk = _f64(k[b, hk, cols])
