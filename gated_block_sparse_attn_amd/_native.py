@@ -47,7 +47,8 @@ class SasProblem(ctypes.Structure):
                 ("budget_k", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("o_dtype", ctypes.c_int32), ("sm_scale", ctypes.c_float),
                 ("gate_act", ctypes.c_int32), ("gate_pos", ctypes.c_int32),
-                ("gate_rank", ctypes.c_int32), ("n_score_heads", ctypes.c_int32)]
+                ("gate_rank", ctypes.c_int32), ("n_score_heads", ctypes.c_int32),
+                ("seq_lens", ctypes.c_void_p)]
 
 
 class SasDecodeProblem(ctypes.Structure):

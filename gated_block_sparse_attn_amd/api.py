@@ -41,6 +41,9 @@ class Problem:
     gate_pos: str = "inner"    # "inner" (log g in the logits) | "outer" (g scales V)
     gate_rank: str = "soft"    # "soft" | "hard_ste" (hard Top-K gates, straight-through)
     score_heads: str = "group" # "group": gates per kv group; "head": per query head
+    # Variable-length batches: optional int32 device tensor [batch] of valid tokens per
+    # sequence (padded layout; None: every sequence holds seq_len tokens).
+    seq_lens: Optional[torch.Tensor] = dataclasses.field(default=None, compare=False)
 
     def __post_init__(self):
         if self.dtype == "fp32" and self.o_dtype != "fp32":
@@ -59,13 +62,15 @@ class Problem:
         return torch.bfloat16 if self.o_dtype == "bf16" else torch.float32
 
     def c(self) -> SasProblem:
+        if self.seq_lens is not None:
+            _expect(self.seq_lens, "seq_lens", (self.batch,), torch.int32)
         return SasProblem(self.batch, self.n_q_heads, self.n_kv_heads, self.seq_len,
                           self.head_dim, self.block_size, self.budget_k,
                           _native.SAS_BF16 if self.dtype == "bf16" else _native.SAS_FP32,
                           _native.SAS_BF16 if self.o_dtype == "bf16" else _native.SAS_FP32,
                           float(self.sm_scale), _native.GATE_ACTS[self.gate_act],
                           _native.GATE_POS[self.gate_pos], _native.GATE_RANK[self.gate_rank],
-                          self.n_score_heads)
+                          self.n_score_heads, _ptr(self.seq_lens))
 
     def default_cap(self) -> int:
         return max(1, min(self.budget_k, self.n_blocks - 1))

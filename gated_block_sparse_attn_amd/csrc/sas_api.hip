@@ -102,6 +102,7 @@ int32_t validate(const sas_problem* p, int32_t sel_cap, bool need_cap, sas::Shap
   s->outer = p->gate_pos == SAS_GATE_OUTER;
   s->hard = p->gate_rank == SAS_GATE_HARD_STE;
   s->Hs = p->n_score_heads == 0 ? p->n_kv_heads : p->n_score_heads;
+  s->lens = p->seq_lens;
   return SAS_OK;
 }
 
@@ -112,7 +113,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 namespace sas {
 
 bool mfma_path(const Shape& s) {
-  return !s.fp32 && s.D == 128 && s.blk == 64 && !s.outer && !s.hard && s.Hs == s.Hkv;
+  return !s.fp32 && s.D == 128 && s.blk == 64 && !s.outer && !s.hard && s.Hs == s.Hkv &&
+         s.lens == nullptr;
 }
 
 BwdWorkspace bwd_workspace_layout(const Shape& s) {

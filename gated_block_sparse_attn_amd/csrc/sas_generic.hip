@@ -49,9 +49,15 @@ struct GenArgs {
   int o_fp32;   // o is stored as float32 (else as T)
   int outer;    // gates scale the value rows after the softmax (else log g bias)
   int hard;     // hard Top-K gates (straight-through estimator): unit gates
+  const int32_t* lens;   // valid tokens per sequence (nullptr: all N)
   float c2;     // sm_scale * log2(e)
   float scale;  // sm_scale
 };
+
+// Valid tokens of sequence b (variable-length batches; clamped into [0, N]).
+__device__ __forceinline__ int seq_len_of(const int32_t* lens, int b, int N) {
+  return lens == nullptr ? N : min(max(lens[b], 0), N);
+}
 
 // Stage rows [row0, row0 + BLK) of a [N, D] matrix into LDS as fp32.
 template <typename T, int D, int BLK>
@@ -68,7 +74,9 @@ __global__ void __launch_bounds__(64) fwd_generic_kernel(GenArgs a) {
   const int bh = blockIdx.y;
   const int bb = bh / a.Hq, h = bh % a.Hq, hk = h / a.G;
   const int t = threadIdx.x;
-  const bool active = t < BLK;
+  const int nb = seq_len_of(a.lens, bb, a.N);
+  const bool active = t < BLK && i * BLK + t < nb;   // padding rows stay inactive
+  const bool any = i * BLK < nb;                      // block holds a valid row (uniform)
   const long long row = ((long long)bb * a.Hs + h / a.Gs) * a.C + i;   // this head's gate row
   const int cnt = min(a.sel_cnt[row], a.cap);
   const int32_t* sel = a.sel_idx + row * a.cap;
@@ -83,7 +91,7 @@ __global__ void __launch_bounds__(64) fwd_generic_kernel(GenArgs a) {
     acc[d] = 0.0f;
   }
   float m = -INFINITY, l = 0.0f;
-  for (int tile = 0; tile <= cnt; ++tile) {
+  for (int tile = 0; any && tile <= cnt; ++tile) {
     const int kb = tile == 0 ? i : sel[tile - 1];
     const float lgv = (tile == 0 || a.hard) ? 0.0f : a.lg[row * a.C + kb] * kLog2e;
     const float beta = a.outer ? 0.0f : lgv;           // bias of the logits
@@ -111,9 +119,9 @@ __global__ void __launch_bounds__(64) fwd_generic_kernel(GenArgs a) {
       }
     }
   }
-  if (active) {
+  if (t < BLK) {   // padding rows: o = 0, lse = 0
     const long long qi = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + t;
-    const float inv = 1.0f / l;
+    const float inv = active ? 1.0f / l : 0.0f;
     if (a.o_fp32) {
       float* orow = (float*)a.out + qi * D;
 #pragma unroll
@@ -123,7 +131,7 @@ __global__ void __launch_bounds__(64) fwd_generic_kernel(GenArgs a) {
 #pragma unroll
       for (int d = 0; d < D; ++d) st(orow + d, acc[d] * inv);
     }
-    a.lse_out[qi] = (m + log2f(l)) * kLn2;
+    a.lse_out[qi] = active ? (m + log2f(l)) * kLn2 : 0.0f;
   }
 }
 
@@ -137,7 +145,9 @@ __global__ void __launch_bounds__(64) bwd_q_generic_kernel(GenArgs a) {
   const int bhk = blockIdx.y;
   const int bb = bhk / a.Hkv, hk = bhk % a.Hkv;
   const int t = threadIdx.x;
-  const bool active = t < BLK;
+  const int nb = seq_len_of(a.lens, bb, a.N);
+  const bool active = t < BLK && i * BLK + t < nb;   // padding rows: dq = 0, Delta = 0
+  const bool any = i * BLK < nb;
   const T* kbase = (const T*)a.k + ((long long)bb * a.Hkv + hk) * a.N * D;
   const T* vbase = (const T*)a.v + ((long long)bb * a.Hkv + hk) * a.N * D;
 
@@ -165,7 +175,7 @@ __global__ void __launch_bounds__(64) bwd_q_generic_kernel(GenArgs a) {
 #pragma unroll
       for (int d = 0; d < D; ++d) { q[d] = 0.0f; dov[d] = 0.0f; dq[d] = 0.0f; }
     }
-    for (int tile = 0; tile <= cnt; ++tile) {
+    for (int tile = 0; any && tile <= cnt; ++tile) {
       const int kb = tile == 0 ? i : sel[tile - 1];
       const float lgv = (tile == 0 || a.hard) ? 0.0f : a.lg[row * a.C + kb] * kLog2e;
       const float beta = a.outer ? 0.0f : lgv;
@@ -193,7 +203,7 @@ __global__ void __launch_bounds__(64) bwd_q_generic_kernel(GenArgs a) {
         }
       }
     }
-    if (active) {
+    if (t < BLK) {
       a.delta[qi] = dx;
       T* dqrow = (T*)a.dq + qi * D;
 #pragma unroll
@@ -218,6 +228,7 @@ __global__ void __launch_bounds__(64) bwd_kv_generic_kernel(GenArgs a) {
   const int bb = bhk / a.Hkv, hk = bhk % a.Hkv;
   const int u = threadIdx.x;
   const bool active = u < BLK;
+  const int nb = seq_len_of(a.lens, bb, a.N);
   const T* kbase = (const T*)a.k + ((long long)bb * a.Hkv + hk) * a.N * D;
   const T* vbase = (const T*)a.v + ((long long)bb * a.Hkv + hk) * a.N * D;
   stage_tile<T, D, BLK>(ks, kbase + (long long)j * BLK * D);
@@ -259,7 +270,7 @@ __global__ void __launch_bounds__(64) bwd_kv_generic_kernel(GenArgs a) {
       const long long q0 = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK;
 #pragma unroll 1
       for (int tq = 0; tq < BLK; ++tq) {
-        if (!active || (i == j && u > tq)) continue;
+        if (!active || (i == j && u > tq) || i * BLK + tq >= nb) continue;   // padding queries
         const T* qrow = (const T*)a.q + (q0 + tq) * D;
         const T* drow = (const T*)a.d_o + (q0 + tq) * D;
         float x = 0.0f, dp = 0.0f;
@@ -314,7 +325,9 @@ __global__ void __launch_bounds__(64) ste_dropped_kernel(GenArgs a) {
   const int bb = bs / a.Hs, sh = bs % a.Hs;
   const int hk = sh * a.Gs / a.G;
   const int t = threadIdx.x;
-  const bool active = t < BLK;
+  const int nb = seq_len_of(a.lens, bb, a.N);
+  if (i * BLK >= nb) return;   // no query in this block: its row stays 0 (key pass)
+  const bool active = t < BLK && i * BLK + t < nb;
   const long long row = ((long long)bb * a.Hs + sh) * a.C + i;
   const int cnt = min(a.sel_cnt[row], a.cap);
   const int32_t* sel = a.sel_idx + row * a.cap;
@@ -358,6 +371,7 @@ GenArgs make_args(const Shape& s) {
   a.o_fp32 = s.o_fp32;
   a.outer = s.outer;
   a.hard = s.hard;
+  a.lens = s.lens;
   a.c2 = s.scale * kLog2e;
   a.scale = s.scale;
   return a;

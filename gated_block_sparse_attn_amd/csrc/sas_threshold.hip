@@ -60,7 +60,8 @@ __global__ void __launch_bounds__(256) threshold_kernel(const float* __restrict_
                                                         int32_t* __restrict__ sel_cnt,
                                                         int32_t* __restrict__ d_status,
                                                         long long rows, int C, int K, int cap,
-                                                        int act) {
+                                                        int act, const int32_t* __restrict__ lens,
+                                                        int Hs, int N) {
   extern __shared__ float s_hist[];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -108,11 +109,22 @@ __global__ void __launch_bounds__(256) threshold_kernel(const float* __restrict_
     lrow[m] = val;
   }
 
+  // Variable-length batch: a row past the sequence's last block holds no
+  // query and selects nothing.
+  bool empty = false;
+  if (lens != nullptr) {
+    const int n = min(max(lens[row / ((long long)Hs * C)], 0), N);
+    const int blk = N / C;
+    empty = i >= (n + blk - 1) / blk;
+  }
+
   // Threshold: the K-th largest historical score, found bit by bit from the
   // most significant end (radix select, no sort): keep the largest key T with
   // #{key >= T} >= K.
   float t;
-  if (K >= i) {
+  if (empty) {
+    t = INFINITY;
+  } else if (K >= i) {
     t = -INFINITY;
   } else if (K == 0) {
     t = INFINITY;
@@ -136,7 +148,7 @@ __global__ void __launch_bounds__(256) threshold_kernel(const float* __restrict_
   int base = 0;
   for (int m0 = 0; m0 < i; m0 += 64) {
     const int m = m0 + lane;
-    const bool p = (m < i) && (s[m < i ? m : 0] >= t);
+    const bool p = !empty && (m < i) && (s[m < i ? m : 0] >= t);
     const unsigned long long mask = __ballot(p);
     if (p) {
       const int pos = base + rank_below(mask);
@@ -200,7 +212,8 @@ hipError_t launch_threshold(const Shape& s, const float* scores, float* log_gate
   const size_t lds = (size_t)nw * s.C * sizeof(float);
   const long long grid = (rows + nw - 1) / nw;
   hipLaunchKernelGGL(threshold_kernel, dim3((unsigned)grid), dim3(64 * nw), lds, st, scores,
-                     log_gate, tau, sel_idx, sel_cnt, d_status, rows, s.C, s.K, s.cap, s.act);
+                     log_gate, tau, sel_idx, sel_cnt, d_status, rows, s.C, s.K, s.cap, s.act,
+                     s.lens, s.Hs, s.N);
   return hipGetLastError();
 }
 

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SAS_ABI_VERSION 5
+#define SAS_ABI_VERSION 6
 
 typedef enum sas_dtype {
   SAS_BF16 = 0, /* q/k/v/o/d_o/dq/dk/dv are bfloat16 (fp32 accumulation) */
@@ -133,6 +133,17 @@ typedef struct sas_problem {
                          per-head log gates, App. E); score head s covers
                          query heads s*(Hq/Hs) .. +Hq/Hs-1.  Hs = Hq with
                          G > 1 runs on the vector-ALU path.                  */
+  const int32_t* seq_lens; /* optional DEVICE int32 [B]: valid tokens n_b of each
+                         sequence (variable-length batch in the padded
+                         [.., N, ..] layout; NULL = every sequence has N).
+                         Sequence b has ceil(n_b / b) blocks, the last one
+                         possibly ragged; query rows t >= n_b are padding
+                         (o, lse, dq written as 0; they attend nothing and
+                         contribute no gradient); gate rows i >= ceil(n_b / b)
+                         select nothing (sel_cnt 0, tau +inf; log_gate still
+                         written; dlog_gate and dscores 0).  Values outside
+                         [0, N] are clamped into it.  Runs on the vector-ALU
+                         path.                                                */
 } sas_problem;
 
 /* ABI version of the loaded library (SAS_ABI_VERSION). */

@@ -21,10 +21,12 @@ def log(msg):
 
 
 def problem_of(w: workloads.Workload, K: int, o_dtype: str = "bf16", gate_act: str = "softmax",
-               gate_pos: str = "inner", gate_rank: str = "soft") -> api.Problem:
+               gate_pos: str = "inner", gate_rank: str = "soft", seq_lens=None) -> api.Problem:
+    lens = None if seq_lens is None else \
+        torch.as_tensor(np.asarray(seq_lens), dtype=torch.int32).to("cuda:0")
     return api.Problem(w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.block,
                        K, w.dtype, 0.0, o_dtype if w.dtype == "bf16" else "fp32", gate_act,
-                       gate_pos, gate_rank, w.score_heads)
+                       gate_pos, gate_rank, w.score_heads, lens)
 
 
 def run_gpu(p: api.Problem, inp: dict, cap=None, poison=True, status=None):
@@ -59,9 +61,9 @@ def f32(t: torch.Tensor) -> np.ndarray:
     return t.float().numpy()
 
 
-def check_selection(gpu, scores_np, K, act="softmax"):
+def check_selection(gpu, scores_np, K, act="softmax", seq_lens=None, block=None):
     """Selected sets, counts and thresholds must match the oracle exactly."""
-    lg, tau, sel = oracle.gate_threshold(scores_np, K, act=act)
+    lg, tau, sel = oracle.gate_threshold(scores_np, K, act=act, seq_lens=seq_lens, block=block)
     cnt = sel.sum(-1)
     assert np.array_equal(gpu["sel_cnt"].numpy(), cnt), "selection counts differ"
     assert np.array_equal(gpu["tau"].numpy(), tau), "thresholds differ"
@@ -107,24 +109,27 @@ def compare(name, got, ref, dtype, mask=None):
 
 
 def full_parity(w, K, inp=None, cap=None, o_dtype="bf16", gate_act="softmax", gate_pos="inner",
-                gate_rank="soft"):
-    """Whole-tensor parity of every output (sizes the oracle finishes quickly)."""
-    p = problem_of(w, K, o_dtype, gate_act, gate_pos, gate_rank)
+                gate_rank="soft", seq_lens=None):
+    """Whole-tensor parity of every output (sizes the oracle finishes quickly).
+    ``seq_lens``: valid tokens per sequence (variable-length batch, padded)."""
+    p = problem_of(w, K, o_dtype, gate_act, gate_pos, gate_rank, seq_lens)
     inp = inp or workloads.generate(w)
     gpu = run_gpu(p, inp, cap=cap)
     scores = inp["scores"].numpy()
-    lg, tau, sel = check_selection(gpu, scores, K, act=gate_act)
+    lens = None if seq_lens is None else np.asarray(seq_lens)
+    lg, tau, sel = check_selection(gpu, scores, K, act=gate_act, seq_lens=lens, block=w.block)
     q, k, v, do = (f32(inp[n]) for n in ("q", "k", "v", "do"))
     if gate_rank == "hard_ste":
         # unit gates on the selected blocks; every historical block gets dg
         zero = np.where(np.isfinite(lg), 0.0, lg)
-        o, lse = oracle.forward(q, k, v, zero, sel, w.block)
-        dq, dk, dv, _ = oracle.backward(q, k, v, do, zero, sel, w.block)
-        dlg = oracle.sas_oracle.ste_gate_grad(q, k, v, do, lg, sel, w.block)
+        o, lse = oracle.forward(q, k, v, zero, sel, w.block, seq_lens=lens)
+        dq, dk, dv, _ = oracle.backward(q, k, v, do, zero, sel, w.block, seq_lens=lens)
+        dlg = oracle.sas_oracle.ste_gate_grad(q, k, v, do, lg, sel, w.block, seq_lens=lens)
         dsc = oracle.sas_oracle.dscores_from_dg(dlg, lg)
     else:
-        o, lse = oracle.forward(q, k, v, lg, sel, w.block, gate_pos=gate_pos)
-        dq, dk, dv, dlg = oracle.backward(q, k, v, do, lg, sel, w.block, gate_pos=gate_pos)
+        o, lse = oracle.forward(q, k, v, lg, sel, w.block, gate_pos=gate_pos, seq_lens=lens)
+        dq, dk, dv, dlg = oracle.backward(q, k, v, do, lg, sel, w.block, gate_pos=gate_pos,
+                                          seq_lens=lens)
         dsc = oracle.dscores(dlg, lg, sel, act=gate_act)
     dt = w.dtype
     compare("o", f32(gpu["o"]), o, dt)
@@ -139,6 +144,9 @@ def full_parity(w, K, inp=None, cap=None, o_dtype="bf16", gate_act="softmax", ga
     c = sel.shape[-1]
     hist = np.broadcast_to(np.tril(np.ones((c, c), bool), -1), sel.shape)
     zero_at = ~hist if gate_rank == "hard_ste" else ~sel
+    if lens is not None:   # rows without a query hold no gradient
+        for b in range(sel.shape[0]):
+            zero_at[b, :, oracle.sas_oracle.n_blocks_of(lens[b], w.block):] = True
     assert np.all(gpu["dlog_gate"].numpy()[zero_at] == 0.0)
     return gpu
 

@@ -20,7 +20,7 @@ def lib():
 def prob(**kw):
     base = dict(batch=1, n_q_heads=8, n_kv_heads=2, seq_len=1024, head_dim=128, block_size=64,
                 budget_k=4, dtype=nat.SAS_BF16, o_dtype=nat.SAS_FP32, sm_scale=0.0, gate_act=0,
-                gate_pos=0, gate_rank=0, n_score_heads=0)
+                gate_pos=0, gate_rank=0, n_score_heads=0, seq_lens=None)
     base.update(kw)
     return nat.SasProblem(**base)
 
@@ -59,8 +59,8 @@ def test_library_exports_every_header_symbol():
 
 
 def test_abi_version():
-    assert lib().sas_abi_version() == 5
-    assert api.abi_version() == 5
+    assert lib().sas_abi_version() == 6
+    assert api.abi_version() == 6
 
 
 @pytest.mark.parametrize("kw,code", [

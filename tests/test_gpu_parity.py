@@ -96,6 +96,46 @@ def test_gate_variants_full_parity(case):
     full_parity(w, K, cap=cap, gate_act=act, gate_pos=pos, gate_rank=rank)
 
 
+VARLEN = [
+    # name, B, Hq, Hkv, N, D, blk, K, dtype, seq_lens, gate_act, gate_pos, gate_rank, score_heads
+    ("varlen_bf16_d128_b64", 3, 8, 2, 640, 128, 64, 3, "bf16", (640, 1, 321),
+     "softmax", "inner", "soft", "group"),
+    ("varlen_fp32_d64_b16_empty", 4, 4, 2, 256, 64, 16, 4, "fp32", (0, 17, 256, 100),
+     "softmax", "inner", "soft", "group"),
+    ("varlen_clamped_lengths", 2, 4, 1, 256, 64, 32, 2, "fp32", (-3, 300),
+     "softmax", "inner", "soft", "group"),
+    ("varlen_outer_sigmoid_bf16", 2, 8, 2, 512, 128, 64, 3, "bf16", (449, 130),
+     "sigmoid", "outer", "soft", "group"),
+    ("varlen_heads_hard_ste_fp32", 2, 4, 2, 256, 64, 16, 3, "fp32", (200, 33),
+     "softmax", "inner", "hard_ste", "head"),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=[c[0] for c in VARLEN])
+def test_varlen_full_parity(case):
+    """Variable-length batches in the padded layout: ragged last blocks, a
+    one-token and an empty sequence, lengths outside [0, N] (clamped), with
+    the gate variants."""
+    name, B, Hq, Hkv, N, D, blk, K, dt, lens, act, pos, rank, heads = case
+    log(f"varlen {name} lens={lens}")
+    w = workloads.custom(B, Hq, Hkv, N, D, blk, K, dtype=dt, seed=zlib.crc32(name.encode()) % 1000,
+                         score_std=2.0, score_heads=heads)
+    cap = max(1, min(K, N // blk - 1))
+    # lengths outside [0, N] go to both sides as they are: the oracle's block
+    # count and valid-row count saturate at 0 and N just as the kernels clamp
+    full_parity(w, K, cap=cap, gate_act=act, gate_pos=pos, gate_rank=rank, seq_lens=lens)
+
+
+def test_varlen_full_lengths_match_dense():
+    """seq_lens = N everywhere gives the dense result (same vector-ALU kernels)."""
+    w = workloads.custom(2, 4, 2, 512, 64, 32, 3, dtype="fp32", seed=5, score_std=2.0)
+    inp = workloads.generate(w)
+    dense = run_gpu(problem_of(w, 3), inp)
+    full = run_gpu(problem_of(w, 3, seq_lens=(512, 512)), inp)
+    for n in dense:
+        assert torch.equal(dense[n], full[n]), n
+
+
 def test_tiny_fp32_workload():
     w = workloads.WORKLOADS["tiny_fp32"]
     log("workload tiny_fp32")
