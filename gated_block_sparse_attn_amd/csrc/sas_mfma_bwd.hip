@@ -940,34 +940,53 @@ bwd_dkdv_kernel(BwdArgs a) {
   }
 }
 
+// One workgroup per (column, quarter of its 64 x 128 tile); each lane sums
+// 8 consecutive fp32 of dK and of dV over the column's chunks, in chunk order
+// (deterministic), four chunks' loads in flight at a time.
 __global__ void __launch_bounds__(256) reduce_kernel(BwdArgs a) {
-  const long long col = blockIdx.x;
+  const long long col = blockIdx.x >> 2;
   const int c0 = a.chunkoff[col];
   const int nch = a.chunkoff[col + 1] - c0;
   if (nch <= 1) return;
   const int j = (int)(col % a.C);
   const long long bhk = col / a.C;
   const long long orow = bhk * a.N + (long long)j * BLK;
-  for (int r = 0; r < 4; ++r) {
-    const int e = (threadIdx.x + r * 256) * 8;
-    float sk[8], sv[8];
+  const int e = (threadIdx.x + (blockIdx.x & 3) * 256) * 8;
+  const float* base = a.partial + (long long)c0 * 2 * 8192 + e;
+  f32x4 sk[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+  f32x4 sv[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+  int cc = 0;
+  for (; cc + 4 <= nch; cc += 4) {
+    f32x4 lk[4][2], lv[4][2];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) { sk[x] = 0.0f; sv[x] = 0.0f; }
-    for (int cc = 0; cc < nch; ++cc) {
-      const float* pk = a.partial + (long long)(c0 + cc) * 2 * 8192 + e;
-      const float* pv = pk + 8192;
-#pragma unroll
-      for (int x = 0; x < 8; ++x) { sk[x] += pk[x]; sv[x] += pv[x]; }
+    for (int u = 0; u < 4; ++u) {
+      const float* pk = base + (long long)(cc + u) * 2 * 8192;
+      lk[u][0] = *(const f32x4*)pk;
+      lk[u][1] = *(const f32x4*)(pk + 4);
+      lv[u][0] = *(const f32x4*)(pk + 8192);
+      lv[u][1] = *(const f32x4*)(pk + 8192 + 4);
     }
-    bf16x8 ok, ov;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      ok[x] = (bf16)sk[x];
-      ov[x] = (bf16)sv[x];
-    }
-    *(bf16x8*)(a.dk + orow * HD + e) = ok;
-    *(bf16x8*)(a.dv + orow * HD + e) = ov;
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) { sk[h] += lk[u][h]; sv[h] += lv[u][h]; }
   }
+  for (; cc < nch; ++cc) {
+    const float* pk = base + (long long)cc * 2 * 8192;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      sk[h] += *(const f32x4*)(pk + 4 * h);
+      sv[h] += *(const f32x4*)(pk + 8192 + 4 * h);
+    }
+  }
+  bf16x8 ok, ov;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    ok[x] = (bf16)sk[x >> 2][x & 3];
+    ov[x] = (bf16)sv[x >> 2][x & 3];
+  }
+  *(bf16x8*)(a.dk + orow * HD + e) = ok;
+  *(bf16x8*)(a.dv + orow * HD + e) = ov;
 }
 
 template <int NH>
@@ -1057,7 +1076,7 @@ hipError_t launch_bwd_dkdv_mfma(const Shape& s, const BwdPtrs& p, char* ws,
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)wl.max_chunks), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)a.ncol), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)(a.ncol * 4)), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.dscores == nullptr) return hipSuccess;
   return launch_dscores(s, p.dlog_gate, p.log_gate, p.dscores, st);
