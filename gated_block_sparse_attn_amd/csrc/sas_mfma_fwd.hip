@@ -277,12 +277,14 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
   // P element pair n (n = 0..7) of a unit: P = exp2(c2 s + beta - m), summed
   // into l and packed (hi, and lo when SPLIT) into the B operand of
   // O^T += V^T P^T: element jj -> k-slice jj / 8, word (jj % 8) / 2
+  const bf16x2 ones2 = {(bf16)1.0f, (bf16)1.0f};
   auto p_pair = [&](int n, const f32x16& sc, float off, uint32_t (&pb)[2][4], uint32_t (&pl)[2][4]) {
     const int jj = 2 * n;
     const f32x2 pp = {__builtin_amdgcn_exp2f(fmaf(sc[jj], a.c2, off)),
                       __builtin_amdgcn_exp2f(fmaf(sc[jj + 1], a.c2, off))};
-    lrow += pp[0] + pp[1];
     const bf16x2 hi = __builtin_convertvector(pp, bf16x2);
+    if (SPLIT) lrow += pp[0] + pp[1];
+    else lrow = __builtin_amdgcn_fdot2_f32_bf16(hi, ones2, lrow, false);   // l sums the P that enter O
     uint32_t wh = __builtin_bit_cast(uint32_t, hi);
     pin(wh);
     pb[jj >> 3][(jj & 7) >> 1] = wh;
@@ -349,27 +351,30 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
   // next unit
   float beta_cur = 0.0f;   // gate of tile t
   float beta_v = beta1;    // gate of the tile whose V was copied last (t + 1)
-  auto window = [&](auto kh_tag, auto diag_tag, int t, f32x16& scur, f32x16& snext) {
+  // PAR = t & 1 (a compile-time LDS slot, so the fragment addresses are
+  // loop invariant)
+  auto window = [&](auto kh_tag, auto diag_tag, auto par_tag, int t, f32x16& scur, f32x16& snext) {
     constexpr int KH = decltype(kh_tag)::value;
     constexpr bool DIAG = decltype(diag_tag)::value;
+    constexpr int PAR = decltype(par_tag)::value;
     const bool more = KH == 0 || t + 1 < nt;   // is there a next unit
     if (KH == 0) {
-      copy_v(tile_block(t + 1, beta_v), (t + 1) & 1);
+      copy_v(tile_block(t + 1, beta_v), PAR ^ 1);
     } else {
       float bk;
-      copy_k(tile_block(t + 2, bk), t & 1);
+      copy_k(tile_block(t + 2, bk), PAR);
     }
     const float off = beta_cur - mrow;
     uint32_t pb[2][4], pl[2][4];
     // next unit: (t, 1) reads K_t, (t + 1, 0) reads K_{t+1}
-    const bf16* kn = KH == 0 ? s_k[t & 1] : s_k[(t + 1) & 1];
+    const bf16* kn = KH == 0 ? s_k[PAR] : s_k[PAR ^ 1];
     if (more) {
       scores_with(kn, KH ^ 1, snext, [&](int m) { p_pair(m, scur, off, pb, pl); });
     } else {
 #pragma unroll
       for (int n = 0; n < 8; ++n) p_pair(n, scur, off, pb, pl);
     }
-    pv(s_v[t & 1], KH, pb, pl);
+    pv(s_v[PAR], KH, pb, pl);
     wait_vm_prev<NW>();
     __syncthreads();
     if (more) {
@@ -382,12 +387,21 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
       }
     }
   };
-  window(std::integral_constant<int, 0>{}, std::true_type{}, 0, s0, s1);
-  window(std::integral_constant<int, 1>{}, std::true_type{}, 0, s1, s0);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  window(I0{}, std::true_type{}, I0{}, 0, s0, s1);
+  window(I1{}, std::true_type{}, I0{}, 0, s1, s0);
+  int t = 1;
 #pragma unroll 1
-  for (int t = 1; t < nt; ++t) {
-    window(std::integral_constant<int, 0>{}, std::false_type{}, t, s0, s1);
-    window(std::integral_constant<int, 1>{}, std::false_type{}, t, s1, s0);
+  for (; t + 1 < nt; t += 2) {   // tiles t (odd) and t + 1 (even)
+    window(I0{}, std::false_type{}, I1{}, t, s0, s1);
+    window(I1{}, std::false_type{}, I1{}, t, s1, s0);
+    window(I0{}, std::false_type{}, I0{}, t + 1, s0, s1);
+    window(I1{}, std::false_type{}, I0{}, t + 1, s1, s0);
+  }
+  if (t < nt) {
+    window(I0{}, std::false_type{}, I1{}, t, s0, s1);
+    window(I1{}, std::false_type{}, I1{}, t, s1, s0);
   }
   wait_vm();   // trailing copies
 
