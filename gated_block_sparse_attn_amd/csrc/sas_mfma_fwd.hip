@@ -277,14 +277,12 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
   // P element pair n (n = 0..7) of a unit: P = exp2(c2 s + beta - m), summed
   // into l and packed (hi, and lo when SPLIT) into the B operand of
   // O^T += V^T P^T: element jj -> k-slice jj / 8, word (jj % 8) / 2
-  const bf16x2 ones2 = {(bf16)1.0f, (bf16)1.0f};
   auto p_pair = [&](int n, const f32x16& sc, float off, uint32_t (&pb)[2][4], uint32_t (&pl)[2][4]) {
     const int jj = 2 * n;
     const f32x2 pp = {__builtin_amdgcn_exp2f(fmaf(sc[jj], a.c2, off)),
                       __builtin_amdgcn_exp2f(fmaf(sc[jj + 1], a.c2, off))};
     const bf16x2 hi = __builtin_convertvector(pp, bf16x2);
-    if (SPLIT) lrow += pp[0] + pp[1];
-    else lrow = __builtin_amdgcn_fdot2_f32_bf16(hi, ones2, lrow, false);   // l sums the P that enter O
+    lrow += pp[0] + pp[1];
     uint32_t wh = __builtin_bit_cast(uint32_t, hi);
     pin(wh);
     pb[jj >> 3][(jj & 7) >> 1] = wh;
