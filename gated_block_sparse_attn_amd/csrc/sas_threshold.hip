@@ -9,7 +9,8 @@
 //
 // One wavefront owns one row (b, h_kv, i) of the [C, C] score table: the
 // row's historical scores (m < i) are staged in LDS once and every pass
-// (max, sum, log-gate write, radix select, compaction) reads them from there.
+// (max, sum, log-gate write, radix select, compaction) reads them from there;
+// the radix select keeps a 256-bin histogram per wavefront in LDS.
 // Both kernels are HBM-bound: they read and write the score-table rows once.
 #include <math.h>
 
@@ -62,7 +63,7 @@ __global__ void __launch_bounds__(256) threshold_kernel(const float* __restrict_
                                                         long long rows, int C, int K, int cap,
                                                         int act, const int32_t* __restrict__ lens,
                                                         int Hs, int N) {
-  extern __shared__ float s_hist[];
+  extern __shared__ float s_lds[];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
@@ -70,15 +71,28 @@ __global__ void __launch_bounds__(256) threshold_kernel(const float* __restrict_
   if (row >= rows) return;  // whole wavefront leaves; no workgroup barrier follows
   const int i = (int)(row % C);
   const float* srow = scores + row * (long long)C;
-  float* s = s_hist + (size_t)w * C;
+  float* s = s_lds + (size_t)w * (C + 256);   // this wavefront's row
+  int* hist = (int*)(s + C);                  // and its 256-bin histogram
 
-  // Stage the historical scores; +0.0f turns -0 into +0 so that the integer
-  // keys order exactly like the fp32 comparison used for the selected set.
+  // Stage the historical scores (four loads in flight per lane); +0.0f turns
+  // -0 into +0 so that the integer keys order exactly like the fp32
+  // comparison used for the selected set.
   float mx = -INFINITY;
-  for (int m = lane; m < i; m += 64) {
-    const float x = srow[m] + 0.0f;
-    s[m] = x;
-    mx = fmaxf(mx, x);
+  for (int m0 = 0; m0 < i; m0 += 256) {
+    float x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int m = m0 + u * 64 + lane;
+      x[u] = m < i ? srow[m] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int m = m0 + u * 64 + lane;
+      if (m < i) {
+        s[m] = x[u] + 0.0f;
+        mx = fmaxf(mx, x[u]);
+      }
+    }
   }
   mx = wave_max_f(mx);
 
@@ -118,9 +132,11 @@ __global__ void __launch_bounds__(256) threshold_kernel(const float* __restrict_
     empty = i >= (n + blk - 1) / blk;
   }
 
-  // Threshold: the K-th largest historical score, found bit by bit from the
-  // most significant end (radix select, no sort): keep the largest key T with
-  // #{key >= T} >= K.
+  // Threshold: the K-th largest historical score (radix select over the
+  // order-preserving integer keys, no sort), eight bits per pass from the
+  // most significant end: a 256-bin histogram of the keys that match the
+  // digits found so far, then the digit d where the count of keys with a
+  // larger digit is < krem <= that count plus bin d.
   float t;
   if (empty) {
     t = INFINITY;
@@ -129,16 +145,41 @@ __global__ void __launch_bounds__(256) threshold_kernel(const float* __restrict_
   } else if (K == 0) {
     t = INFINITY;
   } else {
-    uint32_t prefix = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = prefix | (1u << bit);
-      int cnt = 0;
-      for (int m0 = 0; m0 < i; m0 += 64) {
-        const int m = m0 + lane;
-        const bool p = (m < i) && (f2key(s[m < i ? m : 0]) >= cand);
-        cnt += popc64(__ballot(p));
+    uint32_t prefix = 0u, known = 0u;
+    int krem = K;   // rank of the wanted key among those matching prefix
+    for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hist[q * 64 + lane] = 0;
+      for (int m = lane; m < i; m += 64) {
+        const uint32_t key = f2key(s[m]);
+        if ((key & known) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
       }
-      if (cnt >= K) prefix = cand;
+      // lane l holds bins 255 - 4 l - q (q = 0..3): descending digit order
+      int c[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) c[q] = hist[255 - 4 * lane - q];
+      const int local = c[0] + c[1] + c[2] + c[3];
+      int incl = local;   // inclusive scan over the lanes
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      const int excl = incl - local;
+      const bool hit = excl < krem && krem <= incl;
+      int dig = 0, above = excl;
+      if (hit) {
+        int q = 0;
+        while (above + c[q] < krem) above += c[q++];
+        dig = 255 - 4 * lane - q;
+      }
+      const unsigned long long hm = __ballot(hit);
+      const int src = __builtin_ctzll(hm);   // exactly one lane hits (1 <= krem <= count)
+      dig = __shfl(dig, src, 64);
+      above = __shfl(above, src, 64);
+      prefix |= (uint32_t)dig << shift;
+      known |= 255u << shift;
+      krem -= above;
     }
     t = key2f(prefix);
   }
@@ -208,8 +249,8 @@ hipError_t launch_threshold(const Shape& s, const float* scores, float* log_gate
                             int32_t* sel_idx, int32_t* sel_cnt, int32_t* d_status,
                             hipStream_t st) {
   const long long rows = (long long)s.B * s.Hs * s.C;
-  const int nw = (s.C <= 4096) ? 4 : 1;
-  const size_t lds = (size_t)nw * s.C * sizeof(float);
+  const int nw = (s.C <= 2048) ? 4 : 1;   // at most 34 KB of LDS per workgroup (C <= 8192)
+  const size_t lds = (size_t)nw * (s.C + 256) * sizeof(float);
   const long long grid = (rows + nw - 1) / nw;
   hipLaunchKernelGGL(threshold_kernel, dim3((unsigned)grid), dim3(64 * nw), lds, st, scores,
                      log_gate, tau, sel_idx, sel_cnt, d_status, rows, s.C, s.K, s.cap, s.act,

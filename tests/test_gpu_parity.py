@@ -169,14 +169,21 @@ def test_threshold_ties_and_capacity_flag():
     check_selection(gpu, s.numpy(), 2)
 
 
-def test_threshold_matches_oracle_on_long_rows():
-    # 2048 blocks per row (the 128k-token shape) with Gumbel scores
-    w = workloads.custom(1, 4, 2, 2048 * 16, 64, 16, 32, dtype="fp32", seed=11,
+@pytest.mark.parametrize("C,kind", [(2048, "gumbel"), (2600, "gumbel"), (1000, "ties")],
+                         ids=["c2048", "c2600_one_wave_per_group", "c1000_heavy_ties"])
+def test_threshold_matches_oracle_on_long_rows(C, kind):
+    """Long rows: 2048 blocks (the 128k-token shape), 2600 blocks (rows
+    longer than 2048 run one wavefront per workgroup), and scores rounded to
+    multiples of 1/2 (most keys tied, so the radix select's bins hold many
+    equal keys and the ">= tau" sets exceed K)."""
+    w = workloads.custom(1, 4, 2, C * 16, 64, 16, 32, dtype="fp32", seed=11,
                          score_kind="gumbel")
     p = problem_of(w, 32)
     g = torch.Generator().manual_seed(5)
-    u = torch.rand(1, 2, 2048, 2048, generator=g).clamp_(1e-30, 1 - 2 ** -24)
+    u = torch.rand(1, 2, C, C, generator=g).clamp_(1e-30, 1 - 2 ** -24)
     s = -torch.log(-torch.log(u))
+    if kind == "ties":
+        s = torch.floor(s * 2.0) / 2.0
     gpu = {}
     gpu["log_gate"], gpu["tau"], gpu["sel_idx"], gpu["sel_cnt"] = (
         t.cpu() for t in api.gate_threshold(p, s.cuda(), sel_cap=32))
