@@ -542,7 +542,7 @@ __global__ void chunk_scatter_kernel(BwdArgs a) {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int XS_BYTES = 32 * HD * 2;               // 32 staged rows
-constexpr int SLOT_BYTES = XS_BYTES + 256;           // rows + one statistic (64 floats)
+constexpr int SLOT_BYTES = 256 + XS_BYTES;           // one statistic (64 floats), then the rows
 constexpr int Q_SLOTS = 5, O_SLOTS = 3;
 constexpr int QRING = 0;
 constexpr int ORING = QRING + Q_SLOTS * SLOT_BYTES;
@@ -576,11 +576,12 @@ __device__ __forceinline__ int xsw(int r, int c) { return r * HD + ((c ^ slot16(
 //   B: dP_s (matrix core) overlapped with dS_{s-1} (vector ALU), then
 //      dK_{s-1} += Q_{s-1}^T dS_{s-1}.
 // A step's rows reach LDS by asynchronous global -> LDS copies into two rings
-// shared by the pairs: the A waves copy the Q rows (half each) and Delta into
-// a 5-slot ring (step t is read in windows t - 1 .. t + 1), the B waves the dO
-// rows and LSE into a 3-slot ring (read in window t), two windows before
-// first use, spread between the contraction's MFMAs; every wavefront waits for
-// its own copies before the barrier that publishes them.  The Q / dO operand
+// shared by the pairs: the A waves copy the Q rows (half each; key half 0
+// also Delta) into a 5-slot ring (step t is read in windows t - 1 .. t + 1),
+// the B waves the dO rows (and LSE) into a 3-slot ring (read in window t),
+// two windows before first use, spread between the contraction's MFMAs, with
+// one LDS base (M0) per step; every wavefront waits for its own copies before
+// the barrier that publishes them.  The Q / dO operand
 // fragments are read two MFMAs ahead.  B's per-entry dS sums of the two key
 // halves meet in LDS and are added in a fixed order after the loops
 // (deterministic).
@@ -591,11 +592,27 @@ constexpr int GTAB4 = ITAB4 + 2 * kColChunk * 4;             // itab + btab
 constexpr int KV4_LDS = GTAB4 + 2 * kColChunk * 4;           // dLogG partials [key half][entry]
 static_assert(2 * KV4_LDS <= 160 * 1024, "two workgroups per CU");
 
-// Ring barrier: this wavefront's LDS accesses and all but its newest five
-// global -> LDS copies are complete, then s_barrier.  (__syncthreads would
-// also wait for the newest copies, which are meant to stay in flight.)
-__device__ __forceinline__ void ring_barrier5() {
-  __asm__ volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+// Ring barrier: this wavefront's LDS accesses and all but its newest copies
+// (one step's: five for key half 0, four for key half 1) are complete, then
+// s_barrier.  (__syncthreads would also wait for the newest copies, which
+// are meant to stay in flight.)
+__device__ __forceinline__ void ring_barrier(int kh) {
+  if (kh == 0) __asm__ volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else __asm__ volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// LDS address of the next global -> LDS copies (M0); the 1-wait-state
+// hazard before a copy is covered here.
+__device__ __forceinline__ void set_lds_m0(unsigned lds) {
+  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0" :: "s"(__builtin_amdgcn_readfirstlane(lds))
+                   : "memory", "m0");
+}
+// 16 bytes per lane from base + voff + OFF to LDS M0 + OFF + 16 lane (the
+// instruction offset moves both addresses).
+template <int OFF>
+__device__ __forceinline__ void dma16_at(const void* base, unsigned voff) {
+  __asm__ volatile("global_load_lds_dwordx4 %0, %1 offset:%2" :: "v"(voff), "s"(uniform_ptr(base)),
+                   "i"(OFF) : "memory");
 }
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -655,11 +672,13 @@ bwd_dkdv_kernel(BwdArgs a) {
   char* const ring = smem + (role == 0 ? QRING : ORING);
   const bf16* src = role == 0 ? a.q : a.d_o;
   const float* stat = role == 0 ? a.delta : a.lse;
-  unsigned voff[4];   // this lane's 16 bytes of copy q: rows (kh*4 + q)*4 .. +3
+  // this lane's 16 bytes of copy q: rows (kh*4 + q)*4 .. +3, less the
+  // q * 1024 that the instruction offset adds (rows >= 4 q, so >= 0)
+  unsigned voff[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int row = (kh * 4 + q) * 4 + (lane >> 4);
-    voff[q] = (unsigned)(row * HD + (((lane & 15) ^ slot16(row)) << 3)) * 2;
+    voff[q] = (unsigned)(row * HD + (((lane & 15) ^ slot16(row)) << 3)) * 2 - q * 1024;
   }
   const unsigned soff = (unsigned)l32 * 4;
   int ct = 0, ce = 0, chh = 0, cx = 0, cslot = 0;
@@ -677,18 +696,30 @@ bwd_dkdv_kernel(BwdArgs a) {
     }
     return cp;
   };
-  // five copies per step and wave: four 1 KB row groups, and the statistic
+  // copies per step: four 1 KB row groups per wavefront (one M0 for the
+  // four, placed by the instruction offsets), and the statistic (key half 0)
   auto issue = [&](const Copy& cp, int q) {
-    if (q < 4) dma16s(cp.rows, voff[q], cp.lds + (kh * 4 + q) * 1024);
-    else dma4s(cp.st, soff, cp.lds + XS_BYTES);
+    switch (q) {
+      case 0:
+        set_lds_m0(cp.lds + 256 + kh * 4096);
+        dma16_at<0>(cp.rows, voff[0]);
+        break;
+      case 1: dma16_at<1024>(cp.rows, voff[1]); break;
+      case 2: dma16_at<2048>(cp.rows, voff[2]); break;
+      case 3: dma16_at<3072>(cp.rows, voff[3]); break;
+      default:
+        if (kh == 0) dma4s(cp.st, soff, cp.lds);
+        break;
+    }
   };
   auto copy_next = [&]() {
     const Copy cp = prepare();
 #pragma unroll
     for (int q = 0; q < 5; ++q) issue(cp, q);
   };
-  auto qring = [&](int k) -> char* { return smem + QRING + k * SLOT_BYTES; };
-  auto oring = [&](int k) -> char* { return smem + ORING + k * SLOT_BYTES; };
+  // rows of ring slot k (its statistic sits in the 256 bytes before them)
+  auto qring = [&](int k) -> char* { return smem + QRING + k * SLOT_BYTES + 256; };
+  auto oring = [&](int k) -> char* { return smem + ORING + k * SLOT_BYTES + 256; };
   auto inc = [](int k, int m) { return k + 1 == m ? 0 : k + 1; };
 
   f32x16 acc[4];   // A: dV^T, B: dK^T; lane: key kh*32 + l32, dims dt*32 + 8 (jj/4) + 4 g + jj%4
@@ -725,7 +756,7 @@ bwd_dkdv_kernel(BwdArgs a) {
     }
   };
   auto read_stat = [&](const char* sl, float (&st)[16]) {
-    const float* sp = (const float*)(sl + XS_BYTES);
+    const float* sp = (const float*)(sl - 256);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const f32x4 v = *(const f32x4*)(sp + t * 8 + g * 4);
@@ -820,17 +851,17 @@ bwd_dkdv_kernel(BwdArgs a) {
     copy_next();
     copy_next();
     copy_next();
-    ring_barrier5();   // Q of steps 0, 1 landed
+    ring_barrier(kh);   // Q of steps 0, 1 landed
     rows_product_with(qring(0), r0, [](int) {});   // S_0
     int qk = 1, ok = 0;
     const int nd = itab[0] == j ? 2 * G : 0;
 #pragma unroll 1
     for (int s = 0; s < nd; s += 2) {
       window_a(std::true_type{}, std::integral_constant<int, 0>{}, qring(qk), oring(ok), pbuf(0), 0.0f, r0, r1);
-      ring_barrier5();
+      ring_barrier(kh);
       qk = inc(qk, Q_SLOTS); ok = inc(ok, O_SLOTS);
       window_a(std::true_type{}, std::integral_constant<int, 1>{}, qring(qk), oring(ok), pbuf(1), 0.0f, r1, r0);
-      ring_barrier5();
+      ring_barrier(kh);
       qk = inc(qk, Q_SLOTS); ok = inc(ok, O_SLOTS);
     }
     int ent = nd ? 1 : 0, hh = 0;
@@ -838,10 +869,10 @@ bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll 1
     for (int s = nd; s < n; s += 2) {
       window_a(std::false_type{}, std::integral_constant<int, 0>{}, qring(qk), oring(ok), pbuf(0), beta, r0, r1);
-      ring_barrier5();
+      ring_barrier(kh);
       qk = inc(qk, Q_SLOTS); ok = inc(ok, O_SLOTS);
       window_a(std::false_type{}, std::integral_constant<int, 1>{}, qring(qk), oring(ok), pbuf(1), beta, r1, r0);
-      ring_barrier5();
+      ring_barrier(kh);
       qk = inc(qk, Q_SLOTS); ok = inc(ok, O_SLOTS);
       if (++hh == G) {
         hh = 0;
@@ -862,28 +893,28 @@ bwd_dkdv_kernel(BwdArgs a) {
     };
     copy_next();
     copy_next();
-    ring_barrier5();   // dO of step 0 landed
+    ring_barrier(kh);   // dO of step 0 landed
     {
       const char* o0 = oring(0);
       copy_next();
       rows_product_with(o0, r0, [](int) {});   // dP_0
     }
-    ring_barrier5();
+    ring_barrier(kh);
     int ok = 1, qk = 0;
     int s = 1;
 #pragma unroll 1
     for (; s + 1 < n; s += 2) {
       window_b(oring(ok), qring(qk), pbuf(0), r0, r1, gsum);   // step s - 1 is even
-      ring_barrier5();
+      ring_barrier(kh);
       step_done();
       ok = inc(ok, O_SLOTS); qk = inc(qk, Q_SLOTS);
       window_b(oring(ok), qring(qk), pbuf(1), r1, r0, gsum);
-      ring_barrier5();
+      ring_barrier(kh);
       step_done();
       ok = inc(ok, O_SLOTS); qk = inc(qk, Q_SLOTS);
     }
     window_b(oring(ok), qring(qk), pbuf(0), r0, r1, gsum);   // dP_{n-1}; dS / dK of step n - 2
-    ring_barrier5();
+    ring_barrier(kh);
     step_done();
     qk = inc(qk, Q_SLOTS);
     bf16x8 bop[2];
