@@ -742,10 +742,14 @@ bwd_dkdv_kernel(BwdArgs a) {
   };
   // row contraction into the accumulators (8 MFMAs); the transposed
   // fragments are read two MFMAs ahead; after MFMA m the work per_mfma(m)
+  // (raised wave priority: the other wavefront of the SIMD, in its vector
+  // section, then fills the gaps between these MFMAs)
   auto contract = [&](const char* rows, const bf16x8 (&bop)[2], auto&& per_mfma) {
     bf16x8 ta[2];
     ta[0] = tr_frag(rows, 0, 0);
     ta[1] = tr_frag(rows, 0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int dt = m >> 1, sl = m & 1;
@@ -754,6 +758,7 @@ bwd_dkdv_kernel(BwdArgs a) {
       per_mfma(m);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
   auto read_stat = [&](const char* sl, float (&st)[16]) {
     const float* sp = (const float*)(sl - 256);
