@@ -9,25 +9,27 @@
 // the attention matrix; O = acc / l and LSE = m + log l.
 //
 // gfx950 mapping
-//  * One workgroup per (batch, kv head, query block, chunk of query heads);
-//    two wavefronts per head, each owning 32 of its 64 query rows, so the G
-//    heads of a kv group share every K/V tile staged in LDS (GQA reuse
-//    through LDS) and two wavefronts share each SIMD.
+//  * One workgroup per (batch, kv head, query block, chunk of query heads
+//    (2, or 1 for an odd remainder)); two wavefronts per head, each owning
+//    32 of its 64 query rows, so the heads of a chunk share every K/V tile
+//    staged in LDS, two wavefronts share each SIMD and two workgroups each
+//    CU.
 //  * The scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_16x16x32_bf16: in the accumulator layout a lane then holds
-//    one query column and 4 consecutive keys of each 16-key tile, so
-//      - the row max needs only two cross-lane steps (permlane16/32 swaps),
+//    v_mfma_f32_32x32x16_bf16: in the accumulator layout a lane then holds
+//    one query column and 16 keys of each 32-key half tile, so
+//      - the row max needs one cross-lane step (a permlane32 swap),
 //      - the row sum stays per lane until the end,
-//      - the probabilities are already in the B-operand layout of
-//        O^T += V^T P^T (keys permuted consistently on both operands), so P
-//        never goes through LDS.
+//      - the probabilities, packed pairwise to bf16, are already the B
+//        operand of O^T += V^T P^T (keys permuted consistently on both
+//        operands), so P never goes through LDS.
 //  * K and V tiles are copied global -> LDS asynchronously (global_load_lds,
 //    no registers), row-major with an XOR-swizzled 16-byte chunk order.  The
 //    A operand of K Q^T is one 16-byte read; the A operand of V^T P^T (a
 //    column fragment of V) comes from two transposed reads
 //    (ds_read_b64_tr_b16), so V is never transposed in memory.
-//  * Two LDS stages: the next tile's copy is issued before the current
-//    tile's matrix work (one barrier per tile).
+//  * Two LDS stages per tensor, software-pipelined over half tiles (one
+//    barrier per half tile); the tile loop is unrolled by two so each
+//    window's stage is a compile-time constant.
 //  * The online softmax rescales O lazily (only when a row max grows by more
 //    than 2^8) and the diagonal tile is peeled, so the steady-state tile has
 //    no masking and, almost always, no accumulator rescale.
@@ -457,14 +459,13 @@ hipError_t launch_fwd_mfma(const Shape& s, const void* q, const void* k, const v
   a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.G; a.N = s.N; a.C = s.C; a.cap = s.cap;
   a.c2 = s.scale * kLog2e;
   const long long units = (long long)s.B * s.Hkv * s.C;
-  // the G heads of a group are covered by chunks of 4, then 2, then 1 heads
+  // the G heads of a group are covered by chunks of 2 heads, then 1: two
+  // 4-wavefront workgroups per CU drift out of step, so one's barrier and
+  // softmax phases overlap the other's matrix work (a chunk of 4 heads in one
+  // 8-wavefront workgroup shares each K / V tile more widely but was 2.6 %
+  // slower at the 32k shape)
   int h = 0;
   hipError_t e = hipSuccess;
-  if (s.G / 4 > 0) {
-    e = launch_chunks<4>(a, h, s.G / 4, units, st);
-    h += 4 * (s.G / 4);
-    if (e != hipSuccess) return e;
-  }
   if ((s.G - h) / 2 > 0) {
     e = launch_chunks<2>(a, h, (s.G - h) / 2, units, st);
     h += 2 * ((s.G - h) / 2);
