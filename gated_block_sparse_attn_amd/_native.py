@@ -48,7 +48,8 @@ class SasProblem(ctypes.Structure):
                 ("o_dtype", ctypes.c_int32), ("sm_scale", ctypes.c_float),
                 ("gate_act", ctypes.c_int32), ("gate_pos", ctypes.c_int32),
                 ("gate_rank", ctypes.c_int32), ("n_score_heads", ctypes.c_int32),
-                ("seq_lens", ctypes.c_void_p)]
+                ("seq_lens", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
+                ("total_tokens", ctypes.c_int64)]
 
 
 class SasDecodeProblem(ctypes.Structure):

@@ -44,6 +44,12 @@ class Problem:
     # Variable-length batches: optional int32 device tensor [batch] of valid tokens per
     # sequence (padded layout; None: every sequence holds seq_len tokens).
     seq_lens: Optional[torch.Tensor] = dataclasses.field(default=None, compare=False)
+    # Packed variable-length batches: optional int32 device tensor [batch + 1] of
+    # token offsets (q / o / dO / dq [T, Hq, D], k / v / dk / dv [T, Hkv, D],
+    # lse [Hq, T], T = total_tokens; seq_len = the padded extent of the longest
+    # sequence).  Exclusive with seq_lens.
+    cu_seqlens: Optional[torch.Tensor] = dataclasses.field(default=None, compare=False)
+    total_tokens: int = 0
 
     def __post_init__(self):
         if self.dtype == "fp32" and self.o_dtype != "fp32":
@@ -64,13 +70,16 @@ class Problem:
     def c(self) -> SasProblem:
         if self.seq_lens is not None:
             _expect(self.seq_lens, "seq_lens", (self.batch,), torch.int32)
+        if self.cu_seqlens is not None:
+            _expect(self.cu_seqlens, "cu_seqlens", (self.batch + 1,), torch.int32)
         return SasProblem(self.batch, self.n_q_heads, self.n_kv_heads, self.seq_len,
                           self.head_dim, self.block_size, self.budget_k,
                           _native.SAS_BF16 if self.dtype == "bf16" else _native.SAS_FP32,
                           _native.SAS_BF16 if self.o_dtype == "bf16" else _native.SAS_FP32,
                           float(self.sm_scale), _native.GATE_ACTS[self.gate_act],
                           _native.GATE_POS[self.gate_pos], _native.GATE_RANK[self.gate_rank],
-                          self.n_score_heads, _ptr(self.seq_lens))
+                          self.n_score_heads, _ptr(self.seq_lens), _ptr(self.cu_seqlens),
+                          int(self.total_tokens))
 
     def default_cap(self) -> int:
         return max(1, min(self.budget_k, self.n_blocks - 1))
@@ -117,6 +126,11 @@ def _expect(t: torch.Tensor, name: str, shape, dtype):
 def _shapes(p: Problem, cap: int):
     c = p.n_blocks
     hs = p.n_score_heads
+    if p.cu_seqlens is not None:   # packed batch
+        t = p.total_tokens
+        return dict(q=(t, p.n_q_heads, p.head_dim), kv=(t, p.n_kv_heads, p.head_dim),
+                    lse=(p.n_q_heads, t), table=(p.batch, hs, c, c), row=(p.batch, hs, c),
+                    sel=(p.batch, hs, c, cap))
     return dict(q=(p.batch, p.n_q_heads, p.seq_len, p.head_dim),
                 kv=(p.batch, p.n_kv_heads, p.seq_len, p.head_dim),
                 lse=(p.batch, p.n_q_heads, p.seq_len),

@@ -62,6 +62,14 @@ int32_t validate(const sas_problem* p, int32_t sel_cap, bool need_cap, sas::Shap
       p->n_score_heads != p->n_q_heads)
     return fail(SAS_E_INVALID, "n_score_heads %d must be 0, n_kv_heads or n_q_heads",
                 p->n_score_heads);
+  if (p->cu_seqlens != nullptr) {
+    if (p->seq_lens != nullptr)
+      return fail(SAS_E_INVALID, "seq_lens and cu_seqlens are exclusive (packed batches take "
+                  "their lengths from cu_seqlens)");
+    if (p->total_tokens < 1 || p->total_tokens > (long long)p->batch * p->seq_len)
+      return fail(SAS_E_INVALID, "total_tokens %lld must lie in [1, batch * seq_len = %lld]",
+                  (long long)p->total_tokens, (long long)p->batch * p->seq_len);
+  }
   if (p->gate_rank != SAS_GATE_SOFT && p->gate_rank != SAS_GATE_HARD_STE)
     return fail(SAS_E_INVALID, "gate_rank %d is not a sas_gate_rank", p->gate_rank);
   if (p->gate_rank == SAS_GATE_HARD_STE &&
@@ -103,6 +111,8 @@ int32_t validate(const sas_problem* p, int32_t sel_cap, bool need_cap, sas::Shap
   s->hard = p->gate_rank == SAS_GATE_HARD_STE;
   s->Hs = p->n_score_heads == 0 ? p->n_kv_heads : p->n_score_heads;
   s->lens = p->seq_lens;
+  s->cu = p->cu_seqlens;
+  s->T = p->cu_seqlens != nullptr ? (long long)p->total_tokens : 0;
   return SAS_OK;
 }
 
@@ -114,7 +124,7 @@ namespace sas {
 
 bool mfma_path(const Shape& s) {
   return !s.fp32 && s.D == 128 && s.blk == 64 && !s.outer && !s.hard && s.Hs == s.Hkv &&
-         s.lens == nullptr;
+         s.lens == nullptr && s.cu == nullptr;
 }
 
 BwdWorkspace bwd_workspace_layout(const Shape& s) {

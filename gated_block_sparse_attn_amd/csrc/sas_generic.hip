@@ -50,19 +50,55 @@ struct GenArgs {
   int outer;    // gates scale the value rows after the softmax (else log g bias)
   int hard;     // hard Top-K gates (straight-through estimator): unit gates
   const int32_t* lens;   // valid tokens per sequence (nullptr: all N)
+  const int32_t* cu;     // packed layout: sequence b holds tokens cu[b] .. cu[b+1]-1
+                         // of [T, H, D] tensors (nullptr: padded [B, H, N, D])
+  long long T;           // packed layout: total tokens
   float c2;     // sm_scale * log2(e)
   float scale;  // sm_scale
 };
 
-// Valid tokens of sequence b (variable-length batches; clamped into [0, N]).
-__device__ __forceinline__ int seq_len_of(const int32_t* lens, int b, int N) {
-  return lens == nullptr ? N : min(max(lens[b], 0), N);
+// First token (packed layout) and number of valid tokens of sequence b,
+// clamped so that every row stays inside the tensors: 0 <= start,
+// start + n <= T, 0 <= n <= N.
+struct Seq {
+  long long start;
+  int n;
+};
+__device__ __forceinline__ Seq seq_of(const GenArgs& a, int b) {
+  if (a.cu != nullptr) {
+    const long long s0 = min(max((long long)a.cu[b], 0LL), a.T);
+    const long long s1 = min(max((long long)a.cu[b + 1], s0), a.T);
+    return {s0, (int)min(s1 - s0, (long long)a.N)};
+  }
+  return {0, a.lens == nullptr ? a.N : min(max(a.lens[b], 0), a.N)};
+}
+// Row (in rows of D elements) of token n of sequence b, head h of H heads:
+// padded [B, H, N, D] or packed [T, H, D].
+__device__ __forceinline__ long long row_of(const GenArgs& a, int b, const Seq& sq, int h, int H,
+                                            int n) {
+  return a.cu != nullptr ? (sq.start + n) * H + h : ((long long)b * H + h) * a.N + n;
+}
+// Index of token n of sequence b, query head h, in LSE and Delta: padded
+// [B, Hq, N] or packed [Hq, T].
+__device__ __forceinline__ long long stat_of(const GenArgs& a, int b, const Seq& sq, int h, int n) {
+  return a.cu != nullptr ? (long long)h * a.T + sq.start + n : ((long long)b * a.Hq + h) * a.N + n;
 }
 
-// Stage rows [row0, row0 + BLK) of a [N, D] matrix into LDS as fp32.
+// Stage the BLK rows of key block kb of (sequence b, kv head hk) of a K or V
+// tensor into LDS as fp32.  In the packed layout rows past the sequence's
+// end read as zero (they belong to the next sequence or lie past the tensor);
+// they are never attended.
 template <typename T, int D, int BLK>
-__device__ __forceinline__ void stage_tile(float* dst, const T* src) {
-  for (int e = threadIdx.x; e < BLK * D; e += blockDim.x) dst[e] = ld(src + e);
+__device__ __forceinline__ void stage_block(float* dst, const void* base, const GenArgs& a, int b,
+                                            const Seq& sq, int hk, int kb) {
+  const bool packed = a.cu != nullptr;
+  const T* src = (const T*)base + row_of(a, b, sq, hk, a.Hkv, kb * BLK) * D;
+  const long long stride = packed ? (long long)a.Hkv * D : D;   // elements from token to token
+  const int nvalid = packed ? min(BLK, max(sq.n - kb * BLK, 0)) : BLK;
+  for (int e = threadIdx.x; e < BLK * D; e += blockDim.x) {
+    const int r = e / D, c = e - r * D;
+    dst[e] = r < nvalid ? ld(src + r * stride + c) : 0.0f;
+  }
 }
 
 template <typename T, int D, int BLK>
@@ -74,15 +110,15 @@ __global__ void __launch_bounds__(64) fwd_generic_kernel(GenArgs a) {
   const int bh = blockIdx.y;
   const int bb = bh / a.Hq, h = bh % a.Hq, hk = h / a.G;
   const int t = threadIdx.x;
-  const int nb = seq_len_of(a.lens, bb, a.N);
+  const Seq sq = seq_of(a, bb);
+  const int nb = sq.n;
   const bool active = t < BLK && i * BLK + t < nb;   // padding rows stay inactive
   const bool any = i * BLK < nb;                      // block holds a valid row (uniform)
   const long long row = ((long long)bb * a.Hs + h / a.Gs) * a.C + i;   // this head's gate row
   const int cnt = min(a.sel_cnt[row], a.cap);
   const int32_t* sel = a.sel_idx + row * a.cap;
-  const T* qrow = (const T*)a.q + (((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + t) * D;
-  const T* kbase = (const T*)a.k + ((long long)bb * a.Hkv + hk) * a.N * D;
-  const T* vbase = (const T*)a.v + ((long long)bb * a.Hkv + hk) * a.N * D;
+  const long long qr = row_of(a, bb, sq, h, a.Hq, i * BLK + t);   // dereferenced when active
+  const T* qrow = (const T*)a.q + qr * D;
 
   float q[D], acc[D];
 #pragma unroll
@@ -97,8 +133,8 @@ __global__ void __launch_bounds__(64) fwd_generic_kernel(GenArgs a) {
     const float beta = a.outer ? 0.0f : lgv;           // bias of the logits
     const float gv = a.outer ? exp2f(lgv) : 1.0f;      // factor of the value rows
     __syncthreads();
-    stage_tile<T, D, BLK>(ks, kbase + (long long)kb * BLK * D);
-    stage_tile<T, D, BLK>(vs, vbase + (long long)kb * BLK * D);
+    stage_block<T, D, BLK>(ks, a.k, a, bb, sq, hk, kb);
+    stage_block<T, D, BLK>(vs, a.v, a, bb, sq, hk, kb);
     __syncthreads();
     if (active) {
       // per-key online softmax update (this path favours simplicity)
@@ -119,19 +155,20 @@ __global__ void __launch_bounds__(64) fwd_generic_kernel(GenArgs a) {
       }
     }
   }
-  if (t < BLK) {   // padding rows: o = 0, lse = 0
-    const long long qi = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + t;
+  // padded layout: padding rows get o = 0, lse = 0; packed: only valid rows
+  // exist (the rows after a sequence belong to the next one)
+  if (a.cu != nullptr ? active : t < BLK) {
     const float inv = active ? 1.0f / l : 0.0f;
     if (a.o_fp32) {
-      float* orow = (float*)a.out + qi * D;
+      float* orow = (float*)a.out + qr * D;
 #pragma unroll
       for (int d = 0; d < D; ++d) orow[d] = acc[d] * inv;
     } else {
-      T* orow = (T*)a.out + qi * D;
+      T* orow = (T*)a.out + qr * D;
 #pragma unroll
       for (int d = 0; d < D; ++d) st(orow + d, acc[d] * inv);
     }
-    a.lse_out[qi] = active ? (m + log2f(l)) * kLn2 : 0.0f;
+    a.lse_out[stat_of(a, bb, sq, h, i * BLK + t)] = active ? (m + log2f(l)) * kLn2 : 0.0f;
   }
 }
 
@@ -145,32 +182,32 @@ __global__ void __launch_bounds__(64) bwd_q_generic_kernel(GenArgs a) {
   const int bhk = blockIdx.y;
   const int bb = bhk / a.Hkv, hk = bhk % a.Hkv;
   const int t = threadIdx.x;
-  const int nb = seq_len_of(a.lens, bb, a.N);
+  const Seq sq = seq_of(a, bb);
+  const int nb = sq.n;
   const bool active = t < BLK && i * BLK + t < nb;   // padding rows: dq = 0, Delta = 0
   const bool any = i * BLK < nb;
-  const T* kbase = (const T*)a.k + ((long long)bb * a.Hkv + hk) * a.N * D;
-  const T* vbase = (const T*)a.v + ((long long)bb * a.Hkv + hk) * a.N * D;
 
   for (int hl = 0; hl < a.G; ++hl) {
     const int h = hk * a.G + hl;
     const long long row = ((long long)bb * a.Hs + h / a.Gs) * a.C + i;   // this head's gate row
     const int cnt = min(a.sel_cnt[row], a.cap);
     const int32_t* sel = a.sel_idx + row * a.cap;
-    const long long qi = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + t;
+    const long long qr = row_of(a, bb, sq, h, a.Hq, i * BLK + t);   // q / o / dO / dq row
+    const long long qs = stat_of(a, bb, sq, h, i * BLK + t);        // LSE / Delta entry
     float q[D], dov[D], dq[D];
     float delta = 0.0f, lse2 = 0.0f, dx = 0.0f;
     if (active) {
-      const T* qrow = (const T*)a.q + qi * D;
-      const T* drow = (const T*)a.d_o + qi * D;
+      const T* qrow = (const T*)a.q + qr * D;
+      const T* drow = (const T*)a.d_o + qr * D;
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         q[d] = ld(qrow + d);
         dov[d] = ld(drow + d);
-        const float od = a.o_fp32 ? ((const float*)a.o)[qi * D + d] : ld((const T*)a.o + qi * D + d);
+        const float od = a.o_fp32 ? ((const float*)a.o)[qr * D + d] : ld((const T*)a.o + qr * D + d);
         delta += od * dov[d];
         dq[d] = 0.0f;
       }
-      lse2 = a.lse[qi] * kLog2e;
+      lse2 = a.lse[qs] * kLog2e;
     } else {
 #pragma unroll
       for (int d = 0; d < D; ++d) { q[d] = 0.0f; dov[d] = 0.0f; dq[d] = 0.0f; }
@@ -181,8 +218,8 @@ __global__ void __launch_bounds__(64) bwd_q_generic_kernel(GenArgs a) {
       const float beta = a.outer ? 0.0f : lgv;
       const float gv = a.outer ? exp2f(lgv) : 1.0f;   // outer: dP = g dO . v
       __syncthreads();
-      stage_tile<T, D, BLK>(ks, kbase + (long long)kb * BLK * D);
-      stage_tile<T, D, BLK>(vs, vbase + (long long)kb * BLK * D);
+      stage_block<T, D, BLK>(ks, a.k, a, bb, sq, hk, kb);
+      stage_block<T, D, BLK>(vs, a.v, a, bb, sq, hk, kb);
       __syncthreads();
       if (active) {
 #pragma unroll 1
@@ -203,9 +240,9 @@ __global__ void __launch_bounds__(64) bwd_q_generic_kernel(GenArgs a) {
         }
       }
     }
-    if (t < BLK) {
-      a.delta[qi] = dx;
-      T* dqrow = (T*)a.dq + qi * D;
+    if (a.cu != nullptr ? active : t < BLK) {
+      a.delta[qs] = dx;
+      T* dqrow = (T*)a.dq + qr * D;
 #pragma unroll
       for (int d = 0; d < D; ++d) st(dqrow + d, dq[d] * a.scale);
     }
@@ -228,11 +265,10 @@ __global__ void __launch_bounds__(64) bwd_kv_generic_kernel(GenArgs a) {
   const int bb = bhk / a.Hkv, hk = bhk % a.Hkv;
   const int u = threadIdx.x;
   const bool active = u < BLK;
-  const int nb = seq_len_of(a.lens, bb, a.N);
-  const T* kbase = (const T*)a.k + ((long long)bb * a.Hkv + hk) * a.N * D;
-  const T* vbase = (const T*)a.v + ((long long)bb * a.Hkv + hk) * a.N * D;
-  stage_tile<T, D, BLK>(ks, kbase + (long long)j * BLK * D);
-  stage_tile<T, D, BLK>(vs, vbase + (long long)j * BLK * D);
+  const Seq sq = seq_of(a, bb);
+  const int nb = sq.n;
+  stage_block<T, D, BLK>(ks, a.k, a, bb, sq, hk, j);
+  stage_block<T, D, BLK>(vs, a.v, a, bb, sq, hk, j);
   __syncthreads();
   float dk[D], dv[D];
 #pragma unroll
@@ -267,12 +303,13 @@ __global__ void __launch_bounds__(64) bwd_kv_generic_kernel(GenArgs a) {
     float gsum = 0.0f;
     for (int hl = 0; hl < a.Gs; ++hl) {
       const int h = (hk * ns + si) * a.Gs + hl;
-      const long long q0 = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK;
 #pragma unroll 1
       for (int tq = 0; tq < BLK; ++tq) {
         if (!active || (i == j && u > tq) || i * BLK + tq >= nb) continue;   // padding queries
-        const T* qrow = (const T*)a.q + (q0 + tq) * D;
-        const T* drow = (const T*)a.d_o + (q0 + tq) * D;
+        const long long qr = row_of(a, bb, sq, h, a.Hq, i * BLK + tq);
+        const long long qs = stat_of(a, bb, sq, h, i * BLK + tq);
+        const T* qrow = (const T*)a.q + qr * D;
+        const T* drow = (const T*)a.d_o + qr * D;
         float x = 0.0f, dp = 0.0f;
 #pragma unroll
         for (int d = 0; d < D; ++d) {
@@ -280,8 +317,8 @@ __global__ void __launch_bounds__(64) bwd_kv_generic_kernel(GenArgs a) {
           dp += ld(drow + d) * vs[u * D + d];
         }
         dp *= gv;
-        const float p = exp2f(x * a.c2 + beta - a.lse[q0 + tq] * kLog2e);
-        const float ds = p * (dp - a.delta[q0 + tq]);
+        const float p = exp2f(x * a.c2 + beta - a.lse[qs] * kLog2e);
+        const float ds = p * (dp - a.delta[qs]);
         gsum += a.outer ? p * dp : ds;
         const float pg = p * gv;
 #pragma unroll
@@ -296,8 +333,10 @@ __global__ void __launch_bounds__(64) bwd_kv_generic_kernel(GenArgs a) {
       if (u == 0) a.dlg[(rowbase + i) * a.C + j] = gsum;
     }
   }
-  if (active) {
-    const long long r = ((long long)bb * a.Hkv + hk) * a.N + (long long)j * BLK + u;
+  // padded layout: every row of the block (padding keys get 0); packed: only
+  // the sequence's own rows
+  if (active && (a.cu == nullptr || j * BLK + u < nb)) {
+    const long long r = row_of(a, bb, sq, hk, a.Hkv, j * BLK + u);
     T* dkrow = (T*)a.dk + r * D;
     T* dvrow = (T*)a.dv + r * D;
 #pragma unroll
@@ -325,30 +364,31 @@ __global__ void __launch_bounds__(64) ste_dropped_kernel(GenArgs a) {
   const int bb = bs / a.Hs, sh = bs % a.Hs;
   const int hk = sh * a.Gs / a.G;
   const int t = threadIdx.x;
-  const int nb = seq_len_of(a.lens, bb, a.N);
+  const Seq sq = seq_of(a, bb);
+  const int nb = sq.n;
   if (i * BLK >= nb) return;   // no query in this block: its row stays 0 (key pass)
   const bool active = t < BLK && i * BLK + t < nb;
   const long long row = ((long long)bb * a.Hs + sh) * a.C + i;
   const int cnt = min(a.sel_cnt[row], a.cap);
   const int32_t* sel = a.sel_idx + row * a.cap;
-  const T* kbase = (const T*)a.k + ((long long)bb * a.Hkv + hk) * a.N * D;
-  const T* vbase = (const T*)a.v + ((long long)bb * a.Hkv + hk) * a.N * D;
   int e = 0;
   for (int m = 0; m < i; ++m) {
     while (e < cnt && sel[e] < m) ++e;
     if (e < cnt && sel[e] == m) continue;   // selected: its dS sum comes from the kv pass
     __syncthreads();
-    stage_tile<T, D, BLK>(ks, kbase + (long long)m * BLK * D);
-    stage_tile<T, D, BLK>(vs, vbase + (long long)m * BLK * D);
+    stage_block<T, D, BLK>(ks, a.k, a, bb, sq, hk, m);
+    stage_block<T, D, BLK>(vs, a.v, a, bb, sq, hk, m);
     __syncthreads();
     float acc = 0.0f;
     for (int hl = 0; hl < a.Gs; ++hl) {
-      const long long qi = ((long long)bb * a.Hq + sh * a.Gs + hl) * a.N + (long long)i * BLK + t;
       if (!active) continue;
-      const T* qrow = (const T*)a.q + qi * D;
-      const T* drow = (const T*)a.d_o + qi * D;
-      const float lse2 = a.lse[qi] * kLog2e;
-      const float delta = a.delta[qi];
+      const int h = sh * a.Gs + hl;
+      const long long qr = row_of(a, bb, sq, h, a.Hq, i * BLK + t);
+      const long long qs = stat_of(a, bb, sq, h, i * BLK + t);
+      const T* qrow = (const T*)a.q + qr * D;
+      const T* drow = (const T*)a.d_o + qr * D;
+      const float lse2 = a.lse[qs] * kLog2e;
+      const float delta = a.delta[qs];
 #pragma unroll 1
       for (int u = 0; u < BLK; ++u) {
         float x = 0.0f, dp = 0.0f;
@@ -372,6 +412,8 @@ GenArgs make_args(const Shape& s) {
   a.outer = s.outer;
   a.hard = s.hard;
   a.lens = s.lens;
+  a.cu = s.cu;
+  a.T = s.T;
   a.c2 = s.scale * kLog2e;
   a.scale = s.scale;
   return a;

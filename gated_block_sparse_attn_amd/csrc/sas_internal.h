@@ -25,6 +25,8 @@ struct Shape {
   int B, Hq, Hkv, G, N, D, blk, C, K, cap;
   int Hs;            // score heads: rows of the gate tables per batch (Hkv or Hq)
   const int32_t* lens;  // device [B] valid tokens per sequence, or nullptr
+  const int32_t* cu;    // device [B + 1] token offsets of a packed batch, or nullptr
+  long long T;          // packed batch: total tokens
   int fp32;          // 1: tensors are float32, 0: bfloat16
   int o_fp32;        // 1: the forward output o is float32
   float scale;       // sm_scale (already defaulted)

@@ -62,7 +62,8 @@ __global__ void __launch_bounds__(256) threshold_kernel(const float* __restrict_
                                                         int32_t* __restrict__ d_status,
                                                         long long rows, int C, int K, int cap,
                                                         int act, const int32_t* __restrict__ lens,
-                                                        int Hs, int N) {
+                                                        const int32_t* __restrict__ cu,
+                                                        long long T, int Hs, int N) {
   extern __shared__ float s_lds[];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -126,8 +127,16 @@ __global__ void __launch_bounds__(256) threshold_kernel(const float* __restrict_
   // Variable-length batch: a row past the sequence's last block holds no
   // query and selects nothing.
   bool empty = false;
-  if (lens != nullptr) {
-    const int n = min(max(lens[row / ((long long)Hs * C)], 0), N);
+  if (lens != nullptr || cu != nullptr) {
+    const int b = (int)(row / ((long long)Hs * C));
+    int n;
+    if (cu != nullptr) {   // packed batch: offsets clamped into [0, T] like the attention kernels
+      const long long s0 = min(max((long long)cu[b], 0LL), T);
+      const long long s1 = min(max((long long)cu[b + 1], s0), T);
+      n = (int)min(s1 - s0, (long long)N);
+    } else {
+      n = min(max(lens[b], 0), N);
+    }
     const int blk = N / C;
     empty = i >= (n + blk - 1) / blk;
   }
@@ -254,7 +263,7 @@ hipError_t launch_threshold(const Shape& s, const float* scores, float* log_gate
   const long long grid = (rows + nw - 1) / nw;
   hipLaunchKernelGGL(threshold_kernel, dim3((unsigned)grid), dim3(64 * nw), lds, st, scores,
                      log_gate, tau, sel_idx, sel_cnt, d_status, rows, s.C, s.K, s.cap, s.act,
-                     s.lens, s.Hs, s.N);
+                     s.lens, s.cu, s.T, s.Hs, s.N);
   return hipGetLastError();
 }
 

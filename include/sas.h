@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SAS_ABI_VERSION 6
+#define SAS_ABI_VERSION 7
 
 typedef enum sas_dtype {
   SAS_BF16 = 0, /* q/k/v/o/d_o/dq/dk/dv are bfloat16 (fp32 accumulation) */
@@ -144,6 +144,22 @@ typedef struct sas_problem {
                          written; dlog_gate and dscores 0).  Values outside
                          [0, N] are clamped into it.  Runs on the vector-ALU
                          path.                                                */
+  const int32_t* cu_seqlens; /* optional DEVICE int32 [B + 1]: packed batch
+                         (the cu_seqlens convention of varlen attention):
+                         sequence b holds tokens cu_seqlens[b] ..
+                         cu_seqlens[b+1]-1 of tensors laid out
+                         q, o, dO, dq [T, Hq, D]; k, v, dk, dv [T, Hkv, D];
+                         lse [Hq, T] (T = total_tokens); seq_len is then
+                         the longest sequence's padded extent N (a multiple
+                         of block_size; gate tables stay [B, Hs, C, C] with
+                         C = N / block_size).  Blocks, ragged last blocks
+                         and empty gate rows as for seq_lens; rows of
+                         other sequences are never read as keys nor
+                         written.  Offsets are clamped into [0, T] and
+                         lengths into [0, N].  Exclusive with seq_lens;
+                         vector-ALU path.                                     */
+  int64_t total_tokens; /* T: rows per head of the packed tensors, in
+                         [1, B * N] (ignored without cu_seqlens)              */
 } sas_problem;
 
 /* ABI version of the loaded library (SAS_ABI_VERSION). */

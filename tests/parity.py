@@ -193,3 +193,102 @@ def sampled_parity(w, K, n_units=12, n_kv_blocks=6, inp=None, seed=7):
         compare(f"dk{j}", gk[b, hk, j * blk:(j + 1) * blk], dkj, dt)
         compare(f"dv{j}", gv[b, hk, j * blk:(j + 1) * blk], dvj, dt)
     return gpu
+
+
+# --------------------------------------------------------------------------
+# packed variable-length batches (cu_seqlens layout)
+# --------------------------------------------------------------------------
+
+def pack(x: torch.Tensor, lens) -> torch.Tensor:
+    """[B, H, N, D] -> [T, H, D]: the first lens[b] rows of each sequence,
+    sequence after sequence."""
+    return torch.cat([x[b, :, :n].transpose(0, 1) for b, n in enumerate(lens)], dim=0).contiguous()
+
+
+def unpack(x: np.ndarray, lens, n_pad: int) -> np.ndarray:
+    """[T, H, D] -> [B, H, N, D] (rows past each length are 0)."""
+    t, h, d = x.shape
+    out = np.zeros((len(lens), h, n_pad, d), dtype=x.dtype)
+    off = 0
+    for b, n in enumerate(lens):
+        out[b, :, :n] = np.transpose(x[off:off + n], (1, 0, 2))
+        off += n
+    return out
+
+
+def unpack_stat(x: np.ndarray, lens, n_pad: int) -> np.ndarray:
+    """[H, T] -> [B, H, N]."""
+    h, t = x.shape
+    out = np.zeros((len(lens), h, n_pad), dtype=x.dtype)
+    off = 0
+    for b, n in enumerate(lens):
+        out[b, :, :n] = x[:, off:off + n]
+        off += n
+    return out
+
+
+def run_gpu_packed(w, K, inp, lens, cap, gate_act="softmax", gate_pos="inner", gate_rank="soft",
+                   o_dtype="bf16"):
+    """threshold -> forward -> backward of the packed batch on cuda:0 (NaN-prefilled outputs);
+    returns host tensors in the packed layout."""
+    dev = torch.device("cuda:0")
+    lens = [int(n) for n in lens]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+    t = int(sum(lens))
+    p = api.Problem(w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.block, K,
+                    w.dtype, 0.0, o_dtype if w.dtype == "bf16" else "fp32", gate_act, gate_pos,
+                    gate_rank, w.score_heads, None, cu, t)
+    q, k, v, do = (pack(inp[n], lens).to(dev) for n in ("q", "k", "v", "do"))
+    scores = inp["scores"].to(dev)
+    lg, tau, sel_idx, sel_cnt = api.gate_threshold(p, scores, sel_cap=cap)
+    o = torch.full(q.shape, float("nan"), dtype=p.torch_o_dtype, device=dev)
+    lse = torch.full((w.n_q_heads, t), float("nan"), dtype=torch.float32, device=dev)
+    api.gated_attn_fwd(p, q, k, v, lg, sel_idx, sel_cnt, o=o, lse=lse)
+    outs = dict(dq=torch.full_like(q, float("nan")), dk=torch.full_like(k, float("nan")),
+                dv=torch.full_like(v, float("nan")), dlog_gate=torch.full_like(lg, float("nan")),
+                dscores=torch.full_like(lg, float("nan")))
+    dq, dk, dv, dlg, dsc = api.gated_attn_bwd(p, q, k, v, o, do, lse, lg, sel_idx, sel_cnt,
+                                              outputs=outs)
+    torch.cuda.synchronize()
+    res = dict(log_gate=lg, tau=tau, sel_idx=sel_idx, sel_cnt=sel_cnt, o=o, lse=lse, dq=dq,
+               dk=dk, dv=dv, dlog_gate=dlg, dscores=dsc)
+    return {n: x.cpu() for n, x in res.items()}
+
+
+def packed_parity(w, K, lens, cap=None, gate_act="softmax", gate_pos="inner", gate_rank="soft"):
+    """Packed batch against the oracle run on the padded equivalent (seq_lens):
+    every output row of the packed tensors is compared (each packed row is a
+    valid row of its sequence)."""
+    inp = workloads.generate(w)
+    gpu = run_gpu_packed(w, K, inp, lens, cap, gate_act, gate_pos, gate_rank)
+    lens_np = np.asarray(lens)
+    scores = inp["scores"].numpy()
+    lg, tau, sel = check_selection(gpu, scores, K, act=gate_act, seq_lens=lens_np, block=w.block)
+    q, k, v, do = (f32(inp[n]) for n in ("q", "k", "v", "do"))
+    if gate_rank == "hard_ste":
+        zero = np.where(np.isfinite(lg), 0.0, lg)
+        o, lse = oracle.forward(q, k, v, zero, sel, w.block, seq_lens=lens_np)
+        dq, dk, dv, _ = oracle.backward(q, k, v, do, zero, sel, w.block, seq_lens=lens_np)
+        dlg = oracle.sas_oracle.ste_gate_grad(q, k, v, do, lg, sel, w.block, seq_lens=lens_np)
+        dsc = oracle.sas_oracle.dscores_from_dg(dlg, lg)
+    else:
+        o, lse = oracle.forward(q, k, v, lg, sel, w.block, gate_pos=gate_pos, seq_lens=lens_np)
+        dq, dk, dv, dlg = oracle.backward(q, k, v, do, lg, sel, w.block, gate_pos=gate_pos,
+                                          seq_lens=lens_np)
+        dsc = oracle.dscores(dlg, lg, sel, act=gate_act)
+    n_pad = w.seq_len
+    valid = np.zeros((w.batch, 1, n_pad, 1), dtype=bool)
+    for b, n in enumerate(lens):
+        valid[b, :, :n] = True
+    vq = np.broadcast_to(valid, (w.batch, w.n_q_heads, n_pad, w.head_dim))
+    vk = np.broadcast_to(valid, (w.batch, w.n_kv_heads, n_pad, w.head_dim))
+    vs = np.broadcast_to(valid[..., 0], (w.batch, w.n_q_heads, n_pad))
+    dt = w.dtype
+    compare("o", unpack(f32(gpu["o"]), lens, n_pad), o, dt, mask=vq)
+    compare("lse", unpack_stat(gpu["lse"].numpy(), lens, n_pad), lse, dt, mask=vs)
+    compare("dq", unpack(f32(gpu["dq"]), lens, n_pad), dq, dt, mask=vq)
+    compare("dk", unpack(f32(gpu["dk"]), lens, n_pad), dk, dt, mask=vk)
+    compare("dv", unpack(f32(gpu["dv"]), lens, n_pad), dv, dt, mask=vk)
+    compare("dlog_gate", gpu["dlog_gate"].numpy(), dlg, dt)
+    compare("dscores", gpu["dscores"].numpy(), dsc, dt)
+    return gpu

@@ -20,7 +20,8 @@ def lib():
 def prob(**kw):
     base = dict(batch=1, n_q_heads=8, n_kv_heads=2, seq_len=1024, head_dim=128, block_size=64,
                 budget_k=4, dtype=nat.SAS_BF16, o_dtype=nat.SAS_FP32, sm_scale=0.0, gate_act=0,
-                gate_pos=0, gate_rank=0, n_score_heads=0, seq_lens=None)
+                gate_pos=0, gate_rank=0, n_score_heads=0, seq_lens=None, cu_seqlens=None,
+                total_tokens=0)
     base.update(kw)
     return nat.SasProblem(**base)
 
@@ -59,8 +60,8 @@ def test_library_exports_every_header_symbol():
 
 
 def test_abi_version():
-    assert lib().sas_abi_version() == 6
-    assert api.abi_version() == 6
+    assert lib().sas_abi_version() == 7
+    assert api.abi_version() == 7
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -81,6 +82,10 @@ def test_abi_version():
     (dict(block_size=128, seq_len=1024), nat.SAS_E_UNSUPPORTED),
     (dict(seq_len=1000), nat.SAS_E_UNSUPPORTED),          # ragged last block
     (dict(seq_len=64 * 8193), nat.SAS_E_UNSUPPORTED),     # too many blocks
+    # packed batches: lengths come from cu_seqlens, T within [1, B * N]
+    (dict(cu_seqlens=FAKE, seq_lens=FAKE, total_tokens=100), nat.SAS_E_INVALID),
+    (dict(cu_seqlens=FAKE, total_tokens=0), nat.SAS_E_INVALID),
+    (dict(cu_seqlens=FAKE, total_tokens=1025), nat.SAS_E_INVALID),   # > batch * seq_len
 ])
 def test_invalid_problems_rejected_by_every_entry_point(kw, code):
     p = prob(**kw)

@@ -13,7 +13,8 @@ import torch
 
 from gated_block_sparse_attn_amd import api, workloads
 
-from parity import check_selection, full_parity, log, problem_of, run_gpu, sampled_parity
+from parity import (check_selection, full_parity, log, packed_parity, problem_of, run_gpu,
+                    run_gpu_packed, sampled_parity, unpack, unpack_stat)
 
 pytestmark = pytest.mark.gpu
 
@@ -124,6 +125,54 @@ def test_varlen_full_parity(case):
     # lengths outside [0, N] go to both sides as they are: the oracle's block
     # count and valid-row count saturate at 0 and N just as the kernels clamp
     full_parity(w, K, cap=cap, gate_act=act, gate_pos=pos, gate_rank=rank, seq_lens=lens)
+
+
+PACKED = [
+    # name, B, Hq, Hkv, N, D, blk, K, dtype, seq_lens, gate_act, gate_pos, gate_rank, score_heads
+    ("packed_bf16_d128_b64", 3, 8, 2, 640, 128, 64, 3, "bf16", (640, 1, 321),
+     "softmax", "inner", "soft", "group"),
+    ("packed_fp32_d64_b16_ragged_end", 4, 4, 2, 256, 64, 16, 4, "fp32", (17, 256, 100, 5),
+     "softmax", "inner", "soft", "group"),
+    ("packed_outer_sigmoid_bf16", 2, 8, 2, 512, 128, 64, 3, "bf16", (449, 130),
+     "sigmoid", "outer", "soft", "group"),
+    ("packed_heads_hard_ste_fp32", 2, 4, 2, 256, 64, 32, 3, "fp32", (200, 33),
+     "softmax", "inner", "hard_ste", "head"),
+]
+
+
+@pytest.mark.parametrize("case", PACKED, ids=[c[0] for c in PACKED])
+def test_packed_varlen_full_parity(case):
+    """Packed variable-length batches (cu_seqlens offsets, [T, H, D] tensors):
+    ragged blocks in the middle and at the very end of the packed tensors, a
+    one-token sequence, and the gate variants, against the oracle on the
+    padded equivalent."""
+    name, B, Hq, Hkv, N, D, blk, K, dt, lens, act, pos, rank, heads = case
+    log(f"packed {name} lens={lens}")
+    w = workloads.custom(B, Hq, Hkv, N, D, blk, K, dtype=dt, seed=zlib.crc32(name.encode()) % 1000,
+                         score_std=2.0, score_heads=heads)
+    cap = max(1, min(K, N // blk - 1))
+    packed_parity(w, K, lens, cap=cap, gate_act=act, gate_pos=pos, gate_rank=rank)
+
+
+def test_packed_matches_padded_bitwise():
+    """The same batch packed (cu_seqlens) and padded (seq_lens) gives bit-identical
+    rows: the kernels take the same steps, only the row addresses differ."""
+    lens = (100, 256, 37)
+    w = workloads.custom(3, 4, 2, 256, 64, 16, 4, dtype="fp32", seed=8, score_std=2.0)
+    inp = workloads.generate(w)
+    cap = 4
+    padded = run_gpu(problem_of(w, 4, seq_lens=lens), inp, cap=cap)
+    packed = run_gpu_packed(w, 4, inp, lens, cap)
+    n = w.seq_len
+    for name in ("o", "dq", "dk", "dv"):
+        got = unpack(packed[name].numpy(), lens, n)
+        for b, L in enumerate(lens):
+            assert np.array_equal(got[b, :, :L], padded[name].numpy()[b, :, :L]), name
+    got = unpack_stat(packed["lse"].numpy(), lens, n)
+    for b, L in enumerate(lens):
+        assert np.array_equal(got[b, :, :L], padded["lse"].numpy()[b, :, :L]), "lse"
+    for name in ("log_gate", "tau", "sel_idx", "sel_cnt", "dlog_gate", "dscores"):
+        assert torch.equal(packed[name], padded[name]), name
 
 
 def test_varlen_full_lengths_match_dense():
