@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fwd+bwd effective TFLOP/s at Qwen3-8B shape, 32k ctx, K=16 blocks"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_VALU_TFLOPS = 157.3   # MI355X fp32 vector peak
 
 
 def parse():
@@ -46,6 +47,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time gate/threshold + forward only (metric: 4 D pairs / time)")
+    # variants of the method (each measured on the chosen workload)
+    ap.add_argument("--gate-act", default="softmax", choices=["softmax", "sigmoid", "raw"])
+    ap.add_argument("--gate-pos", default="inner", choices=["inner", "outer"])
+    ap.add_argument("--gate-rank", default="soft", choices=["soft", "hard_ste"])
+    ap.add_argument("--score-heads", default="group", choices=["group", "head"])
+    ap.add_argument("--varlen", default=None, choices=["padded", "packed"],
+                    help="variable-length batch: seeded lengths in [N/2, N] per sequence")
     ap.add_argument("--decode", nargs="?", const="qwen3_4b_decode_b8_64k", default=None,
                     metavar="WORKLOAD",
                     help="time the sparse-decode step (select + attention) of a decode workload "
@@ -109,9 +117,22 @@ def count_pairs(sel_cnt, cap, block, group):
     return group * (units * block * (block + 1) // 2 + block * block * int(cnt.sum().item()))
 
 
-def cpu_baseline(w, K, inp, budget_s, total_pairs, fwd_only=False):
+def unit_pairs(units, cnt, block, heads_per_row, lens=None):
+    """Attended (query, key) pairs of the gate rows `units` = (b, s, i):
+    the causal triangle of the valid rows of block i plus those rows times
+    every selected (full) block, times the query heads of the row."""
+    total = 0
+    for (b, s, i) in units:
+        nv = block if lens is None else max(0, min(block, int(lens[b]) - i * block))
+        total += heads_per_row * (nv * (nv + 1) // 2 + nv * block * int(cnt[b, s, i]))
+    return total
+
+
+def cpu_baseline(w, K, inp, budget_s, total_pairs, fwd_only=False, act="softmax", pos="inner",
+                 rank="soft", lens=None):
     """Time the float64 CPU oracle on a bounded sample of the same workload
-    (forward and backward, or the forward alone)."""
+    (forward and backward, or the forward alone; with the run's gate variant
+    and sequence lengths)."""
     import numpy as np
     import oracle
     try:
@@ -123,24 +144,27 @@ def cpu_baseline(w, K, inp, budget_s, total_pairs, fwd_only=False):
         threads, vendor = os.cpu_count() or 1, "?"
     scores = inp["scores"].numpy()
     t0 = time.perf_counter()
-    lg, _, sel = oracle.gate_threshold(scores, K)
+    lg, _, sel = oracle.gate_threshold(scores, K, act=act, seq_lens=lens, block=w.block)
     t_thr = time.perf_counter() - t0
+    if rank == "hard_ste":   # unit gates on the selected blocks
+        lg = np.where(np.isfinite(lg), 0.0, lg)
     q, k, v, do = (inp[n].float().numpy() for n in ("q", "k", "v", "do"))
     c = w.n_blocks
+    hs = scores.shape[1]
     rng = np.random.default_rng(0)
-    all_units = [(b, h, i) for b in range(w.batch) for h in range(w.n_kv_heads) for i in range(c)]
+    all_units = [(b, h, i) for b in range(w.batch) for h in range(hs) for i in range(c)]
     order = rng.permutation(len(all_units))
     cnt = sel.sum(-1)
 
     def pairs_of(units):
-        return sum(w.group * (w.block * (w.block + 1) // 2 + w.block * w.block * int(cnt[u]))
-                   for u in units)
+        return unit_pairs(units, cnt, w.block, w.n_q_heads // hs, lens)
 
     def run(units):
         t = time.perf_counter()
-        oracle.forward(q, k, v, lg, sel, w.block, query_blocks=units)
+        oracle.forward(q, k, v, lg, sel, w.block, query_blocks=units, gate_pos=pos, seq_lens=lens)
         if not fwd_only:
-            oracle.backward(q, k, v, do, lg, sel, w.block, query_blocks=units)
+            oracle.backward(q, k, v, do, lg, sel, w.block, query_blocks=units, gate_pos=pos,
+                            seq_lens=lens)
         return time.perf_counter() - t
 
     probe = [all_units[j] for j in order[:2]]
@@ -273,23 +297,62 @@ def main():
     import torch
     from gated_block_sparse_attn_amd import api, workloads
 
+    import dataclasses
+
+    import numpy as np
+
     w = workloads.WORKLOADS[args.workload]
+    if args.score_heads != "group":
+        w = dataclasses.replace(w, score_heads=args.score_heads)
     K = args.budget if args.budget is not None else w.budgets[0]
+    dev = torch.device("cuda:0")
+    lens = None
+    if args.varlen:   # seeded lengths, uniform in [N/2, N]
+        lens = np.random.default_rng(1234).integers(w.seq_len // 2, w.seq_len + 1, size=w.batch)
+    seq_t = cu_t = None
+    total_tokens = 0
+    if args.varlen == "padded":
+        seq_t = torch.tensor(lens, dtype=torch.int32, device=dev)
+    elif args.varlen == "packed":
+        cu_t = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+        total_tokens = int(lens.sum())
     p = api.Problem(w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.block, K,
-                    w.dtype, 0.0, args.o_dtype if w.dtype == "bf16" else "fp32")
+                    w.dtype, 0.0, args.o_dtype if w.dtype == "bf16" else "fp32", args.gate_act,
+                    args.gate_pos, args.gate_rank, args.score_heads, seq_t, cu_t, total_tokens)
+    variant = {n: x for n, x in (("gate_act", args.gate_act), ("gate_pos", args.gate_pos),
+                                  ("gate_rank", args.gate_rank),
+                                  ("score_heads", args.score_heads))
+               if x not in ("softmax", "inner", "soft", "group")}
+    if args.varlen:
+        variant["varlen"] = args.varlen
+        variant["seq_lens"] = [int(x) for x in lens]
+    # the matrix-core kernels serve the method's default configuration at
+    # bf16 / D = 128 / b = 64 (sigmoid and raw activations included); every
+    # other configuration runs on the vector-ALU kernels
+    on_mfma = (w.dtype == "bf16" and w.head_dim == 128 and w.block == 64 and
+               args.gate_pos == "inner" and args.gate_rank == "soft" and
+               args.score_heads == "group" and not args.varlen)
     cap = p.default_cap()
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     inp = workloads.generate(w)
-    dev = torch.device("cuda:0")
-    q, k, v, do, scores = (inp[n].to(dev) for n in ("q", "k", "v", "do", "scores"))
+    if args.varlen == "packed":
+        pk = lambda x: torch.cat([x[b, :, :int(n)].transpose(0, 1) for b, n in enumerate(lens)],
+                                 dim=0).contiguous()   # noqa: E731
+        q, k, v, do = (pk(inp[n]).to(dev) for n in ("q", "k", "v", "do"))
+        lse_shape = (w.n_q_heads, total_tokens)
+    else:
+        q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+        lse_shape = tuple(q.shape[:3])
+    scores = inp["scores"].to(dev)
     sh_q, sh_kv = q.shape, k.shape
     c = w.n_blocks
-    lg = torch.empty(w.batch, w.n_kv_heads, c, c, dtype=torch.float32, device=dev)
-    tau = torch.empty(w.batch, w.n_kv_heads, c, dtype=torch.float32, device=dev)
-    sel_idx = torch.empty(w.batch, w.n_kv_heads, c, cap, dtype=torch.int32, device=dev)
-    sel_cnt = torch.empty(w.batch, w.n_kv_heads, c, dtype=torch.int32, device=dev)
+    hs = p.n_score_heads
+    lg = torch.empty(w.batch, hs, c, c, dtype=torch.float32, device=dev)
+    tau = torch.empty(w.batch, hs, c, dtype=torch.float32, device=dev)
+    sel_idx = torch.empty(w.batch, hs, c, cap, dtype=torch.int32, device=dev)
+    sel_cnt = torch.empty(w.batch, hs, c, dtype=torch.int32, device=dev)
     o = torch.empty(sh_q, dtype=p.torch_o_dtype, device=dev)
-    lse = torch.empty(sh_q[:3], dtype=torch.float32, device=dev)
+    lse = torch.empty(lse_shape, dtype=torch.float32, device=dev)
     dq = torch.empty(sh_q, dtype=p.torch_dtype, device=dev)
     dk = torch.empty(sh_kv, dtype=p.torch_dtype, device=dev)
     dv = torch.empty(sh_kv, dtype=p.torch_dtype, device=dev)
@@ -350,38 +413,53 @@ def main():
         stage_ms[name] = {"mean": sum(vals) / len(vals), "median": vals[len(vals) // 2],
                           "min": vals[0]}
 
-    pairs = count_pairs(sel_cnt, cap, w.block, w.group)
+    cnt_np = np.minimum(sel_cnt.cpu().numpy(), cap)
+    if lens is None and args.score_heads == "group":
+        pairs = count_pairs(sel_cnt, cap, w.block, w.group)
+    else:
+        pairs = unit_pairs([(b, s, i) for b in range(w.batch) for s in range(hs) for i in range(c)],
+                           cnt_np, w.block, w.n_q_heads // hs, lens)
     D = w.head_dim
     flops = (4 if args.fwd_only else 14) * D * pairs
     value = flops / (ms_step * 1e-3) / 1e12
     # algorithmic flops of the main kernel of each stage
-    kflops = {"fwd": 4 * D * pairs, "bwd_dq": 6 * D * pairs, "bwd_dkdv": 4 * D * pairs}
+    if on_mfma:
+        kflops = {"fwd": 4 * D * pairs, "bwd_dq": 6 * D * pairs, "bwd_dkdv": 4 * D * pairs}
+        knames = {"fwd": "fwd_mfma_kernel<2>", "bwd_dq": "bwd_dq_kernel<4>",
+                  "bwd_dkdv": "bwd_dkdv_kernel"}
+        bound, peak = "mfma", PEAK_BF16_TFLOPS
+    else:   # vector-ALU kernels: the same algorithmic flops against the fp32 vector peak
+        kflops = {"fwd": 4 * D * pairs, "bwd_dq": 6 * D * pairs, "bwd_dkdv": 4 * D * pairs}
+        knames = {"fwd": "fwd_generic_kernel", "bwd_dq": "bwd_q_generic_kernel",
+                  "bwd_dkdv": "bwd_kv_generic_kernel"}
+        bound, peak = "alu", PEAK_FP32_VALU_TFLOPS
     kflops = {n: f for n, f in kflops.items() if n in stages}
     dom = max(kflops, key=lambda n: stage_ms[n]["mean"])
     achieved = kflops[dom] / (stage_ms[dom]["mean"] * 1e-3) / 1e12
-    traffic = recorded_traffic(w.name, K) if dom == "bwd_dkdv" else None
-    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
-                "kernel": {"fwd": "fwd_mfma_kernel<4>", "bwd_dq": "bwd_dq_kernel<4>",
-                           "bwd_dkdv": "bwd_dkdv_kernel"}[dom],
+    traffic = recorded_traffic(w.name, K) if (dom == "bwd_dkdv" and on_mfma and not variant) \
+        else None
+    roofline = {"bound": bound, "achieved": achieved, "peak": peak,
+                "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic,
+                "kernel": knames[dom],
                 "stage_ms_mean": stage_ms[dom]["mean"],
                 "algorithmic_flops_per_launch": kflops[dom]}
+    vtag = "".join(f", {n}={x}" for n, x in variant.items() if n != "seq_lens")
     if args.fwd_only:
-        metric = f"forward effective TFLOP/s (gate/threshold + forward), {w.name}, K={K}"
-    elif w.name == "qwen3_8b_32k" and K == 16:
+        metric = f"forward effective TFLOP/s (gate/threshold + forward), {w.name}, K={K}{vtag}"
+    elif w.name == "qwen3_8b_32k" and K == 16 and not variant:
         metric = METRIC
     else:
-        metric = f"fwd+bwd effective TFLOP/s, {w.name}, K={K}"
+        metric = f"fwd+bwd effective TFLOP/s, {w.name}, K={K}{vtag}"
     fwd_ms = stage_ms["threshold"]["mean"] + stage_ms["fwd"]["mean"]
     result = {
         "metric": metric, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded torch generator; Qwen3-shaped, random values)",
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "seq_len": w.seq_len, "head_dim": D,
                    "block": w.block, "budget_k": K, "o_dtype": p.o_dtype,
-                   "attended_pairs": pairs, "flops_per_step": flops},
+                   "attended_pairs": pairs, "flops_per_step": flops, **variant},
         "roofline": roofline,
         "stage_ms": stage_ms,
         "wall_s_timed_region": t_wall,
@@ -393,7 +471,8 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         del q, k, v, do
-        result["cpu_baseline"] = cpu_baseline(w, K, inp, args.cpu_seconds, pairs, args.fwd_only)
+        result["cpu_baseline"] = cpu_baseline(w, K, inp, args.cpu_seconds, pairs, args.fwd_only,
+                                              args.gate_act, args.gate_pos, args.gate_rank, lens)
     print(json.dumps(result), flush=True)
 
 

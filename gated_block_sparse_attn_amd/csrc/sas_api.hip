@@ -124,7 +124,7 @@ namespace sas {
 
 bool mfma_path(const Shape& s) {
   return !s.fp32 && s.D == 128 && s.blk == 64 && !s.outer && !s.hard && s.Hs == s.Hkv &&
-         s.lens == nullptr && s.cu == nullptr;
+         s.cu == nullptr;
 }
 
 BwdWorkspace bwd_workspace_layout(const Shape& s) {
@@ -138,6 +138,7 @@ BwdWorkspace bwd_workspace_layout(const Shape& s) {
   size_t off = 0;
   w.delta = off;    off = align256(off + sizeof(float) * (size_t)s.B * s.Hq * s.N);
   if (mfma_path(s)) {
+    w.lsen = off;     off = align256(off + sizeof(float) * (size_t)s.B * s.Hq * s.N);
     w.colmask = off;  off = align256(off + sizeof(uint32_t) * (size_t)nrow * w.words);
     w.collen = off;   off = align256(off + sizeof(int32_t) * (size_t)nrow);
     w.coloff = off;   off = align256(off + sizeof(int32_t) * (size_t)(nrow + 1));

@@ -38,6 +38,7 @@ struct Shape {
 // Workspace carve-up of the backward pass (byte offsets, 256-aligned).
 struct BwdWorkspace {
   size_t delta;      // float  [B*Hq*N]              Delta: sum of P * dP over a query row
+  size_t lsen;       // float  [B*Hq*N]              -LSE log2(e) (-inf: padding row), matrix-core path
   size_t colmask;    // uint32 [B*Hkv*C*W]           bit (j, i): row i selected block j
   size_t collen;     // int32  [B*Hkv*C]             1 + #rows selecting column j
   size_t coloff;     // int32  [B*Hkv*C + 1]         prefix of collen

@@ -58,6 +58,7 @@ struct BwdArgs {
   const float* lse; const float* lg; const int32_t* sel_idx; const int32_t* sel_cnt;
   bf16* dq; bf16* dk; bf16* dv; float* dlg; float* dsc;
   float* delta;
+  float* lsen;     // -LSE log2(e) per query row (-inf on padding rows), from the dq pass
   uint32_t* colmask; int32_t* collen; int32_t* coloff; int32_t* chunkoff; int32_t* collist;
   float* partial;
   int32_t* chunk_rank; int32_t* chunk_hist; int32_t* chunk_order;
@@ -65,6 +66,7 @@ struct BwdArgs {
   int Hq, Hkv, G, N, C, cap, W, o_fp32;
   int head_base, nchunk;
   float c2, scale;
+  const int32_t* lens;   // variable-length batch (padded layout): valid tokens, or nullptr
 };
 
 __device__ __forceinline__ float sum2(float x) {   // lanes l, l ^ 32
@@ -174,6 +176,25 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
   const bf16* kbase = a.k + (long long)bhk * a.N * HD;
   const bf16* vbase = a.v + (long long)bhk * a.N * HD;
   const long long qr = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + half * 32 + l32;
+
+  // Variable-length batch (padded layout): padding rows get dQ = 0 and
+  // Delta = 0; a block without a valid row does nothing else (this return
+  // precedes every copy and barrier and is uniform over the workgroup).
+  const int nb = a.lens == nullptr ? a.N : min(max(a.lens[bb], 0), a.N);
+  if (i * BLK >= nb) {
+    if (g == 0) {
+      a.delta[qr] = 0.0f;
+      a.lsen[qr] = -INFINITY;
+    }
+    bf16* dqp = a.dq + qr * HD + g * 4;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *(bf16x4*)(dqp + dt * 32 + q4 * 8) = bf16x4{(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
+    return;
+  }
+  const bool row_valid = i * BLK + half * 32 + l32 < nb;
 
   auto load_tile = [&](int kb, int stg) {
     tile_to_lds<NW>(s_k[stg], kbase + (long long)kb * TILE, w, lane);
@@ -358,7 +379,10 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
     __syncthreads();
   }
   const float dsum = sum2(dx);
-  if (g == 0) a.delta[qr] = dsum;
+  if (g == 0) {
+    a.delta[qr] = row_valid ? dsum : 0.0f;
+    a.lsen[qr] = row_valid ? -lse2 : -INFINITY;
+  }
 
   // dQ = scale * dQacc (lane: query l32, dims dt*32 + q4*8 + 4 g .. +3)
   bf16* dqp = a.dq + qr * HD + g * 4;
@@ -368,7 +392,7 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
     for (int q4 = 0; q4 < 4; ++q4) {
       bf16x4 r;
 #pragma unroll
-      for (int y = 0; y < 4; ++y) r[y] = (bf16)(dqacc[dt][q4 * 4 + y] * a.scale);
+      for (int y = 0; y < 4; ++y) r[y] = (bf16)(row_valid ? dqacc[dt][q4 * 4 + y] * a.scale : 0.0f);
       *(bf16x4*)(dqp + dt * 32 + q4 * 8) = r;
     }
 }
@@ -671,7 +695,7 @@ bwd_dkdv_kernel(BwdArgs a) {
   const int nslots = role == 0 ? Q_SLOTS : O_SLOTS;
   char* const ring = smem + (role == 0 ? QRING : ORING);
   const bf16* src = role == 0 ? a.q : a.d_o;
-  const float* stat = role == 0 ? a.delta : a.lse;
+  const float* stat = role == 0 ? a.delta : a.lsen;
   // this lane's 16 bytes of copy q: rows (kh*4 + q)*4 .. +3, less the
   // q * 1024 that the instruction offset adds (rows >= 4 q, so >= 0)
   unsigned voff[4];
@@ -792,6 +816,9 @@ bwd_dkdv_kernel(BwdArgs a) {
   // beta - lse) (LSE in os), then dV_s += dO_s^T P_s; P_s also goes to LDS
   // (fp16) for B.  HALF: the step's half of its query block.
   const int key = kh * 32 + l32;
+  // The statistic of the O ring is -LSE log2(e) per query row, written by
+  // the query-major pass (-inf on padding rows of a variable-length batch, so
+  // they get P = 0 and add nothing to dV, dK and dLogG).
   auto window_a = [&](auto diag_tag, auto half_tag, const char* qn, const char* os, _Float16* px,
                       float beta, const f32x16& sprev, f32x16& snext) {
     constexpr bool DIAG = decltype(diag_tag)::value;
@@ -799,7 +826,7 @@ bwd_dkdv_kernel(BwdArgs a) {
     float nl[16];
     read_stat(os, nl);
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) nl[jj] = fmaf(-nl[jj], kLog2e, beta);
+    for (int jj = 0; jj < 16; ++jj) nl[jj] += beta;
     bf16x8 bop[2];
     f16x8 ph[2];
     rows_product_with(qn, snext, [&](int m) {
@@ -1044,6 +1071,7 @@ BwdArgs make_bwd_args(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorks
   a.sel_cnt = p.sel_cnt; a.dq = (bf16*)p.dq; a.dk = (bf16*)p.dk; a.dv = (bf16*)p.dv;
   a.dlg = p.dlog_gate; a.dsc = p.dscores;
   a.delta = (float*)(ws + wl.delta);
+  a.lsen = (float*)(ws + wl.lsen);
   a.colmask = (uint32_t*)(ws + wl.colmask);
   a.collen = (int32_t*)(ws + wl.collen);
   a.coloff = (int32_t*)(ws + wl.coloff);
@@ -1058,6 +1086,7 @@ BwdArgs make_bwd_args(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorks
   a.o_fp32 = s.o_fp32;
   a.c2 = s.scale * kLog2e;
   a.scale = s.scale;
+  a.lens = s.lens;
   return a;
 }
 }  // namespace

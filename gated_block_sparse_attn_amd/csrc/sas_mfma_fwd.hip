@@ -66,6 +66,7 @@ struct FwdArgs {
   int head_base;  // first head (within its kv group) of chunk 0 of this launch
   int nchunk;     // chunks of NW heads per (batch, kv head, query block)
   float c2;       // sm_scale * log2(e)
+  const int32_t* lens;   // variable-length batch: valid tokens per sequence (or nullptr)
 };
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -197,6 +198,28 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
   const bf16* kbase = a.k + (long long)bhk * a.N * HD;
   const bf16* vbase = a.v + (long long)bhk * a.N * HD;
   const long long q0 = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + half * 32;
+
+  // Variable-length batch (padded layout): rows past the sequence's length
+  // are padding; they get o = 0 and lse = 0, and a block without a valid row
+  // does nothing else.  (Padding rows hold finite values; only the valid rows
+  // are ever mixed into a valid row's result: later keys are masked.)
+  const int nb = a.lens == nullptr ? a.N : min(max(a.lens[bb], 0), a.N);
+  if (i * BLK >= nb) {   // uniform over the workgroup: no barrier has been reached
+    const long long qrow = q0 + l32;
+    if (g == 0) a.lse[qrow] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        if (a.o_fp32)
+          *(f32x4*)((float*)a.o + qrow * HD + g * 4 + dt * 32 + q4 * 8) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        else
+          *(bf16x4*)((bf16*)a.o + qrow * HD + g * 4 + dt * 32 + q4 * 8) =
+              bf16x4{(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
+      }
+    return;
+  }
+  const bool row_valid = i * BLK + half * 32 + l32 < nb;
 
   // Q^T as the B operand of S^T = K Q^T (32x32x16): lane holds query row
   // l32 and head dims ks*16 + g*8 .. +7.
@@ -407,9 +430,9 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
   const float ltot = sum2(lrow);
-  const float inv = 1.0f / ltot;
+  const float inv = row_valid ? 1.0f / ltot : 0.0f;   // padding rows: o = 0, lse = 0
   const long long qrow = q0 + l32;
-  if (g == 0) a.lse[qrow] = (mrow + log2f(ltot)) * kLn2;
+  if (g == 0) a.lse[qrow] = row_valid ? (mrow + log2f(ltot)) * kLn2 : 0.0f;
   if (a.o_fp32) {
     float* op = (float*)a.o + qrow * HD + g * 4;
 #pragma unroll
@@ -458,6 +481,7 @@ hipError_t launch_fwd_mfma(const Shape& s, const void* q, const void* k, const v
   a.o_fp32 = s.o_fp32;
   a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.G; a.N = s.N; a.C = s.C; a.cap = s.cap;
   a.c2 = s.scale * kLog2e;
+  a.lens = s.lens;
   const long long units = (long long)s.B * s.Hkv * s.C;
   // the G heads of a group are covered by chunks of 2 heads, then 1: two
   // 4-wavefront workgroups per CU drift out of step, so one's barrier and

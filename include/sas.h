@@ -142,8 +142,10 @@ typedef struct sas_problem {
                          contribute no gradient); gate rows i >= ceil(n_b / b)
                          select nothing (sel_cnt 0, tau +inf; log_gate still
                          written; dlog_gate and dscores 0).  Values outside
-                         [0, N] are clamped into it.  Runs on the vector-ALU
-                         path.                                                */
+                         [0, N] are clamped into it.  Padding rows must hold
+                         finite values (their content never reaches a valid
+                         row).  bf16 / D = 128 / b = 64 problems with the
+                         method's gates run on the matrix-core path.          */
   const int32_t* cu_seqlens; /* optional DEVICE int32 [B + 1]: packed batch
                          (the cu_seqlens convention of varlen attention):
                          sequence b holds tokens cu_seqlens[b] ..

@@ -105,6 +105,11 @@ VARLEN = [
      "softmax", "inner", "soft", "group"),
     ("varlen_clamped_lengths", 2, 4, 1, 256, 64, 32, 2, "fp32", (-3, 300),
      "softmax", "inner", "soft", "group"),
+    # matrix-core path (bf16, D = 128, b = 64): ragged, one-token, empty and full sequences
+    ("varlen_mfma_g4", 4, 8, 2, 1024, 128, 64, 4, "bf16", (1024, 0, 577, 65),
+     "softmax", "inner", "soft", "group"),
+    ("varlen_mfma_g5_sigmoid", 2, 10, 2, 640, 128, 64, 3, "bf16", (1, 383),
+     "sigmoid", "inner", "soft", "group"),
     ("varlen_outer_sigmoid_bf16", 2, 8, 2, 512, 128, 64, 3, "bf16", (449, 130),
      "sigmoid", "outer", "soft", "group"),
     ("varlen_heads_hard_ste_fp32", 2, 4, 2, 256, 64, 16, 3, "fp32", (200, 33),
@@ -173,6 +178,16 @@ def test_packed_matches_padded_bitwise():
         assert np.array_equal(got[b, :, :L], padded["lse"].numpy()[b, :, :L]), "lse"
     for name in ("log_gate", "tau", "sel_idx", "sel_cnt", "dlog_gate", "dscores"):
         assert torch.equal(packed[name], padded[name]), name
+
+
+def test_varlen_mfma_full_lengths_match_dense_bitwise():
+    """Matrix-core path: seq_lens = N everywhere gives the dense run bit for bit."""
+    w = workloads.custom(2, 8, 2, 1024, 128, 64, 4, dtype="bf16", seed=6, score_std=2.0)
+    inp = workloads.generate(w)
+    dense = run_gpu(problem_of(w, 4), inp)
+    full = run_gpu(problem_of(w, 4, seq_lens=(1024, 1024)), inp)
+    for n in dense:
+        assert torch.equal(dense[n], full[n]), n
 
 
 def test_varlen_full_lengths_match_dense():
