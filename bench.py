@@ -331,7 +331,7 @@ def main():
     # other configuration runs on the vector-ALU kernels
     on_mfma = (w.dtype == "bf16" and w.head_dim == 128 and w.block == 64 and
                args.gate_pos == "inner" and args.gate_rank == "soft" and
-               args.score_heads == "group" and not args.varlen)
+               args.score_heads == "group" and args.varlen != "packed")
     cap = p.default_cap()
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     inp = workloads.generate(w)

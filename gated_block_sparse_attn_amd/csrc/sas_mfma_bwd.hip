@@ -67,7 +67,24 @@ struct BwdArgs {
   int head_base, nchunk;
   float c2, scale;
   const int32_t* lens;   // variable-length batch (padded layout): valid tokens, or nullptr
+  const int32_t* cu;     // packed batch: token offsets [B + 1], or nullptr
+  long long T;           // packed batch: total tokens
 };
+
+// First token (packed batch) and valid tokens of sequence b, clamped so that
+// every row stays inside the tensors.
+struct Span {
+  long long start;
+  int n;
+};
+__device__ __forceinline__ Span seq_span(const BwdArgs& a, int b) {
+  if (a.cu != nullptr) {
+    const long long s0 = min(max((long long)a.cu[b], 0LL), a.T);
+    const long long s1 = min(max((long long)a.cu[b + 1], s0), a.T);
+    return {s0, (int)min(s1 - s0, (long long)a.N)};
+  }
+  return {0, a.lens == nullptr ? a.N : min(max(a.lens[b], 0), a.N)};
+}
 
 __device__ __forceinline__ float sum2(float x) {   // lanes l, l ^ 32
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -113,14 +130,18 @@ __device__ __forceinline__ int swz(int r, int c) { return r * HD + ((c ^ slot16(
 
 // Asynchronous global -> LDS copy of one 64 x 128 tile by NW wavefronts
 // (global_load_lds_dwordx4); completion is awaited with s_waitcnt vmcnt(0).
+// Row r comes from g + min(r, rmax) * stride (elements): HD in the padded
+// layout, Hkv * HD in a packed batch, where rows past a sequence's end repeat
+// its last row (causally masked; the clamp keeps reads inside the tensor).
 template <int NW>
-__device__ __forceinline__ void tile_to_lds(bf16* lds, const bf16* g, int w, int lane) {
+__device__ __forceinline__ void tile_to_lds(bf16* lds, const bf16* g, long long stride, int rmax,
+                                            int w, int lane) {
 #pragma unroll
   for (int r = 0; r < 16 / NW; ++r) {
     const int seg = w + NW * r;               // 1 KB segment = rows 4 seg .. 4 seg + 3
     const int row = seg * 4 + (lane >> 4);
     const int c = (lane & 15) ^ slot16(row);
-    dma16(g + row * HD + c * 8, lds_addr(lds + seg * 512));
+    dma16(g + min(row, rmax) * stride + c * 8, lds_addr(lds + seg * 512));
   }
 }
 
@@ -148,7 +169,7 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 //   keys of both operands permuted the same way).
 // K / V tiles are double-buffered in LDS: tile t + 1 is copied while tile t
 // is processed, one barrier per tile.
-template <int NH>
+template <int NH, bool PACKED>
 __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
   constexpr int NW = 2 * NH;
   __shared__ __attribute__((aligned(16))) bf16 s_k[2][TILE];
@@ -173,19 +194,22 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
   const int cnt = min(a.sel_cnt[row], a.cap);
   const int32_t* sel = a.sel_idx + row * a.cap;
   const float* lgrow = a.lg + row * a.C;
-  const bf16* kbase = a.k + (long long)bhk * a.N * HD;
-  const bf16* vbase = a.v + (long long)bhk * a.N * HD;
+  // workspace index of this lane's query row (padded order in every layout)
   const long long qr = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + half * 32 + l32;
 
-  // Variable-length batch (padded layout): padding rows get dQ = 0 and
-  // Delta = 0; a block without a valid row does nothing else (this return
+  // Variable-length batch: padding rows get Delta = 0 and -LSE = -inf in the
+  // workspace, and dQ = 0 in the padded layout (a packed batch has no such
+  // rows); a block without a valid row does nothing else (this return
   // precedes every copy and barrier and is uniform over the workgroup).
-  const int nb = a.lens == nullptr ? a.N : min(max(a.lens[bb], 0), a.N);
+  constexpr bool packed = PACKED;   // packed variable-length batch (compile-time)
+  const Span sp = seq_span(a, bb);
+  const int nb = sp.n;
   if (i * BLK >= nb) {
     if (g == 0) {
       a.delta[qr] = 0.0f;
       a.lsen[qr] = -INFINITY;
     }
+    if (packed) return;
     bf16* dqp = a.dq + qr * HD + g * 4;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -195,10 +219,19 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
     return;
   }
   const bool row_valid = i * BLK + half * 32 + l32 < nb;
+  // tensor rows of this lane's query (q, o, dO, dq) and its LSE entry; in a
+  // packed batch the token is clamped to the sequence's last row
+  const int tok = min(i * BLK + half * 32 + l32, nb - 1);
+  const long long qt = packed ? (sp.start + tok) * a.Hq + h : qr;
+  const long long ql = packed ? (long long)h * a.T + sp.start + tok : qr;
+  const long long kv_stride = packed ? (long long)a.Hkv * HD : HD;
 
   auto load_tile = [&](int kb, int stg) {
-    tile_to_lds<NW>(s_k[stg], kbase + (long long)kb * TILE, w, lane);
-    tile_to_lds<NW>(s_v[stg], vbase + (long long)kb * TILE, w, lane);
+    const long long t0 = packed ? ((sp.start + (long long)kb * BLK) * a.Hkv + hk) * HD
+                                : ((long long)bhk * a.N + (long long)kb * BLK) * HD;
+    const int rmax = packed ? min(BLK - 1, nb - 1 - kb * BLK) : BLK - 1;
+    tile_to_lds<NW>(s_k[stg], a.k + t0, kv_stride, rmax, w, lane);
+    tile_to_lds<NW>(s_v[stg], a.v + t0, kv_stride, rmax, w, lane);
   };
   const int ntiles = cnt + 1;
   load_tile(i, 0);
@@ -212,13 +245,13 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     const int d0 = ks * 16 + g * 8;
-    qf[ks] = *(const bf16x8*)(a.q + qr * HD + d0);
-    dof[ks] = *(const bf16x8*)(a.d_o + qr * HD + d0);
+    qf[ks] = *(const bf16x8*)(a.q + qt * HD + d0);
+    dof[ks] = *(const bf16x8*)(a.d_o + qt * HD + d0);
   }
   if (a.o_fp32) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const float* op = (const float*)a.o + qr * HD + ks * 16 + g * 8;
+      const float* op = (const float*)a.o + qt * HD + ks * 16 + g * 8;
       const f32x4 o0 = *(const f32x4*)op;
       const f32x4 o1 = *(const f32x4*)(op + 4);
 #pragma unroll
@@ -230,13 +263,13 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
   } else {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 ob = *(const bf16x8*)((const bf16*)a.o + qr * HD + ks * 16 + g * 8);
+      const bf16x8 ob = *(const bf16x8*)((const bf16*)a.o + qt * HD + ks * 16 + g * 8);
 #pragma unroll
       for (int x = 0; x < 8; ++x) part_d += (float)ob[x] * (float)dof[ks][x];
     }
   }
   const float dlt = sum2(part_d);
-  const float lse2 = a.lse[qr] * kLog2e;
+  const float lse2 = a.lse[ql] * kLog2e;
   float dx = 0.0f;
 
   f32x16 dqacc[4];   // dQ^T (lane: dims dt*32 + 8 (jj/4) + 4 g + jj%4, query l32)
@@ -385,7 +418,8 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
   }
 
   // dQ = scale * dQacc (lane: query l32, dims dt*32 + q4*8 + 4 g .. +3)
-  bf16* dqp = a.dq + qr * HD + g * 4;
+  if (packed && !row_valid) return;   // the row belongs to no sequence of this batch
+  bf16* dqp = a.dq + qt * HD + g * 4;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -639,6 +673,9 @@ __device__ __forceinline__ void dma16_at(const void* base, unsigned voff) {
                    "i"(OFF) : "memory");
 }
 
+// PACKED: packed variable-length batch (a compile-time switch, so the copies
+// of the fixed-length and padded layouts keep their one-base form).
+template <bool PACKED>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[KV4_LDS];
@@ -668,8 +705,16 @@ bwd_dkdv_kernel(BwdArgs a) {
   const int hk = (int)(bhk % a.Hkv);
   const int bb = (int)(bhk / a.Hkv);
   const int G = a.G;
+  constexpr bool packed = PACKED;
+  const Span sp = seq_span(a, bb);
+  // A packed batch has no rows for a key block past its sequence's end (no
+  // selecting row, only the diagonal entry with no valid query): nothing to
+  // do.  Uniform over the workgroup, before any copy or barrier.
+  if (packed && j * BLK >= sp.n) return;
 
-  long long rowbase = 0;
+  long long rowbase = 0;   // per entry: workspace row of (query block, head 0) (padded order)
+  long long prow = 0;      // packed batch: tensor row of (query block, head 0)
+  int vrem = 0;            // packed batch: valid rows of the entry's query block
   if (lane < ne) {
     const int i = a.collist[a.coloff[col] + e0 + lane];
     if (wv == 0) {
@@ -677,13 +722,18 @@ bwd_dkdv_kernel(BwdArgs a) {
       btab[lane] = i == j ? 0.0f : a.lg[(bhk * a.C + i) * a.C + j] * kLog2e;
     }
     rowbase = ((long long)bb * a.Hq + hk * G) * a.N + (long long)i * BLK;
+    prow = (sp.start + (long long)i * BLK) * a.Hq + hk * G;
+    vrem = sp.n - i * BLK;
   }
 
   // resident B operand of S (A: K_j) or dP (B: V_j): key kh*32 + l32,
   // dims ds*16 + g*8 .. +7
   bf16x8 kf[8];
   {
-    const bf16* t = (role == 0 ? a.k : a.v) + (bhk * a.N + (long long)j * BLK + kh * 32 + l32) * HD;
+    const int key = j * BLK + kh * 32 + l32;
+    const long long kr = packed ? (sp.start + min(key, sp.n - 1)) * a.Hkv + hk
+                                : bhk * a.N + key;
+    const bf16* t = (role == 0 ? a.k : a.v) + kr * HD;
 #pragma unroll
     for (int ds = 0; ds < 8; ++ds) kf[ds] = *(const bf16x8*)(t + ds * 16 + g * 8);
 #pragma unroll
@@ -707,12 +757,21 @@ bwd_dkdv_kernel(BwdArgs a) {
   const unsigned soff = (unsigned)l32 * 4;
   int ct = 0, ce = 0, chh = 0, cx = 0, cslot = 0;
   const unsigned ring_lds = lds_addr(ring);
-  struct Copy { const bf16* rows; const float* st; unsigned lds; };
+  // packed batch: rows of the entry's block are Hq * HD apart; copy q of a
+  // step takes block rows cx*32 + (kh*4 + q)*4 + lane/16, clamped to the
+  // block's last valid row (vr = its valid rows)
+  struct Copy { const bf16* rows; const float* st; unsigned lds; int cx, vr; };
   auto prepare = [&]() -> Copy {
     const long long rbase = (long long)(unsigned)__builtin_amdgcn_readlane((int)rowbase, ce) |
                             ((long long)__builtin_amdgcn_readlane((int)(rowbase >> 32), ce) << 32);
     const long long r0 = rbase + (long long)(unsigned)(chh * a.N + cx * 32);
-    Copy cp{src + r0 * HD, stat + r0, ring_lds + (unsigned)(cslot * SLOT_BYTES)};
+    Copy cp{src + r0 * HD, stat + r0, ring_lds + (unsigned)(cslot * SLOT_BYTES), cx, 0};
+    if (packed) {
+      const long long pb = (long long)(unsigned)__builtin_amdgcn_readlane((int)prow, ce) |
+                           ((long long)__builtin_amdgcn_readlane((int)(prow >> 32), ce) << 32);
+      cp.rows = src + (pb + chh) * HD;   // row 0 of the entry's block, head chh
+      cp.vr = __builtin_amdgcn_readlane(vrem, ce);
+    }
     cslot = cslot + 1 == nslots ? 0 : cslot + 1;
     if (++ct < n) {
       cx ^= 1;
@@ -723,6 +782,17 @@ bwd_dkdv_kernel(BwdArgs a) {
   // copies per step: four 1 KB row groups per wavefront (one M0 for the
   // four, placed by the instruction offsets), and the statistic (key half 0)
   auto issue = [&](const Copy& cp, int q) {
+    if (packed) {   // one LDS base per copy; per-lane clamped rows
+      if (q < 4) {
+        const int row = (kh * 4 + q) * 4 + (lane >> 4);
+        const int br = min(cp.cx * 32 + row, cp.vr - 1);
+        const unsigned vo = (unsigned)((long long)br * a.Hq * HD + (((lane & 15) ^ slot16(row)) << 3)) * 2;
+        dma16s(cp.rows, vo, cp.lds + 256 + (kh * 4 + q) * 1024);
+      } else if (kh == 0) {
+        dma4s(cp.st, soff, cp.lds);
+      }
+      return;
+    }
     switch (q) {
       case 0:
         set_lds_m0(cp.lds + 256 + kh * 4096);
@@ -982,6 +1052,9 @@ bwd_dkdv_kernel(BwdArgs a) {
   const float mul = role == 0 ? 1.0f : a.scale;
   if (nch == 1) {
     bf16* dst = role == 0 ? a.dv : a.dk;
+    const int key = j * BLK + kh * 32 + l32;
+    if (packed && key >= sp.n) return;   // the row belongs to no sequence of this batch
+    const long long r = packed ? (sp.start + key) * a.Hkv + hk : orow + l32;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -989,7 +1062,7 @@ bwd_dkdv_kernel(BwdArgs a) {
         bf16x4 o;
 #pragma unroll
         for (int y = 0; y < 4; ++y) o[y] = (bf16)(acc[dt][q4 * 4 + y] * mul);
-        *(bf16x4*)(dst + (orow + l32) * HD + dt * 32 + q4 * 8 + g * 4) = o;
+        *(bf16x4*)(dst + r * HD + dt * 32 + q4 * 8 + g * 4) = o;
       }
   } else {
     float* dst = a.partial + (long long)gch * 2 * 8192 + (role == 0 ? 8192 : 0) + kh * 32 * HD;
@@ -1015,6 +1088,14 @@ __global__ void __launch_bounds__(256) reduce_kernel(BwdArgs a) {
   const long long bhk = col / a.C;
   const long long orow = bhk * a.N + (long long)j * BLK;
   const int e = (threadIdx.x + (blockIdx.x & 3) * 256) * 8;
+  // packed batch: key row e / HD of the block, if it belongs to the sequence
+  long long prow = -1;
+  if (a.cu != nullptr) {
+    const Span sp = seq_span(a, (int)(bhk / a.Hkv));
+    const int key = j * BLK + e / HD;
+    if (key >= sp.n) return;
+    prow = (sp.start + key) * a.Hkv + (int)(bhk % a.Hkv);
+  }
   const float* base = a.partial + (long long)c0 * 2 * 8192 + e;
   f32x4 sk[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
   f32x4 sv[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
@@ -1048,16 +1129,21 @@ __global__ void __launch_bounds__(256) reduce_kernel(BwdArgs a) {
     ok[x] = (bf16)sk[x >> 2][x & 3];
     ov[x] = (bf16)sv[x >> 2][x & 3];
   }
-  *(bf16x8*)(a.dk + orow * HD + e) = ok;
-  *(bf16x8*)(a.dv + orow * HD + e) = ov;
+  const long long off = prow >= 0 ? prow * HD + e % HD : orow * HD + e;
+  *(bf16x8*)(a.dk + off) = ok;
+  *(bf16x8*)(a.dv + off) = ov;
 }
 
 template <int NH>
 hipError_t launch_dq(BwdArgs a, int head_base, int nchunk, long long units, hipStream_t st) {
   a.head_base = head_base;
   a.nchunk = nchunk;
-  hipLaunchKernelGGL((bwd_dq_kernel<NH>), dim3((unsigned)(units * nchunk)), dim3(NH * 128), 0, st,
-                     a);
+  if (a.cu != nullptr)
+    hipLaunchKernelGGL((bwd_dq_kernel<NH, true>), dim3((unsigned)(units * nchunk)), dim3(NH * 128),
+                       0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<NH, false>), dim3((unsigned)(units * nchunk)), dim3(NH * 128),
+                       0, st, a);
   return hipGetLastError();
 }
 
@@ -1087,6 +1173,8 @@ BwdArgs make_bwd_args(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorks
   a.c2 = s.scale * kLog2e;
   a.scale = s.scale;
   a.lens = s.lens;
+  a.cu = s.cu;
+  a.T = s.T;
   return a;
 }
 }  // namespace
@@ -1138,7 +1226,10 @@ hipError_t launch_bwd_dkdv_mfma(const Shape& s, const BwdPtrs& p, char* ws,
   const long long ntab = a.ncol * s.C;
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)min((ntab + 255) / 256, 65535LL)),
                      dim3(256), 0, st, (uint32_t*)a.dlg, ntab);
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)wl.max_chunks), dim3(256), 0, st, a);
+  if (s.cu != nullptr)
+    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3((unsigned)wl.max_chunks), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3((unsigned)wl.max_chunks), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)(a.ncol * 4)), dim3(256), 0, st, a);

@@ -67,6 +67,8 @@ struct FwdArgs {
   int nchunk;     // chunks of NW heads per (batch, kv head, query block)
   float c2;       // sm_scale * log2(e)
   const int32_t* lens;   // variable-length batch: valid tokens per sequence (or nullptr)
+  const int32_t* cu;     // packed batch: token offsets [B + 1] (or nullptr)
+  long long T;           // packed batch: total tokens
 };
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -123,15 +125,19 @@ __device__ __forceinline__ int swz(int r, int c) { return r * HD + ((c ^ slot16(
 // (global_load_lds_dwordx4: each instruction writes 64 x 16 contiguous bytes
 // of LDS; the lanes pick their global chunk so the result is swizzled).
 // Completion is waited for with s_waitcnt vmcnt(0) before the next barrier.
+// Row r of the tile is read from g + min(r, rmax) * stride (elements): rows
+// are HD apart in the padded layout and Hkv * HD apart in a packed batch,
+// whose last rows past a sequence's end repeat its last row (they are
+// causally masked; the clamp keeps every read inside the tensor).
 template <int NW>
-__device__ __forceinline__ void tile_to_lds(bf16* lds, const bf16* g, int w, int lane) {
-  typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void tile_to_lds(bf16* lds, const bf16* g, long long stride, int rmax,
+                                            int w, int lane) {
 #pragma unroll
   for (int r = 0; r < 16 / NW; ++r) {
     const int seg = w + NW * r;               // 1 KB segment = rows 4 seg .. 4 seg + 3
     const int row = seg * 4 + (lane >> 4);
     const int c = (lane & 15) ^ slot16(row);
-    dma16(g + row * HD + c * 8, lds_addr(lds + seg * 512));
+    dma16(g + min(row, rmax) * stride + c * 8, lds_addr(lds + seg * 512));
   }
 }
 
@@ -170,7 +176,7 @@ __device__ __forceinline__ void wait_vm_prev() {   // all but this window's 16 /
   else __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");
 }
 
-template <int NH, bool SPLIT>
+template <int NH, bool SPLIT, bool PACKED>
 __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
   constexpr int NW = 2 * NH;
   __shared__ __attribute__((aligned(16))) bf16 s_k[2][TILE];
@@ -195,16 +201,32 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
   const int cnt = min(a.sel_cnt[row], a.cap);
   const int32_t* sel = a.sel_idx + row * a.cap;
   const float* lgrow = a.lg + row * a.C;
-  const bf16* kbase = a.k + (long long)bhk * a.N * HD;
-  const bf16* vbase = a.v + (long long)bhk * a.N * HD;
   const long long q0 = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + half * 32;
 
-  // Variable-length batch (padded layout): rows past the sequence's length
-  // are padding; they get o = 0 and lse = 0, and a block without a valid row
-  // does nothing else.  (Padding rows hold finite values; only the valid rows
-  // are ever mixed into a valid row's result: later keys are masked.)
-  const int nb = a.lens == nullptr ? a.N : min(max(a.lens[bb], 0), a.N);
-  if (i * BLK >= nb) {   // uniform over the workgroup: no barrier has been reached
+  // Variable-length batch: rows past the sequence's length are padding.  In
+  // the padded layout they get o = 0 and lse = 0; in a packed batch they do
+  // not exist (reads are clamped to the sequence's last row, nothing is
+  // written).  A block without a valid row does nothing else.  (Padding rows
+  // hold finite values; only valid rows are mixed into a valid row's result:
+  // later keys are masked.)
+  constexpr bool packed = PACKED;   // packed variable-length batch (compile-time)
+  long long start = 0;   // packed: first token of the sequence
+  int nb = a.lens == nullptr ? a.N : min(max(a.lens[bb], 0), a.N);
+  if (packed) {
+    const long long s0 = min(max((long long)a.cu[bb], 0LL), a.T);
+    const long long s1 = min(max((long long)a.cu[bb + 1], s0), a.T);
+    start = s0;
+    nb = (int)min(s1 - s0, (long long)a.N);
+  }
+  // K / V rows: tile kb starts at kv_tile(kb); consecutive tokens kv_stride apart
+  const long long kv_stride = packed ? (long long)a.Hkv * HD : HD;
+  auto kv_tile = [&](int kb) -> long long {
+    return packed ? ((start + (long long)kb * BLK) * a.Hkv + hk) * HD
+                  : ((long long)bhk * a.N + (long long)kb * BLK) * HD;
+  };
+  auto kv_rmax = [&](int kb) { return packed ? min(BLK - 1, nb - 1 - kb * BLK) : BLK - 1; };
+  if (i * BLK >= nb) {   // uniform over the workgroup: no copy or barrier has been issued
+    if (packed) return;
     const long long qrow = q0 + l32;
     if (g == 0) a.lse[qrow] = 0.0f;
 #pragma unroll
@@ -220,12 +242,17 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
     return;
   }
   const bool row_valid = i * BLK + half * 32 + l32 < nb;
+  // this lane's query row (q and o): padded index, or the packed token
+  // (clamped to the sequence's last row)
+  const int tok = min(i * BLK + half * 32 + l32, nb - 1);
+  const long long qrow_i = packed ? (start + tok) * a.Hq + h : q0 + l32;
+  const long long lse_i = packed ? (long long)h * a.T + start + tok : q0 + l32;
 
   // Q^T as the B operand of S^T = K Q^T (32x32x16): lane holds query row
   // l32 and head dims ks*16 + g*8 .. +7.
   bf16x8 qf[8];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)(a.q + (q0 + l32) * HD + ks * 16 + g * 8);
+  for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)(a.q + qrow_i * HD + ks * 16 + g * 8);
 
   // The row's selection, 64 entries at a time, in registers: lane e holds
   // block sel[e0 + e] and its log gate (log2 units); read with readlane.
@@ -354,8 +381,12 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
       }
   };
 
-  auto copy_k = [&](int kb, int slot) { tile_to_lds<NW>(s_k[slot], kbase + (long long)kb * TILE, w, lane); };
-  auto copy_v = [&](int kb, int slot) { tile_to_lds<NW>(s_v[slot], vbase + (long long)kb * TILE, w, lane); };
+  auto copy_k = [&](int kb, int slot) {
+    tile_to_lds<NW>(s_k[slot], a.k + kv_tile(kb), kv_stride, kv_rmax(kb), w, lane);
+  };
+  auto copy_v = [&](int kb, int slot) {
+    tile_to_lds<NW>(s_v[slot], a.v + kv_tile(kb), kv_stride, kv_rmax(kb), w, lane);
+  };
 
   // prologue: K_0, V_0, K_1 in; S of unit 0 (masked) starts the running max
   float beta1 = 0.0f;
@@ -431,8 +462,9 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
   const float ltot = sum2(lrow);
   const float inv = row_valid ? 1.0f / ltot : 0.0f;   // padding rows: o = 0, lse = 0
-  const long long qrow = q0 + l32;
-  if (g == 0) a.lse[qrow] = row_valid ? (mrow + log2f(ltot)) * kLn2 : 0.0f;
+  if (packed && !row_valid) return;   // the row belongs to no sequence of this batch
+  const long long qrow = qrow_i;
+  if (g == 0) a.lse[lse_i] = row_valid ? (mrow + log2f(ltot)) * kLn2 : 0.0f;
   if (a.o_fp32) {
     float* op = (float*)a.o + qrow * HD + g * 4;
 #pragma unroll
@@ -461,11 +493,15 @@ hipError_t launch_chunks(FwdArgs a, int head_base, int nchunk, long long units,
                          hipStream_t st) {
   a.head_base = head_base;
   a.nchunk = nchunk;
-  const long long grid = units * nchunk;
-  if (a.o_fp32)
-    hipLaunchKernelGGL((fwd_mfma_kernel<NH, true>), dim3((unsigned)grid), dim3(NH * 128), 0, st, a);
-  else
-    hipLaunchKernelGGL((fwd_mfma_kernel<NH, false>), dim3((unsigned)grid), dim3(NH * 128), 0, st, a);
+  const dim3 grid((unsigned)(units * nchunk)), block(NH * 128);
+  const bool packed = a.cu != nullptr;
+  if (a.o_fp32) {
+    if (packed) hipLaunchKernelGGL((fwd_mfma_kernel<NH, true, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((fwd_mfma_kernel<NH, true, false>), grid, block, 0, st, a);
+  } else {
+    if (packed) hipLaunchKernelGGL((fwd_mfma_kernel<NH, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((fwd_mfma_kernel<NH, false, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 
@@ -482,6 +518,8 @@ hipError_t launch_fwd_mfma(const Shape& s, const void* q, const void* k, const v
   a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.G; a.N = s.N; a.C = s.C; a.cap = s.cap;
   a.c2 = s.scale * kLog2e;
   a.lens = s.lens;
+  a.cu = s.cu;
+  a.T = s.T;
   const long long units = (long long)s.B * s.Hkv * s.C;
   // the G heads of a group are covered by chunks of 2 heads, then 1: two
   // 4-wavefront workgroups per CU drift out of step, so one's barrier and

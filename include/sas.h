@@ -158,8 +158,9 @@ typedef struct sas_problem {
                          and empty gate rows as for seq_lens; rows of
                          other sequences are never read as keys nor
                          written.  Offsets are clamped into [0, T] and
-                         lengths into [0, N].  Exclusive with seq_lens;
-                         vector-ALU path.                                     */
+                         lengths into [0, N].  Exclusive with seq_lens.
+                         bf16 / D = 128 / b = 64 problems with the method's
+                         gates run on the matrix-core path.                   */
   int64_t total_tokens; /* T: rows per head of the packed tensors, in
                          [1, B * N] (ignored without cu_seqlens)              */
 } sas_problem;

@@ -140,6 +140,11 @@ PACKED = [
      "softmax", "inner", "soft", "group"),
     ("packed_outer_sigmoid_bf16", 2, 8, 2, 512, 128, 64, 3, "bf16", (449, 130),
      "sigmoid", "outer", "soft", "group"),
+    # matrix-core path: ragged blocks inside and at the end of the packed tensors
+    ("packed_mfma_g4_ragged_end", 4, 8, 2, 1024, 128, 64, 4, "bf16", (1024, 65, 1, 700),
+     "softmax", "inner", "soft", "group"),
+    ("packed_mfma_g5_raw", 2, 10, 2, 640, 128, 64, 3, "bf16", (383, 130),
+     "raw", "inner", "soft", "group"),
     ("packed_heads_hard_ste_fp32", 2, 4, 2, 256, 64, 32, 3, "fp32", (200, 33),
      "softmax", "inner", "hard_ste", "head"),
 ]
@@ -159,20 +164,26 @@ def test_packed_varlen_full_parity(case):
     packed_parity(w, K, lens, cap=cap, gate_act=act, gate_pos=pos, gate_rank=rank)
 
 
-def test_packed_matches_padded_bitwise():
+@pytest.mark.parametrize("shape", [(3, 4, 2, 256, 64, 16, 4, "fp32", (100, 256, 37)),
+                                   (3, 8, 2, 1024, 128, 64, 4, "bf16", (1024, 577, 64))],
+                         ids=["vector_alu", "matrix_core"])
+def test_packed_matches_padded_bitwise(shape):
     """The same batch packed (cu_seqlens) and padded (seq_lens) gives bit-identical
-    rows: the kernels take the same steps, only the row addresses differ."""
-    lens = (100, 256, 37)
-    w = workloads.custom(3, 4, 2, 256, 64, 16, 4, dtype="fp32", seed=8, score_std=2.0)
+    rows: the kernels take the same steps, only the row addresses differ (and
+    masked rows read clamped copies, which never reach a result)."""
+    B, Hq, Hkv, N, D, blk, K, dt, lens = shape
+    w = workloads.custom(B, Hq, Hkv, N, D, blk, K, dtype=dt, seed=8, score_std=2.0)
     inp = workloads.generate(w)
-    cap = 4
-    padded = run_gpu(problem_of(w, 4, seq_lens=lens), inp, cap=cap)
-    packed = run_gpu_packed(w, 4, inp, lens, cap)
+    cap = K
+    padded = run_gpu(problem_of(w, K, seq_lens=lens), inp, cap=cap)
+    packed = run_gpu_packed(w, K, inp, lens, cap)
     n = w.seq_len
+    bits = lambda x: x.view(torch.int16 if x.dtype == torch.bfloat16 else torch.int32).numpy()  # noqa: E731
     for name in ("o", "dq", "dk", "dv"):
-        got = unpack(packed[name].numpy(), lens, n)
+        got = unpack(bits(packed[name]), lens, n)
+        want = bits(padded[name])
         for b, L in enumerate(lens):
-            assert np.array_equal(got[b, :, :L], padded[name].numpy()[b, :, :L]), name
+            assert np.array_equal(got[b, :, :L], want[b, :, :L]), name
     got = unpack_stat(packed["lse"].numpy(), lens, n)
     for b, L in enumerate(lens):
         assert np.array_equal(got[b, :, :L], padded["lse"].numpy()[b, :, :L]), "lse"
