@@ -326,12 +326,11 @@ def main():
     if args.varlen:
         variant["varlen"] = args.varlen
         variant["seq_lens"] = [int(x) for x in lens]
-    # the matrix-core kernels serve the method's default configuration at
-    # bf16 / D = 128 / b = 64 (sigmoid and raw activations included); every
-    # other configuration runs on the vector-ALU kernels
+    # the matrix-core kernels serve bf16 / D = 128 / b = 64 with inner soft
+    # gates (any activation, per-group or per-head gates, fixed or variable
+    # lengths); the outer position and hard gates run on the vector-ALU kernels
     on_mfma = (w.dtype == "bf16" and w.head_dim == 128 and w.block == 64 and
-               args.gate_pos == "inner" and args.gate_rank == "soft" and
-               args.score_heads == "group" and args.varlen != "packed")
+               args.gate_pos == "inner" and args.gate_rank == "soft")
     cap = p.default_cap()
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     inp = workloads.generate(w)
@@ -425,7 +424,8 @@ def main():
     # algorithmic flops of the main kernel of each stage
     if on_mfma:
         kflops = {"fwd": 4 * D * pairs, "bwd_dq": 6 * D * pairs, "bwd_dkdv": 4 * D * pairs}
-        knames = {"fwd": "fwd_mfma_kernel<2>", "bwd_dq": "bwd_dq_kernel<4>",
+        nh = 1 if args.score_heads == "head" else 2
+        knames = {"fwd": f"fwd_mfma_kernel<{nh}>", "bwd_dq": f"bwd_dq_kernel<{2 * nh if nh > 1 else 1}>",
                   "bwd_dkdv": "bwd_dkdv_kernel"}
         bound, peak = "mfma", PEAK_BF16_TFLOPS
     else:   # vector-ALU kernels: the same algorithmic flops against the fp32 vector peak

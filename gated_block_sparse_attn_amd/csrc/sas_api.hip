@@ -123,16 +123,16 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 namespace sas {
 
 bool mfma_path(const Shape& s) {
-  return !s.fp32 && s.D == 128 && s.blk == 64 && !s.outer && !s.hard && s.Hs == s.Hkv;
+  return !s.fp32 && s.D == 128 && s.blk == 64 && !s.outer && !s.hard;
 }
 
 BwdWorkspace bwd_workspace_layout(const Shape& s) {
   BwdWorkspace w{};
-  const long long nrow = (long long)s.B * s.Hkv * s.C;  // rows == columns
+  const long long nrow = (long long)s.B * s.Hs * s.C;  // gate-table rows == columns
   // largest possible number of (row, selected block) entries
   long long per_seq = 0;
   for (int i = 0; i < s.C; ++i) per_seq += (i < s.cap ? i : s.cap);
-  const long long emax = per_seq * s.B * s.Hkv;
+  const long long emax = per_seq * s.B * s.Hs;
   w.words = (s.C + 31) / 32;
   size_t off = 0;
   w.delta = off;    off = align256(off + sizeof(float) * (size_t)s.B * s.Hq * s.N);

@@ -64,6 +64,7 @@ struct BwdArgs {
   int32_t* chunk_rank; int32_t* chunk_hist; int32_t* chunk_order;
   long long ncol;  // B * Hkv * C (rows of the score table == columns)
   int Hq, Hkv, G, N, C, cap, W, o_fp32;
+  int Hs, Gs;       // score heads (gate-table rows per batch) and query heads per score head
   int head_base, nchunk;
   float c2, scale;
   const int32_t* lens;   // variable-length batch (padded layout): valid tokens, or nullptr
@@ -190,7 +191,7 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
   const int hk = bhk % a.Hkv;
   const int bb = bhk / a.Hkv;
   const int h = hk * a.G + a.head_base + chunk * NH + (w >> 1);
-  const long long row = (long long)bhk * a.C + i;
+  const long long row = ((long long)bb * a.Hs + h / a.Gs) * a.C + i;   // the head's gate row
   const int cnt = min(a.sel_cnt[row], a.cap);
   const int32_t* sel = a.sel_idx + row * a.cap;
   const float* lgrow = a.lg + row * a.C;
@@ -700,11 +701,16 @@ bwd_dkdv_kernel(BwdArgs a) {
   const int L = a.collen[col];
   const int e0 = c * kColChunk;
   const int ne = min(L, e0 + kColChunk) - e0;
+  // column col = (batch, score head s, key block j); with per-head gates a
+  // kv head's G query heads each have their own columns (G = 1 step per
+  // entry and half), which all add into the kv head's dK / dV partials
   const int j = (int)(col % a.C);
-  const long long bhk = col / a.C;
-  const int hk = (int)(bhk % a.Hkv);
-  const int bb = (int)(bhk / a.Hkv);
-  const int G = a.G;
+  const long long bs = col / a.C;   // gate-table row base: batch * Hs + s
+  const int sh = (int)(bs % a.Hs);
+  const int bb = (int)(bs / a.Hs);
+  const int hk = sh * a.Gs / a.G;
+  const long long bhk = (long long)bb * a.Hkv + hk;
+  const int G = a.Gs;   // query heads per column (the kv group's G with group gates)
   constexpr bool packed = PACKED;
   const Span sp = seq_span(a, bb);
   // A packed batch has no rows for a key block past its sequence's end (no
@@ -719,10 +725,10 @@ bwd_dkdv_kernel(BwdArgs a) {
     const int i = a.collist[a.coloff[col] + e0 + lane];
     if (wv == 0) {
       itab[lane] = i;
-      btab[lane] = i == j ? 0.0f : a.lg[(bhk * a.C + i) * a.C + j] * kLog2e;
+      btab[lane] = i == j ? 0.0f : a.lg[(bs * a.C + i) * a.C + j] * kLog2e;
     }
-    rowbase = ((long long)bb * a.Hq + hk * G) * a.N + (long long)i * BLK;
-    prow = (sp.start + (long long)i * BLK) * a.Hq + hk * G;
+    rowbase = ((long long)bb * a.Hq + sh * G) * a.N + (long long)i * BLK;
+    prow = (sp.start + (long long)i * BLK) * a.Hq + sh * G;
     vrem = sp.n - i * BLK;
   }
 
@@ -1044,13 +1050,13 @@ bwd_dkdv_kernel(BwdArgs a) {
   // dLogG[i, j] of every entry with i != j (key halves added in order)
   if (wv == 1 && lane < ne) {
     const int ib = itab[lane];
-    if (ib != j) a.dlg[(bhk * a.C + ib) * a.C + j] = gtab[lane] + gtab[kColChunk + lane];
+    if (ib != j) a.dlg[(bs * a.C + ib) * a.C + j] = gtab[lane] + gtab[kColChunk + lane];
   }
 
   // epilogue: A writes dV, B writes dK (times the softmax scale), keys kh*32 + l32
   const long long orow = bhk * a.N + (long long)j * BLK + kh * 32;
   const float mul = role == 0 ? 1.0f : a.scale;
-  if (nch == 1) {
+  if (nch == 1 && a.Gs == a.G) {   // the only contributor to these rows
     bf16* dst = role == 0 ? a.dv : a.dk;
     const int key = j * BLK + kh * 32 + l32;
     if (packed && key >= sp.n) return;   // the row belongs to no sequence of this batch
@@ -1079,13 +1085,15 @@ bwd_dkdv_kernel(BwdArgs a) {
 // One workgroup per (column, quarter of its 64 x 128 tile); each lane sums
 // 8 consecutive fp32 of dK and of dV over the column's chunks, in chunk order
 // (deterministic), four chunks' loads in flight at a time.
+// With per-head gates the G score-head columns of a kv column are summed in
+// head order.
 __global__ void __launch_bounds__(256) reduce_kernel(BwdArgs a) {
-  const long long col = blockIdx.x >> 2;
-  const int c0 = a.chunkoff[col];
-  const int nch = a.chunkoff[col + 1] - c0;
-  if (nch <= 1) return;
-  const int j = (int)(col % a.C);
-  const long long bhk = col / a.C;
+  const long long kcol = blockIdx.x >> 2;   // (batch, kv head, key block)
+  const int j = (int)(kcol % a.C);
+  const long long bhk = kcol / a.C;
+  const int ns = a.G / a.Gs;                 // score-head columns per kv column
+  const long long col = ((bhk / a.Hkv) * a.Hs + (bhk % a.Hkv) * ns) * a.C + j;   // the first
+  if (ns == 1 && a.chunkoff[col + 1] - a.chunkoff[col] <= 1) return;   // written directly
   const long long orow = bhk * a.N + (long long)j * BLK;
   const int e = (threadIdx.x + (blockIdx.x & 3) * 256) * 8;
   // packed batch: key row e / HD of the block, if it belongs to the sequence
@@ -1096,9 +1104,12 @@ __global__ void __launch_bounds__(256) reduce_kernel(BwdArgs a) {
     if (key >= sp.n) return;
     prow = (sp.start + key) * a.Hkv + (int)(bhk % a.Hkv);
   }
-  const float* base = a.partial + (long long)c0 * 2 * 8192 + e;
   f32x4 sk[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
   f32x4 sv[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+  for (int t = 0; t < ns; ++t) {
+  const int c0 = a.chunkoff[col + (long long)t * a.C];
+  const int nch = a.chunkoff[col + (long long)t * a.C + 1] - c0;
+  const float* base = a.partial + (long long)c0 * 2 * 8192 + e;
   int cc = 0;
   for (; cc + 4 <= nch; cc += 4) {
     f32x4 lk[4][2], lv[4][2];
@@ -1122,6 +1133,7 @@ __global__ void __launch_bounds__(256) reduce_kernel(BwdArgs a) {
       sk[h] += *(const f32x4*)(pk + 4 * h);
       sv[h] += *(const f32x4*)(pk + 8192 + 4 * h);
     }
+  }
   }
   bf16x8 ok, ov;
 #pragma unroll
@@ -1167,7 +1179,9 @@ BwdArgs make_bwd_args(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorks
   a.chunk_rank = (int32_t*)(ws + wl.chunk_rank);
   a.chunk_hist = (int32_t*)(ws + wl.chunk_hist);
   a.chunk_order = (int32_t*)(ws + wl.chunk_order);
-  a.ncol = (long long)s.B * s.Hkv * s.C;
+  a.ncol = (long long)s.B * s.Hs * s.C;   // gate-table rows == columns
+  a.Hs = s.Hs;
+  a.Gs = s.Hq / s.Hs;
   a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.G; a.N = s.N; a.C = s.C; a.cap = s.cap; a.W = wl.words;
   a.o_fp32 = s.o_fp32;
   a.c2 = s.scale * kLog2e;
@@ -1182,11 +1196,17 @@ BwdArgs make_bwd_args(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorks
 hipError_t launch_bwd_dq_mfma(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorkspace& wl,
                               hipStream_t st) {
   BwdArgs a = make_bwd_args(s, p, ws, wl);
-  const long long units = a.ncol;
+  const long long units = (long long)s.B * s.Hkv * s.C;   // (batch, kv head, query block)
   hipError_t e;
-  // query-major pass (heads in chunks of 4, 2, 1)
+  // query-major pass (heads in chunks of 4, 2, 1; one head per chunk when
+  // every head has its own gates and selection)
   int h = 0;
-  if (s.G / 4 > 0) {
+  if (a.Gs < 2 && s.G > 1) {
+    e = launch_dq<1>(a, 0, s.G, units, st);
+    if (e != hipSuccess) return e;
+    h = s.G;
+  }
+  if (s.G / 4 > 0 && h == 0) {
     e = launch_dq<4>(a, h, s.G / 4, units, st);
     if (e != hipSuccess) return e;
     h += 4 * (s.G / 4);
@@ -1232,7 +1252,8 @@ hipError_t launch_bwd_dkdv_mfma(const Shape& s, const BwdPtrs& p, char* ws,
     hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3((unsigned)wl.max_chunks), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)(a.ncol * 4)), dim3(256), 0, st, a);
+  const long long kcols = (long long)s.B * s.Hkv * s.C;   // (batch, kv head, key block)
+  hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)(kcols * 4)), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.dscores == nullptr) return hipSuccess;
   return launch_dscores(s, p.dlog_gate, p.log_gate, p.dscores, st);

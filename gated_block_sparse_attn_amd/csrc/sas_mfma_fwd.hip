@@ -62,6 +62,7 @@ struct FwdArgs {
   const float* lg; const int32_t* sel_idx; const int32_t* sel_cnt;
   void* o; float* lse;
   int Hq, Hkv, G, N, C, cap;
+  int Hs, Gs;     // score heads (gate-table rows per batch) and query heads per score head
   int o_fp32;     // store o as float32 (else bf16)
   int head_base;  // first head (within its kv group) of chunk 0 of this launch
   int nchunk;     // chunks of NW heads per (batch, kv head, query block)
@@ -197,7 +198,9 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
   const int hk = bhk % a.Hkv;
   const int bb = bhk / a.Hkv;
   const int h = hk * a.G + a.head_base + chunk * NH + (w >> 1);
-  const long long row = (long long)bhk * a.C + i;
+  // gate-table row of this workgroup's heads (all of a chunk share it: with
+  // per-head gates a chunk is one head)
+  const long long row = ((long long)bb * a.Hs + h / a.Gs) * a.C + i;
   const int cnt = min(a.sel_cnt[row], a.cap);
   const int32_t* sel = a.sel_idx + row * a.cap;
   const float* lgrow = a.lg + row * a.C;
@@ -520,7 +523,12 @@ hipError_t launch_fwd_mfma(const Shape& s, const void* q, const void* k, const v
   a.lens = s.lens;
   a.cu = s.cu;
   a.T = s.T;
+  a.Hs = s.Hs;
+  a.Gs = s.Hq / s.Hs;
   const long long units = (long long)s.B * s.Hkv * s.C;
+  if (a.Gs < 2) {   // gates per query head: every head selects its own blocks
+    return launch_chunks<1>(a, 0, s.G, units, st);
+  }
   // the G heads of a group are covered by chunks of 2 heads, then 1: two
   // 4-wavefront workgroups per CU drift out of step, so one's barrier and
   // softmax phases overlap the other's matrix work (a chunk of 4 heads in one

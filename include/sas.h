@@ -131,8 +131,7 @@ typedef struct sas_problem {
                          per-group selection of the paper's GQA setting);
                          Hq: one per query head (the training kernel's
                          per-head log gates, App. E); score head s covers
-                         query heads s*(Hq/Hs) .. +Hq/Hs-1.  Hs = Hq with
-                         G > 1 runs on the vector-ALU path.                  */
+                         query heads s*(Hq/Hs) .. +Hq/Hs-1.                  */
   const int32_t* seq_lens; /* optional DEVICE int32 [B]: valid tokens n_b of each
                          sequence (variable-length batch in the padded
                          [.., N, ..] layout; NULL = every sequence has N).

@@ -80,6 +80,10 @@ VARIANTS = [
      "head"),
     ("heads_outer_bf16_d128_b64_g5", 1, 10, 2, 384, 128, 64, 2, "bf16", "softmax", "outer", "soft",
      "head"),
+    # per-head gates on the matrix-core path: G = 5, sigmoid, a 16-block budget
+    ("heads_mfma_g5", 2, 10, 2, 640, 128, 64, 3, "bf16", "softmax", "inner", "soft", "head"),
+    ("heads_mfma_sigmoid_g4", 1, 8, 2, 1024, 128, 64, 4, "bf16", "sigmoid", "inner", "soft", "head"),
+    ("heads_mfma_k16_g4", 1, 8, 2, 2048, 128, 64, 16, "bf16", "softmax", "inner", "soft", "head"),
 ]
 
 
@@ -145,6 +149,8 @@ PACKED = [
      "softmax", "inner", "soft", "group"),
     ("packed_mfma_g5_raw", 2, 10, 2, 640, 128, 64, 3, "bf16", (383, 130),
      "raw", "inner", "soft", "group"),
+    ("packed_mfma_heads_g4", 3, 8, 2, 768, 128, 64, 3, "bf16", (700, 64, 301),
+     "softmax", "inner", "soft", "head"),
     ("packed_heads_hard_ste_fp32", 2, 4, 2, 256, 64, 32, 3, "fp32", (200, 33),
      "softmax", "inner", "hard_ste", "head"),
 ]
