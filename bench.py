@@ -326,11 +326,11 @@ def main():
     if args.varlen:
         variant["varlen"] = args.varlen
         variant["seq_lens"] = [int(x) for x in lens]
-    # the matrix-core kernels serve bf16 / D = 128 / b = 64 with inner soft
-    # gates (any activation, per-group or per-head gates, fixed or variable
-    # lengths); the outer position and hard gates run on the vector-ALU kernels
+    # the matrix-core kernels serve bf16 / D = 128 / b = 64 with inner gates
+    # (any activation, soft or hard, per-group or per-head, fixed or variable
+    # lengths); the outer position runs on the vector-ALU kernels
     on_mfma = (w.dtype == "bf16" and w.head_dim == 128 and w.block == 64 and
-               args.gate_pos == "inner" and args.gate_rank == "soft")
+               args.gate_pos == "inner")
     cap = p.default_cap()
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     inp = workloads.generate(w)

@@ -84,6 +84,13 @@ __device__ __forceinline__ long long stat_of(const GenArgs& a, int b, const Seq&
   return a.cu != nullptr ? (long long)h * a.T + sq.start + n : ((long long)b * a.Hq + h) * a.N + n;
 }
 
+// Index of token n of sequence b, query head h, in the workspace's Delta
+// array: padded order [B, Hq, N] in every layout (the matrix-core kernels
+// use the same order, so either path's Delta serves the dropped-block pass).
+__device__ __forceinline__ long long ws_of(const GenArgs& a, int b, int h, int n) {
+  return ((long long)b * a.Hq + h) * a.N + n;
+}
+
 // Stage the BLK rows of key block kb of (sequence b, kv head hk) of a K or V
 // tensor into LDS as fp32.  In the packed layout rows past the sequence's
 // end read as zero (they belong to the next sequence or lie past the tensor);
@@ -241,7 +248,7 @@ __global__ void __launch_bounds__(64) bwd_q_generic_kernel(GenArgs a) {
       }
     }
     if (a.cu != nullptr ? active : t < BLK) {
-      a.delta[qs] = dx;
+      a.delta[ws_of(a, bb, h, i * BLK + t)] = dx;
       T* dqrow = (T*)a.dq + qr * D;
 #pragma unroll
       for (int d = 0; d < D; ++d) st(dqrow + d, dq[d] * a.scale);
@@ -318,7 +325,7 @@ __global__ void __launch_bounds__(64) bwd_kv_generic_kernel(GenArgs a) {
         }
         dp *= gv;
         const float p = exp2f(x * a.c2 + beta - a.lse[qs] * kLog2e);
-        const float ds = p * (dp - a.delta[qs]);
+        const float ds = p * (dp - a.delta[ws_of(a, bb, h, i * BLK + tq)]);
         gsum += a.outer ? p * dp : ds;
         const float pg = p * gv;
 #pragma unroll
@@ -388,7 +395,7 @@ __global__ void __launch_bounds__(64) ste_dropped_kernel(GenArgs a) {
       const T* qrow = (const T*)a.q + qr * D;
       const T* drow = (const T*)a.d_o + qr * D;
       const float lse2 = a.lse[qs] * kLog2e;
-      const float delta = a.delta[qs];
+      const float delta = a.delta[ws_of(a, bb, h, i * BLK + t)];
 #pragma unroll 1
       for (int u = 0; u < BLK; ++u) {
         float x = 0.0f, dp = 0.0f;
@@ -498,6 +505,21 @@ hipError_t launch_bwd_dq_generic(const Shape& s, const BwdPtrs& p, char* ws,
   return e;
 }
 
+// Gate gradients of the dropped blocks of hard Top-K gates (any path: the
+// workspace's Delta array has the same layout on both).
+hipError_t launch_ste_dropped(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorkspace& wl,
+                              hipStream_t st) {
+  const GenArgs a = bwd_args(s, p, ws, wl);
+  return dispatch(s, [&](auto tp, auto dc, auto bc) {
+    using T = std::remove_pointer_t<decltype(tp)>;
+    constexpr int D = decltype(dc)::value, BLK = decltype(bc)::value;
+    const size_t lds = 2 * BLK * D * sizeof(float);
+    hipLaunchKernelGGL((ste_dropped_kernel<T, D, BLK>), dim3(s.C, s.B * s.Hs), dim3(64), lds, st,
+                       a);
+    return hipGetLastError();
+  });
+}
+
 hipError_t launch_bwd_dkdv_generic(const Shape& s, const BwdPtrs& p, char* ws,
                                    const BwdWorkspace& wl, hipStream_t st) {
   const GenArgs a = bwd_args(s, p, ws, wl);
@@ -505,16 +527,7 @@ hipError_t launch_bwd_dkdv_generic(const Shape& s, const BwdPtrs& p, char* ws,
     using T = std::remove_pointer_t<decltype(tp)>;
     return bwd_kv_launch<T, decltype(dc)::value, decltype(bc)::value>(a, s, st);
   });
-  if (e == hipSuccess && s.hard) {   // gate gradients of the dropped blocks
-    e = dispatch(s, [&](auto tp, auto dc, auto bc) {
-      using T = std::remove_pointer_t<decltype(tp)>;
-      constexpr int D = decltype(dc)::value, BLK = decltype(bc)::value;
-      const size_t lds = 2 * BLK * D * sizeof(float);
-      hipLaunchKernelGGL((ste_dropped_kernel<T, D, BLK>), dim3(s.C, s.B * s.Hs), dim3(64), lds,
-                         st, a);
-      return hipGetLastError();
-    });
-  }
+  if (e == hipSuccess && s.hard) e = launch_ste_dropped(s, p, ws, wl, st);
   if (e != hipSuccess || p.dscores == nullptr) return e;
   return launch_dscores(s, p.dlog_gate, p.log_gate, p.dscores, st);
 }

@@ -81,6 +81,8 @@ hipError_t launch_bwd_dq_generic(const Shape& s, const BwdPtrs& p, char* ws,
                                  const BwdWorkspace& wl, hipStream_t st);
 hipError_t launch_bwd_dkdv_generic(const Shape& s, const BwdPtrs& p, char* ws,
                                    const BwdWorkspace& wl, hipStream_t st);
+hipError_t launch_ste_dropped(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorkspace& wl,
+                              hipStream_t st);
 hipError_t launch_bwd_dq_mfma(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorkspace& wl,
                               hipStream_t st);
 hipError_t launch_bwd_dkdv_mfma(const Shape& s, const BwdPtrs& p, char* ws,

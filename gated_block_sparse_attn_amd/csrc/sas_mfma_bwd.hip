@@ -65,6 +65,7 @@ struct BwdArgs {
   long long ncol;  // B * Hkv * C (rows of the score table == columns)
   int Hq, Hkv, G, N, C, cap, W, o_fp32;
   int Hs, Gs;       // score heads (gate-table rows per batch) and query heads per score head
+  int hard;         // hard Top-K gates: unit gates on the selected blocks
   int head_base, nchunk;
   float c2, scale;
   const int32_t* lens;   // variable-length batch (padded layout): valid tokens, or nullptr
@@ -385,7 +386,7 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
   auto load_sel = [&](int e0) {
     const int e = e0 + lane;
     selv = e < cnt ? sel[e] : 0;
-    betav = e < cnt ? lgrow[selv] * kLog2e : 0.0f;
+    betav = (e < cnt && !a.hard) ? lgrow[selv] * kLog2e : 0.0f;   // hard gates: unit
     settle(betav);
   };
   load_sel(0);
@@ -430,6 +431,135 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
       for (int y = 0; y < 4; ++y) r[y] = (bf16)(row_valid ? dqacc[dt][q4 * 4 + y] * a.scale : 0.0f);
       *(bf16x4*)(dqp + dt * 32 + q4 * 8) = r;
     }
+}
+
+// ---------------------------------------------------------------------------
+// hard Top-K gates: gate gradients of the dropped blocks
+// ---------------------------------------------------------------------------
+// Straight-through estimator (Sec. 4.1 "Ranking preservation", Eq. 7): the
+// gate gradient of a dropped historical block m of query block i is the
+// attention mass its keys would get under the selected set's normaliser,
+// exp(z - lse), times (dP - Delta), summed over the block's keys, the query
+// block's rows and the score head's query heads.  One workgroup per gate row
+// (batch, score head s, query block i): four wavefronts = two heads x two
+// 32-row halves per round, rounds over the row's Gs heads; the dropped
+// blocks (m < i, not selected) stream through a double-buffered LDS tile;
+// per tile a wavefront sums P (dP - Delta) over its rows and the tile's keys
+// (S^T = K Q^T and dP^T = V dO^T on 32x32x16 MFMAs, one query row per lane),
+// with P = exp2(S c2 - LSE log2 e) from the query-major pass's -LSE copy
+// (-inf on padding rows, so they add nothing) and Delta from the same pass.
+// The four partial sums meet in LDS and are added into the row's per-block
+// accumulator in a fixed order (deterministic).
+__global__ void __launch_bounds__(256) ste_mfma_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 s_k[2][TILE];
+  __shared__ __attribute__((aligned(16))) bf16 s_v[2][TILE];
+  __shared__ float part[2][4];
+  extern __shared__ float s_dyn[];   // selection bitmask (C / 32 words), then C accumulators
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int half = w & 1;
+
+  const long long row = blockIdx.x;   // (batch * Hs + s) * C + i
+  const int i = (int)(row % a.C);
+  const long long bs = row / a.C;
+  const int sh = (int)(bs % a.Hs);
+  const int bb = (int)(bs / a.Hs);
+  const int hk = sh * a.Gs / a.G;
+  const long long bhk = (long long)bb * a.Hkv + hk;
+  const int cnt = min(a.sel_cnt[row], a.cap);
+  const int32_t* sel = a.sel_idx + row * a.cap;
+  const Span sp = seq_span(a, bb);
+  const bool packed = a.cu != nullptr;
+  // no dropped block (every historical block selected) or no valid query:
+  // nothing to write (uniform; before any copy or barrier)
+  if (i - cnt <= 0 || i * BLK >= sp.n) return;
+
+  const int words = (a.C + 31) >> 5;
+  uint32_t* selmask = (uint32_t*)s_dyn;
+  float* accm = s_dyn + words;
+  for (int x = tid; x < words; x += blockDim.x) selmask[x] = 0u;
+  for (int x = tid; x < i; x += blockDim.x) accm[x] = 0.0f;
+  __syncthreads();
+  for (int e = tid; e < cnt; e += blockDim.x) {
+    const int m = min(max(sel[e], 0), a.C - 1);
+    atomicOr(&selmask[m >> 5], 1u << (m & 31));
+  }
+  __syncthreads();
+  // the first dropped block after m (i when there is none); uniform
+  auto next_dropped = [&](int m) {
+    for (++m; m < i; ++m)
+      if (((selmask[m >> 5] >> (m & 31)) & 1u) == 0u) return m;
+    return i;
+  };
+  const long long kv_stride = packed ? (long long)a.Hkv * HD : HD;
+  auto load_tile = [&](int kb, int stg) {   // dropped blocks lie before i: full tiles
+    const long long t0 = packed ? ((sp.start + (long long)kb * BLK) * a.Hkv + hk) * HD
+                                : (bhk * a.N + (long long)kb * BLK) * HD;
+    tile_to_lds<4>(s_k[stg], a.k + t0, kv_stride, BLK - 1, w, lane);
+    tile_to_lds<4>(s_v[stg], a.v + t0, kv_stride, BLK - 1, w, lane);
+  };
+
+  const int m0 = next_dropped(-1);
+  const int rounds = (a.Gs + 1) / 2;
+  for (int r = 0; r < rounds; ++r) {
+    const int hl = 2 * r + (w >> 1);          // head of this wavefront within the score head
+    const bool on = hl < a.Gs;                 // uniform per wavefront
+    const int h = sh * a.Gs + (on ? hl : 0);
+    const int tok = min(i * BLK + half * 32 + l32, sp.n - 1);
+    const long long wsr = ((long long)bb * a.Hq + h) * a.N + (long long)i * BLK + half * 32 + l32;
+    const long long qt = packed ? (sp.start + tok) * a.Hq + h : wsr;
+    bf16x8 qf[8], dof[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      qf[ks] = *(const bf16x8*)(a.q + qt * HD + ks * 16 + g * 8);
+      dof[ks] = *(const bf16x8*)(a.d_o + qt * HD + ks * 16 + g * 8);
+    }
+    const float nl = a.lsen[wsr];      // -LSE log2(e), -inf on padding rows
+    const float dlt = a.delta[wsr];    // sum of P dP over the row's attended keys
+    load_tile(m0, 0);
+    wait_vm();
+    __syncthreads();
+    int m = m0, stg = 0, par = 0;
+    while (m < i) {
+      const int mn = next_dropped(m);
+      if (mn < i) load_tile(mn, stg ^ 1);   // prefetch the next dropped block
+      float acc = 0.0f;
+      if (on) {
+        const bf16* Ks = s_k[stg];
+        const bf16* Vs = s_v[stg];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          const int rr = kh * 32 + l32;
+          f32x16 sc, dp;
+#pragma unroll
+          for (int x = 0; x < 16; ++x) { sc[x] = 0.0f; dp[x] = 0.0f; }
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) {
+            sc = mfma32(*(const bf16x8*)(Ks + swz(rr, ks * 2 + g)), qf[ks], sc);
+            dp = mfma32(*(const bf16x8*)(Vs + swz(rr, ks * 2 + g)), dof[ks], dp);
+          }
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj)
+            acc = fmaf(__builtin_amdgcn_exp2f(fmaf(sc[jj], a.c2, nl)), dp[jj] - dlt, acc);
+        }
+      }
+      acc = wave_sum(acc);
+      if (lane == 0) part[par][w] = acc;
+      wait_vm();
+      __syncthreads();   // partials of block m; block mn staged
+      if (tid == 0) accm[m] += ((part[par][0] + part[par][1]) + part[par][2]) + part[par][3];
+      m = mn;
+      stg ^= 1;
+      par ^= 1;
+    }
+    __syncthreads();   // the next round reuses the tile buffers
+  }
+  float* drow = a.dlg + row * a.C;
+  for (int x = tid; x < i; x += blockDim.x)
+    if (((selmask[x >> 5] >> (x & 31)) & 1u) == 0u) drow[x] = accm[x];
 }
 
 // ---------------------------------------------------------------------------
@@ -725,7 +855,7 @@ bwd_dkdv_kernel(BwdArgs a) {
     const int i = a.collist[a.coloff[col] + e0 + lane];
     if (wv == 0) {
       itab[lane] = i;
-      btab[lane] = i == j ? 0.0f : a.lg[(bs * a.C + i) * a.C + j] * kLog2e;
+      btab[lane] = (i == j || a.hard) ? 0.0f : a.lg[(bs * a.C + i) * a.C + j] * kLog2e;
     }
     rowbase = ((long long)bb * a.Hq + sh * G) * a.N + (long long)i * BLK;
     prow = (sp.start + (long long)i * BLK) * a.Hq + sh * G;
@@ -1182,6 +1312,7 @@ BwdArgs make_bwd_args(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorks
   a.ncol = (long long)s.B * s.Hs * s.C;   // gate-table rows == columns
   a.Hs = s.Hs;
   a.Gs = s.Hq / s.Hs;
+  a.hard = s.hard;
   a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.G; a.N = s.N; a.C = s.C; a.cap = s.cap; a.W = wl.words;
   a.o_fp32 = s.o_fp32;
   a.c2 = s.scale * kLog2e;
@@ -1255,6 +1386,13 @@ hipError_t launch_bwd_dkdv_mfma(const Shape& s, const BwdPtrs& p, char* ws,
   const long long kcols = (long long)s.B * s.Hkv * s.C;   // (batch, kv head, key block)
   hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)(kcols * 4)), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  // hard gates: the gate gradients of the dropped blocks (straight-through
+  // estimator); the key-major pass above wrote those of the selected blocks
+  if (s.hard) {
+    const size_t lds = sizeof(uint32_t) * ((s.C + 31) / 32) + sizeof(float) * s.C;
+    hipLaunchKernelGGL(ste_mfma_kernel, dim3((unsigned)a.ncol), dim3(256), lds, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (p.dscores == nullptr) return hipSuccess;
   return launch_dscores(s, p.dlog_gate, p.log_gate, p.dscores, st);
 }

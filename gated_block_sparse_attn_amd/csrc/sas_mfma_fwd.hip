@@ -63,6 +63,7 @@ struct FwdArgs {
   void* o; float* lse;
   int Hq, Hkv, G, N, C, cap;
   int Hs, Gs;     // score heads (gate-table rows per batch) and query heads per score head
+  int hard;       // hard Top-K gates: the selected blocks carry unit gates
   int o_fp32;     // store o as float32 (else bf16)
   int head_base;  // first head (within its kv group) of chunk 0 of this launch
   int nchunk;     // chunks of NW heads per (batch, kv head, query block)
@@ -265,7 +266,7 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
   auto load_sel = [&](int e0) {
     const int e = e0 + lane;
     selv = e < cnt ? sel[e] : 0;
-    betav = e < cnt ? lgrow[selv] * kLog2e : 0.0f;
+    betav = (e < cnt && !a.hard) ? lgrow[selv] * kLog2e : 0.0f;   // hard gates: unit
     settle(betav);
   };
   // block and log gate of tile t (t = 0: the diagonal block, gate 0; tiles
@@ -525,6 +526,7 @@ hipError_t launch_fwd_mfma(const Shape& s, const void* q, const void* k, const v
   a.T = s.T;
   a.Hs = s.Hs;
   a.Gs = s.Hq / s.Hs;
+  a.hard = s.hard;
   const long long units = (long long)s.B * s.Hkv * s.C;
   if (a.Gs < 2) {   // gates per query head: every head selects its own blocks
     return launch_chunks<1>(a, 0, s.G, units, st);

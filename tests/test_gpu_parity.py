@@ -84,6 +84,10 @@ VARIANTS = [
     ("heads_mfma_g5", 2, 10, 2, 640, 128, 64, 3, "bf16", "softmax", "inner", "soft", "head"),
     ("heads_mfma_sigmoid_g4", 1, 8, 2, 1024, 128, 64, 4, "bf16", "sigmoid", "inner", "soft", "head"),
     ("heads_mfma_k16_g4", 1, 8, 2, 2048, 128, 64, 16, "bf16", "softmax", "inner", "soft", "head"),
+    # hard gates on the matrix-core path (dropped-block gradients from the vector-ALU pass)
+    ("hard_ste_mfma_heads_g4", 1, 8, 2, 768, 128, 64, 3, "bf16", "softmax", "inner", "hard_ste",
+     "head"),
+    ("hard_ste_mfma_g5", 1, 10, 2, 640, 128, 64, 4, "bf16", "softmax", "inner", "hard_ste"),
 ]
 
 
@@ -114,6 +118,8 @@ VARLEN = [
      "softmax", "inner", "soft", "group"),
     ("varlen_mfma_g5_sigmoid", 2, 10, 2, 640, 128, 64, 3, "bf16", (1, 383),
      "sigmoid", "inner", "soft", "group"),
+    ("varlen_mfma_hard_ste", 2, 8, 2, 640, 128, 64, 3, "bf16", (640, 200),
+     "softmax", "inner", "hard_ste", "group"),
     ("varlen_outer_sigmoid_bf16", 2, 8, 2, 512, 128, 64, 3, "bf16", (449, 130),
      "sigmoid", "outer", "soft", "group"),
     ("varlen_heads_hard_ste_fp32", 2, 4, 2, 256, 64, 16, 3, "fp32", (200, 33),
@@ -151,6 +157,8 @@ PACKED = [
      "raw", "inner", "soft", "group"),
     ("packed_mfma_heads_g4", 3, 8, 2, 768, 128, 64, 3, "bf16", (700, 64, 301),
      "softmax", "inner", "soft", "head"),
+    ("packed_mfma_hard_ste", 2, 8, 2, 640, 128, 64, 3, "bf16", (577, 130),
+     "softmax", "inner", "hard_ste", "group"),
     ("packed_heads_hard_ste_fp32", 2, 4, 2, 256, 64, 32, 3, "fp32", (200, 33),
      "softmax", "inner", "hard_ste", "head"),
 ]
