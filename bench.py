@@ -329,8 +329,7 @@ def main():
     # the matrix-core kernels serve bf16 / D = 128 / b = 64 with inner gates
     # (any activation, soft or hard, per-group or per-head, fixed or variable
     # lengths); the outer position runs on the vector-ALU kernels
-    on_mfma = (w.dtype == "bf16" and w.head_dim == 128 and w.block == 64 and
-               args.gate_pos == "inner")
+    on_mfma = w.dtype == "bf16" and w.head_dim == 128 and w.block == 64
     cap = p.default_cap()
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     inp = workloads.generate(w)

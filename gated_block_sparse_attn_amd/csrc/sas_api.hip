@@ -123,7 +123,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 namespace sas {
 
 bool mfma_path(const Shape& s) {
-  return !s.fp32 && s.D == 128 && s.blk == 64 && !s.outer;
+  return !s.fp32 && s.D == 128 && s.blk == 64;
 }
 
 BwdWorkspace bwd_workspace_layout(const Shape& s) {

@@ -66,6 +66,7 @@ struct BwdArgs {
   int Hq, Hkv, G, N, C, cap, W, o_fp32;
   int Hs, Gs;       // score heads (gate-table rows per batch) and query heads per score head
   int hard;         // hard Top-K gates: unit gates on the selected blocks
+  int outer;        // outer gate position
   int head_base, nchunk;
   float c2, scale;
   const int32_t* lens;   // variable-length batch (padded layout): valid tokens, or nullptr
@@ -171,7 +172,9 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 //   keys of both operands permuted the same way).
 // K / V tiles are double-buffered in LDS: tile t + 1 is copied while tile t
 // is processed, one barrier per tile.
-template <int NH, bool PACKED>
+// OUTER: the outer gate position (Sec. 4.1, Tab. 1 row 3): P carries no gate
+// bias and the tile's gate g scales dP (dP = g dO V^T).
+template <int NH, bool PACKED, bool OUTER>
 __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
   constexpr int NW = 2 * NH;
   __shared__ __attribute__((aligned(16))) bf16 s_k[2][TILE];
@@ -308,7 +311,8 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
     constexpr bool DIAG = decltype(diag_tag)::value;
     const bf16* Ks = s_k[stg];
     const bf16* Vs = s_v[stg];
-    const float off = beta - lse2;
+    const float off = (OUTER ? 0.0f : beta) - lse2;
+    const float gv = OUTER ? __builtin_amdgcn_exp2f(beta) : 1.0f;   // outer: the tile's gate
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       const int rr = kh * 32 + l32;
@@ -352,9 +356,11 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
           if (key > qrow) pp[0] = 0.0f;
           if (key + 1 > qrow) pp[1] = 0.0f;
         }
-        dx = fmaf(pp[0], dp[jj], dx);
-        dx = fmaf(pp[1], dp[jj + 1], dx);
-        const f32x2 ds = {pp[0] * (dp[jj] - dlt), pp[1] * (dp[jj + 1] - dlt)};
+        const float dp0 = OUTER ? dp[jj] * gv : dp[jj];
+        const float dp1 = OUTER ? dp[jj + 1] * gv : dp[jj + 1];
+        dx = fmaf(pp[0], dp0, dx);
+        dx = fmaf(pp[1], dp1, dx);
+        const f32x2 ds = {pp[0] * (dp0 - dlt), pp[1] * (dp1 - dlt)};
         dsw[jj >> 3][(jj & 7) >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(ds, bf16x2));
       }
       bf16x8 db[2];
@@ -806,7 +812,9 @@ __device__ __forceinline__ void dma16_at(const void* base, unsigned voff) {
 
 // PACKED: packed variable-length batch (a compile-time switch, so the copies
 // of the fixed-length and padded layouts keep their one-base form).
-template <bool PACKED>
+// OUTER: the outer gate position (Sec. 4.1, Tab. 1 row 3): P carries no gate
+// bias, dV takes g P, dS = P (g dP - Delta) and dLogG sums P g dP.
+template <bool PACKED, bool OUTER>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[KV4_LDS];
@@ -1031,8 +1039,11 @@ bwd_dkdv_kernel(BwdArgs a) {
     constexpr int hrow = decltype(half_tag)::value * 32;
     float nl[16];
     read_stat(os, nl);
+    if (!OUTER) {
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) nl[jj] += beta;
+      for (int jj = 0; jj < 16; ++jj) nl[jj] += beta;
+    }
+    const float gv = OUTER ? __builtin_amdgcn_exp2f(beta) : 1.0f;   // outer: the entry's gate
     bf16x8 bop[2];
     f16x8 ph[2];
     rows_product_with(qn, snext, [&](int m) {
@@ -1047,7 +1058,7 @@ bwd_dkdv_kernel(BwdArgs a) {
       const int h2 = m >> 2, x0 = (m & 3) * 2;
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
-        bop[h2][x0 + x] = (bf16)e2[x];
+        bop[h2][x0 + x] = (bf16)(OUTER ? e2[x] * gv : e2[x]);   // outer: dV takes g P
         ph[h2][x0 + x] = (_Float16)e2[x];
       }
       pin(bop[h2]);
@@ -1063,7 +1074,7 @@ bwd_dkdv_kernel(BwdArgs a) {
   // dP, then dK += Q^T dS.  gsum collects the step's dS (fma with a zero
   // addend and the fp16 operand: one mixed-precision fma).
   auto window_b = [&](const char* on, const char* qs, const _Float16* px, const f32x16& dprev,
-                      f32x16& dcur, float& gsum) {
+                      f32x16& dcur, float& gsum, float gv) {
     float dl[16];
     read_stat(qs, dl);
     f16x8 ph[2];
@@ -1074,8 +1085,10 @@ bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int jj = m * 2 + x;
-        const float ds = fmaf((float)ph[jj >> 3][jj & 7], dprev[jj] - dl[jj], 0.0f);
-        gsum += ds;
+        const float pj = (float)ph[jj >> 3][jj & 7];
+        const float dpj = OUTER ? dprev[jj] * gv : dprev[jj];
+        const float ds = fmaf(pj, dpj - dl[jj], 0.0f);
+        gsum = OUTER ? fmaf(pj, dpj, gsum) : gsum + ds;   // outer: dLogG sums P g dP
         bop[jj >> 3][jj & 7] = (bf16)ds;
       }
       pin(bop[m >> 2]);
@@ -1121,6 +1134,7 @@ bwd_dkdv_kernel(BwdArgs a) {
   } else {
     float gsum = 0.0f;
     int gstep = 0, gent = 0;
+    float gvb = OUTER ? __builtin_amdgcn_exp2f(btab[0]) : 1.0f;   // gate of the dS entry (outer)
     auto step_done = [&]() {
       if (++gstep < 2 * G) return;
       const float tot = wave_sum(gsum);
@@ -1128,6 +1142,7 @@ bwd_dkdv_kernel(BwdArgs a) {
       gstep = 0;
       if (lane == 0) gtab[kh * kColChunk + gent] = tot;
       ++gent;
+      if (OUTER) gvb = __builtin_amdgcn_exp2f(btab[gent < ne ? gent : 0]);
     };
     copy_next();
     copy_next();
@@ -1142,16 +1157,16 @@ bwd_dkdv_kernel(BwdArgs a) {
     int s = 1;
 #pragma unroll 1
     for (; s + 1 < n; s += 2) {
-      window_b(oring(ok), qring(qk), pbuf(0), r0, r1, gsum);   // step s - 1 is even
+      window_b(oring(ok), qring(qk), pbuf(0), r0, r1, gsum, gvb);   // step s - 1 is even
       ring_barrier(kh);
       step_done();
       ok = inc(ok, O_SLOTS); qk = inc(qk, Q_SLOTS);
-      window_b(oring(ok), qring(qk), pbuf(1), r1, r0, gsum);
+      window_b(oring(ok), qring(qk), pbuf(1), r1, r0, gsum, gvb);
       ring_barrier(kh);
       step_done();
       ok = inc(ok, O_SLOTS); qk = inc(qk, Q_SLOTS);
     }
-    window_b(oring(ok), qring(qk), pbuf(0), r0, r1, gsum);   // dP_{n-1}; dS / dK of step n - 2
+    window_b(oring(ok), qring(qk), pbuf(0), r0, r1, gsum, gvb);   // dP_{n-1}; dS / dK of step n - 2
     ring_barrier(kh);
     step_done();
     qk = inc(qk, Q_SLOTS);
@@ -1165,8 +1180,10 @@ bwd_dkdv_kernel(BwdArgs a) {
         const f16x8 ph = *(const f16x8*)(px + (h2 * 64 + lane) * 8);
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
-          const float ds = fmaf((float)ph[x], r1[h2 * 8 + x] - dl[h2 * 8 + x], 0.0f);
-          gsum += ds;
+          const float pj = (float)ph[x];
+          const float dpj = OUTER ? r1[h2 * 8 + x] * gvb : r1[h2 * 8 + x];
+          const float ds = fmaf(pj, dpj - dl[h2 * 8 + x], 0.0f);
+          gsum = OUTER ? fmaf(pj, dpj, gsum) : gsum + ds;
           bop[h2][x] = (bf16)ds;
         }
       }
@@ -1280,12 +1297,14 @@ template <int NH>
 hipError_t launch_dq(BwdArgs a, int head_base, int nchunk, long long units, hipStream_t st) {
   a.head_base = head_base;
   a.nchunk = nchunk;
-  if (a.cu != nullptr)
-    hipLaunchKernelGGL((bwd_dq_kernel<NH, true>), dim3((unsigned)(units * nchunk)), dim3(NH * 128),
-                       0, st, a);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<NH, false>), dim3((unsigned)(units * nchunk)), dim3(NH * 128),
-                       0, st, a);
+  const dim3 grid((unsigned)(units * nchunk)), block(NH * 128);
+  const int v = (a.cu != nullptr ? 2 : 0) | (a.outer ? 1 : 0);
+  switch (v) {
+    case 0: hipLaunchKernelGGL((bwd_dq_kernel<NH, false, false>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((bwd_dq_kernel<NH, false, true>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((bwd_dq_kernel<NH, true, false>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((bwd_dq_kernel<NH, true, true>), grid, block, 0, st, a); break;
+  }
   return hipGetLastError();
 }
 
@@ -1313,6 +1332,7 @@ BwdArgs make_bwd_args(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorks
   a.Hs = s.Hs;
   a.Gs = s.Hq / s.Hs;
   a.hard = s.hard;
+  a.outer = s.outer;
   a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.G; a.N = s.N; a.C = s.C; a.cap = s.cap; a.W = wl.words;
   a.o_fp32 = s.o_fp32;
   a.c2 = s.scale * kLog2e;
@@ -1377,10 +1397,14 @@ hipError_t launch_bwd_dkdv_mfma(const Shape& s, const BwdPtrs& p, char* ws,
   const long long ntab = a.ncol * s.C;
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)min((ntab + 255) / 256, 65535LL)),
                      dim3(256), 0, st, (uint32_t*)a.dlg, ntab);
-  if (s.cu != nullptr)
-    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3((unsigned)wl.max_chunks), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3((unsigned)wl.max_chunks), dim3(256), 0, st, a);
+  const dim3 kgrid((unsigned)wl.max_chunks), kblock(256);
+  const int v = (s.cu != nullptr ? 2 : 0) | (s.outer ? 1 : 0);
+  switch (v) {
+    case 0: hipLaunchKernelGGL((bwd_dkdv_kernel<false, false>), kgrid, kblock, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((bwd_dkdv_kernel<false, true>), kgrid, kblock, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((bwd_dkdv_kernel<true, false>), kgrid, kblock, 0, st, a); break;
+    default: hipLaunchKernelGGL((bwd_dkdv_kernel<true, true>), kgrid, kblock, 0, st, a); break;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long kcols = (long long)s.B * s.Hkv * s.C;   // (batch, kv head, key block)

@@ -64,6 +64,7 @@ struct FwdArgs {
   int Hq, Hkv, G, N, C, cap;
   int Hs, Gs;     // score heads (gate-table rows per batch) and query heads per score head
   int hard;       // hard Top-K gates: the selected blocks carry unit gates
+  int outer;      // outer gate position
   int o_fp32;     // store o as float32 (else bf16)
   int head_base;  // first head (within its kv group) of chunk 0 of this launch
   int nchunk;     // chunks of NW heads per (batch, kv head, query block)
@@ -178,7 +179,10 @@ __device__ __forceinline__ void wait_vm_prev() {   // all but this window's 16 /
   else __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");
 }
 
-template <int NH, bool SPLIT, bool PACKED>
+// OUTER: the outer gate position (Sec. 4.1, Tab. 1 row 3): no logit bias;
+// the probabilities of a tile enter O += P V scaled by the tile's gate, while
+// the normaliser l sums the unscaled ones.
+template <int NH, bool SPLIT, bool PACKED, bool OUTER>
 __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
   constexpr int NW = 2 * NH;
   __shared__ __attribute__((aligned(16))) bf16 s_k[2][TILE];
@@ -333,12 +337,14 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
   // P element pair n (n = 0..7) of a unit: P = exp2(c2 s + beta - m), summed
   // into l and packed (hi, and lo when SPLIT) into the B operand of
   // O^T += V^T P^T: element jj -> k-slice jj / 8, word (jj % 8) / 2
-  auto p_pair = [&](int n, const f32x16& sc, float off, uint32_t (&pb)[2][4], uint32_t (&pl)[2][4]) {
+  auto p_pair = [&](int n, const f32x16& sc, float off, float gv, uint32_t (&pb)[2][4],
+                    uint32_t (&pl)[2][4]) {
     const int jj = 2 * n;
-    const f32x2 pp = {__builtin_amdgcn_exp2f(fmaf(sc[jj], a.c2, off)),
+    const f32x2 p0 = {__builtin_amdgcn_exp2f(fmaf(sc[jj], a.c2, off)),
                       __builtin_amdgcn_exp2f(fmaf(sc[jj + 1], a.c2, off))};
+    lrow += p0[0] + p0[1];
+    const f32x2 pp = OUTER ? f32x2{p0[0] * gv, p0[1] * gv} : p0;   // outer: g P enters O
     const bf16x2 hi = __builtin_convertvector(pp, bf16x2);
-    lrow += pp[0] + pp[1];
     uint32_t wh = __builtin_bit_cast(uint32_t, hi);
     pin(wh);
     pb[jj >> 3][(jj & 7) >> 1] = wh;
@@ -422,15 +428,16 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
       float bk;
       copy_k(tile_block(t + 2, bk), PAR);
     }
-    const float off = beta_cur - mrow;
+    const float off = (OUTER ? 0.0f : beta_cur) - mrow;
+    const float gvw = OUTER ? __builtin_amdgcn_exp2f(beta_cur) : 1.0f;   // outer: the tile's gate
     uint32_t pb[2][4], pl[2][4];
     // next unit: (t, 1) reads K_t, (t + 1, 0) reads K_{t+1}
     const bf16* kn = KH == 0 ? s_k[PAR] : s_k[PAR ^ 1];
     if (more) {
-      scores_with(kn, KH ^ 1, snext, [&](int m) { p_pair(m, scur, off, pb, pl); });
+      scores_with(kn, KH ^ 1, snext, [&](int m) { p_pair(m, scur, off, gvw, pb, pl); });
     } else {
 #pragma unroll
-      for (int n = 0; n < 8; ++n) p_pair(n, scur, off, pb, pl);
+      for (int n = 0; n < 8; ++n) p_pair(n, scur, off, gvw, pb, pl);
     }
     pv(s_v[PAR], KH, pb, pl);
     wait_vm_prev<NW>();
@@ -438,10 +445,10 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
     if (more) {
       if (KH == 0) {
         if (DIAG) mask_diag(1, snext);
-        update_max(std::false_type{}, snext, beta_cur);
+        update_max(std::false_type{}, snext, OUTER ? 0.0f : beta_cur);
       } else {
         beta_cur = beta_v;   // tile t + 1
-        update_max(std::false_type{}, snext, beta_cur);
+        update_max(std::false_type{}, snext, OUTER ? 0.0f : beta_cur);
       }
     }
   };
@@ -498,13 +505,16 @@ hipError_t launch_chunks(FwdArgs a, int head_base, int nchunk, long long units,
   a.head_base = head_base;
   a.nchunk = nchunk;
   const dim3 grid((unsigned)(units * nchunk)), block(NH * 128);
-  const bool packed = a.cu != nullptr;
-  if (a.o_fp32) {
-    if (packed) hipLaunchKernelGGL((fwd_mfma_kernel<NH, true, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((fwd_mfma_kernel<NH, true, false>), grid, block, 0, st, a);
-  } else {
-    if (packed) hipLaunchKernelGGL((fwd_mfma_kernel<NH, false, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((fwd_mfma_kernel<NH, false, false>), grid, block, 0, st, a);
+  const int v = (a.o_fp32 ? 4 : 0) | (a.cu != nullptr ? 2 : 0) | (a.outer ? 1 : 0);
+  switch (v) {
+    case 0: hipLaunchKernelGGL((fwd_mfma_kernel<NH, false, false, false>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((fwd_mfma_kernel<NH, false, false, true>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((fwd_mfma_kernel<NH, false, true, false>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((fwd_mfma_kernel<NH, false, true, true>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((fwd_mfma_kernel<NH, true, false, false>), grid, block, 0, st, a); break;
+    case 5: hipLaunchKernelGGL((fwd_mfma_kernel<NH, true, false, true>), grid, block, 0, st, a); break;
+    case 6: hipLaunchKernelGGL((fwd_mfma_kernel<NH, true, true, false>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((fwd_mfma_kernel<NH, true, true, true>), grid, block, 0, st, a); break;
   }
   return hipGetLastError();
 }
@@ -527,6 +537,7 @@ hipError_t launch_fwd_mfma(const Shape& s, const void* q, const void* k, const v
   a.Hs = s.Hs;
   a.Gs = s.Hq / s.Hs;
   a.hard = s.hard;
+  a.outer = s.outer;
   const long long units = (long long)s.B * s.Hkv * s.C;
   if (a.Gs < 2) {   // gates per query head: every head selects its own blocks
     return launch_chunks<1>(a, 0, s.G, units, st);

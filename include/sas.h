@@ -122,9 +122,9 @@ typedef struct sas_problem {
   float sm_scale;     /* scale of q.k; <= 0 selects 1/sqrt(D).  It never
                          multiplies the log gate (App. E, Alg. 3/4).          */
   int32_t gate_act;   /* a sas_gate_act (SAS_GATE_SOFTMAX for the method)      */
-  int32_t gate_pos;   /* a sas_gate_pos (SAS_GATE_INNER for the method).  The
-                         outer position runs on the vector-ALU path for every
-                         shape.                                                */
+  int32_t gate_pos;   /* a sas_gate_pos (SAS_GATE_INNER for the method).  Both
+                         positions run on the matrix-core path for bf16 with
+                         D = 128 and b = 64.                                   */
   int32_t gate_rank;  /* a sas_gate_rank (SAS_GATE_SOFT for the method)        */
   int32_t n_score_heads; /* Hs: rows of the gate tables per batch element.
                          0 or Hkv: one gate / selection per query group (the
@@ -143,8 +143,8 @@ typedef struct sas_problem {
                          written; dlog_gate and dscores 0).  Values outside
                          [0, N] are clamped into it.  Padding rows must hold
                          finite values (their content never reaches a valid
-                         row).  bf16 / D = 128 / b = 64 problems with the
-                         method's gates run on the matrix-core path.          */
+                         row).  bf16 / D = 128 / b = 64 problems run on
+                         the matrix-core path.                                */
   const int32_t* cu_seqlens; /* optional DEVICE int32 [B + 1]: packed batch
                          (the cu_seqlens convention of varlen attention):
                          sequence b holds tokens cu_seqlens[b] ..
@@ -158,8 +158,8 @@ typedef struct sas_problem {
                          other sequences are never read as keys nor
                          written.  Offsets are clamped into [0, T] and
                          lengths into [0, N].  Exclusive with seq_lens.
-                         bf16 / D = 128 / b = 64 problems with the method's
-                         gates run on the matrix-core path.                   */
+                         bf16 / D = 128 / b = 64 problems run on the
+                         matrix-core path.                                    */
   int64_t total_tokens; /* T: rows per head of the packed tensors, in
                          [1, B * N] (ignored without cu_seqlens)              */
 } sas_problem;

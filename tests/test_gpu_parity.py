@@ -88,6 +88,17 @@ VARIANTS = [
     ("hard_ste_mfma_heads_g4", 1, 8, 2, 768, 128, 64, 3, "bf16", "softmax", "inner", "hard_ste",
      "head"),
     ("hard_ste_mfma_g5", 1, 10, 2, 640, 128, 64, 4, "bf16", "softmax", "inner", "hard_ste"),
+    # outer gate position on the matrix-core path: G = 5, sigmoid / raw gates,
+    # a 16-block budget, per-head gates, and the fp32 output (split P).  Raw
+    # gates exp(s) under the outer position scale o and the gradients by the
+    # row's gate mass sum_j g_j p_j, and the bf16 error with them; scores of
+    # std 1 keep that mass near the unit scale the absolute tolerance assumes
+    ("outer_mfma_g5_sigmoid", 2, 10, 2, 1024, 128, 64, 4, "bf16", "sigmoid", "outer"),
+    ("outer_mfma_raw_k16", 1, 8, 2, 2048, 128, 64, 16, "bf16", "raw", "outer", "soft", "group",
+     "bf16", 1.0),
+    ("outer_mfma_heads_g4", 1, 8, 2, 1024, 128, 64, 4, "bf16", "softmax", "outer", "soft", "head"),
+    ("outer_mfma_fp32_out", 1, 8, 2, 768, 128, 64, 3, "bf16", "softmax", "outer", "soft", "group",
+     "fp32"),
 ]
 
 
@@ -98,11 +109,13 @@ def test_gate_variants_full_parity(case):
     name, B, Hq, Hkv, N, D, blk, K, dt, act, pos = case[:11]
     rank = case[11] if len(case) > 11 else "soft"
     heads = case[12] if len(case) > 12 else "group"
+    o_dtype = case[13] if len(case) > 13 else "bf16"
+    score_std = case[14] if len(case) > 14 else 2.0
     log(f"variant {name}")
     w = workloads.custom(B, Hq, Hkv, N, D, blk, K, dtype=dt, seed=zlib.crc32(name.encode()) % 1000,
-                         score_std=2.0, score_heads=heads)
+                         score_std=score_std, score_heads=heads)
     cap = max(1, min(K, N // blk - 1))
-    full_parity(w, K, cap=cap, gate_act=act, gate_pos=pos, gate_rank=rank)
+    full_parity(w, K, cap=cap, gate_act=act, gate_pos=pos, gate_rank=rank, o_dtype=o_dtype)
 
 
 VARLEN = [
@@ -124,6 +137,8 @@ VARLEN = [
      "sigmoid", "outer", "soft", "group"),
     ("varlen_heads_hard_ste_fp32", 2, 4, 2, 256, 64, 16, 3, "fp32", (200, 33),
      "softmax", "inner", "hard_ste", "head"),
+    ("varlen_mfma_outer_g5", 3, 10, 2, 640, 128, 64, 3, "bf16", (640, 0, 130),
+     "softmax", "outer", "soft", "group"),
 ]
 
 
@@ -161,6 +176,8 @@ PACKED = [
      "softmax", "inner", "hard_ste", "group"),
     ("packed_heads_hard_ste_fp32", 2, 4, 2, 256, 64, 32, 3, "fp32", (200, 33),
      "softmax", "inner", "hard_ste", "head"),
+    ("packed_mfma_outer_heads_g4", 3, 8, 2, 768, 128, 64, 3, "bf16", (700, 64, 301),
+     "softmax", "outer", "soft", "head"),
 ]
 
 
