@@ -53,8 +53,11 @@ struct BwdWorkspace {
   int words;         // W = ceil(C / 32)
 };
 
-// Query blocks per pass-B work item of the matrix-core backward.
+// Query blocks per pass-B work item of the matrix-core backward (per-head
+// gates: G / Gs times as many, at most kColChunkMax, so that a work item
+// covers as many 32-row steps as with one gate row per kv group).
 constexpr int kColChunk = 16;
+constexpr int kColChunkMax = 64;
 
 bool mfma_path(const Shape& s);
 BwdWorkspace bwd_workspace_layout(const Shape& s);

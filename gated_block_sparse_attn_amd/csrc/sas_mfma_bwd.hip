@@ -21,7 +21,7 @@
 //   column kernels      transpose the selection: bit (j, i) of a column mask is
 //                       set when row i selected block j; each column j then
 //                       gets the ascending list {j} u {i > j : j in I_i} and is
-//                       cut into chunks of at most kColChunk query blocks,
+//                       cut into chunks of at most a.cc query blocks,
 //                       ordered for L2 reuse.
 //   bwd_dkdv_kernel     key-major pass: four wavefronts (two pairs, one per
 //                       half of key block j) per column chunk; K_j / V_j are
@@ -67,6 +67,7 @@ struct BwdArgs {
   int Hs, Gs;       // score heads (gate-table rows per batch) and query heads per score head
   int hard;         // hard Top-K gates: unit gates on the selected blocks
   int outer;        // outer gate position
+  int cc;           // query blocks per key-major chunk
   int head_base, nchunk;
   float c2, scale;
   const int32_t* lens;   // variable-length batch (padded layout): valid tokens, or nullptr
@@ -609,7 +610,7 @@ __global__ void __launch_bounds__(1024) scan_kernel(BwdArgs a) {
   for (long long c = beg; c < end; ++c) {
     const int L = a.collen[c];
     sl += L;
-    sc += (L + kColChunk - 1) / kColChunk;
+    sc += (L + a.cc - 1) / a.cc;
   }
   s_len[t] = sl;
   s_chk[t] = sc;
@@ -628,7 +629,7 @@ __global__ void __launch_bounds__(1024) scan_kernel(BwdArgs a) {
     a.coloff[c] = ol;
     a.chunkoff[c] = oc;
     ol += L;
-    oc += (L + kColChunk - 1) / kColChunk;
+    oc += (L + a.cc - 1) / a.cc;
   }
   if (t == 1023) {
     a.coloff[a.ncol] = s_len[1023];
@@ -683,7 +684,7 @@ __global__ void chunk_count_kernel(BwdArgs a) {
   if (g >= a.chunkoff[a.ncol]) return;
   const long long col = chunk_column(a, g);
   const int c = g - a.chunkoff[col];
-  const int first = a.collist[a.coloff[col] + c * kColChunk];
+  const int first = a.collist[a.coloff[col] + c * a.cc];
   const long long key = col - col % a.C + first;   // (batch, kv head) row base + first row
   a.chunk_rank[g] = atomicAdd(&a.chunk_hist[key], 1);
 }
@@ -719,7 +720,7 @@ __global__ void chunk_scatter_kernel(BwdArgs a) {
   if (g >= a.chunkoff[a.ncol]) return;
   const long long col = chunk_column(a, g);
   const int c = g - a.chunkoff[col];
-  const int first = a.collist[a.coloff[col] + c * kColChunk];
+  const int first = a.collist[a.coloff[col] + c * a.cc];
   const long long key = col - col % a.C + first;
   a.chunk_order[a.chunk_hist[key] + a.chunk_rank[g]] = g;
 }
@@ -754,7 +755,7 @@ __device__ __forceinline__ int xsw(int r, int c) { return r * HD + ((c ^ slot16(
 
 
 // One workgroup = four wavefronts = one column chunk (key block j, up to
-// kColChunk query blocks), streamed in steps of 32 query rows of one head
+// a.cc query blocks), streamed in steps of 32 query rows of one head
 // (n steps: entry e, head h, half x -> step 2 (e G + h) + x).  Pair kh (waves
 // 2 kh, 2 kh + 1) owns keys kh*32 .. kh*32 + 31 of the block and splits the
 // work by tensor:
@@ -783,8 +784,8 @@ __device__ __forceinline__ int xsw(int r, int c) { return r * HD + ((c ^ slot16(
 constexpr int PX4_BYTES = 32 * 32 * 2;                       // P of one step, one key half (fp16)
 constexpr int PBUF4 = ORING + O_SLOTS * SLOT_BYTES;
 constexpr int ITAB4 = PBUF4 + 2 * 2 * PX4_BYTES;             // [key half][step parity]
-constexpr int GTAB4 = ITAB4 + 2 * kColChunk * 4;             // itab + btab
-constexpr int KV4_LDS = GTAB4 + 2 * kColChunk * 4;           // dLogG partials [key half][entry]
+constexpr int GTAB4 = ITAB4 + 2 * kColChunkMax * 4;          // itab + btab
+constexpr int KV4_LDS = GTAB4 + 2 * kColChunkMax * 4;        // dLogG partials [key half][entry]
 static_assert(2 * KV4_LDS <= 160 * 1024, "two workgroups per CU");
 
 // Ring barrier: this wavefront's LDS accesses and all but its newest copies
@@ -819,7 +820,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[KV4_LDS];
   int32_t* itab = (int32_t*)(smem + ITAB4);   // query block of each chunk entry
-  float* btab = (float*)(itab + kColChunk);   // its log gate (log2 units; 0 on the diagonal)
+  float* btab = (float*)(itab + kColChunkMax);   // its log gate (log2 units; 0 on the diagonal)
   float* gtab = (float*)(smem + GTAB4);       // [key half][entry] dS sums
 
   const int tid = threadIdx.x;
@@ -837,8 +838,8 @@ bwd_dkdv_kernel(BwdArgs a) {
   const int c = gch - a.chunkoff[col];
   const int nch = a.chunkoff[col + 1] - a.chunkoff[col];
   const int L = a.collen[col];
-  const int e0 = c * kColChunk;
-  const int ne = min(L, e0 + kColChunk) - e0;
+  const int e0 = c * a.cc;
+  const int ne = min(L, e0 + a.cc) - e0;
   // column col = (batch, score head s, key block j); with per-head gates a
   // kv head's G query heads each have their own columns (G = 1 step per
   // entry and half), which all add into the kv head's dK / dV partials
@@ -1140,7 +1141,7 @@ bwd_dkdv_kernel(BwdArgs a) {
       const float tot = wave_sum(gsum);
       gsum = 0.0f;
       gstep = 0;
-      if (lane == 0) gtab[kh * kColChunk + gent] = tot;
+      if (lane == 0) gtab[kh * kColChunkMax + gent] = tot;
       ++gent;
       if (OUTER) gvb = __builtin_amdgcn_exp2f(btab[gent < ne ? gent : 0]);
     };
@@ -1197,7 +1198,7 @@ bwd_dkdv_kernel(BwdArgs a) {
   // dLogG[i, j] of every entry with i != j (key halves added in order)
   if (wv == 1 && lane < ne) {
     const int ib = itab[lane];
-    if (ib != j) a.dlg[(bs * a.C + ib) * a.C + j] = gtab[lane] + gtab[kColChunk + lane];
+    if (ib != j) a.dlg[(bs * a.C + ib) * a.C + j] = gtab[lane] + gtab[kColChunkMax + lane];
   }
 
   // epilogue: A writes dV, B writes dK (times the softmax scale), keys kh*32 + l32
@@ -1333,6 +1334,7 @@ BwdArgs make_bwd_args(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorks
   a.Gs = s.Hq / s.Hs;
   a.hard = s.hard;
   a.outer = s.outer;
+  a.cc = min(kColChunkMax, kColChunk * (s.G / a.Gs));
   a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.G; a.N = s.N; a.C = s.C; a.cap = s.cap; a.W = wl.words;
   a.o_fp32 = s.o_fp32;
   a.c2 = s.scale * kLog2e;
