@@ -275,18 +275,22 @@ def test_threshold_ties_and_capacity_flag():
     check_selection(gpu, s.numpy(), 2)
 
 
-@pytest.mark.parametrize("C,kind", [(2048, "gumbel"), (2600, "gumbel"), (1000, "ties")],
-                         ids=["c2048", "c2600_one_wave_per_group", "c1000_heavy_ties"])
+@pytest.mark.parametrize("C,kind", [(2048, "gumbel"), (2600, "gumbel"), (1000, "ties"),
+                                    (8192, "gumbel")],
+                         ids=["c2048", "c2600_one_wave_per_group", "c1000_heavy_ties",
+                              "c8192_max_blocks"])
 def test_threshold_matches_oracle_on_long_rows(C, kind):
     """Long rows: 2048 blocks (the 128k-token shape), 2600 blocks (rows
-    longer than 2048 run one wavefront per workgroup), and scores rounded to
+    longer than 2048 run one wavefront per workgroup), scores rounded to
     multiples of 1/2 (most keys tied, so the radix select's bins hold many
-    equal keys and the ">= tau" sets exceed K)."""
-    w = workloads.custom(1, 4, 2, C * 16, 64, 16, 32, dtype="fp32", seed=11,
+    equal keys and the ">= tau" sets exceed K), and the largest supported
+    block count (8192, one kv head)."""
+    hkv = 1 if C > 4096 else 2
+    w = workloads.custom(1, 2 * hkv, hkv, C * 16, 64, 16, 32, dtype="fp32", seed=11,
                          score_kind="gumbel")
     p = problem_of(w, 32)
     g = torch.Generator().manual_seed(5)
-    u = torch.rand(1, 2, C, C, generator=g).clamp_(1e-30, 1 - 2 ** -24)
+    u = torch.rand(1, hkv, C, C, generator=g).clamp_(1e-30, 1 - 2 ** -24)
     s = -torch.log(-torch.log(u))
     if kind == "ties":
         s = torch.floor(s * 2.0) / 2.0
@@ -339,6 +343,14 @@ def test_long_context_sampled():
     w = workloads.WORKLOADS["qwen3_8b_128k"]
     log(f"workload {w.name}")
     sampled_parity(w, w.budgets[0], n_units=6, n_kv_blocks=3)
+
+
+def test_max_blocks_sampled():
+    """The largest supported block count: C = 8192 blocks of 64 tokens (a
+    512k-token sequence), GQA 4, K = 16, on the matrix-core path."""
+    w = workloads.custom(1, 4, 1, 8192 * 64, 128, 64, 16, dtype="bf16", seed=31, score_std=2.0)
+    log("workload C = 8192")
+    sampled_parity(w, 16, n_units=6, n_kv_blocks=3)
 
 
 # --------------------------------------------------------------------------
