@@ -257,7 +257,9 @@ def decode_bench(args):
                    "max_blocks": w.max_blocks},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": None,
-                     "kernel": "decode_attn_kernel + decode_combine_kernel",
+                     "kernel": ("decode_attn_mfma_kernel" if (w.dtype == "bf16" and w.head_dim == 128
+                                                                 and w.block == 64 and w.group <= 32)
+                                else "decode_attn_kernel") + " + decode_combine_kernel",
                      "stage_ms_mean": stage_ms["attn"]["mean"],
                      "algorithmic_bytes_per_launch": int(attn_bytes)},
         "stage_ms": stage_ms,

@@ -27,6 +27,8 @@
 // All three are memory-bound: HBM bytes are the selected K / V blocks.
 #include <math.h>
 
+#include <type_traits>
+
 #include "../../include/sas.h"
 #include "sas_internal.h"
 
@@ -351,6 +353,183 @@ __global__ void __launch_bounds__(kAttnThreads) decode_attn_kernel(DecArgs a) {
   }
 }
 
+// ---- matrix-core tile kernel (bf16, D = 128, b = 64, G <= 32) ----
+// One wavefront per (sequence, kv head, tile), the same partials as
+// decode_attn_kernel.  The G query heads are the columns of two 32x32x16
+// MFMA products: S^T = K Q^T (A: key rows of the block, read straight from
+// the page; B: the heads' queries, columns >= G zero) and O^T = V^T P^T (A:
+// transposed reads of the V block staged in LDS; B: the bf16 probabilities,
+// whose accumulator layout already is the B operand's).  Each head's 64
+// scores sit in one column, i.e. in lanes h and h + 32.
+typedef __bf16 dbf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 dbf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 dbf16x2 __attribute__((ext_vector_type(2)));
+typedef float df32x16 __attribute__((ext_vector_type(16)));
+typedef float df32x4 __attribute__((ext_vector_type(4)));
+typedef float df32x2 __attribute__((ext_vector_type(2)));
+constexpr int kMD = 128, kMB = 64;
+
+// element offset of 16-byte chunk c of row r in the staged V block
+__device__ __forceinline__ int dswz(int r, int c) { return r * kMD + ((c ^ slot16(r)) << 3); }
+// gfx950 transposed LDS read: within each 16-lane group, lane u gets element
+// u % 4 of the 8-byte chunks addressed by lanes u / 4 + 4x (x = 0..3)
+__device__ __forceinline__ dbf16x4 dread_tr(const __bf16* p) {
+  typedef __attribute__((address_space(3))) dbf16x4 lds_bf16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+// v_mfma_f32_32x32x16_bf16: lane l (g = l / 32): A row l % 32, k = 8 g .. +7;
+// B column l % 32, same k; C column l % 32, rows 8 (jj / 4) + 4 g + jj % 4
+__device__ __forceinline__ df32x16 dmfma(dbf16x8 a, dbf16x8 b, df32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// max / sum over the lanes l and l ^ 32 (the two lanes of a C column)
+__device__ __forceinline__ float dmax2(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float dsum2(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__global__ void __launch_bounds__(64) decode_attn_mfma_kernel(DecArgs a) {
+  __shared__ __attribute__((aligned(16))) __bf16 vs[kMB * kMD];
+  const int lane = threadIdx.x;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int bh = blockIdx.x;             // b * Hkv + hk
+  const int t = blockIdx.y;              // 0: current block, t >= 1: selected entry t - 1
+  const int b = bh / a.Hkv, hk = bh % a.Hkv;
+  const int G = a.G;
+  int n;
+  bool bad = false;
+  const int c = current_block(a.seq_lens[b], kMB, a.cmax, &n, &bad);
+  const int cnt = min(max(a.sel_cnt[bh], 0), a.cap);
+  float* part = a.part + ((long long)bh * a.T + t) * G * (kMD + 2);
+
+  int blkid = c, nkeys = n - c * kMB;
+  if (t > 0) {
+    if (t > cnt) {   // no such tile: empty partial
+      if (lane < G) {
+        part[lane * (kMD + 2) + kMD] = -INFINITY;
+        part[lane * (kMD + 2) + kMD + 1] = 0.0f;
+      }
+      return;
+    }
+    blkid = a.sel_idx[(long long)bh * a.cap + t - 1];
+    nkeys = kMB;
+    if (blkid < 0 || blkid >= c) {   // not a historical block: flag, attend nothing
+      bad = true;
+      nkeys = 0;
+      blkid = 0;
+    }
+  }
+  int page = a.bt[(long long)b * a.cmax + blkid];
+  if (page < 0 || page >= a.pool) {
+    bad = true;
+    page = 0;
+    nkeys = 0;
+  }
+  if (bad && lane == 0 && a.d_status != nullptr) *a.d_status = SAS_E_INVALID;
+
+  const __bf16* kg = (const __bf16*)a.kp + (((long long)page * a.Hkv + hk) * kMB) * kMD;
+  const __bf16* vg = (const __bf16*)a.vp + (((long long)page * a.Hkv + hk) * kMB) * kMD;
+  // V block -> LDS: 16 asynchronous copies of 1 KB (rows 4 s .. 4 s + 3), each
+  // lane fetching the chunk that its LDS slot holds under the swizzle
+#pragma unroll
+  for (int sg = 0; sg < 16; ++sg) {
+    const int row = sg * 4 + (lane >> 4);
+    const int ch = (lane & 15) ^ slot16(row);
+    dma16(vg + row * kMD + ch * 8, lds_addr(vs + sg * 512));
+  }
+  // K rows (A operand): key kh * 32 + l32, dims ks * 16 + 8 g .. +7
+  dbf16x8 ka[2][8];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      ka[kh][ks] = *(const dbf16x8*)(kg + (kh * 32 + l32) * kMD + ks * 16 + g * 8);
+  // queries (B operand): head l32 of the group, dims ks * 16 + 8 g .. +7
+  dbf16x8 qf[8];
+  const __bf16* qg = (const __bf16*)a.q + ((long long)b * a.Hq + hk * G + min(l32, G - 1)) * kMD;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    qf[ks] = *(const dbf16x8*)(qg + ks * 16 + g * 8);
+    if (l32 >= G) qf[ks] = dbf16x8{};
+  }
+  // S^T of the two 32-key halves
+  df32x16 sc[2];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    sc[kh] = df32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) sc[kh] = dmfma(ka[kh][ks], qf[ks], sc[kh]);
+  }
+  // the head's softmax statistics over the tile (log2 units; keys past the
+  // query are masked)
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const int key = kh * 32 + 8 * (jj >> 2) + 4 * g + (jj & 3);
+      const float z = key < nkeys ? sc[kh][jj] * a.c2 : -INFINITY;
+      sc[kh][jj] = z;
+      mx = fmaxf(mx, z);
+    }
+  mx = dmax2(mx);
+  float l = 0.0f;
+  dbf16x8 pb[2][2];   // [half][16-key slice]: B operand of O^T
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int jj = 0; jj < 16; jj += 2) {
+      df32x2 pp;
+      pp[0] = mx == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sc[kh][jj] - mx);
+      pp[1] = mx == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sc[kh][jj + 1] - mx);
+      l += pp[0] + pp[1];
+      const dbf16x2 h2 = __builtin_convertvector(pp, dbf16x2);
+      pb[kh][jj >> 3][jj & 7] = h2[0];
+      pb[kh][jj >> 3][(jj & 7) + 1] = h2[1];
+    }
+  l = dsum2(l);
+  // O^T = V^T P^T: head-dim tiles dt, A fragments (dims dt * 32 + l32, keys
+  // 16 sl + {4 g .. 4 g + 3, 8 + 4 g .. 8 + 4 g + 3}) by transposed reads
+  const int u = lane & 15;
+  const int dhalf = (lane >> 4) & 1;
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the V copies (and loads) landed
+  __syncthreads();
+  df32x16 oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    oacc[dt] = df32x16{};
+    const int o0 = dswz(g * 4 + (u >> 2), dt * 4 + dhalf * 2 + ((u >> 1) & 1)) + (u & 1) * 4;
+    const int o1 = dswz(g * 4 + (u >> 2) + 8, dt * 4 + dhalf * 2 + ((u >> 1) & 1)) + (u & 1) * 4;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        const __bf16* vp = vs + (kh * 32 + sl * 16) * kMD;
+        const dbf16x8 va = __builtin_shufflevector(dread_tr(vp + o0), dread_tr(vp + o1),
+                                                   0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[dt] = dmfma(va, pb[kh][sl], oacc[dt]);
+      }
+  }
+  // partial of head l32: unnormalised output (dims dt * 32 + 8 q4 + 4 g .. +3), max, sum
+  if (l32 < G) {
+    float* ph = part + l32 * (kMD + 2);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) ph[dt * 32 + q4 * 8 + g * 4 + y] = oacc[dt][q4 * 4 + y];
+    if (g == 0) {
+      ph[kMD] = mx;
+      ph[kMD + 1] = l;
+    }
+  }
+}
+
 // merge the tile partials of one (sequence, query head): wavefront w takes
 // tiles w, w + 4, ... (lane t of a 64-tile chunk reads a tile's (m, l); the
 // output rows are streamed with independent loads, the tile's scale coming
@@ -427,14 +606,19 @@ __global__ void __launch_bounds__(64 * kCombWaves) decode_combine_kernel(DecArgs
 
 template <typename T, int D, int BLK>
 hipError_t launch_attn(const DecArgs& a, int B, hipStream_t st) {
-  const size_t lds = attn_lds<T, D, BLK>(a.G);
-  if (lds > 64 * 1024) {
-    const hipError_t e = hipFuncSetAttribute((const void*)&decode_attn_kernel<T, D, BLK>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+  if (std::is_same<T, __bf16>::value && D == kMD && BLK == kMB && a.G <= 32) {
+    hipLaunchKernelGGL(decode_attn_mfma_kernel, dim3((unsigned)(B * a.Hkv), (unsigned)a.T), dim3(64),
+                       0, st, a);
+  } else {
+    const size_t lds = attn_lds<T, D, BLK>(a.G);
+    if (lds > 64 * 1024) {
+      const hipError_t e = hipFuncSetAttribute((const void*)&decode_attn_kernel<T, D, BLK>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((decode_attn_kernel<T, D, BLK>), dim3((unsigned)(B * a.Hkv), (unsigned)a.T),
+                       dim3(kAttnThreads), lds, st, a);
   }
-  hipLaunchKernelGGL((decode_attn_kernel<T, D, BLK>), dim3((unsigned)(B * a.Hkv), (unsigned)a.T),
-                     dim3(kAttnThreads), lds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)(B * a.Hq)), dim3(64 * kCombWaves),

@@ -5,7 +5,7 @@ Selected sets, counts and thresholds are compared exactly; o and lse within
 rtol = atol = 2e-2 (bf16) or 1e-5 (fp32), and within that fraction of each
 tensor's largest magnitude.  Cases: ragged batches (a single token, exactly
 one block, one block plus a token, a full cache), K = 0, K >= history, GQA
-1 / 4 / 5, head_dim 64 / 128, blocks of 16 / 32 / 64, fp32 and bf16, paged
+1 / 4 / 5 / 32 / 40, head_dim 64 / 128, blocks of 16 / 32 / 64, fp32 and bf16, paged
 caches with shuffled and with shared pages, exact ties, the capacity flag,
 out-of-range lengths / pages / selections flagged from the host side (every
 access stays in bounds), 8192-block rows (512k tokens), and bitwise
@@ -90,6 +90,10 @@ CASES = [
     ("g2_d128_b16_fp32", 1, 4, 2, 128, 16, (333,), 6, "fp32", 0),
     ("k0", 2, 8, 2, 128, 64, (500, 64), 0, "bf16", 0),
     ("k_all", 2, 8, 2, 128, 64, (500, 64), 50, "bf16", 0),
+    # bf16 / D = 128 / b = 64 runs on the matrix-core tile kernel up to G = 32
+    # heads per group (one MFMA column per head); larger groups on the other
+    ("g32_mfma_columns_full", 2, 32, 1, 128, 64, (700, 63), 4, "bf16", 0),
+    ("g40_beyond_mfma_columns", 1, 40, 1, 128, 64, (700,), 4, "bf16", 0),
 ]
 
 
