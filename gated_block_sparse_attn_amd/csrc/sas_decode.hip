@@ -59,7 +59,7 @@ __device__ __forceinline__ int current_block(int n, int blk, int cmax, int* nn, 
   return (v - 1) / blk;
 }
 
-constexpr int kSelMaxThreads = 1024;   // 256 for short rows, 1024 for long ones
+constexpr int kSelMaxThreads = 1024;   // 256 for rows under 512 blocks, 1024 otherwise
 
 __global__ void __launch_bounds__(kSelMaxThreads) decode_select_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
@@ -649,7 +649,7 @@ hipError_t launch_decode_select(const DecodeShape& s, const float* scores, const
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  const int nthr = s.cmax >= 2048 ? kSelMaxThreads : 256;
+  const int nthr = s.cmax >= 512 ? kSelMaxThreads : 256;   // 1024 threads: 12.6 -> 10.0 us at 1024 blocks
   hipLaunchKernelGGL(decode_select_kernel, dim3((unsigned)(s.B * s.Hkv)), dim3(nthr), lds,
                      st, scores, seq_lens, tau, sel_idx, sel_cnt, d_status, s.Hkv, s.cmax, s.blk,
                      s.K, s.cap);
