@@ -3,12 +3,15 @@ header declares, and rejects malformed or unsupported arguments before any
 launch (these calls never reach the GPU, so they run on a CPU-only host)."""
 
 import ctypes
+import os
 
 import pytest
 import torch
 
 from gated_block_sparse_attn_amd import _native as nat
 from gated_block_sparse_attn_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 FAKE = 0x1000  # never dereferenced: validation fails before any launch
 
@@ -226,3 +229,45 @@ def test_decode_null_pointers_capacity_and_workspace():
     assert dattn(p, ws_bytes=n - 1) == nat.SAS_E_WORKSPACE
     assert dattn(p, ws=None) == nat.SAS_E_WORKSPACE
     assert dattn(p, ws=FAKE * 256 + 4, ws_bytes=n) == nat.SAS_E_WORKSPACE
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "sas.h"
+
+int main(void) {
+  sas_problem p;
+  memset(&p, 0, sizeof p);
+  p.batch = 1; p.n_q_heads = 32; p.n_kv_heads = 8; p.seq_len = 32768; p.head_dim = 128;
+  p.block_size = 64; p.budget_k = 16; p.dtype = SAS_BF16; p.o_dtype = SAS_BF16;
+  p.gate_act = SAS_GATE_SOFTMAX; p.gate_pos = SAS_GATE_INNER; p.gate_rank = SAS_GATE_SOFT;
+  if (sas_abi_version() != SAS_ABI_VERSION) { printf("abi %d\n", sas_abi_version()); return 1; }
+  if (sas_gated_attn_bwd_workspace_size(&p, 16) == 0) { printf("size 0: %s\n", sas_last_error()); return 2; }
+  p.head_dim = 96;   /* unsupported: size 0 and a message */
+  if (sas_gated_attn_bwd_workspace_size(&p, 16) != 0 || strlen(sas_last_error()) == 0) return 3;
+  printf("ok\n");
+  return 0;
+}
+"""
+
+
+def test_header_compiles_as_c_and_links(tmp_path):
+    """include/sas.h is plain C (C99): a C program includes it, links against
+    the library and calls its host-side entry points (no GPU needed)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lib_dir = os.path.join(ROOT, "gated_block_sparse_attn_amd")
+    if not os.path.exists(os.path.join(lib_dir, "libsas.so")):
+        pytest.skip("library not built")
+    src = tmp_path / "abi.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "abi"
+    subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-L", lib_dir, "-lsas", "-Wl,-rpath," + lib_dir, "-o", str(exe)],
+                   check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
