@@ -18,5 +18,4 @@ from .sas_oracle import (  # noqa: F401
     forward,
     gate_threshold,
     kth_largest_threshold,
-    selected_lists,
 )

@@ -164,15 +164,6 @@ def gate_threshold(scores: np.ndarray, budget_k: int, act: str = "softmax", seq_
     return log_gate, tau, sel
 
 
-def selected_lists(sel: np.ndarray):
-    """Ascending selected-block index list and count per row of ``sel``."""
-    bsz, hkv, c, _ = sel.shape
-    cnt = sel.sum(axis=-1).astype(np.int64)
-    lists = [[[np.nonzero(sel[b, h, i])[0] for i in range(c)] for h in range(hkv)]
-             for b in range(bsz)]
-    return lists, cnt
-
-
 # ---------------------------------------------------------------------------
 # Attended set of one query block (Eq. 9 with the App. E current-block rule)
 # ---------------------------------------------------------------------------
@@ -348,11 +339,12 @@ def backward(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = No
 
 
 def backward_kv_block(q, k, v, do, log_gate, sel, block: int, b: int, hk: int, j: int,
-                      sm_scale: float | None = None, gate_pos: str = "inner"):
+                      sm_scale: float | None = None, gate_pos: str = "inner", seq_lens=None):
     """dK and dV of one key block j of one (batch, kv head), exactly.
 
     Sums the contributions of every query block that attends block j: the
     diagonal block i = j and every i > j with j in I_i (Eq. 9 gradient).
+    ``seq_lens`` as in ``backward`` (padding rows contribute nothing).
     Returns (dk_j [block, D], dv_j [block, D]).
     """
     c = q.shape[2] // block
@@ -361,13 +353,13 @@ def backward_kv_block(q, k, v, do, log_gate, sel, block: int, b: int, hk: int, j
     heads = range(hk * g // gs, (hk + 1) * g // gs)   # score heads of kv head hk
     users = [(b, sh, i) for sh in heads for i in range(j, c) if i == j or sel[b, sh, i, j]]
     _, dk, dv, _ = backward(q, k, v, do, log_gate, sel, block, sm_scale, query_blocks=users,
-                            gate_pos=gate_pos)
+                            gate_pos=gate_pos, seq_lens=seq_lens)
     rows = slice(j * block, (j + 1) * block)
     return dk[b, hk, rows], dv[b, hk, rows]
 
 
 def ste_gate_grad(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = None,
-                  seq_lens=None):
+                  seq_lens=None, rows=None):
     """Gate gradients of the hard Top-K gates with the straight-through estimator
     (Sec. 4.1 "Ranking preservation", Eq. 7, Tab. 1 row 8).
 
@@ -379,7 +371,9 @@ def ste_gate_grad(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None
     token would get under it); for a selected block this is the block's dS sum.
     The STE passes dL/dg = dL/dg_hat.
     Returns dg float64 [B, Hs, C, C] (score heads as in ``forward``) for every
-    historical block m < i (0 for m >= i).
+    historical block m < i (0 for m >= i).  ``rows``: optional iterable of
+    gate rows (b, s, i) to evaluate (the others stay 0), so that large shapes
+    can be sampled.
     """
     bsz, hq, n, d = q.shape
     g = hq // k.shape[1]
@@ -388,28 +382,29 @@ def ste_gate_grad(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None
     scale = default_scale(d, sm_scale)
     c = n // block
     zero = np.where(np.isfinite(log_gate), 0.0, log_gate)
-    o, lse = forward(q, k, v, zero, sel, block, sm_scale, seq_lens=seq_lens)
+    if rows is None:
+        rows = [(b, sh, i) for b in range(bsz) for sh in range(hs) for i in range(1, c)]
+    rows = sorted(set((int(b), int(sh), int(i)) for (b, sh, i) in rows))
+    o, lse = forward(q, k, v, zero, sel, block, sm_scale, query_blocks=rows, seq_lens=seq_lens)
     dg = np.zeros((bsz, hs, c, c))
-    for b in range(bsz):
-        for sh in range(hs):
-            hk = (sh * gs) // g
-            for i in range(1, c):
-                nv = _valid_rows(b, i, block, seq_lens)
-                if nv == 0:
-                    continue
-                rows = slice(i * block, i * block + nv)
-                for m in range(i):
-                    cols = slice(m * block, (m + 1) * block)
-                    kk = _f64(k[b, hk, cols])
-                    vv = _f64(v[b, hk, cols])
-                    tot = 0.0
-                    for hh in range(sh * gs, (sh + 1) * gs):
-                        dd = _f64(do[b, hh, rows])
-                        z = scale * (_f64(q[b, hh, rows]) @ kk.T)
-                        pw = np.exp(z - lse[b, hh, rows][:, None])
-                        delta = np.sum(dd * o[b, hh, rows], axis=1, keepdims=True)
-                        tot += float(np.sum(pw * (dd @ vv.T - delta)))
-                    dg[b, sh, i, m] = tot
+    for (b, sh, i) in rows:
+        hk = (sh * gs) // g
+        nv = _valid_rows(b, i, block, seq_lens)
+        if i < 1 or nv == 0:
+            continue
+        qrows = slice(i * block, i * block + nv)
+        for m in range(i):
+            cols = slice(m * block, (m + 1) * block)
+            kk = _f64(k[b, hk, cols])
+            vv = _f64(v[b, hk, cols])
+            tot = 0.0
+            for hh in range(sh * gs, (sh + 1) * gs):
+                dd = _f64(do[b, hh, qrows])
+                z = scale * (_f64(q[b, hh, qrows]) @ kk.T)
+                pw = np.exp(z - lse[b, hh, qrows][:, None])
+                delta = np.sum(dd * o[b, hh, qrows], axis=1, keepdims=True)
+                tot += float(np.sum(pw * (dd @ vv.T - delta)))
+            dg[b, sh, i, m] = tot
     return dg
 
 

@@ -229,3 +229,19 @@ def test_ste_hard_gates_match_torch_autograd():
     np.testing.assert_allclose(dg[p["sel"]], dlg_sel[p["sel"]], rtol=1e-11, atol=1e-12)
     # dropped blocks get a gradient of their own (Eq. 7), unlike the sparse scope
     assert np.count_nonzero(np.abs(dg[tri[None, None] & ~p["sel"]]) > 1e-9) > 10
+
+
+def test_ste_gate_grad_sampled_rows_equal_full():
+    """Sampled gate rows of the straight-through gate gradient equal those
+    rows of the full evaluation, and every other row stays 0."""
+    p = rand_problem(33, B=2, Hq=4, Hkv=2, N=40, D=8, block=4, K=3)
+    full = sas_oracle.ste_gate_grad(p["q"], p["k"], p["v"], p["do"], p["lg"], p["sel"], 4)
+    rows = [(0, 0, 9), (1, 1, 4), (1, 0, 1), (0, 1, 0)]
+    part = sas_oracle.ste_gate_grad(p["q"], p["k"], p["v"], p["do"], p["lg"], p["sel"], 4,
+                                    rows=rows)
+    mask = np.zeros(full.shape[:3], bool)
+    for (b, h, i) in rows:
+        mask[b, h, i] = True
+    np.testing.assert_allclose(part[mask], full[mask], rtol=1e-13, atol=1e-14)
+    assert np.all(part[~mask] == 0.0)
+    assert np.count_nonzero(part[mask]) > 5

@@ -115,3 +115,21 @@ def test_varlen_hard_gates_equal_padded_run():
         cb = -(-n // 4)
         np.testing.assert_allclose(dg[b, :, :cb], dg2[b, :, :cb], rtol=1e-12, atol=1e-12)
         assert np.all(dg[b, :, cb:] == 0.0)
+
+
+def test_backward_kv_block_with_lengths_equals_full_backward():
+    """The one-key-block evaluation used to sample dK / dV at large shapes
+    agrees with the full backward on a ragged batch (padding rows add
+    nothing), at the inner and the outer gate position."""
+    p = problem(19, B=2, Hq=4, Hkv=2, N=32, D=8, block=4, K=2)
+    lens = np.array([32, 13])
+    lg, _, sel = oracle.gate_threshold(p["scores"], 2, seq_lens=lens, block=4)
+    for pos in ("inner", "outer"):
+        _, dk, dv, _ = oracle.backward(p["q"], p["k"], p["v"], p["do"], lg, sel, 4, gate_pos=pos,
+                                       seq_lens=lens)
+        for (b, h, j) in [(0, 0, 0), (1, 1, 3), (1, 0, 2), (0, 1, 7)]:
+            dkj, dvj = oracle.backward_kv_block(p["q"], p["k"], p["v"], p["do"], lg, sel, 4, b, h,
+                                                j, gate_pos=pos, seq_lens=lens)
+            np.testing.assert_allclose(dkj, dk[b, h, 4 * j:4 * j + 4], atol=1e-12)
+            np.testing.assert_allclose(dvj, dv[b, h, 4 * j:4 * j + 4], atol=1e-12)
+    assert np.all(dk[1, :, 13:] == 0.0) and np.all(dv[1, :, 13:] == 0.0)
