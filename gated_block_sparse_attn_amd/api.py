@@ -300,12 +300,23 @@ class SASAttention(torch.autograd.Function):
     forward(q, k, v, scores, block_size, budget_k, sm_scale) -> o
     Gradients flow to q, k, v and to the selector scores (App. D.3); the
     Top-K selection itself is piecewise constant and passes no gradient.
+
+    The selected lists hold min(budget_k, C - 1) entries per row.  Scores tied
+    at a row's threshold can select more blocks than that (every tied block is
+    kept); the library then flags SAS_E_CAPACITY on the device, and this
+    function raises SasError (the check reads the flag back, one host
+    synchronisation per call).
     """
 
     @staticmethod
     def forward(ctx, q, k, v, scores, block_size: int, budget_k: int, sm_scale: float = 0.0):
         p = Problem.from_tensors(q, k, block_size, budget_k, sm_scale)
-        log_gate, _, sel_idx, sel_cnt = gate_threshold(p, scores)
+        status = torch.zeros(1, dtype=torch.int32, device=q.device)
+        log_gate, _, sel_idx, sel_cnt = gate_threshold(p, scores, status=status)
+        code = int(status.item())
+        if code != _native.SAS_OK:
+            raise SasError(code, "sas_gate_threshold: more blocks tied at a row's threshold than "
+                           f"the {sel_idx.shape[-1]} entries of its selected list (SAS_E_CAPACITY)")
         o, lse = gated_attn_fwd(p, q, k, v, log_gate, sel_idx, sel_cnt)
         ctx.save_for_backward(q, k, v, o, lse, log_gate, sel_idx, sel_cnt)
         ctx.problem = p

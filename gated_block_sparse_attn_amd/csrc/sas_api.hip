@@ -143,7 +143,10 @@ BwdWorkspace bwd_workspace_layout(const Shape& s) {
     w.coloff = off;   off = align256(off + sizeof(int32_t) * (size_t)(nrow + 1));
     w.chunkoff = off; off = align256(off + sizeof(int32_t) * (size_t)(nrow + 1));
     w.collist = off;  off = align256(off + sizeof(int32_t) * (size_t)(emax + nrow));
-    w.max_chunks = (emax + nrow + kColChunk - 1) / kColChunk + nrow;
+    // chunks of at most cc entries: sum over columns of ceil(L / cc) with
+    // sum L = emax + nrow (each column also holds its diagonal entry)
+    const int cc = col_chunk(s);
+    w.max_chunks = (emax + nrow + (long long)nrow * (cc - 1)) / cc;
     w.partial = off;  off = align256(off + sizeof(float) * 2 * 64 * 128 * (size_t)w.max_chunks);
     w.chunk_rank = off;  off = align256(off + sizeof(int32_t) * (size_t)w.max_chunks);
     w.chunk_hist = off;  off = align256(off + sizeof(int32_t) * (size_t)(nrow + 1));

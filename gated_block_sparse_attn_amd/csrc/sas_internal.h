@@ -58,6 +58,12 @@ struct BwdWorkspace {
 // covers as many 32-row steps as with one gate row per kv group).
 constexpr int kColChunk = 16;
 constexpr int kColChunkMax = 64;
+// query blocks per key-major chunk of problem s
+inline int col_chunk(const Shape& s) {
+  const int gs = s.Hq / s.Hs;
+  const int cc = kColChunk * (s.G / gs);
+  return cc < kColChunkMax ? cc : kColChunkMax;
+}
 
 bool mfma_path(const Shape& s);
 BwdWorkspace bwd_workspace_layout(const Shape& s);

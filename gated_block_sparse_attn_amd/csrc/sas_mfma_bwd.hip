@@ -457,6 +457,13 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
 // (-inf on padding rows, so they add nothing) and Delta from the same pass.
 // The four partial sums meet in LDS and are added into the row's per-block
 // accumulator in a fixed order (deterministic).
+constexpr size_t kSteStaticLds = 2 * 2 * TILE * sizeof(bf16) + 2 * 4 * sizeof(float);
+__host__ __device__ constexpr size_t ste_dynamic_lds(int C) {
+  return sizeof(uint32_t) * (size_t)((C + 31) / 32) + sizeof(float) * (size_t)C;
+}
+static_assert(kSteStaticLds + ste_dynamic_lds(8192) <= 160 * 1024,
+              "the dropped-block pass fits the largest supported block count");
+
 __global__ void __launch_bounds__(256) ste_mfma_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 s_k[2][TILE];
   __shared__ __attribute__((aligned(16))) bf16 s_v[2][TILE];
@@ -1334,7 +1341,7 @@ BwdArgs make_bwd_args(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorks
   a.Gs = s.Hq / s.Hs;
   a.hard = s.hard;
   a.outer = s.outer;
-  a.cc = min(kColChunkMax, kColChunk * (s.G / a.Gs));
+  a.cc = col_chunk(s);
   a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.G; a.N = s.N; a.C = s.C; a.cap = s.cap; a.W = wl.words;
   a.o_fp32 = s.o_fp32;
   a.c2 = s.scale * kLog2e;
@@ -1415,7 +1422,13 @@ hipError_t launch_bwd_dkdv_mfma(const Shape& s, const BwdPtrs& p, char* ws,
   // hard gates: the gate gradients of the dropped blocks (straight-through
   // estimator); the key-major pass above wrote those of the selected blocks
   if (s.hard) {
-    const size_t lds = sizeof(uint32_t) * ((s.C + 31) / 32) + sizeof(float) * s.C;
+    // dynamic LDS beside the kernel's 64 KB of tiles: the row's selection
+    // bit mask and one accumulator per block (33 KB at the 8192-block limit)
+    const size_t lds = ste_dynamic_lds(s.C);
+    if (kSteStaticLds + lds > 160 * 1024) return hipErrorInvalidValue;   // validated on the host
+    e = hipFuncSetAttribute((const void*)&ste_mfma_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(ste_mfma_kernel, dim3((unsigned)a.ncol), dim3(256), lds, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

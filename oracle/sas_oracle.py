@@ -329,8 +329,10 @@ def backward(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = No
             delta = np.sum(p * dp, axis=1, keepdims=True)
             ds = p * (dp - delta)
             dq[b, hh, rows] = scale * (ds @ kk)
-            np.add.at(dk[b, hk], keys, scale * (ds.T @ qq))
-            np.add.at(dv[b, hk], keys, gkey[:, None] * (p.T @ dd))
+            # the attended keys of a query block are distinct, so the indexed
+            # add accumulates each key row once
+            dk[b, hk, keys] += scale * (ds.T @ qq)
+            dv[b, hk, keys] += gkey[:, None] * (p.T @ dd)
             ds_sum += (p * dp).sum(axis=0) if gate_pos == "outer" else ds.sum(axis=0)
         for m in np.unique(kblk):
             if m != i:
