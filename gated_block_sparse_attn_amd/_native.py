@@ -81,7 +81,10 @@ SIGNATURES = {
     "sas_decode_workspace_size": ([_PD, _i32], ctypes.c_size_t),
     "sas_decode_attn": ([_PD, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
                          ctypes.c_size_t, _vp, _vp], _i32),
+    "sas_decode_attn_noalloc": ([_PD, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
+                                 _vp], _i32),
 }
+DECODE_SCRATCH_BYTES = 32 << 20   # SAS_DECODE_SCRATCH_BYTES
 
 _lib = None
 

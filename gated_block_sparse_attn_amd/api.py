@@ -20,7 +20,7 @@ from ._native import SasError, SasProblem, check, lib
 __all__ = ["Problem", "SasError", "gate_threshold", "gated_attn_fwd", "gated_attn_bwd",
            "gated_attn_bwd_dq", "gated_attn_bwd_dkdv", "bwd_workspace_size", "abi_version",
            "SASAttention", "sas_attention", "DecodeProblem", "decode_select",
-           "decode_workspace_size", "decode_attn"]
+           "decode_workspace_size", "decode_attn", "decode_attn_noalloc"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -437,4 +437,31 @@ def decode_attn(p: DecodeProblem, q, k_pool, v_pool, block_table, seq_lens, sel_
                                 _ptr(block_table), _ptr(seq_lens), _ptr(sel_idx), _ptr(sel_cnt),
                                 cap, _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
                                 _ptr(status), _stream(stream)))
+    return o, lse
+
+
+def decode_attn_noalloc(p: DecodeProblem, q, k_pool, v_pool, block_table, seq_lens, sel_idx,
+                        sel_cnt, o, lse, status: Optional[torch.Tensor] = None, stream=None):
+    """sas_decode_attn_noalloc: sas_decode_attn with the library's fixed
+    per-device scratch instead of a workspace; o and lse are the caller's
+    (nothing is allocated here or in the library)."""
+    cap = sel_idx.shape[-1]
+    dt = p.torch_dtype
+    pool = (p.pool_blocks, p.n_kv_heads, p.block_size, p.head_dim)
+    _expect(q, "q", (p.batch, p.n_q_heads, p.head_dim), dt)
+    _expect(k_pool, "k_pool", pool, dt)
+    _expect(v_pool, "v_pool", pool, dt)
+    _expect(block_table, "block_table", (p.batch, p.max_blocks), torch.int32)
+    _expect(seq_lens, "seq_lens", (p.batch,), torch.int32)
+    _expect(sel_idx, "sel_idx", (p.batch, p.n_kv_heads, cap), torch.int32)
+    _expect(sel_cnt, "sel_cnt", (p.batch, p.n_kv_heads), torch.int32)
+    _expect(o, "o", (p.batch, p.n_q_heads, p.head_dim), dt)
+    _expect(lse, "lse", (p.batch, p.n_q_heads), torch.float32)
+    if status is not None:
+        _expect(status, "status", (1,), torch.int32)
+    pc = p.c()
+    check(lib().sas_decode_attn_noalloc(ctypes_ref(pc), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                        _ptr(block_table), _ptr(seq_lens), _ptr(sel_idx),
+                                        _ptr(sel_cnt), cap, _ptr(o), _ptr(lse), _ptr(status),
+                                        _stream(stream)))
     return o, lse

@@ -382,4 +382,30 @@ int32_t sas_decode_attn(const sas_decode_problem* p, const void* q, const void* 
   return ok();
 }
 
+int32_t sas_decode_attn_noalloc(const sas_decode_problem* p, const void* q, const void* k_pool,
+                                const void* v_pool, const int32_t* block_table,
+                                const int32_t* seq_lens, const int32_t* sel_idx,
+                                const int32_t* sel_cnt, int32_t sel_cap, void* o, float* lse,
+                                int32_t* d_status, void* stream) {
+  sas::DecodeShape s;
+  int32_t rc = validate_decode(p, sel_cap, &s);
+  if (rc != SAS_OK) return rc;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !sel_idx || !sel_cnt || !o || !lse)
+    return fail(SAS_E_INVALID, "sas_decode_attn_noalloc: a required pointer is NULL");
+  const size_t need = decode_ws_bytes(s);
+  if (need > sas::kDecodeScratchBytes)
+    return fail(SAS_E_WORKSPACE, "sas_decode_attn_noalloc: the problem needs %zu bytes of scratch "
+                "(batch * n_kv_heads * (sel_cap + 1) * G * (head_dim + 2) floats); the fixed "
+                "scratch holds %zu", need, sas::kDecodeScratchBytes);
+  if (sas::decode_attn_lds_bytes(s) > 160 * 1024)
+    return fail(SAS_E_UNSUPPORTED, "sas_decode_attn_noalloc: too many query heads per kv head");
+  void* scratch = nullptr;
+  hipError_t e = sas::decode_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "sas_decode_attn_noalloc scratch lookup");
+  e = sas::launch_decode_attn(s, q, k_pool, v_pool, block_table, seq_lens, sel_idx, sel_cnt, o,
+                              lse, (float*)scratch, d_status, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sas_decode_attn_noalloc launch");
+  return ok();
+}
+
 }  // extern "C"

@@ -27,6 +27,7 @@
 // All three are memory-bound: HBM bytes are the selected K / V blocks.
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/sas.h"
@@ -634,6 +635,40 @@ hipError_t launch_attn_d(const DecArgs& a, int B, int blk, hipStream_t st) {
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// fixed scratch of the allocation-free decode entry point
+// ---------------------------------------------------------------------------
+// The tile partials of sas_decode_attn_noalloc live in this array instead of
+// a caller workspace.  Each device holds its own copy (from the library's
+// code-object load until the process ends).  In host code `scratch` names a
+// host-side stand-in, never the device memory: its device address is looked
+// up once per device with hipGetSymbolAddress and only that address is
+// handed to kernels.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {   // first use on this device (it is current)
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 size_t decode_attn_lds_bytes(const DecodeShape& s) {
   const size_t el = s.fp32 ? 4 : 2;

@@ -14,6 +14,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/sas.h"
+
 namespace sas {
 
 // log2(e) and ln(2): the kernels run the softmax in base 2 (v_exp_f32 is exp2)
@@ -104,6 +106,10 @@ struct DecodeShape {
   float scale;
 };
 size_t decode_attn_lds_bytes(const DecodeShape& s);
+// Fixed device scratch of the allocation-free decode entry point: bytes, and
+// its device address on the current device (looked up on first use).
+constexpr size_t kDecodeScratchBytes = SAS_DECODE_SCRATCH_BYTES;
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_decode_select(const DecodeShape& s, const float* scores, const int32_t* seq_lens,
                                 float* tau, int32_t* sel_idx, int32_t* sel_cnt, int32_t* d_status,
                                 hipStream_t st);

@@ -401,6 +401,32 @@ int32_t sas_decode_attn(const sas_decode_problem* p, const void* q, const void* 
                         float* lse, void* workspace, size_t workspace_bytes, int32_t* d_status,
                         void* stream);
 
+/*
+ * sas_decode_attn_noalloc -- sas_decode_attn for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same kernels and results, with the
+ * tile partials in a fixed scratch array that the library holds on each
+ * device (SAS_DECODE_SCRATCH_BYTES = 32 MiB, allocated when the library's
+ * code object is loaded on the device and kept until the process ends)
+ * instead of a workspace argument.  No device memory is allocated or freed.
+ * Arguments, layouts and outputs as for sas_decode_attn; the scratch is the
+ * one of the current device, so `stream` must belong to the current device.
+ * Errors: as sas_decode_attn, and SAS_E_WORKSPACE (before any launch) when
+ * the problem needs more than SAS_DECODE_SCRATCH_BYTES, i.e.
+ * 4 * batch * n_kv_heads * (sel_cap + 1) * (n_q_heads / n_kv_heads) *
+ * (head_dim + 2) bytes rounded up to 256.
+ * Every call on one device shares that device's scratch: calls that overlap
+ * in time on one device (other streams, other host threads) race and must be
+ * serialised by the caller.  The scratch keeps the last call's partials;
+ * nothing in it needs clearing between calls.
+ */
+#define SAS_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+int32_t sas_decode_attn_noalloc(const sas_decode_problem* p, const void* q, const void* k_pool,
+                                const void* v_pool, const int32_t* block_table,
+                                const int32_t* seq_lens, const int32_t* sel_idx,
+                                const int32_t* sel_cnt, int32_t sel_cap, void* o, float* lse,
+                                int32_t* d_status, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -231,6 +231,31 @@ def test_decode_null_pointers_capacity_and_workspace():
     assert dattn(p, ws=FAKE * 256 + 4, ws_bytes=n) == nat.SAS_E_WORKSPACE
 
 
+def dattn_noalloc(p, cap=4, **ptrs):
+    a = {n: FAKE for n in ("q", "kp", "vp", "bt", "n", "si", "sc", "o", "lse")}
+    a.update(ptrs)
+    return lib().sas_decode_attn_noalloc(ctypes.byref(p) if p is not None else None, a["q"],
+                                         a["kp"], a["vp"], a["bt"], a["n"], a["si"], a["sc"], cap,
+                                         a["o"], a["lse"], None, None)
+
+
+def test_decode_noalloc_validates_before_launch():
+    """The allocation-free decode entry point rejects what sas_decode_attn
+    rejects, and a problem whose tile partials exceed its fixed scratch
+    (SAS_E_WORKSPACE, with the size in the message), all on the host."""
+    assert dattn_noalloc(None) == nat.SAS_E_INVALID
+    assert dattn_noalloc(dprob(batch=0)) == nat.SAS_E_INVALID
+    assert dattn_noalloc(dprob(head_dim=80)) == nat.SAS_E_UNSUPPORTED
+    assert dattn_noalloc(dprob(), lse=None) == nat.SAS_E_INVALID
+    assert dattn_noalloc(dprob(), cap=3) == nat.SAS_E_INVALID
+    # 64 sequences x 8 kv heads x 65 tiles x G 8 x 130 floats = 138 MB > 32 MiB
+    big = dprob(batch=64, n_q_heads=64, n_kv_heads=8, max_blocks=8192, pool_blocks=8192,
+                budget_k=64)
+    assert lib().sas_decode_workspace_size(ctypes.byref(big), 64) > nat.DECODE_SCRATCH_BYTES
+    assert dattn_noalloc(big, cap=64) == nat.SAS_E_WORKSPACE
+    assert b"fixed scratch" in lib().sas_last_error()
+
+
 C_PROGRAM = r"""
 #include <stdio.h>
 #include <string.h>
