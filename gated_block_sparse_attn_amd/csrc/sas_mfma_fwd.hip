@@ -152,6 +152,15 @@ __device__ __forceinline__ void wait_vm() { __asm__ volatile("s_waitcnt vmcnt(0)
 template <typename T>
 __device__ __forceinline__ void pin(T& x) { __asm__ volatile("" : "+v"(x)); }
 
+// max(a, b, c) in one v_max3_f32, without the NaN canonicalisation that
+// fmaxf gets in IEEE mode (for values produced by MFMAs and exp2, which are
+// never signalling NaNs)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  __asm__("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Rescale threshold of the lazy online softmax (log2 units): the running max
 // is only moved (and O, l rescaled) when a tile raises some row's max by more
 // than this; otherwise exp2 arguments stay <= kLazy, so P <= 2^kLazy.
@@ -319,10 +328,15 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
   // and l are rescaled only when the row's max grows by more than kLazy)
   auto update_max = [&](auto first_tag, const f32x16& sc, float beta) {
     constexpr bool FIRST = decltype(first_tag)::value;
-    float mx = sc[0];
+    // v_max3 chains; the row's other 16 keys sit in lane l ^ 32
+    float mx = max3f(sc[0], sc[1], sc[2]);
 #pragma unroll
-    for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, sc[jj]);
-    const float tmax = max2(mx) * a.c2 + beta;
+    for (int jj = 3; jj < 15; jj += 2) mx = max3f(mx, sc[jj], sc[jj + 1]);
+    mx = max3f(mx, sc[15], sc[15]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                     false, false);
+    mx = max3f(mx, __uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    const float tmax = mx * a.c2 + beta;
     if (FIRST) {
       mrow = tmax;
     } else if (__builtin_amdgcn_ballot_w64(tmax > mrow + kLazy) != 0) {   // wave-uniform, rare
@@ -342,12 +356,17 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
     const int jj = 2 * n;
     const f32x2 p0 = {__builtin_amdgcn_exp2f(fmaf(sc[jj], a.c2, off)),
                       __builtin_amdgcn_exp2f(fmaf(sc[jj + 1], a.c2, off))};
-    lrow += p0[0] + p0[1];
     const f32x2 pp = OUTER ? f32x2{p0[0] * gv, p0[1] * gv} : p0;   // outer: g P enters O
     const bf16x2 hi = __builtin_convertvector(pp, bf16x2);
     uint32_t wh = __builtin_bit_cast(uint32_t, hi);
     pin(wh);
     pb[jj >> 3][(jj & 7) >> 1] = wh;
+    if (OUTER || SPLIT) {
+      lrow += p0[0] + p0[1];   // the unscaled (outer) or unrounded (split) weights
+    } else {
+      // the bf16 weights that enter O, one dot product per pair
+      lrow = __builtin_amdgcn_fdot2_f32_bf16(hi, bf16x2{(bf16)1.0f, (bf16)1.0f}, lrow, false);
+    }
     if (SPLIT) {
       const bf16x2 lo = __builtin_convertvector(pp - __builtin_convertvector(hi, f32x2), bf16x2);
       uint32_t wl = __builtin_bit_cast(uint32_t, lo);
@@ -391,12 +410,26 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
       }
   };
 
-  auto copy_k = [&](int kb, int slot) {
-    tile_to_lds<NW>(s_k[slot], a.k + kv_tile(kb), kv_stride, kv_rmax(kb), w, lane);
+  // this lane's byte offsets in a tile for the wave's 1 KB segments (rows
+  // 4 seg .. 4 seg + 3, seg = w + NW r), swizzled as tile_to_lds does; the
+  // padded layout copies with one scalar base per tile
+  unsigned voff[16 / NW];
+#pragma unroll
+  for (int r = 0; r < 16 / NW; ++r) {
+    const int rr = (w + NW * r) * 4 + (lane >> 4);
+    voff[r] = (unsigned)(rr * HD + (((lane & 15) ^ slot16(rr)) << 3)) * 2;
+  }
+  auto copy_tile = [&](const bf16* src, bf16* lds, int kb) {
+    if (packed) {   // rows clamped per lane to the sequence's last row
+      tile_to_lds<NW>(lds, src + kv_tile(kb), kv_stride, kv_rmax(kb), w, lane);
+    } else {
+      const bf16* base = src + kv_tile(kb);
+#pragma unroll
+      for (int r = 0; r < 16 / NW; ++r) dma16s(base, voff[r], lds_addr(lds + (w + NW * r) * 512));
+    }
   };
-  auto copy_v = [&](int kb, int slot) {
-    tile_to_lds<NW>(s_v[slot], a.v + kv_tile(kb), kv_stride, kv_rmax(kb), w, lane);
-  };
+  auto copy_k = [&](int kb, int slot) { copy_tile(a.k, s_k[slot], kb); };
+  auto copy_v = [&](int kb, int slot) { copy_tile(a.v, s_v[slot], kb); };
 
   // prologue: K_0, V_0, K_1 in; S of unit 0 (masked) starts the running max
   float beta1 = 0.0f;
