@@ -385,14 +385,9 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
       tro[dt][hh] = swz(g * 4 + (u >> 2) + 8 * hh, dt * 4 + dhalf * 2 + ((u >> 1) & 1)) + (u & 1) * 4;
-  auto pv = [&](const bf16* Vs, int kh, const uint32_t (&pbw)[2][4], const uint32_t (&plw)[2][4]) {
-    bf16x8 pb[2], pl[2];
-#pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
-      pb[sl] = __builtin_bit_cast(bf16x8, u32x4{pbw[sl][0], pbw[sl][1], pbw[sl][2], pbw[sl][3]});
-      pl[sl] = __builtin_bit_cast(bf16x8, u32x4{plw[sl][0], plw[sl][1], plw[sl][2], plw[sl][3]});
-    }
-    bf16x8 va[4][2];
+  // the V^T fragments of a unit are read at the start of its window, so their
+  // LDS latency hides behind the S products and the softmax of the window
+  auto read_va = [&](const bf16* Vs, int kh, bf16x8 (&va)[4][2]) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -401,6 +396,14 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
         va[dt][sl] = __builtin_shufflevector(ds_read_tr(vp + tro[dt][0]), ds_read_tr(vp + tro[dt][1]),
                                              0, 1, 2, 3, 4, 5, 6, 7);
       }
+  };
+  auto pv = [&](const bf16x8 (&va)[4][2], const uint32_t (&pbw)[2][4], const uint32_t (&plw)[2][4]) {
+    bf16x8 pb[2], pl[2];
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      pb[sl] = __builtin_bit_cast(bf16x8, u32x4{pbw[sl][0], pbw[sl][1], pbw[sl][2], pbw[sl][3]});
+      pl[sl] = __builtin_bit_cast(bf16x8, u32x4{plw[sl][0], plw[sl][1], plw[sl][2], plw[sl][3]});
+    }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -464,6 +467,10 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
     const float off = (OUTER ? 0.0f : beta_cur) - mrow;
     const float gvw = OUTER ? __builtin_amdgcn_exp2f(beta_cur) : 1.0f;   // outer: the tile's gate
     uint32_t pb[2][4], pl[2][4];
+    bf16x8 va[4][2];
+    // (a packed batch's per-lane clamped copies leave no registers for the
+    // early read: there the fragments are read just before the product)
+    if (!PACKED) read_va(s_v[PAR], KH, va);
     // next unit: (t, 1) reads K_t, (t + 1, 0) reads K_{t+1}
     const bf16* kn = KH == 0 ? s_k[PAR] : s_k[PAR ^ 1];
     if (more) {
@@ -472,7 +479,8 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
       for (int n = 0; n < 8; ++n) p_pair(n, scur, off, gvw, pb, pl);
     }
-    pv(s_v[PAR], KH, pb, pl);
+    if (PACKED) read_va(s_v[PAR], KH, va);
+    pv(va, pb, pl);
     wait_vm_prev<NW>();
     __syncthreads();
     if (more) {
