@@ -245,10 +245,49 @@ def decode_bench(args):
     attn_bytes = (2 * rows * w.head_dim * el + 2 * w.batch * w.n_q_heads * w.head_dim * el
                   + 4 * w.batch * w.n_q_heads)
     achieved = attn_bytes / (stage_ms["attn"]["mean"] * 1e-3) / 1e9
+    o_eager, lse_eager = o.clone(), lse.clone()
+
+    # The same step captured once in a HIP graph and replayed (how a serving
+    # loop runs decode): the attention goes through the allocation-free entry
+    # point, so nothing is allocated under capture.  Every replay's o / lse
+    # is checked bit-equal to the eager step.
+    def step_noalloc():
+        api.decode_select(p, t["scores"], t["seq_lens"], sel_cap=cap, outputs=(tau, si, sc))
+        api.decode_attn_noalloc(p, t["q"], t["k_pool"], t["v_pool"], t["block_table"],
+                                t["seq_lens"], si, sc, o, lse)
+
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        step_noalloc()   # first use of the per-device scratch outside the capture
+        cs.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cs):
+            step_noalloc()
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    ms_graph = g0.elapsed_time(g1) / args.steps
+    assert torch.equal(o.view(torch.int16 if o.dtype == torch.bfloat16 else torch.int32),
+                       o_eager.view(torch.int16 if o.dtype == torch.bfloat16 else torch.int32)), \
+        "graph replay differs from the eager step"
+    assert torch.equal(lse, lse_eager), "graph replay differs from the eager step"
+
     result = {
         "metric": "sparse decode tokens/s (select + attention, one new token per sequence)",
-        "value": w.batch / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "value": w.batch / (ms_graph * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_graph,
+        "timing": "HIP graph replay of the whole step (eager launches: ms_per_step_eager)",
+        "ms_per_step_eager": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded torch generator; Qwen3-shaped paged cache, random values)",
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,

@@ -10,12 +10,14 @@
 // context, so the selection gets a workgroup per row).
 //
 // Kernels:
-//   decode_select_kernel   one workgroup per (sequence, kv head): stages the
+//   decode_select_kernel   one workgroup per (sequence, kv head): holds the
 //                          row's historical scores as order-preserving
-//                          integer keys in LDS, finds the K-th largest key by
-//                          four 8-bit MSB-first radix passes (LDS histogram +
-//                          one wavefront's suffix scan), then compacts
-//                          {m : key >= tau} in ascending order.
+//                          integer keys in registers, bounds the K-th
+//                          largest from below by the group maxima (a value
+//                          histogram when that bound does not narrow it
+//                          enough), finds it exactly among the few keys
+//                          above the bound, then compacts {m : key >= tau}
+//                          in ascending order.
 //   decode_attn_kernel     one workgroup per (sequence, kv head, tile): tile
 //                          0 is the current block (tokens up to the query),
 //                          tile t >= 1 the (t-1)-th selected block.  The K / V
@@ -60,18 +62,111 @@ __device__ __forceinline__ int current_block(int n, int blk, int cmax, int* nn, 
   return (v - 1) / blk;
 }
 
-constexpr int kSelMaxThreads = 1024;   // 256 for rows under 512 blocks, 1024 otherwise
+// Per (sequence, kv head) row: the threshold T is the K-th largest of the c_s
+// historical scores, over order-preserving integer keys held in registers
+// (thread t holds blocks t KPT .. t KPT + KPT - 1).  The row is cut into 128
+// groups of consecutive threads.  When K <= 128, T is at least the K-th
+// largest group maximum (K groups each hold a key at or above it), so every
+// key >= T lies in that maximum's bin of a 256-bin histogram of the group
+// maxima (bins linear in the score between the row's minimum and maximum) or
+// above it -- usually a few keys beyond K.  Those keys go to an LDS list and
+// each finds its rank among the others; the one with fewer than K above it
+// and at least K at or above it is T.  Without such a bound, or when the
+// list overflows (dense ties), 256-bin histograms of the remaining keys
+// (linear in the score, then in the integer key) narrow the range level by
+// level until it fits the list.  Then the ascending compaction
+// {m < c_s : key_m >= T} from a scan of per-thread counts.
+constexpr int kSelMaxThreads = 1024;   // 256 for rows of up to 1024 blocks, 1024 otherwise
+constexpr int kSelGroups = 128;
+constexpr int kSelBins = 256;
+constexpr int kSelCand = 256;          // keys the exact search takes
 
+// DPP lane exchanges (rows of 16 lanes): quad_perm [1,0,3,2], quad_perm
+// [2,3,0,1], row_half_mirror, row_mirror, row_shr:n, row_bcast:15 / :31
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWS, 0xF, false);
+}
+// max over aligned groups of S lanes (S = 2, 8 or 16), in every lane
+template <int S>
+__device__ __forceinline__ uint32_t group_max(uint32_t v) {
+  v = max(v, dpp<0xB1>(v, v));
+  if (S >= 4) v = max(v, dpp<0x4E>(v, v));
+  if (S >= 8) v = max(v, dpp<0x141>(v, v));
+  if (S >= 16) v = max(v, dpp<0x140>(v, v));
+  return v;
+}
+__device__ __forceinline__ uint32_t row_min(uint32_t v) {
+  v = min(v, dpp<0xB1>(v, v));
+  v = min(v, dpp<0x4E>(v, v));
+  v = min(v, dpp<0x141>(v, v));
+  return min(v, dpp<0x140>(v, v));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = row_min(v);
+  const uint32_t a = min((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                         (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t b = min((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                         (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return min(a, b);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = group_max<16>(v);
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                         (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                         (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return max(a, b);
+}
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  uint32_t u = (uint32_t)v;
+  u += dpp<0x111>(0u, u);
+  u += dpp<0x112>(0u, u);
+  u += dpp<0x114>(0u, u);
+  u += dpp<0x118>(0u, u);
+  u += dpp<0x142, 0xA>(0u, u);
+  u += dpp<0x143, 0xC>(0u, u);
+  return (int)u;
+}
+
+// 256 bins over the keys in [lo, hi], non-decreasing in the key: linear in
+// the score when allowed and the range is finite and resolvable in fp32,
+// else 2^sh-wide key bins
+struct KeyBins {
+  uint32_t lo;
+  float flo, scale;
+  int sh;
+  bool byval;
+  __device__ KeyBins(uint32_t lo_, uint32_t hi, bool by_value) : lo(lo_) {
+    flo = key2f(lo);
+    const float span = key2f(hi) - flo;
+    scale = kSelBins / span;
+    byval = by_value && isfinite(flo) && isfinite(span) && isfinite(scale) && scale > 0.0f;
+    sh = hi == lo ? 0 : max(0, 24 - __builtin_clz(hi - lo));   // (hi - lo) >> sh < 256
+  }
+  __device__ int operator()(uint32_t k) const {
+    if (byval) return min((int)((key2f(k) - flo) * scale), kSelBins - 1);
+    return (int)((k - lo) >> sh);
+  }
+};
+
+template <int KPT>
 __global__ void __launch_bounds__(kSelMaxThreads) decode_select_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
     float* __restrict__ tau, int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt,
     int32_t* __restrict__ d_status, int Hkv, int cmax, int blk, int K, int cap) {
-  extern __shared__ uint32_t s_key[];          // cmax keys
-  __shared__ int s_hist[256];
-  __shared__ int s_wave[kSelMaxThreads / 64];
-  __shared__ uint32_t s_pick[2];               // digit, count above it
+  __shared__ int s_hist[kSelBins];
+  __shared__ __align__(16) uint32_t s_cand[kSelCand];
+  __shared__ uint32_t s_gmax[kSelGroups];
+  __shared__ int s_wsum[kSelMaxThreads / 64];
+  __shared__ int s_pick[3];                    // boundary bin, keys above it, keys in it
+  __shared__ uint32_t s_ext[2];                // boundary-bin key range (row maximum first)
+  __shared__ int s_ncand;
+  __shared__ uint32_t s_t;
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
+  const int nw = nthr >> 6;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const long long row = blockIdx.x;            // b * Hkv + h
@@ -80,8 +175,24 @@ __global__ void __launch_bounds__(kSelMaxThreads) decode_select_kernel(
   bool bad = false;
   const int c = current_block(seq_lens[b], blk, cmax, &n, &bad);
   const float* srow = scores + row * (long long)cmax;
-  for (int m = tid; m < c; m += nthr) s_key[m] = f2key(srow[m] + 0.0f);   // -0 -> +0
-  __syncthreads();
+  const int m0 = tid * KPT;
+  // the loads do not wait for the length: every m < cmax is in the row
+  float raw[KPT];
+  if (KPT % 4 == 0 && (cmax & 3) == 0 && ((uintptr_t)srow & 15) == 0) {
+#pragma unroll
+    for (int j = 0; j < KPT / 4; ++j) {
+      const float4 v = m0 + 4 * j < cmax ? *(const float4*)(srow + m0 + 4 * j)
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+      raw[4 * j] = v.x; raw[4 * j + 1] = v.y; raw[4 * j + 2] = v.z; raw[4 * j + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int x = 0; x < KPT; ++x) raw[x] = m0 + x < cmax ? srow[m0 + x] : 0.f;
+  }
+  const int nv = min(max(c - m0, 0), KPT);     // historical blocks this thread holds
+  uint32_t key[KPT];
+#pragma unroll
+  for (int x = 0; x < KPT; ++x) key[x] = x < nv ? f2key(raw[x] + 0.0f) : 0u;   // -0 -> +0
 
   uint32_t tkey;   // select m iff key >= tkey; none when K == 0
   bool none = false;
@@ -91,92 +202,198 @@ __global__ void __launch_bounds__(kSelMaxThreads) decode_select_kernel(
     tkey = 0xFFFFFFFFu;
     none = true;
   } else {
-    uint32_t prefix = 0u, mask = 0u;
-    int kk = K;   // rank of the wanted key among the keys matching prefix
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int x = tid; x < 256; x += nthr) s_hist[x] = 0;
-      __syncthreads();
-      // histogram of the next digit over the keys matching the prefix; the
-      // wave's most common case -- every candidate with the first
-      // candidate's digit -- is one atomic (scores of one row share their
-      // leading bits, which would otherwise serialise on one bin)
-      for (int m0 = 0; m0 < c; m0 += nthr) {
-        const int m = m0 + tid;
-        const uint32_t k = m < c ? s_key[m] : 0u;
-        const bool cand = m < c && (k & mask) == prefix;
-        const uint32_t dg = (k >> shift) & 255u;
-        const unsigned long long cb = __ballot(cand);
-        if (cb != 0ull) {
-          const int first = __builtin_ctzll(cb);
-          const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)dg, first);
-          const bool same = cand && dg == d0;
-          const unsigned long long sb = __ballot(same);
-          if (lane == first) atomicAdd(&s_hist[d0], __popcll(sb));
-          if (cand && !same) atomicAdd(&s_hist[dg], 1);
-        }
-      }
-      __syncthreads();
-      if (w == 0) {
-        // lane l holds digits 255 - 4l .. 252 - 4l (descending); inclusive
-        // prefix over lanes = keys with a digit >= 252 - 4l
+    // group maxima: groups of nthr / 128 threads (2 or 8)
+    uint32_t hi = 0u;
+#pragma unroll
+    for (int x = 0; x < KPT; ++x)
+      if (x < nv) hi = max(hi, key[x]);
+    const int gs = nthr / kSelGroups;
+    const uint32_t gm = gs == 8 ? group_max<8>(hi) : group_max<2>(hi);
+    if ((lane & (gs - 1)) == 0) s_gmax[tid / gs] = gm;
+    for (int i = tid; i < kSelBins; i += nthr) s_hist[i] = 0;
+    if (tid == 0) s_ncand = 0;
+    __syncthreads();
+    if (w == 0) {
+      // groups holding at least one historical block; their maxima span the row's keys' top
+      const int ng = min(kSelGroups, (c + gs * KPT - 1) / (gs * KPT));
+      const bool v0 = lane < ng, v1 = lane + 64 < ng;
+      const uint32_t g0 = s_gmax[lane], g1 = s_gmax[lane + 64];
+      const uint32_t ghi = wave_max_u32(max(v0 ? g0 : 0u, v1 ? g1 : 0u));
+      uint32_t l0 = 0u;
+      if (K <= ng) {
+        // T is at least the K-th largest group maximum, so at least the
+        // smallest group maximum in that maximum's bin or above
+        const uint32_t glo = wave_min_u32(min(v0 ? g0 : 0xFFFFFFFFu, v1 ? g1 : 0xFFFFFFFFu));
+        const KeyBins bins(glo, ghi, true);
+        const int b0 = v0 ? bins(g0) : -1, b1 = v1 ? bins(g1) : -1;
+        if (v0) atomicAdd(&s_hist[b0], 1);
+        if (v1) atomicAdd(&s_hist[b1], 1);
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+        // lane l holds bins 255 - 4l .. 252 - 4l (descending); the inclusive
+        // scan over lanes counts the maxima in bins >= 252 - 4l
         int v4[4], v = 0;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) { v4[x] = s_hist[255 - 4 * lane - x]; v += v4[x]; }
-        int incl = v;
+        for (int x = 0; x < 4; ++x) { v4[x] = s_hist[kSelBins - 1 - 4 * lane - x]; v += v4[x]; }
+        const int incl = wave_incl_scan(v);
+        const int L = __builtin_ctzll(__ballot(incl >= K));   // K <= ng: some lane hits
+        int cum = incl - v, x = 0;
+        while (x < 3 && cum + v4[x] < K) cum += v4[x++];
+        const int blo = __builtin_amdgcn_readlane(kSelBins - 1 - 4 * lane - x, L);
+        l0 = wave_min_u32(min(v0 && b0 >= blo ? g0 : 0xFFFFFFFFu, v1 && b1 >= blo ? g1 : 0xFFFFFFFFu));
+      }
+      if (lane == 0) { s_t = l0; s_ext[1] = ghi; }
+    }
+    __syncthreads();
+    const uint32_t l0 = s_t;       // every key >= T is >= l0
+    uint32_t rhi = s_ext[1];       // the row's largest key
+    // keys >= l0 into the list (when they fit)
+    unsigned long long bits[KPT];
+    int tot = 0;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_up(incl, o, 64);
-          if (lane >= o) incl += y;
-        }
-        const unsigned long long hit = __ballot(incl >= kk);
-        const int L = __builtin_ctzll(hit);   // kk <= #candidates, so some lane hits
-        if (lane == L) {
-          int cum = incl - v;
+    for (int x = 0; x < KPT; ++x) {
+      bits[x] = __ballot(x < nv && key[x] >= l0);
+      tot += __popcll(bits[x]);
+    }
+    int base = 0;
+    if (lane == 0 && tot > 0) base = atomicAdd(&s_ncand, tot);
+    base = __builtin_amdgcn_readfirstlane(base);
 #pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            if (cum + v4[x] >= kk) {
-              s_pick[0] = (uint32_t)(255 - 4 * lane - x);
-              s_pick[1] = (uint32_t)cum;
-              break;
+    for (int x = 0; x < KPT; ++x) {
+      if ((bits[x] >> lane) & 1ull) {
+        const int pos = base + rank_below(bits[x]);
+        if (pos < kSelCand) s_cand[pos] = key[x];
+      }
+      base += __popcll(bits[x]);
+    }
+    for (int i = tid; i < kSelBins; i += nthr) s_hist[i] = 0;
+    __syncthreads();
+    {
+      int nb = s_ncand;
+      int kk = K;
+      uint32_t rlo = l0;
+      bool fits = nb <= kSelCand;
+      for (int level = 0; !fits && rlo != rhi; ++level) {
+        // keys in [rlo, rhi] (more than the list holds) rank kk-th among
+        // themselves; bins linear in the score at the first level only
+        const KeyBins bin_of(rlo, rhi, level == 0);
+#pragma unroll
+        for (int x = 0; x < KPT; ++x)
+          if (x < nv && key[x] >= rlo && key[x] <= rhi) atomicAdd(&s_hist[bin_of(key[x])], 1);
+        __syncthreads();
+        if (w == 0) {
+          // lane l holds bins 255 - 4l .. 252 - 4l (descending); the
+          // inclusive scan over lanes counts the keys in bins >= 252 - 4l
+          int v4[4], v = 0;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) { v4[x] = s_hist[kSelBins - 1 - 4 * lane - x]; v += v4[x]; }
+          const int incl = wave_incl_scan(v);
+          const unsigned long long hit = __ballot(incl >= kk);
+          const int L = __builtin_ctzll(hit);  // kk <= keys in range, so some lane hits
+          if (lane == L) {
+            int cum = incl - v;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              if (cum + v4[x] >= kk) {
+                s_pick[0] = kSelBins - 1 - 4 * lane - x;
+                s_pick[1] = cum;
+                s_pick[2] = v4[x];
+                break;
+              }
+              cum += v4[x];
             }
-            cum += v4[x];
+          }
+          if (lane == 0) { s_ext[0] = 0xFFFFFFFFu; s_ext[1] = 0u; s_ncand = 0; }
+        }
+        __syncthreads();
+        const int bsel = s_pick[0];
+        kk -= s_pick[1];
+        nb = s_pick[2];
+        fits = nb <= kSelCand;
+        // the boundary bin's keys: their range, and the keys themselves when
+        // the list holds them all
+        uint32_t cl = 0xFFFFFFFFu, ch = 0u;
+#pragma unroll
+        for (int x = 0; x < KPT; ++x) {
+          const uint32_t k = key[x];
+          const bool in = x < nv && k >= rlo && k <= rhi && bin_of(k) == bsel;
+          if (in) { cl = min(cl, k); ch = max(ch, k); }
+          if (fits) {
+            const unsigned long long bb = __ballot(in);
+            if (bb != 0ull) {
+              const int first = __builtin_ctzll(bb);
+              int bs = 0;
+              if (lane == first) bs = atomicAdd(&s_ncand, __popcll(bb));
+              bs = __builtin_amdgcn_readlane(bs, first);
+              if (in) s_cand[bs + rank_below(bb)] = k;
+            }
           }
         }
+        cl = wave_min_u32(cl);
+        ch = wave_max_u32(ch);
+        if (lane == 0 && ch >= cl) { atomicMin(&s_ext[0], cl); atomicMax(&s_ext[1], ch); }
+        for (int i = tid; i < kSelBins; i += nthr) s_hist[i] = 0;
+        __syncthreads();
+        rlo = s_ext[0];
+        rhi = s_ext[1];
       }
-      __syncthreads();
-      prefix |= s_pick[0] << shift;
-      mask |= 255u << shift;
-      kk -= (int)s_pick[1];
-      __syncthreads();
+      if (rlo == rhi) {
+        tkey = rlo;
+      } else {
+        // the list holds every key in [rlo, rhi] (nb of them); the kk-th
+        // largest is the entry with fewer than kk entries above it and at
+        // least kk at or above it
+        if (tid < nb) {
+          const uint32_t ci = s_cand[tid];
+          int gt = 0, ge = 0;
+          const uint4* c4 = (const uint4*)s_cand;
+          int j = 0;
+          for (; j + 4 <= nb; j += 4) {
+            const uint4 q = c4[j >> 2];
+            gt += (q.x > ci) + (q.y > ci) + (q.z > ci) + (q.w > ci);
+            ge += (q.x >= ci) + (q.y >= ci) + (q.z >= ci) + (q.w >= ci);
+          }
+          for (; j < nb; ++j) {
+            const uint32_t q = s_cand[j];
+            gt += q > ci;
+            ge += q >= ci;
+          }
+          if (gt < kk && kk <= ge) s_t = ci;   // every such entry holds the same key
+        }
+        __syncthreads();
+        tkey = s_t;
+      }
     }
-    tkey = prefix;
   }
 
-  // ascending compaction of {m < c : key_m >= tkey}
-  int32_t* out = sel_idx + row * (long long)cap;
-  int base = 0;
-  for (int m0 = 0; m0 < c; m0 += nthr) {
-    const int m = m0 + tid;
-    const bool p = !none && m < c && s_key[m] >= tkey;
-    const unsigned long long bits = __ballot(p);
-    if (lane == 0) s_wave[w] = __popcll(bits);
-    __syncthreads();
-    int off = base;
-    for (int x = 0; x < w; ++x) off += s_wave[x];
-    if (p) {
-      const int pos = off + rank_below(bits);
-      if (pos < cap) out[pos] = m;
-    }
-    for (int x = 0; x < nthr / 64; ++x) base += s_wave[x];
-    __syncthreads();
+  // ascending compaction: the output position of thread tid's selected
+  // blocks is the number selected by lower threads plus its own earlier ones
+  int mine = 0;
+#pragma unroll
+  for (int x = 0; x < KPT; ++x) mine += (!none && x < nv && key[x] >= tkey) ? 1 : 0;
+  const int incl = wave_incl_scan(mine);
+  if (lane == 63) s_wsum[w] = incl;
+  __syncthreads();
+  int pos = incl - mine, total = 0;
+  for (int y = 0; y < nw; ++y) {
+    const int v = s_wsum[y];
+    total += v;
+    pos += y < w ? v : 0;
   }
-  for (int pos = base + tid; pos < cap; pos += nthr) out[pos] = -1;
+  int32_t* out = sel_idx + row * (long long)cap;
+#pragma unroll
+  for (int x = 0; x < KPT; ++x) {
+    if (!none && x < nv && key[x] >= tkey) {
+      if (pos < cap) out[pos] = m0 + x;
+      ++pos;
+    }
+  }
+  for (int p = total + tid; p < cap; p += nthr) out[p] = -1;
   if (tid == 0) {
-    sel_cnt[row] = base;
+    sel_cnt[row] = total;
     if (tau != nullptr) tau[row] = (K >= c) ? -INFINITY : (none ? INFINITY : key2f(tkey));
     if (d_status != nullptr) {
       if (bad) *d_status = SAS_E_INVALID;
-      else if (base > cap) *d_status = SAS_E_CAPACITY;
+      else if (total > cap) *d_status = SAS_E_CAPACITY;
     }
   }
 }
@@ -532,13 +749,16 @@ __global__ void __launch_bounds__(64) decode_attn_mfma_kernel(DecArgs a) {
 }
 
 // merge the tile partials of one (sequence, query head): wavefront w takes
-// tiles w, w + 4, ... (lane t of a 64-tile chunk reads a tile's (m, l); the
-// output rows are streamed with independent loads, the tile's scale coming
-// by readlane); the four wavefronts are then added in a fixed order.
+// tiles w, w + 4, ..., loads up to kCombBatch of them at once (one memory
+// round trip) and folds them in tile order into a running (max, sum,
+// output) with the online-softmax rescale; the four wavefronts' results are
+// then rescaled to the common max and added in wave order (deterministic).
 constexpr int kCombWaves = 4;
+constexpr int kCombBatch = 16;
 
 template <typename T, int D>
 __global__ void __launch_bounds__(64 * kCombWaves) decode_combine_kernel(DecArgs a) {
+  constexpr int PER = D / 64;   // output values per lane
   __shared__ float s_red[kCombWaves][D + 2];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -549,57 +769,63 @@ __global__ void __launch_bounds__(64 * kCombWaves) decode_combine_kernel(DecArgs
   const int nt = min(max(a.sel_cnt[bh], 0), a.cap) + 1;
   const float* p0 = a.part + (long long)bh * a.T * a.G * (D + 2) + hh * (D + 2);
   const long long stride = (long long)a.G * (D + 2);
-  float M = -INFINITY;
-  for (int t = threadIdx.x; t < nt; t += 64 * kCombWaves) M = fmaxf(M, p0[t * stride + D]);
+  float mw = -INFINITY, lw = 0.0f;
+  float acc[PER];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  if (lane == 0) s_red[w][0] = M;
-  __syncthreads();
-  M = s_red[0][0];
-#pragma unroll
-  for (int x = 1; x < kCombWaves; ++x) M = fmaxf(M, s_red[x][0]);
-  __syncthreads();
-  float L = 0.0f;
-  float acc[D / 64];
-#pragma unroll
-  for (int x = 0; x < D / 64; ++x) acc[x] = 0.0f;
-  // this wavefront's tiles: w + kCombWaves * j
+  for (int x = 0; x < PER; ++x) acc[x] = 0.0f;
+  // this wavefront's tiles: w + kCombWaves * j, j < nw
   const int nw = nt > w ? (nt - w + kCombWaves - 1) / kCombWaves : 0;
-  for (int j0 = 0; j0 < nw; j0 += 64) {
-    const int t = w + kCombWaves * (j0 + lane);
-    float sc = 0.0f;
-    if (j0 + lane < nw) {
-      const float m = p0[t * stride + D];
-      sc = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-      L = fmaf(p0[t * stride + D + 1], sc, L);
-    }
-    const int n = min(64, nw - j0);
-    const float* pc = p0 + (w + (long long)kCombWaves * j0) * stride;
-#pragma unroll 8
-    for (int j = 0; j < n; ++j) {
-      const float s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), j));
+  for (int j0 = 0; j0 < nw; j0 += kCombBatch) {
+    const int n = min(kCombBatch, nw - j0);
+    float mt[kCombBatch], lt[kCombBatch], ot[kCombBatch][PER];
 #pragma unroll
-      for (int x = 0; x < D / 64; ++x)
-        acc[x] = fmaf(pc[(long long)j * kCombWaves * stride + x * 64 + lane], s, acc[x]);
+    for (int j = 0; j < kCombBatch; ++j) {
+      if (j < n) {
+        const float* pt = p0 + (long long)(w + kCombWaves * (j0 + j)) * stride;
+        mt[j] = pt[D];
+        lt[j] = pt[D + 1];
+#pragma unroll
+        for (int x = 0; x < PER; ++x) ot[j][x] = pt[x * 64 + lane];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kCombBatch; ++j) {
+      if (j < n) {
+        const float mn = fmaxf(mw, mt[j]);
+        const float so = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - mn);
+        const float sn = mt[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mt[j] - mn);
+        lw = lw * so + lt[j] * sn;
+#pragma unroll
+        for (int x = 0; x < PER; ++x) acc[x] = acc[x] * so + ot[j][x] * sn;
+        mw = mn;
+      }
     }
   }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
-#pragma unroll
-  for (int x = 0; x < D / 64; ++x) s_red[w][x * 64 + lane] = acc[x];
-  if (lane == 0) s_red[w][D] = L;
+  for (int x = 0; x < PER; ++x) s_red[w][x * 64 + lane] = acc[x];
+  if (lane == 0) {
+    s_red[w][D] = mw;
+    s_red[w][D + 1] = lw;
+  }
   __syncthreads();
   if (w != 0) return;
-  float Lt = 0.0f;
+  float M = -INFINITY;
 #pragma unroll
-  for (int y = 0; y < kCombWaves; ++y) Lt += s_red[y][D];
+  for (int y = 0; y < kCombWaves; ++y) M = fmaxf(M, s_red[y][D]);
+  float sy[kCombWaves], Lt = 0.0f;
+#pragma unroll
+  for (int y = 0; y < kCombWaves; ++y) {
+    const float m = s_red[y][D];
+    sy[y] = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+    Lt += s_red[y][D + 1] * sy[y];
+  }
   const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
   T* op = (T*)a.o + (long long)bq * D;
 #pragma unroll
-  for (int x = 0; x < D / 64; ++x) {
+  for (int x = 0; x < PER; ++x) {
     float v = 0.0f;
 #pragma unroll
-    for (int y = 0; y < kCombWaves; ++y) v += s_red[y][x * 64 + lane];
+    for (int y = 0; y < kCombWaves; ++y) v += s_red[y][x * 64 + lane] * sy[y];
     op[x * 64 + lane] = (T)(v * inv);
   }
   if (lane == 0) a.lse[bq] = (M + log2f(Lt)) * kLn2;
@@ -678,16 +904,19 @@ size_t decode_attn_lds_bytes(const DecodeShape& s) {
 hipError_t launch_decode_select(const DecodeShape& s, const float* scores, const int32_t* seq_lens,
                                 float* tau, int32_t* sel_idx, int32_t* sel_cnt, int32_t* d_status,
                                 hipStream_t st) {
-  const size_t lds = sizeof(uint32_t) * (size_t)s.cmax;
-  if (lds > 60 * 1024) {   // with the kernel's static LDS this passes 64 KB
-    const hipError_t e = hipFuncSetAttribute((const void*)&decode_select_kernel,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  const int nthr = s.cmax >= 512 ? kSelMaxThreads : 256;   // 1024 threads: 12.6 -> 10.0 us at 1024 blocks
-  hipLaunchKernelGGL(decode_select_kernel, dim3((unsigned)(s.B * s.Hkv)), dim3(nthr), lds,
-                     st, scores, seq_lens, tau, sel_idx, sel_cnt, d_status, s.Hkv, s.cmax, s.blk,
-                     s.K, s.cap);
+  // 256 threads up to 1024 blocks, else 1024; KPT = keys per thread, a power of two
+  const int nthr = s.cmax > 1024 ? kSelMaxThreads : 256;
+  int kpt = 1;
+  while (kpt * nthr < s.cmax) kpt *= 2;
+  if (kpt > 16) return hipErrorInvalidValue;   // rows of at most 16384 blocks
+  void (*kern)(const float*, const int32_t*, float*, int32_t*, int32_t*, int32_t*, int, int, int,
+               int, int) = kpt == 1   ? decode_select_kernel<1>
+                           : kpt == 2 ? decode_select_kernel<2>
+                           : kpt == 4 ? decode_select_kernel<4>
+                           : kpt == 8 ? decode_select_kernel<8>
+                                      : decode_select_kernel<16>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(s.B * s.Hkv)), dim3(nthr), 0, st, scores, seq_lens,
+                     tau, sel_idx, sel_cnt, d_status, s.Hkv, s.cmax, s.blk, s.K, s.cap);
   return hipGetLastError();
 }
 

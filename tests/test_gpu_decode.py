@@ -126,6 +126,40 @@ def test_decode_ties_and_capacity_flag():
     check_select(gpu, inp, w.block, 2)
 
 
+@pytest.mark.parametrize("blocks,K,kind", [(8192, 32, "gumbel"), (16384, 32, "gumbel"),
+                                            (8192, 100, "gumbel"), (8192, 32, "halves"),
+                                            (16384, 64, "few_ties"), (600, 32, "halves")],
+                         ids=["c8192_k32", "c16384_k32", "c8192_k100", "c8192_heavy_ties",
+                              "c16384_tied_top", "c600_heavy_ties"])
+def test_decode_select_long_rows(blocks, K, kind):
+    """The selection alone on long rows (up to the 16384-block limit): Gumbel
+    scores; scores rounded to multiples of 1/2, so most keys tie and the
+    tied candidates exceed what the exact search gathers; and rows whose top
+    scores tie at the threshold.  Sets, counts and thresholds exact."""
+    B, Hkv = 2, 2
+    lens = (blocks * 64, blocks * 64 - 5000)
+    g = torch.Generator().manual_seed(blocks + K)
+    u = torch.rand(B, Hkv, blocks, generator=g).clamp_(1e-30, 1 - 2 ** -24)
+    s = -torch.log(-torch.log(u))
+    if kind == "halves":
+        s = torch.floor(s * 2.0) / 2.0
+    elif kind == "few_ties":
+        s[:, :, 100:100 + 3 * K:3] = 30.0    # K tied maxima, then the Gumbel rest
+        s[:, :, 7] = 30.0                    # one more tie at the top
+    p = api.DecodeProblem(B, 8, Hkv, 128, 64, blocks, 1, K, "bf16")
+    cap = K + 8
+    dev = torch.device("cuda:0")
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    tau, si, sc = api.decode_select(p, s.to(dev), torch.tensor(lens, dtype=torch.int32, device=dev),
+                                    sel_cap=cap, status=status)
+    torch.cuda.synchronize()
+    inp = {"scores": s, "seq_lens": torch.tensor(lens, dtype=torch.int32)}
+    gpu = {"tau": tau.cpu(), "sel_idx": si.cpu(), "sel_cnt": sc.cpu()}
+    sel = check_select(gpu, inp, 64, K)
+    over = sel.sum(-1) > cap
+    assert int(status.item()) == (-4 if over.any() else 0)
+
+
 def test_decode_out_of_range_inputs_are_flagged():
     """Lengths, pages and selected indices outside their ranges are clamped or
     skipped by the kernels (every access stays in bounds) and flagged."""
