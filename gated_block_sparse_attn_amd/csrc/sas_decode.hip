@@ -347,6 +347,16 @@ __global__ void __launch_bounds__(kSelMaxThreads) decode_select_kernel(
           int gt = 0, ge = 0;
           const uint4* c4 = (const uint4*)s_cand;
           int j = 0;
+          for (; j + 16 <= nb; j += 16) {   // four 16-byte reads in flight
+            uint4 q[4];
+#pragma unroll
+            for (int y = 0; y < 4; ++y) q[y] = c4[(j >> 2) + y];
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+              gt += (q[y].x > ci) + (q[y].y > ci) + (q[y].z > ci) + (q[y].w > ci);
+              ge += (q[y].x >= ci) + (q[y].y >= ci) + (q[y].z >= ci) + (q[y].w >= ci);
+            }
+          }
           for (; j + 4 <= nb; j += 4) {
             const uint4 q = c4[j >> 2];
             gt += (q.x > ci) + (q.y > ci) + (q.z > ci) + (q.w > ci);
@@ -373,12 +383,12 @@ __global__ void __launch_bounds__(kSelMaxThreads) decode_select_kernel(
   const int incl = wave_incl_scan(mine);
   if (lane == 63) s_wsum[w] = incl;
   __syncthreads();
-  int pos = incl - mine, total = 0;
-  for (int y = 0; y < nw; ++y) {
-    const int v = s_wsum[y];
-    total += v;
-    pos += y < w ? v : 0;
-  }
+  // lane y < nw holds wave y's count; their scan gives this wave's offset
+  // and the total
+  const int wc = lane < nw ? s_wsum[lane] : 0;
+  const int wincl = wave_incl_scan(wc);
+  const int total = __builtin_amdgcn_readlane(wincl, 63);
+  int pos = incl - mine + (w > 0 ? __builtin_amdgcn_readlane(wincl, w - 1) : 0);
   int32_t* out = sel_idx + row * (long long)cap;
 #pragma unroll
   for (int x = 0; x < KPT; ++x) {
