@@ -241,6 +241,15 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
   };
   const int ntiles = cnt + 1;
   load_tile(i, 0);
+  // the row's selection (lane e: block of entry e), read up to the capacity
+  // so that it goes out with the loads of Q, dO and O below instead of
+  // waiting for the count (its gate gather follows the Delta computation)
+  int selv = 0;
+  float betav = 0.0f;
+  {
+    const int raw = lane < a.cap ? sel[lane] : 0;
+    selv = lane < cnt ? raw : 0;
+  }
 
   // Q^T and dO^T as B operands (lane: query row l32, dims ks*16 + g*8 .. +7);
   // dlt = rowsum(O * dO) over the row's two lanes (the Delta of dS in this
@@ -387,16 +396,19 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
   };
 
   // the row's selection, 64 entries at a time, in registers (lane e: block
-  // sel[e0 + e] and its log gate in log2 units), read with readlane
-  int selv = 0;
-  float betav = 0.0f;
+  // sel[e0 + e] and its log gate in log2 units), read with readlane; both
+  // loads complete inside the (rarely taken) reload branch, so that no load
+  // is in flight where the branch joins the tile loop
   auto load_sel = [&](int e0) {
     const int e = e0 + lane;
     selv = e < cnt ? sel[e] : 0;
     betav = (e < cnt && !a.hard) ? lgrow[selv] * kLog2e : 0.0f;   // hard gates: unit
+    settle(selv);
     settle(betav);
   };
-  load_sel(0);
+  betav = (lane < cnt && !a.hard) ? lgrow[selv] * kLog2e : 0.0f;   // hard gates: unit
+  settle(selv);
+  settle(betav);
 
   wait_vm();
   __syncthreads();

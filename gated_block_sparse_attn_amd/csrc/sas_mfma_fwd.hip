@@ -266,10 +266,8 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
   const long long lse_i = packed ? (long long)h * a.T + start + tok : q0 + l32;
 
   // Q^T as the B operand of S^T = K Q^T (32x32x16): lane holds query row
-  // l32 and head dims ks*16 + g*8 .. +7.
+  // l32 and head dims ks*16 + g*8 .. +7 (loaded in the prologue below)
   bf16x8 qf[8];
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)(a.q + qrow_i * HD + ks * 16 + g * 8);
 
   // The row's selection, 64 entries at a time, in registers: lane e holds
   // block sel[e0 + e] and its log gate (log2 units); read with readlane.
@@ -280,6 +278,11 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
     const int e = e0 + lane;
     selv = e < cnt ? sel[e] : 0;
     betav = (e < cnt && !a.hard) ? lgrow[selv] * kLog2e : 0.0f;   // hard gates: unit
+    // both loads complete inside this (rarely taken) branch: a load still in
+    // flight at the join would make the compiler wait for every outstanding
+    // memory operation there, i.e. for the tile copies of the previous window
+    // at the start of every window
+    settle(selv);
     settle(betav);
   };
   // block and log gate of tile t (t = 0: the diagonal block, gate 0; tiles
@@ -292,7 +295,6 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
     beta = lane_value(betav, e & 63);
     return lane_value(selv, e & 63);
   };
-  load_sel(0);
 
   // O^T (lane: head dims dt*32 + 8 (jj/4) + 4 g + jj%4, query l32)
   f32x16 oacc[4];
@@ -434,11 +436,24 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
   auto copy_k = [&](int kb, int slot) { copy_tile(a.k, s_k[slot], kb); };
   auto copy_v = [&](int kb, int slot) { copy_tile(a.v, s_v[slot], kb); };
 
-  // prologue: K_0, V_0, K_1 in; S of unit 0 (masked) starts the running max
+  // prologue: K_0, V_0, K_1 in; S of unit 0 (masked) starts the running max.
+  // The diagonal tiles' copies, the Q rows and the selection (read up to the
+  // capacity, so without waiting for the count) go out together; then K of
+  // tile 1 and the gate gather, which need the selection: two memory
+  // latencies instead of the four of count, selection, gates, copies.
   float beta1 = 0.0f;
   copy_k(i, 0);
   copy_v(i, 0);
-  copy_k(tile_block(1, beta1), 1);
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)(a.q + qrow_i * HD + ks * 16 + g * 8);
+  {
+    const int raw = lane < a.cap ? sel[lane] : 0;
+    selv = lane < cnt ? raw : 0;
+  }
+  copy_k(nt > 1 ? lane_value(selv, 0) : i, 1);
+  betav = (lane < cnt && !a.hard) ? lgrow[selv] * kLog2e : 0.0f;
+  settle(betav);
+  if (nt > 1) beta1 = lane_value(betav, 0);
   wait_vm();
   __syncthreads();
   f32x16 s0, s1;   // S of the unit being finished / the next unit
