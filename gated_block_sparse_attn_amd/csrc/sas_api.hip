@@ -150,7 +150,7 @@ BwdWorkspace bwd_workspace_layout(const Shape& s) {
     w.partial = off;  off = align256(off + sizeof(float) * 2 * 64 * 128 * (size_t)w.max_chunks);
     w.chunk_rank = off;  off = align256(off + sizeof(int32_t) * (size_t)w.max_chunks);
     w.chunk_hist = off;  off = align256(off + sizeof(int32_t) * (size_t)(nrow + 1));
-    w.chunk_order = off; off = align256(off + sizeof(int32_t) * (size_t)w.max_chunks);
+    w.chunk_desc = off; off = align256(off + 4 * sizeof(int32_t) * (size_t)w.max_chunks);
   }
   w.total = off;
   return w;

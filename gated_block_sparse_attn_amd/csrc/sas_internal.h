@@ -49,7 +49,8 @@ struct BwdWorkspace {
   size_t partial;    // float  [max_chunks * 2 * 64 * 128]  split dK/dV partial sums
   size_t chunk_rank; // int32  [max_chunks]           rank of a chunk inside its order bucket
   size_t chunk_hist; // int32  [B*Hkv*C + 1]         chunks per (batch, kv head, first row)
-  size_t chunk_order;// int32  [max_chunks]           chunk ids sorted by that key
+  size_t chunk_desc; // int32x4 [max_chunks]          per key-major workgroup: chunk id, column,
+                     //                               list offset, entries (bit 30: only chunk)
   size_t total;
   long long max_chunks;
   int words;         // W = ceil(C / 32)
@@ -132,6 +133,14 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
   const int q = nwg >> 3, r = nwg & 7;
   const int x = bid & 7, idx = bid >> 3;
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + idx;
+}
+
+// The hardware workgroup id that xcd_remap maps to logical id u (its inverse).
+__device__ __forceinline__ int xcd_unmap(int u, int nwg) {
+  const int q = nwg >> 3, r = nwg & 7;
+  const int x = u < r * (q + 1) ? u / (q + 1) : r + (u - r * (q + 1)) / q;
+  const int start = x * q + min(x, r);
+  return (u - start) * 8 + x;
 }
 
 // Swizzle of the 16-byte chunks of a row-major LDS tile with 256-byte rows:

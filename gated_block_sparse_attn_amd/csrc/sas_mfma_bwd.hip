@@ -61,7 +61,7 @@ struct BwdArgs {
   float* lsen;     // -LSE log2(e) per query row (-inf on padding rows), from the dq pass
   uint32_t* colmask; int32_t* collen; int32_t* coloff; int32_t* chunkoff; int32_t* collist;
   float* partial;
-  int32_t* chunk_rank; int32_t* chunk_hist; int32_t* chunk_order;
+  int32_t* chunk_rank; int32_t* chunk_hist; int32_t* chunk_desc;
   long long ncol;  // B * Hkv * C (rows of the score table == columns)
   int Hq, Hkv, G, N, C, cap, W, o_fp32;
   int Hs, Gs;       // score heads (gate-table rows per batch) and query heads per score head
@@ -734,14 +734,27 @@ __global__ void __launch_bounds__(1024) scan_ints_kernel(int32_t* x, long long n
   if (t == 1023) x[n] = s[1023];
 }
 
+// Writes the descriptor of chunk g at its place in the order, indexed by the
+// hardware workgroup id that runs it (the inverse of the key-major kernel's
+// XCD remap): the key-major workgroup then finds its work with one load
+// instead of a binary search over the chunk offsets.
 __global__ void chunk_scatter_kernel(BwdArgs a) {
   const int g = blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= a.chunkoff[a.ncol]) return;
+  const int total = a.chunkoff[a.ncol];
+  if (g >= total) return;
   const long long col = chunk_column(a, g);
   const int c = g - a.chunkoff[col];
-  const int first = a.collist[a.coloff[col] + c * a.cc];
+  const int nch = a.chunkoff[col + 1] - a.chunkoff[col];
+  const int e0 = c * a.cc;
+  const int first = a.collist[a.coloff[col] + e0];
   const long long key = col - col % a.C + first;
-  a.chunk_order[a.chunk_hist[key] + a.chunk_rank[g]] = g;
+  const int ne = min(a.collen[col], e0 + a.cc) - e0;
+  const int pos = a.chunk_hist[key] + a.chunk_rank[g];
+  int32_t* d = a.chunk_desc + 4 * (long long)xcd_unmap(pos, total);
+  d[0] = g;
+  d[1] = (int)col;
+  d[2] = a.coloff[col] + e0;
+  d[3] = ne | (nch == 1 ? (1 << 30) : 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -850,15 +863,16 @@ bwd_dkdv_kernel(BwdArgs a) {
   const int g = lane >> 5;
   const int l32 = lane & 31;
 
-  const int total = a.chunkoff[a.ncol];
+  // this workgroup's chunk (descriptor written by chunk_scatter_kernel at
+  // this hardware id; scalar loads, both in flight together)
+  typedef __attribute__((address_space(4))) const int32_t cint;
+  const int total = *(cint*)(a.chunkoff + a.ncol);
+  const cint* dsc = (cint*)(a.chunk_desc + 4 * (long long)blockIdx.x);
+  const int gch = dsc[0], dcol = dsc[1], loff = dsc[2], dne = dsc[3];
   if ((int)blockIdx.x >= total) return;
-  const int gch = a.chunk_order[xcd_remap(blockIdx.x, total)];
-  const long long col = chunk_column(a, gch);
-  const int c = gch - a.chunkoff[col];
-  const int nch = a.chunkoff[col + 1] - a.chunkoff[col];
-  const int L = a.collen[col];
-  const int e0 = c * a.cc;
-  const int ne = min(L, e0 + a.cc) - e0;
+  const long long col = dcol;
+  const int ne = dne & ((1 << 30) - 1);
+  const bool only_chunk = (dne >> 30) & 1;
   // column col = (batch, score head s, key block j); with per-head gates a
   // kv head's G query heads each have their own columns (G = 1 step per
   // entry and half), which all add into the kv head's dK / dV partials
@@ -876,11 +890,28 @@ bwd_dkdv_kernel(BwdArgs a) {
   // do.  Uniform over the workgroup, before any copy or barrier.
   if (packed && j * BLK >= sp.n) return;
 
+  // resident B operand of S (A: K_j) or dP (B: V_j): key kh*32 + l32,
+  // dims ds*16 + g*8 .. +7 (in flight with the column list below; the first
+  // products wait for them)
+  bf16x8 kf[8];
+  {
+    const int key = j * BLK + kh * 32 + l32;
+    const long long kr = packed ? (sp.start + min(key, sp.n - 1)) * a.Hkv + hk
+                                : bhk * a.N + key;
+    const bf16* t = (role == 0 ? a.k : a.v) + kr * HD;
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) kf[ds] = *(const bf16x8*)(t + ds * 16 + g * 8);
+  }
+
+  // The entry table (itab, btab) written here by wavefront 0 is read by the
+  // other wavefronts only after their first ring barrier (an s_barrier after
+  // lgkmcnt(0)), so the first row copies go out without a barrier of their
+  // own, as soon as the column list has arrived.
   long long rowbase = 0;   // per entry: workspace row of (query block, head 0) (padded order)
   long long prow = 0;      // packed batch: tensor row of (query block, head 0)
   int vrem = 0;            // packed batch: valid rows of the entry's query block
   if (lane < ne) {
-    const int i = a.collist[a.coloff[col] + e0 + lane];
+    const int i = a.collist[loff + lane];
     if (wv == 0) {
       itab[lane] = i;
       btab[lane] = (i == j || a.hard) ? 0.0f : a.lg[(bs * a.C + i) * a.C + j] * kLog2e;
@@ -890,20 +921,6 @@ bwd_dkdv_kernel(BwdArgs a) {
     vrem = sp.n - i * BLK;
   }
 
-  // resident B operand of S (A: K_j) or dP (B: V_j): key kh*32 + l32,
-  // dims ds*16 + g*8 .. +7
-  bf16x8 kf[8];
-  {
-    const int key = j * BLK + kh * 32 + l32;
-    const long long kr = packed ? (sp.start + min(key, sp.n - 1)) * a.Hkv + hk
-                                : bhk * a.N + key;
-    const bf16* t = (role == 0 ? a.k : a.v) + kr * HD;
-#pragma unroll
-    for (int ds = 0; ds < 8; ++ds) kf[ds] = *(const bf16x8*)(t + ds * 16 + g * 8);
-#pragma unroll
-    for (int ds = 0; ds < 8; ++ds) settle(kf[ds]);
-  }
-  __syncthreads();   // item table
 
   const int n = 2 * ne * G;   // steps: entry e, head h, half x -> step 2 (e G + h) + x
   const int nslots = role == 0 ? Q_SLOTS : O_SLOTS;
@@ -1154,7 +1171,7 @@ bwd_dkdv_kernel(BwdArgs a) {
   } else {
     float gsum = 0.0f;
     int gstep = 0, gent = 0;
-    float gvb = OUTER ? __builtin_amdgcn_exp2f(btab[0]) : 1.0f;   // gate of the dS entry (outer)
+    float gvb = 1.0f;   // gate of the dS entry (outer; read after the first ring barrier)
     auto step_done = [&]() {
       if (++gstep < 2 * G) return;
       const float tot = wave_sum(gsum);
@@ -1166,7 +1183,8 @@ bwd_dkdv_kernel(BwdArgs a) {
     };
     copy_next();
     copy_next();
-    ring_barrier(kh);   // dO of step 0 landed
+    ring_barrier(kh);   // dO of step 0 landed (and the entry table written)
+    if (OUTER) gvb = __builtin_amdgcn_exp2f(btab[0]);
     {
       const char* o0 = oring(0);
       copy_next();
@@ -1223,7 +1241,7 @@ bwd_dkdv_kernel(BwdArgs a) {
   // epilogue: A writes dV, B writes dK (times the softmax scale), keys kh*32 + l32
   const long long orow = bhk * a.N + (long long)j * BLK + kh * 32;
   const float mul = role == 0 ? 1.0f : a.scale;
-  if (nch == 1 && a.Gs == a.G) {   // the only contributor to these rows
+  if (only_chunk && a.Gs == a.G) {   // the only contributor to these rows
     bf16* dst = role == 0 ? a.dv : a.dk;
     const int key = j * BLK + kh * 32 + l32;
     if (packed && key >= sp.n) return;   // the row belongs to no sequence of this batch
@@ -1347,7 +1365,7 @@ BwdArgs make_bwd_args(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorks
   a.partial = (float*)(ws + wl.partial);
   a.chunk_rank = (int32_t*)(ws + wl.chunk_rank);
   a.chunk_hist = (int32_t*)(ws + wl.chunk_hist);
-  a.chunk_order = (int32_t*)(ws + wl.chunk_order);
+  a.chunk_desc = (int32_t*)(ws + wl.chunk_desc);
   a.ncol = (long long)s.B * s.Hs * s.C;   // gate-table rows == columns
   a.Hs = s.Hs;
   a.Gs = s.Hq / s.Hs;
