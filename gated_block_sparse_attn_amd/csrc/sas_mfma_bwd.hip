@@ -175,9 +175,16 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // is processed, one barrier per tile.
 // OUTER: the outer gate position (Sec. 4.1, Tab. 1 row 3): P carries no gate
 // bias and the tile's gate g scales dP (dP = g dO V^T).
-template <int NH, bool PACKED, bool OUTER>
-__global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
-  constexpr int NW = 2 * NH;
+//
+// KS (one head, four wavefronts): wavefront (kq, half) takes keys kq*32 ..
+// +31 of every tile for its 32 query rows; the two key halves' dQ and
+// P * dP sums are added in LDS at the end.  A one-head workgroup (per-head
+// gates) then has four wavefronts on its 64 KB of K / V stages, so two such
+// workgroups fill a CU's SIMDs twice.
+template <int NH, bool PACKED, bool OUTER, bool KS = false>
+__global__ void __launch_bounds__(NH * 128 * (KS ? 2 : 1), 2) bwd_dq_kernel(BwdArgs a) {
+  static_assert(!KS || NH == 1, "the key split is for one-head workgroups");
+  constexpr int NW = 2 * NH * (KS ? 2 : 1);
   __shared__ __attribute__((aligned(16))) bf16 s_k[2][TILE];
   __shared__ __attribute__((aligned(16))) bf16 s_v[2][TILE];
 
@@ -187,6 +194,7 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
   const int g = lane >> 5;
   const int l32 = lane & 31;
   const int half = w & 1;
+  const int kq = KS ? (w >> 1) : 0;   // KS: this wave's key half of every tile
 
   const int unit = xcd_remap(blockIdx.x, gridDim.x);
   const int chunk = unit % a.nchunk;
@@ -195,7 +203,7 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
   const int bhk = rest / a.C;
   const int hk = bhk % a.Hkv;
   const int bb = bhk / a.Hkv;
-  const int h = hk * a.G + a.head_base + chunk * NH + (w >> 1);
+  const int h = hk * a.G + a.head_base + chunk * NH + (KS ? 0 : (w >> 1));
   const long long row = ((long long)bb * a.Hs + h / a.Gs) * a.C + i;   // the head's gate row
   const int cnt = min(a.sel_cnt[row], a.cap);
   const int32_t* sel = a.sel_idx + row * a.cap;
@@ -211,6 +219,7 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
   const Span sp = seq_span(a, bb);
   const int nb = sp.n;
   if (i * BLK >= nb) {
+    if (kq != 0) return;   // KS: the kq = 0 waves write the block
     if (g == 0) {
       a.delta[qr] = 0.0f;
       a.lsen[qr] = -INFINITY;
@@ -324,7 +333,8 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
     const float off = (OUTER ? 0.0f : beta) - lse2;
     const float gv = OUTER ? __builtin_amdgcn_exp2f(beta) : 1.0f;   // outer: the tile's gate
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
+    for (int kk = 0; kk < (KS ? 1 : 2); ++kk) {
+      const int kh = KS ? kq : kk;
       const int rr = kh * 32 + l32;
       f32x16 sc, dp;
 #pragma unroll
@@ -431,6 +441,33 @@ __global__ void __launch_bounds__(NH * 128, 2) bwd_dq_kernel(BwdArgs a) {
     tile(std::false_type{}, stg, beta);
     wait_vm();
     __syncthreads();
+  }
+  if (KS) {
+    // add the kq = 1 waves' dQ^T and P * dP sums into the kq = 0 waves'
+    // (K stages: dQ^T, lane-major 16-byte vectors; V stage 0: the sums); the
+    // loop's last barrier has retired every read of the stages
+    f32x4* xo = (f32x4*)&s_k[0][0] + half * 16 * 64 + lane;
+    float* xd = (float*)&s_v[0][0] + half * 64 + lane;
+    if (kq == 1) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          xo[(dt * 4 + q4) * 64] = f32x4{dqacc[dt][q4 * 4], dqacc[dt][q4 * 4 + 1], dqacc[dt][q4 * 4 + 2],
+                                         dqacc[dt][q4 * 4 + 3]};
+      *xd = dx;
+    }
+    __syncthreads();
+    if (kq == 1) return;
+    dx += *xd;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 ob = xo[(dt * 4 + q4) * 64];
+#pragma unroll
+        for (int y = 0; y < 4; ++y) dqacc[dt][q4 * 4 + y] += ob[y];
+      }
   }
   const float dsum = sum2(dx);
   if (g == 0) {
@@ -1331,17 +1368,17 @@ __global__ void __launch_bounds__(256) reduce_kernel(BwdArgs a) {
   *(bf16x8*)(a.dv + off) = ov;
 }
 
-template <int NH>
+template <int NH, bool KS = false>
 hipError_t launch_dq(BwdArgs a, int head_base, int nchunk, long long units, hipStream_t st) {
   a.head_base = head_base;
   a.nchunk = nchunk;
-  const dim3 grid((unsigned)(units * nchunk)), block(NH * 128);
+  const dim3 grid((unsigned)(units * nchunk)), block(NH * 128 * (KS ? 2 : 1));
   const int v = (a.cu != nullptr ? 2 : 0) | (a.outer ? 1 : 0);
   switch (v) {
-    case 0: hipLaunchKernelGGL((bwd_dq_kernel<NH, false, false>), grid, block, 0, st, a); break;
-    case 1: hipLaunchKernelGGL((bwd_dq_kernel<NH, false, true>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((bwd_dq_kernel<NH, true, false>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((bwd_dq_kernel<NH, true, true>), grid, block, 0, st, a); break;
+    case 0: hipLaunchKernelGGL((bwd_dq_kernel<NH, false, false, KS>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((bwd_dq_kernel<NH, false, true, KS>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((bwd_dq_kernel<NH, true, false, KS>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((bwd_dq_kernel<NH, true, true, KS>), grid, block, 0, st, a); break;
   }
   return hipGetLastError();
 }
@@ -1392,7 +1429,7 @@ hipError_t launch_bwd_dq_mfma(const Shape& s, const BwdPtrs& p, char* ws, const 
   // every head has its own gates and selection)
   int h = 0;
   if (a.Gs < 2 && s.G > 1) {
-    e = launch_dq<1>(a, 0, s.G, units, st);
+    e = launch_dq<1, true>(a, 0, s.G, units, st);   // one head per workgroup, keys split
     if (e != hipSuccess) return e;
     h = s.G;
   }

@@ -165,6 +165,9 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 // is only moved (and O, l rescaled) when a tile raises some row's max by more
 // than this; otherwise exp2 arguments stay <= kLazy, so P <= 2^kLazy.
 constexpr float kLazy = 8.0f;
+// Floor of the running max of a key-split wavefront (log2 units): far below
+// any score, far above -inf, so exp2(x - floor) of a masked key stays 0.
+constexpr float kMaskFloor = 1.0e30f;
 
 // One workgroup = NH query heads of one (batch, kv head, query block); two
 // wavefronts per head, each owning 32 of the 64 query rows (two 16-row tiles).
@@ -191,9 +194,19 @@ __device__ __forceinline__ void wait_vm_prev() {   // all but this window's 16 /
 // OUTER: the outer gate position (Sec. 4.1, Tab. 1 row 3): no logit bias;
 // the probabilities of a tile enter O += P V scaled by the tile's gate, while
 // the normaliser l sums the unscaled ones.
-template <int NH, bool SPLIT, bool PACKED, bool OUTER>
-__global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
-  constexpr int NW = 2 * NH;
+//
+// KS (one head, four wavefronts): the keys of every tile are split between
+// two wavefront pairs, wavefront (kq, half) taking keys kq*32 .. +31 for its
+// 32 query rows.  One window per tile: S of the wave's next unit (tile t + 1)
+// with the softmax of unit t, then its PV; window t copies V_{t+1} and
+// K_{t+2} into the slots window t - 1 released.  The two key halves' running
+// max, sum and O meet in LDS at the end (the usual softmax merge).  This
+// gives a one-head workgroup (per-head gates) four wavefronts on the same
+// 64 KB of K / V slots, so two such workgroups fill a CU's SIMDs twice.
+template <int NH, bool SPLIT, bool PACKED, bool OUTER, bool KS = false>
+__global__ void __launch_bounds__(NH * 128 * (KS ? 2 : 1), 2) fwd_mfma_kernel(FwdArgs a) {
+  static_assert(!KS || NH == 1, "the key split is for one-head workgroups");
+  constexpr int NW = 2 * NH * (KS ? 2 : 1);
   __shared__ __attribute__((aligned(16))) bf16 s_k[2][TILE];
   __shared__ __attribute__((aligned(16))) bf16 s_v[2][TILE];
 
@@ -203,6 +216,7 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
   const int g = lane >> 5;          // half of the 32x32 operand k range
   const int l32 = lane & 31;        // query column of this lane
   const int half = w & 1;           // rows half*32 .. half*32 + 31 of the block
+  const int kq = KS ? (w >> 1) : 0;   // KS: this wave's key half of every tile
 
   const int unit = xcd_remap(blockIdx.x, gridDim.x);
   const int chunk = unit % a.nchunk;
@@ -211,7 +225,7 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
   const int bhk = rest / a.C;
   const int hk = bhk % a.Hkv;
   const int bb = bhk / a.Hkv;
-  const int h = hk * a.G + a.head_base + chunk * NH + (w >> 1);
+  const int h = hk * a.G + a.head_base + chunk * NH + (KS ? 0 : (w >> 1));
   // gate-table row of this workgroup's heads (all of a chunk share it: with
   // per-head gates a chunk is one head)
   const long long row = ((long long)bb * a.Hs + h / a.Gs) * a.C + i;
@@ -243,7 +257,7 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
   };
   auto kv_rmax = [&](int kb) { return packed ? min(BLK - 1, nb - 1 - kb * BLK) : BLK - 1; };
   if (i * BLK >= nb) {   // uniform over the workgroup: no copy or barrier has been issued
-    if (packed) return;
+    if (packed || kq != 0) return;
     const long long qrow = q0 + l32;
     if (g == 0) a.lse[qrow] = 0.0f;
 #pragma unroll
@@ -340,7 +354,9 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
     mx = max3f(mx, __uint_as_float(sw[0]), __uint_as_float(sw[1]));
     const float tmax = mx * a.c2 + beta;
     if (FIRST) {
-      mrow = tmax;
+      // KS: a wave's first unit can be wholly masked (keys 32..63 of the
+      // diagonal tile for rows 0..31): a finite floor keeps exp2 at 0 there
+      mrow = KS ? fmaxf(tmax, -kMaskFloor) : tmax;
     } else if (__builtin_amdgcn_ballot_w64(tmax > mrow + kLazy) != 0) {   // wave-uniform, rare
       const float mnew = fmaxf(mrow, tmax);
       const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
@@ -457,8 +473,8 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
   wait_vm();
   __syncthreads();
   f32x16 s0, s1;   // S of the unit being finished / the next unit
-  scores_with(s_k[0], 0, s0, [](int) {});
-  mask_diag(0, s0);
+  scores_with(s_k[0], kq, s0, [](int) {});
+  mask_diag(kq, s0);
   update_max(std::true_type{}, s0, 0.0f);
 
   // window (t, kh): copy (V_{t+1} for kh = 0, K_{t+2} for kh = 1); S of the
@@ -508,23 +524,102 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
       }
     }
   };
+  // KS window t (PAR = t & 1): V_{t+1} -> V slot PAR ^ 1 and K_{t+2} -> K
+  // slot PAR (both last read in window t - 1); S of unit (t + 1, kq) from K
+  // slot PAR ^ 1 with the softmax of unit (t, kq); O += V_t^T P; the copies
+  // land before the barrier (window t + 1 reads both)
+  auto window_ks = [&](auto par_tag, int t, f32x16& scur, f32x16& snext) {
+    constexpr int PAR = decltype(par_tag)::value;
+    const bool more = t + 1 < nt;
+    copy_v(tile_block(t + 1, beta_v), PAR ^ 1);
+    {
+      float bk;
+      copy_k(tile_block(t + 2, bk), PAR);
+    }
+    const float off = (OUTER ? 0.0f : beta_cur) - mrow;
+    const float gvw = OUTER ? __builtin_amdgcn_exp2f(beta_cur) : 1.0f;
+    uint32_t pb[2][4], pl[2][4];
+    bf16x8 va[4][2];
+    if (!PACKED) read_va(s_v[PAR], kq, va);
+    if (more) {
+      scores_with(s_k[PAR ^ 1], kq, snext, [&](int m) { p_pair(m, scur, off, gvw, pb, pl); });
+    } else {
+#pragma unroll
+      for (int n = 0; n < 8; ++n) p_pair(n, scur, off, gvw, pb, pl);
+    }
+    if (PACKED) read_va(s_v[PAR], kq, va);
+    pv(va, pb, pl);
+    wait_vm();
+    __syncthreads();
+    if (more) {
+      beta_cur = beta_v;   // tile t + 1
+      update_max(std::false_type{}, snext, OUTER ? 0.0f : beta_cur);
+    }
+  };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  window(I0{}, std::true_type{}, I0{}, 0, s0, s1);
-  window(I1{}, std::true_type{}, I0{}, 0, s1, s0);
-  int t = 1;
+  if (KS) {
+    __syncthreads();   // every wave's S of unit 0 has read K slot 0 (window 0 refills it)
+    window_ks(I0{}, 0, s0, s1);
+    int t = 1;
 #pragma unroll 1
-  for (; t + 1 < nt; t += 2) {   // tiles t (odd) and t + 1 (even)
-    window(I0{}, std::false_type{}, I1{}, t, s0, s1);
-    window(I1{}, std::false_type{}, I1{}, t, s1, s0);
-    window(I0{}, std::false_type{}, I0{}, t + 1, s0, s1);
-    window(I1{}, std::false_type{}, I0{}, t + 1, s1, s0);
-  }
-  if (t < nt) {
-    window(I0{}, std::false_type{}, I1{}, t, s0, s1);
-    window(I1{}, std::false_type{}, I1{}, t, s1, s0);
+    for (; t + 1 < nt; t += 2) {   // tiles t (odd) and t + 1 (even)
+      window_ks(I1{}, t, s1, s0);
+      window_ks(I0{}, t + 1, s0, s1);
+    }
+    if (t < nt) window_ks(I1{}, t, s1, s0);
+  } else {
+    window(I0{}, std::true_type{}, I0{}, 0, s0, s1);
+    window(I1{}, std::true_type{}, I0{}, 0, s1, s0);
+    int t = 1;
+#pragma unroll 1
+    for (; t + 1 < nt; t += 2) {   // tiles t (odd) and t + 1 (even)
+      window(I0{}, std::false_type{}, I1{}, t, s0, s1);
+      window(I1{}, std::false_type{}, I1{}, t, s1, s0);
+      window(I0{}, std::false_type{}, I0{}, t + 1, s0, s1);
+      window(I1{}, std::false_type{}, I0{}, t + 1, s1, s0);
+    }
+    if (t < nt) {
+      window(I0{}, std::false_type{}, I1{}, t, s0, s1);
+      window(I1{}, std::false_type{}, I1{}, t, s1, s0);
+    }
   }
   wait_vm();   // trailing copies
+
+  if (KS) {
+    // merge the key halves: the kq = 1 waves leave m, their partial sums and
+    // O^T in LDS (K slots: O, lane-major 16-byte vectors; V slot 0: m, l),
+    // the kq = 0 waves fold them into their own and write the rows
+    __syncthreads();   // every wave is done with the K / V slots
+    f32x4* xo = (f32x4*)&s_k[0][0] + half * 16 * 64 + lane;
+    float* xm = (float*)&s_v[0][0] + (half * 64 + lane) * 2;
+    if (kq == 1) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          xo[(dt * 4 + q4) * 64] = f32x4{oacc[dt][q4 * 4], oacc[dt][q4 * 4 + 1], oacc[dt][q4 * 4 + 2],
+                                         oacc[dt][q4 * 4 + 3]};
+      xm[0] = mrow;
+      xm[1] = lrow;
+    }
+    __syncthreads();
+    if (kq == 1) return;
+    const float mb = xm[0];
+    const float mnew = fmaxf(mrow, mb);
+    const float aa = __builtin_amdgcn_exp2f(mrow - mnew);
+    const float ab = __builtin_amdgcn_exp2f(mb - mnew);
+    lrow = lrow * aa + xm[1] * ab;
+    mrow = mnew;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 ob = xo[(dt * 4 + q4) * 64];
+#pragma unroll
+        for (int y = 0; y < 4; ++y) oacc[dt][q4 * 4 + y] = oacc[dt][q4 * 4 + y] * aa + ob[y] * ab;
+      }
+  }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
   const float ltot = sum2(lrow);
@@ -555,22 +650,22 @@ __global__ void __launch_bounds__(NH * 128, 2) fwd_mfma_kernel(FwdArgs a) {
   }
 }
 
-template <int NH>
+template <int NH, bool KS = false>
 hipError_t launch_chunks(FwdArgs a, int head_base, int nchunk, long long units,
                          hipStream_t st) {
   a.head_base = head_base;
   a.nchunk = nchunk;
-  const dim3 grid((unsigned)(units * nchunk)), block(NH * 128);
+  const dim3 grid((unsigned)(units * nchunk)), block(NH * 128 * (KS ? 2 : 1));
   const int v = (a.o_fp32 ? 4 : 0) | (a.cu != nullptr ? 2 : 0) | (a.outer ? 1 : 0);
   switch (v) {
-    case 0: hipLaunchKernelGGL((fwd_mfma_kernel<NH, false, false, false>), grid, block, 0, st, a); break;
-    case 1: hipLaunchKernelGGL((fwd_mfma_kernel<NH, false, false, true>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((fwd_mfma_kernel<NH, false, true, false>), grid, block, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((fwd_mfma_kernel<NH, false, true, true>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((fwd_mfma_kernel<NH, true, false, false>), grid, block, 0, st, a); break;
-    case 5: hipLaunchKernelGGL((fwd_mfma_kernel<NH, true, false, true>), grid, block, 0, st, a); break;
-    case 6: hipLaunchKernelGGL((fwd_mfma_kernel<NH, true, true, false>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((fwd_mfma_kernel<NH, true, true, true>), grid, block, 0, st, a); break;
+    case 0: hipLaunchKernelGGL((fwd_mfma_kernel<NH, false, false, false, KS>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((fwd_mfma_kernel<NH, false, false, true, KS>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((fwd_mfma_kernel<NH, false, true, false, KS>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((fwd_mfma_kernel<NH, false, true, true, KS>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((fwd_mfma_kernel<NH, true, false, false, KS>), grid, block, 0, st, a); break;
+    case 5: hipLaunchKernelGGL((fwd_mfma_kernel<NH, true, false, true, KS>), grid, block, 0, st, a); break;
+    case 6: hipLaunchKernelGGL((fwd_mfma_kernel<NH, true, true, false, KS>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((fwd_mfma_kernel<NH, true, true, true, KS>), grid, block, 0, st, a); break;
   }
   return hipGetLastError();
 }
@@ -596,7 +691,8 @@ hipError_t launch_fwd_mfma(const Shape& s, const void* q, const void* k, const v
   a.outer = s.outer;
   const long long units = (long long)s.B * s.Hkv * s.C;
   if (a.Gs < 2) {   // gates per query head: every head selects its own blocks
-    return launch_chunks<1>(a, 0, s.G, units, st);
+    // (one head per workgroup, its tiles' keys split over two wave pairs)
+    return launch_chunks<1, true>(a, 0, s.G, units, st);
   }
   // the G heads of a group are covered by chunks of 2 heads, then 1: two
   // 4-wavefront workgroups per CU drift out of step, so one's barrier and
