@@ -128,28 +128,31 @@ bool mfma_path(const Shape& s) {
 
 BwdWorkspace bwd_workspace_layout(const Shape& s) {
   BwdWorkspace w{};
-  const long long nrow = (long long)s.B * s.Hs * s.C;  // gate-table rows == columns
+  const long long nrow = (long long)s.B * s.Hs * s.C;   // gate-table rows
+  const long long ncol = (long long)s.B * s.Hkv * s.C;  // key-major columns
+  const int nsh = s.Hs / s.Hkv;                         // score heads per kv head
   // largest possible number of (row, selected block) entries
   long long per_seq = 0;
   for (int i = 0; i < s.C; ++i) per_seq += (i < s.cap ? i : s.cap);
   const long long emax = per_seq * s.B * s.Hs;
-  w.words = (s.C + 31) / 32;
+  w.words = (int)(((long long)s.C * nsh + 31) / 32);   // a column's bits: (query block, score head)
   size_t off = 0;
   w.delta = off;    off = align256(off + sizeof(float) * (size_t)s.B * s.Hq * s.N);
   if (mfma_path(s)) {
     w.lsen = off;     off = align256(off + sizeof(float) * (size_t)s.B * s.Hq * s.N);
-    w.colmask = off;  off = align256(off + sizeof(uint32_t) * (size_t)nrow * w.words);
-    w.collen = off;   off = align256(off + sizeof(int32_t) * (size_t)nrow);
-    w.coloff = off;   off = align256(off + sizeof(int32_t) * (size_t)(nrow + 1));
-    w.chunkoff = off; off = align256(off + sizeof(int32_t) * (size_t)(nrow + 1));
+    w.colmask = off;  off = align256(off + sizeof(uint32_t) * (size_t)ncol * w.words);
+    w.collen = off;   off = align256(off + sizeof(int32_t) * (size_t)ncol);
+    w.coloff = off;   off = align256(off + sizeof(int32_t) * (size_t)(ncol + 1));
+    w.chunkoff = off; off = align256(off + sizeof(int32_t) * (size_t)(ncol + 1));
     w.collist = off;  off = align256(off + sizeof(int32_t) * (size_t)(emax + nrow));
     // chunks of at most cc entries: sum over columns of ceil(L / cc) with
-    // sum L = emax + nrow (each column also holds its diagonal entry)
+    // sum L = emax + nrow (each column also holds one diagonal entry per
+    // score head)
     const int cc = col_chunk(s);
-    w.max_chunks = (emax + nrow + (long long)nrow * (cc - 1)) / cc;
+    w.max_chunks = (emax + nrow + (long long)ncol * (cc - 1)) / cc;
     w.partial = off;  off = align256(off + sizeof(float) * 2 * 64 * 128 * (size_t)w.max_chunks);
     w.chunk_rank = off;  off = align256(off + sizeof(int32_t) * (size_t)w.max_chunks);
-    w.chunk_hist = off;  off = align256(off + sizeof(int32_t) * (size_t)(nrow + 1));
+    w.chunk_hist = off;  off = align256(off + sizeof(int32_t) * (size_t)(ncol + 1));
     w.chunk_desc = off; off = align256(off + 4 * sizeof(int32_t) * (size_t)w.max_chunks);
   }
   w.total = off;

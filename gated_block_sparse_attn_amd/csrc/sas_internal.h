@@ -41,11 +41,12 @@ struct Shape {
 struct BwdWorkspace {
   size_t delta;      // float  [B*Hq*N]              Delta: sum of P * dP over a query row
   size_t lsen;       // float  [B*Hq*N]              -LSE log2(e) (-inf: padding row), matrix-core path
-  size_t colmask;    // uint32 [B*Hkv*C*W]           bit (j, i): row i selected block j
-  size_t collen;     // int32  [B*Hkv*C]             1 + #rows selecting column j
+  size_t colmask;    // uint32 [B*Hkv*C*W]           column j, bit i*nsh + sl: query block i of
+                     //                               score head sl (of the kv head) selected j
+  size_t collen;     // int32  [B*Hkv*C]             nsh + #(row, score head) selecting j
   size_t coloff;     // int32  [B*Hkv*C + 1]         prefix of collen
   size_t chunkoff;   // int32  [B*Hkv*C + 1]         prefix of ceil(collen / CH)
-  size_t collist;    // int32  [B*Hkv*C*(cap+1)]     column lists, diagonal first
+  size_t collist;    // int32  [B*Hs*C*(cap+1)]      column lists (codes i*nsh + sl), diagonal first
   size_t partial;    // float  [max_chunks * 2 * 64 * 128]  split dK/dV partial sums
   size_t chunk_rank; // int32  [max_chunks]           rank of a chunk inside its order bucket
   size_t chunk_hist; // int32  [B*Hkv*C + 1]         chunks per (batch, kv head, first row)
@@ -53,7 +54,7 @@ struct BwdWorkspace {
                      //                               list offset, entries (bit 30: only chunk)
   size_t total;
   long long max_chunks;
-  int words;         // W = ceil(C / 32)
+  int words;         // W = ceil(C * nsh / 32), nsh = Hs / Hkv score heads per kv head
 };
 
 // Query blocks per pass-B work item of the matrix-core backward (per-head

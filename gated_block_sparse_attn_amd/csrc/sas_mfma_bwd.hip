@@ -62,7 +62,10 @@ struct BwdArgs {
   uint32_t* colmask; int32_t* collen; int32_t* coloff; int32_t* chunkoff; int32_t* collist;
   float* partial;
   int32_t* chunk_rank; int32_t* chunk_hist; int32_t* chunk_desc;
-  long long ncol;  // B * Hkv * C (rows of the score table == columns)
+  long long nrow;  // B * Hs * C: gate-table rows
+  long long ncol;  // B * Hkv * C: key-major columns (batch, kv head, key block)
+  int nsh;         // score heads per kv head (Hs / Hkv): a column entry is
+                   // (query block i, score head sl of the kv head), code i * nsh + sl
   int Hq, Hkv, G, N, C, cap, W, o_fp32;
   int Hs, Gs;       // score heads (gate-table rows per batch) and query heads per score head
   int hard;         // hard Top-K gates: unit gates on the selected blocks
@@ -638,19 +641,22 @@ __global__ void mark_kernel(BwdArgs a) {
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long row = gid / a.cap;
   const int t = (int)(gid % a.cap);
-  if (row >= a.ncol) return;
+  if (row >= a.nrow) return;
   const int cnt = min(a.sel_cnt[row], a.cap);
   if (t >= cnt) return;
   const int m = a.sel_idx[row * a.cap + t];
   const int i = (int)(row % a.C);
-  const long long col = row - i + m;  // same (batch, kv head), block m
-  atomicOr(&a.colmask[col * a.W + (i >> 5)], 1u << (i & 31));
+  const long long bs = row / a.C;   // batch * Hs + score head
+  const long long bhk = bs / a.nsh;   // batch * Hkv + kv head (Hs = Hkv * nsh)
+  const int code = i * a.nsh + (int)(bs % a.nsh);
+  const long long col = bhk * a.C + m;   // (batch, kv head), block m
+  atomicOr(&a.colmask[col * a.W + (code >> 5)], 1u << (code & 31));
 }
 
 __global__ void count_kernel(BwdArgs a) {
   const long long col = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (col >= a.ncol) return;
-  int L = 1;  // the diagonal block
+  int L = a.nsh;  // the diagonal block, once per score head
   for (int w = 0; w < a.W; ++w) L += __popc(a.colmask[col * a.W + w]);
   a.collen[col] = L;
 }
@@ -699,8 +705,8 @@ __global__ void __launch_bounds__(256) fill_lists_kernel(BwdArgs a) {
   if (col >= a.ncol) return;
   const int j = (int)(col % a.C);
   int32_t* out = a.collist + a.coloff[col];
-  if (lane == 0) out[0] = j;
-  int run = 1;
+  for (int x = lane; x < a.nsh; x += 64) out[x] = j * a.nsh + x;   // the diagonal entries
+  int run = a.nsh;
   for (int w0 = 0; w0 < a.W; w0 += 64) {
     const int wi = w0 + lane;
     uint32_t bits = wi < a.W ? a.colmask[col * a.W + wi] : 0u;
@@ -740,8 +746,8 @@ __global__ void chunk_count_kernel(BwdArgs a) {
   if (g >= a.chunkoff[a.ncol]) return;
   const long long col = chunk_column(a, g);
   const int c = g - a.chunkoff[col];
-  const int first = a.collist[a.coloff[col] + c * a.cc];
-  const long long key = col - col % a.C + first;   // (batch, kv head) row base + first row
+  const int first = a.collist[a.coloff[col] + c * a.cc] / a.nsh;   // its first query block
+  const long long key = col - col % a.C + first;   // (batch, kv head) row base + first block
   a.chunk_rank[g] = atomicAdd(&a.chunk_hist[key], 1);
 }
 
@@ -783,7 +789,7 @@ __global__ void chunk_scatter_kernel(BwdArgs a) {
   const int c = g - a.chunkoff[col];
   const int nch = a.chunkoff[col + 1] - a.chunkoff[col];
   const int e0 = c * a.cc;
-  const int first = a.collist[a.coloff[col] + e0];
+  const int first = a.collist[a.coloff[col] + e0] / a.nsh;
   const long long key = col - col % a.C + first;
   const int ne = min(a.collen[col], e0 + a.cc) - e0;
   const int pos = a.chunk_hist[key] + a.chunk_rank[g];
@@ -910,16 +916,15 @@ bwd_dkdv_kernel(BwdArgs a) {
   const long long col = dcol;
   const int ne = dne & ((1 << 30) - 1);
   const bool only_chunk = (dne >> 30) & 1;
-  // column col = (batch, score head s, key block j); with per-head gates a
-  // kv head's G query heads each have their own columns (G = 1 step per
-  // entry and half), which all add into the kv head's dK / dV partials
+  // column col = (batch, kv head, key block j); an entry is (query block i,
+  // score head sl of the kv head) with its own gate row, covering the score
+  // head's G = Gs query heads (the kv group with group gates, one head with
+  // per-head gates)
   const int j = (int)(col % a.C);
-  const long long bs = col / a.C;   // gate-table row base: batch * Hs + s
-  const int sh = (int)(bs % a.Hs);
-  const int bb = (int)(bs / a.Hs);
-  const int hk = sh * a.Gs / a.G;
-  const long long bhk = (long long)bb * a.Hkv + hk;
-  const int G = a.Gs;   // query heads per column (the kv group's G with group gates)
+  const long long bhk = col / a.C;
+  const int hk = (int)(bhk % a.Hkv);
+  const int bb = (int)(bhk / a.Hkv);
+  const int G = a.Gs;   // query heads per entry
   constexpr bool packed = PACKED;
   const Span sp = seq_span(a, bb);
   // A packed batch has no rows for a key block past its sequence's end (no
@@ -947,16 +952,23 @@ bwd_dkdv_kernel(BwdArgs a) {
   long long rowbase = 0;   // per entry: workspace row of (query block, head 0) (padded order)
   long long prow = 0;      // packed batch: tensor row of (query block, head 0)
   int vrem = 0;            // packed batch: valid rows of the entry's query block
+  int diag_e = 0;   // this lane's entry is a diagonal one (query block j)
   if (lane < ne) {
-    const int i = a.collist[loff + lane];
+    const int code = a.collist[loff + lane];
+    const int i = code / a.nsh;
+    const long long bs = bhk * a.nsh + code % a.nsh;   // gate-table row base: batch * Hs + s
+    const int sh = (int)(bs % a.Hs);
     if (wv == 0) {
-      itab[lane] = i;
+      itab[lane] = code;
       btab[lane] = (i == j || a.hard) ? 0.0f : a.lg[(bs * a.C + i) * a.C + j] * kLog2e;
     }
     rowbase = ((long long)bb * a.Hq + sh * G) * a.N + (long long)i * BLK;
     prow = (sp.start + (long long)i * BLK) * a.Hq + sh * G;
     vrem = sp.n - i * BLK;
+    diag_e = i == j;
   }
+  // the diagonal entries (one per score head) lead the column's list
+  const int ndiag = __builtin_popcountll(__builtin_amdgcn_ballot_w64(diag_e != 0));
 
 
   const int n = 2 * ne * G;   // steps: entry e, head h, half x -> step 2 (e G + h) + x
@@ -1179,7 +1191,7 @@ bwd_dkdv_kernel(BwdArgs a) {
     ring_barrier(kh);   // Q of steps 0, 1 landed
     rows_product_with(qring(0), r0, [](int) {});   // S_0
     int qk = 1, ok = 0;
-    const int nd = itab[0] == j ? 2 * G : 0;
+    const int nd = 2 * G * ndiag;
 #pragma unroll 1
     for (int s = 0; s < nd; s += 2) {
       window_a(std::true_type{}, std::integral_constant<int, 0>{}, qring(qk), oring(ok), pbuf(0), 0.0f, r0, r1);
@@ -1189,7 +1201,7 @@ bwd_dkdv_kernel(BwdArgs a) {
       ring_barrier(kh);
       qk = inc(qk, Q_SLOTS); ok = inc(ok, O_SLOTS);
     }
-    int ent = nd ? 1 : 0, hh = 0;
+    int ent = ndiag, hh = 0;
     float beta = btab[ent < ne ? ent : 0];
 #pragma unroll 1
     for (int s = nd; s < n; s += 2) {
@@ -1269,16 +1281,19 @@ bwd_dkdv_kernel(BwdArgs a) {
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the trailing copies
   __syncthreads();   // dLogG partials of both key halves are in gtab
 
-  // dLogG[i, j] of every entry with i != j (key halves added in order)
+  // dLogG[i, j] of every entry with i != j, in its score head's gate row
+  // (key halves added in order)
   if (wv == 1 && lane < ne) {
-    const int ib = itab[lane];
+    const int code = itab[lane];
+    const int ib = code / a.nsh;
+    const long long bs = bhk * a.nsh + code % a.nsh;
     if (ib != j) a.dlg[(bs * a.C + ib) * a.C + j] = gtab[lane] + gtab[kColChunkMax + lane];
   }
 
   // epilogue: A writes dV, B writes dK (times the softmax scale), keys kh*32 + l32
   const long long orow = bhk * a.N + (long long)j * BLK + kh * 32;
   const float mul = role == 0 ? 1.0f : a.scale;
-  if (only_chunk && a.Gs == a.G) {   // the only contributor to these rows
+  if (only_chunk) {   // the only contributor to these rows
     bf16* dst = role == 0 ? a.dv : a.dk;
     const int key = j * BLK + kh * 32 + l32;
     if (packed && key >= sp.n) return;   // the row belongs to no sequence of this batch
@@ -1307,15 +1322,11 @@ bwd_dkdv_kernel(BwdArgs a) {
 // One workgroup per (column, quarter of its 64 x 128 tile); each lane sums
 // 8 consecutive fp32 of dK and of dV over the column's chunks, in chunk order
 // (deterministic), four chunks' loads in flight at a time.
-// With per-head gates the G score-head columns of a kv column are summed in
-// head order.
 __global__ void __launch_bounds__(256) reduce_kernel(BwdArgs a) {
-  const long long kcol = blockIdx.x >> 2;   // (batch, kv head, key block)
-  const int j = (int)(kcol % a.C);
-  const long long bhk = kcol / a.C;
-  const int ns = a.G / a.Gs;                 // score-head columns per kv column
-  const long long col = ((bhk / a.Hkv) * a.Hs + (bhk % a.Hkv) * ns) * a.C + j;   // the first
-  if (ns == 1 && a.chunkoff[col + 1] - a.chunkoff[col] <= 1) return;   // written directly
+  const long long col = blockIdx.x >> 2;   // (batch, kv head, key block)
+  const int j = (int)(col % a.C);
+  const long long bhk = col / a.C;
+  if (a.chunkoff[col + 1] - a.chunkoff[col] <= 1) return;   // written directly
   const long long orow = bhk * a.N + (long long)j * BLK;
   const int e = (threadIdx.x + (blockIdx.x & 3) * 256) * 8;
   // packed batch: key row e / HD of the block, if it belongs to the sequence
@@ -1328,9 +1339,8 @@ __global__ void __launch_bounds__(256) reduce_kernel(BwdArgs a) {
   }
   f32x4 sk[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
   f32x4 sv[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-  for (int t = 0; t < ns; ++t) {
-  const int c0 = a.chunkoff[col + (long long)t * a.C];
-  const int nch = a.chunkoff[col + (long long)t * a.C + 1] - c0;
+  const int c0 = a.chunkoff[col];
+  const int nch = a.chunkoff[col + 1] - c0;
   const float* base = a.partial + (long long)c0 * 2 * 8192 + e;
   int cc = 0;
   for (; cc + 4 <= nch; cc += 4) {
@@ -1355,7 +1365,6 @@ __global__ void __launch_bounds__(256) reduce_kernel(BwdArgs a) {
       sk[h] += *(const f32x4*)(pk + 4 * h);
       sv[h] += *(const f32x4*)(pk + 8192 + 4 * h);
     }
-  }
   }
   bf16x8 ok, ov;
 #pragma unroll
@@ -1403,7 +1412,9 @@ BwdArgs make_bwd_args(const Shape& s, const BwdPtrs& p, char* ws, const BwdWorks
   a.chunk_rank = (int32_t*)(ws + wl.chunk_rank);
   a.chunk_hist = (int32_t*)(ws + wl.chunk_hist);
   a.chunk_desc = (int32_t*)(ws + wl.chunk_desc);
-  a.ncol = (long long)s.B * s.Hs * s.C;   // gate-table rows == columns
+  a.nrow = (long long)s.B * s.Hs * s.C;    // gate-table rows
+  a.ncol = (long long)s.B * s.Hkv * s.C;   // key-major columns
+  a.nsh = s.Hs / s.Hkv;
   a.Hs = s.Hs;
   a.Gs = s.Hq / s.Hs;
   a.hard = s.hard;
@@ -1451,7 +1462,7 @@ hipError_t launch_bwd_dq_mfma(const Shape& s, const BwdPtrs& p, char* ws, const 
   const long long nmask = a.ncol * a.W;
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)min((nmask + 255) / 256, 65535LL)),
                      dim3(256), 0, st, a.colmask, nmask);
-  const long long nmark = a.ncol * s.cap;
+  const long long nmark = a.nrow * s.cap;
   hipLaunchKernelGGL(mark_kernel, dim3((unsigned)((nmark + 255) / 256)), dim3(256), 0, st, a);
   hipLaunchKernelGGL(count_kernel, dim3((unsigned)((a.ncol + 255) / 256)), dim3(256), 0, st, a);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, a);
@@ -1470,7 +1481,7 @@ hipError_t launch_bwd_dkdv_mfma(const Shape& s, const BwdPtrs& p, char* ws,
                                 const BwdWorkspace& wl, hipStream_t st) {
   BwdArgs a = make_bwd_args(s, p, ws, wl);
   // dLogG: zero everywhere, then the key-major pass writes the selected entries
-  const long long ntab = a.ncol * s.C;
+  const long long ntab = a.nrow * s.C;
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)min((ntab + 255) / 256, 65535LL)),
                      dim3(256), 0, st, (uint32_t*)a.dlg, ntab);
   const dim3 kgrid((unsigned)wl.max_chunks), kblock(256);
@@ -1496,7 +1507,7 @@ hipError_t launch_bwd_dkdv_mfma(const Shape& s, const BwdPtrs& p, char* ws,
     e = hipFuncSetAttribute((const void*)&ste_mfma_kernel,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(ste_mfma_kernel, dim3((unsigned)a.ncol), dim3(256), lds, st, a);
+    hipLaunchKernelGGL(ste_mfma_kernel, dim3((unsigned)a.nrow), dim3(256), lds, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (p.dscores == nullptr) return hipSuccess;
