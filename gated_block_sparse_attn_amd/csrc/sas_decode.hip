@@ -776,16 +776,49 @@ __global__ void __launch_bounds__(64 * kCombWaves) decode_combine_kernel(DecArgs
   const int b = bq / a.Hq, h = bq % a.Hq;
   const int hk = h / a.G, hh = h % a.G;
   const int bh = b * a.Hkv + hk;
-  const int nt = min(max(a.sel_cnt[bh], 0), a.cap) + 1;
+  const int cnt_raw = a.sel_cnt[bh];
   const float* p0 = a.part + (long long)bh * a.T * a.G * (D + 2) + hh * (D + 2);
   const long long stride = (long long)a.G * (D + 2);
   float mw = -INFINITY, lw = 0.0f;
   float acc[PER];
 #pragma unroll
   for (int x = 0; x < PER; ++x) acc[x] = 0.0f;
-  // this wavefront's tiles: w + kCombWaves * j, j < nw
+  // this wavefront's tiles: w + kCombWaves * j.  The first batch is read for
+  // every tile slot (all T slots lie in the buffer) together with the
+  // count, so that one memory latency serves both; slots past the count are
+  // skipped below (their O was never written).
+  auto fold = [&](float m, float l, const float (&ov)[PER]) {
+    const float mn = fmaxf(mw, m);
+    const float so = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - mn);
+    const float sn = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+    lw = lw * so + l * sn;
+#pragma unroll
+    for (int x = 0; x < PER; ++x) acc[x] = acc[x] * so + ov[x] * sn;
+    mw = mn;
+  };
+  const int nw_cap = a.T > w ? (a.T - w + kCombWaves - 1) / kCombWaves : 0;
+  const int n0 = min(kCombBatch, nw_cap);
+  {
+    float mt[kCombBatch], lt[kCombBatch], ot[kCombBatch][PER];
+#pragma unroll
+    for (int j = 0; j < kCombBatch; ++j) {
+      if (j < n0) {
+        const float* pt = p0 + (long long)(w + kCombWaves * j) * stride;
+        mt[j] = pt[D];
+        lt[j] = pt[D + 1];
+#pragma unroll
+        for (int x = 0; x < PER; ++x) ot[j][x] = pt[x * 64 + lane];
+      }
+    }
+    const int nt = min(max(cnt_raw, 0), a.cap) + 1;
+    const int nw = nt > w ? (nt - w + kCombWaves - 1) / kCombWaves : 0;
+#pragma unroll
+    for (int j = 0; j < kCombBatch; ++j)
+      if (j < min(n0, nw)) fold(mt[j], lt[j], ot[j]);
+  }
+  const int nt = min(max(cnt_raw, 0), a.cap) + 1;
   const int nw = nt > w ? (nt - w + kCombWaves - 1) / kCombWaves : 0;
-  for (int j0 = 0; j0 < nw; j0 += kCombBatch) {
+  for (int j0 = kCombBatch; j0 < nw; j0 += kCombBatch) {
     const int n = min(kCombBatch, nw - j0);
     float mt[kCombBatch], lt[kCombBatch], ot[kCombBatch][PER];
 #pragma unroll
@@ -799,17 +832,8 @@ __global__ void __launch_bounds__(64 * kCombWaves) decode_combine_kernel(DecArgs
       }
     }
 #pragma unroll
-    for (int j = 0; j < kCombBatch; ++j) {
-      if (j < n) {
-        const float mn = fmaxf(mw, mt[j]);
-        const float so = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - mn);
-        const float sn = mt[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mt[j] - mn);
-        lw = lw * so + lt[j] * sn;
-#pragma unroll
-        for (int x = 0; x < PER; ++x) acc[x] = acc[x] * so + ot[j][x] * sn;
-        mw = mn;
-      }
-    }
+    for (int j = 0; j < kCombBatch; ++j)
+      if (j < n) fold(mt[j], lt[j], ot[j]);
   }
 #pragma unroll
   for (int x = 0; x < PER; ++x) s_red[w][x * 64 + lane] = acc[x];
