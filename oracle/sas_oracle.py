@@ -267,7 +267,7 @@ def forward(q, k, v, log_gate, sel, block: int, sm_scale: float | None = None,
 
 
 def backward(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = None,
-             query_blocks=None, gate_pos: str = "inner", seq_lens=None):
+             query_blocks=None, gate_pos: str = "inner", seq_lens=None, term_mass: bool = False):
     """Gradients of Eq. 9 w.r.t. q, k, v and the block log gates.
 
     Follows the recomputation view of App. E: P from the attended logits,
@@ -286,6 +286,12 @@ def backward(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = No
     and dLogG rows are exact; dK/dV hold only their contributions).
     ``seq_lens``: padding query rows contribute nothing and get dQ = 0.
     Returns (dq, dk, dv, dlog_gate) in float64.
+
+    ``term_mass``: also return the sums of the absolute values of the terms
+    that dK and dV add up (sm_scale |dS|^T |Q| and |g| P^T |dO|), the scale
+    of the rounding error of a sum whose terms are rounded (the tests bound
+    the error of the bf16 products with it); (dq, dk, dv, dlog_gate,
+    dk_mass, dv_mass).
     """
     bsz, hq, n, d = q.shape
     g = hq // k.shape[1]
@@ -297,6 +303,8 @@ def backward(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = No
     dk = np.zeros(k.shape)
     dv = np.zeros(v.shape)
     dlg = np.zeros((bsz, hs, c, c))
+    dk_mass = np.zeros(k.shape) if term_mass else None
+    dv_mass = np.zeros(v.shape) if term_mass else None
     units = query_blocks if query_blocks is not None else \
         [(b, h, i) for b in range(bsz) for h in range(hs) for i in range(c)]
     for (b, sh, i) in units:
@@ -333,31 +341,40 @@ def backward(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = No
             # add accumulates each key row once
             dk[b, hk, keys] += scale * (ds.T @ qq)
             dv[b, hk, keys] += gkey[:, None] * (p.T @ dd)
+            if term_mass:
+                dk_mass[b, hk, keys] += scale * (np.abs(ds).T @ np.abs(qq))
+                dv_mass[b, hk, keys] += np.abs(gkey)[:, None] * (p.T @ np.abs(dd))
             ds_sum += (p * dp).sum(axis=0) if gate_pos == "outer" else ds.sum(axis=0)
         for m in np.unique(kblk):
             if m != i:
                 dlg[b, sh, i, m] = ds_sum[kblk == m].sum()
+    if term_mass:
+        return dq, dk, dv, dlg, dk_mass, dv_mass
     return dq, dk, dv, dlg
 
 
 def backward_kv_block(q, k, v, do, log_gate, sel, block: int, b: int, hk: int, j: int,
-                      sm_scale: float | None = None, gate_pos: str = "inner", seq_lens=None):
+                      sm_scale: float | None = None, gate_pos: str = "inner", seq_lens=None,
+                      term_mass: bool = False):
     """dK and dV of one key block j of one (batch, kv head), exactly.
 
     Sums the contributions of every query block that attends block j: the
     diagonal block i = j and every i > j with j in I_i (Eq. 9 gradient).
     ``seq_lens`` as in ``backward`` (padding rows contribute nothing).
-    Returns (dk_j [block, D], dv_j [block, D]).
+    Returns (dk_j [block, D], dv_j [block, D]), and with ``term_mass`` also
+    the block's term masses as in ``backward``.
     """
     c = q.shape[2] // block
     g = q.shape[1] // k.shape[1]
     gs = q.shape[1] // sel.shape[1]
     heads = range(hk * g // gs, (hk + 1) * g // gs)   # score heads of kv head hk
     users = [(b, sh, i) for sh in heads for i in range(j, c) if i == j or sel[b, sh, i, j]]
-    _, dk, dv, _ = backward(q, k, v, do, log_gate, sel, block, sm_scale, query_blocks=users,
-                            gate_pos=gate_pos, seq_lens=seq_lens)
+    out = backward(q, k, v, do, log_gate, sel, block, sm_scale, query_blocks=users,
+                   gate_pos=gate_pos, seq_lens=seq_lens, term_mass=term_mass)
     rows = slice(j * block, (j + 1) * block)
-    return dk[b, hk, rows], dv[b, hk, rows]
+    if term_mass:
+        return out[1][b, hk, rows], out[2][b, hk, rows], out[4][b, hk, rows], out[5][b, hk, rows]
+    return out[1][b, hk, rows], out[2][b, hk, rows]
 
 
 def ste_gate_grad(q, k, v, do, log_gate, sel, block: int, sm_scale: float | None = None,

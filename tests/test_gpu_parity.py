@@ -85,6 +85,13 @@ VARIANTS = [
     ("heads_mfma_g5", 2, 10, 2, 640, 128, 64, 3, "bf16", "softmax", "inner", "soft", "head"),
     ("heads_mfma_sigmoid_g4", 1, 8, 2, 1024, 128, 64, 4, "bf16", "sigmoid", "inner", "soft", "head"),
     ("heads_mfma_k16_g4", 1, 8, 2, 2048, 128, 64, 16, "bf16", "softmax", "inner", "soft", "head"),
+    # many score heads per kv head: each key-major column holds G diagonal
+    # entries and the selections of G heads (several chunks per column)
+    ("heads_mfma_g16", 1, 16, 1, 1024, 128, 64, 4, "bf16", "softmax", "inner", "soft", "head"),
+    ("heads_mfma_g32_k8", 1, 32, 1, 768, 128, 64, 8, "bf16", "softmax", "inner", "soft", "head"),
+    # fp32 output (split P) on the key-split per-head forward
+    ("heads_mfma_fp32_out", 1, 8, 2, 768, 128, 64, 3, "bf16", "softmax", "inner", "soft", "head",
+     "fp32"),
     # hard gates on the matrix-core path (dropped-block gradients from the vector-ALU pass)
     ("hard_ste_mfma_heads_g4", 1, 8, 2, 768, 128, 64, 3, "bf16", "softmax", "inner", "hard_ste",
      "head"),
@@ -131,6 +138,9 @@ VARLEN = [
      "softmax", "inner", "soft", "group"),
     ("varlen_mfma_g5_sigmoid", 2, 10, 2, 640, 128, 64, 3, "bf16", (1, 383),
      "sigmoid", "inner", "soft", "group"),
+    # per-head gates, padded layout: padding blocks in the key-split kernels
+    ("varlen_mfma_heads_g4", 3, 8, 2, 768, 128, 64, 3, "bf16", (700, 64, 0),
+     "softmax", "inner", "soft", "head"),
     ("varlen_mfma_hard_ste", 2, 8, 2, 640, 128, 64, 3, "bf16", (640, 200),
      "softmax", "inner", "hard_ste", "group"),
     ("varlen_outer_sigmoid_bf16", 2, 8, 2, 512, 128, 64, 3, "bf16", (449, 130),

@@ -294,6 +294,45 @@ def test_backward_matches_torch_autograd():
     assert np.all(dlg[~p["sel"]] == 0.0)
 
 
+def test_backward_term_masses_match_dense_autograd_terms():
+    """The absolute term sums behind dK and dV (the scale of their rounding
+    error): scale |dS|^T |Q| and P^T |dO| over the attending query rows of
+    every query head of the kv group, with P and dS = dL/dz taken from torch
+    autograd over the dense masked logits z; they bound |dK| and |dV|."""
+    p = rand_problem(23, B=1, Hq=4, Hkv=2, N=32, D=8, block=4, K=2)
+    dq, dk, dv, dlg, dkm, dvm = oracle.backward(p["q"], p["k"], p["v"], p["do"], p["lg"],
+                                                p["sel"], 4, term_mass=True)
+    dq0, dk0, dv0, dlg0 = oracle.backward(p["q"], p["k"], p["v"], p["do"], p["lg"], p["sel"], 4)
+    for x, y in ((dq, dq0), (dk, dk0), (dv, dv0), (dlg, dlg0)):
+        np.testing.assert_array_equal(x, y)
+    B, Hq, N, D = p["q"].shape
+    G = Hq // p["k"].shape[1]
+    scale = 1.0 / math.sqrt(D)
+    tb = torch.arange(N) // 4
+    causal = torch.arange(N)[None, :] <= torch.arange(N)[:, None]
+    lg = torch.from_numpy(np.where(np.isfinite(p["lg"]), p["lg"], 0.0))
+    sel = torch.from_numpy(p["sel"])
+    ref_k = np.zeros_like(dkm)
+    ref_v = np.zeros_like(dvm)
+    for h in range(Hq):
+        hk = h // G
+        same = tb[:, None] == tb[None, :]
+        bias = torch.where(same & causal, torch.zeros(N, N, dtype=torch.float64),
+                           torch.where(sel[0, hk][tb][:, tb], lg[0, hk][tb][:, tb],
+                                       torch.full((N, N), -math.inf, dtype=torch.float64)))
+        q = torch.from_numpy(p["q"][0, h])
+        z = (scale * q @ torch.from_numpy(p["k"][0, hk]).T + bias).requires_grad_(True)
+        pr = torch.softmax(z, dim=-1)
+        do = torch.from_numpy(p["do"][0, h])
+        (pr @ torch.from_numpy(p["v"][0, hk]) * do).sum().backward()
+        ref_k[0, hk] += scale * (z.grad.abs().T @ q.abs()).numpy()
+        ref_v[0, hk] += (pr.detach().T @ do.abs()).numpy()
+    np.testing.assert_allclose(dkm, ref_k, atol=1e-11)
+    np.testing.assert_allclose(dvm, ref_v, atol=1e-11)
+    assert np.all(np.abs(dk) <= dkm + 1e-12) and np.all(np.abs(dv) <= dvm + 1e-12)
+    assert np.any(dkm > np.abs(dk) + 1e-6) and np.any(dvm > np.abs(dv) + 1e-6)
+
+
 def test_backward_kv_block_equals_full_backward():
     p = rand_problem(17, B=2, Hq=4, Hkv=2, N=32, D=8, block=4, K=2)
     _, dk, dv, _ = oracle.backward(p["q"], p["k"], p["v"], p["do"], p["lg"], p["sel"], 4)
