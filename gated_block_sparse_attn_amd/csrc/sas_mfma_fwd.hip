@@ -321,10 +321,13 @@ __global__ void __launch_bounds__(NH * 128 * (KS ? 2 : 1), 2) fwd_mfma_kernel(Fw
   // S^T of keys kh*32 .. +31 of the K tile in Ks (lane: query l32, keys
   // 8 (jj/4) + 4 g + jj%4); after MFMA m (m = 0..7) the work per_mfma(m) is
   // issued (sched_barrier keeps the interleave)
-  auto scores_with = [&](const bf16* Ks, int kh, f32x16& sc, auto&& per_mfma) {
-    bf16x8 ka[8];
+  // (the K fragments are read by load_ka, issued before a window's V^T
+  // reads so that the first product does not queue behind them)
+  auto load_ka = [&](const bf16* Ks, int kh, bf16x8 (&ka)[8]) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) ka[ks] = *(const bf16x8*)(Ks + swz(kh * 32 + l32, ks * 2 + g));
+  };
+  auto scores_from = [&](const bf16x8 (&ka)[8], f32x16& sc, auto&& per_mfma) {
 #pragma unroll
     for (int x = 0; x < 16; ++x) sc[x] = 0.0f;
 #pragma unroll
@@ -333,6 +336,11 @@ __global__ void __launch_bounds__(NH * 128 * (KS ? 2 : 1), 2) fwd_mfma_kernel(Fw
       per_mfma(ks);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  auto scores_with = [&](const bf16* Ks, int kh, f32x16& sc, auto&& per_mfma) {
+    bf16x8 ka[8];
+    load_ka(Ks, kh, ka);
+    scores_from(ka, sc, per_mfma);
   };
   // causal mask of the diagonal tile: key > query -> -inf
   auto mask_diag = [&](int kh, f32x16& sc) {
@@ -499,13 +507,19 @@ __global__ void __launch_bounds__(NH * 128 * (KS ? 2 : 1), 2) fwd_mfma_kernel(Fw
     const float gvw = OUTER ? __builtin_amdgcn_exp2f(beta_cur) : 1.0f;   // outer: the tile's gate
     uint32_t pb[2][4], pl[2][4];
     bf16x8 va[4][2];
+    // next unit: (t, 1) reads K_t, (t + 1, 0) reads K_{t+1}
+    const bf16* kn = KH == 0 ? s_k[PAR] : s_k[PAR ^ 1];
+    // K fragments first (not with split P, whose lo terms leave no
+    // registers for both sets in flight)
+    constexpr bool K_FIRST = !SPLIT;
+    bf16x8 ka[8];
+    if (K_FIRST && more) load_ka(kn, KH ^ 1, ka);
     // (a packed batch's per-lane clamped copies leave no registers for the
     // early read: there the fragments are read just before the product)
     if (!PACKED) read_va(s_v[PAR], KH, va);
-    // next unit: (t, 1) reads K_t, (t + 1, 0) reads K_{t+1}
-    const bf16* kn = KH == 0 ? s_k[PAR] : s_k[PAR ^ 1];
     if (more) {
-      scores_with(kn, KH ^ 1, snext, [&](int m) { p_pair(m, scur, off, gvw, pb, pl); });
+      if (!K_FIRST) load_ka(kn, KH ^ 1, ka);
+      scores_from(ka, snext, [&](int m) { p_pair(m, scur, off, gvw, pb, pl); });
     } else {
 #pragma unroll
       for (int n = 0; n < 8; ++n) p_pair(n, scur, off, gvw, pb, pl);
