@@ -92,8 +92,10 @@ typedef enum sas_gate_rank {
                            attention mass its tokens would get under the
                            selected set's normaliser, Eq. 7), written to
                            dlog_gate, and dscores = g (dg - sum_l g_l dg_l).
-                           Softmax activation and inner position only; runs on
-                           the vector-ALU path (full-scope work).            */
+                           Softmax activation and inner position only.  The
+                           dropped blocks' gradients are full-scope work: on
+                           the matrix-core path one more kernel pass over
+                           every historical block of each gate row.        */
 } sas_gate_rank;
 
 typedef enum sas_status {
@@ -233,7 +235,25 @@ int32_t sas_gated_attn_fwd(const sas_problem* p, const void* q, const void* k, c
                            int32_t sel_cap, void* o, float* lse, void* stream);
 
 /* Bytes of device workspace sas_gated_attn_bwd needs for problem p and the
- * given sel_cap (0 if p or sel_cap is invalid; then sas_last_error says why). */
+ * given sel_cap (0 if p or sel_cap is invalid; then sas_last_error says why).
+ *
+ * The sum of these parts, each rounded up to 256 bytes, with
+ * Hs = score heads (n_kv_heads, or n_q_heads with per-head gates),
+ * C = blocks per sequence, nrow = B Hs C gate rows, ncol = B Hkv C key
+ * columns, E = B Hs sum_{i<C} min(i, sel_cap) selected entries:
+ *   vector-ALU path (fp32, or head_dim != 128, or block_size != 64):
+ *     4 B Hq N (Delta);
+ *   matrix-core path, in addition:
+ *     4 B Hq N (-LSE in log2 units), 4 ncol ceil(C Hs / (32 Hkv)) (column
+ *     bit masks), 16 ncol + 12 (column lengths and offsets, chunk offsets
+ *     and counts),
+ *     4 (E + nrow) (column lists), and per column chunk 65536 bytes (fp32
+ *     dK and dV partials of a column split over several chunks) + 20 bytes
+ *     (schedule), for at most (E + nrow + ncol (cc - 1)) / cc chunks of up
+ *     to cc entries, cc = 16 with group gates and min(64, 16 G) with
+ *     per-head gates.
+ * The partials dominate: about 0.5 GiB for batch 1, 32 / 8 heads, 32k
+ * tokens, sel_cap 16, and 3.0 GiB at 128k tokens with sel_cap 32. */
 size_t sas_gated_attn_bwd_workspace_size(const sas_problem* p, int32_t sel_cap);
 
 /*
