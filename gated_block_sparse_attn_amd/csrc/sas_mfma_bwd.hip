@@ -737,17 +737,37 @@ __device__ __forceinline__ long long chunk_column(const BwdArgs& a, int g) {
   return lo;
 }
 
-// Order of the key-major work: chunks sorted by (batch, kv head, first query
-// block they read).  Workgroups that run at the same time then stream nearby
-// query blocks, so their Q / dO rows are shared through the L2 / MALL.  The
-// order only schedules work; every result is reduced in a fixed order.
+// Order of the key-major work: chunks sorted by (batch, kv head, order
+// bucket).  The bucket of a chunk is the first query block it reads, so that
+// workgroups that run at the same time stream nearby query blocks and share
+// their Q / dO rows through the L2 / MALL.  Chunks that start in the last
+// third of the sequence are bucketed by length instead (longest first; within
+// one length, by first query block in R / cc coarse steps): there the lists
+// run out, and a long chunk that starts late would run on alone after the
+// others have finished.  (Same-box A/B at 32k: key-major kernel 2-3 % faster
+// than with first-block buckets throughout.)  The order only schedules work;
+// every result is reduced in a fixed order.
+__device__ __forceinline__ long long chunk_key(const BwdArgs& a, long long col, int first, int ne) {
+  const int T = a.C - a.C / 3;
+  const int R = a.C - T;
+  int k = first;
+  if (first >= T && R > 1) {
+    const int sb = max(1, R / a.cc);
+    const int cls = a.cc - min(ne, a.cc);   // 0: the longest chunks
+    k = T + min(R - 1, cls * sb + (int)((long long)(first - T) * sb / R));
+  }
+  return col - col % a.C + k;   // (batch, kv head) row base + bucket
+}
+
+// rank of each chunk inside its order bucket
 __global__ void chunk_count_kernel(BwdArgs a) {
   const int g = blockIdx.x * blockDim.x + threadIdx.x;
   if (g >= a.chunkoff[a.ncol]) return;
   const long long col = chunk_column(a, g);
   const int c = g - a.chunkoff[col];
   const int first = a.collist[a.coloff[col] + c * a.cc] / a.nsh;   // its first query block
-  const long long key = col - col % a.C + first;   // (batch, kv head) row base + first block
+  const int ne = min(a.collen[col], c * a.cc + a.cc) - c * a.cc;
+  const long long key = chunk_key(a, col, first, ne);
   a.chunk_rank[g] = atomicAdd(&a.chunk_hist[key], 1);
 }
 
@@ -790,8 +810,8 @@ __global__ void chunk_scatter_kernel(BwdArgs a) {
   const int nch = a.chunkoff[col + 1] - a.chunkoff[col];
   const int e0 = c * a.cc;
   const int first = a.collist[a.coloff[col] + e0] / a.nsh;
-  const long long key = col - col % a.C + first;
   const int ne = min(a.collen[col], e0 + a.cc) - e0;
+  const long long key = chunk_key(a, col, first, ne);
   const int pos = a.chunk_hist[key] + a.chunk_rank[g];
   int32_t* d = a.chunk_desc + 4 * (long long)xcd_unmap(pos, total);
   d[0] = g;
