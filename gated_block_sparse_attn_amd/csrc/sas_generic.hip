@@ -529,7 +529,7 @@ hipError_t launch_bwd_dkdv_generic(const Shape& s, const BwdPtrs& p, char* ws,
   });
   if (e == hipSuccess && s.hard) e = launch_ste_dropped(s, p, ws, wl, st);
   if (e != hipSuccess || p.dscores == nullptr) return e;
-  return launch_dscores(s, p.dlog_gate, p.log_gate, p.dscores, st);
+  return launch_dscores(s, p.dlog_gate, p.log_gate, p.dscores, nullptr, nullptr, st);
 }
 
 }  // namespace sas

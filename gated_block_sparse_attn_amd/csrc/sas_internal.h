@@ -76,8 +76,13 @@ BwdWorkspace bwd_workspace_layout(const Shape& s);
 hipError_t launch_threshold(const Shape& s, const float* scores, float* log_gate, float* tau,
                             int32_t* sel_idx, int32_t* sel_cnt, int32_t* d_status,
                             hipStream_t st);
-hipError_t launch_dscores(const Shape& s, const float* dlog_gate, const float* log_gate,
-                          float* dscores, hipStream_t st);
+// dscores from the dLogG table.  With sel_idx == nullptr (and always with
+// hard gates) the table must be complete (zero outside the written entries).
+// Otherwise the table holds valid values only at each row's selected blocks,
+// and this call also writes the rest of it as 0.
+hipError_t launch_dscores(const Shape& s, float* dlog_gate, const float* log_gate,
+                          float* dscores, const int32_t* sel_idx, const int32_t* sel_cnt,
+                          hipStream_t st);
 
 hipError_t launch_fwd_generic(const Shape& s, const void* q, const void* k, const void* v,
                               const float* log_gate, const int32_t* sel_idx,

@@ -477,6 +477,17 @@ __global__ void __launch_bounds__(NH * 128 * (KS ? 2 : 1), 2) bwd_dq_kernel(BwdA
     a.delta[qr] = row_valid ? dsum : 0.0f;
     a.lsen[qr] = row_valid ? -lse2 : -INFINITY;
   }
+  // the row's selection into the key-major column bit masks (zeroed before
+  // this kernel): bit i*nsh + sl of column (batch, kv head, block m) for each
+  // selected m, set by one wavefront per gate row (the first row half of the
+  // score head's first query head), after its last tile so that these
+  // atomics hold up no wait of the tile loop
+  if (half == 0 && h % a.Gs == 0) {
+    const int code = i * a.nsh + (h / a.Gs - hk * a.nsh);
+    const uint32_t bit = 1u << (code & 31);
+    uint32_t* cm = a.colmask + (long long)bhk * a.C * a.W + (code >> 5);
+    for (int e = lane; e < cnt; e += 64) atomicOr(cm + (long long)sel[e] * a.W, bit);
+  }
 
   // dQ = scale * dQacc (lane: query l32, dims dt*32 + q4*8 + 4 g .. +3)
   if (packed && !row_valid) return;   // the row belongs to no sequence of this batch
@@ -635,22 +646,6 @@ __global__ void fill_zero_kernel(uint32_t* p, long long n) {
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
        e += (long long)gridDim.x * blockDim.x)
     p[e] = 0u;
-}
-
-__global__ void mark_kernel(BwdArgs a) {
-  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long row = gid / a.cap;
-  const int t = (int)(gid % a.cap);
-  if (row >= a.nrow) return;
-  const int cnt = min(a.sel_cnt[row], a.cap);
-  if (t >= cnt) return;
-  const int m = a.sel_idx[row * a.cap + t];
-  const int i = (int)(row % a.C);
-  const long long bs = row / a.C;   // batch * Hs + score head
-  const long long bhk = bs / a.nsh;   // batch * Hkv + kv head (Hs = Hkv * nsh)
-  const int code = i * a.nsh + (int)(bs % a.nsh);
-  const long long col = bhk * a.C + m;   // (batch, kv head), block m
-  atomicOr(&a.colmask[col * a.W + (code >> 5)], 1u << (code & 31));
 }
 
 __global__ void count_kernel(BwdArgs a) {
@@ -1456,6 +1451,11 @@ hipError_t launch_bwd_dq_mfma(const Shape& s, const BwdPtrs& p, char* ws, const 
   BwdArgs a = make_bwd_args(s, p, ws, wl);
   const long long units = (long long)s.B * s.Hkv * s.C;   // (batch, kv head, query block)
   hipError_t e;
+  // column bit masks of the selection transpose: zeroed here, set by the
+  // query-major kernels at the end of each gate row's work
+  const long long nmask = a.ncol * a.W;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)min((nmask + 255) / 256, 65535LL)),
+                     dim3(256), 0, st, a.colmask, nmask);
   // query-major pass (heads in chunks of 4, 2, 1; one head per chunk when
   // every head has its own gates and selection)
   int h = 0;
@@ -1478,12 +1478,7 @@ hipError_t launch_bwd_dq_mfma(const Shape& s, const BwdPtrs& p, char* ws, const 
     e = launch_dq<1>(a, h, 1, units, st);
     if (e != hipSuccess) return e;
   }
-  // selection transpose for the key-major stage
-  const long long nmask = a.ncol * a.W;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)min((nmask + 255) / 256, 65535LL)),
-                     dim3(256), 0, st, a.colmask, nmask);
-  const long long nmark = a.nrow * s.cap;
-  hipLaunchKernelGGL(mark_kernel, dim3((unsigned)((nmark + 255) / 256)), dim3(256), 0, st, a);
+  // selection transpose for the key-major stage (the masks are set)
   hipLaunchKernelGGL(count_kernel, dim3((unsigned)((a.ncol + 255) / 256)), dim3(256), 0, st, a);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, a);
   hipLaunchKernelGGL(fill_lists_kernel, dim3((unsigned)((a.ncol + 3) / 4)), dim3(256), 0, st, a);
@@ -1500,10 +1495,16 @@ hipError_t launch_bwd_dq_mfma(const Shape& s, const BwdPtrs& p, char* ws, const 
 hipError_t launch_bwd_dkdv_mfma(const Shape& s, const BwdPtrs& p, char* ws,
                                 const BwdWorkspace& wl, hipStream_t st) {
   BwdArgs a = make_bwd_args(s, p, ws, wl);
-  // dLogG: zero everywhere, then the key-major pass writes the selected entries
-  const long long ntab = a.nrow * s.C;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)min((ntab + 255) / 256, 65535LL)),
-                     dim3(256), 0, st, (uint32_t*)a.dlg, ntab);
+  // dLogG: the key-major pass writes the selected entries (with hard gates
+  // the dropped-block pass adds the other historical blocks of every row that
+  // holds a query).  With soft gates the dScores kernel writes the rest of the
+  // table as 0; otherwise it is zeroed here first.
+  const bool ds_fills = p.dscores != nullptr && !s.hard;
+  if (!ds_fills) {
+    const long long ntab = a.nrow * s.C;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)min((ntab + 255) / 256, 65535LL)),
+                       dim3(256), 0, st, (uint32_t*)a.dlg, ntab);
+  }
   const dim3 kgrid((unsigned)wl.max_chunks), kblock(256);
   const int v = (s.cu != nullptr ? 2 : 0) | (s.outer ? 1 : 0);
   switch (v) {
@@ -1531,7 +1532,8 @@ hipError_t launch_bwd_dkdv_mfma(const Shape& s, const BwdPtrs& p, char* ws,
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (p.dscores == nullptr) return hipSuccess;
-  return launch_dscores(s, p.dlog_gate, p.log_gate, p.dscores, st);
+  return launch_dscores(s, p.dlog_gate, p.log_gate, p.dscores, ds_fills ? p.sel_idx : nullptr,
+                        p.sel_cnt, st);
 }
 
 }  // namespace sas

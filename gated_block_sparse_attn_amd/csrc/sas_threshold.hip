@@ -221,34 +221,66 @@ __global__ void __launch_bounds__(256) threshold_kernel(const float* __restrict_
 // raw logits: ds_m = dLogG_m.  Hard gates (straight-through estimator): the
 // table holds dg itself for every historical block (full scope), so
 // ds_m = g_m (dg_m - sum_l g_l dg_l).
-__global__ void __launch_bounds__(256) dscores_kernel(const float* __restrict__ dlg,
-                                                      const float* __restrict__ lg,
-                                                      float* __restrict__ ds, long long rows,
-                                                      int C, int act, int hard) {
+//
+// One wavefront per gate row.  fill (sel_idx given; soft gates): the
+// key-major pass wrote dLogG only at the row's selected blocks, so the other
+// entries are not read and are written here as 0; the selected ones are
+// marked in a per-row LDS bit mask.
+constexpr int kDsRows = 4;                 // gate rows per workgroup
+constexpr int kDsMaxWords = 8192 / 32;     // bit mask words of the longest row
+__global__ void __launch_bounds__(64 * kDsRows) dscores_kernel(
+    float* __restrict__ dlg, const float* __restrict__ lg, float* __restrict__ ds, long long rows,
+    int C, int act, int hard, const int32_t* __restrict__ sel_idx,
+    const int32_t* __restrict__ sel_cnt, int cap) {
+  __shared__ uint32_t s_sel[kDsRows][kDsMaxWords];
   const int lane = threadIdx.x & 63;
-  const long long row = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  const int wv = threadIdx.x >> 6;
+  const long long row = (long long)blockIdx.x * kDsRows + wv;
+  const bool live = row < rows;
+  const bool fill = sel_idx != nullptr && !hard;
+  const bool masked = fill;   // only the selected entries are valid
+  if (masked) {   // every wavefront reaches both barriers
+    const int nw = (C + 31) / 32;
+    for (int x = lane; x < nw; x += 64) s_sel[wv][x] = 0u;
+    __syncthreads();
+    if (live) {
+      const int cnt = min(sel_cnt[row], cap);
+      const int32_t* sr = sel_idx + row * (long long)cap;
+      for (int e = lane; e < cnt; e += 64) {
+        const int m = sr[e];
+        atomicOr(&s_sel[wv][m >> 5], 1u << (m & 31));
+      }
+    }
+    __syncthreads();
+  }
+  if (!live) return;
   const int i = (int)(row % C);
-  const float* drow = dlg + row * (long long)C;
+  float* drow = dlg + row * (long long)C;
   const float* grow = lg + row * (long long)C;
   float* orow = ds + row * (long long)C;
+  auto dval = [&](int m) -> float {   // dLogG[i, m] of a historical block m < i
+    if (masked && ((s_sel[wv][m >> 5] >> (m & 31)) & 1u) == 0u) return 0.0f;
+    return drow[m];
+  };
+  float tot = 0.0f;
   if (hard) {   // dlog_gate holds dg of every historical block: g (dg - sum g dg)
-    float tot = 0.0f;
-    for (int m = lane; m < i; m += 64) tot += expf(grow[m]) * drow[m];
+    for (int m = lane; m < i; m += 64) tot += expf(grow[m]) * dval(m);
     tot = wave_sum_f(tot);
-    for (int m = lane; m < C; m += 64)
-      orow[m] = (m < i) ? expf(grow[m]) * (drow[m] - tot) : 0.0f;
   } else if (act == SAS_GATE_SOFTMAX) {
-    float tot = 0.0f;
-    for (int m = lane; m < i; m += 64) tot += drow[m];
+    for (int m = lane; m < i; m += 64) tot += dval(m);
     tot = wave_sum_f(tot);
-    for (int m = lane; m < C; m += 64)
-      orow[m] = (m < i) ? (drow[m] - expf(grow[m]) * tot) : 0.0f;
-  } else if (act == SAS_GATE_SIGMOID) {
-    for (int m = lane; m < C; m += 64)
-      orow[m] = (m < i) ? drow[m] * (1.0f - expf(grow[m])) : 0.0f;
-  } else {
-    for (int m = lane; m < C; m += 64) orow[m] = (m < i) ? drow[m] : 0.0f;
+  }
+  for (int m = lane; m < C; m += 64) {
+    const float d = m < i ? dval(m) : 0.0f;
+    if (fill) drow[m] = d;
+    float o = 0.0f;
+    if (m < i) {
+      if (hard) o = expf(grow[m]) * (d - tot);
+      else if (act == SAS_GATE_SOFTMAX) o = d - expf(grow[m]) * tot;
+      else if (act == SAS_GATE_SIGMOID) o = d * (1.0f - expf(grow[m]));
+      else o = d;
+    }
+    orow[m] = o;
   }
 }
 
@@ -267,12 +299,13 @@ hipError_t launch_threshold(const Shape& s, const float* scores, float* log_gate
   return hipGetLastError();
 }
 
-hipError_t launch_dscores(const Shape& s, const float* dlog_gate, const float* log_gate,
-                          float* dscores, hipStream_t st) {
+hipError_t launch_dscores(const Shape& s, float* dlog_gate, const float* log_gate,
+                          float* dscores, const int32_t* sel_idx, const int32_t* sel_cnt,
+                          hipStream_t st) {
   const long long rows = (long long)s.B * s.Hs * s.C;
-  const long long grid = (rows + 3) / 4;
-  hipLaunchKernelGGL(dscores_kernel, dim3((unsigned)grid), dim3(256), 0, st, dlog_gate, log_gate,
-                     dscores, rows, s.C, s.act, s.hard);
+  const long long grid = (rows + kDsRows - 1) / kDsRows;
+  hipLaunchKernelGGL(dscores_kernel, dim3((unsigned)grid), dim3(64 * kDsRows), 0, st, dlog_gate,
+                     log_gate, dscores, rows, s.C, s.act, s.hard, sel_idx, sel_cnt, s.cap);
   return hipGetLastError();
 }
 
