@@ -223,9 +223,10 @@ __global__ void __launch_bounds__(256) threshold_kernel(const float* __restrict_
 // ds_m = g_m (dg_m - sum_l g_l dg_l).
 //
 // One wavefront per gate row.  fill (sel_idx given; soft gates): the
-// key-major pass wrote dLogG only at the row's selected blocks, so the other
-// entries are not read and are written here as 0; the selected ones are
-// marked in a per-row LDS bit mask.
+// key-major pass wrote dLogG only at the row's selected blocks, so the values
+// of the other entries are not used and are written here as 0; the selected
+// ones are marked in a per-row LDS bit mask, and the softmax sum gathers them
+// from the row's selection list.
 constexpr int kDsRows = 4;                 // gate rows per workgroup
 constexpr int kDsMaxWords = 8192 / 32;     // bit mask words of the longest row
 __global__ void __launch_bounds__(64 * kDsRows) dscores_kernel(
@@ -239,6 +240,11 @@ __global__ void __launch_bounds__(64 * kDsRows) dscores_kernel(
   const bool live = row < rows;
   const bool fill = sel_idx != nullptr && !hard;
   const bool masked = fill;   // only the selected entries are valid
+  const int i = live ? (int)(row % C) : 0;
+  float* drow = dlg + (live ? row : 0) * (long long)C;
+  const float* grow = lg + (live ? row : 0) * (long long)C;
+  float* orow = ds + (live ? row : 0) * (long long)C;
+  float tot = 0.0f;
   if (masked) {   // every wavefront reaches both barriers
     const int nw = (C + 31) / 32;
     for (int x = lane; x < nw; x += 64) s_sel[wv][x] = 0u;
@@ -249,38 +255,53 @@ __global__ void __launch_bounds__(64 * kDsRows) dscores_kernel(
       for (int e = lane; e < cnt; e += 64) {
         const int m = sr[e];
         atomicOr(&s_sel[wv][m >> 5], 1u << (m & 31));
+        if (act == SAS_GATE_SOFTMAX) tot += drow[m];   // the row's sum over its selected blocks
       }
     }
     __syncthreads();
+    if (act == SAS_GATE_SOFTMAX) tot = wave_sum_f(tot);
   }
   if (!live) return;
-  const int i = (int)(row % C);
-  float* drow = dlg + row * (long long)C;
-  const float* grow = lg + row * (long long)C;
-  float* orow = ds + row * (long long)C;
-  auto dval = [&](int m) -> float {   // dLogG[i, m] of a historical block m < i
-    if (masked && ((s_sel[wv][m >> 5] >> (m & 31)) & 1u) == 0u) return 0.0f;
-    return drow[m];
-  };
-  float tot = 0.0f;
   if (hard) {   // dlog_gate holds dg of every historical block: g (dg - sum g dg)
-    for (int m = lane; m < i; m += 64) tot += expf(grow[m]) * dval(m);
+    for (int m = lane; m < i; m += 64) tot += expf(grow[m]) * drow[m];
     tot = wave_sum_f(tot);
-  } else if (act == SAS_GATE_SOFTMAX) {
-    for (int m = lane; m < i; m += 64) tot += dval(m);
+  } else if (act == SAS_GATE_SOFTMAX && !masked) {
+    for (int m = lane; m < i; m += 64) tot += drow[m];
     tot = wave_sum_f(tot);
   }
-  for (int m = lane; m < C; m += 64) {
-    const float d = m < i ? dval(m) : 0.0f;
-    if (fill) drow[m] = d;
-    float o = 0.0f;
+  // entry m: dLogG value raw (the load is in the row whatever m is; values of
+  // unwritten entries are not used) and log gate lgm -> (dLogG, dscores)
+  auto entry = [&](int m, float raw, float lgm, float& d, float& o) {
+    const bool valid = m < i && (!masked || ((s_sel[wv][m >> 5] >> (m & 31)) & 1u) != 0u);
+    d = valid ? raw : 0.0f;
+    o = 0.0f;
     if (m < i) {
-      if (hard) o = expf(grow[m]) * (d - tot);
-      else if (act == SAS_GATE_SOFTMAX) o = d - expf(grow[m]) * tot;
-      else if (act == SAS_GATE_SIGMOID) o = d * (1.0f - expf(grow[m]));
+      if (hard) o = expf(lgm) * (d - tot);
+      else if (act == SAS_GATE_SOFTMAX) o = d - expf(lgm) * tot;
+      else if (act == SAS_GATE_SIGMOID) o = d * (1.0f - expf(lgm));
       else o = d;
     }
-    orow[m] = o;
+  };
+  const bool vec = (C & 3) == 0 && (((uintptr_t)dlg | (uintptr_t)lg | (uintptr_t)ds) & 15) == 0;
+  if (vec) {   // 16-byte pieces (every row then starts 16-byte aligned)
+    for (int m0 = 4 * lane; m0 < C; m0 += 256) {
+      const float4 r = *(const float4*)(drow + m0);
+      const float4 gl = *(const float4*)(grow + m0);
+      float4 dv, ov;
+      entry(m0, r.x, gl.x, dv.x, ov.x);
+      entry(m0 + 1, r.y, gl.y, dv.y, ov.y);
+      entry(m0 + 2, r.z, gl.z, dv.z, ov.z);
+      entry(m0 + 3, r.w, gl.w, dv.w, ov.w);
+      if (fill) *(float4*)(drow + m0) = dv;
+      *(float4*)(orow + m0) = ov;
+    }
+  } else {
+    for (int m = lane; m < C; m += 64) {
+      float d, o;
+      entry(m, drow[m], grow[m], d, o);
+      if (fill) drow[m] = d;
+      orow[m] = o;
+    }
   }
 }
 
