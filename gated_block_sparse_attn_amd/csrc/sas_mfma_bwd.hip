@@ -654,6 +654,7 @@ __global__ void count_kernel(BwdArgs a) {
   int L = a.nsh;  // the diagonal block, once per score head
   for (int w = 0; w < a.W; ++w) L += __popc(a.colmask[col * a.W + w]);
   a.collen[col] = L;
+  a.chunk_hist[col] = 0;   // the order buckets' counters (chunk_count_kernel)
 }
 
 // exclusive prefix sums of the column lengths and chunk counts (one workgroup)
@@ -1484,8 +1485,6 @@ hipError_t launch_bwd_dq_mfma(const Shape& s, const BwdPtrs& p, char* ws, const 
   hipLaunchKernelGGL(fill_lists_kernel, dim3((unsigned)((a.ncol + 3) / 4)), dim3(256), 0, st, a);
   // schedule order of the key-major chunks
   const unsigned cgrid = (unsigned)((wl.max_chunks + 255) / 256);
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)min((a.ncol + 256) / 256, 65535LL)),
-                     dim3(256), 0, st, (uint32_t*)a.chunk_hist, a.ncol + 1);
   hipLaunchKernelGGL(chunk_count_kernel, dim3(cgrid), dim3(256), 0, st, a);
   hipLaunchKernelGGL(scan_ints_kernel, dim3(1), dim3(1024), 0, st, a.chunk_hist, a.ncol);
   hipLaunchKernelGGL(chunk_scatter_kernel, dim3(cgrid), dim3(256), 0, st, a);
