@@ -592,3 +592,36 @@ def test_staged_backward_matches_combined(shape):
     torch.cuda.synchronize()
     for name, got, want in zip(("dq", "dk", "dv", "dlog_gate", "dscores"), (dq, dk, dv, dlg, dsc), ref):
         assert torch.equal(got.cpu(), want.cpu()), f"{name} differs between staged and combined backward"
+
+
+def test_dscores_unaligned_tables_match_aligned():
+    """dLogG and dScores written into tables that start 4 bytes past a
+    16-byte boundary (the dScores pass then takes its element-wise row path
+    instead of 16-byte pieces) equal those written into aligned tables, bit
+    for bit, and so do dQ, dK and dV."""
+    B, Hq, Hkv, N, D, blk, K = 1, 8, 2, 2048, 128, 64, 4
+    log("dScores with unaligned tables")
+    w = workloads.custom(B, Hq, Hkv, N, D, blk, K, dtype="bf16", seed=12, score_std=2.0)
+    p = problem_of(w, K)
+    inp = workloads.generate(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do, sc = (inp[n].to(dev) for n in ("q", "k", "v", "do", "scores"))
+    lg, tau, si, cnt = api.gate_threshold(p, sc)
+    o, lse = api.gated_attn_fwd(p, q, k, v, lg, si, cnt)
+    ws = torch.empty(api.bwd_workspace_size(p, si.shape[-1]), dtype=torch.uint8, device=dev)
+    n = lg.numel()
+    buf = torch.full((2 * n + 1,), float("nan"), dtype=torch.float32, device=dev)
+    tables = {"aligned": (torch.full_like(lg, float("nan")), torch.full_like(lg, float("nan"))),
+              "unaligned": (buf[1:1 + n].view(lg.shape), buf[1 + n:].view(lg.shape))}
+    assert tables["aligned"][0].data_ptr() % 16 == 0
+    assert tables["unaligned"][0].data_ptr() % 16 == 4
+    out = {}
+    for name, (dlg, dsc) in tables.items():
+        dq, dk, dv = (torch.full_like(x, float("nan")) for x in (q, k, v))
+        api.gated_attn_bwd_dq(p, q, k, v, o, do, lse, lg, si, cnt, dq, ws)
+        api.gated_attn_bwd_dkdv(p, q, k, v, do, lse, lg, si, cnt, dk, dv, dlg, dsc, ws)
+        torch.cuda.synchronize()
+        out[name] = [x.cpu() for x in (dq, dk, dv, dlg, dsc)]
+    for label, a, b in zip(("dq", "dk", "dv", "dlog_gate", "dscores"), out["aligned"], out["unaligned"]):
+        assert torch.isfinite(a).all(), label
+        assert torch.equal(a, b), f"{label} differs between aligned and unaligned tables"
