@@ -625,3 +625,30 @@ def test_dscores_unaligned_tables_match_aligned():
     for label, a, b in zip(("dq", "dk", "dv", "dlog_gate", "dscores"), out["aligned"], out["unaligned"]):
         assert torch.isfinite(a).all(), label
         assert torch.equal(a, b), f"{label} differs between aligned and unaligned tables"
+
+
+@pytest.mark.parametrize("gate_act", ["softmax", "sigmoid"])
+def test_dlog_gate_without_dscores_matches(gate_act):
+    """Without a dScores output the dLogG table is zero-filled before the
+    key-major pass instead of completed by the dScores pass: dQ, dK, dV and
+    dLogG must equal those of the call that asks for dScores, bit for bit
+    (every element written: the tables start NaN-filled)."""
+    B, Hq, Hkv, N, D, blk, K = 1, 8, 2, 2048, 128, 64, 6
+    log(f"backward without dScores ({gate_act})")
+    w = workloads.custom(B, Hq, Hkv, N, D, blk, K, dtype="bf16", seed=13, score_std=2.0)
+    p = problem_of(w, K, gate_act=gate_act)
+    inp = workloads.generate(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do, sc = (inp[n].to(dev) for n in ("q", "k", "v", "do", "scores"))
+    lg, tau, si, cnt = api.gate_threshold(p, sc)
+    o, lse = api.gated_attn_fwd(p, q, k, v, lg, si, cnt)
+    res = {}
+    for want in (True, False):
+        outs = {"dlog_gate": torch.full_like(lg, float("nan"))}
+        got = api.gated_attn_bwd(p, q, k, v, o, do, lse, lg, si, cnt, want_dscores=want, outputs=outs)
+        torch.cuda.synchronize()
+        res[want] = [x.cpu() for x in got[:4]]
+        assert (got[4] is not None) == want
+    for label, a, b in zip(("dq", "dk", "dv", "dlog_gate"), res[True], res[False]):
+        assert torch.isfinite(b).all(), label
+        assert torch.equal(a, b), f"{label} differs with and without dScores"
